@@ -1,0 +1,188 @@
+"""CPU oracle for batch-invariant GEMM and attention (float64, plain C).
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU
+baseline leg of the benchmark may import this package.  The library under
+test never imports it, and it imports nothing from the library.
+
+The definitions follow the mlx-batch-invariant README:
+  * section "Use" -- linear(x, w, bias) with w in (N, K), matmul(a, b) with
+    b in (K, N), addmm(c, a, b, alpha, beta) and
+    scaled_dot_product_attention(q, k, v, mask="causal");
+  * section "Accuracy" -- results are judged against a float64 reference.
+Inputs may be torch tensors (any dtype, any device-less CPU tensor) or numpy
+arrays; they are converted exactly to float64 before the C code sees them.
+Outputs are unrounded float64 numpy arrays.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        from . import build as _b
+        _b.build()
+    _lib = _bind(ctypes.CDLL(_LIB_PATH))
+    return _lib
+
+
+class use_library:
+    """Context manager that points this module at another build of oracle.c.
+
+    Used only by the tests that plant mistakes in a copy of the oracle to show
+    that the pins catch them.
+    """
+
+    def __init__(self, path: str):
+        self.path = path
+
+    def __enter__(self):
+        global _lib
+        self.saved = _lib
+        _lib = _bind(ctypes.CDLL(self.path))
+        return self
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self.saved
+        return False
+
+
+def _bind(lib):
+    d, i64, p = ctypes.c_double, ctypes.c_int64, ctypes.c_void_p
+    lib.oracle_gemm_f64.argtypes = [p, i64, p, i64, ctypes.c_int, p, i64, d, d, p, i64, i64, i64, i64]
+    lib.oracle_gemm_f64.restype = None
+    lib.oracle_sdpa_f64.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, d,
+                                    ctypes.c_int, p, p]
+    lib.oracle_sdpa_f64.restype = None
+    lib.oracle_threads.restype = ctypes.c_int
+    lib.oracle_set_threads.argtypes = [ctypes.c_int]
+    return lib
+
+
+def threads() -> int:
+    """Number of OpenMP threads the oracle will use."""
+    return int(_load().oracle_threads())
+
+
+def set_threads(n: int) -> None:
+    _load().oracle_set_threads(int(n))
+
+
+def _f64(x) -> np.ndarray:
+    """Exact conversion of a torch tensor / numpy array to C-contiguous float64."""
+    if hasattr(x, "detach"):
+        x = x.detach().to("cpu")
+        import torch
+        x = x.to(torch.float64).numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def gemm(a, b, b_is_nk: bool, c=None, alpha: float = 1.0, beta: float = 1.0) -> np.ndarray:
+    """alpha * (a @ B) + beta * c, with B = b.T when b_is_nk (b is (N, K)), else B = b (K, N).
+
+    c may be None, a length-N row (broadcast over rows) or an (M, N) matrix.
+    With beta == 0 c is not read.
+    """
+    A = _f64(a)
+    Bm = _f64(b)
+    M, K = A.shape
+    if b_is_nk:
+        N, Kb = Bm.shape
+    else:
+        Kb, N = Bm.shape
+    if Kb != K:
+        raise ValueError(f"inner dims differ: {K} vs {Kb}")
+    out = np.empty((M, N), dtype=np.float64)
+    cptr, ldc = None, 0
+    Cm = None
+    if c is not None and beta != 0.0:
+        Cm = _f64(c)
+        if Cm.ndim == 1:
+            if Cm.shape[0] != N:
+                raise ValueError("bias length must be N")
+            ldc = 0
+        else:
+            if Cm.shape != (M, N):
+                raise ValueError("C must be (M, N)")
+            ldc = N
+        cptr = _ptr(Cm)
+    _load().oracle_gemm_f64(_ptr(A), K, _ptr(Bm), Bm.shape[1], 1 if b_is_nk else 0,
+                            cptr, ldc, float(alpha), float(beta), _ptr(out), N, M, N, K)
+    return out
+
+
+def linear(x, w, bias=None) -> np.ndarray:
+    """y = x @ w.T + bias, w in the (N, K) layout (README, section "Use")."""
+    return gemm(x, w, True, bias, 1.0, 1.0)
+
+
+def matmul(a, b) -> np.ndarray:
+    """y = a @ b, b in the (K, N) layout (README, section "Use")."""
+    return gemm(a, b, False, None, 1.0, 0.0)
+
+
+def addmm(c, a, b, alpha: float = 1.0, beta: float = 1.0) -> np.ndarray:
+    """alpha * (a @ b) + beta * c, b in (K, N) (README, section "Use")."""
+    return gemm(a, b, False, c, alpha, beta)
+
+
+def sdpa(q, k, v, causal: bool = False, mask=None, scale: float | None = None) -> np.ndarray:
+    """Softmax attention over (B, Hq, Lq, D) queries and (B, Hkv, S, D) keys / values.
+
+    Bottom-right causal alignment, query head h reads KV head floor(h*Hkv/Hq),
+    mask is boolean (True = attend) and broadcastable to (B, Hq, Lq, S).
+    scale defaults to 1/sqrt(D).
+    """
+    Q, Kt, V = _f64(q), _f64(k), _f64(v)
+    B, Hq, Lq, D = Q.shape
+    Bk, Hkv, S, Dk = Kt.shape
+    if V.shape != Kt.shape or Bk != B or Dk != D:
+        raise ValueError("k / v shapes do not match q")
+    if Hq % Hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    if scale is None:
+        scale = 1.0 / float(np.sqrt(D))
+    out = np.empty((B, Hq, Lq, D), dtype=np.float64)
+    i64x4 = ctypes.c_int64 * 4
+
+    def strides(a):
+        return i64x4(*[s // a.itemsize for s in a.strides])
+
+    mptr, mstr = None, i64x4(0, 0, 0, 0)
+    M8 = None
+    if mask is not None:
+        if hasattr(mask, "detach"):
+            mask = mask.detach().to("cpu").numpy()
+        M8 = np.asarray(mask).astype(np.uint8)
+        while M8.ndim < 4:
+            M8 = M8[None]
+        M8 = np.ascontiguousarray(M8)
+        st = []
+        for dim, want in zip(range(4), (B, Hq, Lq, S)):
+            if M8.shape[dim] == want:
+                st.append(M8.strides[dim])
+            elif M8.shape[dim] == 1:
+                st.append(0)
+            else:
+                raise ValueError(f"mask dim {dim} is {M8.shape[dim]}, expected 1 or {want}")
+        mstr = i64x4(*st)
+        mptr = _ptr(M8)
+    _load().oracle_sdpa_f64(_ptr(Q), strides(Q), _ptr(Kt), strides(Kt), _ptr(V), strides(V),
+                            _ptr(out), B, Hq, Hkv, Lq, S, D, float(scale), 1 if causal else 0,
+                            mptr, mstr)
+    return out
