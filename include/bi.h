@@ -1,0 +1,210 @@
+/*
+ * bi.h -- batch-invariant matrix multiply and attention for AMD CDNA4 (gfx950).
+ *
+ * What "batch-invariant" means here (mlx-batch-invariant README, section
+ * 'What "batch-invariant" means here'): the bits of every output row are the
+ * same whatever the number of other rows in the call, whatever those rows
+ * hold, however many query tokens were submitted together (decode or chunked
+ * prefill), however long the KV cache is, and whether the call was made
+ * eagerly or replayed from a captured HIP graph.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *    never allocates, frees or keeps a pointer after returning, never
+ *    synchronises, and enqueues all its work on `stream` (a hipStream_t;
+ *    NULL means the legacy default stream).  Calls are therefore safe to
+ *    record into a HIP graph.
+ *  - Element strides and leading dimensions are given in ELEMENTS.  The
+ *    innermost dimension of every tensor must be contiguous (stride 1).
+ *  - Every argument is validated on the host before anything is enqueued.
+ *    A call that returns an error has written nothing.  No C++ exception
+ *    crosses this interface.  bi_last_error() describes the last failure on
+ *    the calling thread.
+ *  - Nothing the library does depends on an environment variable or a
+ *    global switch: the arithmetic of a call is a function of its
+ *    arguments' values and of the compile-time tile and chunk constants,
+ *    whose identity is reported by bi_abi_version().
+ *  - Unsupported inputs are refused with BI_ERR_UNSUPPORTED; nothing falls
+ *    back to a different (batch-variant) kernel.  (README, section "Use":
+ *    anything that cannot be made invariant raises instead of silently
+ *    falling back.)
+ */
+#ifndef BI_H
+#define BI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    BI_OK = 0,
+    BI_ERR_INVALID = 1,     /* malformed arguments: bad shapes, null pointers, Hq % Hkv != 0 ... */
+    BI_ERR_UNSUPPORTED = 2, /* well-formed but outside the supported set (dtype pair, alignment, D) */
+    BI_ERR_WORKSPACE = 3,   /* workspace pointer null or smaller than the *_workspace_bytes query */
+    BI_ERR_DEVICE = 4       /* the HIP runtime reported an error (launch failure, no device) */
+} bi_status;
+
+typedef enum {
+    BI_F32 = 0,   /* IEEE binary32 */
+    BI_F16 = 1,   /* IEEE binary16 */
+    BI_BF16 = 2   /* bfloat16 (upper half of a binary32) */
+} bi_dtype;
+
+/*
+ * Matrix multiply family (README, section "Use": linear, matmul, addmm;
+ * section "How the kernels work", GEMM paragraph).
+ *
+ * Arithmetic contract, identical for all three calls and every M:
+ *   acc[m,n] = fp32 sum over k of A[m,k] * B[k,n], formed by one chain of
+ *              gfx950 MFMA instructions (16x16x32 for bf16/fp16 inputs,
+ *              16x16x4 for fp32 inputs) walking k upwards in fixed groups of
+ *              32 (resp. 4), starting from 0.  The chain depends on K only;
+ *              nothing splits K, and no tile choice changes the chain.
+ *   t        = fp32(beta) * fp32(C[m,n])          (0 when there is no C / beta == 0)
+ *   y[m,n]   = round_to_out_dtype( fmaf(alpha, acc, t) )
+ *              i.e. the bias / C term is added to the fp32 accumulator and
+ *              the sum is rounded ONCE to the output dtype (round to nearest
+ *              even; NaN stays NaN).
+ *
+ * Supported dtype pairs (in_dt -> out_dt):
+ *   F32 -> F32, BF16 -> BF16, F16 -> F16, BF16 -> F32, F16 -> F32.
+ * The bias / C tensor, when present, has the OUTPUT dtype.
+ * Shapes: M, N, K >= 0 and < 2^31.  M == 0 or N == 0 enqueues nothing.
+ * Alignment (else BI_ERR_UNSUPPORTED): every base pointer 16-byte aligned;
+ *   K a multiple of 8 (16-bit inputs) or 4 (fp32 inputs); lda / ldb / ldw
+ *   multiples of 8 (16-bit) or 4 (fp32) elements; for the (K, N) layout of
+ *   bi_matmul / bi_addmm also N a multiple of 8 (16-bit) or 4 (fp32).
+ */
+
+/* y (M,N) = x (M,K) . w^T + bias,  w in the (N,K) nn.Linear layout.
+ * x: row m at x + m*ldx (ldx >= K).  w: row n at w + n*ldw (ldw >= K).
+ * bias: NULL or N contiguous elements of out_dt.  y: row m at y + m*ldy (ldy >= N). */
+bi_status bi_linear(const void *x, int64_t ldx,
+                    const void *w, int64_t ldw,
+                    const void *bias,
+                    void *y, int64_t ldy,
+                    int64_t M, int64_t N, int64_t K,
+                    bi_dtype in_dt, bi_dtype out_dt,
+                    void *stream);
+
+/* c (M,N) = a (M,K) . b (K,N).  b: row k at b + k*ldb (ldb >= N). */
+bi_status bi_matmul(const void *a, int64_t lda,
+                    const void *b, int64_t ldb,
+                    void *c, int64_t ldc,
+                    int64_t M, int64_t N, int64_t K,
+                    bi_dtype in_dt, bi_dtype out_dt,
+                    void *stream);
+
+/* out (M,N) = alpha * (a (M,K) . b (K,N)) + beta * cin.
+ * cin: out_dt elements, row m at cin + m*ldcin; ldcin == 0 broadcasts one
+ * row of N elements to every m (the bias form).  When beta == 0, cin is not
+ * read and may be NULL (BLAS convention).  out may alias cin only if
+ * ldo == ldcin and the pointers are equal (each element is read before its
+ * own write and by no other thread). */
+bi_status bi_addmm(const void *cin, int64_t ldcin,
+                   const void *a, int64_t lda,
+                   const void *b, int64_t ldb,
+                   void *out, int64_t ldo,
+                   int64_t M, int64_t N, int64_t K,
+                   float alpha, float beta,
+                   bi_dtype in_dt, bi_dtype out_dt,
+                   void *stream);
+
+/*
+ * Scaled dot-product attention with grouped-query heads (README, section
+ * "Use": scaled_dot_product_attention(q, k, v, mask="causal"); section "How
+ * the kernels work", attention paragraph; section "Why MLX is not
+ * invariant", attention bullets, for what must not change the bits).
+ *
+ * q (B, Hq, Lq, D), k and v (B, Hkv, S, D), o (B, Hq, Lq, D); all share
+ * dtype dt (F32, F16 or BF16) and have element strides *_str[0..3] with
+ * *_str[3] == 1.  Query head h reads KV head floor(h * Hkv / Hq).
+ * Query i sits at key position S - Lq + i (bottom-right alignment); with
+ * causal != 0 it sees keys j <= S - Lq + i.  mask: NULL, or uint8 over
+ * (B, Hq, Lq, S) with element strides mask_str[0..3] (0 broadcasts that
+ * dimension, any value for the key dimension), nonzero = may attend.
+ * scale multiplies q.k; pass 1/sqrt(D) for the usual softmax scaling.
+ * A query that sees no key produces a row of zeros.
+ *
+ * Arithmetic contract (fixed, independent of B, Lq, S and of the other rows):
+ *   keys are cut at absolute positions into splits of 256, each split into
+ *   blocks of 64.  Within a split, blocks are folded in ascending order with
+ *   an online softmax in fp32 (exp2 with the scale pre-multiplied by
+ *   log2(e)); a block with no visible key leaves the running state
+ *   untouched.  Split partials (m, l, O) are then folded left to right in
+ *   ascending split order, O is divided by l, -0 becomes +0, and the result
+ *   is rounded once to dt.  For 16-bit dt the softmax weights are rounded
+ *   to dt before the P.V product; fp32 keeps them in fp32.
+ *
+ * Supported: D in {64, 128}; Hq % Hkv == 0; Lq <= S when causal; every
+ * base pointer 16-byte aligned and every stride except the last a multiple
+ * of 8 (16-bit) or 4 (fp32) elements.
+ * Workspace: ws must hold bi_sdpa_workspace_bytes(B, Hq, Lq, S, D) bytes,
+ * 256-byte aligned, device memory owned by the caller; its contents on entry
+ * do not matter and on return are unspecified.  Two calls that run at the
+ * same time must not share a workspace.
+ */
+bi_status bi_sdpa(const void *q, const int64_t q_str[4],
+                  const void *k, const int64_t k_str[4],
+                  const void *v, const int64_t v_str[4],
+                  void *o, const int64_t o_str[4],
+                  int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t S, int64_t D,
+                  float scale, int causal,
+                  const uint8_t *mask, const int64_t mask_str[4],
+                  bi_dtype dt,
+                  void *ws, size_t ws_bytes,
+                  void *stream);
+
+/* Bytes of workspace bi_sdpa needs for these sizes (0 when there is nothing to do). */
+size_t bi_sdpa_workspace_bytes(int64_t B, int64_t Hq, int64_t Lq, int64_t S, int64_t D);
+
+/*
+ * Batch-VARIANT comparator, for measurement only.  It runs the same
+ * fragment loads, MFMA instruction and epilogue as bi_linear but cuts K
+ * into `splits` contiguous ranges whose fp32 partial sums are added in a
+ * second pass -- the M-dependent split-K tuning that the README (section
+ * "Why MLX is not invariant", matmul paragraph) identifies as the source of
+ * batch variance.  Its results are NOT batch-invariant by design.
+ * splits must be in 1..16; K is cut into that many ranges of whole k-groups,
+ * as even as possible.  ws must hold bi_variant_workspace_bytes(M, N, splits)
+ * bytes (256-byte aligned device memory); same dtype / alignment rules as
+ * bi_linear.
+ * bi_variant_splits(M) is the M-keyed policy: 8 for M <= 16, 4 for M <= 64,
+ * 2 for M <= 128, 1 above.
+ */
+bi_status bi_variant_linear(const void *x, int64_t ldx,
+                            const void *w, int64_t ldw,
+                            const void *bias,
+                            void *y, int64_t ldy,
+                            int64_t M, int64_t N, int64_t K,
+                            bi_dtype in_dt, bi_dtype out_dt,
+                            int splits, void *ws, size_t ws_bytes,
+                            void *stream);
+size_t bi_variant_workspace_bytes(int64_t M, int64_t N, int splits);
+int bi_variant_splits(int64_t M);
+
+/* Which kernel configuration a GEMM of this shape runs on ("gemm_skinny_nk/fm1",
+ * "gemm_tiled_kn/128x128", ...; b_kn != 0 for the (K, N) layout of bi_matmul /
+ * bi_addmm).  Informational: every configuration computes the same bits.
+ * Returns "none" for empty or oversized shapes. */
+const char *bi_gemm_kernel_name(int64_t M, int64_t N, int b_kn);
+
+/* Name of a status code ("BI_OK", ...); never NULL. */
+const char *bi_status_name(bi_status s);
+/* Message describing the last error on the calling thread; "" after success.
+ * Valid until the next bi_* call on this thread. */
+const char *bi_last_error(void);
+/* (ABI major << 16) | bits version.  The bits version changes whenever a
+ * compile-time constant that shapes the arithmetic (k-group order, KV block
+ * and split sizes) changes, i.e. whenever output bits may change. */
+int bi_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BI_H */

@@ -1,0 +1,295 @@
+"""Batch-invariant GEMM and attention for AMD MI355X (gfx950).
+
+Python binding of libbi.so: argument marshalling only.  Every step of the
+computation runs in the library's HIP kernels; PyTorch provides device
+memory and the current stream.  There is no fallback: a call the library
+cannot serve invariantly raises (mlx-batch-invariant README, section "Use":
+unsupported cases raise NotImplementedError rather than silently falling
+back).
+
+Entry points (same names as the C ABI, plus the README's short names):
+    bi_linear(x, w, bias=None)              y = x w^T + bias, w is (N, K)
+    bi_matmul(a, b)                         y = a b, b is (K, N)
+    bi_addmm(c, a, b, alpha=1, beta=1)      y = alpha a b + beta c
+    bi_sdpa(q, k, v, causal=False, mask=None, scale=None)
+    bi_variant_linear(x, w, bias=None, splits=None)   batch-VARIANT comparator
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+
+import torch
+
+from . import _native
+from ._native import BI_BF16, BI_F16, BI_F32
+
+__all__ = ["bi_linear", "bi_matmul", "bi_addmm", "bi_sdpa", "bi_variant_linear",
+           "linear", "matmul", "addmm", "scaled_dot_product_attention",
+           "abi_version", "library_path", "BiError"]
+
+_DT = {torch.float32: BI_F32, torch.float16: BI_F16, torch.bfloat16: BI_BF16}
+
+
+class BiError(RuntimeError):
+    """The library reported a device error or a workspace problem."""
+
+
+def library_path() -> str:
+    return _native.LIB_PATH
+
+
+def abi_version() -> int:
+    return int(_native.load().bi_abi_version())
+
+
+def _raise(status: int, fn: str):
+    lib = _native.load()
+    msg = (lib.bi_last_error() or b"").decode()
+    name = lib.bi_status_name(status).decode()
+    text = f"{fn}: {name}: {msg}"
+    if status == _native.BI_ERR_UNSUPPORTED:
+        raise NotImplementedError(text)
+    if status == _native.BI_ERR_INVALID:
+        raise ValueError(text)
+    raise BiError(text)
+
+
+def _check(status: int, fn: str):
+    if status != _native.BI_OK:
+        _raise(status, fn)
+
+
+def _dt(t: torch.Tensor, what: str) -> int:
+    try:
+        return _DT[t.dtype]
+    except KeyError:
+        raise NotImplementedError(f"{what}: dtype {t.dtype} is not supported") from None
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _on_gpu(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("tensors are on different devices")
+    return dev
+
+
+def _rows(t: torch.Tensor) -> torch.Tensor:
+    """View a (..., K) tensor as (M, K) with a unit inner stride (copies only if it must: exact)."""
+    t2 = t.reshape(math.prod(t.shape[:-1]), t.shape[-1])
+    if t2.stride(-1) != 1:
+        t2 = t2.contiguous()
+    return t2
+
+
+def _ld(t: torch.Tensor) -> int:
+    return t.stride(0) if t.dim() == 2 and t.shape[0] > 1 else max(t.shape[-1], 1)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _aligned_ld(t: torch.Tensor) -> torch.Tensor:
+    """Row pitch must be a multiple of 16 bytes; compact copies satisfy that whenever K allows."""
+    epc = 16 // t.element_size()
+    if t.dim() == 2 and t.shape[0] > 1 and t.stride(0) % epc != 0:
+        return t.contiguous()
+    return t
+
+
+def bi_linear(x: torch.Tensor, w: torch.Tensor, bias: torch.Tensor | None = None,
+              out_dtype: torch.dtype | None = None) -> torch.Tensor:
+    """y = x w^T + bias with w in the (N, K) nn.Linear layout; leading dims of x are batch."""
+    dev = _on_gpu(x, w, bias)
+    if x.dtype != w.dtype:
+        raise ValueError("x and w must share a dtype")
+    out_dtype = out_dtype or x.dtype
+    lead = x.shape[:-1]
+    x2 = _aligned_ld(_rows(x))
+    w2 = _aligned_ld(_rows(w))
+    M, K = x2.shape
+    N = w2.shape[0]
+    if w2.shape[1] != K:
+        raise ValueError(f"inner dims differ: x has K={K}, w has K={w2.shape[1]}")
+    b = None
+    if bias is not None:
+        if bias.shape != (N,) or bias.dtype != out_dtype:
+            raise ValueError("bias must be (N,) in the output dtype")
+        b = bias.contiguous()
+    y = torch.empty((M, N), dtype=out_dtype, device=dev)
+    lib = _native.load()
+    st = lib.bi_linear(_ptr(x2), _ld(x2), _ptr(w2), _ld(w2), _ptr(b), _ptr(y), max(N, 1),
+                       M, N, K, _dt(x2, "bi_linear"), _dt(y, "bi_linear"), _stream(dev))
+    _check(st, "bi_linear")
+    return y.reshape(*lead, N)
+
+
+def bi_matmul(a: torch.Tensor, b: torch.Tensor, out_dtype: torch.dtype | None = None) -> torch.Tensor:
+    """y = a b with b in the (K, N) layout; leading dims of a are batch."""
+    dev = _on_gpu(a, b)
+    if a.dtype != b.dtype:
+        raise ValueError("a and b must share a dtype")
+    if b.dim() != 2:
+        raise NotImplementedError("bi_matmul: batched right operands are not supported")
+    out_dtype = out_dtype or a.dtype
+    lead = a.shape[:-1]
+    a2 = _aligned_ld(_rows(a))
+    b2 = _aligned_ld(_rows(b))
+    M, K = a2.shape
+    if b2.shape[0] != K:
+        raise ValueError("inner dims differ")
+    N = b2.shape[1]
+    y = torch.empty((M, N), dtype=out_dtype, device=dev)
+    lib = _native.load()
+    st = lib.bi_matmul(_ptr(a2), _ld(a2), _ptr(b2), _ld(b2), _ptr(y), max(N, 1), M, N, K,
+                       _dt(a2, "bi_matmul"), _dt(y, "bi_matmul"), _stream(dev))
+    _check(st, "bi_matmul")
+    return y.reshape(*lead, N)
+
+
+def bi_addmm(c: torch.Tensor | None, a: torch.Tensor, b: torch.Tensor, alpha: float = 1.0,
+             beta: float = 1.0, out_dtype: torch.dtype | None = None) -> torch.Tensor:
+    """alpha (a b) + beta c, b in (K, N); c is (M, N) or a broadcast (N,) row."""
+    dev = _on_gpu(a, b, c)
+    if a.dtype != b.dtype:
+        raise ValueError("a and b must share a dtype")
+    if a.dim() != 2 or b.dim() != 2:
+        raise NotImplementedError("bi_addmm: 2-D operands only")
+    out_dtype = out_dtype or a.dtype
+    a2 = _aligned_ld(_rows(a))
+    b2 = _aligned_ld(_rows(b))
+    M, K = a2.shape
+    if b2.shape[0] != K:
+        raise ValueError("inner dims differ")
+    N = b2.shape[1]
+    c2, ldc = None, 0
+    if beta != 0.0:
+        if c is None:
+            raise ValueError("c is required when beta != 0")
+        if c.dtype != out_dtype:
+            raise ValueError("c must have the output dtype")
+        if c.dim() == 1 or (c.dim() == 2 and c.shape[0] == 1 and M != 1):
+            c2 = c.reshape(-1).contiguous()
+            if c2.shape[0] != N:
+                raise ValueError("broadcast c must have N elements")
+            ldc = 0
+        else:
+            if tuple(c.shape) != (M, N):
+                raise ValueError("c must be (M, N) or (N,)")
+            c2 = c if c.stride(-1) == 1 else c.contiguous()
+            ldc = c2.stride(0) if M > 1 else N
+    y = torch.empty((M, N), dtype=out_dtype, device=dev)
+    lib = _native.load()
+    st = lib.bi_addmm(_ptr(c2), ldc, _ptr(a2), _ld(a2), _ptr(b2), _ld(b2), _ptr(y), max(N, 1), M, N, K,
+                      float(alpha), float(beta), _dt(a2, "bi_addmm"), _dt(y, "bi_addmm"), _stream(dev))
+    _check(st, "bi_addmm")
+    return y
+
+
+def sdpa_workspace_bytes(B: int, Hq: int, Lq: int, S: int, D: int) -> int:
+    return int(_native.load().bi_sdpa_workspace_bytes(B, Hq, Lq, S, D))
+
+
+def _mask_strides(mask: torch.Tensor, shape) -> tuple:
+    m = mask
+    while m.dim() < 4:
+        m = m.unsqueeze(0)
+    st = []
+    for d, want in enumerate(shape):
+        if m.shape[d] == want:
+            st.append(m.stride(d) if want > 1 else 0)
+        elif m.shape[d] == 1:
+            st.append(0)
+        else:
+            raise ValueError(f"mask dim {d} is {m.shape[d]}, expected 1 or {want}")
+    return m, st
+
+
+def bi_sdpa(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+            mask: torch.Tensor | None = None, scale: float | None = None,
+            workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Softmax attention, q (B, Hq, Lq, D), k / v (B, Hkv, S, D), bottom-right causal, bool mask."""
+    dev = _on_gpu(q, k, v, mask)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share a dtype")
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or k.shape != v.shape:
+        raise ValueError("q must be (B, Hq, Lq, D) and k, v (B, Hkv, S, D)")
+    B, Hq, Lq, D = q.shape
+    Bk, Hkv, S, Dk = k.shape
+    if Bk != B or Dk != D:
+        raise ValueError("k / v batch or head dim differ from q")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    qs = q if q.stride(-1) == 1 else q.contiguous()
+    ks = k if k.stride(-1) == 1 else k.contiguous()
+    vs = v if v.stride(-1) == 1 else v.contiguous()
+    o = torch.empty((B, Hq, Lq, D), dtype=q.dtype, device=dev)
+    mptr, mstr = None, None
+    m8 = None
+    if mask is not None:
+        if mask.dtype not in (torch.bool, torch.uint8):
+            raise NotImplementedError("only boolean masks are supported")
+        m8, st = _mask_strides(mask.to(torch.uint8) if mask.dtype == torch.bool else mask, (B, Hq, Lq, S))
+        mptr, mstr = _ptr(m8), _native.i64x4(st)
+    lib = _native.load()
+    need = int(lib.bi_sdpa_workspace_bytes(B, Hq, Lq, S, D))
+    ws = workspace
+    if need > 0 and (ws is None or ws.numel() * ws.element_size() < need):
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    st = lib.bi_sdpa(_ptr(qs), _native.i64x4(qs.stride()), _ptr(ks), _native.i64x4(ks.stride()),
+                     _ptr(vs), _native.i64x4(vs.stride()), _ptr(o), _native.i64x4(o.stride()),
+                     B, Hq, Hkv, Lq, S, D, float(scale), 1 if causal else 0, mptr, mstr,
+                     _dt(q, "bi_sdpa"), _ptr(ws) if ws is not None else None,
+                     need if ws is not None else 0, _stream(dev))
+    _check(st, "bi_sdpa")
+    return o
+
+
+def bi_variant_linear(x: torch.Tensor, w: torch.Tensor, bias: torch.Tensor | None = None,
+                      splits: int | None = None, out_dtype: torch.dtype | None = None) -> torch.Tensor:
+    """Batch-VARIANT comparator: bi_linear's kernels with M-keyed split-K (not invariant)."""
+    dev = _on_gpu(x, w, bias)
+    out_dtype = out_dtype or x.dtype
+    x2 = _aligned_ld(_rows(x))
+    w2 = _aligned_ld(_rows(w))
+    M, K = x2.shape
+    N = w2.shape[0]
+    lib = _native.load()
+    if splits is None:
+        splits = int(lib.bi_variant_splits(M))
+    b = bias.contiguous() if bias is not None else None
+    y = torch.empty((M, N), dtype=out_dtype, device=dev)
+    need = int(lib.bi_variant_workspace_bytes(M, N, splits))
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = lib.bi_variant_linear(_ptr(x2), _ld(x2), _ptr(w2), _ld(w2), _ptr(b), _ptr(y), max(N, 1),
+                               M, N, K, _dt(x2, "bi_variant_linear"), _dt(y, "bi_variant_linear"),
+                               int(splits), _ptr(ws), need, _stream(dev))
+    _check(st, "bi_variant_linear")
+    return y.reshape(*x.shape[:-1], N)
+
+
+# README, section "Use": the short names.
+linear = bi_linear
+matmul = bi_matmul
+addmm = bi_addmm
+
+
+def scaled_dot_product_attention(q, k, v, mask=None, scale=None):
+    """README-style call: mask is None, "causal" or a boolean tensor."""
+    if isinstance(mask, str):
+        if mask != "causal":
+            raise ValueError("mask must be None, 'causal' or a boolean tensor")
+        return bi_sdpa(q, k, v, causal=True, scale=scale)
+    return bi_sdpa(q, k, v, causal=False, mask=mask, scale=scale)

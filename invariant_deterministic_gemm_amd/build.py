@@ -1,0 +1,68 @@
+"""Build libbi.so (the C-ABI library of HIP kernels) for gfx950, in-tree.
+
+hipcc cross-compiles for gfx950 without a GPU present.  Flags:
+  * -ffp-contract=off: no implicit a*b+c fusion, so every fused multiply-add
+    in the kernels is an explicit fmaf and all template instantiations round
+    the same way;
+  * -Xclang -target-feature -Xclang -packed-fp32-ops: keep the compiler from
+    emitting packed fp32 VALU instructions.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIB = os.path.join(PKG, "libbi.so")
+SOURCES = ["api.hip", "gemm.hip", "sdpa.hip"]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+
+def hipcc_flags() -> list:
+    return ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-Wall", "-Wno-unused-function",
+            "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+
+
+def build(verbose: bool = False, jobs: int = 4) -> str:
+    objs = []
+    procs = []
+    for src in SOURCES:
+        obj = os.path.join(CSRC, "_" + src.replace(".hip", ".o"))
+        cmd = [HIPCC, *hipcc_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
+        objs.append(obj)
+        if len(procs) >= jobs:
+            _drain(procs, verbose)
+    _drain(procs, verbose)
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", LIB + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(LIB + ".tmp", LIB)
+    for o in objs:
+        os.remove(o)
+    return LIB
+
+
+def _drain(procs, verbose):
+    while procs:
+        src, p = procs.pop(0)
+        out, _ = p.communicate()
+        # the host pass does not know the packed-fp32 feature and says so; that is expected
+        lines = [l for l in out.splitlines() if "packed-fp32-ops" not in l and l.strip()]
+        if p.returncode != 0:
+            sys.stderr.write(out)
+            raise RuntimeError(f"hipcc failed on {src}")
+        if verbose and lines:
+            print("\n".join(lines), flush=True)
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,299 @@
+// libbi host side: argument validation, kernel selection and error reporting
+// behind the C ABI declared in include/bi.h.
+//
+// Selection rules (mlx-batch-invariant README, section "Why MLX is not
+// invariant": the variance there comes entirely from WHICH kernel a shape
+// picks).  Here every configuration a call can pick runs the same
+// per-element arithmetic, so selection may look at M for occupancy without
+// affecting bits; nothing looks at the stream, the device state or the
+// environment.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdint>
+#include <string>
+
+#include "bi.h"
+#include "device.h"
+#include "gemm.h"
+#include "sdpa.h"
+
+namespace {
+
+constexpr int kAbiMajor = 1;
+// Bump when a compile-time constant that shapes arithmetic changes
+// (k-step order, MFMA shapes, KV_SPLIT / KV_BLOCK, combine order).
+constexpr int kBitsVersion = 1;
+
+thread_local std::string g_last_error;
+
+bi_status fail(bi_status s, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+bi_status ok() {
+    g_last_error.clear();
+    return BI_OK;
+}
+
+int esize(bi_dtype d) { return d == BI_F32 ? 4 : 2; }
+
+bool dtype_known(int d) { return d == BI_F32 || d == BI_F16 || d == BI_BF16; }
+
+bool pair_supported(bi_dtype in, bi_dtype out) {
+    if (in == BI_F32) return out == BI_F32;
+    if (in == BI_BF16) return out == BI_BF16 || out == BI_F32;
+    if (in == BI_F16) return out == BI_F16 || out == BI_F32;
+    return false;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned_to(const void *p, int a) { return (reinterpret_cast<uintptr_t>(p) % (uintptr_t)a) == 0; }
+
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+
+bi_status device_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return ok();
+    return fail(BI_ERR_DEVICE, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+// Shared checks of the GEMM family.  `b_kn` selects the (K, N) layout of B.
+bi_status check_gemm(const char *fn, const void *a, int64_t lda, const void *b, int64_t ldb, bool b_kn,
+                     const void *y, int64_t ldy, int64_t M, int64_t N, int64_t K, bi_dtype in_dt,
+                     bi_dtype out_dt) {
+    if (!dtype_known(in_dt) || !dtype_known(out_dt))
+        return fail(BI_ERR_INVALID, "%s: unknown dtype code (in %d, out %d)", fn, (int)in_dt, (int)out_dt);
+    if (!pair_supported(in_dt, out_dt))
+        return fail(BI_ERR_UNSUPPORTED, "%s: dtype pair in=%d out=%d is not supported", fn, (int)in_dt,
+                    (int)out_dt);
+    if (M < 0 || N < 0 || K < 0) return fail(BI_ERR_INVALID, "%s: negative size M=%lld N=%lld K=%lld", fn,
+                                             (long long)M, (long long)N, (long long)K);
+    if (M > kMaxDim || N > kMaxDim || K > kMaxDim)
+        return fail(BI_ERR_UNSUPPORTED, "%s: sizes must be below 2^31", fn);
+    if (M == 0 || N == 0) return ok();
+    if (y == nullptr) return fail(BI_ERR_INVALID, "%s: output pointer is null", fn);
+    if (K > 0 && (a == nullptr || b == nullptr)) return fail(BI_ERR_INVALID, "%s: input pointer is null", fn);
+    if (lda < K) return fail(BI_ERR_INVALID, "%s: lda=%lld < K=%lld", fn, (long long)lda, (long long)K);
+    if (b_kn ? (ldb < N) : (ldb < K))
+        return fail(BI_ERR_INVALID, "%s: ldb=%lld too small", fn, (long long)ldb);
+    if (ldy < N) return fail(BI_ERR_INVALID, "%s: ldy=%lld < N=%lld", fn, (long long)ldy, (long long)N);
+    const int epc = 16 / esize(in_dt);
+    if (K % epc != 0)
+        return fail(BI_ERR_UNSUPPORTED, "%s: K=%lld must be a multiple of %d for this dtype", fn, (long long)K, epc);
+    if (K > 0) {
+        if (!aligned16(a) || !aligned16(b))
+            return fail(BI_ERR_UNSUPPORTED, "%s: input pointers must be 16-byte aligned", fn);
+        if (lda % epc != 0 || ldb % epc != 0)
+            return fail(BI_ERR_UNSUPPORTED, "%s: lda / ldb must be multiples of %d elements", fn, epc);
+        if (b_kn && N % epc != 0)
+            return fail(BI_ERR_UNSUPPORTED, "%s: N=%lld must be a multiple of %d for a (K, N) operand", fn,
+                        (long long)N, epc);
+    }
+    if (!aligned_to(y, esize(out_dt))) return fail(BI_ERR_UNSUPPORTED, "%s: output pointer misaligned", fn);
+    return ok();
+}
+
+bi::GemmParams make_params(const void *a, int64_t lda, const void *b, int64_t ldb, const void *c, int64_t ldc,
+                           void *y, int64_t ldy, int64_t M, int64_t N, int64_t K, float alpha, float beta) {
+    bi::GemmParams p{};
+    p.A = a;
+    p.lda = lda;
+    p.B = b;
+    p.ldb = ldb;
+    p.C = c;
+    p.ldc = ldc;
+    p.Y = y;
+    p.ldy = ldy;
+    p.M = (int)M;
+    p.N = (int)N;
+    p.K = (int)K;
+    p.alpha = alpha;
+    p.beta = beta;
+    p.splits = 1;
+    p.partial = nullptr;
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+bi_status bi_linear(const void *x, int64_t ldx, const void *w, int64_t ldw, const void *bias, void *y,
+                    int64_t ldy, int64_t M, int64_t N, int64_t K, bi_dtype in_dt, bi_dtype out_dt,
+                    void *stream) {
+    bi_status s = check_gemm("bi_linear", x, ldx, w, ldw, false, y, ldy, M, N, K, in_dt, out_dt);
+    if (s != BI_OK || M == 0 || N == 0) return s;
+    if (bias != nullptr && !aligned_to(bias, esize(out_dt)))
+        return fail(BI_ERR_UNSUPPORTED, "bi_linear: bias pointer misaligned");
+    bi::GemmParams p = make_params(x, ldx, w, ldw, bias, 0, y, ldy, M, N, K, 1.0f, 1.0f);
+    return device_status(bi::launch_gemm(p, in_dt, out_dt, false, (hipStream_t)stream), "bi_linear");
+}
+
+bi_status bi_matmul(const void *a, int64_t lda, const void *b, int64_t ldb, void *c, int64_t ldc, int64_t M,
+                    int64_t N, int64_t K, bi_dtype in_dt, bi_dtype out_dt, void *stream) {
+    bi_status s = check_gemm("bi_matmul", a, lda, b, ldb, true, c, ldc, M, N, K, in_dt, out_dt);
+    if (s != BI_OK || M == 0 || N == 0) return s;
+    bi::GemmParams p = make_params(a, lda, b, ldb, nullptr, 0, c, ldc, M, N, K, 1.0f, 0.0f);
+    return device_status(bi::launch_gemm(p, in_dt, out_dt, true, (hipStream_t)stream), "bi_matmul");
+}
+
+bi_status bi_addmm(const void *cin, int64_t ldcin, const void *a, int64_t lda, const void *b, int64_t ldb,
+                   void *out, int64_t ldo, int64_t M, int64_t N, int64_t K, float alpha, float beta,
+                   bi_dtype in_dt, bi_dtype out_dt, void *stream) {
+    bi_status s = check_gemm("bi_addmm", a, lda, b, ldb, true, out, ldo, M, N, K, in_dt, out_dt);
+    if (s != BI_OK || M == 0 || N == 0) return s;
+    if (!std::isfinite(alpha) || !std::isfinite(beta))
+        return fail(BI_ERR_INVALID, "bi_addmm: alpha and beta must be finite");
+    const void *c = nullptr;
+    if (beta != 0.0f) {
+        if (cin == nullptr) return fail(BI_ERR_INVALID, "bi_addmm: cin is null while beta != 0");
+        if (ldcin != 0 && ldcin < N)
+            return fail(BI_ERR_INVALID, "bi_addmm: ldcin=%lld must be 0 or >= N", (long long)ldcin);
+        if (ldcin < 0) return fail(BI_ERR_INVALID, "bi_addmm: negative ldcin");
+        if (!aligned_to(cin, esize(out_dt))) return fail(BI_ERR_UNSUPPORTED, "bi_addmm: cin misaligned");
+        if (cin == out && ldcin != ldo)
+            return fail(BI_ERR_INVALID, "bi_addmm: out may alias cin only with ldo == ldcin");
+        c = cin;
+    }
+    bi::GemmParams p = make_params(a, lda, b, ldb, c, ldcin, out, ldo, M, N, K, alpha, beta);
+    return device_status(bi::launch_gemm(p, in_dt, out_dt, true, (hipStream_t)stream), "bi_addmm");
+}
+
+size_t bi_sdpa_workspace_bytes(int64_t B, int64_t Hq, int64_t Lq, int64_t S, int64_t D) {
+    return bi::sdpa_workspace_bytes(B, Hq, Lq, S, D);
+}
+
+bi_status bi_sdpa(const void *q, const int64_t q_str[4], const void *k, const int64_t k_str[4], const void *v,
+                  const int64_t v_str[4], void *o, const int64_t o_str[4], int64_t B, int64_t Hq, int64_t Hkv,
+                  int64_t Lq, int64_t S, int64_t D, float scale, int causal, const uint8_t *mask,
+                  const int64_t mask_str[4], bi_dtype dt, void *ws, size_t ws_bytes, void *stream) {
+    const char *fn = "bi_sdpa";
+    if (!dtype_known(dt)) return fail(BI_ERR_INVALID, "%s: unknown dtype code %d", fn, (int)dt);
+    if (B < 0 || Hq < 0 || Hkv <= 0 || Lq < 0 || S < 0 || D <= 0)
+        return fail(BI_ERR_INVALID, "%s: bad sizes B=%lld Hq=%lld Hkv=%lld Lq=%lld S=%lld D=%lld", fn,
+                    (long long)B, (long long)Hq, (long long)Hkv, (long long)Lq, (long long)S, (long long)D);
+    if (Hq % Hkv != 0) return fail(BI_ERR_INVALID, "%s: Hq=%lld is not a multiple of Hkv=%lld", fn,
+                                   (long long)Hq, (long long)Hkv);
+    if (causal && Lq > S)
+        return fail(BI_ERR_INVALID, "%s: causal attention needs Lq <= S (Lq=%lld, S=%lld)", fn, (long long)Lq,
+                    (long long)S);
+    if (D != 64 && D != 128)
+        return fail(BI_ERR_UNSUPPORTED, "%s: head dim %lld not supported (64 or 128)", fn, (long long)D);
+    if (!std::isfinite(scale)) return fail(BI_ERR_INVALID, "%s: scale must be finite", fn);
+    if (B == 0 || Hq == 0 || Lq == 0) return ok();
+    if (!q_str || !k_str || !v_str || !o_str) return fail(BI_ERR_INVALID, "%s: stride array is null", fn);
+    if (q == nullptr || o == nullptr || (S > 0 && (k == nullptr || v == nullptr)))
+        return fail(BI_ERR_INVALID, "%s: tensor pointer is null", fn);
+    const int epc = 16 / esize(dt);
+    const int64_t *strs[4] = {q_str, k_str, v_str, o_str};
+    const void *ptrs[4] = {q, k, v, o};
+    const char *names[4] = {"q", "k", "v", "o"};
+    for (int t = 0; t < 4; ++t) {
+        if (strs[t][3] != 1) return fail(BI_ERR_UNSUPPORTED, "%s: %s must be contiguous in its last dim", fn, names[t]);
+        for (int d = 0; d < 3; ++d)
+            if (strs[t][d] < 0 || strs[t][d] % epc != 0)
+                return fail(BI_ERR_UNSUPPORTED, "%s: %s stride[%d]=%lld must be a non-negative multiple of %d",
+                            fn, names[t], d, (long long)strs[t][d], epc);
+        if ((t != 1 && t != 2) || S > 0)
+            if (!aligned16(ptrs[t])) return fail(BI_ERR_UNSUPPORTED, "%s: %s must be 16-byte aligned", fn, names[t]);
+    }
+    const int64_t G = Hq / Hkv;
+    const int64_t R = G * Lq;
+    if ((R + 15) / 16 > 65535 || B * Hkv > 65535 || B * Hq * Lq > kMaxDim || S > kMaxDim - 2 * bi::KV_SPLIT)
+        return fail(BI_ERR_UNSUPPORTED, "%s: problem too large for one launch", fn);
+    if (mask != nullptr) {
+        if (!mask_str) return fail(BI_ERR_INVALID, "%s: mask strides are null", fn);
+        for (int d = 0; d < 4; ++d)
+            if (mask_str[d] < 0) return fail(BI_ERR_INVALID, "%s: negative mask stride", fn);
+    }
+    const size_t need = bi::sdpa_workspace_bytes(B, Hq, Lq, S, D);
+    if (need > 0 && (ws == nullptr || ws_bytes < need))
+        return fail(BI_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                    ws == nullptr ? (size_t)0 : ws_bytes);
+    if (need > 0 && !aligned_to(ws, 256)) return fail(BI_ERR_UNSUPPORTED, "%s: workspace must be 256-byte aligned", fn);
+
+    bi::SdpaParams p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    for (int d = 0; d < 3; ++d) {
+        p.qs[d] = q_str[d];
+        p.ks[d] = k_str[d];
+        p.vs[d] = v_str[d];
+        p.os[d] = o_str[d];
+    }
+    p.mask = mask;
+    for (int d = 0; d < 4; ++d) p.ms[d] = mask ? mask_str[d] : 0;
+    p.B = (int)B;
+    p.Hq = (int)Hq;
+    p.Hkv = (int)Hkv;
+    p.Lq = (int)Lq;
+    p.S = (int)S;
+    p.G = (int)G;
+    p.causal = causal ? 1 : 0;
+    p.c = (float)((double)scale * 1.4426950408889634);   // log2(e), rounded once to fp32
+    if (need > 0) {
+        bi::sdpa_bind_workspace(p, ws, (int)D);
+    } else {
+        p.nsplit = 0;
+    }
+    return device_status(bi::launch_sdpa(p, dt, (int)D, (hipStream_t)stream), fn);
+}
+
+int bi_variant_splits(int64_t M) {
+    if (M <= 16) return 8;
+    if (M <= 64) return 4;
+    if (M <= 128) return 2;
+    return 1;
+}
+
+size_t bi_variant_workspace_bytes(int64_t M, int64_t N, int splits) {
+    if (splits <= 1 || M <= 0 || N <= 0) return 0;
+    return (size_t)splits * (size_t)M * (size_t)N * 4;
+}
+
+bi_status bi_variant_linear(const void *x, int64_t ldx, const void *w, int64_t ldw, const void *bias, void *y,
+                            int64_t ldy, int64_t M, int64_t N, int64_t K, bi_dtype in_dt, bi_dtype out_dt,
+                            int splits, void *ws, size_t ws_bytes, void *stream) {
+    bi_status s = check_gemm("bi_variant_linear", x, ldx, w, ldw, false, y, ldy, M, N, K, in_dt, out_dt);
+    if (s != BI_OK || M == 0 || N == 0) return s;
+    if (splits < 1 || splits > 16) return fail(BI_ERR_INVALID, "bi_variant_linear: splits must be in 1..16");
+    const size_t need = bi_variant_workspace_bytes(M, N, splits);
+    if (need > 0 && (ws == nullptr || ws_bytes < need))
+        return fail(BI_ERR_WORKSPACE, "bi_variant_linear: workspace of %zu bytes needed", need);
+    if (need > 0 && !aligned16(ws)) return fail(BI_ERR_UNSUPPORTED, "bi_variant_linear: workspace misaligned");
+    bi::GemmParams p = make_params(x, ldx, w, ldw, bias, 0, y, ldy, M, N, K, 1.0f, 1.0f);
+    return device_status(bi::launch_gemm_splitk(p, in_dt, out_dt, splits, (float *)ws, (hipStream_t)stream),
+                         "bi_variant_linear");
+}
+
+const char *bi_gemm_kernel_name(int64_t M, int64_t N, int b_kn) {
+    if (M <= 0 || N <= 0 || M > kMaxDim || N > kMaxDim) return "none";
+    return bi::gemm_kernel_name((int)M, (int)N, b_kn != 0);
+}
+
+const char *bi_status_name(bi_status s) {
+    switch (s) {
+        case BI_OK: return "BI_OK";
+        case BI_ERR_INVALID: return "BI_ERR_INVALID";
+        case BI_ERR_UNSUPPORTED: return "BI_ERR_UNSUPPORTED";
+        case BI_ERR_WORKSPACE: return "BI_ERR_WORKSPACE";
+        case BI_ERR_DEVICE: return "BI_ERR_DEVICE";
+    }
+    return "BI_UNKNOWN_STATUS";
+}
+
+const char *bi_last_error(void) { return g_last_error.c_str(); }
+
+int bi_abi_version(void) { return (kAbiMajor << 16) | kBitsVersion; }
+
+}  // extern "C"

@@ -1,0 +1,33 @@
+// Host-visible launch interface of the attention kernels (internal to libbi).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bi {
+
+// Fixed arithmetic constants of the attention recipe.  Changing either
+// changes output bits, so they are part of the bits version.
+constexpr int KV_SPLIT = 256;   // keys per split, at absolute positions [256 s, 256 s + 256)
+constexpr int KV_BLOCK = 64;    // keys per block inside a split
+
+struct SdpaParams {
+    const void *q, *k, *v;
+    void *o;
+    int64_t qs[3], ks[3], vs[3], os[3];   // element strides of dims 0..2 (dim 3 is contiguous)
+    const uint8_t *mask;                  // nullable
+    int64_t ms[4];
+    int B, Hq, Hkv, Lq, S, G;             // G = Hq / Hkv
+    int causal;
+    float c;                              // scale * log2(e), rounded once to fp32
+    int nsplit;                           // ceil(S / KV_SPLIT)
+    float *ws_ml;                         // [rows][nsplit][2]  (m, l)
+    float *ws_o;                          // [rows][nsplit][D]
+};
+
+size_t sdpa_workspace_bytes(int64_t B, int64_t Hq, int64_t Lq, int64_t S, int64_t D);
+// Carves ws into ws_ml / ws_o and sets nsplit.
+void sdpa_bind_workspace(SdpaParams &p, void *ws, int D);
+hipError_t launch_sdpa(const SdpaParams &p, int dt, int D, hipStream_t stream);
+
+}  // namespace bi

@@ -1,0 +1,347 @@
+// Batch-invariant scaled dot-product attention for gfx950.
+//
+// Method (mlx-batch-invariant README, section "How the kernels work",
+// attention paragraph): online softmax in fp32 and a FIXED reduction
+// structure that no query length, batch size or context length can change.
+// The README's section "Why MLX is not invariant" lists what must not move
+// the bits: the query count picking another kernel, the split-KV count
+// depending on the GQA factor times the query count, and a one-pass /
+// two-pass switch as the KV cache grows.
+//
+// CDNA4 realisation.  One kernel body serves decode and prefill:
+//   * keys are cut at ABSOLUTE positions into splits of KV_SPLIT = 256 keys
+//     and each split into blocks of KV_BLOCK = 64 keys;
+//   * one wavefront handles a tile of 16 query rows (the G query heads that
+//     share a KV head times consecutive query positions, packed row =
+//     query_index * G + head_in_group) against one split, so K and V are
+//     read once per KV head;
+//   * per block, in ascending order, and per row:
+//        S^T = K . Q^T on the MFMA (contracting over d in fixed chunks),
+//        s  = fp32(S * c) with c = scale * log2(e) computed once on the host,
+//        invisible keys (causal, mask, or past S) -> s = -inf,
+//        m_blk = max s;  a block with m_blk = -inf leaves (m, l, O) untouched,
+//        m' = max(m, m_blk), alpha = exp2(m - m'), p = exp2(s - m'),
+//        l = fmaf(l, alpha, sum p)  (sum in a fixed lane / register order),
+//        O = O * alpha, then O += P . V on the MFMA (P rounded to the input
+//        dtype for bf16 / fp16, kept fp32 for fp32);
+//   * split partials (m, l, O) go to a workspace, and a second kernel folds
+//     them left to right in ascending split order, divides by l, turns -0
+//     into +0 and rounds once.
+// A row's result therefore depends only on its own query, the keys it may
+// see, and the fixed split / block boundaries: a token decoded alone (keys
+// after it absent) and the same token inside a prefill chunk (keys after it
+// masked) run the same operations on the same operands, and appending masked
+// keys to the cache only appends identity steps.
+
+#include "device.h"
+#include "sdpa.h"
+
+namespace bi {
+
+template <int dt, int D> struct AttnShape {
+    static constexpr int EB = Elem<dt>::bytes;
+    static constexpr int EPC = 16 / EB;
+    static constexpr int NCH = D * EB / 64;          // 16-byte chunks of d per lane (contraction over d)
+    static constexpr int ND = D / 16;                // 16-wide d tiles of the output
+    static constexpr int VROW = D * EB + (EB == 2 ? 8 : 16);   // padded LDS row of V (bytes)
+    static constexpr int VCH = D * EB / 16;          // 16-byte chunks per V row
+    // element offset of this lane group's chunk c of a row, for the q.k contraction
+    static __device__ __forceinline__ int d_of(int c, int g) {
+        if constexpr (EB == 2) return 32 * c + 8 * g;     // one MFMA per chunk: k slots 8g..8g+7
+        else return g * (D / 4) + 4 * c;                  // four MFMAs per chunk, one d each
+    }
+};
+
+template <int dt>
+__device__ __forceinline__ f32x4 attn_mfma_chunk(u32x4 a, u32x4 b, f32x4 c) {
+    if constexpr (dt == DT_F32) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            c = Mfma<DT_F32>::step(__uint_as_float(a[u]), __uint_as_float(b[u]), c);
+        return c;
+    } else {
+        return Mfma<dt>::step(a, b, c);
+    }
+}
+
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int dt, int D>
+__global__ __launch_bounds__(64) void sdpa_split(SdpaParams p) {
+    using A = AttnShape<dt, D>;
+    constexpr float NEG_INF = -__builtin_huge_valf();
+    __shared__ __attribute__((aligned(16))) char vs[KV_BLOCK * A::VROW];
+
+    const int lane = threadIdx.x;
+    const int r16 = lane & 15;
+    const int g = lane >> 4;
+    const int sp = blockIdx.x;
+    const int tile = blockIdx.y;
+    const int b = blockIdx.z / p.Hkv;
+    const int gk = blockIdx.z % p.Hkv;
+    const int R = p.G * p.Lq;
+
+    // the score row this lane carries (column r16 of S^T)
+    const int rg = tile * 16 + r16;
+    const bool row_ok = rg < R;
+    const int rgc = min(rg, R - 1);
+    const int iq = rgc / p.G;
+    const int h = gk * p.G + rgc % p.G;
+    const int pos = p.S - p.Lq + iq;
+
+    const int kbeg = sp * KV_SPLIT;
+    const int kend = min(kbeg + KV_SPLIT, p.S);
+    int nblk = (kend - kbeg + KV_BLOCK - 1) / KV_BLOCK;
+    if (p.causal) {
+        // rows are ordered by query index, so the tile's last row sees the most keys
+        const int rlast = min(tile * 16 + 15, R - 1);
+        const int pos_last = p.S - p.Lq + rlast / p.G;
+        nblk = pos_last < kbeg ? 0 : min(nblk, (pos_last - kbeg) / KV_BLOCK + 1);
+    }
+
+    const char *qrow = static_cast<const char *>(p.q) +
+                       ((int64_t)b * p.qs[0] + (int64_t)h * p.qs[1] + (int64_t)iq * p.qs[2]) * A::EB;
+    const char *kbase = static_cast<const char *>(p.k) + ((int64_t)b * p.ks[0] + (int64_t)gk * p.ks[1]) * A::EB;
+    const char *vbase = static_cast<const char *>(p.v) + ((int64_t)b * p.vs[0] + (int64_t)gk * p.vs[1]) * A::EB;
+    const uint8_t *mrow = p.mask ? p.mask + (int64_t)b * p.ms[0] + (int64_t)h * p.ms[1] + (int64_t)iq * p.ms[2]
+                                 : nullptr;
+
+    u32x4 qf[A::NCH];
+#pragma unroll
+    for (int c = 0; c < A::NCH; ++c) qf[c] = ldg16(qrow + A::d_of(c, g) * A::EB);
+
+    float m_run = NEG_INF, l_run = 0.0f;
+    f32x4 o[A::ND];
+#pragma unroll
+    for (int t = 0; t < A::ND; ++t) o[t] = zero4();
+
+    for (int blk = 0; blk < nblk; ++blk) {
+        const int kb = kbeg + blk * KV_BLOCK;
+        // ---- K fragments straight from HBM (A operand of S^T = K Q^T)
+        u32x4 kf[4][A::NCH];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+            const int key = kb + 16 * kt + r16;
+            const char *krow = kbase + (int64_t)key * p.ks[2] * A::EB;
+#pragma unroll
+            for (int c = 0; c < A::NCH; ++c)
+                kf[kt][c] = key < p.S ? ldg16(krow + A::d_of(c, g) * A::EB) : zero_u4();
+        }
+        // ---- V block -> LDS, row-major with padded rows; absent keys are zero
+        u32x4 vr[KV_BLOCK * A::VCH / 64];
+#pragma unroll
+        for (int i = 0; i < KV_BLOCK * A::VCH / 64; ++i) {
+            const int id = lane + 64 * i;
+            const int key = id / A::VCH, c = id % A::VCH;
+            vr[i] = (kb + key < p.S) ? ldg16(vbase + ((int64_t)(kb + key) * p.vs[2] + c * A::EPC) * A::EB)
+                                     : zero_u4();
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < KV_BLOCK * A::VCH / 64; ++i) {
+            const int id = lane + 64 * i;
+            const int key = id / A::VCH, c = id % A::VCH;
+            char *dst = vs + key * A::VROW + c * 16;
+            if constexpr (A::EB == 2) {
+                reinterpret_cast<u32x2 *>(dst)[0] = u32x2{vr[i][0], vr[i][1]};
+                reinterpret_cast<u32x2 *>(dst)[1] = u32x2{vr[i][2], vr[i][3]};
+            } else {
+                *reinterpret_cast<u32x4 *>(dst) = vr[i];
+            }
+        }
+        // ---- scores: lane holds S^T[key 16 kt + 4 g + i][row r16]
+        f32x4 st[4];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+            st[kt] = zero4();
+#pragma unroll
+            for (int c = 0; c < A::NCH; ++c) st[kt] = attn_mfma_chunk<dt>(kf[kt][c], qf[c], st[kt]);
+        }
+        float s[4][4];
+        float mb = NEG_INF;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int key = kb + 16 * kt + 4 * g + i;
+                bool ok = row_ok && key < p.S;
+                if (p.causal) ok = ok && key <= pos;
+                if (mrow) ok = ok && mrow[(int64_t)key * p.ms[3]] != 0;
+                const float sv = st[kt][i] * p.c;
+                s[kt][i] = ok ? sv : NEG_INF;
+                mb = fmaxf(mb, s[kt][i]);
+            }
+        mb = fmaxf(mb, __shfl_xor(mb, 16));
+        mb = fmaxf(mb, __shfl_xor(mb, 32));
+        const bool empty = mb == NEG_INF;
+        const float m_new = empty ? m_run : fmaxf(m_run, mb);
+        const float alpha = empty ? 1.0f : exp2_hw(m_run - m_new);
+        float pr[4][4];
+        float rs = 0.0f;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                pr[kt][i] = s[kt][i] == NEG_INF ? 0.0f : exp2_hw(s[kt][i] - m_new);
+                rs = rs + pr[kt][i];
+            }
+        rs = rs + __shfl_xor(rs, 16);
+        rs = rs + __shfl_xor(rs, 32);
+        l_run = __builtin_fmaf(l_run, alpha, rs);
+        m_run = m_new;
+        // ---- rescale O: lane holds O rows 4 g + i
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float ai = __shfl(alpha, 4 * g + i);
+#pragma unroll
+            for (int t = 0; t < A::ND; ++t) o[t][i] = o[t][i] * ai;
+        }
+        __syncthreads();   // V block visible in LDS
+        // ---- O += P . V
+        if constexpr (A::EB == 2) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                // k slot 8 g + j <-> key 32 c + 4 g + j (j < 4), 32 c + 16 + 4 g + (j - 4) (j >= 4)
+                const u32x4 pf = u32x4{pack2<dt>(pr[2 * c][0], pr[2 * c][1]), pack2<dt>(pr[2 * c][2], pr[2 * c][3]),
+                                       pack2<dt>(pr[2 * c + 1][0], pr[2 * c + 1][1]),
+                                       pack2<dt>(pr[2 * c + 1][2], pr[2 * c + 1][3])};
+                const int key0 = 32 * c + 4 * g;
+#pragma unroll
+                for (int t = 0; t < A::ND; ++t) {
+                    const char *col = vs + (16 * t + r16) * 2;
+                    uint32_t w[4];
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const int ka = key0 + (jj < 2 ? 2 * jj : 16 + 2 * (jj - 2));
+                        const uint32_t lo = *reinterpret_cast<const uint16_t *>(col + ka * A::VROW);
+                        const uint32_t hi = *reinterpret_cast<const uint16_t *>(col + (ka + 1) * A::VROW);
+                        w[jj] = lo | (hi << 16);
+                    }
+                    o[t] = Mfma<dt>::step(pf, u32x4{w[0], w[1], w[2], w[3]}, o[t]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int key = 16 * kt + 4 * g + i;
+#pragma unroll
+                    for (int t = 0; t < A::ND; ++t) {
+                        const float vv = *reinterpret_cast<const float *>(vs + key * A::VROW + (16 * t + r16) * 4);
+                        o[t] = Mfma<DT_F32>::step(pr[kt][i], vv, o[t]);
+                    }
+                }
+        }
+        __syncthreads();   // everyone done with this V block
+    }
+
+    // ---- partials
+    if (g == 0 && row_ok) {
+        const int64_t rowid = ((int64_t)b * p.Hq + h) * p.Lq + iq;
+        float *ml = p.ws_ml + (rowid * p.nsplit + sp) * 2;
+        ml[0] = m_run;
+        ml[1] = l_run;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int ro = tile * 16 + 4 * g + i;
+        if (ro < R) {
+            const int iq_o = ro / p.G;
+            const int h_o = gk * p.G + ro % p.G;
+            const int64_t rowid = ((int64_t)b * p.Hq + h_o) * p.Lq + iq_o;
+            float *dst = p.ws_o + (rowid * p.nsplit + sp) * D;
+#pragma unroll
+            for (int t = 0; t < A::ND; ++t) dst[16 * t + r16] = o[t][i];
+        }
+    }
+}
+
+// Fold the split partials of one query row left to right, normalise, round.
+template <int dt, int D>
+__global__ __launch_bounds__(64) void sdpa_combine(SdpaParams p) {
+    constexpr float NEG_INF = -__builtin_huge_valf();
+    constexpr int PER = D / 64;
+    const int64_t rowid = blockIdx.x;
+    const int iq = (int)(rowid % p.Lq);
+    const int h = (int)((rowid / p.Lq) % p.Hq);
+    const int b = (int)(rowid / ((int64_t)p.Lq * p.Hq));
+    const float *ml = p.ws_ml + rowid * p.nsplit * 2;
+    const float *po = p.ws_o + rowid * p.nsplit * D;
+
+    bool have = false;
+    float m = 0.0f, l = 0.0f;
+    float o[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) o[j] = 0.0f;
+    for (int sp = 0; sp < p.nsplit; ++sp) {
+        const float ms = ml[2 * sp], ls = ml[2 * sp + 1];
+        if (ms == NEG_INF) continue;              // split saw no key of this row
+        if (!have) {
+            m = ms;
+            l = ls;
+#pragma unroll
+            for (int j = 0; j < PER; ++j) o[j] = po[sp * D + threadIdx.x + 64 * j];
+            have = true;
+            continue;
+        }
+        const float m2 = fmaxf(m, ms);
+        const float a = exp2_hw(m - m2);
+        const float bs = exp2_hw(ms - m2);
+        l = __builtin_fmaf(l, a, ls * bs);
+#pragma unroll
+        for (int j = 0; j < PER; ++j) o[j] = __builtin_fmaf(o[j], a, po[sp * D + threadIdx.x + 64 * j] * bs);
+        m = m2;
+    }
+    char *orow = static_cast<char *>(p.o) +
+                 ((int64_t)b * p.os[0] + (int64_t)h * p.os[1] + (int64_t)iq * p.os[2]) * Elem<dt>::bytes;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        float r = have ? o[j] / l : 0.0f;
+        r = r + 0.0f;                              // -0 -> +0
+        store_from_f32<dt>(orow, threadIdx.x + 64 * j, r);
+    }
+}
+
+size_t sdpa_workspace_bytes(int64_t B, int64_t Hq, int64_t Lq, int64_t S, int64_t D) {
+    if (B <= 0 || Hq <= 0 || Lq <= 0 || S <= 0 || D <= 0) return 0;
+    const int64_t rows = B * Hq * Lq;
+    const int64_t nsplit = (S + KV_SPLIT - 1) / KV_SPLIT;
+    const int64_t ml = (rows * nsplit * 2 * 4 + 255) / 256 * 256;
+    return (size_t)(ml + rows * nsplit * D * 4);
+}
+
+void sdpa_bind_workspace(SdpaParams &p, void *ws, int D) {
+    const int64_t rows = (int64_t)p.B * p.Hq * p.Lq;
+    p.nsplit = (p.S + KV_SPLIT - 1) / KV_SPLIT;
+    const int64_t ml = (rows * p.nsplit * 2 * 4 + 255) / 256 * 256;
+    p.ws_ml = static_cast<float *>(ws);
+    p.ws_o = reinterpret_cast<float *>(static_cast<char *>(ws) + ml);
+    (void)D;
+}
+
+template <int dt, int D>
+static hipError_t launch_typed(const SdpaParams &p, hipStream_t st) {
+    const int R = p.G * p.Lq;
+    if (p.nsplit > 0) {
+        const dim3 g1((unsigned)p.nsplit, (unsigned)((R + 15) / 16), (unsigned)(p.B * p.Hkv));
+        hipLaunchKernelGGL((sdpa_split<dt, D>), g1, dim3(64), 0, st, p);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const dim3 g2((unsigned)((int64_t)p.B * p.Hq * p.Lq));
+    hipLaunchKernelGGL((sdpa_combine<dt, D>), g2, dim3(64), 0, st, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_sdpa(const SdpaParams &p, int dt, int D, hipStream_t st) {
+    if (dt == DT_BF16 && D == 128) return launch_typed<DT_BF16, 128>(p, st);
+    if (dt == DT_BF16 && D == 64) return launch_typed<DT_BF16, 64>(p, st);
+    if (dt == DT_F16 && D == 128) return launch_typed<DT_F16, 128>(p, st);
+    if (dt == DT_F16 && D == 64) return launch_typed<DT_F16, 64>(p, st);
+    if (dt == DT_F32 && D == 128) return launch_typed<DT_F32, 128>(p, st);
+    if (dt == DT_F32 && D == 64) return launch_typed<DT_F32, 64>(p, st);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace bi

@@ -1,0 +1,160 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/bi.h declares, and rejects malformed or unsupported arguments on the
+host before touching the device (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from invariant_deterministic_gemm_amd import _native
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bi.h")
+
+F32, F16, BF16 = _native.BI_F32, _native.BI_F16, _native.BI_BF16
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+
+# Fake, never-dereferenced device addresses: validation must reject the call
+# before any of them is used.
+P16 = ctypes.c_void_p(0x7f0000000000)
+P16b = ctypes.c_void_p(0x7f0000100000)
+P_MIS = ctypes.c_void_p(0x7f0000000002)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _native.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bi_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_what_the_binding_binds():
+    assert declared_functions() == sorted(_native.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_exported_symbols_with_nm():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", _native.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (bi_\w+)", out))
+    assert set(declared_functions()) <= exported
+
+
+def test_abi_version_and_status_names(lib):
+    v = lib.bi_abi_version()
+    assert v >> 16 == 1 and (v & 0xffff) >= 1
+    names = [lib.bi_status_name(s).decode() for s in range(5)]
+    assert names == ["BI_OK", "BI_ERR_INVALID", "BI_ERR_UNSUPPORTED", "BI_ERR_WORKSPACE", "BI_ERR_DEVICE"]
+    assert lib.bi_status_name(99).decode() == "BI_UNKNOWN_STATUS"
+
+
+def linear(lib, M=4, N=32, K=64, ind=BF16, outd=BF16, x=P16, w=P16b, ldx=None, ldw=None, ldy=None, bias=None):
+    return lib.bi_linear(x, K if ldx is None else ldx, w, K if ldw is None else ldw, bias, P16,
+                         N if ldy is None else ldy, M, N, K, ind, outd, None)
+
+
+def test_gemm_validation(lib):
+    assert linear(lib, ind=F32, outd=BF16) == UNSUPPORTED
+    assert linear(lib, ind=BF16, outd=F16) == UNSUPPORTED
+    assert "not supported" in lib.bi_last_error().decode()
+    assert linear(lib, ind=7) == INVALID
+    assert linear(lib, M=-1) == INVALID
+    assert linear(lib, K=60) == UNSUPPORTED          # K % 8 for 16-bit inputs
+    assert linear(lib, x=P_MIS) == UNSUPPORTED
+    assert linear(lib, ldx=63) == INVALID
+    assert linear(lib, ldx=68) == UNSUPPORTED        # row pitch not a multiple of 16 bytes
+    assert linear(lib, ldy=16) == INVALID
+    assert linear(lib, x=None) == INVALID
+    # empty problems succeed without doing anything
+    assert linear(lib, M=0) == OK
+    assert linear(lib, N=0) == OK
+    assert lib.bi_last_error().decode() == ""
+
+
+def test_matmul_addmm_validation(lib):
+    # (K, N) operand: N must be a multiple of 8 for 16-bit inputs
+    assert lib.bi_matmul(P16, 64, P16b, 36, P16, 36, 4, 36, 64, BF16, BF16, None) == UNSUPPORTED
+    assert lib.bi_matmul(P16, 64, P16b, 16, P16, 32, 4, 32, 64, BF16, BF16, None) == INVALID  # ldb < N
+    # beta != 0 needs cin; ldcin must be 0 or >= N
+    assert lib.bi_addmm(None, 0, P16, 64, P16b, 32, P16, 32, 4, 32, 64, 1.0, 1.0, BF16, BF16, None) == INVALID
+    assert lib.bi_addmm(P16, 8, P16, 64, P16b, 32, P16, 32, 4, 32, 64, 1.0, 1.0, BF16, BF16, None) == INVALID
+    assert lib.bi_addmm(P16, 0, P16, 64, P16b, 32, P16, 32, 4, 32, 64, float("nan"), 1.0, BF16, BF16,
+                        None) == INVALID
+    assert lib.bi_addmm(None, 0, P16, 64, P16b, 32, P16, 32, 0, 32, 64, 1.0, 1.0, BF16, BF16, None) == OK
+
+
+def strides(shape):
+    s = [1] * 4
+    for d in (2, 1, 0):
+        s[d] = s[d + 1] * shape[d + 1]
+    return _native.i64x4(s)
+
+
+def sdpa(lib, B=1, Hq=4, Hkv=2, Lq=1, S=16, D=128, dt=BF16, causal=1, ws=P16, wsb=1 << 30, qstr=None,
+         scale=0.088):
+    qs = qstr or strides((B, Hq, Lq, D))
+    kv = strides((B, Hkv, S, D))
+    return lib.bi_sdpa(P16, qs, P16b, kv, P16b, kv, P16, strides((B, Hq, Lq, D)), B, Hq, Hkv, Lq, S, D,
+                       scale, causal, None, None, dt, ws, wsb, None)
+
+
+def test_sdpa_validation(lib):
+    assert sdpa(lib, Hq=6, Hkv=4) == INVALID
+    assert sdpa(lib, Hkv=0) == INVALID
+    assert sdpa(lib, D=96) == UNSUPPORTED               # head dims 64 and 128 only
+    assert sdpa(lib, D=32) == UNSUPPORTED
+    assert sdpa(lib, Lq=17, S=16, causal=1) == INVALID  # causal needs Lq <= S
+    assert sdpa(lib, dt=9) == INVALID
+    assert sdpa(lib, scale=float("inf")) == INVALID
+    assert sdpa(lib, ws=None) == WORKSPACE
+    need = lib.bi_sdpa_workspace_bytes(1, 4, 1, 16, 128)
+    assert need > 0
+    assert sdpa(lib, wsb=need - 4) == WORKSPACE
+    assert sdpa(lib, ws=ctypes.c_void_p(0x7f0000000010)) == UNSUPPORTED   # workspace 256-byte aligned
+    bad = strides((1, 4, 1, 128))
+    bad[3] = 2
+    assert sdpa(lib, qstr=bad) == UNSUPPORTED
+    bad = strides((1, 4, 1, 128))
+    bad[2] = 100                                          # not a multiple of 8 elements
+    assert sdpa(lib, qstr=bad) == UNSUPPORTED
+    assert sdpa(lib, B=0) == OK
+    assert sdpa(lib, Lq=0) == OK
+
+
+def test_sdpa_workspace_formula(lib):
+    # (rows * nsplit * 2 floats, padded to 256 B) + rows * nsplit * D floats
+    rows, nsplit, D = 2 * 32 * 3, (1000 + 255) // 256, 128
+    ml = (rows * nsplit * 8 + 255) // 256 * 256
+    assert lib.bi_sdpa_workspace_bytes(2, 32, 3, 1000, D) == ml + rows * nsplit * D * 4
+    assert lib.bi_sdpa_workspace_bytes(1, 1, 1, 0, 128) == 0
+
+
+def test_variant_policy_and_validation(lib):
+    assert [lib.bi_variant_splits(m) for m in (1, 16, 17, 64, 65, 128, 129, 4096)] == [8, 8, 4, 4, 2, 2, 1, 1]
+    assert lib.bi_variant_workspace_bytes(4, 32, 8) == 8 * 4 * 32 * 4
+    assert lib.bi_variant_workspace_bytes(4, 32, 1) == 0
+    assert lib.bi_variant_linear(P16, 64, P16b, 64, None, P16, 32, 4, 32, 64, BF16, BF16, 0, None, 0,
+                                 None) == INVALID
+    assert lib.bi_variant_linear(P16, 64, P16b, 64, None, P16, 32, 4, 32, 64, BF16, BF16, 4, None, 0,
+                                 None) == WORKSPACE
+
+
+def test_python_binding_rejects_cpu_tensors_and_dtypes():
+    import torch
+    import invariant_deterministic_gemm_amd as bi
+    x = torch.zeros(2, 8)
+    with pytest.raises(ValueError):
+        bi.bi_linear(x, x)
+    with pytest.raises(ValueError):
+        bi.scaled_dot_product_attention(torch.zeros(1, 1, 1, 64), torch.zeros(1, 1, 1, 64),
+                                        torch.zeros(1, 1, 1, 64), mask="sliding")

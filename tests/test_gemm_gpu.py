@@ -1,0 +1,246 @@
+"""GPU tests of the invariant GEMM entry points (bi_linear, bi_matmul, bi_addmm).
+
+* exact pins: integer-valued inputs make every summation order exact, so the
+  GPU must equal the oracle rounded once to the output dtype, bit for bit;
+* oracle tolerance on the seeded workloads (fp32: 1e-5, bf16/fp16: 2e-2);
+* invariance on raw bit patterns across batch size (every M of each sweep
+  and every tile-switch boundary), batch neighbours (other rows redrawn or
+  NaN), repeated calls, call form (linear / addmm / matmul) and HIP-graph
+  replay;
+* the negative control: the split-K comparator must NOT be invariant.
+"""
+import numpy as np
+import pytest
+import torch
+
+import invariant_deterministic_gemm_amd as bi
+import oracle
+import synthetic
+from helpers import assert_bits_equal, assert_close_to_oracle, n_bit_diff, round_ref
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+PAIRS = [(torch.float32, torch.float32), (torch.bfloat16, torch.bfloat16), (torch.float16, torch.float16),
+         (torch.bfloat16, torch.float32), (torch.float16, torch.float32)]
+# M values that cross every kernel switch: skinny row-fragment counts (16/32/48/64),
+# skinny -> tiled (64/65) and the 64x64 / 128x128 tile choice.
+M_EDGES = [1, 2, 15, 16, 17, 31, 32, 33, 47, 48, 49, 63, 64, 65, 127, 128, 129, 255, 256, 257]
+
+
+def ints(shape, seed, dt, lo=-3, hi=3):
+    return synthetic.randint(shape, seed, lo, hi, dt)
+
+
+@pytest.mark.parametrize("ind,outd", PAIRS, ids=lambda d: str(d).split(".")[-1])
+def test_integer_inputs_are_exact_for_every_layout(ind, outd):
+    K = 136 if ind != torch.float32 else 132        # ragged last k step
+    N = 72
+    M = 300
+    x = ints((M, K), 11, ind)
+    w = ints((N, K), 12, ind)
+    b = ints((N,), 13, outd, -5, 5)
+    C = ints((M, N), 14, outd, -5, 5)
+    ref_lin = oracle.linear(x, w, b)
+    ref_mm = oracle.matmul(x, w.t().contiguous())
+    ref_add = oracle.addmm(C, x, w.t().contiguous(), 2.0, -1.0)
+    xg, wg, bg, Cg = (t.to(DEV) for t in (x, w, b, C))
+    wt = wg.t().contiguous()
+    for m in (1, 5, 16, 17, 64, 65, 200, 300):
+        assert_bits_equal(bi.bi_linear(xg[:m], wg, bg, out_dtype=outd).cpu(), round_ref(ref_lin[:m], outd),
+                          f"linear M={m}")
+        assert_bits_equal(bi.bi_matmul(xg[:m], wt, out_dtype=outd).cpu(), round_ref(ref_mm[:m], outd),
+                          f"matmul M={m}")
+        assert_bits_equal(bi.bi_addmm(Cg[:m], xg[:m], wt, 2.0, -1.0, out_dtype=outd).cpu(),
+                          round_ref(ref_add[:m], outd), f"addmm M={m}")
+
+
+def test_identity_permutation_and_onehot_weights():
+    K = 64
+    x = ints((40, K), 21, torch.bfloat16, -100, 100)
+    eye = torch.eye(K, dtype=torch.bfloat16)
+    perm = torch.randperm(K, generator=torch.Generator().manual_seed(22))
+    y = bi.bi_linear(x.to(DEV), eye.to(DEV)).cpu()
+    assert_bits_equal(y, x, "identity weight")
+    y = bi.bi_linear(x.to(DEV), eye[perm].contiguous().to(DEV)).cpu()
+    assert_bits_equal(y, x[:, perm], "permutation weight")
+    w = synthetic.randn((24, K), 23, 1.0, torch.float32)
+    onehot = torch.zeros(3, K)
+    onehot[0, 5] = 1
+    onehot[1, 0] = 1
+    onehot[2, K - 1] = 1
+    y = bi.bi_linear(onehot.to(DEV), w.to(DEV)).cpu()
+    assert_bits_equal(y, w[:, [5, 0, K - 1]].t().contiguous(), "one-hot rows select columns of W")
+
+
+def test_config1_fp32_linear_invariant_and_accurate():
+    d = synthetic.cfg1_inputs()
+    x, w, b = (t.to(DEV) for t in (d["x"], d["w"], d["b"]))
+    ref = oracle.linear(d["x"], d["w"], d["b"])
+    full = bi.bi_linear(x, w, b)
+    assert_close_to_oracle(full.cpu(), ref, "config 1 fp32")
+    for m in range(1, 9):
+        y = bi.bi_linear(x[:m], w, b)
+        assert_bits_equal(y, full[:m], f"config 1, M={m}")
+        assert_close_to_oracle(y.cpu(), ref[:m], f"config 1, M={m}")
+    for r in range(8):
+        assert_bits_equal(bi.bi_linear(x[r:r + 1], w, b), full[r:r + 1], f"config 1 single row {r}")
+
+
+@pytest.mark.parametrize("N", [4096, 14336])
+def test_config2_bf16_linear_addmm_sweep(N):
+    d = synthetic.cfg2_inputs(N, M_max=257)
+    x, w, b, c = (d[k].to(DEV) for k in ("x", "w", "b", "c"))
+    wt = w.t().contiguous()
+    full = bi.bi_linear(x, w, b)
+    full_add = bi.bi_addmm(b, x, wt, 1.0, 1.0)
+    assert_bits_equal(full_add, full, "addmm(b row, x, W^T) == linear(x, W, b)")
+    full_c = bi.bi_addmm(c, x, wt, 1.0, 1.0)
+    for m in sorted(set(synthetic.CFG2["M_values"] + M_EDGES)):
+        assert_bits_equal(bi.bi_linear(x[:m], w, b), full[:m], f"linear N={N} M={m}")
+        assert_bits_equal(bi.bi_addmm(b, x[:m], wt, 1.0, 1.0), full[:m], f"addmm N={N} M={m}")
+        assert_bits_equal(bi.bi_addmm(c[:m], x[:m], wt, 1.0, 1.0), full_c[:m], f"addmm full C N={N} M={m}")
+    # single-row calls
+    for r in (0, 1, 17, 100, 255):
+        assert_bits_equal(bi.bi_linear(x[r:r + 1], w, b), full[r:r + 1], f"row {r} alone")
+    # oracle on a row subset (full N)
+    rows = [0, 3, 16, 64, 129, 256] if N == 4096 else [0, 33, 200]
+    ref = oracle.linear(d["x"][rows], d["w"], d["b"])
+    assert_close_to_oracle(full[rows].cpu(), ref, f"config 2 N={N}")
+    refc = oracle.addmm(d["c"][rows], d["x"][rows], d["w"].t().contiguous(), 1.0, 1.0)
+    assert_close_to_oracle(full_c[rows].cpu(), refc, f"config 2 addmm full C N={N}")
+
+
+def test_neighbour_rows_cannot_move_a_row():
+    d = synthetic.cfg2_inputs(4096, M_max=64)
+    x, w, b = (d[k].to(DEV) for k in ("x", "w", "b"))
+    base = bi.bi_linear(x, w, b)
+    other = synthetic.randn((64, 4096), 999, 1.0, torch.bfloat16).to(DEV)
+    for r in (0, 5, 31, 63):
+        for fill in ("redraw", "nan", "inf", "zero"):
+            x2 = other.clone() if fill == "redraw" else torch.full_like(x, {"nan": float("nan"),
+                                                                             "inf": float("inf"),
+                                                                             "zero": 0.0}[fill])
+            x2[r] = x[r]
+            for m in (r + 1, 64):
+                y = bi.bi_linear(x2[:m], w, b)
+                assert_bits_equal(y[r], base[r], f"row {r}, neighbours {fill}, M={m}")
+    # large M through the tiled kernel
+    d = synthetic.cfg2_inputs(4096, M_max=512)
+    x, w = d["x"].to(DEV), d["w"].to(DEV)
+    base = bi.bi_linear(x, w)
+    x2 = torch.full_like(x, float("nan"))
+    x2[300] = x[300]
+    assert_bits_equal(bi.bi_linear(x2, w)[300], base[300], "row 300 among NaN rows, M=512")
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16])
+def test_config5_logits_rows_match_their_m1_call(dt):
+    d = synthetic.cfg5_inputs(dt)
+    h, w = d["h"].to(DEV), d["w"].to(DEV)
+    singles = torch.stack([bi.bi_linear(h[r:r + 1], w)[0] for r in range(64)])
+    singles32 = torch.stack([bi.bi_linear(h[r:r + 1], w, out_dtype=torch.float32)[0] for r in (0, 63)])
+    for m in range(1, 65):
+        y = bi.bi_linear(h[:m], w)
+        assert_bits_equal(y, singles[:m], f"logits {dt} M={m}")
+    y32 = bi.bi_linear(h, w, out_dtype=torch.float32)
+    assert_bits_equal(y32[[0, 63]], singles32, "fp32-output logits")
+    ref = oracle.linear(d["h"][[0, 31, 63]], d["w"])
+    assert_close_to_oracle(singles[[0, 31, 63]].cpu(), ref, f"logits {dt}")
+
+
+def test_bias_is_rounded_once():
+    d = synthetic.cfg2_inputs(4096, M_max=8)
+    x, w, b = (d[k].to(DEV) for k in ("x", "w", "b"))
+    y = bi.bi_linear(x, w, b)
+    y_twice = (bi.bi_linear(x, w).float() + b.float()).to(torch.bfloat16)   # round, add, round again
+    assert n_bit_diff(y, y_twice) > 0, "one rounding must differ from rounding twice somewhere"
+    ref = oracle.linear(d["x"], d["w"], d["b"])
+    e1 = np.abs(y.cpu().double().numpy() - ref).max()
+    e2 = np.abs(y_twice.cpu().double().numpy() - ref).max()
+    assert e1 <= e2
+
+
+def test_beta_zero_ignores_nan_c():
+    d = synthetic.cfg2_inputs(4096, M_max=4)
+    x, w = d["x"].to(DEV), d["w"].to(DEV)
+    cnan = torch.full((4, 4096), float("nan"), dtype=torch.bfloat16, device=DEV)
+    y = bi.bi_addmm(cnan, x, w.t().contiguous(), 1.0, 0.0)
+    assert torch.isfinite(y).all()
+    assert_bits_equal(y, bi.bi_matmul(x, w.t().contiguous()), "beta = 0 equals matmul")
+
+
+def test_ragged_and_empty_shapes():
+    x = synthetic.randn((37, 104), 31, 1.0, torch.bfloat16)
+    w = synthetic.randn((45, 104), 32, 1.0, torch.bfloat16)
+    b = synthetic.randn((45,), 33, 1.0, torch.bfloat16)
+    y = bi.bi_linear(x.to(DEV), w.to(DEV), b.to(DEV))
+    assert_close_to_oracle(y.cpu(), oracle.linear(x, w, b), "ragged 37x45x104")
+    assert bi.bi_linear(x[:0].to(DEV), w.to(DEV)).shape == (0, 45)
+    assert bi.bi_linear(x.to(DEV), w[:0].to(DEV)).shape == (37, 0)
+    y0 = bi.bi_linear(x[:, :0].contiguous().to(DEV), w[:, :0].contiguous().to(DEV), b.to(DEV))
+    assert_bits_equal(y0.cpu(), b.expand(37, 45).contiguous(), "K = 0 leaves only the bias")
+    # leading batch dims are flattened into M
+    x3 = synthetic.randn((2, 3, 104), 34, 1.0, torch.bfloat16).to(DEV)
+    y3 = bi.bi_linear(x3, w.to(DEV))
+    assert y3.shape == (2, 3, 45)
+    assert_bits_equal(y3.reshape(6, 45), bi.bi_linear(x3.reshape(6, 104), w.to(DEV)), "3-D input")
+
+
+def test_strided_inputs():
+    base = synthetic.randn((20, 256), 41, 1.0, torch.bfloat16).to(DEV)
+    w = synthetic.randn((64, 128), 42, 1.0, torch.bfloat16).to(DEV)
+    xs = base[:, 64:192]                    # row pitch 256 elements
+    y = bi.bi_linear(xs, w)
+    assert_bits_equal(y, bi.bi_linear(xs.contiguous(), w), "strided rows")
+
+
+def test_repeat_calls_are_bitwise_identical():
+    d = synthetic.cfg2_inputs(4096, M_max=256)
+    x, w, b = (d[k].to(DEV) for k in ("x", "w", "b"))
+    for m in (1, 64, 256):
+        first = bi.bi_linear(x[:m], w, b)
+        for _ in range(20):
+            assert_bits_equal(bi.bi_linear(x[:m], w, b), first, f"repeat M={m}")
+
+
+def test_graph_replay_matches_eager():
+    d = synthetic.cfg2_inputs(4096, M_max=128)
+    x, w, b = (d[k].to(DEV) for k in ("x", "w", "b"))
+    eager = {m: bi.bi_linear(x[:m], w, b) for m in (1, 8, 128)}
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for m in (1, 8, 128):                # warm-up on the capture stream
+            bi.bi_linear(x[:m], w, b)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        outs = {m: bi.bi_linear(x[:m], w, b) for m in (1, 8, 128)}
+    for rep in range(4):
+        outs_prev = {m: o.clone() for m, o in outs.items()}
+        for o in outs.values():
+            o.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for m in outs:
+            assert_bits_equal(outs[m], eager[m], f"graph replay {rep}, M={m}")
+        _ = bi.bi_linear(x[:3], w, b)        # eager work between replays
+        torch.cuda.synchronize()
+        assert outs_prev is not None
+
+
+def test_splitk_comparator_is_correct_but_batch_variant():
+    d = synthetic.cfg2_inputs(4096, M_max=256)
+    x, w, b = (d[k].to(DEV) for k in ("x", "w", "b"))
+    ref = oracle.linear(d["x"][:4], d["w"], d["b"])
+    diffs = 0
+    v_full = bi.bi_variant_linear(x, w, b)            # M = 256 -> 1 split
+    for m in (1, 16, 17, 64, 65, 128):
+        v = bi.bi_variant_linear(x[:m], w, b)
+        if m >= 4:
+            assert_close_to_oracle(v[:4].cpu(), ref, f"variant M={m}")
+        diffs += n_bit_diff(v, v_full[:m])
+    assert diffs > 0, "negative control: M-keyed split-K must change some bits"
+    # and with one split it is the invariant kernel itself
+    assert_bits_equal(bi.bi_variant_linear(x[:8], w, b, splits=1), bi.bi_linear(x[:8], w, b), "splits=1")

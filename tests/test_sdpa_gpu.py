@@ -1,0 +1,239 @@
+"""GPU tests of the invariant attention entry point (bi_sdpa).
+
+* exact pins: zero queries make every weight exp2(0) = 1, so with integer
+  values the output is the correctly rounded mean; a row that sees one key
+  returns that key's value row;
+* oracle tolerance on the seeded workloads;
+* invariance on raw bit patterns: every token of a prefill chunk equals its
+  own decode call (K / V truncated after it) and the full-cache decode with a
+  mask, for every query length of the sweep; growing the KV cache with masked
+  keys (crossing 4096) leaves results unchanged; batch neighbours, GQA vs
+  repeated-KV MHA, causal and masked-key invariants; repeats and graph replay.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import invariant_deterministic_gemm_amd as bi
+import oracle
+import synthetic
+from helpers import assert_bits_equal, assert_close_to_oracle, round_ref
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+DTS = [torch.float32, torch.bfloat16, torch.float16]
+
+
+def _ids(d):
+    return str(d).split(".")[-1]
+
+
+@pytest.mark.parametrize("dt", DTS, ids=_ids)
+@pytest.mark.parametrize("D", [64, 128])
+def test_zero_query_gives_exact_mean(dt, D):
+    B, Hq, Hkv, S = 1, 4, 2, 700                 # three splits, ragged last block
+    q = torch.zeros(B, Hq, S, D, dtype=dt)
+    k = synthetic.randn((B, Hkv, S, D), 51, 1.0, dt)
+    v = synthetic.randint((B, Hkv, S, D), 52, -8, 8, dt)
+    o = bi.bi_sdpa(q.to(DEV), k.to(DEV), v.to(DEV), causal=True).cpu()
+    ref = oracle.sdpa(q, k, v, causal=True)
+    assert_bits_equal(o, round_ref(ref, dt), f"zero-query means {dt} D={D}")
+
+
+@pytest.mark.parametrize("dt", DTS, ids=_ids)
+def test_single_visible_key_returns_its_value(dt):
+    B, Hq, Hkv, S, D = 2, 8, 2, 300, 128
+    q = synthetic.randn((B, Hq, S, D), 61, 1.0, dt)
+    k = synthetic.randn((B, Hkv, S, D), 62, 1.0, dt)
+    v = synthetic.randn((B, Hkv, S, D), 63, 1.0, dt)
+    o = bi.bi_sdpa(q.to(DEV), k.to(DEV), v.to(DEV), causal=True).cpu()
+    for h in range(Hq):
+        assert_bits_equal(o[:, h, 0], v[:, h * Hkv // Hq, 0], f"row 0 sees only key 0 (h={h})")
+    mask = torch.zeros(1, 1, 1, S, dtype=torch.bool)
+    mask[..., 123] = True
+    o = bi.bi_sdpa(q[:, :, :3].to(DEV), k.to(DEV), v.to(DEV), mask=mask.to(DEV)).cpu()
+    for h in range(Hq):
+        for i in range(3):
+            assert_bits_equal(o[:, h, i], v[:, h * Hkv // Hq, 123], "mask with one key")
+
+
+def test_rows_without_visible_keys_are_zero():
+    q = synthetic.randn((1, 4, 2, 128), 71, 1.0, torch.bfloat16).to(DEV)
+    k = synthetic.randn((1, 2, 50, 128), 72, 1.0, torch.bfloat16).to(DEV)
+    mask = torch.zeros(1, 1, 2, 50, dtype=torch.bool, device=DEV)
+    o = bi.bi_sdpa(q, k, k, mask=mask)
+    assert_bits_equal(o, torch.zeros_like(o), "no visible key")
+    o = bi.bi_sdpa(q, k[:, :, :0], k[:, :, :0])
+    assert_bits_equal(o, torch.zeros_like(o), "empty cache")
+
+
+@pytest.mark.parametrize("B", [1, 2])
+def test_config3_prefill_tokens_equal_their_decode(B):
+    S = 1024
+    d = synthetic.cfg3_inputs(B=max(B, 1), S=S + 64)
+    q, k, v = (d[n].to(DEV) for n in ("q", "k", "v"))
+    scale = 1.0 / math.sqrt(128)
+    # decode references for the last 64 positions of S = 1024, two ways
+    dec = {}
+    for p in range(S - 64, S):
+        dec[p] = bi.bi_sdpa(q[:, :, p:p + 1], k[:, :, :p + 1], v[:, :, :p + 1], causal=True, scale=scale)
+        m = torch.zeros(1, 1, 1, S, dtype=torch.bool, device=DEV)
+        m[..., :p + 1] = True
+        dm = bi.bi_sdpa(q[:, :, p:p + 1], k[:, :, :S], v[:, :, :S], mask=m, scale=scale)
+        assert_bits_equal(dm, dec[p], f"decode p={p}: truncated cache vs full cache + mask")
+    for L in synthetic.CFG3["Lq_values"] + [3, 33]:
+        o = bi.bi_sdpa(q[:, :, S - L:S], k[:, :, :S], v[:, :, :S], causal=True, scale=scale)
+        for i in range(L):
+            p = S - L + i
+            assert_bits_equal(o[:, :, i:i + 1], dec[p], f"q_len={L}, token {i} (position {p})")
+    # the same chunks against a cache of 1024 + L (chunk at the end)
+    for L in (1, 9, 64):
+        SS = S + L
+        o = bi.bi_sdpa(q[:, :, SS - L:SS], k[:, :, :SS], v[:, :, :SS], causal=True, scale=scale)
+        for i in range(L):
+            p = SS - L + i
+            ref = bi.bi_sdpa(q[:, :, p:p + 1], k[:, :, :p + 1], v[:, :, :p + 1], causal=True, scale=scale)
+            assert_bits_equal(o[:, :, i:i + 1], ref, f"cache {SS}, q_len={L}, token {i}")
+
+
+def test_config3_accuracy_against_oracle():
+    S = 1024
+    d = synthetic.cfg3_inputs(B=1, S=S)
+    q, k, v = (d[n].to(DEV) for n in ("q", "k", "v"))
+    for L in (1, 9, 64):
+        o = bi.bi_sdpa(q[:, :, S - L:], k, v, causal=True)
+        ref = oracle.sdpa(d["q"][:, :, S - L:], d["k"], d["v"], causal=True)
+        assert_close_to_oracle(o.cpu(), ref, f"config 3 q_len={L}")
+
+
+def test_batch_neighbours_and_gqa_equal_mha():
+    S = 1024
+    d = synthetic.cfg3_inputs(B=4, S=S)
+    q, k, v = (d[n].to(DEV) for n in ("q", "k", "v"))
+    L = 16
+    full = bi.bi_sdpa(q[:, :, S - L:], k, v, causal=True)
+    for b in range(4):
+        one = bi.bi_sdpa(q[b:b + 1, :, S - L:], k[b:b + 1], v[b:b + 1], causal=True)
+        assert_bits_equal(full[b:b + 1], one, f"batch element {b} alone vs in a batch of 4")
+    # neighbours replaced by NaN
+    q2, k2, v2 = (torch.full_like(t, float("nan")) for t in (q, k, v))
+    q2[2], k2[2], v2[2] = q[2], k[2], v[2]
+    o2 = bi.bi_sdpa(q2[:, :, S - L:], k2, v2, causal=True)
+    assert_bits_equal(o2[2], full[2], "NaN batch neighbours")
+    # GQA == MHA with K/V repeated per group
+    G = 4
+    krep = k.repeat_interleave(G, dim=1).contiguous()
+    vrep = v.repeat_interleave(G, dim=1).contiguous()
+    mha = bi.bi_sdpa(q[:, :, S - L:], krep, vrep, causal=True)
+    assert_bits_equal(mha, full, "GQA vs repeated-KV MHA")
+    # a single head of a group called alone (G = 1)
+    h = 5
+    solo = bi.bi_sdpa(q[:, h:h + 1, S - L:], k[:, h // G:h // G + 1], v[:, h // G:h // G + 1], causal=True)
+    assert_bits_equal(solo, full[:, h:h + 1], "one query head alone")
+
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16], ids=_ids)
+def test_config4_context_growth_with_masked_keys(dt):
+    d = synthetic.cfg4_inputs(dt, S=4200)
+    q, k, v = (d[n].to(DEV) for n in ("q", "k", "v"))
+    lo, hi = synthetic.CFG4["S_lo"], synthetic.CFG4["S_hi"]
+    for n0 in (4000, 4095, 4096, 4097):
+        base = bi.bi_sdpa(q, k[:, :, :n0], v[:, :, :n0])
+        ref = oracle.sdpa(d["q"], d["k"][:, :, :n0], d["v"][:, :, :n0])
+        assert_close_to_oracle(base.cpu(), ref, f"config 4 {dt} S={n0}")
+        for n in range(n0, hi + 1, 7 if n0 == 4000 else 1):
+            m = torch.zeros(1, 1, 1, n, dtype=torch.bool, device=DEV)
+            m[..., :n0] = True
+            o = bi.bi_sdpa(q, k[:, :, :n], v[:, :, :n], mask=m)
+            assert_bits_equal(o, base, f"{dt}: S={n} with keys >= {n0} masked vs S={n0}")
+    prev = bi.bi_sdpa(q, k[:, :, :lo - 1], v[:, :, :lo - 1])
+    for n in range(lo, hi + 1):
+        m = torch.ones(1, 1, 1, n, dtype=torch.bool, device=DEV)
+        m[..., n - 1] = False
+        o = bi.bi_sdpa(q, k[:, :, :n], v[:, :, :n], mask=m)
+        assert_bits_equal(o, prev, f"{dt}: S={n} with its newest key masked vs S={n - 1}")
+        prev = bi.bi_sdpa(q, k[:, :, :n], v[:, :, :n])
+
+
+def test_causal_and_masked_key_values_are_never_read():
+    B, Hq, Hkv, L, S, D = 1, 8, 2, 40, 600, 128
+    q = synthetic.randn((B, Hq, L, D), 81, 1.0, torch.bfloat16).to(DEV)
+    k = synthetic.randn((B, Hkv, S, D), 82, 1.0, torch.bfloat16).to(DEV)
+    v = synthetic.randn((B, Hkv, S, D), 83, 1.0, torch.bfloat16).to(DEV)
+    base = bi.bi_sdpa(q, k, v, causal=True)
+    for i in (0, 17, 39):
+        p = S - L + i
+        k2, v2 = k.clone(), v.clone()
+        k2[:, :, p + 1:] = 1e4
+        v2[:, :, p + 1:] = -3e3
+        assert_bits_equal(bi.bi_sdpa(q, k2, v2, causal=True)[:, :, i], base[:, :, i], f"causal row {i}")
+    mask = torch.ones(1, 1, L, S, dtype=torch.bool, device=DEV)
+    mask[..., 100:130] = False
+    mask[..., 7] = False
+    mb = bi.bi_sdpa(q, k, v, mask=mask)
+    k2, v2 = k.clone(), v.clone()
+    k2[:, :, 100:130] = 5e3
+    v2[:, :, 7] = -7e3
+    assert_bits_equal(bi.bi_sdpa(q, k2, v2, mask=mask), mb, "masked key values are not read")
+    ref = oracle.sdpa(q.cpu(), k.cpu(), v.cpu(), mask=mask.cpu())
+    assert_close_to_oracle(mb.cpu(), ref, "boolean mask")
+    # per-head mask equal to the broadcast one
+    mfull = mask.expand(B, Hq, L, S).contiguous()
+    assert_bits_equal(bi.bi_sdpa(q, k, v, mask=mfull), mb, "expanded mask")
+
+
+@pytest.mark.parametrize("dt", DTS, ids=_ids)
+@pytest.mark.parametrize("D", [64, 128])
+def test_accuracy_small_shapes(dt, D):
+    B, Hq, Hkv, L, S = 2, 6, 3, 20, 333
+    q = synthetic.randn((B, Hq, L, D), 91, 1.0, dt)
+    k = synthetic.randn((B, Hkv, S, D), 92, 1.0, dt)
+    v = synthetic.randn((B, Hkv, S, D), 93, 1.0, dt)
+    for causal in (False, True):
+        o = bi.bi_sdpa(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal)
+        assert_close_to_oracle(o.cpu(), oracle.sdpa(q, k, v, causal=causal), f"{dt} D={D} causal={causal}")
+
+
+def test_strided_qkv_views():
+    S, D = 512, 128
+    qkv = synthetic.randn((1, 300, 3 * 4, D), 95, 1.0, torch.bfloat16).to(DEV)   # (B, L, 3H, D)
+    q = qkv[:, :, 0:4].transpose(1, 2)
+    k = qkv[:, :, 4:8:2].transpose(1, 2)
+    v = qkv[:, :, 8:12:2].transpose(1, 2)
+    o = bi.bi_sdpa(q, k, v, causal=True)
+    oc = bi.bi_sdpa(q.contiguous(), k.contiguous(), v.contiguous(), causal=True)
+    assert_bits_equal(o, oc, "strided views vs contiguous copies")
+    assert S > 0
+
+
+def test_repeat_and_graph_replay():
+    d = synthetic.cfg3_inputs(B=1, S=1024)
+    q, k, v = (d[n].to(DEV) for n in ("q", "k", "v"))
+    eager = bi.bi_sdpa(q[:, :, -9:], k, v, causal=True)
+    for _ in range(20):
+        assert_bits_equal(bi.bi_sdpa(q[:, :, -9:], k, v, causal=True), eager, "repeat")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        bi.bi_sdpa(q[:, :, -9:], k, v, causal=True)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out = bi.bi_sdpa(q[:, :, -9:], k, v, causal=True)
+    for rep in range(4):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert_bits_equal(out, eager, f"graph replay {rep}")
+        bi.bi_sdpa(q[:, :, -1:], k, v, causal=True)
+        torch.cuda.synchronize()
+
+
+def test_readme_style_call():
+    d = synthetic.cfg3_inputs(B=1, S=256)
+    q, k, v = (d[n].to(DEV) for n in ("q", "k", "v"))
+    assert_bits_equal(bi.scaled_dot_product_attention(q[:, :, -4:], k, v, mask="causal"),
+                      bi.bi_sdpa(q[:, :, -4:], k, v, causal=True), "mask='causal'")
+    assert np.isfinite(bi.scaled_dot_product_attention(q[:, :, -4:], k, v).float().cpu().numpy()).all()
