@@ -1,0 +1,389 @@
+"""Benchmark of the batch-invariant GEMM and attention kernels on one MI355X.
+
+One step = one pass of the whole hot path over the seeded synthetic workload
+of the bf16 linear / addmm configuration (K = 4096, N in {4096, 14336},
+M in {1, 2, 3, 4, 7, 8, 16, 33, 64, 128, 256}, bias added, alpha = beta = 1)
+plus the bf16 causal GQA attention sweep (Hq = 32, Hkv = 8, D = 128, KV cache
+1024, q_len in {1, 2, 4, 8, 9, 16, 64}).
+
+The step is captured as HIP graphs, one per kernel configuration, replayed
+back to back; events between the replays time each configuration inside the
+timed region, which gives the per-launch average of the dominant kernel for
+the roofline.  Weight matrices rotate through enough copies to exceed the
+256 MB Infinity Cache, so weight reads come from HBM.  After timing, the
+outputs of every batch size are compared bit for bit with the largest batch
+(GEMM) and with the longest query chunk (attention).
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0       # dense bf16 MFMA
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-cells", action="store_true", help="skip the per-cell roofline table")
+    ap.add_argument("--cpu-threads", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import invariant_deterministic_gemm_amd as bi
+    import synthetic
+    from invariant_deterministic_gemm_amd import _native
+
+    lib = _native.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    K = synthetic.CFG2["K"]
+    Ms = synthetic.CFG2["M_values"]
+    Ns = synthetic.CFG2["N_values"]
+    Mmax = max(Ms)
+
+    # ------------------------------------------------------------ inputs
+    t0 = time.time()
+    data = {}
+    copies = {4096: 8, 14336: 4}          # > 256 MB of weights per N and layout
+    for N in Ns:
+        d = synthetic.cfg2_inputs(N, M_max=Mmax)
+        w = d["w"].to(dev)
+        ws = [w] + [w.clone() for _ in range(copies[N] - 1)]
+        wts = [w.t().contiguous()] + [None] * (copies[N] - 1)
+        for i in range(1, copies[N]):
+            wts[i] = wts[0].clone()
+        data[N] = dict(x=d["x"].to(dev), w=ws, wt=wts, b=d["b"].to(dev),
+                       sha=synthetic.sha256(d["w"]))
+    c3 = synthetic.cfg3_inputs(B=1, S=synthetic.CFG3["S"])
+    q3, k3, v3 = (c3[n].to(dev) for n in ("q", "k", "v"))
+    S3 = synthetic.CFG3["S"]
+    Lqs = synthetic.CFG3["Lq_values"]
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.time() - t0:.1f}s")
+
+    # ------------------------------------------------------------ the step, grouped by kernel
+    launches = []     # (group, kind, fn, flops, bytes, meta)
+    ctr = {N: 0 for N in Ns}
+    for N in Ns:
+        dN = data[N]
+        for M in Ms:
+            for form in ("linear", "addmm"):
+                i = ctr[N] % copies[N]
+                ctr[N] += 1
+                if form == "linear":
+                    kname = lib.bi_gemm_kernel_name(M, N, 0).decode()
+                    fn = (lambda x=dN["x"][:M], w=dN["w"][i], b=dN["b"]: bi.bi_linear(x, w, b))
+                else:
+                    kname = lib.bi_gemm_kernel_name(M, N, 1).decode()
+                    fn = (lambda x=dN["x"][:M], wt=dN["wt"][i], b=dN["b"]: bi.bi_addmm(b, x, wt, 1.0, 1.0))
+                flops = 2.0 * M * N * K + M * N
+                nbytes = 2.0 * (M * K + N * K + M * N + N)
+                launches.append((kname, "gemm", fn, flops, nbytes, dict(N=N, M=M, form=form)))
+    for L in Lqs:
+        fn = (lambda L=L: bi.bi_sdpa(q3[:, :, S3 - L:], k3, v3, causal=True))
+        nbytes = 2.0 * (2 * 8 * S3 * 128 + 2 * 32 * L * 128)
+        vis = sum(S3 - L + i + 1 for i in range(L))
+        flops = 4.0 * 32 * 128 * vis
+        launches.append(("sdpa_split+combine", "sdpa", fn, flops, nbytes, dict(Lq=L)))
+
+    groups = {}
+    for rec in launches:
+        groups.setdefault(rec[0], []).append(rec)
+    names = list(groups)
+
+    # warm every path eagerly once, then capture one graph per group
+    for rec in launches:
+        rec[2]()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for rec in launches:
+            rec[2]()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs, outs = {}, {}
+    for g in names:
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            outs[g] = [rec[2]() for rec in groups[g]]
+        graphs[g] = gr
+    torch.cuda.synchronize()
+    log(f"captured {len(names)} graphs over {len(launches)} launches")
+
+    def run_step(evs=None):
+        for j, g in enumerate(names):
+            if evs is not None:
+                evs[j][0].record()
+            graphs[g].replay()
+            if evs is not None:
+                evs[j][1].record()
+
+    for _ in range(args.warmup):
+        run_step()
+    torch.cuda.synchronize()
+
+    K_steps = args.steps
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in names] for _ in range(K_steps)]
+    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(K_steps + 1)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    step_ev[0].record()
+    for s in range(K_steps):
+        run_step(evs[s])
+        step_ev[s + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    gpu_ms = step_ev[0].elapsed_time(step_ev[-1])
+    ms_per_step = wall * 1e3 / K_steps
+    group_ms = {g: sum(evs[s][j][0].elapsed_time(evs[s][j][1]) for s in range(K_steps)) / K_steps
+                for j, g in enumerate(names)}
+    log(f"timed {K_steps} steps: wall {ms_per_step:.3f} ms/step, gpu events {gpu_ms / K_steps:.3f} ms/step")
+
+    gemm_flops = sum(r[3] for r in launches if r[1] == "gemm")
+    gemm_ms = sum(group_ms[g] for g in names if groups[g][0][1] == "gemm")
+    sdpa_bytes = sum(r[4] for r in launches if r[1] == "sdpa")
+    sdpa_ms = sum(group_ms[g] for g in names if groups[g][0][1] == "sdpa")
+    # whole-step GEMM throughput over the wall-clock step (attention time included in the denominator)
+    value = gemm_flops / (ms_per_step * 1e-3) / 1e12
+
+    # ------------------------------------------------------------ bit checks (outside the timed region)
+    diff_rows = 0
+    checked_rows = 0
+    for N in Ns:
+        dN = data[N]
+        for form in ("linear", "addmm"):
+            if form == "linear":
+                ref = bi.bi_linear(dN["x"], dN["w"][0], dN["b"])
+            else:
+                ref = bi.bi_addmm(dN["b"], dN["x"], dN["wt"][0], 1.0, 1.0)
+            for g in names:
+                for rec, out in zip(groups[g], outs[g]):
+                    meta = rec[5]
+                    if rec[1] != "gemm" or meta["N"] != N or meta["form"] != form:
+                        continue
+                    M = meta["M"]
+                    neq = (out.view(torch.int16) != ref[:M].view(torch.int16)).any(dim=1)
+                    diff_rows += int(neq.sum().item())
+                    checked_rows += M
+    ref_o = bi.bi_sdpa(q3[:, :, S3 - 64:], k3, v3, causal=True)
+    for rec, out in zip(groups["sdpa_split+combine"], outs["sdpa_split+combine"]):
+        L = rec[5]["Lq"]
+        neq = (out.view(torch.int16) != ref_o[:, :, 64 - L:].view(torch.int16)).any(dim=-1)
+        diff_rows += int(neq.sum().item())
+        checked_rows += int(neq.numel())
+    log(f"bit check: {diff_rows} of {checked_rows} rows differ")
+
+    # ------------------------------------------------------------ dominant kernel roofline
+    dom = max(names, key=lambda g: group_ms[g])
+    dl = groups[dom]
+    avg_ms = group_ms[dom] / len(dl)
+    if dl[0][1] == "gemm" and all(r[5]["M"] <= 64 for r in dl):
+        bound, unit, peak = "hbm", "GB/s", HBM_PEAK_GBPS
+        per_launch = sum(r[4] for r in dl) / len(dl)
+        achieved = per_launch / (avg_ms * 1e-3) / 1e9
+    elif dl[0][1] == "gemm":
+        bound, unit, peak = "mfma", "TFLOP/s", BF16_PEAK_TFLOPS
+        per_launch = sum(r[3] for r in dl) / len(dl)
+        achieved = per_launch / (avg_ms * 1e-3) / 1e12
+    else:
+        bound, unit, peak = "hbm", "GB/s", HBM_PEAK_GBPS
+        per_launch = sum(r[4] for r in dl) / len(dl)
+        achieved = per_launch / (avg_ms * 1e-3) / 1e9
+    roofline = {"bound": bound, "kernel": dom, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4), "traffic": None,
+                "launches_per_step": len(dl), "avg_launch_us": round(avg_ms * 1e3, 3),
+                "algorithmic_per_launch": per_launch}
+
+    # ------------------------------------------------------------ per-cell table (outside the step)
+    cells = {}
+    if not args.no_cells:
+        cells = measure_cells(bi, lib, torch, dev, synthetic, data, launches, groups, names, group_ms)
+
+    # ------------------------------------------------------------ CPU oracle baseline
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(torch, synthetic, args)
+
+    out = {
+        "metric": "invariant GEMM TFLOP/s + SDPA GB/s at 1 GPU; bit-differing rows across batch = 0",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K_steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "bf16 linear+addmm K=4096 N={4096,14336} M-sweep {1..256} "
+                               "+ bf16 causal GQA SDPA Hq=32 Hkv=8 D=128 S=1024 q_len-sweep",
+                   "global_batch": sum(Ms), "seq_len": S3, "parallelism": "none (1 GPU)"},
+        "gemm_tflops_gpu_time": round(gemm_flops / (gemm_ms * 1e-3) / 1e12, 3),
+        "sdpa_GBps": round(sdpa_bytes / (sdpa_ms * 1e-3) / 1e9, 2),
+        "bit_differing_rows": diff_rows,
+        "bit_checked_rows": checked_rows,
+        "group_ms": {g: round(v, 4) for g, v in group_ms.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "cells": cells,
+        "input_sha256": {str(N): data[N]["sha"] for N in Ns},
+    }
+    print(json.dumps(out), flush=True)
+
+
+def _time_graph(torch, fn, reps=20, iters=10):
+    """Median per-call ms of fn replayed from a captured graph (reps calls per replay)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(iters):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        b.synchronize()
+        ts.append(a.elapsed_time(b) / reps)
+    ts.sort()
+    return ts[len(ts) // 2]
+
+
+def measure_cells(bi, lib, torch, dev, synthetic, data, launches, groups, names, group_ms):
+    cells = {"decode_gemm": [], "large_m_gemm": [], "decode_attention": [], "comparator": {}}
+    K = 4096
+    # decode GEMM: weights rotate through copies inside one graph, so reads are cold
+    logits = synthetic.cfg5_inputs(torch.bfloat16, M_max=8)
+    wl = logits["w"].to(dev)
+    wls = [wl, wl.clone()]
+    xl = logits["h"].to(dev)
+    for N in (4096, 14336, 32000):
+        for M in (1, 2, 4, 8):
+            if N == 32000:
+                ws, x = wls, xl
+            else:
+                ws, x = data[N]["w"], data[N]["x"]
+            it = iter(range(10 ** 9))
+            fn = (lambda: bi.bi_linear(x[:M], ws[next(it) % len(ws)]))
+            ms = _time_graph(torch, fn, reps=len(ws) * 2)
+            nbytes = 2.0 * (M * K + N * K + M * N)
+            gbps = nbytes / (ms * 1e-3) / 1e9
+            cells["decode_gemm"].append({"M": M, "N": N, "us": round(ms * 1e3, 2), "GBps": round(gbps, 1),
+                                         "frac_hbm": round(gbps / HBM_PEAK_GBPS, 4),
+                                         "kernel": lib.bi_gemm_kernel_name(M, N, 0).decode()})
+    del wls, wl
+    # large-M GEMM (added points, above the configs' M = 256)
+    for N in (4096, 14336):
+        w = data[N]["w"][0]
+        for M in (512, 1024, 4096):
+            x = synthetic.randn((M, K), 0x5EED77, 1.0, torch.bfloat16).to(dev)
+            ms = _time_graph(torch, lambda: bi.bi_linear(x, w), reps=5, iters=6)
+            tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+            cells["large_m_gemm"].append({"M": M, "N": N, "us": round(ms * 1e3, 1), "TFLOPs": round(tf, 1),
+                                          "frac_mfma": round(tf / BF16_PEAK_TFLOPS, 4),
+                                          "kernel": lib.bi_gemm_kernel_name(M, N, 0).decode()})
+    # decode attention on the pages' sweep shape (Hq 32, Hkv 8, D 128, bf16, q_len 1)
+    for B, S in ((8, 2048), (8, 8192), (32, 8192), (32, 32768)):
+        # multi-GB timing-only inputs: seeded draws on the GPU generator
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(0x5EED90 + B * 100000 + S)
+        q = torch.randn((B, 32, 1, 128), generator=gen, device=dev).to(torch.bfloat16)
+        k = torch.randn((B, 8, S, 128), generator=gen, device=dev).to(torch.bfloat16)
+        v = torch.randn((B, 8, S, 128), generator=gen, device=dev).to(torch.bfloat16)
+        ws = torch.empty(bi.sdpa_workspace_bytes(B, 32, 1, S, 128), dtype=torch.uint8, device=dev)
+        ms = _time_graph(torch, lambda: bi.bi_sdpa(q, k, v, causal=True, workspace=ws), reps=4, iters=6)
+        nbytes = 2.0 * (B * 8 * S * 128 * 2 + 2 * B * 32 * 128)
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        cells["decode_attention"].append({"B": B, "S": S, "us": round(ms * 1e3, 1), "GBps": round(gbps, 1),
+                                          "frac_hbm": round(gbps / HBM_PEAK_GBPS, 4)})
+        del q, k, v, ws
+    # batch-variant comparator on the linear half of the step: cost ratio and negative control
+    inv_ms = var_ms = 0.0
+    diff = 0
+    for N in (4096, 14336):
+        dN = data[N]
+        ws = dN["w"]
+        full_var = bi.bi_variant_linear(dN["x"], ws[0], dN["b"])
+        for M in synthetic.CFG2["M_values"]:
+            x = dN["x"][:M]
+            it1, it2 = iter(range(10 ** 9)), iter(range(10 ** 9))
+            inv_ms += _time_graph(torch, lambda: bi.bi_linear(x, ws[next(it1) % len(ws)], dN["b"]),
+                                  reps=len(ws), iters=5)
+            var_ms += _time_graph(torch, lambda: bi.bi_variant_linear(x, ws[next(it2) % len(ws)], dN["b"]),
+                                  reps=len(ws), iters=5)
+            v = bi.bi_variant_linear(x, dN["w"][0], dN["b"])
+            diff += int((v.view(torch.int16) != full_var[:M].view(torch.int16)).any(dim=1).sum().item())
+    cells["comparator"] = {"invariant_ms": round(inv_ms, 4), "variant_ms": round(var_ms, 4),
+                           "invariant_over_variant_time": round(inv_ms / var_ms, 4),
+                           "variant_rows_differing_from_M256": diff}
+    return cells
+
+
+def cpu_baseline(torch, synthetic, args):
+    import numpy as np  # noqa: F401
+    import oracle
+    if args.cpu_threads > 0:
+        oracle.set_threads(args.cpu_threads)
+    threads = oracle.threads()
+    Ms = synthetic.CFG2["M_values"]
+    inputs = [synthetic.cfg2_inputs(N, M_max=max(Ms)) for N in synthetic.CFG2["N_values"]]
+    flops = 0.0
+    passes = 0
+    t0 = time.perf_counter()
+    # whole passes over the sample until at least args.cpu_seconds have gone by
+    while passes == 0 or time.perf_counter() - t0 < args.cpu_seconds:
+        for d in inputs:
+            # the largest batch of the sweep: its rows contain every smaller batch's rows
+            oracle.linear(d["x"], d["w"], d["b"])
+            flops += 2.0 * d["x"].shape[0] * d["w"].shape[0] * d["w"].shape[1]
+        passes += 1
+    t = time.perf_counter() - t0
+    log(f"cpu oracle: {flops / 1e9:.1f} GFLOP in {t:.1f}s on {threads} threads ({passes} passes)")
+    return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{passes} passes of the float64 oracle linear on the M=256 batch (x 256x4096, bias) "
+                      "for N=4096 and N=14336, i.e. every row of the GEMM sweep once per pass; "
+                      "attention not included",
+            "seconds": round(t, 2)}
+
+
+if __name__ == "__main__":
+    main()
