@@ -77,9 +77,8 @@ def main():
         d = synthetic.cfg2_inputs(N, M_max=Mmax)
         w = d["w"].to(dev)
         ws = [w] + [w.clone() for _ in range(copies[N] - 1)]
-        wts = [w.t().contiguous()] + [None] * (copies[N] - 1)
-        for i in range(1, copies[N]):
-            wts[i] = wts[0].clone()
+        # addmm(b, x, W^T) with W^T the transposed view of the (N, K) weight, as a linear layer calls it
+        wts = [wc.t() for wc in ws]
         data[N] = dict(x=d["x"].to(dev), w=ws, wt=wts, b=d["b"].to(dev),
                        sha=synthetic.sha256(d["w"]))
     c3 = synthetic.cfg3_inputs(B=1, S=synthetic.CFG3["S"])
@@ -102,7 +101,7 @@ def main():
                     kname = lib.bi_gemm_kernel_name(M, N, 0).decode()
                     fn = (lambda x=dN["x"][:M], w=dN["w"][i], b=dN["b"]: bi.bi_linear(x, w, b))
                 else:
-                    kname = lib.bi_gemm_kernel_name(M, N, 1).decode()
+                    kname = lib.bi_gemm_kernel_name(M, N, 0).decode()
                     fn = (lambda x=dN["x"][:M], wt=dN["wt"][i], b=dN["b"]: bi.bi_addmm(b, x, wt, 1.0, 1.0))
                 flops = 2.0 * M * N * K + M * N
                 nbytes = 2.0 * (M * K + N * K + M * N + N)

@@ -75,9 +75,19 @@ typedef enum {
  * The bias / C tensor, when present, has the OUTPUT dtype.
  * Shapes: M, N, K >= 0 and < 2^31.  M == 0 or N == 0 enqueues nothing.
  * Alignment (else BI_ERR_UNSUPPORTED): every base pointer 16-byte aligned;
- *   K a multiple of 8 (16-bit inputs) or 4 (fp32 inputs); lda / ldb / ldw
- *   multiples of 8 (16-bit) or 4 (fp32) elements; for the (K, N) layout of
- *   bi_matmul / bi_addmm also N a multiple of 8 (16-bit) or 4 (fp32).
+ *   K a multiple of 8 (16-bit inputs) or 4 (fp32 inputs); lda, ldw and the
+ *   non-unit stride of b multiples of 8 (16-bit) or 4 (fp32) elements; for a
+ *   row-major (K, N) operand of bi_matmul / bi_addmm also N a multiple of 8
+ *   (16-bit) or 4 (fp32).
+ *
+ * The (K, N) operand b of bi_matmul / bi_addmm is described by two element
+ * strides, b_stride_k (between consecutive k) and b_stride_n (between
+ * consecutive n); one of them must be 1:
+ *   b_stride_n == 1 : row-major (K, N), row k at b + k * b_stride_k;
+ *   b_stride_k == 1 : column-major (K, N), i.e. the (N, K) nn.Linear layout
+ *                     (a transposed view such as w.t()), column n at
+ *                     b + n * b_stride_n.
+ * Both layouts give bit-identical results (same per-element chain).
  */
 
 /* y (M,N) = x (M,K) . w^T + bias,  w in the (N,K) nn.Linear layout.
@@ -91,15 +101,15 @@ bi_status bi_linear(const void *x, int64_t ldx,
                     bi_dtype in_dt, bi_dtype out_dt,
                     void *stream);
 
-/* c (M,N) = a (M,K) . b (K,N).  b: row k at b + k*ldb (ldb >= N). */
+/* c (M,N) = a (M,K) . b (K,N), b described by (b_stride_k, b_stride_n) as above. */
 bi_status bi_matmul(const void *a, int64_t lda,
-                    const void *b, int64_t ldb,
+                    const void *b, int64_t b_stride_k, int64_t b_stride_n,
                     void *c, int64_t ldc,
                     int64_t M, int64_t N, int64_t K,
                     bi_dtype in_dt, bi_dtype out_dt,
                     void *stream);
 
-/* out (M,N) = alpha * (a (M,K) . b (K,N)) + beta * cin.
+/* out (M,N) = alpha * (a (M,K) . b (K,N)) + beta * cin, b as for bi_matmul.
  * cin: out_dt elements, row m at cin + m*ldcin; ldcin == 0 broadcasts one
  * row of N elements to every m (the bias form).  When beta == 0, cin is not
  * read and may be NULL (BLAS convention).  out may alias cin only if
@@ -107,7 +117,7 @@ bi_status bi_matmul(const void *a, int64_t lda,
  * own write and by no other thread). */
 bi_status bi_addmm(const void *cin, int64_t ldcin,
                    const void *a, int64_t lda,
-                   const void *b, int64_t ldb,
+                   const void *b, int64_t b_stride_k, int64_t b_stride_n,
                    void *out, int64_t ldo,
                    int64_t M, int64_t N, int64_t K,
                    float alpha, float beta,
@@ -188,8 +198,8 @@ size_t bi_variant_workspace_bytes(int64_t M, int64_t N, int splits);
 int bi_variant_splits(int64_t M);
 
 /* Which kernel configuration a GEMM of this shape runs on ("gemm_skinny_nk/fm1",
- * "gemm_tiled_kn/128x128", ...; b_kn != 0 for the (K, N) layout of bi_matmul /
- * bi_addmm).  Informational: every configuration computes the same bits.
+ * "gemm_tiled_kn/128x128", ...; b_kn != 0 for a row-major (K, N) operand of
+ * bi_matmul / bi_addmm, 0 for bi_linear and for column-major operands).  Informational: every configuration computes the same bits.
  * Returns "none" for empty or oversized shapes. */
 const char *bi_gemm_kernel_name(int64_t M, int64_t N, int b_kn);
 

@@ -109,6 +109,19 @@ def _aligned_ld(t: torch.Tensor) -> torch.Tensor:
     return t
 
 
+def _kn_operand(b: torch.Tensor) -> torch.Tensor:
+    """A (K, N) operand as given when one of its strides is 1 (row- or column-major), else a copy."""
+    if b.dim() != 2:
+        raise NotImplementedError("batched right operands are not supported")
+    K, N = b.shape
+    epc = 16 // b.element_size()
+    if b.stride(1) == 1 and (K <= 1 or (b.stride(0) >= N and b.stride(0) % epc == 0)):
+        return b
+    if b.stride(0) == 1 and (N <= 1 or (b.stride(1) >= K and b.stride(1) % epc == 0)):
+        return b
+    return b.contiguous()
+
+
 def bi_linear(x: torch.Tensor, w: torch.Tensor, bias: torch.Tensor | None = None,
               out_dtype: torch.dtype | None = None) -> torch.Tensor:
     """y = x w^T + bias with w in the (N, K) nn.Linear layout; leading dims of x are batch."""
@@ -146,14 +159,14 @@ def bi_matmul(a: torch.Tensor, b: torch.Tensor, out_dtype: torch.dtype | None = 
     out_dtype = out_dtype or a.dtype
     lead = a.shape[:-1]
     a2 = _aligned_ld(_rows(a))
-    b2 = _aligned_ld(_rows(b))
+    b2 = _kn_operand(b)
     M, K = a2.shape
     if b2.shape[0] != K:
         raise ValueError("inner dims differ")
     N = b2.shape[1]
     y = torch.empty((M, N), dtype=out_dtype, device=dev)
     lib = _native.load()
-    st = lib.bi_matmul(_ptr(a2), _ld(a2), _ptr(b2), _ld(b2), _ptr(y), max(N, 1), M, N, K,
+    st = lib.bi_matmul(_ptr(a2), _ld(a2), _ptr(b2), b2.stride(0), b2.stride(1), _ptr(y), max(N, 1), M, N, K,
                        _dt(a2, "bi_matmul"), _dt(y, "bi_matmul"), _stream(dev))
     _check(st, "bi_matmul")
     return y.reshape(*lead, N)
@@ -169,7 +182,7 @@ def bi_addmm(c: torch.Tensor | None, a: torch.Tensor, b: torch.Tensor, alpha: fl
         raise NotImplementedError("bi_addmm: 2-D operands only")
     out_dtype = out_dtype or a.dtype
     a2 = _aligned_ld(_rows(a))
-    b2 = _aligned_ld(_rows(b))
+    b2 = _kn_operand(b)
     M, K = a2.shape
     if b2.shape[0] != K:
         raise ValueError("inner dims differ")
@@ -192,7 +205,8 @@ def bi_addmm(c: torch.Tensor | None, a: torch.Tensor, b: torch.Tensor, alpha: fl
             ldc = c2.stride(0) if M > 1 else N
     y = torch.empty((M, N), dtype=out_dtype, device=dev)
     lib = _native.load()
-    st = lib.bi_addmm(_ptr(c2), ldc, _ptr(a2), _ld(a2), _ptr(b2), _ld(b2), _ptr(y), max(N, 1), M, N, K,
+    st = lib.bi_addmm(_ptr(c2), ldc, _ptr(a2), _ld(a2), _ptr(b2), b2.stride(0), b2.stride(1), _ptr(y),
+                      max(N, 1), M, N, K,
                       float(alpha), float(beta), _dt(a2, "bi_addmm"), _dt(y, "bi_addmm"), _stream(dev))
     _check(st, "bi_addmm")
     return y

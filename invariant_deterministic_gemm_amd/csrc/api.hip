@@ -101,6 +101,27 @@ bi_status check_gemm(const char *fn, const void *a, int64_t lda, const void *b, 
     return ok();
 }
 
+// Resolve the (K, N) operand of bi_matmul / bi_addmm given by two strides into
+// one of the two kernel layouts.
+bi_status resolve_b(const char *fn, int64_t sk, int64_t sn, int64_t K, int64_t N, bool &b_kn, int64_t &ldb) {
+    if (sk == 1 && (N <= 1 || sn != 1)) {          // column-major: the (N, K) layout
+        b_kn = false;
+        ldb = N <= 1 ? (K > 0 ? K : 1) : sn;
+        if (N > 1 && sn < K)
+            return fail(BI_ERR_INVALID, "%s: b column stride %lld < K=%lld", fn, (long long)sn, (long long)K);
+        return BI_OK;
+    }
+    if (sn == 1) {                                   // row-major (K, N)
+        b_kn = true;
+        ldb = K <= 1 ? (N > 0 ? N : 1) : sk;
+        if (K > 1 && sk < N)
+            return fail(BI_ERR_INVALID, "%s: b row stride %lld < N=%lld", fn, (long long)sk, (long long)N);
+        return BI_OK;
+    }
+    return fail(BI_ERR_UNSUPPORTED, "%s: b needs a unit stride along k or n (got %lld, %lld)", fn,
+                (long long)sk, (long long)sn);
+}
+
 bi::GemmParams make_params(const void *a, int64_t lda, const void *b, int64_t ldb, const void *c, int64_t ldc,
                            void *y, int64_t ldy, int64_t M, int64_t N, int64_t K, float alpha, float beta) {
     bi::GemmParams p{};
@@ -137,18 +158,30 @@ bi_status bi_linear(const void *x, int64_t ldx, const void *w, int64_t ldw, cons
     return device_status(bi::launch_gemm(p, in_dt, out_dt, false, (hipStream_t)stream), "bi_linear");
 }
 
-bi_status bi_matmul(const void *a, int64_t lda, const void *b, int64_t ldb, void *c, int64_t ldc, int64_t M,
-                    int64_t N, int64_t K, bi_dtype in_dt, bi_dtype out_dt, void *stream) {
-    bi_status s = check_gemm("bi_matmul", a, lda, b, ldb, true, c, ldc, M, N, K, in_dt, out_dt);
+bi_status bi_matmul(const void *a, int64_t lda, const void *b, int64_t b_stride_k, int64_t b_stride_n, void *c,
+                    int64_t ldc, int64_t M, int64_t N, int64_t K, bi_dtype in_dt, bi_dtype out_dt, void *stream) {
+    bool b_kn = true;
+    int64_t ldb = 0;
+    if (M > 0 && N > 0) {
+        bi_status r = resolve_b("bi_matmul", b_stride_k, b_stride_n, K, N, b_kn, ldb);
+        if (r != BI_OK) return r;
+    }
+    bi_status s = check_gemm("bi_matmul", a, lda, b, ldb, b_kn, c, ldc, M, N, K, in_dt, out_dt);
     if (s != BI_OK || M == 0 || N == 0) return s;
     bi::GemmParams p = make_params(a, lda, b, ldb, nullptr, 0, c, ldc, M, N, K, 1.0f, 0.0f);
-    return device_status(bi::launch_gemm(p, in_dt, out_dt, true, (hipStream_t)stream), "bi_matmul");
+    return device_status(bi::launch_gemm(p, in_dt, out_dt, b_kn, (hipStream_t)stream), "bi_matmul");
 }
 
-bi_status bi_addmm(const void *cin, int64_t ldcin, const void *a, int64_t lda, const void *b, int64_t ldb,
-                   void *out, int64_t ldo, int64_t M, int64_t N, int64_t K, float alpha, float beta,
-                   bi_dtype in_dt, bi_dtype out_dt, void *stream) {
-    bi_status s = check_gemm("bi_addmm", a, lda, b, ldb, true, out, ldo, M, N, K, in_dt, out_dt);
+bi_status bi_addmm(const void *cin, int64_t ldcin, const void *a, int64_t lda, const void *b, int64_t b_stride_k,
+                   int64_t b_stride_n, void *out, int64_t ldo, int64_t M, int64_t N, int64_t K, float alpha,
+                   float beta, bi_dtype in_dt, bi_dtype out_dt, void *stream) {
+    bool b_kn = true;
+    int64_t ldb = 0;
+    if (M > 0 && N > 0) {
+        bi_status r = resolve_b("bi_addmm", b_stride_k, b_stride_n, K, N, b_kn, ldb);
+        if (r != BI_OK) return r;
+    }
+    bi_status s = check_gemm("bi_addmm", a, lda, b, ldb, b_kn, out, ldo, M, N, K, in_dt, out_dt);
     if (s != BI_OK || M == 0 || N == 0) return s;
     if (!std::isfinite(alpha) || !std::isfinite(beta))
         return fail(BI_ERR_INVALID, "bi_addmm: alpha and beta must be finite");
@@ -164,7 +197,7 @@ bi_status bi_addmm(const void *cin, int64_t ldcin, const void *a, int64_t lda, c
         c = cin;
     }
     bi::GemmParams p = make_params(a, lda, b, ldb, c, ldcin, out, ldo, M, N, K, alpha, beta);
-    return device_status(bi::launch_gemm(p, in_dt, out_dt, true, (hipStream_t)stream), "bi_addmm");
+    return device_status(bi::launch_gemm(p, in_dt, out_dt, b_kn, (hipStream_t)stream), "bi_addmm");
 }
 
 size_t bi_sdpa_workspace_bytes(int64_t B, int64_t Hq, int64_t Lq, int64_t S, int64_t D) {

@@ -82,15 +82,18 @@ def test_gemm_validation(lib):
 
 
 def test_matmul_addmm_validation(lib):
-    # (K, N) operand: N must be a multiple of 8 for 16-bit inputs
-    assert lib.bi_matmul(P16, 64, P16b, 36, P16, 36, 4, 36, 64, BF16, BF16, None) == UNSUPPORTED
-    assert lib.bi_matmul(P16, 64, P16b, 16, P16, 32, 4, 32, 64, BF16, BF16, None) == INVALID  # ldb < N
+    # row-major (K, N) operand: N must be a multiple of 8 for 16-bit inputs
+    assert lib.bi_matmul(P16, 64, P16b, 36, 1, P16, 36, 4, 36, 64, BF16, BF16, None) == UNSUPPORTED
+    assert lib.bi_matmul(P16, 64, P16b, 16, 1, P16, 32, 4, 32, 64, BF16, BF16, None) == INVALID  # rows overlap
+    assert lib.bi_matmul(P16, 64, P16b, 1, 32, P16, 32, 4, 32, 64, BF16, BF16, None) == INVALID  # cols overlap
+    assert lib.bi_matmul(P16, 64, P16b, 2, 128, P16, 32, 4, 32, 64, BF16, BF16, None) == UNSUPPORTED
+    assert lib.bi_matmul(P16, 64, P16b, 1, 68, P16, 32, 4, 32, 64, BF16, BF16, None) == UNSUPPORTED  # pitch
     # beta != 0 needs cin; ldcin must be 0 or >= N
-    assert lib.bi_addmm(None, 0, P16, 64, P16b, 32, P16, 32, 4, 32, 64, 1.0, 1.0, BF16, BF16, None) == INVALID
-    assert lib.bi_addmm(P16, 8, P16, 64, P16b, 32, P16, 32, 4, 32, 64, 1.0, 1.0, BF16, BF16, None) == INVALID
-    assert lib.bi_addmm(P16, 0, P16, 64, P16b, 32, P16, 32, 4, 32, 64, float("nan"), 1.0, BF16, BF16,
+    assert lib.bi_addmm(None, 0, P16, 64, P16b, 32, 1, P16, 32, 4, 32, 64, 1.0, 1.0, BF16, BF16, None) == INVALID
+    assert lib.bi_addmm(P16, 8, P16, 64, P16b, 32, 1, P16, 32, 4, 32, 64, 1.0, 1.0, BF16, BF16, None) == INVALID
+    assert lib.bi_addmm(P16, 0, P16, 64, P16b, 32, 1, P16, 32, 4, 32, 64, float("nan"), 1.0, BF16, BF16,
                         None) == INVALID
-    assert lib.bi_addmm(None, 0, P16, 64, P16b, 32, P16, 32, 0, 32, 64, 1.0, 1.0, BF16, BF16, None) == OK
+    assert lib.bi_addmm(None, 0, P16, 64, P16b, 32, 1, P16, 32, 0, 32, 64, 1.0, 1.0, BF16, BF16, None) == OK
 
 
 def strides(shape):

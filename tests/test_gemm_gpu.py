@@ -53,6 +53,11 @@ def test_integer_inputs_are_exact_for_every_layout(ind, outd):
                           f"matmul M={m}")
         assert_bits_equal(bi.bi_addmm(Cg[:m], xg[:m], wt, 2.0, -1.0, out_dtype=outd).cpu(),
                           round_ref(ref_add[:m], outd), f"addmm M={m}")
+        # the same operand as a transposed view (column-major (K, N)) takes the (N, K) kernels
+        assert_bits_equal(bi.bi_matmul(xg[:m], wg.t(), out_dtype=outd).cpu(), round_ref(ref_mm[:m], outd),
+                          f"matmul, transposed view, M={m}")
+        assert_bits_equal(bi.bi_addmm(Cg[:m], xg[:m], wg.t(), 2.0, -1.0, out_dtype=outd).cpu(),
+                          round_ref(ref_add[:m], outd), f"addmm, transposed view, M={m}")
 
 
 def test_identity_permutation_and_onehot_weights():
@@ -95,10 +100,13 @@ def test_config2_bf16_linear_addmm_sweep(N):
     full = bi.bi_linear(x, w, b)
     full_add = bi.bi_addmm(b, x, wt, 1.0, 1.0)
     assert_bits_equal(full_add, full, "addmm(b row, x, W^T) == linear(x, W, b)")
+    assert_bits_equal(bi.bi_addmm(b, x, w.t(), 1.0, 1.0), full, "addmm(b row, x, W.t() view) == linear")
+    assert_bits_equal(bi.bi_matmul(x, w.t()), bi.bi_matmul(x, wt), "matmul: view == row-major copy")
     full_c = bi.bi_addmm(c, x, wt, 1.0, 1.0)
     for m in sorted(set(synthetic.CFG2["M_values"] + M_EDGES)):
         assert_bits_equal(bi.bi_linear(x[:m], w, b), full[:m], f"linear N={N} M={m}")
         assert_bits_equal(bi.bi_addmm(b, x[:m], wt, 1.0, 1.0), full[:m], f"addmm N={N} M={m}")
+        assert_bits_equal(bi.bi_addmm(b, x[:m], w.t(), 1.0, 1.0), full[:m], f"addmm view N={N} M={m}")
         assert_bits_equal(bi.bi_addmm(c[:m], x[:m], wt, 1.0, 1.0), full_c[:m], f"addmm full C N={N} M={m}")
     # single-row calls
     for r in (0, 1, 17, 100, 255):
