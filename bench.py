@@ -98,10 +98,10 @@ def main():
                 i = ctr[N] % copies[N]
                 ctr[N] += 1
                 if form == "linear":
-                    kname = lib.bi_gemm_kernel_name(M, N, 0).decode()
+                    kname = lib.bi_gemm_kernel_name(M, N, K, _native.BI_BF16, 0).decode()
                     fn = (lambda x=dN["x"][:M], w=dN["w"][i], b=dN["b"]: bi.bi_linear(x, w, b))
                 else:
-                    kname = lib.bi_gemm_kernel_name(M, N, 0).decode()
+                    kname = lib.bi_gemm_kernel_name(M, N, K, _native.BI_BF16, 0).decode()
                     fn = (lambda x=dN["x"][:M], wt=dN["wt"][i], b=dN["b"]: bi.bi_addmm(b, x, wt, 1.0, 1.0))
                 flops = 2.0 * M * N * K + M * N
                 nbytes = 2.0 * (M * K + N * K + M * N + N)
@@ -308,7 +308,7 @@ def measure_cells(bi, lib, torch, dev, synthetic, data, launches, groups, names,
             gbps = nbytes / (ms * 1e-3) / 1e9
             cells["decode_gemm"].append({"M": M, "N": N, "us": round(ms * 1e3, 2), "GBps": round(gbps, 1),
                                          "frac_hbm": round(gbps / HBM_PEAK_GBPS, 4),
-                                         "kernel": lib.bi_gemm_kernel_name(M, N, 0).decode()})
+                                         "kernel": lib.bi_gemm_kernel_name(M, N, K, bi.BI_BF16, 0).decode()})
     del wls, wl
     # large-M GEMM (added points, above the configs' M = 256)
     for N in (4096, 14336):
@@ -319,7 +319,7 @@ def measure_cells(bi, lib, torch, dev, synthetic, data, launches, groups, names,
             tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
             cells["large_m_gemm"].append({"M": M, "N": N, "us": round(ms * 1e3, 1), "TFLOPs": round(tf, 1),
                                           "frac_mfma": round(tf / BF16_PEAK_TFLOPS, 4),
-                                          "kernel": lib.bi_gemm_kernel_name(M, N, 0).decode()})
+                                          "kernel": lib.bi_gemm_kernel_name(M, N, K, bi.BI_BF16, 0).decode()})
     # decode attention on the pages' sweep shape (Hq 32, Hkv 8, D 128, bf16, q_len 1)
     for B, S in ((8, 2048), (8, 8192), (32, 8192), (32, 32768)):
         # multi-GB timing-only inputs: seeded draws on the GPU generator

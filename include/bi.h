@@ -201,7 +201,7 @@ int bi_variant_splits(int64_t M);
  * "gemm_tiled_kn/128x128", ...; b_kn != 0 for a row-major (K, N) operand of
  * bi_matmul / bi_addmm, 0 for bi_linear and for column-major operands).  Informational: every configuration computes the same bits.
  * Returns "none" for empty or oversized shapes. */
-const char *bi_gemm_kernel_name(int64_t M, int64_t N, int b_kn);
+const char *bi_gemm_kernel_name(int64_t M, int64_t N, int64_t K, bi_dtype in_dt, int b_kn);
 
 /* Name of a status code ("BI_OK", ...); never NULL. */
 const char *bi_status_name(bi_status s);

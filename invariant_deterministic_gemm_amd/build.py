@@ -17,7 +17,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libbi.so")
-SOURCES = ["api.hip", "gemm.hip", "sdpa.hip"]
+SOURCES = ["api.hip", "gemm.hip", "gemm32.hip", "sdpa.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 

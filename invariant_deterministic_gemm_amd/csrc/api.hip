@@ -309,9 +309,10 @@ bi_status bi_variant_linear(const void *x, int64_t ldx, const void *w, int64_t l
                          "bi_variant_linear");
 }
 
-const char *bi_gemm_kernel_name(int64_t M, int64_t N, int b_kn) {
-    if (M <= 0 || N <= 0 || M > kMaxDim || N > kMaxDim) return "none";
-    return bi::gemm_kernel_name((int)M, (int)N, b_kn != 0);
+const char *bi_gemm_kernel_name(int64_t M, int64_t N, int64_t K, bi_dtype in_dt, int b_kn) {
+    if (M <= 0 || N <= 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim || !dtype_known(in_dt))
+        return "none";
+    return bi::gemm_kernel_name((int)M, (int)N, (int)K, (int)in_dt, b_kn != 0);
 }
 
 const char *bi_status_name(bi_status s) {

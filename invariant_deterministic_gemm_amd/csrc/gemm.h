@@ -34,7 +34,7 @@ hipError_t launch_gemm_splitk(const GemmParams &p, int in_dt, int out_dt, int sp
                               hipStream_t stream);
 
 // Name of the kernel configuration launch_gemm picks ("gemm_skinny_nk/fm1", ...).
-const char *gemm_kernel_name(int M, int N, bool b_kn);
+const char *gemm_kernel_name(int M, int N, int K, int in_dt, bool b_kn);
 
 // Number of k steps (one 16-byte chunk per lane each) a K of this dtype needs.
 int gemm_k_steps(int K, int in_dt);

@@ -1,4 +1,6 @@
-// Batch-invariant GEMM kernels for gfx950.
+// Batch-invariant GEMM kernels for fp32 inputs on gfx950, the split-K
+// comparator's reduce, and the host dispatch for every dtype (16-bit inputs
+// run the 32x32x16 kernels of gemm32.hip).
 //
 // Method (mlx-batch-invariant README, section "How the kernels work", GEMM
 // paragraph): one workgroup owns the entire reduction over K, the trip count
@@ -25,55 +27,14 @@
 // the same epilogue
 //      y = round_out( fmaf(alpha, acc, beta * c) ).
 
+#include <cstdio>
+
 #include "device.h"
 #include "gemm.h"
+#include "gemm_common.h"
+#include "gemm32.h"
 
 namespace bi {
-
-template <int dt> struct Chunk {
-    static constexpr int EB = Elem<dt>::bytes;
-    static constexpr int EPC = 16 / EB;     // elements per 16-byte chunk
-    static constexpr int CK = 4 * EPC;      // k per step (four lane groups)
-};
-
-// One step of the chain for one 16x16 output fragment.
-template <int dt>
-__device__ __forceinline__ f32x4 mfma_chunk(u32x4 a, u32x4 b, f32x4 c) {
-    if constexpr (dt == DT_F32) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-            c = Mfma<DT_F32>::step(__uint_as_float(a[u]), __uint_as_float(b[u]), c);
-        return c;
-    } else {
-        return Mfma<dt>::step(a, b, c);
-    }
-}
-
-// Epilogue for one element: one fp32 fma with the C / bias term, one rounding.
-template <int odt>
-__device__ __forceinline__ void epilogue(const GemmParams &p, int m, int n, float acc) {
-    float t = 0.0f;
-    if (p.C != nullptr) {
-        const float c = load_as_f32<odt>(p.C, (int64_t)m * p.ldc + n);
-        t = p.beta * c;
-    }
-    store_from_f32<odt>(p.Y, (int64_t)m * p.ldy + n, __builtin_fmaf(p.alpha, acc, t));
-}
-
-template <int odt>
-__device__ __forceinline__ void finish(const GemmParams &p, int split, int m, int n, float acc) {
-    if (p.splits > 1) {
-        p.partial[((int64_t)split * p.M + m) * p.N + n] = acc;
-    } else {
-        epilogue<odt>(p, m, n, acc);
-    }
-}
-
-// k steps covered by one split (the whole chain when splits == 1).
-__device__ __forceinline__ void split_range(const GemmParams &p, int split, int &sb, int &se) {
-    sb = (int)((int64_t)p.total_steps * split / p.splits);
-    se = (int)((int64_t)p.total_steps * (split + 1) / p.splits);
-}
 
 // ============================================================ skinny kernels
 // One wavefront per 16-column strip of the output, all M <= 16 * FM rows.
@@ -415,29 +376,27 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce(GemmParams p, const fl
 
 // ============================================================ host dispatch
 int gemm_k_steps(int K, int in_dt) {
-    const int ck = (in_dt == DT_F32) ? 16 : 32;
-    return (K + ck - 1) / ck;
+    (void)in_dt;                 // 16 k per step for every dtype (one 16-byte chunk per lane)
+    return (K + 15) / 16;
 }
 
-// Kernel configuration for a problem.  Every configuration runs the same
-// per-element chain, so this choice is free to look at M (occupancy); it is
-// the only place the selection rule lives.
-struct GemmPlan {
-    int kind;      // 0 = skinny (one wave per 16 columns), 1 = tiled
-    int fm;        // skinny: 16-row fragments per wave
-    int bm, bn;    // tiled: workgroup tile
+// fp32 inputs: 16x16x4 chain (skinny kernel for M <= 64, LDS-tiled above).
+// Every configuration runs the same per-element chain; M only picks occupancy.
+struct GemmPlan16 {
+    int kind;          // 0 = skinny (one wave per 16 columns), 1 = LDS-tiled
+    int fm;            // skinny: 16-row fragments per wave
+    int bm;            // tiled: square tile
 };
 
-static GemmPlan plan_gemm(int M, int N) {
-    if (M <= 64) return GemmPlan{0, (M + 15) / 16 > 0 ? (M + 15) / 16 : 1, 0, 0};
+static GemmPlan16 plan16(int M, int N) {
+    if (M <= 64) return GemmPlan16{0, (M + 15) / 16 > 0 ? (M + 15) / 16 : 1, 0};
     const long tiles128 = (long)((M + 127) / 128) * ((N + 127) / 128);
-    if (tiles128 >= 256) return GemmPlan{1, 0, 128, 128};
-    return GemmPlan{1, 0, 64, 64};
+    return GemmPlan16{1, 0, tiles128 >= 256 ? 128 : 64};
 }
 
-template <int idt, int odt>
-static hipError_t launch_typed(const GemmParams &p, bool b_kn, hipStream_t st) {
-    const GemmPlan pl = plan_gemm(p.M, p.N);
+static hipError_t launch_f32(const GemmParams &p, bool b_kn, hipStream_t st) {
+    constexpr int idt = DT_F32, odt = DT_F32;
+    const GemmPlan16 pl = plan16(p.M, p.N);
     const unsigned sp = (unsigned)p.splits;
     if (pl.kind == 0) {
         const dim3 grid((p.N + 15) / 16, sp), block(64);
@@ -467,38 +426,35 @@ static hipError_t launch_typed(const GemmParams &p, bool b_kn, hipStream_t st) {
     return hipGetLastError();
 }
 
-const char *gemm_kernel_name(int M, int N, bool b_kn) {
-    const GemmPlan pl = plan_gemm(M, N);
-    static const char *skinny[2][4] = {
-        {"gemm_skinny_nk/fm1", "gemm_skinny_nk/fm2", "gemm_skinny_nk/fm3", "gemm_skinny_nk/fm4"},
-        {"gemm_skinny_kn/fm1", "gemm_skinny_kn/fm2", "gemm_skinny_kn/fm3", "gemm_skinny_kn/fm4"}};
-    if (pl.kind == 0) return skinny[b_kn ? 1 : 0][pl.fm - 1];
-    if (pl.bm == 128) return b_kn ? "gemm_tiled_kn/128x128" : "gemm_tiled_nk/128x128";
-    return b_kn ? "gemm_tiled_kn/64x64" : "gemm_tiled_nk/64x64";
+const char *gemm_kernel_name(int M, int N, int K, int in_dt, bool b_kn) {
+    if (in_dt != DT_F32) return gemm32_kernel_name(M, N, K, b_kn, 1);
+    const GemmPlan16 pl = plan16(M, N);
+    static thread_local char buf[64];
+    if (pl.kind == 0) snprintf(buf, sizeof buf, "gemm_skinny_%s/fm%d", b_kn ? "kn" : "nk", pl.fm);
+    else snprintf(buf, sizeof buf, "gemm_tiled_%s/%dx%d", b_kn ? "kn" : "nk", pl.bm, pl.bm);
+    return buf;
 }
 
-template <int idt, int odt>
-static hipError_t dispatch(const GemmParams &p0, bool b_kn, int splits, float *ws, hipStream_t st) {
+static hipError_t dispatch_dt(const GemmParams &p0, int in_dt, int out_dt, bool b_kn, int splits, float *ws,
+                              hipStream_t st) {
     GemmParams p = p0;
-    p.total_steps = gemm_k_steps(p.K, idt);
+    p.total_steps = gemm_k_steps(p.K, in_dt);
     p.splits = splits;
     p.partial = splits > 1 ? ws : nullptr;
-    hipError_t e = launch_typed<idt, odt>(p, b_kn, st);
+    hipError_t e;
+    if (in_dt == DT_F32) {
+        if (out_dt != DT_F32) return hipErrorInvalidValue;
+        e = launch_f32(p, b_kn, st);
+    } else {
+        e = launch_gemm32(p, in_dt, out_dt, b_kn, st);
+    }
     if (e != hipSuccess || splits <= 1) return e;
     const int64_t total = (int64_t)p.M * p.N;
-    hipLaunchKernelGGL((gemm_splitk_reduce<odt>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
-                       p, (const float *)ws, splits);
+    const dim3 grid((unsigned)((total + 255) / 256));
+    if (out_dt == DT_F32) hipLaunchKernelGGL((gemm_splitk_reduce<DT_F32>), grid, dim3(256), 0, st, p, (const float *)ws, splits);
+    else if (out_dt == DT_BF16) hipLaunchKernelGGL((gemm_splitk_reduce<DT_BF16>), grid, dim3(256), 0, st, p, (const float *)ws, splits);
+    else hipLaunchKernelGGL((gemm_splitk_reduce<DT_F16>), grid, dim3(256), 0, st, p, (const float *)ws, splits);
     return hipGetLastError();
-}
-
-static hipError_t dispatch_dt(const GemmParams &p, int in_dt, int out_dt, bool b_kn, int splits, float *ws,
-                              hipStream_t st) {
-    if (in_dt == DT_F32 && out_dt == DT_F32) return dispatch<DT_F32, DT_F32>(p, b_kn, splits, ws, st);
-    if (in_dt == DT_BF16 && out_dt == DT_BF16) return dispatch<DT_BF16, DT_BF16>(p, b_kn, splits, ws, st);
-    if (in_dt == DT_F16 && out_dt == DT_F16) return dispatch<DT_F16, DT_F16>(p, b_kn, splits, ws, st);
-    if (in_dt == DT_BF16 && out_dt == DT_F32) return dispatch<DT_BF16, DT_F32>(p, b_kn, splits, ws, st);
-    if (in_dt == DT_F16 && out_dt == DT_F32) return dispatch<DT_F16, DT_F32>(p, b_kn, splits, ws, st);
-    return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm(const GemmParams &p, int in_dt, int out_dt, bool b_kn, hipStream_t st) {

@@ -252,3 +252,26 @@ def test_splitk_comparator_is_correct_but_batch_variant():
     assert diffs > 0, "negative control: M-keyed split-K must change some bits"
     # and with one split it is the invariant kernel itself
     assert_bits_equal(bi.bi_variant_linear(x[:8], w, b, splits=1), bi.bi_linear(x[:8], w, b), "splits=1")
+
+
+@pytest.mark.parametrize("N", [4096, 14336])
+def test_large_m_rows_match_small_m_calls(N):
+    """Rows of big-M calls (256x256 / 256x224 / 128x128 / 64x64 tiles) equal the same rows computed
+    by small-M calls (skinny kernel) and stay within the oracle gate."""
+    K = 4096
+    x = synthetic.randn((4096, K), 0x5EED3A, 1.0, torch.bfloat16).to(DEV)
+    w = synthetic.randn((N, K), 0x5EED3B, 0.02, torch.bfloat16).to(DEV)
+    b = synthetic.randn((N,), 0x5EED3C, 1.0, torch.bfloat16).to(DEV)
+    lib = bi._native.load()
+    full = bi.bi_linear(x, w, b)
+    seen = set()
+    for m in (4096, 2048, 1024, 777, 512, 300, 129, 65, 64, 16, 1):
+        seen.add(lib.bi_gemm_kernel_name(m, N, K, bi.BI_BF16, 0).decode())
+        y = bi.bi_linear(x[:m], w, b)
+        assert_bits_equal(y, full[:m], f"N={N} M={m}")
+    for r0 in (0, 255, 256, 1000, 4095):
+        assert_bits_equal(bi.bi_linear(x[r0:r0 + 1], w, b), full[r0:r0 + 1], f"N={N} row {r0} alone")
+    assert len(seen) >= 3, seen
+    rows = [0, 255, 256, 2049, 4095]
+    ref = oracle.linear(x[rows].cpu(), w.cpu(), b.cpu())
+    assert_close_to_oracle(full[rows].cpu(), ref, f"large M, N={N}")
