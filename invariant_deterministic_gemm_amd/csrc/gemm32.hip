@@ -4,13 +4,17 @@
 // paragraph): the whole K reduction of an output element stays in one place
 // with a trip count that depends on K alone; no split-K, no atomics, fp32
 // accumulation, bias added in fp32 and rounded once.  The chain itself is
-// described in gemm32.h.  Three kernels run it:
-//   gemm32_skinny_{nk,kn}  one wavefront per 32-column strip, M <= 64;
+// described in gemm32.h.  Four kernels run it:
+//   gemm32_strip           M <= 64, (N, K) layout: four wavefronts per strip of
+//                          16 or 32 columns feeding one chain per fragment;
+//   gemm32_skinny_{nk,kn}  one wavefront per 32-column strip, M <= 64 (the
+//                          (K, N) layout and the split-K comparator);
 //   gemm32_tile            LDS-tiled, register-staged loads (any layout, any K,
 //                          and the split-K comparator);
 //   gemm32_ring            LDS-tiled with direct-to-LDS loads through a ring of
 //                          stages, (N, K) layout, K a multiple of 32: the
 //                          large-M path.
+#include <algorithm>
 #include <cstdio>
 
 #include "gemm32.h"
@@ -169,6 +173,157 @@ __global__ __launch_bounds__(64) void gemm32_skinny_kn(GemmParams p) {
                 const int m = 32 * f + frag_row(r, h);
                 if (m < p.M) finish<odt>(p, split, m, n, acc[f][r]);
             }
+    }
+}
+
+// ============================================================ cooperative strip kernel
+// Small M with B in the (N, K) layout.  One workgroup of four wavefronts per
+// strip of SW output columns (SW = 32, or 16 with fragment columns 16..31
+// repeating 0..15, which doubles the number of workgroups for narrow N and
+// leaves every column's chain unchanged): all four stream the strip's weight
+// rows and AR rows of A into an LDS ring with direct-to-LDS loads, so many more
+// bytes are in flight per strip than one wavefront can keep outstanding; the
+// wavefront that owns 32-row fragment f (f < FM) runs the chain for it out of
+// LDS, reading stage t + 1 while the MFMAs of stage t run.
+// A stage covers 128 k: SW B rows then AR A rows, 256 bytes each, chunk c of
+// row r at slot c ^ (r & 15) (16 consecutive rows of one chunk hit 16 distinct
+// bank groups).  Load instruction q moves rows 4q .. 4q+3 of the stage (1 KiB);
+// wave w issues instructions w, w + 4, ... (waves below Q mod 4 issue one more,
+// and wait with their own vmcnt thresholds).  Chunks past K are fetched from a
+// clamped in-bounds address and replaced by zeros when read, and steps past
+// the end of the chain are not run (an extra zero step could turn -0 into +0).
+template <int idt, int odt, int SW, int FM, int AR, int NS>
+__global__ __launch_bounds__(256) void gemm32_strip(GemmParams p) {
+    constexpr int NW = 4;
+    constexpr int ROWB = 256;
+    constexpr int QB = SW / 4, QA = AR / 4, Q = QB + QA;
+    constexpr int QHI = (Q + NW - 1) / NW, QLO = Q / NW, NHI = Q % NW;
+    constexpr int STAGE = Q * 1024;
+    static_assert(SW == 16 || SW == 32, "strip width");
+    static_assert(AR % 4 == 0 && AR >= 4 && AR <= 32 * FM, "A rows per stage");
+    static_assert(NS >= 2 && QHI * (NS - 1) <= 63, "vmcnt range");
+    __shared__ __attribute__((aligned(1024))) char lds[NS * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int n0 = blockIdx.x * SW;
+    const int nchunk = p.K >> 3;                 // 16-byte chunks per row
+    const int nstages = (p.K + 127) >> 7;
+    const int total_steps = p.total_steps;
+    const int myq = wave < NHI ? QHI : QLO;
+
+    // load side: lane L of instruction q covers stage row 4 q + L / 16, slot L mod 16
+    const char *src[QHI];
+    int cl[QHI];
+#pragma unroll
+    for (int j = 0; j < QHI; ++j) {
+        const int q = min(wave + NW * j, Q - 1);
+        const int row = 4 * q + (lane >> 4);
+        cl[j] = (lane & 15) ^ (row & 15);
+        if (row < SW)
+            src[j] = static_cast<const char *>(p.B) + (int64_t)min(n0 + row, p.N - 1) * p.ldb * 2;
+        else
+            src[j] = static_cast<const char *>(p.A) + (int64_t)min(row - SW, p.M - 1) * p.lda * 2;
+    }
+    auto issue = [&](int stage) {
+        char *buf = lds + (stage % NS) * STAGE;
+#pragma unroll
+        for (int j = 0; j < QHI; ++j) {
+            if (j < myq) {
+                const int q = wave + NW * j;
+                const int g = min(stage * 16 + cl[j], nchunk - 1);
+                __builtin_amdgcn_global_load_lds(static_cast<const void *>(src[j] + (int64_t)g * 16),
+                                                 BI_LDS_PTR(buf + q * 1024), 16, 0, 0);
+            }
+        }
+    };
+    // wait until at most `keep` (NS - 1, NS - 2 or 0) of this wave's stages are in flight
+    auto wait_keep = [&](int keep) {
+        if (wave < NHI) {
+            if (keep == NS - 1) BI_WAIT_VMCNT(QHI * (NS - 1));
+            else if (keep == NS - 2) BI_WAIT_VMCNT(QHI * (NS - 2));
+            else BI_WAIT_VMCNT(0);
+        } else {
+            if (keep == NS - 1) BI_WAIT_VMCNT(QLO * (NS - 1));
+            else if (keep == NS - 2) BI_WAIT_VMCNT(QLO * (NS - 2));
+            else BI_WAIT_VMCNT(0);
+        }
+    };
+
+    // consume side
+    const int r32 = lane & 31, h = lane >> 5;
+    const bool consumer = wave < FM;
+    const int arow = SW + min(32 * wave + r32, AR - 1);
+    const int brow = r32 & (SW - 1);
+    const int aoff = arow * ROWB, boff = brow * ROWB;
+    const int aswz = arow & 15, bswz = brow & 15;
+    f32x16 acc = zero16();
+    u32x4 fa[8], fb[8];
+    auto frag = [&](int stage, int u, u32x4 &a, u32x4 &b) {
+        const char *buf = lds + (stage % NS) * STAGE;
+        const int c = 2 * u + h;
+        a = *reinterpret_cast<const u32x4 *>(buf + aoff + ((c ^ aswz) << 4));
+        b = *reinterpret_cast<const u32x4 *>(buf + boff + ((c ^ bswz) << 4));
+    };
+    // the eight steps of a full stage, each followed by the read of the same
+    // step of the next stage into the registers it just consumed
+    auto mma_then_read = [&](int stage) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            acc = Mfma32<idt>::step(fa[u], fb[u], acc);
+            frag(stage + 1, u, fa[u], fb[u]);
+        }
+    };
+    // the last stage: only steps of the chain, chunks past K read as zero
+    auto mma_last = [&](int stage) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (stage * 8 + u < total_steps) {
+                const bool past = stage * 16 + 2 * u + h >= nchunk;
+                acc = Mfma32<idt>::step(past ? zero_u4() : fa[u], past ? zero_u4() : fb[u], acc);
+            }
+        }
+    };
+
+    // prologue: all NS buffers in flight, stage 0 landed everywhere and read
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+        if (s < nstages) issue(s);
+    if (nstages > 0) {
+        wait_keep(nstages >= NS ? NS - 1 : 0);
+        __builtin_amdgcn_s_barrier();
+        if (consumer) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) frag(0, u, fa[u], fb[u]);
+        }
+    }
+    // iteration t: stage t + 1 has landed (at most NS - 2 stages still in
+    // flight) and every wave's reads of stage t are done, so the buffer of
+    // stage t is refilled with stage t + NS; then the MFMAs of stage t run
+    // while stage t + 1 is read.  Only the last stage can be partial.
+    int t = 0;
+    for (; t < nstages - NS; ++t) {
+        wait_keep(NS - 2);
+        __builtin_amdgcn_s_waitcnt(0xc07f);          // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        issue(t + NS);
+        if (consumer) mma_then_read(t);
+    }
+    for (; t < nstages - 1; ++t) {
+        BI_WAIT_VMCNT(0);
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_s_barrier();
+        if (consumer) mma_then_read(t);
+    }
+    if (nstages > 0 && consumer) mma_last(nstages - 1);
+    if (!consumer) return;
+    const int n = n0 + r32;
+    if (r32 < SW && n < p.N) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int m = 32 * wave + frag_row(r, h);
+            if (m < p.M) epilogue<odt>(p, m, n, acc[r]);
+        }
     }
 }
 
@@ -379,30 +534,36 @@ __device__ __forceinline__ void store_tile_staged(const GemmParams &p, const f32
 }
 
 // ============================================================ deep-ring kernel
-// (N, K) layout, K a multiple of 32, no split.  NS LDS stages of 32 k each (64-byte
-// LDS rows, 4 chunks, slot = c ^ ((row >> 2) & 3): 16 consecutive rows hit 16
-// distinct bank groups), all NS stages in flight with manual vmcnt waits and
-// raw barriers, and the fragment reads of one step overlapping the MFMAs of
-// the other:
+// (N, K) layout, K a multiple of KS, no split.  NS LDS stages of KS k each
+// (KS = 32: 64-byte LDS rows; KS = 64: 128-byte rows).  Within a 256-byte bank
+// window of RPW = 256 / row-bytes rows, chunk c of row r sits at slot
+// c ^ ((r / RPW) mod chunks-per-row), so the 16 rows one ds_read_b128 pass
+// serves hit 16 distinct bank groups.  All NS stages are in flight with manual
+// vmcnt waits and raw barriers, and the fragment reads of each step overlap
+// the MFMAs of the one before:
 //   iteration t (step-0 fragments of stage t already in registers):
-//     read step-1 fragments of stage t; MFMAs of step 0;
+//     for each step u but the last: read step u + 1 of stage t; MFMAs of u;
 //     wait for this wave's loads of stage t + 1; barrier (now every wave has
 //     finished reading stage t and stage t + 1 has landed everywhere);
-//     issue stage t + NS into the buffer stage t used; read step-0 fragments of
-//     stage t + 1; MFMAs of step 1.
-// PIPE = 0 selects the plain order instead (wait, barrier, refill, read and
-// multiply the current stage).  Every wave issues exactly QW loads per stage,
-// so the vmcnt thresholds are exact.
-template <int idt, int odt, int BM, int BN, int WGM, int WGN, int NS, int PIPE = 1>
+//     issue stage t + NS into the buffer stage t used; read step 0 of stage
+//     t + 1; MFMAs of the last step.
+// Every wave issues exactly QW loads per stage, so the vmcnt thresholds are exact.
+template <int idt, int odt, int BM, int BN, int WGM, int WGN, int NS, int KS = 32>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm32_ring(GemmParams p) {
     constexpr int NW = WGM * WGN;
     constexpr int WM = BM / WGM, WN = BN / WGN;
     constexpr int FM = WM / 32, FN = WN / 32;
-    constexpr int ROWB = 64;
+    constexpr int ROWB = KS * 2;
+    constexpr int CPR = ROWB / 16;                   // chunks per row
+    constexpr int RPW = 256 / ROWB;                  // rows per 256-byte bank window
+    constexpr int RPI = 1024 / ROWB;                 // rows per 1 KiB load instruction
+    constexpr int SPS = KS / 16;                     // chain steps per stage
     constexpr int STAGE = (BM + BN) * ROWB;
-    constexpr int QA = BM / 16, QB = BN / 16;        // 1 KiB load instructions (16 rows) per stage
+    constexpr int QA = BM / RPI, QB = BN / RPI;
     constexpr int QW = (QA + QB) / NW;
+    static_assert(KS == 32 || KS == 64, "stage width");
     static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile");
+    static_assert(BM % RPI == 0 && BN % RPI == 0, "whole load instructions");
     static_assert((QA + QB) % NW == 0, "every wave must issue the same number of loads per stage");
     static_assert(NS >= 2 && QW * (NS - 1) <= 63, "vmcnt range");
     __shared__ __attribute__((aligned(1024))) char lds[NS * STAGE];
@@ -416,14 +577,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm32_ring(GemmParams p) {
     int tm, tn;
     tile_coords(blockIdx.x, ntm, ntn, 8, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
-    const int nstages = p.total_steps / 2;
+    const int nstages = p.total_steps / SPS;
 
     const char *src[QW];
 #pragma unroll
     for (int j = 0; j < QW; ++j) {
         const int q = wave + NW * j;
-        const int rloc = (q < QA ? q : q - QA) * 16 + (lane >> 2);
-        const int c = (lane & 3) ^ ((rloc >> 2) & 3);
+        const int rloc = (q < QA ? q : q - QA) * RPI + lane / CPR;
+        const int c = (lane % CPR) ^ ((rloc / RPW) % CPR);
         if (q < QA)
             src[j] = static_cast<const char *>(p.A) + (int64_t)min(m0 + rloc, p.M - 1) * p.lda * 2 + c * 16;
         else
@@ -446,12 +607,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm32_ring(GemmParams p) {
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
             const int row = wm * WM + 32 * i + r32;
-            af[i] = *reinterpret_cast<const u32x4 *>(As + row * ROWB + ((c ^ ((row >> 2) & 3)) << 4));
+            af[i] = *reinterpret_cast<const u32x4 *>(As + row * ROWB + ((c ^ ((row / RPW) % CPR)) << 4));
         }
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
             const int row = wn * WN + 32 * j + r32;
-            bfr[j] = *reinterpret_cast<const u32x4 *>(Bs + row * ROWB + ((c ^ ((row >> 2) & 3)) << 4));
+            bfr[j] = *reinterpret_cast<const u32x4 *>(Bs + row * ROWB + ((c ^ ((row / RPW) % CPR)) << 4));
         }
     };
     f32x16 acc[FM][FN];
@@ -466,68 +627,45 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm32_ring(GemmParams p) {
             for (int j = 0; j < FN; ++j) acc[i][j] = Mfma32<idt>::step(af[i], bfr[j], acc[i][j]);
     };
 
-    if constexpr (PIPE == 0) {
-        // plain order: wait for stage t, barrier, refill the buffer stage t - 1 used, read and multiply stage t
-#pragma unroll
-        for (int s = 0; s < NS - 1; ++s)
-            if (s < nstages) issue(s);
-        const int steady = nstages - (NS - 1);
-        int t = 0;
-        for (; t < steady; ++t) {
-            BI_WAIT_VMCNT(QW * (NS - 2));
-            __builtin_amdgcn_s_barrier();
-            issue(t + NS - 1);
-            u32x4 a0[FM], b0[FN], a1[FM], b1[FN];
-            read_step(t, 0, a0, b0);
-            mma(a0, b0);
-            read_step(t, 1, a1, b1);
-            mma(a1, b1);
-        }
-        for (; t < nstages; ++t) {
-            BI_WAIT_VMCNT(0);
-            __builtin_amdgcn_s_barrier();
-            u32x4 a0[FM], b0[FN], a1[FM], b1[FN];
-            read_step(t, 0, a0, b0);
-            mma(a0, b0);
-            read_step(t, 1, a1, b1);
-            mma(a1, b1);
-        }
-        __builtin_amdgcn_s_waitcnt(0xc07f);
-    } else {
     // prologue: stages 0 .. NS-1 in flight; stage 0 landed everywhere; its step 0 read
 #pragma unroll
-        for (int s = 0; s < NS; ++s)
-            if (s < nstages) issue(s);
-        u32x4 a0[FM], b0[FN], a1[FM], b1[FN];
-        if (nstages > 0) {
-            if (nstages >= NS) BI_WAIT_VMCNT(QW * (NS - 1));
-            else BI_WAIT_VMCNT(0);
-            __builtin_amdgcn_s_barrier();
-            read_step(0, 0, a0, b0);
+    for (int s = 0; s < NS; ++s)
+        if (s < nstages) issue(s);
+    u32x4 fa[2][FM], fb[2][FN];
+    if (nstages > 0) {
+        if (nstages >= NS) BI_WAIT_VMCNT(QW * (NS - 1));
+        else BI_WAIT_VMCNT(0);
+        __builtin_amdgcn_s_barrier();
+        read_step(0, 0, fa[0], fb[0]);
+    }
+    // steady state: every iteration issues stage t + NS and may leave NS - 2 stages in flight
+    const int steady = nstages - NS;
+    int t = 0;
+    for (; t < steady; ++t) {
+#pragma unroll
+        for (int u = 0; u < SPS - 1; ++u) {
+            read_step(t, u + 1, fa[(u + 1) & 1], fb[(u + 1) & 1]);
+            mma(fa[u & 1], fb[u & 1]);
         }
-        // steady state: every iteration issues stage t + NS and may leave NS - 2 stages in flight
-        const int steady = nstages - NS;
-        int t = 0;
-        for (; t < steady; ++t) {
-            read_step(t, 1, a1, b1);
-            mma(a0, b0);
-            BI_WAIT_VMCNT(QW * (NS - 2));
-            __builtin_amdgcn_s_waitcnt(0xc07f);          // lgkmcnt(0): this wave's LDS reads of stage t are done
-            __builtin_amdgcn_s_barrier();
-            issue(t + NS);
-            read_step(t + 1, 0, a0, b0);
-            mma(a1, b1);
+        BI_WAIT_VMCNT(QW * (NS - 2));
+        __builtin_amdgcn_s_waitcnt(0xc07f);          // lgkmcnt(0): this wave's LDS reads of stage t are done
+        __builtin_amdgcn_s_barrier();
+        issue(t + NS);
+        read_step(t + 1, 0, fa[SPS & 1], fb[SPS & 1]);
+        mma(fa[(SPS - 1) & 1], fb[(SPS - 1) & 1]);
+    }
+    // tail: nothing left to issue; drain
+    for (; t < nstages; ++t) {
+#pragma unroll
+        for (int u = 0; u < SPS - 1; ++u) {
+            read_step(t, u + 1, fa[(u + 1) & 1], fb[(u + 1) & 1]);
+            mma(fa[u & 1], fb[u & 1]);
         }
-        // tail: nothing left to issue; drain
-        for (; t < nstages; ++t) {
-            read_step(t, 1, a1, b1);
-            mma(a0, b0);
-            BI_WAIT_VMCNT(0);
-            __builtin_amdgcn_s_waitcnt(0xc07f);
-            __builtin_amdgcn_s_barrier();
-            if (t + 1 < nstages) read_step(t + 1, 0, a0, b0);
-            mma(a1, b1);
-        }
+        BI_WAIT_VMCNT(0);
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_s_barrier();
+        if (t + 1 < nstages) read_step(t + 1, 0, fa[SPS & 1], fb[SPS & 1]);
+        mma(fa[(SPS - 1) & 1], fb[(SPS - 1) & 1]);
     }
     if constexpr (BM * BN * Elem<odt>::bytes <= NS * STAGE) {
         store_tile_staged<odt, BM, BN, WGM, WGN>(p, acc, m0, n0, lds);
@@ -549,30 +687,58 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm32_ring(GemmParams p) {
 
 // ============================================================ plan + launch
 struct Plan32 {
-    int kind;                 // 0 skinny, 1 register-staged tile, 2 deep-ring tile
-    int fm;                   // skinny fragments
+    int kind;                 // 0 skinny, 1 register-staged tile, 2 deep-ring tile, 3 cooperative strip
+    int fm;                   // skinny / strip fragments
     int bm, bn;               // tile
 };
 
-// Deep-ring tiles and a rough relative per-tile efficiency (bigger tiles reuse
-// more data per byte moved); used only to pick a tile, never changes bits.
-struct Cfg32 { int bm, bn; float eff; };
-static const Cfg32 kRing32[] = {{256, 256, 1.0f}, {128, 128, 0.8f}, {64, 64, 0.5f}};
+// Deep-ring tiles, largest first.  The plan takes the largest tile that still
+// yields about one tile per CU (192 of 256), else the smallest: below that the
+// chip is short of waves, above it bigger tiles move fewer bytes per flop.
+// Used only to pick a kernel, never changes bits.
+struct Cfg32 { int bm, bn; };
+static const Cfg32 kRing32[] = {{256, 256}, {256, 128}, {128, 128}, {128, 64}, {64, 64}};
+constexpr long kRingMinTiles = 192;
+
+// Strip instantiations (width, fragments, A rows per stage, stages) and the
+// LDS each takes; used only to pick a kernel, never changes bits.
+struct StripCfg { int sw, fm, ar, ns; };
+static StripCfg strip_cfg(int M, int sw) {
+    if (M <= 16) return sw == 16 ? StripCfg{16, 1, 16, 6} : StripCfg{32, 1, 16, 6};
+    if (M <= 32) return sw == 16 ? StripCfg{16, 1, 32, 4} : StripCfg{32, 1, 32, 5};
+    return StripCfg{32, 2, 64, 4};
+}
+static int strip_width(int M, int N) {
+    if (M > 16) return 32;
+    // workgroup rounds times strip width: a proxy for time when the weight
+    // stream is shared evenly; ties go to the wider strip (less A re-reading)
+    long best_cost = -1;
+    int best = 32;
+    for (int sw : {32, 16}) {
+        const StripCfg c = strip_cfg(M, sw);
+        const long lds = (long)c.ns * (c.sw + c.ar) * 256;
+        const long per_cu = std::min(3L, (160L * 1024) / lds);
+        const long wgs = (N + sw - 1) / sw;
+        const long cost = ((wgs + 256 * per_cu - 1) / (256 * per_cu)) * sw;
+        if (best_cost < 0 || cost < best_cost) {
+            best_cost = cost;
+            best = sw;
+        }
+    }
+    return best;
+}
 
 static Plan32 plan32(int M, int N, int K, bool b_kn, int splits) {
-    if (M <= 64) return Plan32{0, M <= 32 ? 1 : 2, 0, 0};
-    if (!b_kn && splits == 1 && K % 32 == 0) {
-        float best = -1.0f;
-        Plan32 pl{};
+    if (M <= 64) {
+        if (!b_kn && splits == 1) return Plan32{3, M <= 32 ? 1 : 2, M, strip_width(M, N)};
+        return Plan32{0, M <= 32 ? 1 : 2, 0, 0};
+    }
+    if (!b_kn && splits == 1 && K % 64 == 0) {
         for (const Cfg32 &c : kRing32) {
             const long tiles = (long)((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
-            const float cost = (float)((tiles + 255) / 256) * (float)(c.bm * c.bn) / c.eff;
-            if (best < 0.0f || cost < best) {
-                best = cost;
-                pl = Plan32{2, 0, c.bm, c.bn};
-            }
+            if (tiles >= kRingMinTiles) return Plan32{2, 0, c.bm, c.bn};
         }
-        return pl;
+        return Plan32{2, 0, 64, 64};
     }
     const long tiles128 = (long)((M + 127) / 128) * ((N + 127) / 128);
     if (tiles128 >= 256) return Plan32{1, 0, 128, 128};
@@ -594,14 +760,31 @@ static hipError_t launch32_typed(const GemmParams &p, bool b_kn, hipStream_t st)
         }
         return hipGetLastError();
     }
+    if (pl.kind == 3) {
+        const StripCfg c = strip_cfg(p.M, pl.bn);
+        const dim3 grid((p.N + c.sw - 1) / c.sw), block(256);
+        if (c.sw == 16) {
+            if (c.ar == 16) hipLaunchKernelGGL((gemm32_strip<idt, odt, 16, 1, 16, 6>), grid, block, 0, st, p);
+            else hipLaunchKernelGGL((gemm32_strip<idt, odt, 16, 1, 32, 4>), grid, block, 0, st, p);
+        } else {
+            if (c.ar == 16) hipLaunchKernelGGL((gemm32_strip<idt, odt, 32, 1, 16, 6>), grid, block, 0, st, p);
+            else if (c.ar == 32) hipLaunchKernelGGL((gemm32_strip<idt, odt, 32, 1, 32, 5>), grid, block, 0, st, p);
+            else hipLaunchKernelGGL((gemm32_strip<idt, odt, 32, 2, 64, 4>), grid, block, 0, st, p);
+        }
+        return hipGetLastError();
+    }
     if (pl.kind == 2) {
         const unsigned tiles = (unsigned)(((p.M + pl.bm - 1) / pl.bm) * ((p.N + pl.bn - 1) / pl.bn));
-        if (pl.bm == 256)
-            hipLaunchKernelGGL((gemm32_ring<idt, odt, 256, 256, 2, 4, 5>), dim3(tiles), dim3(512), 0, st, p);
+        if (pl.bm == 256 && pl.bn == 256)
+            hipLaunchKernelGGL((gemm32_ring<idt, odt, 256, 256, 2, 4, 5, 32>), dim3(tiles), dim3(512), 0, st, p);
+        else if (pl.bm == 256)
+            hipLaunchKernelGGL((gemm32_ring<idt, odt, 256, 128, 4, 2, 3, 64>), dim3(tiles), dim3(512), 0, st, p);
+        else if (pl.bn == 128)
+            hipLaunchKernelGGL((gemm32_ring<idt, odt, 128, 128, 2, 2, 3, 64>), dim3(tiles), dim3(256), 0, st, p);
         else if (pl.bm == 128)
-            hipLaunchKernelGGL((gemm32_ring<idt, odt, 128, 128, 2, 2, 4>), dim3(tiles), dim3(256), 0, st, p);
+            hipLaunchKernelGGL((gemm32_ring<idt, odt, 128, 64, 2, 2, 4, 64>), dim3(tiles), dim3(256), 0, st, p);
         else
-            hipLaunchKernelGGL((gemm32_ring<idt, odt, 64, 64, 2, 2, 4>), dim3(tiles), dim3(256), 0, st, p);
+            hipLaunchKernelGGL((gemm32_ring<idt, odt, 64, 64, 2, 2, 4, 64>), dim3(tiles), dim3(256), 0, st, p);
         return hipGetLastError();
     }
     if (pl.bm == 128) {
@@ -628,6 +811,10 @@ const char *gemm32_kernel_name(int M, int N, int K, bool b_kn, int splits) {
     const Plan32 pl = plan32(M, N, K, b_kn, splits);
     static thread_local char buf[64];
     if (pl.kind == 0) snprintf(buf, sizeof buf, "gemm32_skinny_%s/fm%d", b_kn ? "kn" : "nk", pl.fm);
+    else if (pl.kind == 3) {
+        const StripCfg c = strip_cfg(M, pl.bn);
+        snprintf(buf, sizeof buf, "gemm32_strip_nk/w%d_a%d", c.sw, c.ar);
+    }
     else if (pl.kind == 1) snprintf(buf, sizeof buf, "gemm32_tile_%s/%dx%d", b_kn ? "kn" : "nk", pl.bm, pl.bn);
     else snprintf(buf, sizeof buf, "gemm32_ring_nk/%dx%d", pl.bm, pl.bn);
     return buf;
