@@ -5,8 +5,8 @@
 // with a trip count that depends on K alone; no split-K, no atomics, fp32
 // accumulation, bias added in fp32 and rounded once.  The chain itself is
 // described in gemm32.h.  Four kernels run it:
-//   gemm32_strip           M <= 64, (N, K) layout: four wavefronts per strip of
-//                          16 or 32 columns feeding one chain per fragment;
+//   gemm32_strip           M <= 64, (N, K) layout: loader wavefronts per strip
+//                          of 16 or 32 columns feeding one chain per fragment;
 //   gemm32_skinny_{nk,kn}  one wavefront per 32-column strip, M <= 64 (the
 //                          (K, N) layout and the split-K comparator);
 //   gemm32_tile            LDS-tiled, register-staged loads (any layout, any K,
@@ -14,7 +14,6 @@
 //   gemm32_ring            LDS-tiled with direct-to-LDS loads through a ring of
 //                          stages, (N, K) layout, K a multiple of 32: the
 //                          large-M path.
-#include <algorithm>
 #include <cstdio>
 
 #include "gemm32.h"
@@ -177,27 +176,28 @@ __global__ __launch_bounds__(64) void gemm32_skinny_kn(GemmParams p) {
 }
 
 // ============================================================ cooperative strip kernel
-// Small M with B in the (N, K) layout.  One workgroup of four wavefronts per
-// strip of SW output columns (SW = 32, or 16 with fragment columns 16..31
-// repeating 0..15, which doubles the number of workgroups for narrow N and
-// leaves every column's chain unchanged): all four stream the strip's weight
-// rows and AR rows of A into an LDS ring with direct-to-LDS loads, so many more
-// bytes are in flight per strip than one wavefront can keep outstanding; the
-// wavefront that owns 32-row fragment f (f < FM) runs the chain for it out of
-// LDS, reading stage t + 1 while the MFMAs of stage t run.
+// Small M with B in the (N, K) layout.  One workgroup per strip of SW output
+// columns (SW = 32, or 16 with fragment columns 16..31 repeating 0..15, which
+// doubles the number of workgroups for narrow N and leaves every column's
+// chain unchanged).  NL loader wavefronts stream the strip's weight rows and AR
+// rows of A into an LDS ring with direct-to-LDS loads, so many more bytes are
+// in flight per strip than one wavefront can keep outstanding; FM consumer
+// wavefronts, one per 32-row fragment, issue no global loads (so memory
+// back-pressure never stalls a chain) and run the chain out of LDS, reading
+// stage t + 1 while the MFMAs of stage t run.
 // A stage covers 128 k: SW B rows then AR A rows, 256 bytes each, chunk c of
 // row r at slot c ^ (r & 15) (16 consecutive rows of one chunk hit 16 distinct
 // bank groups).  Load instruction q moves rows 4q .. 4q+3 of the stage (1 KiB);
-// wave w issues instructions w, w + 4, ... (waves below Q mod 4 issue one more,
-// and wait with their own vmcnt thresholds).  Chunks past K are fetched from a
-// clamped in-bounds address and replaced by zeros when read, and steps past
-// the end of the chain are not run (an extra zero step could turn -0 into +0).
-template <int idt, int odt, int SW, int FM, int AR, int NS>
-__global__ __launch_bounds__(256) void gemm32_strip(GemmParams p) {
-    constexpr int NW = 4;
+// loader l issues instructions l, l + NL, ... (loaders below Q mod NL issue
+// one more, and wait with their own vmcnt thresholds).  Chunks past K are
+// fetched from a clamped in-bounds address and replaced by zeros when read,
+// and steps past the end of the chain are not run (an extra zero step could
+// turn -0 into +0).
+template <int idt, int odt, int SW, int FM, int AR, int NS, int NL>
+__global__ __launch_bounds__(64 * (FM + NL)) void gemm32_strip(GemmParams p) {
     constexpr int ROWB = 256;
     constexpr int QB = SW / 4, QA = AR / 4, Q = QB + QA;
-    constexpr int QHI = (Q + NW - 1) / NW, QLO = Q / NW, NHI = Q % NW;
+    constexpr int QHI = (Q + NL - 1) / NL, QLO = Q / NL, NHI = Q % NL;
     constexpr int STAGE = Q * 1024;
     static_assert(SW == 16 || SW == 32, "strip width");
     static_assert(AR % 4 == 0 && AR >= 4 && AR <= 32 * FM, "A rows per stage");
@@ -210,14 +210,16 @@ __global__ __launch_bounds__(256) void gemm32_strip(GemmParams p) {
     const int nchunk = p.K >> 3;                 // 16-byte chunks per row
     const int nstages = (p.K + 127) >> 7;
     const int total_steps = p.total_steps;
-    const int myq = wave < NHI ? QHI : QLO;
+    const bool consumer = wave < FM;
+    const int lw = consumer ? 0 : wave - FM;     // loader index
+    const int myq = consumer ? 0 : (lw < NHI ? QHI : QLO);
 
     // load side: lane L of instruction q covers stage row 4 q + L / 16, slot L mod 16
     const char *src[QHI];
     int cl[QHI];
 #pragma unroll
     for (int j = 0; j < QHI; ++j) {
-        const int q = min(wave + NW * j, Q - 1);
+        const int q = min(lw + NL * j, Q - 1);
         const int row = 4 * q + (lane >> 4);
         cl[j] = (lane & 15) ^ (row & 15);
         if (row < SW)
@@ -230,16 +232,17 @@ __global__ __launch_bounds__(256) void gemm32_strip(GemmParams p) {
 #pragma unroll
         for (int j = 0; j < QHI; ++j) {
             if (j < myq) {
-                const int q = wave + NW * j;
+                const int q = lw + NL * j;
                 const int g = min(stage * 16 + cl[j], nchunk - 1);
                 __builtin_amdgcn_global_load_lds(static_cast<const void *>(src[j] + (int64_t)g * 16),
                                                  BI_LDS_PTR(buf + q * 1024), 16, 0, 0);
             }
         }
     };
-    // wait until at most `keep` (NS - 1, NS - 2 or 0) of this wave's stages are in flight
+    // loaders: wait until at most `keep` (NS - 1, NS - 2 or 0) of their stages are in flight
     auto wait_keep = [&](int keep) {
-        if (wave < NHI) {
+        if (consumer) return;
+        if (lw < NHI) {
             if (keep == NS - 1) BI_WAIT_VMCNT(QHI * (NS - 1));
             else if (keep == NS - 2) BI_WAIT_VMCNT(QHI * (NS - 2));
             else BI_WAIT_VMCNT(0);
@@ -252,7 +255,6 @@ __global__ __launch_bounds__(256) void gemm32_strip(GemmParams p) {
 
     // consume side
     const int r32 = lane & 31, h = lane >> 5;
-    const bool consumer = wave < FM;
     const int arow = SW + min(32 * wave + r32, AR - 1);
     const int brow = r32 & (SW - 1);
     const int aoff = arow * ROWB, boff = brow * ROWB;
@@ -298,16 +300,16 @@ __global__ __launch_bounds__(256) void gemm32_strip(GemmParams p) {
         }
     }
     // iteration t: stage t + 1 has landed (at most NS - 2 stages still in
-    // flight) and every wave's reads of stage t are done, so the buffer of
-    // stage t is refilled with stage t + NS; then the MFMAs of stage t run
-    // while stage t + 1 is read.  Only the last stage can be partial.
+    // flight) and every consumer's reads of stage t are done, so loaders
+    // refill the buffer of stage t with stage t + NS while consumers run the
+    // MFMAs of stage t and read stage t + 1.  Only the last stage can be partial.
     int t = 0;
     for (; t < nstages - NS; ++t) {
         wait_keep(NS - 2);
         __builtin_amdgcn_s_waitcnt(0xc07f);          // lgkmcnt(0)
         __builtin_amdgcn_s_barrier();
-        issue(t + NS);
         if (consumer) mma_then_read(t);
+        else issue(t + NS);
     }
     for (; t < nstages - 1; ++t) {
         BI_WAIT_VMCNT(0);
@@ -700,37 +702,22 @@ struct Cfg32 { int bm, bn; };
 static const Cfg32 kRing32[] = {{256, 256}, {256, 128}, {128, 128}, {128, 64}, {64, 64}};
 constexpr long kRingMinTiles = 192;
 
-// Strip instantiations (width, fragments, A rows per stage, stages) and the
-// LDS each takes; used only to pick a kernel, never changes bits.
-struct StripCfg { int sw, fm, ar, ns; };
-static StripCfg strip_cfg(int M, int sw) {
-    if (M <= 16) return sw == 16 ? StripCfg{16, 1, 16, 6} : StripCfg{32, 1, 16, 6};
-    if (M <= 32) return sw == 16 ? StripCfg{16, 1, 32, 4} : StripCfg{32, 1, 32, 5};
-    return StripCfg{32, 2, 64, 4};
-}
-static int strip_width(int M, int N) {
-    if (M > 16) return 32;
-    // workgroup rounds times strip width: a proxy for time when the weight
-    // stream is shared evenly; ties go to the wider strip (less A re-reading)
-    long best_cost = -1;
-    int best = 32;
-    for (int sw : {32, 16}) {
-        const StripCfg c = strip_cfg(M, sw);
-        const long lds = (long)c.ns * (c.sw + c.ar) * 256;
-        const long per_cu = std::min(3L, (160L * 1024) / lds);
-        const long wgs = (N + sw - 1) / sw;
-        const long cost = ((wgs + 256 * per_cu - 1) / (256 * per_cu)) * sw;
-        if (best_cost < 0 || cost < best_cost) {
-            best_cost = cost;
-            best = sw;
-        }
-    }
-    return best;
+// Strip instantiations (width, fragments, A rows per stage, stages, loader
+// waves); used only to pick a kernel, never changes bits.  Narrow strips
+// double the workgroups when 32-wide strips would leave CUs idle, and always
+// for M <= 4; wider strips re-read A from L2 half as often.
+struct StripCfg { int sw, fm, ar, ns, nl; };
+static StripCfg strip_cfg(int M, int N) {
+    const bool narrow = M <= 4 || (N + 15) / 16 <= 256;
+    if (M <= 4) return StripCfg{16, 1, 4, 4, 3};
+    if (M <= 16) return narrow ? StripCfg{16, 1, 16, 6, 3} : StripCfg{32, 1, 16, 6, 3};
+    if (M <= 32) return narrow ? StripCfg{16, 1, 32, 4, 3} : StripCfg{32, 1, 32, 4, 3};
+    return narrow ? StripCfg{16, 2, 64, 4, 2} : StripCfg{32, 2, 64, 3, 2};
 }
 
 static Plan32 plan32(int M, int N, int K, bool b_kn, int splits) {
     if (M <= 64) {
-        if (!b_kn && splits == 1) return Plan32{3, M <= 32 ? 1 : 2, M, strip_width(M, N)};
+        if (!b_kn && splits == 1) return Plan32{3, M <= 32 ? 1 : 2, 0, 0};
         return Plan32{0, M <= 32 ? 1 : 2, 0, 0};
     }
     if (!b_kn && splits == 1 && K % 64 == 0) {
@@ -761,16 +748,15 @@ static hipError_t launch32_typed(const GemmParams &p, bool b_kn, hipStream_t st)
         return hipGetLastError();
     }
     if (pl.kind == 3) {
-        const StripCfg c = strip_cfg(p.M, pl.bn);
-        const dim3 grid((p.N + c.sw - 1) / c.sw), block(256);
-        if (c.sw == 16) {
-            if (c.ar == 16) hipLaunchKernelGGL((gemm32_strip<idt, odt, 16, 1, 16, 6>), grid, block, 0, st, p);
-            else hipLaunchKernelGGL((gemm32_strip<idt, odt, 16, 1, 32, 4>), grid, block, 0, st, p);
-        } else {
-            if (c.ar == 16) hipLaunchKernelGGL((gemm32_strip<idt, odt, 32, 1, 16, 6>), grid, block, 0, st, p);
-            else if (c.ar == 32) hipLaunchKernelGGL((gemm32_strip<idt, odt, 32, 1, 32, 5>), grid, block, 0, st, p);
-            else hipLaunchKernelGGL((gemm32_strip<idt, odt, 32, 2, 64, 4>), grid, block, 0, st, p);
-        }
+        const StripCfg c = strip_cfg(p.M, p.N);
+        const dim3 grid((p.N + c.sw - 1) / c.sw), block(64 * (c.fm + c.nl));
+        if (c.ar == 4) hipLaunchKernelGGL((gemm32_strip<idt, odt, 16, 1, 4, 4, 3>), grid, block, 0, st, p);
+        else if (c.ar == 16 && c.sw == 16) hipLaunchKernelGGL((gemm32_strip<idt, odt, 16, 1, 16, 6, 3>), grid, block, 0, st, p);
+        else if (c.ar == 16) hipLaunchKernelGGL((gemm32_strip<idt, odt, 32, 1, 16, 6, 3>), grid, block, 0, st, p);
+        else if (c.ar == 32 && c.sw == 16) hipLaunchKernelGGL((gemm32_strip<idt, odt, 16, 1, 32, 4, 3>), grid, block, 0, st, p);
+        else if (c.ar == 32) hipLaunchKernelGGL((gemm32_strip<idt, odt, 32, 1, 32, 4, 3>), grid, block, 0, st, p);
+        else if (c.sw == 16) hipLaunchKernelGGL((gemm32_strip<idt, odt, 16, 2, 64, 4, 2>), grid, block, 0, st, p);
+        else hipLaunchKernelGGL((gemm32_strip<idt, odt, 32, 2, 64, 3, 2>), grid, block, 0, st, p);
         return hipGetLastError();
     }
     if (pl.kind == 2) {
@@ -812,7 +798,7 @@ const char *gemm32_kernel_name(int M, int N, int K, bool b_kn, int splits) {
     static thread_local char buf[64];
     if (pl.kind == 0) snprintf(buf, sizeof buf, "gemm32_skinny_%s/fm%d", b_kn ? "kn" : "nk", pl.fm);
     else if (pl.kind == 3) {
-        const StripCfg c = strip_cfg(M, pl.bn);
+        const StripCfg c = strip_cfg(M, N);
         snprintf(buf, sizeof buf, "gemm32_strip_nk/w%d_a%d", c.sw, c.ar);
     }
     else if (pl.kind == 1) snprintf(buf, sizeof buf, "gemm32_tile_%s/%dx%d", b_kn ? "kn" : "nk", pl.bm, pl.bn);

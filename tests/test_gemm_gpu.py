@@ -60,6 +60,26 @@ def test_integer_inputs_are_exact_for_every_layout(ind, outd):
                           round_ref(ref_add[:m], outd), f"addmm, transposed view, M={m}")
 
 
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16])
+def test_small_m_strip_configs_are_exact_with_tails(dt):
+    """Every small-M strip configuration (16- and 32-column strips, A rows per stage 4 / 16 / 32 / 64)
+    on integer inputs: N ragged for both strip widths, K ragged for the 128-k stage and the 16-k step."""
+    lib = bi._native.load()
+    K, N = 1000, 4100
+    x = ints((64, K), 51, dt)
+    w = ints((N, K), 52, dt)
+    b = ints((N,), 53, dt, -5, 5)
+    ref = oracle.linear(x, w, b)
+    xg, wg, bg = x.to(DEV), w.to(DEV), b.to(DEV)
+    seen = set()
+    for m in (1, 3, 4, 5, 8, 16, 17, 31, 32, 33, 64):
+        for n in (N, 4096, 72):
+            seen.add(lib.bi_gemm_kernel_name(m, n, K, bi.BI_BF16 if dt == torch.bfloat16 else bi.BI_F16, 0).decode())
+            y = bi.bi_linear(xg[:m], wg[:n], bg[:n]).cpu()
+            assert_bits_equal(y, round_ref(ref[:m, :n], dt), f"M={m} N={n}")
+    assert len([k for k in seen if "strip" in k]) >= 6, seen
+
+
 def test_identity_permutation_and_onehot_weights():
     K = 64
     x = ints((40, K), 21, torch.bfloat16, -100, 100)
