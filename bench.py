@@ -15,13 +15,30 @@ outputs of every batch size are compared bit for bit with the largest batch
 (GEMM) and with the longest query chunk (attention).
 
 Prints one JSON line on stdout; progress goes to stderr.
+
+Profiling helpers (used to make the summaries kept under profiles/):
+  --pmc-pass ORDER.json   run one step eagerly (no graphs) after a 256 MiB
+                          calibration copy and write the dispatch order, for
+                          `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE`;
+  --summarize-pmc FETCH_DIR WRITE_DIR --order ORDER.json --out FILE.md
+                          per-launch HBM traffic of every kernel group,
+                          scaled by the calibration copy;
+  --summarize-stats KERNEL_STATS.csv --out FILE.md --title T --cmd C
+                          the rocprofv3 kernel statistics as a table.
+The roofline's "traffic" is read from the committed traffic summary and
+reported only while the kernel sources still hash to the value recorded
+when the counters were taken.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -30,6 +47,22 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0       # dense bf16 MFMA
+CSRC = os.path.join(ROOT, "invariant_deterministic_gemm_amd", "csrc")
+TRAFFIC_MD = os.path.join(ROOT, "profiles", "bench_step_bf16_gemm_sweep_sdpa_sweep_hbm_traffic.md")
+CALIB_BYTES = 256 * 2 ** 20     # bytes read and bytes written by the calibration copy
+# sources whose text fixes each kernel family's memory traffic
+FAMILY_SOURCES = {
+    "gemm": ["device.h", "gemm.h", "gemm_common.h", "gemm32.h", "gemm32.hip", "gemm.hip", "api.hip"],
+    "sdpa": ["device.h", "sdpa.h", "sdpa.hip", "api.hip"],
+}
+
+
+def family_hash(family: str) -> str:
+    h = hashlib.sha256()
+    for f in FAMILY_SOURCES[family]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
 
 
 def log(*a):
@@ -45,31 +78,23 @@ def parse():
     ap.add_argument("--no-cells", action="store_true", help="skip the per-cell roofline table")
     ap.add_argument("--cpu-threads", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--pmc-pass", metavar="ORDER_JSON", default=None,
+                    help="run one eager step for counter collection and write its dispatch order")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None)
+    ap.add_argument("--summarize-stats", metavar="KERNEL_STATS_CSV", default=None)
+    ap.add_argument("--order", default=None)
+    ap.add_argument("--out", default=None)
+    ap.add_argument("--title", default="")
+    ap.add_argument("--cmd", action="append", default=[])
     return ap.parse_args()
 
 
-def main():
-    args = parse()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(run with --gpus 1).", file=sys.stderr)
-        sys.exit(2)
-
-    import torch
-
-    import invariant_deterministic_gemm_amd as bi
-    import synthetic
-    from invariant_deterministic_gemm_amd import _native
-
-    lib = _native.load()
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
+def build_step(torch, bi, lib, _native, synthetic, dev):
+    """Inputs of the step, its launches and their grouping by kernel configuration."""
     K = synthetic.CFG2["K"]
     Ms = synthetic.CFG2["M_values"]
     Ns = synthetic.CFG2["N_values"]
     Mmax = max(Ms)
-
-    # ------------------------------------------------------------ inputs
     t0 = time.time()
     data = {}
     copies = {4096: 8, 14336: 4}          # > 256 MB of weights per N and layout
@@ -88,7 +113,6 @@ def main():
     torch.cuda.synchronize()
     log(f"inputs ready in {time.time() - t0:.1f}s")
 
-    # ------------------------------------------------------------ the step, grouped by kernel
     launches = []     # (group, kind, fn, flops, bytes, meta)
     ctr = {N: 0 for N in Ns}
     for N in Ns:
@@ -97,11 +121,10 @@ def main():
             for form in ("linear", "addmm"):
                 i = ctr[N] % copies[N]
                 ctr[N] += 1
+                kname = lib.bi_gemm_kernel_name(M, N, K, _native.BI_BF16, 0).decode()
                 if form == "linear":
-                    kname = lib.bi_gemm_kernel_name(M, N, K, _native.BI_BF16, 0).decode()
                     fn = (lambda x=dN["x"][:M], w=dN["w"][i], b=dN["b"]: bi.bi_linear(x, w, b))
                 else:
-                    kname = lib.bi_gemm_kernel_name(M, N, K, _native.BI_BF16, 0).decode()
                     fn = (lambda x=dN["x"][:M], wt=dN["wt"][i], b=dN["b"]: bi.bi_addmm(b, x, wt, 1.0, 1.0))
                 flops = 2.0 * M * N * K + M * N
                 nbytes = 2.0 * (M * K + N * K + M * N + N)
@@ -116,7 +139,39 @@ def main():
     groups = {}
     for rec in launches:
         groups.setdefault(rec[0], []).append(rec)
-    names = list(groups)
+    return dict(K=K, Ms=Ms, Ns=Ns, data=data, q3=q3, k3=k3, v3=v3, S3=S3, launches=launches,
+                groups=groups, names=list(groups))
+
+
+def main():
+    args = parse()
+    if args.summarize_stats:
+        summarize_stats(args)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(args)
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import invariant_deterministic_gemm_amd as bi
+    import synthetic
+    from invariant_deterministic_gemm_amd import _native
+
+    lib = _native.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    st = build_step(torch, bi, lib, _native, synthetic, dev)
+    if args.pmc_pass:
+        pmc_pass(torch, st, args.pmc_pass)
+        return
+    K, Ms, Ns, data = st["K"], st["Ms"], st["Ns"], st["data"]
+    q3, k3, v3, S3 = st["q3"], st["k3"], st["v3"], st["S3"]
+    launches, groups, names = st["launches"], st["groups"], st["names"]
 
     # warm every path eagerly once, then capture one graph per group
     for rec in launches:
@@ -219,7 +274,7 @@ def main():
         per_launch = sum(r[4] for r in dl) / len(dl)
         achieved = per_launch / (avg_ms * 1e-3) / 1e9
     roofline = {"bound": bound, "kernel": dom, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-                "frac": round(achieved / peak, 4), "traffic": None,
+                "frac": round(achieved / peak, 4), "traffic": measured_traffic(dom, dl[0][1]),
                 "launches_per_step": len(dl), "avg_launch_us": round(avg_ms * 1e3, 3),
                 "algorithmic_per_launch": per_launch}
 
@@ -382,6 +437,139 @@ def cpu_baseline(torch, synthetic, args):
                       "for N=4096 and N=14336, i.e. every row of the GEMM sweep once per pass; "
                       "attention not included",
             "seconds": round(t, 2)}
+
+
+# ---------------------------------------------------------------- profiling helpers
+def pmc_pass(torch, st, order_path):
+    """One eager pass for counter collection: a calibration copy of known size, then every launch
+    of the step once, in order; writes which kernel group each of our dispatches belongs to."""
+    src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device="cuda").uniform_()
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.mul(src, 2.0, out=dst)              # reads and writes CALIB_BYTES each
+    torch.cuda.synchronize()
+    order = []
+    for rec in st["launches"]:
+        rec[2]()
+        order.append({"group": rec[0], "kind": rec[1], "dispatches": 2 if rec[1] == "sdpa" else 1,
+                      "algorithmic_bytes": rec[4]})
+    torch.cuda.synchronize()
+    with open(order_path, "w") as f:
+        json.dump({"calibration_bytes": CALIB_BYTES, "launches": order}, f)
+    log(f"pmc pass: {len(order)} launches written to {order_path}")
+
+
+def _counter_rows(d, counter):
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    per = {}
+    for fn in files:
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                k = int(r["Dispatch_Id"])
+                e = per.setdefault(k, [r["Kernel_Name"], 0.0])
+                e[1] += float(r["Counter_Value"])
+    return [(k, v[0], v[1]) for k, v in sorted(per.items())]
+
+
+def _attribute(rows, order, calib_bytes):
+    """Calibration factor and per-group counter totals from one counter's dispatch rows."""
+    ours = [(k, n, v) for k, n, v in rows if "bi::" in n]
+    first = ours[0][0] if ours else None
+    calib = [v for k, n, v in rows if "bi::" not in n and (first is None or k < first)]
+    big = max(calib) if calib else 0.0
+    if big * 1024 < 0.5 * calib_bytes:
+        raise SystemExit("calibration copy not found among the dispatches")
+    factor = calib_bytes / (big * 1024)       # counter reads KiB
+    expect = sum(o["dispatches"] for o in order)
+    if len(ours) != expect:
+        raise SystemExit(f"{len(ours)} library dispatches in the counters, {expect} expected")
+    tot = {}
+    it = iter(ours)
+    for o in order:
+        for _ in range(o["dispatches"]):
+            _, _, v = next(it)
+            tot[o["group"]] = tot.get(o["group"], 0.0) + v
+    return factor, big, tot
+
+
+def summarize_pmc(args):
+    with open(args.order) as f:
+        od = json.load(f)
+    order, cb = od["launches"], od["calibration_bytes"]
+    fdir, wdir = args.summarize_pmc
+    ff, fbig, ftot = _attribute(_counter_rows(fdir, "FETCH_SIZE"), order, cb)
+    wf, wbig, wtot = _attribute(_counter_rows(wdir, "WRITE_SIZE"), order, cb)
+    nl, alg, kind = {}, {}, {}
+    for o in order:
+        nl[o["group"]] = nl.get(o["group"], 0) + 1
+        alg[o["group"]] = alg.get(o["group"], 0.0) + o["algorithmic_bytes"]
+        kind[o["group"]] = o["kind"]
+    lines = [f"# {args.title or 'HBM traffic per launch of every kernel group of one bench step'}", "",
+             "Commands (run from the repository root on one MI355X):", "", "```"] + args.cmd + ["```", "",
+             f"Calibration: one elementwise copy reading and writing {cb} bytes each; FETCH_SIZE read "
+             f"{fbig:.0f} KiB for it (scale {ff:.4f}), WRITE_SIZE {wbig:.0f} KiB (scale {wf:.4f}).  "
+             "Counter values below are scaled by these factors.", "",
+             "| kernel group | launches | fetched MB / launch | written MB / launch | traffic MB / launch "
+             "| algorithmic MB / launch | traffic / algorithmic |",
+             "|---|---:|---:|---:|---:|---:|---:|"]
+    groups = {}
+    for g in nl:
+        fb = ftot[g] * 1024 * ff / nl[g]
+        wb = wtot[g] * 1024 * wf / nl[g]
+        a = alg[g] / nl[g]
+        groups[g] = {"traffic_bytes": round(fb + wb), "fetch_bytes": round(fb), "write_bytes": round(wb),
+                     "algorithmic_bytes": round(a), "family": kind[g]}
+        lines.append(f"| `{g}` | {nl[g]} | {fb / 1e6:.2f} | {wb / 1e6:.2f} | {(fb + wb) / 1e6:.2f} | "
+                     f"{a / 1e6:.2f} | {(fb + wb) / a:.3f} |")
+    hashes = {fam: family_hash(fam) for fam in FAMILY_SOURCES}
+    lines += ["", "Kernel sources hashed when the counters were taken (bench.py reports the traffic only "
+                  "while these still match):", ""]
+    lines += [f"- {fam}: `{h}`" for fam, h in hashes.items()]
+    lines += ["", "<!-- traffic-json " + json.dumps({"hashes": hashes, "groups": groups}) + " -->", ""]
+    with open(args.out, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
+def measured_traffic(group, family):
+    """Scaled FETCH_SIZE + WRITE_SIZE bytes per launch of a kernel group, from the committed summary,
+    or None when there is none or the kernel sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_MD) as f:
+            m = re.search(r"<!-- traffic-json (.*) -->", f.read())
+        d = json.loads(m.group(1))
+        g = d["groups"][group]
+        if d["hashes"].get(g["family"]) != family_hash(g["family"]):
+            return None
+        return g["traffic_bytes"]
+    except (OSError, AttributeError, KeyError, ValueError):
+        return None
+
+
+def summarize_stats(args):
+    with open(args.summarize_stats) as f:
+        rows = list(csv.DictReader(f))
+    lines = [f"# {args.title}", "", "Command (run from the repository root on one MI355X):", "", "```"] + \
+        args.cmd + ["```", "",
+                    "rocprofv3 kernel statistics (every dispatch of the run: warm-up, graph capture and the "
+                    "timed steps):", "",
+                    "| kernel | calls | avg us | min us | max us | % time |", "|---|---:|---:|---:|---:|---:|"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        if float(r["Percentage"]) < 0.3:
+            continue
+        name = r["Name"].replace("|", "/")
+        if len(name) > 90:
+            name = name[:87] + "..."
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['Percentage']):.1f} |")
+    with open(args.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 if __name__ == "__main__":

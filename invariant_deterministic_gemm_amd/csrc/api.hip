@@ -25,7 +25,8 @@ namespace {
 constexpr int kAbiMajor = 1;
 // Bump when a compile-time constant that shapes arithmetic changes
 // (k-step order, MFMA shapes, KV_SPLIT / KV_BLOCK, combine order).
-constexpr int kBitsVersion = 1;
+// 2: 16-bit GEMM chain on v_mfma_f32_32x32x16 (was 16x16x32).
+constexpr int kBitsVersion = 2;
 
 thread_local std::string g_last_error;
 

@@ -7,17 +7,17 @@
 // depends on K alone, there is no split-K and no atomics, accumulators are
 // fp32, and the bias is added into the fp32 accumulator and rounded once.
 //
-// CDNA4 realisation.  Every output element (m, n) is produced by ONE chain
-// of MFMA instructions over k, identical in every kernel configuration:
+// CDNA4 realisation for fp32 inputs.  Every output element (m, n) is
+// produced by ONE chain of MFMA instructions over k, identical in every
+// kernel configuration:
 //
-//   k "steps" of CK elements walk upwards from k = 0 (CK = 32 for bf16/fp16,
-//   16 for fp32).  In a step, lane group g = lane / 16 holds the 16-byte
-//   chunk k in [s*CK + g*EPC, s*CK + (g+1)*EPC) of its row of A and of its
-//   column of B (EPC = elements per 16 bytes: 8, or 4 for fp32).
-//     bf16/fp16: one v_mfma_f32_16x16x32 per step, k slots in that order;
-//     fp32:      four v_mfma_f32_16x16x4_f32 per step, u = 0..3, where the
-//                instruction u takes element u of every lane group's chunk.
-//   The accumulator starts at +0; chunks past K are zero.
+//   k "steps" of 16 elements walk upwards from k = 0.  In a step, lane group
+//   g = lane / 16 holds the 16-byte chunk k in [16 s + 4 g, 16 s + 4 g + 4)
+//   of its row of A and of its column of B; four v_mfma_f32_16x16x4_f32 run
+//   per step, u = 0..3, instruction u taking element u of every lane group's
+//   chunk.  The accumulator starts at +0; chunks past K are zero.
+// (The kernels below are written over the dtype for symmetry, but the host
+// dispatch sends only fp32 inputs here.)
 //
 // MFMA output element (i, j) depends only on A row i, B column j and the
 // incoming accumulator (i, j), so the tile shape, the grid and the position
