@@ -61,10 +61,10 @@ typedef enum {
  * Arithmetic contract, identical for all three calls and every M:
  *   acc[m,n] = fp32 sum over k of A[m,k] * B[k,n], formed by one chain of
  *              gfx950 MFMA instructions walking k upwards from 0 in fixed
- *              steps: v_mfma_f32_32x32x16_{bf16,f16} for 16-bit inputs (one
- *              step per 16 k), v_mfma_f32_16x16x4_f32 for fp32 inputs (one
- *              step per 4 k); the accumulator starts at +0 and k past K
- *              contributes exact zeros.  The chain depends on K only;
+ *              steps: one v_mfma_f32_16x16x32_{bf16,f16} per 32 k for 16-bit
+ *              inputs, four v_mfma_f32_16x16x4_f32 per 16 k for fp32 inputs;
+ *              the accumulator starts at +0 and k past K contributes exact
+ *              zeros.  The chain depends on K only;
  *              nothing splits K, and no tile choice changes the chain.
  *   t        = fp32(beta) * fp32(C[m,n])          (0 when there is no C / beta == 0)
  *   y[m,n]   = round_to_out_dtype( fmaf(alpha, acc, t) )

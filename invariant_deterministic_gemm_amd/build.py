@@ -5,7 +5,10 @@ hipcc cross-compiles for gfx950 without a GPU present.  Flags:
     in the kernels is an explicit fmaf and all template instantiations round
     the same way;
   * -Xclang -target-feature -Xclang -packed-fp32-ops: keep the compiler from
-    emitting packed fp32 VALU instructions.
+    emitting packed fp32 VALU instructions;
+  * -mllvm -amdgpu-mfma-vgpr-form=1: MFMA accumulators live in VGPRs (gfx950
+    allows both register files), which keeps the compiler from copying
+    accumulators between AGPRs and VGPRs inside the k loops.
 """
 from __future__ import annotations
 
@@ -17,13 +20,14 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libbi.so")
-SOURCES = ["api.hip", "gemm.hip", "gemm32.hip", "sdpa.hip"]
+SOURCES = ["api.hip", "gemm.hip", "gemm16.hip", "sdpa.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
 def hipcc_flags() -> list:
     return ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-mllvm", "-amdgpu-mfma-vgpr-form=1",
             "-Wall", "-Wno-unused-function",
             "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 

@@ -25,8 +25,8 @@ namespace {
 constexpr int kAbiMajor = 1;
 // Bump when a compile-time constant that shapes arithmetic changes
 // (k-step order, MFMA shapes, KV_SPLIT / KV_BLOCK, combine order).
-// 2: 16-bit GEMM chain on v_mfma_f32_32x32x16 (was 16x16x32).
-constexpr int kBitsVersion = 2;
+// 3: 16-bit GEMM chain on v_mfma_f32_16x16x32 again (2 used 32x32x16).
+constexpr int kBitsVersion = 3;
 
 thread_local std::string g_last_error;
 

@@ -1,30 +1,32 @@
-// Batch-invariant GEMM kernels for fp32 inputs on gfx950, the split-K
-// comparator's reduce, and the host dispatch for every dtype (16-bit inputs
-// run the 32x32x16 kernels of gemm32.hip).
+// Generic batch-invariant GEMM kernels for gfx950 (every dtype, any layout,
+// any K, split ranges for the comparator), the split-K comparator's reduce,
+// and the host dispatch.  16-bit calls with (N, K) weights go to the faster
+// strip / ring kernels of gemm16.hip when they apply; both files run the
+// same per-element chain.
 //
 // Method (mlx-batch-invariant README, section "How the kernels work", GEMM
 // paragraph): one workgroup owns the entire reduction over K, the trip count
 // depends on K alone, there is no split-K and no atomics, accumulators are
 // fp32, and the bias is added into the fp32 accumulator and rounded once.
 //
-// CDNA4 realisation for fp32 inputs.  Every output element (m, n) is
-// produced by ONE chain of MFMA instructions over k, identical in every
-// kernel configuration:
+// CDNA4 realisation.  Every output element (m, n) is produced by ONE chain
+// of MFMA instructions over k, identical in every kernel configuration:
 //
-//   k "steps" of 16 elements walk upwards from k = 0.  In a step, lane group
-//   g = lane / 16 holds the 16-byte chunk k in [16 s + 4 g, 16 s + 4 g + 4)
-//   of its row of A and of its column of B; four v_mfma_f32_16x16x4_f32 run
-//   per step, u = 0..3, instruction u taking element u of every lane group's
-//   chunk.  The accumulator starts at +0; chunks past K are zero.
-// (The kernels below are written over the dtype for symmetry, but the host
-// dispatch sends only fp32 inputs here.)
+//   k "steps" of CK elements walk upwards from k = 0 (CK = 32 for bf16/fp16,
+//   16 for fp32).  In a step, lane group g = lane / 16 holds the 16-byte
+//   chunk k in [s*CK + g*EPC, s*CK + (g+1)*EPC) of its row of A and of its
+//   column of B (EPC = elements per 16 bytes: 8, or 4 for fp32).
+//     bf16/fp16: one v_mfma_f32_16x16x32 per step, k slots in that order;
+//     fp32:      four v_mfma_f32_16x16x4_f32 per step, u = 0..3, where the
+//                instruction u takes element u of every lane group's chunk.
+//   The accumulator starts at +0; chunks past K are zero; no step past the
+//   last one (ceil(K / CK)) runs.
 //
 // MFMA output element (i, j) depends only on A row i, B column j and the
 // incoming accumulator (i, j), so the tile shape, the grid and the position
 // of a row inside a tile do not change any element's bits.  That is what lets
-// the host pick a skinny kernel for small M and an LDS-tiled kernel for large
-// M without changing results: both run exactly the chain above, followed by
-// the same epilogue
+// the host pick a kernel by M without changing results: every kernel runs
+// exactly the chain above, followed by the same epilogue
 //      y = round_out( fmaf(alpha, acc, beta * c) ).
 
 #include <cstdio>
@@ -32,7 +34,7 @@
 #include "device.h"
 #include "gemm.h"
 #include "gemm_common.h"
-#include "gemm32.h"
+#include "gemm16.h"
 
 namespace bi {
 
@@ -376,8 +378,8 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce(GemmParams p, const fl
 
 // ============================================================ host dispatch
 int gemm_k_steps(int K, int in_dt) {
-    (void)in_dt;                 // 16 k per step for every dtype (one 16-byte chunk per lane)
-    return (K + 15) / 16;
+    // one 16-byte chunk per lane group per step: 32 k for 16-bit inputs, 16 k for fp32
+    return in_dt == DT_F32 ? (K + 15) / 16 : (K + 31) / 32;
 }
 
 // fp32 inputs: 16x16x4 chain (skinny kernel for M <= 64, LDS-tiled above).
@@ -394,8 +396,11 @@ static GemmPlan16 plan16(int M, int N) {
     return GemmPlan16{1, 0, tiles128 >= 256 ? 128 : 64};
 }
 
-static hipError_t launch_f32(const GemmParams &p, bool b_kn, hipStream_t st) {
-    constexpr int idt = DT_F32, odt = DT_F32;
+// The generic kernels (any layout, any K, split ranges): skinny for M <= 64,
+// LDS-tiled above.  Every configuration runs the same per-element chain; M
+// only picks occupancy.
+template <int idt, int odt>
+static hipError_t launch_generic(const GemmParams &p, bool b_kn, hipStream_t st) {
     const GemmPlan16 pl = plan16(p.M, p.N);
     const unsigned sp = (unsigned)p.splits;
     if (pl.kind == 0) {
@@ -426,8 +431,17 @@ static hipError_t launch_f32(const GemmParams &p, bool b_kn, hipStream_t st) {
     return hipGetLastError();
 }
 
+static hipError_t launch_generic_dt(const GemmParams &p, int in_dt, int out_dt, bool b_kn, hipStream_t st) {
+    if (in_dt == DT_F32 && out_dt == DT_F32) return launch_generic<DT_F32, DT_F32>(p, b_kn, st);
+    if (in_dt == DT_BF16 && out_dt == DT_BF16) return launch_generic<DT_BF16, DT_BF16>(p, b_kn, st);
+    if (in_dt == DT_F16 && out_dt == DT_F16) return launch_generic<DT_F16, DT_F16>(p, b_kn, st);
+    if (in_dt == DT_BF16 && out_dt == DT_F32) return launch_generic<DT_BF16, DT_F32>(p, b_kn, st);
+    if (in_dt == DT_F16 && out_dt == DT_F32) return launch_generic<DT_F16, DT_F32>(p, b_kn, st);
+    return hipErrorInvalidValue;
+}
+
 const char *gemm_kernel_name(int M, int N, int K, int in_dt, bool b_kn) {
-    if (in_dt != DT_F32) return gemm32_kernel_name(M, N, K, b_kn, 1);
+    if (in_dt != DT_F32 && gemm16_applies(M, N, K, b_kn, 1)) return gemm16_kernel_name(M, N, K);
     const GemmPlan16 pl = plan16(M, N);
     static thread_local char buf[64];
     if (pl.kind == 0) snprintf(buf, sizeof buf, "gemm_skinny_%s/fm%d", b_kn ? "kn" : "nk", pl.fm);
@@ -442,12 +456,8 @@ static hipError_t dispatch_dt(const GemmParams &p0, int in_dt, int out_dt, bool 
     p.splits = splits;
     p.partial = splits > 1 ? ws : nullptr;
     hipError_t e;
-    if (in_dt == DT_F32) {
-        if (out_dt != DT_F32) return hipErrorInvalidValue;
-        e = launch_f32(p, b_kn, st);
-    } else {
-        e = launch_gemm32(p, in_dt, out_dt, b_kn, st);
-    }
+    if (in_dt != DT_F32 && gemm16_applies(p.M, p.N, p.K, b_kn, splits)) e = launch_gemm16(p, in_dt, out_dt, st);
+    else e = launch_generic_dt(p, in_dt, out_dt, b_kn, st);
     if (e != hipSuccess || splits <= 1) return e;
     const int64_t total = (int64_t)p.M * p.N;
     const dim3 grid((unsigned)((total + 255) / 256));

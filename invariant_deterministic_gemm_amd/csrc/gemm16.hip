@@ -1,0 +1,492 @@
+// Batch-invariant GEMM kernels for 16-bit inputs on gfx950 (v_mfma_f32_16x16x32).
+//
+// Method (mlx-batch-invariant README, section "How the kernels work", GEMM
+// paragraph): the whole K reduction of an output element stays in one place
+// with a trip count that depends on K alone; no split-K, no atomics, fp32
+// accumulation, bias added in fp32 and rounded once.  The chain itself is
+// described in gemm16.h.  Two kernels here run it for B in the (N, K) layout:
+//   gemm16_strip  M <= 64: loader wavefronts stream a 16-column strip of the
+//                 weights (and the rows of A) into LDS for one consumer
+//                 wavefront that runs the chains of all M rows;
+//   gemm16_ring   M > 64, K a multiple of 64: LDS tiles fed through a ring of
+//                 stages by direct-to-LDS loads.
+// Everything else (row-major (K, N) weights, other K, the split-K comparator)
+// runs the generic kernels of gemm.hip, which implement the same chain.
+#include <cstdio>
+
+#include "gemm16.h"
+#include "gemm_common.h"
+
+namespace bi {
+
+// ============================================================ cooperative strip kernel
+// One workgroup per 16 output columns.  NL loader wavefronts stream the
+// strip's 16 weight rows and AR rows of A into an LDS ring with direct-to-LDS
+// loads, so many more bytes are in flight per strip than one wavefront could
+// keep outstanding.  The consumer wavefront issues no global loads (so memory
+// back-pressure never stalls the chains) and runs FM independent 16-row
+// fragment chains out of LDS, reading stage t + 1 (into a second register
+// set) while the MFMAs of stage t run.
+// A stage covers 128 k: 16 B rows then AR A rows, 256 bytes each, chunk c of
+// row r at slot c ^ (r & 15) (the 16 rows one ds_read_b128 pass serves hit 16
+// distinct bank groups).  Load instruction q moves rows 4q .. 4q+3 of the
+// stage (1 KiB); loader l issues instructions l, l + NL, ... (loaders below
+// Q mod NL issue one more, and wait with their own vmcnt thresholds).  Chunks
+// past K are fetched from a clamped in-bounds address and replaced by zeros
+// when read, and steps past the end of the chain are not run.
+template <int idt, int odt, int FM, int AR, int NS, int NL>
+__global__ __launch_bounds__(64 * (1 + NL)) void gemm16_strip(GemmParams p) {
+    constexpr int ROWB = 256;
+    constexpr int QB = 4, QA = AR / 4, Q = QB + QA;
+    constexpr int QHI = (Q + NL - 1) / NL, QLO = Q / NL, NHI = Q % NL;
+    constexpr int STAGE = Q * 1024;
+    static_assert(AR % 4 == 0 && AR >= 4 && AR <= 16 * FM, "A rows per stage");
+    static_assert(NS >= 2 && QHI * (NS - 1) <= 63, "vmcnt range");
+    __shared__ __attribute__((aligned(1024))) char lds[NS * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int n0 = blockIdx.x * 16;
+    const int nchunk = p.K >> 3;                 // 16-byte chunks per row
+    const int nstages = (p.K + 127) >> 7;
+    const int total_steps = p.total_steps;
+    const bool consumer = wave == 0;
+    const int lw = consumer ? 0 : wave - 1;      // loader index
+    const int myq = consumer ? 0 : (lw < NHI ? QHI : QLO);
+
+    // load side: lane L of instruction q covers stage row 4 q + L / 16, slot L mod 16
+    const char *src[QHI];
+    int cl[QHI];
+#pragma unroll
+    for (int j = 0; j < QHI; ++j) {
+        const int q = min(lw + NL * j, Q - 1);
+        const int row = 4 * q + (lane >> 4);
+        cl[j] = (lane & 15) ^ (row & 15);
+        if (row < 16)
+            src[j] = static_cast<const char *>(p.B) + (int64_t)min(n0 + row, p.N - 1) * p.ldb * 2;
+        else
+            src[j] = static_cast<const char *>(p.A) + (int64_t)min(row - 16, p.M - 1) * p.lda * 2;
+    }
+    auto issue = [&](int stage) {
+        char *buf = lds + (stage % NS) * STAGE;
+#pragma unroll
+        for (int j = 0; j < QHI; ++j) {
+            if (j < myq) {
+                const int q = lw + NL * j;
+                const int gc = min(stage * 16 + cl[j], nchunk - 1);
+                __builtin_amdgcn_global_load_lds(static_cast<const void *>(src[j] + (int64_t)gc * 16),
+                                                 BI_LDS_PTR(buf + q * 1024), 16, 0, 0);
+            }
+        }
+    };
+    // loaders: wait until at most `keep` (NS - 1, NS - 2 or 0) of their stages are in flight
+    auto wait_keep = [&](int keep) {
+        if (consumer) return;
+        if (lw < NHI) {
+            if (keep == NS - 1) BI_WAIT_VMCNT(QHI * (NS - 1));
+            else if (keep == NS - 2) BI_WAIT_VMCNT(QHI * (NS - 2));
+            else BI_WAIT_VMCNT(0);
+        } else {
+            if (keep == NS - 1) BI_WAIT_VMCNT(QLO * (NS - 1));
+            else if (keep == NS - 2) BI_WAIT_VMCNT(QLO * (NS - 2));
+            else BI_WAIT_VMCNT(0);
+        }
+    };
+
+    // consume side
+    const int r16 = lane & 15, g = lane >> 4;
+    int aoff[FM], aswz[FM];
+#pragma unroll
+    for (int f = 0; f < FM; ++f) {
+        const int arow = 16 + min(16 * f + r16, AR - 1);
+        aoff[f] = arow * ROWB;
+        aswz[f] = arow & 15;
+    }
+    const int boff = r16 * ROWB;
+    f32x4 acc[FM];
+#pragma unroll
+    for (int f = 0; f < FM; ++f) acc[f] = zero4();
+    // two register sets: the fragments of stage t and those of stage t + 1
+    u32x4 xa[4][FM], xb[4], ya[4][FM], yb[4];
+    auto read_stage = [&](int stage, u32x4 (&a)[4][FM], u32x4 (&b)[4]) {
+        const char *buf = lds + (stage % NS) * STAGE;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int c = 4 * u + g;
+            b[u] = *reinterpret_cast<const u32x4 *>(buf + boff + ((c ^ r16) << 4));
+#pragma unroll
+            for (int f = 0; f < FM; ++f)
+                a[u][f] = *reinterpret_cast<const u32x4 *>(buf + aoff[f] + ((c ^ aswz[f]) << 4));
+        }
+    };
+    auto mma_stage = [&](const u32x4 (&a)[4][FM], const u32x4 (&b)[4]) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int f = 0; f < FM; ++f) acc[f] = Mfma<idt>::step(a[u][f], b[u], acc[f]);
+    };
+    // the last stage: only steps of the chain, chunks past K read as zero
+    auto mma_last = [&](int stage, const u32x4 (&a)[4][FM], const u32x4 (&b)[4]) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (stage * 4 + u < total_steps) {
+                const bool past = stage * 16 + 4 * u + g >= nchunk;
+                const u32x4 bb = past ? zero_u4() : b[u];
+#pragma unroll
+                for (int f = 0; f < FM; ++f) acc[f] = Mfma<idt>::step(past ? zero_u4() : a[u][f], bb, acc[f]);
+            }
+        }
+    };
+    // stage t's fragments are in registers: read stage t + 1 into the other
+    // set, then run stage t's MFMAs (the reads complete under the chain)
+    auto consume_xy = [&](int stage) { read_stage(stage + 1, ya, yb); mma_stage(xa, xb); };
+    auto consume_yx = [&](int stage) { read_stage(stage + 1, xa, xb); mma_stage(ya, yb); };
+    auto sync_steady = [&]() {
+        wait_keep(NS - 2);
+        __builtin_amdgcn_s_waitcnt(0xc07f);          // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+    };
+    auto sync_drain = [&]() {
+        BI_WAIT_VMCNT(0);
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_s_barrier();
+    };
+
+    // prologue: all NS buffers in flight, stage 0 landed everywhere and read
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+        if (s < nstages) issue(s);
+    if (nstages > 0) {
+        wait_keep(nstages >= NS ? NS - 1 : 0);
+        __builtin_amdgcn_s_barrier();
+        if (consumer) read_stage(0, xa, xb);
+    }
+    // iteration t: stage t + 1 has landed (at most NS - 2 stages still in
+    // flight) and the consumer's reads of stage t are done, so loaders refill
+    // the buffer of stage t with stage t + NS while the consumer reads stage
+    // t + 1 and runs the MFMAs of stage t.  Only the last stage can be partial.
+    // The loop is unrolled twice so that the two register sets alternate.
+    int t = 0;
+    const int steady = nstages - NS;
+    for (; t + 2 <= steady; t += 2) {
+        sync_steady();
+        if (consumer) consume_xy(t);
+        else issue(t + NS);
+        sync_steady();
+        if (consumer) consume_yx(t + 1);
+        else issue(t + 1 + NS);
+    }
+    bool in_y = false;                               // the set holding stage t's fragments
+    if (t < steady) {
+        sync_steady();
+        if (consumer) consume_xy(t);
+        else issue(t + NS);
+        ++t;
+        in_y = true;
+    }
+    for (; t < nstages - 1; ++t) {
+        sync_drain();
+        if (consumer) {
+            if (in_y) consume_yx(t);
+            else consume_xy(t);
+        }
+        in_y = !in_y;
+    }
+    if (nstages > 0 && consumer) {
+        if (in_y) mma_last(nstages - 1, ya, yb);
+        else mma_last(nstages - 1, xa, xb);
+    }
+    if (!consumer) return;
+    const int n = n0 + r16;
+    if (n < p.N) {
+#pragma unroll
+        for (int f = 0; f < FM; ++f)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = 16 * f + 4 * g + i;
+                if (m < p.M) epilogue<odt>(p, m, n, acc[f][i]);
+            }
+    }
+}
+
+// ============================================================ LDS-staged epilogue
+// The BM x BN tile goes through LDS (rows of BN output elements, 16-byte
+// chunk index XOR ((row / 4) mod 4) * 2, so the four rows one fragment store
+// touches land on distinct banks) and is written with 16-byte coalesced
+// stores.  Same arithmetic as `epilogue`: one fmaf with the C / bias term, one
+// rounding; the bias of a column is read once.
+template <int odt, int BM, int BN, int WGM, int WGN>
+__device__ __forceinline__ void store_tile16(const GemmParams &p, const f32x4 (&acc)[BM / WGM / 16][BN / WGN / 16],
+                                             int m0, int n0, char *lds) {
+    constexpr int WM = BM / WGM, WN = BN / WGN;
+    constexpr int FM = WM / 16, FN = WN / 16;
+    constexpr int EO = Elem<odt>::bytes;
+    constexpr int ROW = BN * EO;
+    constexpr int NT = 64 * WGM * WGN;
+    static_assert(ROW % 128 == 0, "rows must hold whole groups of 8 chunks");
+    auto pos = [](int row, int byte) {
+        return row * ROW + ((((byte >> 4) ^ (((row >> 2) & 3) << 1)) << 4) | (byte & 15));
+    };
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WGN, wn = wave % WGN;
+    const int r16 = lane & 15, g = lane >> 4;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+        const int nl = wn * WN + 16 * j + r16;
+        const int n = min(n0 + nl, p.N - 1);
+        float tb = 0.0f;
+        if (p.C != nullptr && p.ldc == 0) tb = p.beta * load_as_f32<odt>(p.C, n);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int ml = wm * WM + 16 * i + 4 * g + e;
+                float t = tb;
+                if (p.C != nullptr && p.ldc != 0) {
+                    const int m = min(m0 + ml, p.M - 1);
+                    t = p.beta * load_as_f32<odt>(p.C, (int64_t)m * p.ldc + n);
+                }
+                const float y = __builtin_fmaf(p.alpha, acc[i][j][e], t);
+                char *dst = lds + pos(ml, nl * EO);
+                if constexpr (EO == 2) *reinterpret_cast<uint16_t *>(dst) =
+                    (uint16_t)(odt == DT_BF16 ? f32_to_bf16(y) : f32_to_f16(y));
+                else *reinterpret_cast<float *>(dst) = y;
+            }
+    }
+    __syncthreads();
+    constexpr int CPR = BN * EO / 16;                  // 16-byte chunks per tile row
+    constexpr int EPC = 16 / EO;
+    for (int id = tid; id < BM * CPR; id += NT) {
+        const int ml = id / CPR, c = id % CPR;
+        const int m = m0 + ml, n = n0 + c * EPC;
+        if (m >= p.M || n >= p.N) continue;
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(lds + pos(ml, c * 16));
+        char *gdst = static_cast<char *>(p.Y) + ((int64_t)m * p.ldy + n) * EO;
+        if (n + EPC <= p.N && ((reinterpret_cast<uintptr_t>(gdst) & 15) == 0)) {
+            *reinterpret_cast<u32x4 *>(gdst) = v;
+        } else {
+            const int cnt = min(EPC, p.N - n);
+            for (int e = 0; e < cnt; ++e) {
+                if constexpr (EO == 2) reinterpret_cast<uint16_t *>(gdst)[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+                else reinterpret_cast<uint32_t *>(gdst)[e] = v[e];
+            }
+        }
+    }
+}
+
+// ============================================================ deep-ring tile kernel
+// BM x BN tile, WGM x WGN wavefronts, K a multiple of 64.  NS LDS stages of 64
+// k (two chain steps; 128-byte LDS rows of 8 chunks, chunk c of row r at slot
+// c ^ ((r / 2) mod 8), so the 16 rows one ds_read_b128 pass serves hit 16
+// distinct bank groups).  All NS stages are in flight with manual vmcnt waits
+// and raw barriers, and the fragment reads of one step overlap the MFMAs of
+// the other:
+//   iteration t (step-0 fragments of stage t already in registers):
+//     read step 1 of stage t; MFMAs of step 0;
+//     wait for this wave's loads of stage t + 1; barrier (now every wave has
+//     finished reading stage t and stage t + 1 has landed everywhere);
+//     issue stage t + NS into the buffer stage t used; read step 0 of stage
+//     t + 1; MFMAs of step 1.
+// Every wave issues exactly QW loads per stage, so the vmcnt thresholds are exact.
+template <int idt, int odt, int BM, int BN, int WGM, int WGN, int NS>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm16_ring(GemmParams p) {
+    constexpr int NW = WGM * WGN;
+    constexpr int WM = BM / WGM, WN = BN / WGN;
+    constexpr int FM = WM / 16, FN = WN / 16;
+    constexpr int ROWB = 128, CPR = 8, RPW = 2, RPI = 8;
+    constexpr int STAGE = (BM + BN) * ROWB;
+    constexpr int QA = BM / RPI, QB = BN / RPI;
+    constexpr int QW = (QA + QB) / NW;
+    static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile");
+    static_assert((QA + QB) % NW == 0, "every wave must issue the same number of loads per stage");
+    static_assert(NS >= 2 && QW * (NS - 1) <= 63, "vmcnt range");
+    __shared__ __attribute__((aligned(1024))) char lds[NS * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WGN, wn = wave % WGN;
+    const int r16 = lane & 15, g = lane >> 4;
+
+    const int ntm = (p.M + BM - 1) / BM, ntn = (p.N + BN - 1) / BN;
+    int tm, tn;
+    tile_coords(blockIdx.x, ntm, ntn, 8, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int nstages = p.K / 64;
+
+    const char *src[QW];
+#pragma unroll
+    for (int j = 0; j < QW; ++j) {
+        const int q = wave + NW * j;
+        const int rloc = (q < QA ? q : q - QA) * RPI + lane / CPR;
+        const int c = (lane % CPR) ^ ((rloc / RPW) % CPR);
+        if (q < QA)
+            src[j] = static_cast<const char *>(p.A) + (int64_t)min(m0 + rloc, p.M - 1) * p.lda * 2 + c * 16;
+        else
+            src[j] = static_cast<const char *>(p.B) + (int64_t)min(n0 + rloc, p.N - 1) * p.ldb * 2 + c * 16;
+    }
+    auto issue = [&](int stage) {
+        const int64_t koff = (int64_t)stage * ROWB;
+        char *buf = lds + (stage % NS) * STAGE;
+#pragma unroll
+        for (int j = 0; j < QW; ++j) {
+            const int q = wave + NW * j;
+            __builtin_amdgcn_global_load_lds(static_cast<const void *>(src[j] + koff), BI_LDS_PTR(buf + q * 1024), 16,
+                                             0, 0);
+        }
+    };
+    auto read_step = [&](int stage, int u, u32x4 (&af)[FM], u32x4 (&bfr)[FN]) {
+        const char *As = lds + (stage % NS) * STAGE;
+        const char *Bs = As + BM * ROWB;
+        const int c = 4 * u + g;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int row = wm * WM + 16 * i + r16;
+            af[i] = *reinterpret_cast<const u32x4 *>(As + row * ROWB + ((c ^ ((row / RPW) % CPR)) << 4));
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int row = wn * WN + 16 * j + r16;
+            bfr[j] = *reinterpret_cast<const u32x4 *>(Bs + row * ROWB + ((c ^ ((row / RPW) % CPR)) << 4));
+        }
+    };
+    f32x4 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = zero4();
+    auto mma = [&](const u32x4 (&af)[FM], const u32x4 (&bfr)[FN]) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) acc[i][j] = Mfma<idt>::step(af[i], bfr[j], acc[i][j]);
+    };
+
+    // prologue: stages 0 .. NS-1 in flight; stage 0 landed everywhere; its step 0 read
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+        if (s < nstages) issue(s);
+    u32x4 a0[FM], b0[FN], a1[FM], b1[FN];
+    if (nstages > 0) {
+        if (nstages >= NS) BI_WAIT_VMCNT(QW * (NS - 1));
+        else BI_WAIT_VMCNT(0);
+        __builtin_amdgcn_s_barrier();
+        read_step(0, 0, a0, b0);
+    }
+    // steady state: every iteration issues stage t + NS and may leave NS - 2 stages in flight
+    const int steady = nstages - NS;
+    int t = 0;
+    for (; t < steady; ++t) {
+        read_step(t, 1, a1, b1);
+        mma(a0, b0);
+        BI_WAIT_VMCNT(QW * (NS - 2));
+        __builtin_amdgcn_s_waitcnt(0xc07f);          // lgkmcnt(0): this wave's LDS reads of stage t are done
+        __builtin_amdgcn_s_barrier();
+        issue(t + NS);
+        read_step(t + 1, 0, a0, b0);
+        mma(a1, b1);
+    }
+    // tail: nothing left to issue; drain
+    for (; t < nstages; ++t) {
+        read_step(t, 1, a1, b1);
+        mma(a0, b0);
+        BI_WAIT_VMCNT(0);
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_s_barrier();
+        if (t + 1 < nstages) read_step(t + 1, 0, a0, b0);
+        mma(a1, b1);
+    }
+    if constexpr (BM * BN * Elem<odt>::bytes <= NS * STAGE) {
+        store_tile16<odt, BM, BN, WGM, WGN>(p, acc, m0, n0, lds);     // the ring's LDS holds the whole tile
+    } else {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int n = n0 + wn * WN + 16 * j + r16;
+                if (n >= p.N) continue;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int m = m0 + wm * WM + 16 * i + 4 * g + e;
+                    if (m < p.M) epilogue<odt>(p, m, n, acc[i][j][e]);
+                }
+            }
+    }
+}
+
+// ============================================================ plan + launch
+// Strip instantiations by M (fragments, A rows per stage, stages, loader
+// waves) and ring tiles, largest first.  The ring plan takes the largest tile
+// that still yields about one tile per CU (192 of 256), else the smallest.
+// Used only to pick a kernel, never changes bits.
+struct StripCfg { int fm, ar, ns, nl; };
+static StripCfg strip_cfg(int M) {
+    if (M <= 4) return StripCfg{1, 4, 6, 3};
+    if (M <= 16) return StripCfg{1, 16, 6, 3};
+    if (M <= 32) return StripCfg{2, 32, 4, 3};
+    return StripCfg{4, 64, 4, 3};
+}
+struct RingCfg { int bm, bn; };
+static const RingCfg kRing[] = {{256, 256}, {256, 128}, {128, 128}, {128, 64}, {64, 64}};
+constexpr long kRingMinTiles = 192;
+
+static RingCfg ring_cfg(int M, int N) {
+    for (const RingCfg &c : kRing) {
+        const long tiles = (long)((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
+        if (tiles >= kRingMinTiles) return c;
+    }
+    return RingCfg{64, 64};
+}
+
+bool gemm16_applies(int M, int N, int K, bool b_kn, int splits) {
+    (void)N;
+    if (b_kn || splits != 1) return false;
+    return M <= 64 || K % 64 == 0;
+}
+
+template <int idt, int odt>
+static hipError_t launch16_typed(const GemmParams &p, hipStream_t st) {
+    if (p.M <= 64) {
+        const StripCfg c = strip_cfg(p.M);
+        const dim3 grid((p.N + 15) / 16), block(64 * (1 + c.nl));
+        if (c.ar == 4) hipLaunchKernelGGL((gemm16_strip<idt, odt, 1, 4, 6, 3>), grid, block, 0, st, p);
+        else if (c.ar == 16) hipLaunchKernelGGL((gemm16_strip<idt, odt, 1, 16, 6, 3>), grid, block, 0, st, p);
+        else if (c.ar == 32) hipLaunchKernelGGL((gemm16_strip<idt, odt, 2, 32, 4, 3>), grid, block, 0, st, p);
+        else hipLaunchKernelGGL((gemm16_strip<idt, odt, 4, 64, 4, 3>), grid, block, 0, st, p);
+        return hipGetLastError();
+    }
+    const RingCfg c = ring_cfg(p.M, p.N);
+    const unsigned tiles = (unsigned)(((p.M + c.bm - 1) / c.bm) * ((p.N + c.bn - 1) / c.bn));
+    if (c.bm == 256 && c.bn == 256)
+        hipLaunchKernelGGL((gemm16_ring<idt, odt, 256, 256, 2, 4, 2>), dim3(tiles), dim3(512), 0, st, p);
+    else if (c.bm == 256)
+        hipLaunchKernelGGL((gemm16_ring<idt, odt, 256, 128, 4, 2, 3>), dim3(tiles), dim3(512), 0, st, p);
+    else if (c.bn == 128)
+        hipLaunchKernelGGL((gemm16_ring<idt, odt, 128, 128, 2, 2, 3>), dim3(tiles), dim3(256), 0, st, p);
+    else if (c.bm == 128)
+        hipLaunchKernelGGL((gemm16_ring<idt, odt, 128, 64, 2, 2, 4>), dim3(tiles), dim3(256), 0, st, p);
+    else
+        hipLaunchKernelGGL((gemm16_ring<idt, odt, 64, 64, 2, 2, 4>), dim3(tiles), dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm16(const GemmParams &p, int in_dt, int out_dt, hipStream_t st) {
+    if (in_dt == DT_BF16 && out_dt == DT_BF16) return launch16_typed<DT_BF16, DT_BF16>(p, st);
+    if (in_dt == DT_F16 && out_dt == DT_F16) return launch16_typed<DT_F16, DT_F16>(p, st);
+    if (in_dt == DT_BF16 && out_dt == DT_F32) return launch16_typed<DT_BF16, DT_F32>(p, st);
+    if (in_dt == DT_F16 && out_dt == DT_F32) return launch16_typed<DT_F16, DT_F32>(p, st);
+    return hipErrorInvalidValue;
+}
+
+const char *gemm16_kernel_name(int M, int N, int K) {
+    (void)K;
+    static thread_local char buf[64];
+    if (M <= 64) snprintf(buf, sizeof buf, "gemm16_strip_nk/a%d", strip_cfg(M).ar);
+    else {
+        const RingCfg c = ring_cfg(M, N);
+        snprintf(buf, sizeof buf, "gemm16_ring_nk/%dx%d", c.bm, c.bn);
+    }
+    return buf;
+}
+
+}  // namespace bi
