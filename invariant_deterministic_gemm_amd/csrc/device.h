@@ -74,15 +74,13 @@ template <> __device__ __forceinline__ uint32_t pack2<DT_F16>(float a, float b) 
     return f32_to_f16(a) | (f32_to_f16(b) << 16);
 }
 
-// ---------------------------------------------------------------- 16x16 MFMA steps
-// 16x16 output-fragment shapes:
+// ---------------------------------------------------------------- the MFMA step
+// One 16x16 output-fragment instruction per input dtype, used by every GEMM
+// and attention kernel:
 //   bf16 / fp16 : v_mfma_f32_16x16x32_{bf16,f16}; a lane holds 8 consecutive
 //                 k of one row (A) or one column (B): lane l covers row /
-//                 column l % 16 and k slots 8*(l/16) .. 8*(l/16)+7.  Used by
-//                 the attention kernels (the 16-bit GEMM chain is the
-//                 32x32x16 one of gemm32.h).
-//   fp32        : v_mfma_f32_16x16x4_f32; lane l holds k slot l/16.  The
-//                 fp32 GEMM chain and the fp32 attention path.
+//                 column l % 16 and k slots 8*(l/16) .. 8*(l/16)+7.
+//   fp32        : v_mfma_f32_16x16x4_f32; lane l holds k slot l/16.
 // The 16x16 fp32 result: lane l, register i holds row 4*(l/16)+i, column l%16.
 template <int dt> struct Mfma;
 template <> struct Mfma<DT_BF16> {
