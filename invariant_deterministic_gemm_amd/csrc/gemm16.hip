@@ -5,11 +5,12 @@
 // with a trip count that depends on K alone; no split-K, no atomics, fp32
 // accumulation, bias added in fp32 and rounded once.  The chain itself is
 // described in gemm16.h.  Two kernels here run it for B in the (N, K) layout:
-//   gemm16_strip  M <= 64: loader wavefronts stream a 16-column strip of the
-//                 weights (and the rows of A) into LDS for one consumer
-//                 wavefront that runs the chains of all M rows;
-//   gemm16_ring   M > 64, K a multiple of 64: LDS tiles fed through a ring of
-//                 stages by direct-to-LDS loads.
+//   gemm16_strip  M <= 32, and M <= 64 unless N is wide: loader wavefronts
+//                 stream a 16- or 32-column strip of the weights (and the
+//                 rows of A) into LDS for one consumer wavefront that runs
+//                 the chains of all M rows;
+//   gemm16_ring   larger M, K a multiple of 64: LDS tiles fed through a ring
+//                 of stages by direct-to-LDS loads.
 // Everything else (row-major (K, N) weights, other K, the split-K comparator)
 // runs the generic kernels of gemm.hip, which implement the same chain.
 #include <cstdio>
@@ -20,24 +21,25 @@
 namespace bi {
 
 // ============================================================ cooperative strip kernel
-// One workgroup per 16 output columns.  NL loader wavefronts stream the
-// strip's 16 weight rows and AR rows of A into an LDS ring with direct-to-LDS
+// One workgroup per strip of 16 NB output columns.  NL loader wavefronts
+// stream the strip's weight rows and AR rows of A into an LDS ring with direct-to-LDS
 // loads, so many more bytes are in flight per strip than one wavefront could
 // keep outstanding.  The consumer wavefront issues no global loads (so memory
-// back-pressure never stalls the chains) and runs FM independent 16-row
-// fragment chains out of LDS, reading stage t + 1 (into a second register
+// back-pressure never stalls the chains) and runs the FM x NB independent
+// 16x16 fragment chains out of LDS, reading stage t + 1 (into a second register
 // set) while the MFMAs of stage t run.
-// A stage covers 128 k: 16 B rows then AR A rows, 256 bytes each, chunk c of
+// A stage covers 128 k: 16 NB B rows then AR A rows, 256 bytes each, chunk c of
 // row r at slot c ^ (r & 15) (the 16 rows one ds_read_b128 pass serves hit 16
 // distinct bank groups).  Load instruction q moves rows 4q .. 4q+3 of the
 // stage (1 KiB); loader l issues instructions l, l + NL, ... (loaders below
 // Q mod NL issue one more, and wait with their own vmcnt thresholds).  Chunks
 // past K are fetched from a clamped in-bounds address and replaced by zeros
 // when read, and steps past the end of the chain are not run.
-template <int idt, int odt, int FM, int AR, int NS, int NL>
+template <int idt, int odt, int NB, int FM, int AR, int NS, int NL>
 __global__ __launch_bounds__(64 * (1 + NL)) void gemm16_strip(GemmParams p) {
     constexpr int ROWB = 256;
-    constexpr int QB = 4, QA = AR / 4, Q = QB + QA;
+    constexpr int SW = 16 * NB;                  // strip width: NB 16-column fragments
+    constexpr int QB = SW / 4, QA = AR / 4, Q = QB + QA;
     constexpr int QHI = (Q + NL - 1) / NL, QLO = Q / NL, NHI = Q % NL;
     constexpr int STAGE = Q * 1024;
     static_assert(AR % 4 == 0 && AR >= 4 && AR <= 16 * FM, "A rows per stage");
@@ -46,7 +48,7 @@ __global__ __launch_bounds__(64 * (1 + NL)) void gemm16_strip(GemmParams p) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int n0 = blockIdx.x * 16;
+    const int n0 = blockIdx.x * SW;
     const int nchunk = p.K >> 3;                 // 16-byte chunks per row
     const int nstages = (p.K + 127) >> 7;
     const int total_steps = p.total_steps;
@@ -62,10 +64,10 @@ __global__ __launch_bounds__(64 * (1 + NL)) void gemm16_strip(GemmParams p) {
         const int q = min(lw + NL * j, Q - 1);
         const int row = 4 * q + (lane >> 4);
         cl[j] = (lane & 15) ^ (row & 15);
-        if (row < 16)
+        if (row < SW)
             src[j] = static_cast<const char *>(p.B) + (int64_t)min(n0 + row, p.N - 1) * p.ldb * 2;
         else
-            src[j] = static_cast<const char *>(p.A) + (int64_t)min(row - 16, p.M - 1) * p.lda * 2;
+            src[j] = static_cast<const char *>(p.A) + (int64_t)min(row - SW, p.M - 1) * p.lda * 2;
     }
     auto issue = [&](int stage) {
         char *buf = lds + (stage % NS) * STAGE;
@@ -98,42 +100,49 @@ __global__ __launch_bounds__(64 * (1 + NL)) void gemm16_strip(GemmParams p) {
     int aoff[FM], aswz[FM];
 #pragma unroll
     for (int f = 0; f < FM; ++f) {
-        const int arow = 16 + min(16 * f + r16, AR - 1);
+        const int arow = SW + min(16 * f + r16, AR - 1);
         aoff[f] = arow * ROWB;
         aswz[f] = arow & 15;
     }
-    const int boff = r16 * ROWB;
-    f32x4 acc[FM];
+    f32x4 acc[NB][FM];
 #pragma unroll
-    for (int f = 0; f < FM; ++f) acc[f] = zero4();
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int f = 0; f < FM; ++f) acc[j][f] = zero4();
     // two register sets: the fragments of stage t and those of stage t + 1
-    u32x4 xa[4][FM], xb[4], ya[4][FM], yb[4];
-    auto read_stage = [&](int stage, u32x4 (&a)[4][FM], u32x4 (&b)[4]) {
+    u32x4 xa[4][FM], xb[4][NB], ya[4][FM], yb[4][NB];
+    auto read_stage = [&](int stage, u32x4 (&a)[4][FM], u32x4 (&b)[4][NB]) {
         const char *buf = lds + (stage % NS) * STAGE;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int c = 4 * u + g;
-            b[u] = *reinterpret_cast<const u32x4 *>(buf + boff + ((c ^ r16) << 4));
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+                b[u][j] = *reinterpret_cast<const u32x4 *>(buf + (16 * j + r16) * ROWB + ((c ^ r16) << 4));
 #pragma unroll
             for (int f = 0; f < FM; ++f)
                 a[u][f] = *reinterpret_cast<const u32x4 *>(buf + aoff[f] + ((c ^ aswz[f]) << 4));
         }
     };
-    auto mma_stage = [&](const u32x4 (&a)[4][FM], const u32x4 (&b)[4]) {
+    auto mma_stage = [&](const u32x4 (&a)[4][FM], const u32x4 (&b)[4][NB]) {
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
-            for (int f = 0; f < FM; ++f) acc[f] = Mfma<idt>::step(a[u][f], b[u], acc[f]);
+            for (int j = 0; j < NB; ++j)
+#pragma unroll
+                for (int f = 0; f < FM; ++f) acc[j][f] = Mfma<idt>::step(a[u][f], b[u][j], acc[j][f]);
     };
     // the last stage: only steps of the chain, chunks past K read as zero
-    auto mma_last = [&](int stage, const u32x4 (&a)[4][FM], const u32x4 (&b)[4]) {
+    auto mma_last = [&](int stage, const u32x4 (&a)[4][FM], const u32x4 (&b)[4][NB]) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             if (stage * 4 + u < total_steps) {
                 const bool past = stage * 16 + 4 * u + g >= nchunk;
-                const u32x4 bb = past ? zero_u4() : b[u];
 #pragma unroll
-                for (int f = 0; f < FM; ++f) acc[f] = Mfma<idt>::step(past ? zero_u4() : a[u][f], bb, acc[f]);
+                for (int j = 0; j < NB; ++j)
+#pragma unroll
+                    for (int f = 0; f < FM; ++f)
+                        acc[j][f] = Mfma<idt>::step(past ? zero_u4() : a[u][f], past ? zero_u4() : b[u][j], acc[j][f]);
             }
         }
     };
@@ -197,14 +206,16 @@ __global__ __launch_bounds__(64 * (1 + NL)) void gemm16_strip(GemmParams p) {
         else mma_last(nstages - 1, xa, xb);
     }
     if (!consumer) return;
-    const int n = n0 + r16;
-    if (n < p.N) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+        const int n = n0 + 16 * j + r16;
+        if (n >= p.N) continue;
 #pragma unroll
         for (int f = 0; f < FM; ++f)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int m = 16 * f + 4 * g + i;
-                if (m < p.M) epilogue<odt>(p, m, n, acc[f][i]);
+                if (m < p.M) epilogue<odt>(p, m, n, acc[j][f][i]);
             }
     }
 }
@@ -419,12 +430,22 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm16_ring(GemmParams p) {
 // waves) and ring tiles, largest first.  The ring plan takes the largest tile
 // that still yields about one tile per CU (192 of 256), else the smallest.
 // Used only to pick a kernel, never changes bits.
-struct StripCfg { int fm, ar, ns, nl; };
-static StripCfg strip_cfg(int M) {
-    if (M <= 4) return StripCfg{1, 4, 6, 3};
-    if (M <= 16) return StripCfg{1, 16, 6, 3};
-    if (M <= 32) return StripCfg{2, 32, 4, 3};
-    return StripCfg{4, 64, 4, 3};
+struct StripCfg { int nb, fm, ar, ns, nl; };
+// More than one 16-column strip per CU: A re-reads from L2 start to cost.
+static bool wide_n(int N) { return (N + 15) / 16 > 256; }
+static StripCfg strip_cfg(int M, int N) {
+    // 32-column strips halve the re-reads of A once N is wide
+    if (M <= 4) return StripCfg{1, 1, 4, 6, 3};
+    if (M <= 16) return StripCfg{1, 1, 16, 6, 3};
+    if (M <= 32) return wide_n(N) ? StripCfg{2, 2, 32, 4, 3} : StripCfg{1, 2, 32, 4, 3};
+    return wide_n(N) ? StripCfg{2, 4, 64, 3, 3} : StripCfg{1, 4, 64, 4, 3};
+}
+// Strip for M <= 32; for M <= 64 too unless N is wide and the ring applies
+// (at M > 32 the ring's tiles re-read far less of A than 32-column strips).
+static bool use_strip(int M, int N, int K) {
+    if (M <= 32) return true;
+    if (M <= 64) return !(wide_n(N) && K % 64 == 0);
+    return false;
 }
 struct RingCfg { int bm, bn; };
 static const RingCfg kRing[] = {{256, 256}, {256, 128}, {128, 128}, {128, 64}, {64, 64}};
@@ -446,13 +467,15 @@ bool gemm16_applies(int M, int N, int K, bool b_kn, int splits) {
 
 template <int idt, int odt>
 static hipError_t launch16_typed(const GemmParams &p, hipStream_t st) {
-    if (p.M <= 64) {
-        const StripCfg c = strip_cfg(p.M);
-        const dim3 grid((p.N + 15) / 16), block(64 * (1 + c.nl));
-        if (c.ar == 4) hipLaunchKernelGGL((gemm16_strip<idt, odt, 1, 4, 6, 3>), grid, block, 0, st, p);
-        else if (c.ar == 16) hipLaunchKernelGGL((gemm16_strip<idt, odt, 1, 16, 6, 3>), grid, block, 0, st, p);
-        else if (c.ar == 32) hipLaunchKernelGGL((gemm16_strip<idt, odt, 2, 32, 4, 3>), grid, block, 0, st, p);
-        else hipLaunchKernelGGL((gemm16_strip<idt, odt, 4, 64, 4, 3>), grid, block, 0, st, p);
+    if (use_strip(p.M, p.N, p.K)) {
+        const StripCfg c = strip_cfg(p.M, p.N);
+        const dim3 grid((p.N + 16 * c.nb - 1) / (16 * c.nb)), block(64 * (1 + c.nl));
+        if (c.ar == 4) hipLaunchKernelGGL((gemm16_strip<idt, odt, 1, 1, 4, 6, 3>), grid, block, 0, st, p);
+        else if (c.ar == 16) hipLaunchKernelGGL((gemm16_strip<idt, odt, 1, 1, 16, 6, 3>), grid, block, 0, st, p);
+        else if (c.ar == 32 && c.nb == 1) hipLaunchKernelGGL((gemm16_strip<idt, odt, 1, 2, 32, 4, 3>), grid, block, 0, st, p);
+        else if (c.ar == 32) hipLaunchKernelGGL((gemm16_strip<idt, odt, 2, 2, 32, 4, 3>), grid, block, 0, st, p);
+        else if (c.nb == 1) hipLaunchKernelGGL((gemm16_strip<idt, odt, 1, 4, 64, 4, 3>), grid, block, 0, st, p);
+        else hipLaunchKernelGGL((gemm16_strip<idt, odt, 2, 4, 64, 3, 3>), grid, block, 0, st, p);
         return hipGetLastError();
     }
     const RingCfg c = ring_cfg(p.M, p.N);
@@ -479,9 +502,11 @@ hipError_t launch_gemm16(const GemmParams &p, int in_dt, int out_dt, hipStream_t
 }
 
 const char *gemm16_kernel_name(int M, int N, int K) {
-    (void)K;
     static thread_local char buf[64];
-    if (M <= 64) snprintf(buf, sizeof buf, "gemm16_strip_nk/a%d", strip_cfg(M).ar);
+    if (use_strip(M, N, K)) {
+        const StripCfg c = strip_cfg(M, N);
+        snprintf(buf, sizeof buf, "gemm16_strip_nk/w%d_a%d", 16 * c.nb, c.ar);
+    }
     else {
         const RingCfg c = ring_cfg(M, N);
         snprintf(buf, sizeof buf, "gemm16_ring_nk/%dx%d", c.bm, c.bn);
