@@ -52,7 +52,7 @@ TRAFFIC_MD = os.path.join(ROOT, "profiles", "bench_step_bf16_gemm_sweep_sdpa_swe
 CALIB_BYTES = 256 * 2 ** 20     # bytes read and bytes written by the calibration copy
 # sources whose text fixes each kernel family's memory traffic
 FAMILY_SOURCES = {
-    "gemm": ["device.h", "gemm.h", "gemm_common.h", "gemm32.h", "gemm32.hip", "gemm.hip", "api.hip"],
+    "gemm": ["device.h", "gemm.h", "gemm_common.h", "gemm16.h", "gemm16.hip", "gemm.hip", "api.hip"],
     "sdpa": ["device.h", "sdpa.h", "sdpa.hip", "api.hip"],
 }
 

@@ -257,6 +257,338 @@ __global__ __launch_bounds__(64) void sdpa_split(SdpaParams p) {
     }
 }
 
+// 16-bit inputs, D = 128: the same arithmetic as sdpa_split (bit for bit), with
+// the K and V blocks loaded into LDS by direct-to-LDS loads and no registers
+// held for them: the next block's K is requested as soon as this block's
+// scores have read K, its V as soon as P.V has read V, so each transfer
+// overlaps the other half of the block's work (32 KiB of LDS per wavefront,
+// five wavefronts per CU).  LDS rows are the 256-byte key rows; K chunk c of
+// row r sits at slot c ^ (r mod 16) (the 16 key rows one fragment read serves
+// hit 16 distinct bank groups), V chunk c at slot c ^ 2 (r mod 8) (the four
+// 32-byte row pieces one transpose read serves hit distinct banks).  The P.V
+// operand is gathered with ds_read_b64_tr_b16: within each 16-lane group,
+// output lane i element v is element i mod 4 of source lane i / 4 + 4 v, so
+// source lane j points at key row base + j / 4, columns 16 t + 4 (j mod 4).
+// Keys past S are loaded from a clamped row and their V rows are zeroed in
+// LDS before use (their scores are -inf anyway).
+// P rounded to the input dtype, two values per dword (low = a).  P is finite
+// and in [0, 1]; bf16 uses the gfx950 round-to-nearest-even pack instruction.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+template <int dt> __device__ __forceinline__ uint32_t pack_p(float a, float b) {
+    if constexpr (dt == DT_BF16) return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)a, (__bf16)b});
+    else return pack2<dt>(a, b);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_read_tr16(const char *lds_addr) {
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4 *)((__attribute__((address_space(3))) char *)lds_addr));
+    return __builtin_bit_cast(u32x2, v);
+}
+
+// One wavefront's share: split `sp` of row tile `tile` of (b, gk), its K / V
+// blocks staged in `lds` (2 * KV_BLOCK * 256 bytes); leaves the split's
+// (m, l) of row r16 and its O fragment (rows 4 g + i, columns 16 t + r16).
+template <int dt>
+__device__ __forceinline__ void split16_body(const SdpaParams &p, int sp, int tile, int b, int gk, char *lds,
+                                             float &m_out, float &l_out, f32x4 (&o)[8]) {
+    constexpr int D = 128;
+    constexpr int ROWB = D * 2;                       // bytes per key row
+    constexpr int KBYTES = KV_BLOCK * ROWB;           // one K (or V) block
+    constexpr int QB = KBYTES / 1024;                 // 1 KiB load instructions per block half
+    static_assert(QB == 16, "four key rows per load instruction");
+    constexpr float NEG_INF = -__builtin_huge_valf();
+    const int lane = threadIdx.x & 63;
+    const int r16 = lane & 15;
+    const int g = lane >> 4;
+    const int R = p.G * p.Lq;
+
+    const int rg = tile * 16 + r16;
+    const bool row_ok = rg < R;
+    const int rgc = min(rg, R - 1);
+    const int iq = rgc / p.G;
+    const int h = gk * p.G + rgc % p.G;
+    const int pos = p.S - p.Lq + iq;
+
+    const int kbeg = sp * KV_SPLIT;
+    const int kend = min(kbeg + KV_SPLIT, p.S);
+    int nblk = (kend - kbeg + KV_BLOCK - 1) / KV_BLOCK;
+    if (p.causal) {
+        const int rlast = min(tile * 16 + 15, R - 1);
+        const int pos_last = p.S - p.Lq + rlast / p.G;
+        nblk = pos_last < kbeg ? 0 : min(nblk, (pos_last - kbeg) / KV_BLOCK + 1);
+    }
+
+    const char *qrow = static_cast<const char *>(p.q) +
+                       ((int64_t)b * p.qs[0] + (int64_t)h * p.qs[1] + (int64_t)iq * p.qs[2]) * 2;
+    const char *kbase = static_cast<const char *>(p.k) + ((int64_t)b * p.ks[0] + (int64_t)gk * p.ks[1]) * 2;
+    const char *vbase = static_cast<const char *>(p.v) + ((int64_t)b * p.vs[0] + (int64_t)gk * p.vs[1]) * 2;
+    const uint8_t *mrow = p.mask ? p.mask + (int64_t)b * p.ms[0] + (int64_t)h * p.ms[1] + (int64_t)iq * p.ms[2]
+                                 : nullptr;
+
+    // load side: instruction q covers key rows 4 q .. 4 q + 3 of the block; lane L row 4 q + L / 16,
+    // slot L mod 16.  The swizzled chunk depends on q only through q mod 4 (K) and q mod 2 (V), so the
+    // per-lane parts are computed once and a block's addresses are one base plus multiples of the stride.
+    const int lrow = lane >> 4, lslot = lane & 15;
+    const int64_t kstr = p.ks[2] * 2, vstr = p.vs[2] * 2;      // bytes between key rows
+    const char *klane = kbase + lrow * kstr;
+    const char *vlane = vbase + lrow * vstr;
+    int kch[4], vch[2];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) kch[r] = (lslot ^ ((4 * r + lrow) & 15)) << 4;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) vch[r] = (lslot ^ (((4 * r + lrow) & 7) << 1)) << 4;
+    auto issueK = [&](int blk) {
+        const int kb = kbeg + blk * KV_BLOCK;
+        if (kb + KV_BLOCK <= p.S) {
+            const char *bp = klane + (int64_t)kb * kstr;
+#pragma unroll
+            for (int q = 0; q < QB; ++q) {
+                __builtin_amdgcn_global_load_lds(static_cast<const void *>(bp + kch[q & 3]),
+                                                 BI_LDS_PTR(lds + q * 1024), 16, 0, 0);
+                bp += 4 * kstr;
+            }
+        } else {                                       // the block crosses S: rows past it read row S - 1
+#pragma unroll
+            for (int q = 0; q < QB; ++q) {
+                const int key = min(kb + 4 * q + lrow, p.S - 1);
+                __builtin_amdgcn_global_load_lds(static_cast<const void *>(kbase + key * kstr + kch[q & 3]),
+                                                 BI_LDS_PTR(lds + q * 1024), 16, 0, 0);
+            }
+        }
+    };
+    auto issueV = [&](int blk) {
+        const int kb = kbeg + blk * KV_BLOCK;
+        if (kb + KV_BLOCK <= p.S) {
+            const char *bp = vlane + (int64_t)kb * vstr;
+#pragma unroll
+            for (int q = 0; q < QB; ++q) {
+                __builtin_amdgcn_global_load_lds(static_cast<const void *>(bp + vch[q & 1]),
+                                                 BI_LDS_PTR(lds + KBYTES + q * 1024), 16, 0, 0);
+                bp += 4 * vstr;
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < QB; ++q) {
+                const int key = min(kb + 4 * q + lrow, p.S - 1);
+                __builtin_amdgcn_global_load_lds(static_cast<const void *>(vbase + key * vstr + vch[q & 1]),
+                                                 BI_LDS_PTR(lds + KBYTES + q * 1024), 16, 0, 0);
+            }
+        }
+    };
+    // the tile's first row has the smallest query position: a block wholly at or before it, inside S
+    // and without a mask, is visible to every row and needs no per-key test
+    const int pos_first = p.S - p.Lq + (tile * 16) / p.G;
+
+    u32x4 qf[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) qf[c] = ldg16(qrow + (32 * c + 8 * g) * 2);
+
+    float m_run = NEG_INF, l_run = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) o[t] = zero4();
+
+    if (nblk > 0) {
+        issueK(0);
+        issueV(0);
+    }
+    for (int blk = 0; blk < nblk; ++blk) {
+        const int kb = kbeg + blk * KV_BLOCK;
+        const char *Ks = lds;
+        const char *Vs = lds + KBYTES;
+        BI_WAIT_VMCNT(QB);                            // K of this block landed (its V may be in flight)
+        // ---- scores: lane holds S^T[key 16 kt + 4 g + i][row r16]
+        f32x4 st[4];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+            st[kt] = zero4();
+            const int row = 16 * kt + r16;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const u32x4 kf = *reinterpret_cast<const u32x4 *>(Ks + row * ROWB + (((4 * c + g) ^ (row & 15)) << 4));
+                st[kt] = Mfma<dt>::step(kf, qf[c], st[kt]);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);           // every K read of this block done
+        if (blk + 1 < nblk) issueK(blk + 1);
+        float s[4][4];
+        float mb = NEG_INF;
+        const bool visible = p.mask == nullptr && kb + KV_BLOCK <= p.S && (!p.causal || kb + KV_BLOCK - 1 <= pos_first);
+        if (visible) {
+            // rows past R get real scores too: they are per-row, never stored, and touch no other row
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    s[kt][i] = st[kt][i] * p.c;
+                    mb = fmaxf(mb, s[kt][i]);
+                }
+        } else {
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int key = kb + 16 * kt + 4 * g + i;
+                    bool ok = row_ok && key < p.S;
+                    if (p.causal) ok = ok && key <= pos;
+                    if (mrow) ok = ok && mrow[(int64_t)key * p.ms[3]] != 0;
+                    const float sv = st[kt][i] * p.c;
+                    s[kt][i] = ok ? sv : NEG_INF;
+                    mb = fmaxf(mb, s[kt][i]);
+                }
+        }
+        mb = fmaxf(mb, __shfl_xor(mb, 16));
+        mb = fmaxf(mb, __shfl_xor(mb, 32));
+        const bool empty = mb == NEG_INF;
+        const float m_new = empty ? m_run : fmaxf(m_run, mb);
+        const float alpha = empty ? 1.0f : exp2_hw(m_run - m_new);
+        float pr[4][4];
+        float rs = 0.0f;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                pr[kt][i] = s[kt][i] == NEG_INF ? 0.0f : exp2_hw(s[kt][i] - m_new);
+                rs = rs + pr[kt][i];
+            }
+        rs = rs + __shfl_xor(rs, 16);
+        rs = rs + __shfl_xor(rs, 32);
+        l_run = __builtin_fmaf(l_run, alpha, rs);
+        m_run = m_new;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float ai = __shfl(alpha, 4 * g + i);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) o[t][i] = o[t][i] * ai;
+        }
+        if (blk + 1 < nblk) BI_WAIT_VMCNT(QB);         // V of this block landed (next K may be in flight)
+        else BI_WAIT_VMCNT(0);
+        if (kb + KV_BLOCK > p.S) {
+            for (int row = max(p.S - kb, 0) + lrow; row < KV_BLOCK; row += 4)
+                *reinterpret_cast<u32x4 *>(const_cast<char *>(Vs) + row * ROWB + lslot * 16) = zero_u4();
+            __builtin_amdgcn_s_waitcnt(0xc07f);
+        }
+        // ---- O += P . V: k slot 8 g + j <-> key 32 c + 4 g + j (j < 4), 32 c + 16 + 4 g + (j - 4) (j >= 4)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const u32x4 pf = u32x4{pack_p<dt>(pr[2 * c][0], pr[2 * c][1]), pack_p<dt>(pr[2 * c][2], pr[2 * c][3]),
+                                   pack_p<dt>(pr[2 * c + 1][0], pr[2 * c + 1][1]),
+                                   pack_p<dt>(pr[2 * c + 1][2], pr[2 * c + 1][3])};
+            const int row0 = 32 * c + 4 * g + (r16 >> 2);
+            const int row1 = row0 + 16;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const int ch = 2 * t + ((r16 & 3) >> 1);
+                const int off = 8 * (r16 & 1);
+                const u32x2 lo = lds_read_tr16(Vs + row0 * ROWB + ((ch ^ ((row0 & 7) << 1)) << 4) + off);
+                const u32x2 hi = lds_read_tr16(Vs + row1 * ROWB + ((ch ^ ((row1 & 7) << 1)) << 4) + off);
+                o[t] = Mfma<dt>::step(pf, u32x4{lo[0], lo[1], hi[0], hi[1]}, o[t]);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);           // every V read of this block done
+        if (blk + 1 < nblk) issueV(blk + 1);
+    }
+
+    m_out = m_run;
+    l_out = l_run;
+}
+
+template <int dt>
+__global__ __launch_bounds__(64) void sdpa_split16(SdpaParams p) {
+    __shared__ __attribute__((aligned(1024))) char lds[2 * KV_BLOCK * 256];   // K block, then V block
+    const int lane = threadIdx.x;
+    const int r16 = lane & 15, g = lane >> 4;
+    const int sp = blockIdx.x, tile = blockIdx.y;
+    const int b = blockIdx.z / p.Hkv, gk = blockIdx.z % p.Hkv;
+    const int R = p.G * p.Lq;
+    float m_run, l_run;
+    f32x4 o[8];
+    split16_body<dt>(p, sp, tile, b, gk, lds, m_run, l_run, o);
+    const int rg = tile * 16 + r16;
+    if (g == 0 && rg < R) {
+        const int64_t rowid = ((int64_t)b * p.Hq + gk * p.G + rg % p.G) * p.Lq + rg / p.G;
+        float *ml = p.ws_ml + (rowid * p.nsplit + sp) * 2;
+        ml[0] = m_run;
+        ml[1] = l_run;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int ro = tile * 16 + 4 * g + i;
+        if (ro < R) {
+            const int64_t rowid = ((int64_t)b * p.Hq + gk * p.G + ro % p.G) * p.Lq + ro / p.G;
+            float *dst = p.ws_o + (rowid * p.nsplit + sp) * 128;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) dst[16 * t + r16] = o[t][i];
+        }
+    }
+}
+
+// Short KV (at most MAXW splits): one workgroup per row tile with one
+// wavefront per split, the split partials exchanged through LDS and folded
+// in the workgroup with exactly sdpa_combine's arithmetic (ascending split
+// order, same operations), so the result is bit-identical to the two-kernel
+// path and needs no workspace round trip or second launch.
+constexpr int FUSED_MAXW = 4;
+template <int dt>
+__global__ __launch_bounds__(64 * FUSED_MAXW) void sdpa_fused16(SdpaParams p) {
+    constexpr float NEG_INF = -__builtin_huge_valf();
+    constexpr int D = 128;
+    constexpr int PER_WAVE = 2 * KV_BLOCK * 256;
+    __shared__ __attribute__((aligned(1024))) char lds[FUSED_MAXW * PER_WAVE];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nw = blockDim.x >> 6;                  // == nsplit
+    const int r16 = lane & 15, g = lane >> 4;
+    const int tile = blockIdx.x;
+    const int b = blockIdx.y / p.Hkv, gk = blockIdx.y % p.Hkv;
+    const int R = p.G * p.Lq;
+    float m_run, l_run;
+    f32x4 o[8];
+    split16_body<dt>(p, wave, tile, b, gk, lds + wave * PER_WAVE, m_run, l_run, o);
+    __syncthreads();                                 // every wavefront is done with its K / V blocks
+    float *pml = reinterpret_cast<float *>(lds);                     // [split][16 rows][2]
+    float *po = pml + FUSED_MAXW * 16 * 2;                           // [split][16 rows][D]
+    if (g == 0) {
+        pml[(wave * 16 + r16) * 2] = m_run;
+        pml[(wave * 16 + r16) * 2 + 1] = l_run;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) po[(wave * 16 + 4 * g + i) * D + 16 * t + r16] = o[t][i];
+    __syncthreads();
+    for (int e = tid; e < 16 * D; e += 64 * nw) {
+        const int row = e / D, d = e % D;
+        const int ro = tile * 16 + row;
+        if (ro >= R) continue;
+        bool have = false;
+        float m = 0.0f, l = 0.0f, acc = 0.0f;
+        for (int sp = 0; sp < nw; ++sp) {
+            const float ms = pml[(sp * 16 + row) * 2], ls = pml[(sp * 16 + row) * 2 + 1];
+            if (ms == NEG_INF) continue;
+            const float os = po[(sp * 16 + row) * D + d];
+            if (!have) {
+                m = ms;
+                l = ls;
+                acc = os;
+                have = true;
+                continue;
+            }
+            const float m2 = fmaxf(m, ms);
+            const float a = exp2_hw(m - m2);
+            const float bs = exp2_hw(ms - m2);
+            l = __builtin_fmaf(l, a, ls * bs);
+            acc = __builtin_fmaf(acc, a, os * bs);
+            m = m2;
+        }
+        float r = have ? acc / l : 0.0f;
+        r = r + 0.0f;                                // -0 -> +0
+        const int iq = ro / p.G, h = gk * p.G + ro % p.G;
+        char *orow = static_cast<char *>(p.o) +
+                     ((int64_t)b * p.os[0] + (int64_t)h * p.os[1] + (int64_t)iq * p.os[2]) * Elem<dt>::bytes;
+        store_from_f32<dt>(orow, d, r);
+    }
+}
+
 // Fold the split partials of one query row left to right, normalise, round.
 template <int dt, int D>
 __global__ __launch_bounds__(64) void sdpa_combine(SdpaParams p) {
@@ -323,9 +655,17 @@ void sdpa_bind_workspace(SdpaParams &p, void *ws, int D) {
 template <int dt, int D>
 static hipError_t launch_typed(const SdpaParams &p, hipStream_t st) {
     const int R = p.G * p.Lq;
+    if constexpr (dt != DT_F32 && D == 128) {
+        if (p.nsplit >= 1 && p.nsplit <= FUSED_MAXW) {
+            const dim3 gf((unsigned)((R + 15) / 16), (unsigned)(p.B * p.Hkv));
+            hipLaunchKernelGGL((sdpa_fused16<dt>), gf, dim3(64 * p.nsplit), 0, st, p);
+            return hipGetLastError();
+        }
+    }
     if (p.nsplit > 0) {
         const dim3 g1((unsigned)p.nsplit, (unsigned)((R + 15) / 16), (unsigned)(p.B * p.Hkv));
-        hipLaunchKernelGGL((sdpa_split<dt, D>), g1, dim3(64), 0, st, p);
+        if constexpr (dt != DT_F32 && D == 128) hipLaunchKernelGGL((sdpa_split16<dt>), g1, dim3(64), 0, st, p);
+        else hipLaunchKernelGGL((sdpa_split<dt, D>), g1, dim3(64), 0, st, p);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -157,6 +157,28 @@ def test_config4_context_growth_with_masked_keys(dt):
         prev = bi.bi_sdpa(q, k[:, :, :n], v[:, :, :n])
 
 
+@pytest.mark.parametrize("dt", DTS, ids=_ids)
+def test_context_growth_across_split_counts(dt):
+    """Masked keys appended past 256, 512, 768 and 1024 keys (where the number
+    of 256-key splits, and with it the launch shape, changes) leave the bits
+    unchanged; decode and a 5-token chunk both."""
+    S_max = 1100
+    q = synthetic.randn((2, 16, 5, 128), 0x5EED40, 1.0, dt).to(DEV)
+    k = synthetic.randn((2, 8, S_max, 128), 0x5EED41, 1.0, dt).to(DEV)
+    v = synthetic.randn((2, 8, S_max, 128), 0x5EED42, 1.0, dt).to(DEV)
+    for n0 in (250, 256, 500, 700, 1000, 1024):
+        for L in (1, 5):
+            base = bi.bi_sdpa(q[:, :, :L], k[:, :, :n0], v[:, :, :n0], causal=True)
+            for n in sorted({n0 + 1, n0 + 7, 257, 513, 769, 1025, 1100}):
+                if n <= n0:
+                    continue
+                m = torch.zeros(1, 1, L, n, dtype=torch.bool, device=DEV)
+                for i in range(L):
+                    m[..., i, :n0 - L + 1 + i] = True
+                o = bi.bi_sdpa(q[:, :, :L], k[:, :, :n], v[:, :, :n], mask=m)
+                assert_bits_equal(o, base, f"{dt} q_len={L}: S={n} with keys >= {n0} masked vs S={n0}")
+
+
 def test_causal_and_masked_key_values_are_never_read():
     B, Hq, Hkv, L, S, D = 1, 8, 2, 40, 600, 128
     q = synthetic.randn((B, Hq, L, D), 81, 1.0, torch.bfloat16).to(DEV)
