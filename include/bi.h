@@ -205,6 +205,13 @@ int bi_variant_splits(int64_t M);
  * Returns "none" for empty or oversized shapes. */
 const char *bi_gemm_kernel_name(int64_t M, int64_t N, int64_t K, bi_dtype in_dt, int b_kn);
 
+/* Which attention kernels a bi_sdpa call of these sizes runs ("sdpa_fused16" for
+ * 16-bit D = 128 with S <= 1024, "sdpa_split16+combine" above, "sdpa_split+combine"
+ * for fp32 and D = 64).  Informational: the split / block structure, and with it
+ * every output bit, is the same whichever runs.  Returns "none" for empty,
+ * oversized or unsupported sizes. */
+const char *bi_sdpa_kernel_name(int64_t B, int64_t Hq, int64_t Lq, int64_t S, int64_t D, bi_dtype dt);
+
 /* Name of a status code ("BI_OK", ...); never NULL. */
 const char *bi_status_name(bi_status s);
 /* Message describing the last error on the calling thread; "" after success.

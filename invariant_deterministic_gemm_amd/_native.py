@@ -32,6 +32,7 @@ SIGNATURES = {
     "bi_variant_workspace_bytes": (_sz, [_i64, _i64, _i]),
     "bi_variant_splits": (_i, [_i64]),
     "bi_gemm_kernel_name": (ctypes.c_char_p, [_i64, _i64, _i64, _i, _i]),
+    "bi_sdpa_kernel_name": (ctypes.c_char_p, [_i64, _i64, _i64, _i64, _i64, _i]),
     "bi_status_name": (ctypes.c_char_p, [_i]),
     "bi_last_error": (ctypes.c_char_p, []),
     "bi_abi_version": (_i, []),

@@ -316,6 +316,13 @@ const char *bi_gemm_kernel_name(int64_t M, int64_t N, int64_t K, bi_dtype in_dt,
     return bi::gemm_kernel_name((int)M, (int)N, (int)K, (int)in_dt, b_kn != 0);
 }
 
+const char *bi_sdpa_kernel_name(int64_t B, int64_t Hq, int64_t Lq, int64_t S, int64_t D, bi_dtype dt) {
+    if (B <= 0 || Hq <= 0 || Lq <= 0 || S <= 0 || B > kMaxDim || Hq > kMaxDim || Lq > kMaxDim || S > kMaxDim ||
+        (D != 64 && D != 128) || !dtype_known(dt))
+        return "none";
+    return bi::sdpa_kernel_name((int)S, (int)D, (int)dt);
+}
+
 const char *bi_status_name(bi_status s) {
     switch (s) {
         case BI_OK: return "BI_OK";

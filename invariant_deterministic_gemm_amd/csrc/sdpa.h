@@ -29,5 +29,7 @@ size_t sdpa_workspace_bytes(int64_t B, int64_t Hq, int64_t Lq, int64_t S, int64_
 // Carves ws into ws_ml / ws_o and sets nsplit.
 void sdpa_bind_workspace(SdpaParams &p, void *ws, int D);
 hipError_t launch_sdpa(const SdpaParams &p, int dt, int D, hipStream_t stream);
+// Names of the kernels launch_sdpa runs for a KV length S ("sdpa_fused16", ...).
+const char *sdpa_kernel_name(int S, int D, int dt);
 
 }  // namespace bi

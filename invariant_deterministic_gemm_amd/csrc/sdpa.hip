@@ -674,6 +674,12 @@ static hipError_t launch_typed(const SdpaParams &p, hipStream_t st) {
     return hipGetLastError();
 }
 
+const char *sdpa_kernel_name(int S, int D, int dt) {
+    const int nsplit = (S + KV_SPLIT - 1) / KV_SPLIT;
+    if (dt != DT_F32 && D == 128) return nsplit <= FUSED_MAXW ? "sdpa_fused16" : "sdpa_split16+combine";
+    return "sdpa_split+combine";
+}
+
 hipError_t launch_sdpa(const SdpaParams &p, int dt, int D, hipStream_t st) {
     if (dt == DT_BF16 && D == 128) return launch_typed<DT_BF16, 128>(p, st);
     if (dt == DT_BF16 && D == 64) return launch_typed<DT_BF16, 64>(p, st);

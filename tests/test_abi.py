@@ -161,3 +161,16 @@ def test_python_binding_rejects_cpu_tensors_and_dtypes():
     with pytest.raises(ValueError):
         bi.scaled_dot_product_attention(torch.zeros(1, 1, 1, 64), torch.zeros(1, 1, 1, 64),
                                         torch.zeros(1, 1, 1, 64), mask="sliding")
+
+
+def test_kernel_name_queries(lib):
+    assert lib.bi_sdpa_kernel_name(1, 32, 1, 1024, 128, BF16).decode() == "sdpa_fused16"
+    assert lib.bi_sdpa_kernel_name(1, 32, 64, 1025, 128, F16).decode() == "sdpa_split16+combine"
+    assert lib.bi_sdpa_kernel_name(1, 32, 1, 300, 128, F32).decode() == "sdpa_split+combine"
+    assert lib.bi_sdpa_kernel_name(1, 32, 1, 300, 64, BF16).decode() == "sdpa_split+combine"
+    for bad in ((0, 32, 1, 10, 128, BF16), (1, 32, 1, 0, 128, BF16), (1, 32, 1, 10, 96, BF16),
+                (1, 32, 1, 10, 128, 7)):
+        assert lib.bi_sdpa_kernel_name(*bad).decode() == "none"
+    assert lib.bi_gemm_kernel_name(1, 4096, 4096, BF16, 0).decode().startswith("gemm16_strip_nk/")
+    assert lib.bi_gemm_kernel_name(4096, 4096, 4096, BF16, 0).decode().startswith("gemm16_ring_nk/")
+    assert lib.bi_gemm_kernel_name(0, 4096, 4096, BF16, 0).decode() == "none"
