@@ -9,8 +9,11 @@
 //                 stream a 16- or 32-column strip of the weights (and the
 //                 rows of A) into LDS for one consumer wavefront that runs
 //                 the chains of all M rows;
-//   gemm16_ring   larger M, K a multiple of 64: LDS tiles fed through a ring
-//                 of stages by direct-to-LDS loads.
+//   gemm16_ring   M in the thousands (256-row tiles), K a multiple of 64:
+//                 LDS tiles fed through a ring of stages by direct-to-LDS loads;
+//   gemm16_pipe   M above the strip range up to the thousands: the same
+//                 loads with fragments read several steps ahead and one
+//                 barrier per stage.
 // Everything else (row-major (K, N) weights, other K, the split-K comparator)
 // runs the generic kernels of gemm.hip, which implement the same chain.
 #include <cstdio>
@@ -425,6 +428,158 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm16_ring(GemmParams p) {
     }
 }
 
+// ============================================================ pipelined ring kernel
+// BM x BN tile, WGM x WGN wavefronts, KS-wide k stages (K a multiple of KS),
+// NS LDS stages (at least 3).  Rows are KS * 2 bytes; chunk c of row r sits
+// at slot c ^ (r mod 16) for 256-byte rows and c ^ ((r / 2) mod 8) for
+// 128-byte rows (the 16 rows one ds_read_b128 pass serves hit distinct bank
+// groups).  Two things keep the MFMAs fed:
+//   * fragments are read DR chain steps ahead into a ring of DR + 1 register
+//     sets, so each step's LDS latency hides under the MFMAs of the steps
+//     before it;
+//   * a stage's buffer is refilled one stage late: the barrier taken DR steps
+//     before the end of stage t (once stage t + 1 has landed) hands the
+//     buffer of stage t - 1, which every wavefront has finished reading, to
+//     the loads of stage t + NS - 1.  No wavefront waits for its own LDS
+//     reads before a barrier, and one barrier per stage is the only
+//     synchronisation.
+// The chain itself (step order, k-slot mapping, instruction) is the one
+// described in gemm16.h.
+template <int KS> __device__ __forceinline__ int pipe_swz(int row) {
+    if constexpr (KS == 128) return row & 15;
+    else return (row >> 1) & 7;
+}
+
+template <int idt, int odt, int BM, int BN, int WGM, int WGN, int NS, int KS, int DR>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm16_pipe(GemmParams p) {
+    constexpr int NW = WGM * WGN;
+    constexpr int WM = BM / WGM, WN = BN / WGN;
+    constexpr int FM = WM / 16, FN = WN / 16;
+    constexpr int ROWB = 2 * KS, CPR = KS / 8, RPI = 64 / CPR;
+    constexpr int STAGE = (BM + BN) * ROWB;
+    constexpr int Q = (BM + BN) / RPI, QW = Q / NW;
+    constexpr int SPS = KS / 32;                     // chain steps per stage
+    constexpr int NSET = DR + 1;
+    constexpr int U = (NSET % SPS == 0) ? NSET : (SPS % NSET == 0 ? SPS : NSET * SPS);
+    static_assert(KS == 64 || KS == 128, "stage width");
+    static_assert(WM % 16 == 0 && WN % 16 == 0 && BM % 16 == 0, "wave tile");
+    static_assert(Q % NW == 0, "every wave issues the same number of loads per stage");
+    static_assert(NS >= 3 && QW * (NS - 2) <= 63, "vmcnt range");
+    static_assert(DR >= 1 && DR <= SPS, "read-ahead");
+    __shared__ __attribute__((aligned(1024))) char lds[NS * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WGN, wn = wave % WGN;
+    const int r16 = lane & 15, g = lane >> 4;
+
+    const int ntm = (p.M + BM - 1) / BM, ntn = (p.N + BN - 1) / BN;
+    int tm, tn;
+    tile_coords(blockIdx.x, ntm, ntn, 8, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int nstages = p.K / KS;
+    const int nsteps = nstages * SPS;
+
+    // load side: instruction q covers stage rows RPI q .. RPI q + RPI - 1; lane L row RPI q + L / CPR,
+    // slot L mod CPR, which receives chunk slot ^ swz(row)
+    const char *src[QW];
+#pragma unroll
+    for (int j = 0; j < QW; ++j) {
+        const int q = wave + NW * j;
+        const int rloc = q * RPI + lane / CPR;
+        const int c = (lane % CPR) ^ pipe_swz<KS>(rloc);
+        if (rloc < BM)
+            src[j] = static_cast<const char *>(p.A) + (int64_t)min(m0 + rloc, p.M - 1) * p.lda * 2 + c * 16;
+        else
+            src[j] = static_cast<const char *>(p.B) + (int64_t)min(n0 + rloc - BM, p.N - 1) * p.ldb * 2 + c * 16;
+    }
+    auto issue = [&](int stage) {
+        const int64_t koff = (int64_t)stage * ROWB;
+        char *buf = lds + (stage % NS) * STAGE;
+#pragma unroll
+        for (int j = 0; j < QW; ++j) {
+            const int q = wave + NW * j;
+            __builtin_amdgcn_global_load_lds(static_cast<const void *>(src[j] + koff), BI_LDS_PTR(buf + q * 1024), 16,
+                                             0, 0);
+        }
+    };
+    int aoff[FM], boff[FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) aoff[i] = (wm * WM + 16 * i + r16) * ROWB;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) boff[j] = (BM + wn * WN + 16 * j + r16) * ROWB;
+    const int swz = pipe_swz<KS>(r16);             // rows of a fragment start at multiples of 16
+    u32x4 fa[NSET][FM], fb[NSET][FN];
+    auto read_step = [&](int step, u32x4 (&a)[FM], u32x4 (&b)[FN]) {
+        const char *buf = lds + ((step / SPS) % NS) * STAGE;
+        const int c = 4 * (step % SPS) + g;
+        const int off = (c ^ swz) << 4;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) a[i] = *reinterpret_cast<const u32x4 *>(buf + aoff[i] + off);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) b[j] = *reinterpret_cast<const u32x4 *>(buf + boff[j] + off);
+    };
+    f32x4 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = zero4();
+
+    // prologue: stages 0 .. NS - 2 in flight, stage 0 landed everywhere, steps 0 .. DR - 1 read
+    const int pro = min(NS - 1, nstages);
+    for (int s = 0; s < pro; ++s) issue(s);
+    if (nstages > 0) {
+        if (pro == NS - 1) BI_WAIT_VMCNT(QW * (NS - 2));
+        else BI_WAIT_VMCNT(0);
+        __builtin_amdgcn_s_barrier();
+#pragma unroll
+        for (int d = 0; d < DR; ++d)
+            if (d < nsteps) read_step(d, fa[d], fb[d]);
+    }
+    // step s: read step s + DR (crossing into stage t + 1 first waits for it and refills the buffer of
+    // stage t - 1 with stage t + NS - 1), then run the MFMAs of step s
+    for (int s0 = 0; s0 < nsteps; s0 += U) {
+#pragma unroll
+        for (int d = 0; d < U; ++d) {
+            const int s = s0 + d;
+            if (s < nsteps) {
+                const int sr = s + DR;
+                if (sr < nsteps) {
+                    if ((d + DR) % SPS == 0) {
+                        const int tr = sr / SPS;           // the stage being entered (>= 1)
+                        if (tr + NS - 3 <= nstages - 1) BI_WAIT_VMCNT(QW * (NS - 3));
+                        else BI_WAIT_VMCNT(0);
+                        __builtin_amdgcn_s_barrier();
+                        if (tr + NS - 2 < nstages) issue(tr + NS - 2);
+                    }
+                    read_step(sr, fa[(d + DR) % NSET], fb[(d + DR) % NSET]);
+                }
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+                        acc[i][j] = Mfma<idt>::step(fa[d % NSET][i], fb[d % NSET][j], acc[i][j]);
+            }
+        }
+    }
+    if constexpr (BM * BN * Elem<odt>::bytes <= NS * STAGE) {
+        store_tile16<odt, BM, BN, WGM, WGN>(p, acc, m0, n0, lds);
+    } else {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int n = n0 + wn * WN + 16 * j + r16;
+                if (n >= p.N) continue;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int m = m0 + wm * WM + 16 * i + 4 * g + e;
+                    if (m < p.M) epilogue<odt>(p, m, n, acc[i][j][e]);
+                }
+            }
+    }
+}
+
 // ============================================================ plan + launch
 // Strip instantiations by M (fragments, A rows per stage, stages, loader
 // waves) and ring tiles, largest first.  The ring plan takes the largest tile
@@ -447,16 +602,31 @@ static bool use_strip(int M, int N, int K) {
     if (M <= 64) return !(wide_n(N) && K % 64 == 0);
     return false;
 }
-struct RingCfg { int bm, bn; };
-static const RingCfg kRing[] = {{256, 256}, {256, 128}, {128, 128}, {128, 64}, {64, 64}};
-constexpr long kRingMinTiles = 192;
+// Tiles for M above the strip range, largest first.  The plan takes the
+// largest tile that yields about one tile per CU (192 of 256), skipping tiles at
+// least twice as tall as M (their rows would be mostly clamped copies), else the
+// smallest one allowed.  The 256-row tiles run the two-stage ring; the others
+// the pipelined kernel, except that the 128x64 tile runs the ring when it spans
+// more than one row of tiles (measured faster there), and the 32x64 and 64x64
+// tiles, which use 128-k stages, fall back to the ring's 64x64 tile when K is
+// not a multiple of 128.
+enum TileKind { RING256x256, RING256x128, PIPE128x128, PIPE128x64, PIPE64x64, PIPE32x64, RING128x64, RING64x64 };
+struct TileCfg { int bm, bn; TileKind kind; };
+static const TileCfg kTiles[] = {{256, 256, RING256x256}, {256, 128, RING256x128}, {128, 128, PIPE128x128},
+                                 {128, 64, PIPE128x64},   {64, 64, PIPE64x64},     {32, 64, PIPE32x64}};
+constexpr long kMinTiles = 192;
 
-static RingCfg ring_cfg(int M, int N) {
-    for (const RingCfg &c : kRing) {
+static TileCfg tile_cfg(int M, int N, int K) {
+    TileCfg pick = kTiles[0];
+    for (const TileCfg &c : kTiles) {
+        if (c.bm >= 2 * M && c.bm > 32) continue;
+        pick = c;
         const long tiles = (long)((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
-        if (tiles >= kRingMinTiles) return c;
+        if (tiles >= kMinTiles) break;
     }
-    return RingCfg{64, 64};
+    if ((pick.kind == PIPE64x64 || pick.kind == PIPE32x64) && K % 128 != 0) pick = TileCfg{64, 64, RING64x64};
+    if (pick.kind == PIPE128x64 && M > 128) pick.kind = RING128x64;
+    return pick;
 }
 
 bool gemm16_applies(int M, int N, int K, bool b_kn, int splits) {
@@ -478,18 +648,34 @@ static hipError_t launch16_typed(const GemmParams &p, hipStream_t st) {
         else hipLaunchKernelGGL((gemm16_strip<idt, odt, 2, 4, 64, 3, 3>), grid, block, 0, st, p);
         return hipGetLastError();
     }
-    const RingCfg c = ring_cfg(p.M, p.N);
+    const TileCfg c = tile_cfg(p.M, p.N, p.K);
     const unsigned tiles = (unsigned)(((p.M + c.bm - 1) / c.bm) * ((p.N + c.bn - 1) / c.bn));
-    if (c.bm == 256 && c.bn == 256)
-        hipLaunchKernelGGL((gemm16_ring<idt, odt, 256, 256, 2, 4, 2>), dim3(tiles), dim3(512), 0, st, p);
-    else if (c.bm == 256)
-        hipLaunchKernelGGL((gemm16_ring<idt, odt, 256, 128, 4, 2, 3>), dim3(tiles), dim3(512), 0, st, p);
-    else if (c.bn == 128)
-        hipLaunchKernelGGL((gemm16_ring<idt, odt, 128, 128, 2, 2, 3>), dim3(tiles), dim3(256), 0, st, p);
-    else if (c.bm == 128)
-        hipLaunchKernelGGL((gemm16_ring<idt, odt, 128, 64, 2, 2, 4>), dim3(tiles), dim3(256), 0, st, p);
-    else
-        hipLaunchKernelGGL((gemm16_ring<idt, odt, 64, 64, 2, 2, 4>), dim3(tiles), dim3(256), 0, st, p);
+    switch (c.kind) {
+        case RING256x256:
+            hipLaunchKernelGGL((gemm16_ring<idt, odt, 256, 256, 2, 4, 2>), dim3(tiles), dim3(512), 0, st, p);
+            break;
+        case RING256x128:
+            hipLaunchKernelGGL((gemm16_ring<idt, odt, 256, 128, 4, 2, 3>), dim3(tiles), dim3(512), 0, st, p);
+            break;
+        case PIPE128x128:
+            hipLaunchKernelGGL((gemm16_pipe<idt, odt, 128, 128, 2, 4, 4, 64, 2>), dim3(tiles), dim3(512), 0, st, p);
+            break;
+        case PIPE128x64:
+            hipLaunchKernelGGL((gemm16_pipe<idt, odt, 128, 64, 4, 2, 6, 64, 2>), dim3(tiles), dim3(512), 0, st, p);
+            break;
+        case PIPE64x64:
+            hipLaunchKernelGGL((gemm16_pipe<idt, odt, 64, 64, 2, 4, 4, 128, 2>), dim3(tiles), dim3(512), 0, st, p);
+            break;
+        case PIPE32x64:
+            hipLaunchKernelGGL((gemm16_pipe<idt, odt, 32, 64, 2, 4, 5, 128, 2>), dim3(tiles), dim3(512), 0, st, p);
+            break;
+        case RING128x64:
+            hipLaunchKernelGGL((gemm16_ring<idt, odt, 128, 64, 2, 2, 4>), dim3(tiles), dim3(256), 0, st, p);
+            break;
+        case RING64x64:
+            hipLaunchKernelGGL((gemm16_ring<idt, odt, 64, 64, 2, 2, 4>), dim3(tiles), dim3(256), 0, st, p);
+            break;
+    }
     return hipGetLastError();
 }
 
@@ -508,8 +694,9 @@ const char *gemm16_kernel_name(int M, int N, int K) {
         snprintf(buf, sizeof buf, "gemm16_strip_nk/w%d_a%d", 16 * c.nb, c.ar);
     }
     else {
-        const RingCfg c = ring_cfg(M, N);
-        snprintf(buf, sizeof buf, "gemm16_ring_nk/%dx%d", c.bm, c.bn);
+        const TileCfg c = tile_cfg(M, N, K);
+        const bool ring = c.kind == RING256x256 || c.kind == RING256x128 || c.kind == RING128x64 || c.kind == RING64x64;
+        snprintf(buf, sizeof buf, "gemm16_%s_nk/%dx%d", ring ? "ring" : "pipe", c.bm, c.bn);
     }
     return buf;
 }

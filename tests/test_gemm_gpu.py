@@ -295,3 +295,30 @@ def test_large_m_rows_match_small_m_calls(N):
     rows = [0, 255, 256, 2049, 4095]
     ref = oracle.linear(x[rows].cpu(), w.cpu(), b.cpu())
     assert_close_to_oracle(full[rows].cpu(), ref, f"large M, N={N}")
+
+
+@pytest.mark.parametrize("K", [1024, 960])
+def test_every_tile_configuration_is_exact(K):
+    """Integer inputs through every large-M tile configuration (the two-stage ring tiles and the
+    pipelined tiles, with 128-k or 64-k stages), M and N ragged: sampled rows equal the oracle
+    rounded once, and every row equals the same row of the largest call."""
+    lib = bi._native.load()
+    Ns = (72, 1000, 4100, 14336)
+    Ms = (65, 100, 128, 129, 200, 256, 257, 300, 700, 1024, 2048)
+    x = ints((max(Ms), K), 61, torch.bfloat16)
+    w = ints((max(Ns), K), 62, torch.bfloat16)
+    b = ints((max(Ns),), 63, torch.bfloat16, -5, 5)
+    xg, wg, bg = x.to(DEV), w.to(DEV), b.to(DEV)
+    seen = set()
+    for n in Ns:
+        full = bi.bi_linear(xg, wg[:n], bg[:n])
+        rows = [0, 1, 63, 64, 127, 128, 255, 256, 1000, max(Ms) - 1]
+        ref = oracle.linear(x[rows], w[:n], b[:n])
+        assert_bits_equal(full[rows].cpu(), round_ref(ref, torch.bfloat16), f"N={n} sampled rows vs oracle")
+        for m in Ms:
+            seen.add(lib.bi_gemm_kernel_name(m, n, K, bi.BI_BF16, 0).decode())
+            assert_bits_equal(bi.bi_linear(xg[:m], wg[:n], bg[:n]), full[:m], f"K={K} N={n} M={m}")
+    expect = {"gemm16_ring_nk/256x256", "gemm16_ring_nk/256x128", "gemm16_pipe_nk/128x128",
+              "gemm16_pipe_nk/128x64", "gemm16_ring_nk/128x64"}
+    expect |= {"gemm16_pipe_nk/64x64", "gemm16_pipe_nk/32x64"} if K % 128 == 0 else {"gemm16_ring_nk/64x64"}
+    assert expect <= seen, (sorted(expect - seen), sorted(seen))
