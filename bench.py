@@ -52,7 +52,7 @@ TRAFFIC_MD = os.path.join(ROOT, "profiles", "bench_step_bf16_gemm_sweep_sdpa_swe
 CALIB_BYTES = 256 * 2 ** 20     # bytes read and bytes written by the calibration copy
 # sources whose text fixes each kernel family's memory traffic
 FAMILY_SOURCES = {
-    "gemm": ["device.h", "gemm.h", "gemm_common.h", "gemm16.h", "gemm16.hip", "gemm.hip", "api.hip"],
+    "gemm": ["device.h", "gemm.h", "gemm_common.h", "gemm16.h", "gemm16_store.h", "gemm16.hip", "gemm.hip", "api.hip"],
     "sdpa": ["device.h", "sdpa.h", "sdpa.hip", "api.hip"],
 }
 
@@ -329,7 +329,8 @@ def _time_graph(torch, fn, reps=20, iters=10):
     with torch.cuda.graph(g):
         for _ in range(reps):
             fn()
-    g.replay()
+    for _ in range(3):                        # warm-up replays: clocks settle before timing
+        g.replay()
     torch.cuda.synchronize()
     ts = []
     for _ in range(iters):

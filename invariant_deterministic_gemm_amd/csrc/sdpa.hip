@@ -66,6 +66,19 @@ __device__ __forceinline__ f32x4 attn_mfma_chunk(u32x4 a, u32x4 b, f32x4 c) {
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Work item of a one-dimensional grid of `ntile` query-row tiles times
+// `ngroup` (split, batch, KV head) groups.  Workgroups are dealt to the eight
+// XCDs in turn, so when the grid size is a multiple of 8 the ids are permuted
+// to give each XCD one contiguous run of groups: the tiles that read the same
+// K / V block then share one L2.  Picks work only, never arithmetic.
+__device__ __forceinline__ void attn_work(int ntile, int ngroup, int &tile, int &group) {
+    const int total = ntile * ngroup;
+    int L = blockIdx.x;
+    if ((total & 7) == 0) L = (L & 7) * (total >> 3) + (L >> 3);
+    tile = L % ntile;
+    group = L / ntile;
+}
+
 template <int dt, int D>
 __global__ __launch_bounds__(64) void sdpa_split(SdpaParams p) {
     using A = AttnShape<dt, D>;
@@ -75,11 +88,12 @@ __global__ __launch_bounds__(64) void sdpa_split(SdpaParams p) {
     const int lane = threadIdx.x;
     const int r16 = lane & 15;
     const int g = lane >> 4;
-    const int sp = blockIdx.x;
-    const int tile = blockIdx.y;
-    const int b = blockIdx.z / p.Hkv;
-    const int gk = blockIdx.z % p.Hkv;
     const int R = p.G * p.Lq;
+    int tile, grp;
+    attn_work((R + 15) / 16, p.nsplit * p.B * p.Hkv, tile, grp);
+    const int sp = grp % p.nsplit;
+    const int b = grp / p.nsplit / p.Hkv;
+    const int gk = grp / p.nsplit % p.Hkv;
 
     // the score row this lane carries (column r16 of S^T)
     const int rg = tile * 16 + r16;
@@ -493,17 +507,25 @@ __device__ __forceinline__ void split16_body(const SdpaParams &p, int sp, int ti
     l_out = l_run;
 }
 
-template <int dt>
-__global__ __launch_bounds__(64) void sdpa_split16(SdpaParams p) {
-    __shared__ __attribute__((aligned(1024))) char lds[2 * KV_BLOCK * 256];   // K block, then V block
-    const int lane = threadIdx.x;
+// W wavefronts per workgroup take W consecutive splits of one (batch, KV
+// head, row tile): neighbouring wavefronts stream neighbouring K / V ranges.
+// Each wavefront writes its own split's partial; the work split never changes
+// the arithmetic.
+template <int dt, int W>
+__global__ __launch_bounds__(64 * W) void sdpa_split16(SdpaParams p) {
+    __shared__ __attribute__((aligned(1024))) char lds[W * 2 * KV_BLOCK * 256];   // per wave: K block, V block
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r16 = lane & 15, g = lane >> 4;
-    const int sp = blockIdx.x, tile = blockIdx.y;
-    const int b = blockIdx.z / p.Hkv, gk = blockIdx.z % p.Hkv;
     const int R = p.G * p.Lq;
+    const int nsg = (p.nsplit + W - 1) / W;          // split groups per (batch, KV head)
+    int tile, grp;
+    attn_work((R + 15) / 16, nsg * p.B * p.Hkv, tile, grp);
+    const int sp = (grp % nsg) * W + wave;
+    const int b = grp / nsg / p.Hkv, gk = grp / nsg % p.Hkv;
+    if (sp >= p.nsplit) return;
     float m_run, l_run;
     f32x4 o[8];
-    split16_body<dt>(p, sp, tile, b, gk, lds, m_run, l_run, o);
+    split16_body<dt>(p, sp, tile, b, gk, lds + wave * 2 * KV_BLOCK * 256, m_run, l_run, o);
     const int rg = tile * 16 + r16;
     if (g == 0 && rg < R) {
         const int64_t rowid = ((int64_t)b * p.Hq + gk * p.G + rg % p.G) * p.Lq + rg / p.G;
@@ -538,9 +560,10 @@ __global__ __launch_bounds__(64 * FUSED_MAXW) void sdpa_fused16(SdpaParams p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nw = blockDim.x >> 6;                  // == nsplit
     const int r16 = lane & 15, g = lane >> 4;
-    const int tile = blockIdx.x;
-    const int b = blockIdx.y / p.Hkv, gk = blockIdx.y % p.Hkv;
     const int R = p.G * p.Lq;
+    int tile, grp;
+    attn_work((R + 15) / 16, p.B * p.Hkv, tile, grp);
+    const int b = grp / p.Hkv, gk = grp % p.Hkv;
     float m_run, l_run;
     f32x4 o[8];
     split16_body<dt>(p, wave, tile, b, gk, lds + wave * PER_WAVE, m_run, l_run, o);
@@ -590,11 +613,15 @@ __global__ __launch_bounds__(64 * FUSED_MAXW) void sdpa_fused16(SdpaParams p) {
 }
 
 // Fold the split partials of one query row left to right, normalise, round.
+// One thread per output column; the partials of CH splits are loaded together
+// (independent loads in flight at once), then folded one split at a time in
+// ascending order.
 template <int dt, int D>
-__global__ __launch_bounds__(64) void sdpa_combine(SdpaParams p) {
+__global__ __launch_bounds__(D) void sdpa_combine(SdpaParams p) {
     constexpr float NEG_INF = -__builtin_huge_valf();
-    constexpr int PER = D / 64;
+    constexpr int CH = 16;
     const int64_t rowid = blockIdx.x;
+    const int d = threadIdx.x;
     const int iq = (int)(rowid % p.Lq);
     const int h = (int)((rowid / p.Lq) % p.Hq);
     const int b = (int)(rowid / ((int64_t)p.Lq * p.Hq));
@@ -602,37 +629,39 @@ __global__ __launch_bounds__(64) void sdpa_combine(SdpaParams p) {
     const float *po = p.ws_o + rowid * p.nsplit * D;
 
     bool have = false;
-    float m = 0.0f, l = 0.0f;
-    float o[PER];
+    float m = 0.0f, l = 0.0f, o = 0.0f;
+    for (int s0 = 0; s0 < p.nsplit; s0 += CH) {
+        float ms[CH], ls[CH], os[CH];
 #pragma unroll
-    for (int j = 0; j < PER; ++j) o[j] = 0.0f;
-    for (int sp = 0; sp < p.nsplit; ++sp) {
-        const float ms = ml[2 * sp], ls = ml[2 * sp + 1];
-        if (ms == NEG_INF) continue;              // split saw no key of this row
-        if (!have) {
-            m = ms;
-            l = ls;
-#pragma unroll
-            for (int j = 0; j < PER; ++j) o[j] = po[sp * D + threadIdx.x + 64 * j];
-            have = true;
-            continue;
+        for (int u = 0; u < CH; ++u) {
+            const int sp = min(s0 + u, p.nsplit - 1);
+            ms[u] = ml[2 * sp];
+            ls[u] = ml[2 * sp + 1];
+            os[u] = po[sp * D + d];
         }
-        const float m2 = fmaxf(m, ms);
-        const float a = exp2_hw(m - m2);
-        const float bs = exp2_hw(ms - m2);
-        l = __builtin_fmaf(l, a, ls * bs);
 #pragma unroll
-        for (int j = 0; j < PER; ++j) o[j] = __builtin_fmaf(o[j], a, po[sp * D + threadIdx.x + 64 * j] * bs);
-        m = m2;
+        for (int u = 0; u < CH; ++u) {
+            if (s0 + u >= p.nsplit || ms[u] == NEG_INF) continue;   // past the end / split saw no key of this row
+            if (!have) {
+                m = ms[u];
+                l = ls[u];
+                o = os[u];
+                have = true;
+                continue;
+            }
+            const float m2 = fmaxf(m, ms[u]);
+            const float a = exp2_hw(m - m2);
+            const float bs = exp2_hw(ms[u] - m2);
+            l = __builtin_fmaf(l, a, ls[u] * bs);
+            o = __builtin_fmaf(o, a, os[u] * bs);
+            m = m2;
+        }
     }
     char *orow = static_cast<char *>(p.o) +
                  ((int64_t)b * p.os[0] + (int64_t)h * p.os[1] + (int64_t)iq * p.os[2]) * Elem<dt>::bytes;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-        float r = have ? o[j] / l : 0.0f;
-        r = r + 0.0f;                              // -0 -> +0
-        store_from_f32<dt>(orow, threadIdx.x + 64 * j, r);
-    }
+    float r = have ? o / l : 0.0f;
+    r = r + 0.0f;                                  // -0 -> +0
+    store_from_f32<dt>(orow, d, r);
 }
 
 size_t sdpa_workspace_bytes(int64_t B, int64_t Hq, int64_t Lq, int64_t S, int64_t D) {
@@ -657,20 +686,28 @@ static hipError_t launch_typed(const SdpaParams &p, hipStream_t st) {
     const int R = p.G * p.Lq;
     if constexpr (dt != DT_F32 && D == 128) {
         if (p.nsplit >= 1 && p.nsplit <= FUSED_MAXW) {
-            const dim3 gf((unsigned)((R + 15) / 16), (unsigned)(p.B * p.Hkv));
-            hipLaunchKernelGGL((sdpa_fused16<dt>), gf, dim3(64 * p.nsplit), 0, st, p);
+            const int64_t nwg = (int64_t)((R + 15) / 16) * p.B * p.Hkv;
+            if (nwg > INT32_MAX) return hipErrorInvalidConfiguration;
+            hipLaunchKernelGGL((sdpa_fused16<dt>), dim3((unsigned)nwg), dim3(64 * p.nsplit), 0, st, p);
             return hipGetLastError();
         }
     }
     if (p.nsplit > 0) {
-        const dim3 g1((unsigned)p.nsplit, (unsigned)((R + 15) / 16), (unsigned)(p.B * p.Hkv));
-        if constexpr (dt != DT_F32 && D == 128) hipLaunchKernelGGL((sdpa_split16<dt>), g1, dim3(64), 0, st, p);
-        else hipLaunchKernelGGL((sdpa_split<dt, D>), g1, dim3(64), 0, st, p);
+        if constexpr (dt != DT_F32 && D == 128) {
+            constexpr int W = 2;                         // splits per workgroup (measured best for long caches)
+            const int64_t nwg = (int64_t)((p.nsplit + W - 1) / W) * ((R + 15) / 16) * p.B * p.Hkv;
+            if (nwg > INT32_MAX) return hipErrorInvalidConfiguration;
+            hipLaunchKernelGGL((sdpa_split16<dt, W>), dim3((unsigned)nwg), dim3(64 * W), 0, st, p);
+        } else {
+            const int64_t nwg = (int64_t)p.nsplit * ((R + 15) / 16) * p.B * p.Hkv;
+            if (nwg > INT32_MAX) return hipErrorInvalidConfiguration;
+            hipLaunchKernelGGL((sdpa_split<dt, D>), dim3((unsigned)nwg), dim3(64), 0, st, p);
+        }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     const dim3 g2((unsigned)((int64_t)p.B * p.Hq * p.Lq));
-    hipLaunchKernelGGL((sdpa_combine<dt, D>), g2, dim3(64), 0, st, p);
+    hipLaunchKernelGGL((sdpa_combine<dt, D>), g2, dim3(D), 0, st, p);
     return hipGetLastError();
 }
 
