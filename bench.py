@@ -329,7 +329,12 @@ def _time_graph(torch, fn, reps=20, iters=10):
     with torch.cuda.graph(g):
         for _ in range(reps):
             fn()
-    for _ in range(3):                        # warm-up replays: clocks settle before timing
+    # warm-up replays for about 30 ms, so clocks have settled before timing
+    t0 = time.perf_counter()
+    g.replay()
+    torch.cuda.synchronize()
+    once = time.perf_counter() - t0
+    for _ in range(min(200, int(0.03 / max(once, 1e-6)) + 1)):
         g.replay()
     torch.cuda.synchronize()
     ts = []
