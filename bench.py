@@ -350,7 +350,8 @@ def _time_graph(torch, fn, reps=20, iters=10):
 
 
 def measure_cells(bi, lib, torch, dev, synthetic, data, launches, groups, names, group_ms):
-    cells = {"decode_gemm": [], "large_m_gemm": [], "decode_attention": [], "comparator": {}}
+    cells = {"decode_gemm": [], "large_m_gemm": [], "decode_attention": [], "prefill_attention": [],
+             "comparator": {}}
     K = 4096
     # decode GEMM: weights rotate through copies inside one graph, so reads are cold
     logits = synthetic.cfg5_inputs(torch.bfloat16, M_max=8)
@@ -390,13 +391,27 @@ def measure_cells(bi, lib, torch, dev, synthetic, data, launches, groups, names,
         q = torch.randn((B, 32, 1, 128), generator=gen, device=dev).to(torch.bfloat16)
         k = torch.randn((B, 8, S, 128), generator=gen, device=dev).to(torch.bfloat16)
         v = torch.randn((B, 8, S, 128), generator=gen, device=dev).to(torch.bfloat16)
-        ws = torch.empty(bi.sdpa_workspace_bytes(B, 32, 1, S, 128), dtype=torch.uint8, device=dev)
+        ws = torch.empty(bi.sdpa_workspace_bytes(B, 32, 1, S, 128, torch.bfloat16), dtype=torch.uint8, device=dev)
         ms = _time_graph(torch, lambda: bi.bi_sdpa(q, k, v, causal=True, workspace=ws), reps=4, iters=6)
         nbytes = 2.0 * (B * 8 * S * 128 * 2 + 2 * B * 32 * 128)
         gbps = nbytes / (ms * 1e-3) / 1e9
         cells["decode_attention"].append({"B": B, "S": S, "us": round(ms * 1e3, 1), "GBps": round(gbps, 1),
                                           "frac_hbm": round(gbps / HBM_PEAK_GBPS, 4)})
         del q, k, v, ws
+    # long causal prefill (query chunk = whole cache): workspace-free kernel, flops of visible pairs
+    for S in (4096, 8192):
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(0x5EED95 + S)
+        q = torch.randn((1, 32, S, 128), generator=gen, device=dev).to(torch.bfloat16)
+        k = torch.randn((1, 8, S, 128), generator=gen, device=dev).to(torch.bfloat16)
+        v = torch.randn((1, 8, S, 128), generator=gen, device=dev).to(torch.bfloat16)
+        ms = _time_graph(torch, lambda: bi.bi_sdpa(q, k, v, causal=True), reps=2, iters=5)
+        flops = 4.0 * 32 * 128 * (S * (S + 1) / 2)
+        tf = flops / (ms * 1e-3) / 1e12
+        cells["prefill_attention"].append({"B": 1, "Lq": S, "S": S, "us": round(ms * 1e3, 1), "TFLOPs": round(tf, 1),
+                                           "frac_mfma": round(tf / BF16_PEAK_TFLOPS, 4),
+                                           "kernel": lib.bi_sdpa_kernel_name(1, 32, S, S, 128, bi.BI_BF16).decode()})
+        del q, k, v
     # batch-variant comparator on the linear half of the step: cost ratio and negative control
     inv_ms = var_ms = 0.0
     diff = 0

@@ -155,10 +155,13 @@ bi_status bi_addmm(const void *cin, int64_t ldcin,
  * Supported: D in {64, 128}; Hq % Hkv == 0; Lq <= S when causal; every
  * base pointer 16-byte aligned and every stride except the last a multiple
  * of 8 (16-bit) or 4 (fp32) elements.
- * Workspace: ws must hold bi_sdpa_workspace_bytes(B, Hq, Lq, S, D) bytes,
+ * Workspace: ws must hold bi_sdpa_workspace_bytes(B, Hq, Lq, S, D, dt) bytes,
  * 256-byte aligned, device memory owned by the caller; its contents on entry
  * do not matter and on return are unspecified.  Two calls that run at the
- * same time must not share a workspace.
+ * same time must not share a workspace.  The query returns 0 (ws may then be
+ * NULL) for the shapes served without a workspace: 16-bit dt with D = 128
+ * and either S <= 1024 (one launch, splits folded in LDS) or Lq >= 384
+ * (prefill: splits folded in registers).  Every path computes the same bits.
  */
 bi_status bi_sdpa(const void *q, const int64_t q_str[4],
                   const void *k, const int64_t k_str[4],
@@ -171,8 +174,9 @@ bi_status bi_sdpa(const void *q, const int64_t q_str[4],
                   void *ws, size_t ws_bytes,
                   void *stream);
 
-/* Bytes of workspace bi_sdpa needs for these sizes (0 when there is nothing to do). */
-size_t bi_sdpa_workspace_bytes(int64_t B, int64_t Hq, int64_t Lq, int64_t S, int64_t D);
+/* Bytes of workspace bi_sdpa needs for these sizes and dtype (0 when there is
+ * nothing to do, when the path taken needs none, or for an unknown dtype). */
+size_t bi_sdpa_workspace_bytes(int64_t B, int64_t Hq, int64_t Lq, int64_t S, int64_t D, bi_dtype dt);
 
 /*
  * Batch-VARIANT comparator, for measurement only.  It runs the same
@@ -205,11 +209,12 @@ int bi_variant_splits(int64_t M);
  * Returns "none" for empty or oversized shapes. */
 const char *bi_gemm_kernel_name(int64_t M, int64_t N, int64_t K, bi_dtype in_dt, int b_kn);
 
-/* Which attention kernels a bi_sdpa call of these sizes runs ("sdpa_fused16" for
- * 16-bit D = 128 with S <= 1024, "sdpa_split16+combine" above, "sdpa_split+combine"
- * for fp32 and D = 64).  Informational: the split / block structure, and with it
- * every output bit, is the same whichever runs.  Returns "none" for empty,
- * oversized or unsupported sizes. */
+/* Which attention kernels a bi_sdpa call of these sizes runs: "sdpa_fused16"
+ * (16-bit, D = 128, S <= 1024), "sdpa_prefill16" (16-bit, D = 128, S > 1024,
+ * Lq >= 384), "sdpa_split16+combine" (other 16-bit D = 128 calls) or
+ * "sdpa_split+combine" (fp32, D = 64).  Informational: the split / block
+ * structure, and with it every output bit, is the same whichever runs.
+ * Returns "none" for empty, oversized or unsupported sizes. */
 const char *bi_sdpa_kernel_name(int64_t B, int64_t Hq, int64_t Lq, int64_t S, int64_t D, bi_dtype dt);
 
 /* Name of a status code ("BI_OK", ...); never NULL. */

@@ -201,8 +201,9 @@ bi_status bi_addmm(const void *cin, int64_t ldcin, const void *a, int64_t lda, c
     return device_status(bi::launch_gemm(p, in_dt, out_dt, b_kn, (hipStream_t)stream), "bi_addmm");
 }
 
-size_t bi_sdpa_workspace_bytes(int64_t B, int64_t Hq, int64_t Lq, int64_t S, int64_t D) {
-    return bi::sdpa_workspace_bytes(B, Hq, Lq, S, D);
+size_t bi_sdpa_workspace_bytes(int64_t B, int64_t Hq, int64_t Lq, int64_t S, int64_t D, bi_dtype dt) {
+    if (!dtype_known(dt)) return 0;
+    return bi::sdpa_workspace_bytes(B, Hq, Lq, S, D, (int)dt);
 }
 
 bi_status bi_sdpa(const void *q, const int64_t q_str[4], const void *k, const int64_t k_str[4], const void *v,
@@ -248,7 +249,7 @@ bi_status bi_sdpa(const void *q, const int64_t q_str[4], const void *k, const in
         for (int d = 0; d < 4; ++d)
             if (mask_str[d] < 0) return fail(BI_ERR_INVALID, "%s: negative mask stride", fn);
     }
-    const size_t need = bi::sdpa_workspace_bytes(B, Hq, Lq, S, D);
+    const size_t need = bi::sdpa_workspace_bytes(B, Hq, Lq, S, D, (int)dt);
     if (need > 0 && (ws == nullptr || ws_bytes < need))
         return fail(BI_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
                     ws == nullptr ? (size_t)0 : ws_bytes);
@@ -275,11 +276,8 @@ bi_status bi_sdpa(const void *q, const int64_t q_str[4], const void *k, const in
     p.G = (int)G;
     p.causal = causal ? 1 : 0;
     p.c = (float)((double)scale * 1.4426950408889634);   // log2(e), rounded once to fp32
-    if (need > 0) {
-        bi::sdpa_bind_workspace(p, ws, (int)D);
-    } else {
-        p.nsplit = 0;
-    }
+    p.nsplit = (int)((S + bi::KV_SPLIT - 1) / bi::KV_SPLIT);
+    if (need > 0) bi::sdpa_bind_workspace(p, ws);
     return device_status(bi::launch_sdpa(p, dt, (int)D, (hipStream_t)stream), fn);
 }
 
@@ -320,7 +318,7 @@ const char *bi_sdpa_kernel_name(int64_t B, int64_t Hq, int64_t Lq, int64_t S, in
     if (B <= 0 || Hq <= 0 || Lq <= 0 || S <= 0 || B > kMaxDim || Hq > kMaxDim || Lq > kMaxDim || S > kMaxDim ||
         (D != 64 && D != 128) || !dtype_known(dt))
         return "none";
-    return bi::sdpa_kernel_name((int)S, (int)D, (int)dt);
+    return bi::sdpa_kernel_name(Lq, S, D, (int)dt);
 }
 
 const char *bi_status_name(bi_status s) {

@@ -300,6 +300,139 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const char *lds_addr) {
     return __builtin_bit_cast(u32x2, v);
 }
 
+// The 16 query rows of one row tile as one wavefront sees them: lane r16
+// carries score row r16 (column r16 of S^T); lanes hold O rows 4 g + i.
+struct Rows16 {
+    bool row_ok;            // score row r16 is a real row (rows past R are computed and never stored)
+    int pos;                // its key position (bottom-right alignment)
+    int pos_first;          // key position of the tile's first row, the smallest in the tile
+    const uint8_t *mrow;    // its mask row, or null
+    u32x4 qf[4];            // its q fragments (d chunks 32 c + 8 g .. + 7)
+};
+
+template <int dt>
+__device__ __forceinline__ void rows16_load(const SdpaParams &p, int tile, int b, int gk, Rows16 &r) {
+    const int lane = threadIdx.x & 63;
+    const int r16 = lane & 15, g = lane >> 4;
+    const int R = p.G * p.Lq;
+    const int rg = tile * 16 + r16;
+    r.row_ok = rg < R;
+    const int rgc = min(rg, R - 1);
+    const int iq = rgc / p.G;
+    const int h = gk * p.G + rgc % p.G;
+    r.pos = p.S - p.Lq + iq;
+    r.pos_first = p.S - p.Lq + (tile * 16) / p.G;
+    r.mrow = p.mask ? p.mask + (int64_t)b * p.ms[0] + (int64_t)h * p.ms[1] + (int64_t)iq * p.ms[2] : nullptr;
+    const char *qrow = static_cast<const char *>(p.q) +
+                       ((int64_t)b * p.qs[0] + (int64_t)h * p.qs[1] + (int64_t)iq * p.qs[2]) * 2;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) r.qf[c] = ldg16(qrow + (32 * c + 8 * g) * 2);
+}
+
+// One 64-key block [kb, kb + 64) of the online softmax for a wavefront's 16
+// rows; K and V blocks in LDS (256-byte key rows, K chunk c at slot
+// c ^ (r mod 16), V chunk c at slot c ^ 2 (r mod 8); V rows of keys past S
+// must read as zero by the time v_ready() returns).  k_done() runs once every
+// K read of the block is complete, v_ready() before the first V read.
+template <int dt, class KDone, class VReady>
+__device__ __forceinline__ void attn_block16(const SdpaParams &p, const Rows16 &r, const char *Ks, const char *Vs,
+                                             int kb, float &m_run, float &l_run, f32x4 (&o)[8], KDone k_done,
+                                             VReady v_ready) {
+    constexpr int ROWB = 256;
+    constexpr float NEG_INF = -__builtin_huge_valf();
+    const int lane = threadIdx.x & 63;
+    const int r16 = lane & 15, g = lane >> 4;
+    // ---- scores: lane holds S^T[key 16 kt + 4 g + i][row r16].  All K fragments are read first; the four
+    // chains (one per kt) each accumulate d chunks c = 0 .. 3 in order.
+    u32x4 kf[4][4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            kf[kt][c] = *reinterpret_cast<const u32x4 *>(Ks + (16 * kt + r16) * ROWB + (((4 * c + g) ^ r16) << 4));
+    f32x4 st[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) st[kt] = zero4();
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) st[kt] = Mfma<dt>::step(kf[kt][c], r.qf[c], st[kt]);
+    __builtin_amdgcn_s_waitcnt(0xc07f);               // every K read of this block done
+    k_done();
+    float s[4][4];
+    const bool visible = p.mask == nullptr && kb + KV_BLOCK <= p.S && (!p.causal || kb + KV_BLOCK - 1 <= r.pos_first);
+    if (visible) {
+        // rows past R get real scores too: they are per-row, never stored, and touch no other row
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s[kt][i] = st[kt][i] * p.c;
+    } else {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int key = kb + 16 * kt + 4 * g + i;
+                bool ok = r.row_ok && key < p.S;
+                if (p.causal) ok = ok && key <= r.pos;
+                if (r.mrow) ok = ok && r.mrow[(int64_t)key * p.ms[3]] != 0;
+                const float sv = st[kt][i] * p.c;
+                s[kt][i] = ok ? sv : NEG_INF;
+            }
+    }
+    // block maximum of the row (exact in any order): a tree over the lane's 16 scores, then the lane groups
+    float mk[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) mk[kt] = fmaxf(fmaxf(s[kt][0], s[kt][1]), fmaxf(s[kt][2], s[kt][3]));
+    float mb = fmaxf(NEG_INF, fmaxf(fmaxf(mk[0], mk[1]), fmaxf(mk[2], mk[3])));   // all-NaN -> -inf, as a scan from -inf
+    mb = fmaxf(mb, __shfl_xor(mb, 16));
+    mb = fmaxf(mb, __shfl_xor(mb, 32));
+    const bool empty = mb == NEG_INF;
+    const float m_new = empty ? m_run : fmaxf(m_run, mb);
+    const float alpha = empty ? 1.0f : exp2_hw(m_run - m_new);
+    float pr[4][4];
+    float rs = 0.0f;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            pr[kt][i] = s[kt][i] == NEG_INF ? 0.0f : exp2_hw(s[kt][i] - m_new);
+            rs = rs + pr[kt][i];
+        }
+    rs = rs + __shfl_xor(rs, 16);
+    rs = rs + __shfl_xor(rs, 32);
+    l_run = __builtin_fmaf(l_run, alpha, rs);
+    m_run = m_new;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float ai = __shfl(alpha, 4 * g + i);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) o[t][i] = o[t][i] * ai;
+    }
+    v_ready();
+    // ---- O += P . V: k slot 8 g + j <-> key 32 c + 4 g + j (j < 4), 32 c + 16 + 4 g + (j - 4) (j >= 4).
+    // The V fragments of a half (c) are read before its eight MFMAs; o[t] takes c = 0 then c = 1.
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const u32x4 pf = u32x4{pack_p<dt>(pr[2 * c][0], pr[2 * c][1]), pack_p<dt>(pr[2 * c][2], pr[2 * c][3]),
+                               pack_p<dt>(pr[2 * c + 1][0], pr[2 * c + 1][1]),
+                               pack_p<dt>(pr[2 * c + 1][2], pr[2 * c + 1][3])};
+        const int row0 = 32 * c + 4 * g + (r16 >> 2);
+        const int row1 = row0 + 16;
+        u32x4 vf[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int ch = 2 * t + ((r16 & 3) >> 1);
+            const int off = 8 * (r16 & 1);
+            const u32x2 lo = lds_read_tr16(Vs + row0 * ROWB + ((ch ^ ((row0 & 7) << 1)) << 4) + off);
+            const u32x2 hi = lds_read_tr16(Vs + row1 * ROWB + ((ch ^ ((row1 & 7) << 1)) << 4) + off);
+            vf[t] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) o[t] = Mfma<dt>::step(pf, vf[t], o[t]);
+    }
+}
+
 // One wavefront's share: split `sp` of row tile `tile` of (b, gk), its K / V
 // blocks staged in `lds` (2 * KV_BLOCK * 256 bytes); leaves the split's
 // (m, l) of row r16 and its O fragment (rows 4 g + i, columns 16 t + r16).
@@ -313,32 +446,20 @@ __device__ __forceinline__ void split16_body(const SdpaParams &p, int sp, int ti
     static_assert(QB == 16, "four key rows per load instruction");
     constexpr float NEG_INF = -__builtin_huge_valf();
     const int lane = threadIdx.x & 63;
-    const int r16 = lane & 15;
-    const int g = lane >> 4;
     const int R = p.G * p.Lq;
-
-    const int rg = tile * 16 + r16;
-    const bool row_ok = rg < R;
-    const int rgc = min(rg, R - 1);
-    const int iq = rgc / p.G;
-    const int h = gk * p.G + rgc % p.G;
-    const int pos = p.S - p.Lq + iq;
 
     const int kbeg = sp * KV_SPLIT;
     const int kend = min(kbeg + KV_SPLIT, p.S);
     int nblk = (kend - kbeg + KV_BLOCK - 1) / KV_BLOCK;
     if (p.causal) {
+        // rows are ordered by query index, so the tile's last row sees the most keys
         const int rlast = min(tile * 16 + 15, R - 1);
         const int pos_last = p.S - p.Lq + rlast / p.G;
         nblk = pos_last < kbeg ? 0 : min(nblk, (pos_last - kbeg) / KV_BLOCK + 1);
     }
 
-    const char *qrow = static_cast<const char *>(p.q) +
-                       ((int64_t)b * p.qs[0] + (int64_t)h * p.qs[1] + (int64_t)iq * p.qs[2]) * 2;
     const char *kbase = static_cast<const char *>(p.k) + ((int64_t)b * p.ks[0] + (int64_t)gk * p.ks[1]) * 2;
     const char *vbase = static_cast<const char *>(p.v) + ((int64_t)b * p.vs[0] + (int64_t)gk * p.vs[1]) * 2;
-    const uint8_t *mrow = p.mask ? p.mask + (int64_t)b * p.ms[0] + (int64_t)h * p.ms[1] + (int64_t)iq * p.ms[2]
-                                 : nullptr;
 
     // load side: instruction q covers key rows 4 q .. 4 q + 3 of the block; lane L row 4 q + L / 16,
     // slot L mod 16.  The swizzled chunk depends on q only through q mod 4 (K) and q mod 2 (V), so the
@@ -390,14 +511,9 @@ __device__ __forceinline__ void split16_body(const SdpaParams &p, int sp, int ti
             }
         }
     };
-    // the tile's first row has the smallest query position: a block wholly at or before it, inside S
-    // and without a mask, is visible to every row and needs no per-key test
-    const int pos_first = p.S - p.Lq + (tile * 16) / p.G;
 
-    u32x4 qf[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) qf[c] = ldg16(qrow + (32 * c + 8 * g) * 2);
-
+    Rows16 r;
+    rows16_load<dt>(p, tile, b, gk, r);
     float m_run = NEG_INF, l_run = 0.0f;
 #pragma unroll
     for (int t = 0; t < 8; ++t) o[t] = zero4();
@@ -408,97 +524,22 @@ __device__ __forceinline__ void split16_body(const SdpaParams &p, int sp, int ti
     }
     for (int blk = 0; blk < nblk; ++blk) {
         const int kb = kbeg + blk * KV_BLOCK;
-        const char *Ks = lds;
-        const char *Vs = lds + KBYTES;
+        char *Vs = lds + KBYTES;
         BI_WAIT_VMCNT(QB);                            // K of this block landed (its V may be in flight)
-        // ---- scores: lane holds S^T[key 16 kt + 4 g + i][row r16]
-        f32x4 st[4];
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-            st[kt] = zero4();
-            const int row = 16 * kt + r16;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const u32x4 kf = *reinterpret_cast<const u32x4 *>(Ks + row * ROWB + (((4 * c + g) ^ (row & 15)) << 4));
-                st[kt] = Mfma<dt>::step(kf, qf[c], st[kt]);
-            }
-        }
-        __builtin_amdgcn_s_waitcnt(0xc07f);           // every K read of this block done
-        if (blk + 1 < nblk) issueK(blk + 1);
-        float s[4][4];
-        float mb = NEG_INF;
-        const bool visible = p.mask == nullptr && kb + KV_BLOCK <= p.S && (!p.causal || kb + KV_BLOCK - 1 <= pos_first);
-        if (visible) {
-            // rows past R get real scores too: they are per-row, never stored, and touch no other row
-#pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    s[kt][i] = st[kt][i] * p.c;
-                    mb = fmaxf(mb, s[kt][i]);
+        attn_block16<dt>(
+            p, r, lds, Vs, kb, m_run, l_run, o,
+            [&]() {
+                if (blk + 1 < nblk) issueK(blk + 1);
+            },
+            [&]() {
+                if (blk + 1 < nblk) BI_WAIT_VMCNT(QB);     // V of this block landed (next K may be in flight)
+                else BI_WAIT_VMCNT(0);
+                if (kb + KV_BLOCK > p.S) {
+                    for (int row = max(p.S - kb, 0) + lrow; row < KV_BLOCK; row += 4)
+                        *reinterpret_cast<u32x4 *>(Vs + row * ROWB + lslot * 16) = zero_u4();
+                    __builtin_amdgcn_s_waitcnt(0xc07f);
                 }
-        } else {
-#pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int key = kb + 16 * kt + 4 * g + i;
-                    bool ok = row_ok && key < p.S;
-                    if (p.causal) ok = ok && key <= pos;
-                    if (mrow) ok = ok && mrow[(int64_t)key * p.ms[3]] != 0;
-                    const float sv = st[kt][i] * p.c;
-                    s[kt][i] = ok ? sv : NEG_INF;
-                    mb = fmaxf(mb, s[kt][i]);
-                }
-        }
-        mb = fmaxf(mb, __shfl_xor(mb, 16));
-        mb = fmaxf(mb, __shfl_xor(mb, 32));
-        const bool empty = mb == NEG_INF;
-        const float m_new = empty ? m_run : fmaxf(m_run, mb);
-        const float alpha = empty ? 1.0f : exp2_hw(m_run - m_new);
-        float pr[4][4];
-        float rs = 0.0f;
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                pr[kt][i] = s[kt][i] == NEG_INF ? 0.0f : exp2_hw(s[kt][i] - m_new);
-                rs = rs + pr[kt][i];
-            }
-        rs = rs + __shfl_xor(rs, 16);
-        rs = rs + __shfl_xor(rs, 32);
-        l_run = __builtin_fmaf(l_run, alpha, rs);
-        m_run = m_new;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float ai = __shfl(alpha, 4 * g + i);
-#pragma unroll
-            for (int t = 0; t < 8; ++t) o[t][i] = o[t][i] * ai;
-        }
-        if (blk + 1 < nblk) BI_WAIT_VMCNT(QB);         // V of this block landed (next K may be in flight)
-        else BI_WAIT_VMCNT(0);
-        if (kb + KV_BLOCK > p.S) {
-            for (int row = max(p.S - kb, 0) + lrow; row < KV_BLOCK; row += 4)
-                *reinterpret_cast<u32x4 *>(const_cast<char *>(Vs) + row * ROWB + lslot * 16) = zero_u4();
-            __builtin_amdgcn_s_waitcnt(0xc07f);
-        }
-        // ---- O += P . V: k slot 8 g + j <-> key 32 c + 4 g + j (j < 4), 32 c + 16 + 4 g + (j - 4) (j >= 4)
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const u32x4 pf = u32x4{pack_p<dt>(pr[2 * c][0], pr[2 * c][1]), pack_p<dt>(pr[2 * c][2], pr[2 * c][3]),
-                                   pack_p<dt>(pr[2 * c + 1][0], pr[2 * c + 1][1]),
-                                   pack_p<dt>(pr[2 * c + 1][2], pr[2 * c + 1][3])};
-            const int row0 = 32 * c + 4 * g + (r16 >> 2);
-            const int row1 = row0 + 16;
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const int ch = 2 * t + ((r16 & 3) >> 1);
-                const int off = 8 * (r16 & 1);
-                const u32x2 lo = lds_read_tr16(Vs + row0 * ROWB + ((ch ^ ((row0 & 7) << 1)) << 4) + off);
-                const u32x2 hi = lds_read_tr16(Vs + row1 * ROWB + ((ch ^ ((row1 & 7) << 1)) << 4) + off);
-                o[t] = Mfma<dt>::step(pf, u32x4{lo[0], lo[1], hi[0], hi[1]}, o[t]);
-            }
-        }
+            });
         __builtin_amdgcn_s_waitcnt(0xc07f);           // every V read of this block done
         if (blk + 1 < nblk) issueV(blk + 1);
     }
@@ -612,6 +653,163 @@ __global__ __launch_bounds__(64 * FUSED_MAXW) void sdpa_fused16(SdpaParams p) {
     }
 }
 
+// Long prefill without a workspace: a workgroup of W wavefronts takes W
+// consecutive row tiles of one (batch, KV head) and walks all key blocks in
+// ascending order, each block loaded once into LDS for all W tiles (NB
+// buffers: blocks j + 1 .. j + NB - 1 load while block j is computed).  Every wavefront
+// runs exactly split16_body's per-block arithmetic on its tile, starting a
+// fresh (m, l, O) at each 256-key split boundary, and folds each split's
+// partial into a running state in registers with sdpa_combine's exact
+// operations in ascending split order, so every row gets the bits of the
+// split + combine path.  Blocks past the workgroup's last causal position are
+// not visited; for the tiles that stop earlier they are empty blocks, whose
+// split partials the fold skips, as it does for splits the split path never
+// launches.
+template <int dt, int W, int NB>
+__global__ __launch_bounds__(64 * W) void sdpa_prefill16(SdpaParams p) {
+    constexpr int ROWB = 256;
+    constexpr int KBYTES = KV_BLOCK * ROWB;            // one K (or V) block
+    constexpr int QBLK = 2 * KBYTES / 1024;            // 1 KiB loads per block (K then V)
+    constexpr int QW = QBLK / W;                       // loads per wavefront per block
+    constexpr int BPS = KV_SPLIT / KV_BLOCK;           // blocks per split
+    constexpr float NEG_INF = -__builtin_huge_valf();
+    static_assert(QBLK % W == 0, "every wavefront issues the same number of loads");
+    static_assert(NB >= 2 && QW * (NB - 2) <= 63, "vmcnt range");
+    __shared__ __attribute__((aligned(1024))) char lds[NB * 2 * KBYTES];  // [buffer][K block | V block]
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r16 = lane & 15, g = lane >> 4;
+    const int R = p.G * p.Lq;
+    const int ntile = (R + 15) / 16;
+    int wt, grp;
+    attn_work((ntile + W - 1) / W, p.B * p.Hkv, wt, grp);
+    const int b = grp / p.Hkv, gk = grp % p.Hkv;
+    const int tile = wt * W + wave;                    // tiles past the last compute clamped rows, store nothing
+
+    // keys the workgroup needs: up to its last row's causal position
+    const int rlast = min(wt * W * 16 + W * 16 - 1, R - 1);
+    const int nkeys = p.causal ? min(p.S - p.Lq + rlast / p.G + 1, p.S) : p.S;
+    const int nblk = (nkeys + KV_BLOCK - 1) / KV_BLOCK;
+
+    const char *kbase = static_cast<const char *>(p.k) + ((int64_t)b * p.ks[0] + (int64_t)gk * p.ks[1]) * 2;
+    const char *vbase = static_cast<const char *>(p.v) + ((int64_t)b * p.vs[0] + (int64_t)gk * p.vs[1]) * 2;
+    const int64_t kstr = p.ks[2] * 2, vstr = p.vs[2] * 2;
+    // load q = wave + W j of a block: q < 16 -> K key rows 4 q .. 4 q + 3, else V key rows 4 (q - 16) ..;
+    // lane L row 4 (q mod 16) + L / 16, slot L mod 16 (K chunk slot ^ (row mod 16), V chunk slot ^ 2 (row mod 8))
+    const int lrow = lane >> 4, lslot = lane & 15;
+    auto issue = [&](int blk) {
+        const int kb = blk * KV_BLOCK;
+        char *buf = lds + (blk % NB) * 2 * KBYTES;
+#pragma unroll
+        for (int j = 0; j < QW; ++j) {
+            const int q = wave + W * j;
+            const int qq = q & 15;
+            const int row = 4 * qq + lrow;
+            const int key = min(kb + row, p.S - 1);
+            if (q < 16) {
+                const int ch = lslot ^ (row & 15);
+                __builtin_amdgcn_global_load_lds(static_cast<const void *>(kbase + key * kstr + ch * 16),
+                                                 BI_LDS_PTR(buf + qq * 1024), 16, 0, 0);
+            } else {
+                const int ch = lslot ^ ((row & 7) << 1);
+                __builtin_amdgcn_global_load_lds(static_cast<const void *>(vbase + key * vstr + ch * 16),
+                                                 BI_LDS_PTR(buf + KBYTES + qq * 1024), 16, 0, 0);
+            }
+        }
+    };
+
+    Rows16 r;
+    rows16_load<dt>(p, tile, b, gk, r);
+    // running fold over splits (per score row in lane r16) and the current split's state
+    bool have = false;
+    float mt = 0.0f, lt = 0.0f;
+    f32x4 ot[8];
+    float m_run = NEG_INF, l_run = 0.0f;
+    f32x4 o[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        ot[t] = zero4();
+        o[t] = zero4();
+    }
+    auto fold_split = [&]() {
+        // sdpa_combine's step for this split's partial, per row: skip an empty partial, copy the first
+        // non-empty one, otherwise rescale both sides to the larger maximum
+        const bool skip = m_run == NEG_INF;
+        const bool first = !skip && !have;
+        const float m2 = fmaxf(mt, m_run);
+        const float a = exp2_hw(mt - m2);
+        const float bs = exp2_hw(m_run - m2);
+        if (first) {
+            mt = m_run;
+            lt = l_run;
+        } else if (!skip) {
+            lt = __builtin_fmaf(lt, a, l_run * bs);
+            mt = m2;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int src = 4 * g + i;
+            const bool skip_i = __shfl((int)skip, src) != 0;
+            const bool first_i = __shfl((int)first, src) != 0;
+            const float a_i = __shfl(a, src), b_i = __shfl(bs, src);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                if (first_i) ot[t][i] = o[t][i];
+                else if (!skip_i) ot[t][i] = __builtin_fmaf(ot[t][i], a_i, o[t][i] * b_i);
+            }
+        }
+        have = have || !skip;
+        m_run = NEG_INF;
+        l_run = 0.0f;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) o[t] = zero4();
+    };
+
+    // blocks blk .. blk + NB - 2 are in flight when block blk is waited for; block blk + NB - 1 goes into
+    // the buffer block blk - 1 used, once every wavefront is past it
+    for (int j = 0; j < NB - 1 && j < nblk; ++j) issue(j);
+    for (int blk = 0; blk < nblk; ++blk) {
+        const int kb = blk * KV_BLOCK;
+        char *Ks = lds + (blk % NB) * 2 * KBYTES;
+        char *Vs = Ks + KBYTES;
+        if (blk + NB - 2 < nblk) BI_WAIT_VMCNT(QW * (NB - 2));   // this wavefront's loads of block blk landed
+        else BI_WAIT_VMCNT(0);
+        if (kb + KV_BLOCK > p.S) {
+            // V rows past S read as zero; each wavefront clears the rows its own loads filled
+#pragma unroll
+            for (int j = 0; j < QW; ++j) {
+                const int q = wave + W * j;
+                const int row = 4 * (q & 15) + lrow;
+                if (q >= 16 && kb + row >= p.S) *reinterpret_cast<u32x4 *>(Vs + row * ROWB + lslot * 16) = zero_u4();
+            }
+            __builtin_amdgcn_s_waitcnt(0xc07f);
+        }
+        __syncthreads();                                 // block blk visible to all; block blk - 1 no longer read
+        if (blk + NB - 1 < nblk) issue(blk + NB - 1);
+        attn_block16<dt>(p, r, Ks, Vs, kb, m_run, l_run, o, []() {}, []() {});
+        if ((blk + 1) % BPS == 0 || blk + 1 == nblk) fold_split();
+    }
+
+    // normalise, canonicalise -0, round once: O rows 4 g + i, columns 16 t + r16
+    const float lrow_l = lt;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int ro = tile * 16 + 4 * g + i;
+        const bool have_i = __shfl((int)have, 4 * g + i) != 0;
+        const float l_i = __shfl(lrow_l, 4 * g + i);
+        if (ro >= R) continue;
+        const int iq = ro / p.G, h = gk * p.G + ro % p.G;
+        char *orow = static_cast<char *>(p.o) +
+                     ((int64_t)b * p.os[0] + (int64_t)h * p.os[1] + (int64_t)iq * p.os[2]) * Elem<dt>::bytes;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            float v = have_i ? ot[t][i] / l_i : 0.0f;
+            v = v + 0.0f;                                // -0 -> +0
+            store_from_f32<dt>(orow, 16 * t + r16, v);
+        }
+    }
+}
+
 // Fold the split partials of one query row left to right, normalise, round.
 // One thread per output column; the partials of CH splits are loaded together
 // (independent loads in flight at once), then folded one split at a time in
@@ -664,28 +862,47 @@ __global__ __launch_bounds__(D) void sdpa_combine(SdpaParams p) {
     store_from_f32<dt>(orow, d, r);
 }
 
-size_t sdpa_workspace_bytes(int64_t B, int64_t Hq, int64_t Lq, int64_t S, int64_t D) {
+// Query chunks of at least this many rows against caches longer than four
+// splits take the workspace-free prefill kernel (measured: below ~300 rows the
+// split kernel's extra parallelism wins, above it the shared K / V blocks do).
+constexpr int64_t PREFILL_MIN_LQ = 384;
+
+SdpaPath sdpa_path(int64_t Lq, int64_t S, int64_t D, int dt) {
+    if (dt == DT_F32 || D != 128 || S <= 0) return SDPA_SPLIT;
+    if ((S + KV_SPLIT - 1) / KV_SPLIT <= FUSED_MAXW) return SDPA_FUSED16;
+    if (Lq >= PREFILL_MIN_LQ) return SDPA_PREFILL16;
+    return SDPA_SPLIT;
+}
+
+size_t sdpa_workspace_bytes(int64_t B, int64_t Hq, int64_t Lq, int64_t S, int64_t D, int dt) {
     if (B <= 0 || Hq <= 0 || Lq <= 0 || S <= 0 || D <= 0) return 0;
+    if (sdpa_path(Lq, S, D, dt) != SDPA_SPLIT) return 0;
     const int64_t rows = B * Hq * Lq;
     const int64_t nsplit = (S + KV_SPLIT - 1) / KV_SPLIT;
     const int64_t ml = (rows * nsplit * 2 * 4 + 255) / 256 * 256;
     return (size_t)(ml + rows * nsplit * D * 4);
 }
 
-void sdpa_bind_workspace(SdpaParams &p, void *ws, int D) {
+void sdpa_bind_workspace(SdpaParams &p, void *ws) {
     const int64_t rows = (int64_t)p.B * p.Hq * p.Lq;
-    p.nsplit = (p.S + KV_SPLIT - 1) / KV_SPLIT;
     const int64_t ml = (rows * p.nsplit * 2 * 4 + 255) / 256 * 256;
     p.ws_ml = static_cast<float *>(ws);
     p.ws_o = reinterpret_cast<float *>(static_cast<char *>(ws) + ml);
-    (void)D;
 }
 
 template <int dt, int D>
 static hipError_t launch_typed(const SdpaParams &p, hipStream_t st) {
     const int R = p.G * p.Lq;
+    const SdpaPath path = sdpa_path(p.Lq, p.S, D, dt);
     if constexpr (dt != DT_F32 && D == 128) {
-        if (p.nsplit >= 1 && p.nsplit <= FUSED_MAXW) {
+        if (path == SDPA_PREFILL16) {
+            constexpr int W = 4;                         // row tiles per workgroup sharing each K / V block
+            const int64_t nwg = (int64_t)(((R + 15) / 16 + W - 1) / W) * p.B * p.Hkv;
+            if (nwg > INT32_MAX) return hipErrorInvalidConfiguration;
+            hipLaunchKernelGGL((sdpa_prefill16<dt, W, 2>), dim3((unsigned)nwg), dim3(64 * W), 0, st, p);
+            return hipGetLastError();
+        }
+        if (path == SDPA_FUSED16) {
             const int64_t nwg = (int64_t)((R + 15) / 16) * p.B * p.Hkv;
             if (nwg > INT32_MAX) return hipErrorInvalidConfiguration;
             hipLaunchKernelGGL((sdpa_fused16<dt>), dim3((unsigned)nwg), dim3(64 * p.nsplit), 0, st, p);
@@ -711,10 +928,12 @@ static hipError_t launch_typed(const SdpaParams &p, hipStream_t st) {
     return hipGetLastError();
 }
 
-const char *sdpa_kernel_name(int S, int D, int dt) {
-    const int nsplit = (S + KV_SPLIT - 1) / KV_SPLIT;
-    if (dt != DT_F32 && D == 128) return nsplit <= FUSED_MAXW ? "sdpa_fused16" : "sdpa_split16+combine";
-    return "sdpa_split+combine";
+const char *sdpa_kernel_name(int64_t Lq, int64_t S, int64_t D, int dt) {
+    switch (sdpa_path(Lq, S, D, dt)) {
+        case SDPA_FUSED16: return "sdpa_fused16";
+        case SDPA_PREFILL16: return "sdpa_prefill16";
+        default: return dt != DT_F32 && D == 128 ? "sdpa_split16+combine" : "sdpa_split+combine";
+    }
 }
 
 hipError_t launch_sdpa(const SdpaParams &p, int dt, int D, hipStream_t st) {

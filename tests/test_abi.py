@@ -119,11 +119,12 @@ def test_sdpa_validation(lib):
     assert sdpa(lib, Lq=17, S=16, causal=1) == INVALID  # causal needs Lq <= S
     assert sdpa(lib, dt=9) == INVALID
     assert sdpa(lib, scale=float("inf")) == INVALID
-    assert sdpa(lib, ws=None) == WORKSPACE
-    need = lib.bi_sdpa_workspace_bytes(1, 4, 1, 16, 128)
+    # fp32 runs the split path, which needs a workspace
+    assert sdpa(lib, dt=F32, ws=None) == WORKSPACE
+    need = lib.bi_sdpa_workspace_bytes(1, 4, 1, 16, 128, F32)
     assert need > 0
-    assert sdpa(lib, wsb=need - 4) == WORKSPACE
-    assert sdpa(lib, ws=ctypes.c_void_p(0x7f0000000010)) == UNSUPPORTED   # workspace 256-byte aligned
+    assert sdpa(lib, dt=F32, wsb=need - 4) == WORKSPACE
+    assert sdpa(lib, dt=F32, ws=ctypes.c_void_p(0x7f0000000010)) == UNSUPPORTED   # workspace 256-byte aligned
     bad = strides((1, 4, 1, 128))
     bad[3] = 2
     assert sdpa(lib, qstr=bad) == UNSUPPORTED
@@ -135,11 +136,21 @@ def test_sdpa_validation(lib):
 
 
 def test_sdpa_workspace_formula(lib):
-    # (rows * nsplit * 2 floats, padded to 256 B) + rows * nsplit * D floats
-    rows, nsplit, D = 2 * 32 * 3, (1000 + 255) // 256, 128
-    ml = (rows * nsplit * 8 + 255) // 256 * 256
-    assert lib.bi_sdpa_workspace_bytes(2, 32, 3, 1000, D) == ml + rows * nsplit * D * 4
-    assert lib.bi_sdpa_workspace_bytes(1, 1, 1, 0, 128) == 0
+    # split path: (rows * nsplit * 2 floats, padded to 256 B) + rows * nsplit * D floats
+    def split_bytes(B, Hq, Lq, S, D):
+        rows, nsplit = B * Hq * Lq, (S + 255) // 256
+        return (rows * nsplit * 8 + 255) // 256 * 256 + rows * nsplit * D * 4
+    assert lib.bi_sdpa_workspace_bytes(2, 32, 3, 1000, 128, F32) == split_bytes(2, 32, 3, 1000, 128)
+    assert lib.bi_sdpa_workspace_bytes(2, 32, 3, 1000, 64, BF16) == split_bytes(2, 32, 3, 1000, 64)
+    assert lib.bi_sdpa_workspace_bytes(2, 32, 3, 2000, 128, F16) == split_bytes(2, 32, 3, 2000, 128)
+    # 16-bit D = 128: S <= 1024 (fused) and Lq >= 128 (prefill) need none
+    assert lib.bi_sdpa_workspace_bytes(2, 32, 3, 1000, 128, BF16) == 0
+    assert lib.bi_sdpa_workspace_bytes(2, 32, 3, 1024, 128, BF16) == 0
+    assert lib.bi_sdpa_workspace_bytes(2, 32, 3, 1025, 128, BF16) == split_bytes(2, 32, 3, 1025, 128)
+    assert lib.bi_sdpa_workspace_bytes(1, 32, 384, 32768, 128, BF16) == 0
+    assert lib.bi_sdpa_workspace_bytes(1, 32, 383, 32768, 128, BF16) == split_bytes(1, 32, 383, 32768, 128)
+    assert lib.bi_sdpa_workspace_bytes(1, 1, 1, 0, 128, BF16) == 0
+    assert lib.bi_sdpa_workspace_bytes(1, 1, 1, 10, 128, 7) == 0
 
 
 def test_variant_policy_and_validation(lib):
@@ -166,6 +177,9 @@ def test_python_binding_rejects_cpu_tensors_and_dtypes():
 def test_kernel_name_queries(lib):
     assert lib.bi_sdpa_kernel_name(1, 32, 1, 1024, 128, BF16).decode() == "sdpa_fused16"
     assert lib.bi_sdpa_kernel_name(1, 32, 64, 1025, 128, F16).decode() == "sdpa_split16+combine"
+    assert lib.bi_sdpa_kernel_name(1, 32, 384, 1025, 128, F16).decode() == "sdpa_prefill16"
+    assert lib.bi_sdpa_kernel_name(1, 32, 383, 1025, 128, F16).decode() == "sdpa_split16+combine"
+    assert lib.bi_sdpa_kernel_name(1, 32, 384, 1024, 128, BF16).decode() == "sdpa_fused16"
     assert lib.bi_sdpa_kernel_name(1, 32, 1, 300, 128, F32).decode() == "sdpa_split+combine"
     assert lib.bi_sdpa_kernel_name(1, 32, 1, 300, 64, BF16).decode() == "sdpa_split+combine"
     for bad in ((0, 32, 1, 10, 128, BF16), (1, 32, 1, 0, 128, BF16), (1, 32, 1, 10, 96, BF16),

@@ -259,3 +259,51 @@ def test_readme_style_call():
     assert_bits_equal(bi.scaled_dot_product_attention(q[:, :, -4:], k, v, mask="causal"),
                       bi.bi_sdpa(q[:, :, -4:], k, v, causal=True), "mask='causal'")
     assert np.isfinite(bi.scaled_dot_product_attention(q[:, :, -4:], k, v).float().cpu().numpy()).all()
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16], ids=_ids)
+def test_prefill_path_matches_split_path_and_decode(dt):
+    """Query chunks of >= 384 rows against caches of more than 1024 keys run the workspace-free
+    prefill kernel; chunks of 383 run the split + combine kernels.  The tokens two such chunks share
+    must have the same bits, and sampled tokens must equal their own decode call."""
+    lib = bi._native.load()
+    BI = bi.BI_BF16 if dt == torch.bfloat16 else bi.BI_F16
+    for (B, Hq, Hkv, S) in [(2, 32, 8, 2085), (1, 16, 8, 1500), (1, 8, 8, 1100)]:
+        q = synthetic.randn((B, Hq, 500, 128), 0x5EED50 + S, 1.0, dt).to(DEV)
+        k = synthetic.randn((B, Hkv, S, 128), 0x5EED51 + S, 1.0, dt).to(DEV)
+        v = synthetic.randn((B, Hkv, S, 128), 0x5EED52 + S, 1.0, dt).to(DEV)
+        assert lib.bi_sdpa_kernel_name(B, Hq, 384, S, 128, BI).decode() == "sdpa_prefill16"
+        assert lib.bi_sdpa_kernel_name(B, Hq, 383, S, 128, BI).decode() == "sdpa_split16+combine"
+        split = bi.bi_sdpa(q[:, :, -383:], k, v, causal=True)
+        for L in (384, 390, 500):
+            pre = bi.bi_sdpa(q[:, :, -L:], k, v, causal=True)
+            assert_bits_equal(pre[:, :, -383:], split, f"S={S} Hq={Hq}: q_len {L} (prefill) vs 383 (split)")
+            for i in (0, L // 2, L - 1):
+                p = S - L + i
+                dec = bi.bi_sdpa(q[:, :, 500 - L + i:500 - L + i + 1], k[:, :, :p + 1], v[:, :, :p + 1], causal=True)
+                assert_bits_equal(pre[:, :, i:i + 1], dec, f"S={S} q_len {L} token {i} vs its decode")
+        # no causal mask, boolean mask with holes
+        mask = torch.ones(1, 1, 1, S, dtype=torch.bool, device=DEV)
+        mask[..., 50:300] = False
+        a = bi.bi_sdpa(q[:, :, -384:], k, v, mask=mask)
+        c = bi.bi_sdpa(q[:, :, -383:], k, v, mask=mask)
+        assert_bits_equal(a[:, :, -383:], c, f"S={S}: masked, prefill vs split")
+        ref = oracle.sdpa(q[:1, :, -384:].cpu(), k[:1].cpu(), v[:1].cpu(), mask=mask.cpu())
+        assert_close_to_oracle(a[:1].cpu(), ref, f"S={S}: masked prefill vs oracle")
+
+
+def test_long_causal_prefill_needs_no_workspace():
+    """A 4096-token causal prefill against its own 4096-key cache (the split path would need a
+    multi-GB workspace): no workspace is requested, sampled rows match the oracle and equal a decode."""
+    S = 4096
+    q = synthetic.randn((1, 32, S, 128), 0x5EED60, 1.0, torch.bfloat16).to(DEV)
+    k = synthetic.randn((1, 8, S, 128), 0x5EED61, 1.0, torch.bfloat16).to(DEV)
+    v = synthetic.randn((1, 8, S, 128), 0x5EED62, 1.0, torch.bfloat16).to(DEV)
+    assert bi.sdpa_workspace_bytes(1, 32, S, S, 128, torch.bfloat16) == 0
+    o = bi.bi_sdpa(q, k, v, causal=True)
+    qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
+    for p in (0, 1, 255, 256, 1000, 2047, 4095):
+        ref = oracle.sdpa(qc[:, :, p:p + 1], kc[:, :, :p + 1], vc[:, :, :p + 1], causal=True)
+        assert_close_to_oracle(o[:, :, p:p + 1].cpu(), ref, f"row {p}")
+        dec = bi.bi_sdpa(q[:, :, p:p + 1], k[:, :, :p + 1], v[:, :, :p + 1], causal=True)
+        assert_bits_equal(o[:, :, p:p + 1], dec, f"row {p} vs its decode")
