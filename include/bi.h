@@ -203,6 +203,24 @@ bi_status bi_variant_linear(const void *x, int64_t ldx,
 size_t bi_variant_workspace_bytes(int64_t M, int64_t N, int splits);
 int bi_variant_splits(int64_t M);
 
+/*
+ * Row sum / row mean over the last dimension (README, section "Why MLX is not
+ * invariant", the paragraph listing the ops a batch-invariant stack relies on
+ * besides matmul and attention: sum and mean among them).
+ *
+ * y[m] = round_to_dt( sum over n < N of x[m, n] ), or that sum divided by N
+ * (one IEEE fp32 division) when mean != 0.  x: M rows of N elements, row m at
+ * x + m * ldx (ldx >= N, in elements; ignored when M == 1).  y: M contiguous
+ * elements of dtype dt (F32, F16 or BF16, the same as x).  Each row is reduced
+ * in fp32 in an order fixed by N alone: 256 threads, thread t adds elements
+ * t, t + 256, ... in ascending order from +0, the 64 partials of a wavefront
+ * are combined over lane distances 32, 16, ..., 1, the four wavefront sums as
+ * (w0 + w1) + (w2 + w3).  No row depends on M or on the other rows.  N == 0
+ * gives 0 (sum) or NaN (mean).  M == 0 enqueues nothing.
+ */
+bi_status bi_rowsum(const void *x, int64_t ldx, void *y, int64_t M, int64_t N, int mean, bi_dtype dt,
+                    void *stream);
+
 /* Which kernel configuration a GEMM of this shape runs on ("gemm_skinny_nk/fm1",
  * "gemm_tiled_kn/128x128", ...; b_kn != 0 for a row-major (K, N) operand of
  * bi_matmul / bi_addmm, 0 for bi_linear and for column-major operands).  Informational: every configuration computes the same bits.

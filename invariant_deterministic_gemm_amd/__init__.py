@@ -12,6 +12,7 @@ Entry points (same names as the C ABI, plus the README's short names):
     bi_matmul(a, b)                         y = a b, b is (K, N)
     bi_addmm(c, a, b, alpha=1, beta=1)      y = alpha a b + beta c
     bi_sdpa(q, k, v, causal=False, mask=None, scale=None)
+    bi_rowsum(x, mean=False)                row sum / mean over the last dim
     bi_variant_linear(x, w, bias=None, splits=None)   batch-VARIANT comparator
 """
 from __future__ import annotations
@@ -24,7 +25,7 @@ import torch
 from . import _native
 from ._native import BI_BF16, BI_F16, BI_F32
 
-__all__ = ["bi_linear", "bi_matmul", "bi_addmm", "bi_sdpa", "bi_variant_linear",
+__all__ = ["bi_linear", "bi_matmul", "bi_addmm", "bi_sdpa", "bi_rowsum", "bi_variant_linear",
            "linear", "matmul", "addmm", "scaled_dot_product_attention",
            "abi_version", "library_path", "BiError"]
 
@@ -272,6 +273,21 @@ def bi_sdpa(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fa
     return o
 
 
+def bi_rowsum(x: torch.Tensor, mean: bool = False) -> torch.Tensor:
+    """Sum (or mean) of x over its last dimension, in an order fixed by the row length alone."""
+    dev = _on_gpu(x)
+    lead = x.shape[:-1]
+    N = x.shape[-1]
+    x2 = _rows(x)
+    M = x2.shape[0]
+    y = torch.empty((M,), dtype=x.dtype, device=dev)
+    lib = _native.load()
+    st = lib.bi_rowsum(_ptr(x2), x2.stride(0) if M > 1 else max(N, 1), _ptr(y), M, N, 1 if mean else 0,
+                       _dt(x2, "bi_rowsum"), _stream(dev))
+    _check(st, "bi_rowsum")
+    return y.reshape(lead)
+
+
 def bi_variant_linear(x: torch.Tensor, w: torch.Tensor, bias: torch.Tensor | None = None,
                       splits: int | None = None, out_dtype: torch.dtype | None = None) -> torch.Tensor:
     """Batch-VARIANT comparator: bi_linear's kernels with M-keyed split-K (not invariant)."""
@@ -308,3 +324,9 @@ def scaled_dot_product_attention(q, k, v, mask=None, scale=None):
             raise ValueError("mask must be None, 'causal' or a boolean tensor")
         return bi_sdpa(q, k, v, causal=True, scale=scale)
     return bi_sdpa(q, k, v, causal=False, mask=mask, scale=scale)
+
+
+# README, section "Use": route the framework's matmul and attention through these kernels.
+from .mode import batch_invariant_mode  # noqa: E402
+
+__all__ += ["batch_invariant_mode"]

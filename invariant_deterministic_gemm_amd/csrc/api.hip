@@ -18,6 +18,7 @@
 #include "bi.h"
 #include "device.h"
 #include "gemm.h"
+#include "rowsum.h"
 #include "sdpa.h"
 
 namespace {
@@ -306,6 +307,19 @@ bi_status bi_variant_linear(const void *x, int64_t ldx, const void *w, int64_t l
     bi::GemmParams p = make_params(x, ldx, w, ldw, bias, 0, y, ldy, M, N, K, 1.0f, 1.0f);
     return device_status(bi::launch_gemm_splitk(p, in_dt, out_dt, splits, (float *)ws, (hipStream_t)stream),
                          "bi_variant_linear");
+}
+
+bi_status bi_rowsum(const void *x, int64_t ldx, void *y, int64_t M, int64_t N, int mean, bi_dtype dt,
+                    void *stream) {
+    const char *fn = "bi_rowsum";
+    if (!dtype_known(dt)) return fail(BI_ERR_INVALID, "%s: unknown dtype code %d", fn, (int)dt);
+    if (M < 0 || N < 0 || M > kMaxDim || N > kMaxDim)
+        return fail(BI_ERR_INVALID, "%s: bad sizes M=%lld N=%lld", fn, (long long)M, (long long)N);
+    if (M == 0) return ok();
+    if (y == nullptr || (N > 0 && x == nullptr)) return fail(BI_ERR_INVALID, "%s: tensor pointer is null", fn);
+    if (M > 1 && ldx < N) return fail(BI_ERR_INVALID, "%s: ldx=%lld < N=%lld", fn, (long long)ldx, (long long)N);
+    return device_status(bi::launch_rowsum(x, M > 1 ? ldx : N, y, M, N, mean ? 1 : 0, (int)dt, (hipStream_t)stream),
+                         fn);
 }
 
 const char *bi_gemm_kernel_name(int64_t M, int64_t N, int64_t K, bi_dtype in_dt, int b_kn) {

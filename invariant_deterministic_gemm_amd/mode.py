@@ -1,0 +1,282 @@
+"""Route PyTorch's matmul family and scaled-dot-product attention through the
+batch-invariant kernels (mlx-batch-invariant README, section "Use": a context
+that patches the framework's matmul and attention, strict by default).
+
+    with batch_invariant_mode():          # strict: unsupported calls raise
+        y = model(x)
+
+    with batch_invariant_mode(strict=False) as m:
+        y = model(x)                      # unsupported calls run stock PyTorch
+    m.fallbacks                           # how many did, by function name
+
+Intercepted at the Python API (a TorchFunctionMode), for GPU tensors:
+    torch.nn.functional.linear, torch.mm, torch.addmm, torch.matmul, torch.bmm,
+    the Tensor methods mm / addmm / matmul / bmm and the @ operator,
+    torch.nn.functional.scaled_dot_product_attention,
+    torch.sum / torch.mean and the Tensor methods, when they reduce floating
+    point tensors over the last dimension alone (full reductions and other
+    dims are not row-wise and pass through).  On this GPU PyTorch's fp32
+    last-dim sum and mean change their order with the number of rows, so
+    they are routed too; softmax, log_softmax, layer_norm, rms_norm and max
+    were measured invariant and are left alone.
+Every routed call runs the library's kernels through the C ABI binding, so
+results equal bi_linear / bi_matmul / bi_addmm / bi_sdpa / bi_rowsum bit for
+bit and no row depends on the batch.  A batched matmul runs one GEMM per batch element.
+Calls whose tensors are all on the CPU are not the library's business and
+pass through untouched in either mode.
+
+Not routed (raises NotImplementedError when strict; runs stock PyTorch and
+is counted otherwise): dtypes other than fp32 / fp16 / bf16, mixed dtypes,
+inputs that require gradients while grad mode is on (the kernels are
+forward-only), out= arguments, broadcast batch dims in a matmul, attention
+with dropout, a float (additive) mask, head dims other than 64 / 128, a
+causal flag together with a mask, and anything the library itself refuses
+(for example K not a multiple of 8 for 16-bit inputs).  torch's is_causal
+aligns the mask to the top-left corner; it is passed on as the library's
+causal flag when the query and key lengths are equal (the two alignments
+coincide) and as the equivalent boolean mask otherwise.
+"""
+from __future__ import annotations
+
+import contextlib
+from collections import Counter
+
+import torch
+import torch.nn.functional as F
+from torch.overrides import TorchFunctionMode
+
+from . import bi_addmm, bi_linear, bi_matmul, bi_rowsum, bi_sdpa
+
+_SUPPORTED = (torch.float32, torch.float16, torch.bfloat16)
+
+
+class Unsupported(Exception):
+    """A call the invariant kernels cannot serve (raised inside the mode only)."""
+
+
+class _NotOurs(Exception):
+    """A call of a routed function that is not a row-wise operation (passed to torch, not counted)."""
+
+
+def _need(cond: bool, why: str):
+    if not cond:
+        raise Unsupported(why)
+
+
+def _check_tensors(*ts):
+    dt = None
+    for t in ts:
+        if t is None:
+            continue
+        _need(isinstance(t, torch.Tensor), "non-tensor operand")
+        _need(t.dtype in _SUPPORTED, f"dtype {t.dtype}")
+        _need(not (torch.is_grad_enabled() and t.requires_grad), "operand requires grad (forward-only kernels)")
+        dt = dt or t.dtype
+        _need(t.dtype == dt, "mixed dtypes")
+
+
+def plan_matmul(a_shape, b_shape) -> str:
+    """How torch.matmul(a, b) maps onto the kernels, from the shapes alone:
+    'mm'  a (..., K) x b (K, N): one GEMM over the flattened rows of a;
+    'mv'  a (..., K) x b (K,); 'vm' a (K,) x b (K, N); 'dot' a (K,) x b (K,);
+    'batched' a (*B, M, K) x b (*B, K, N) with equal batch dims: one GEMM per element.
+    Raises Unsupported otherwise (scalars, broadcast batch dims)."""
+    da, db = len(a_shape), len(b_shape)
+    if da == 0 or db == 0:
+        raise Unsupported("scalar operand")
+    if db == 1:
+        return "mv" if da >= 2 else "dot"
+    if db == 2:
+        return "vm" if da == 1 else "mm"
+    if da == db and tuple(a_shape[:-2]) == tuple(b_shape[:-2]):
+        return "batched"
+    raise Unsupported(f"matmul of shapes {tuple(a_shape)} and {tuple(b_shape)} (broadcast batch dims)")
+
+
+def _matmul(input, other):
+    a, b = input, other
+    _check_tensors(a, b)
+    kind = plan_matmul(tuple(a.shape), tuple(b.shape))
+    if kind == "mm":
+        return bi_matmul(a, b)
+    if kind == "mv":
+        return bi_linear(a, b.reshape(1, -1)).squeeze(-1)
+    if kind == "vm":
+        return bi_matmul(a.reshape(1, -1), b).squeeze(0)
+    if kind == "dot":
+        return bi_linear(a.reshape(1, -1), b.reshape(1, -1)).reshape(())
+    lead = a.shape[:-2]
+    a3 = a.reshape(-1, a.shape[-2], a.shape[-1])
+    b3 = b.reshape(-1, b.shape[-2], b.shape[-1])
+    out = torch.empty((a3.shape[0], a.shape[-2], b.shape[-1]), dtype=a.dtype, device=a.device)
+    for i in range(a3.shape[0]):
+        out[i] = bi_matmul(a3[i], b3[i])
+    return out.reshape(*lead, a.shape[-2], b.shape[-1])
+
+
+def _rmatmul(input, other):               # Tensor.__rmatmul__(self, other) computes other @ self
+    return _matmul(other, input)
+
+
+def _linear(input, weight, bias=None):
+    _check_tensors(input, weight, bias)
+    _need(weight.dim() == 2, "weight must be 2-D")
+    _need(bias is None or bias.dim() == 1, "bias must be 1-D")
+    return bi_linear(input, weight, bias)
+
+
+def _mm(input, mat2):
+    _check_tensors(input, mat2)
+    _need(input.dim() == 2 and mat2.dim() == 2, "mm needs 2-D operands")
+    return bi_matmul(input, mat2)
+
+
+def _bmm(input, mat2):
+    _need(input.dim() == 3 and mat2.dim() == 3, "bmm needs 3-D operands")
+    return _matmul(input, mat2)
+
+
+def _addmm(input, mat1, mat2, beta=1, alpha=1):
+    _check_tensors(input, mat1, mat2)
+    _need(mat1.dim() == 2 and mat2.dim() == 2, "addmm needs 2-D operands")
+    M, N = mat1.shape[0], mat2.shape[1]
+    c = input
+    if c.dim() == 2 and tuple(c.shape) == (1, N) and M != 1:
+        c = c.reshape(N)
+    _need((c.dim() == 1 and c.shape[0] == N) or (c.dim() == 2 and tuple(c.shape) == (M, N)),
+          f"addmm input of shape {tuple(input.shape)} does not broadcast the library's way")
+    return bi_addmm(c, mat1, mat2, float(alpha), float(beta))
+
+
+def _sdpa(query, key, value, attn_mask=None, dropout_p=0.0, is_causal=False, scale=None, enable_gqa=False):
+    q, k, v = query, key, value
+    _check_tensors(q, k, v)
+    _need(dropout_p == 0.0, "dropout")
+    _need(q.dim() == 4 and k.dim() == 4 and v.dim() == 4, "q, k, v must be 4-D")
+    _need(q.shape[-1] in (64, 128) and k.shape[-1] == q.shape[-1] and v.shape[-1] == q.shape[-1], "head dim")
+    Hq, Hkv = q.shape[1], k.shape[1]
+    _need(Hq == Hkv or (enable_gqa and Hq % Hkv == 0), "query / key head counts")
+    Lq, S = q.shape[2], k.shape[2]
+    if attn_mask is not None:
+        _need(not is_causal, "causal flag together with a mask")
+        _need(attn_mask.dtype == torch.bool, "float (additive) mask")
+        return bi_sdpa(q, k, v, mask=attn_mask, scale=scale)
+    if is_causal:
+        if Lq == S:
+            return bi_sdpa(q, k, v, causal=True, scale=scale)
+        # torch aligns is_causal to the top-left corner: query i sees keys 0 .. i
+        top_left = torch.ones(Lq, S, dtype=torch.bool, device=q.device).tril()
+        return bi_sdpa(q, k, v, mask=top_left, scale=scale)
+    return bi_sdpa(q, k, v, scale=scale)
+
+
+def _last_dim_only(x, dim) -> bool:
+    if isinstance(dim, (list, tuple)):
+        if len(dim) != 1:
+            return False
+        dim = dim[0]
+    return isinstance(dim, int) and x.dim() > 0 and dim in (-1, x.dim() - 1)
+
+
+def _reduce(input, dim=None, keepdim=False, dtype=None, mean=False):
+    # only a reduction over the last dimension alone is row-wise; anything else is not the mode's
+    if not (isinstance(input, torch.Tensor) and input.is_floating_point() and dim is not None
+            and _last_dim_only(input, dim)):
+        raise _NotOurs
+    _need(dtype is None or dtype == input.dtype, "dtype= conversion")
+    _check_tensors(input)
+    y = bi_rowsum(input, mean=mean)
+    return y.unsqueeze(-1) if keepdim else y
+
+
+def _sum(input, dim=None, keepdim=False, dtype=None):
+    return _reduce(input, dim, keepdim, dtype, mean=False)
+
+
+def _mean(input, dim=None, keepdim=False, dtype=None):
+    return _reduce(input, dim, keepdim, dtype, mean=True)
+
+
+# torch function -> (handler, names of torch's parameters in order); handlers use the same names
+_ROUTES = {
+    F.linear: (_linear, ("input", "weight", "bias")),
+    torch.mm: (_mm, ("input", "mat2")),
+    torch.Tensor.mm: (_mm, ("input", "mat2")),
+    torch.addmm: (_addmm, ("input", "mat1", "mat2", "beta", "alpha")),
+    torch.Tensor.addmm: (_addmm, ("input", "mat1", "mat2", "beta", "alpha")),
+    torch.matmul: (_matmul, ("input", "other")),
+    torch.Tensor.matmul: (_matmul, ("input", "other")),
+    torch.Tensor.__matmul__: (_matmul, ("input", "other")),
+    torch.Tensor.__rmatmul__: (_rmatmul, ("input", "other")),
+    torch.bmm: (_bmm, ("input", "mat2")),
+    torch.Tensor.bmm: (_bmm, ("input", "mat2")),
+    F.scaled_dot_product_attention: (_sdpa, ("query", "key", "value", "attn_mask", "dropout_p", "is_causal",
+                                             "scale", "enable_gqa")),
+    torch.sum: (_sum, ("input", "dim", "keepdim", "dtype")),
+    torch.Tensor.sum: (_sum, ("input", "dim", "keepdim", "dtype")),
+    torch.mean: (_mean, ("input", "dim", "keepdim", "dtype")),
+    torch.Tensor.mean: (_mean, ("input", "dim", "keepdim", "dtype")),
+}
+
+
+def routed_functions():
+    """Names of the torch functions the mode intercepts."""
+    return sorted({getattr(f, "__name__", str(f)) for f in _ROUTES})
+
+
+def _call(route, args, kwargs):
+    fn, names = route
+    _need("out" not in kwargs, "out= argument")
+    _need(len(args) <= len(names), "too many arguments")
+    kw = dict(zip(names, args))
+    for k, v in kwargs.items():
+        _need(k in names and k not in kw, f"argument {k}")
+        kw[k] = v
+    return fn(**kw)
+
+
+def _tensors_in(args, kwargs):
+    for x in list(args) + list(kwargs.values()):
+        if isinstance(x, torch.Tensor):
+            yield x
+
+
+class _InvariantMode(TorchFunctionMode):
+    def __init__(self, strict: bool):
+        super().__init__()
+        self.strict = strict
+        self.fallbacks = Counter()
+        self.routed = Counter()
+
+    def __torch_function__(self, func, types, args=(), kwargs=None):
+        kwargs = kwargs or {}
+        route = _ROUTES.get(func)
+        if route is None or not any(t.is_cuda for t in _tensors_in(args, kwargs)):
+            return func(*args, **kwargs)
+        name = getattr(func, "__name__", str(func))
+        try:
+            out = _call(route, args, kwargs)
+        except _NotOurs:
+            return func(*args, **kwargs)
+        except (Unsupported, NotImplementedError) as e:
+            if self.strict:
+                raise NotImplementedError(f"batch_invariant_mode: {name}: {e}") from None
+            self.fallbacks[name] += 1
+            return func(*args, **kwargs)
+        self.routed[name] += 1
+        return out
+
+
+@contextlib.contextmanager
+def batch_invariant_mode(strict: bool = True):
+    """Route torch matmuls and attention on GPU tensors through the batch-invariant kernels.
+
+    strict=True: a call the kernels cannot serve raises NotImplementedError, so nothing silently
+    runs a batch-variant kernel.  strict=False: such calls run stock PyTorch and are counted in the
+    yielded object's `fallbacks`; routed calls are counted in `routed`."""
+    mode = _InvariantMode(strict)
+    with mode:
+        yield mode
+
+
+__all__ = ["batch_invariant_mode", "plan_matmul", "routed_functions", "Unsupported"]

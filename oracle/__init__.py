@@ -65,6 +65,8 @@ def _bind(lib):
     lib.oracle_sdpa_f64.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, d,
                                     ctypes.c_int, p, p]
     lib.oracle_sdpa_f64.restype = None
+    lib.oracle_rowsum_f64.argtypes = [p, i64, i64, i64, ctypes.c_int, p]
+    lib.oracle_rowsum_f64.restype = None
     lib.oracle_threads.restype = ctypes.c_int
     lib.oracle_set_threads.argtypes = [ctypes.c_int]
     return lib
@@ -186,3 +188,17 @@ def sdpa(q, k, v, causal: bool = False, mask=None, scale: float | None = None) -
                             _ptr(out), B, Hq, Hkv, Lq, S, D, float(scale), 1 if causal else 0,
                             mptr, mstr)
     return out
+
+
+def rowsum(x, mean: bool = False) -> np.ndarray:
+    """Sum (or mean) of x over its last dimension, in float64 (README, section "Why MLX is not
+    invariant": sum and mean among the ops a batch-invariant stack relies on)."""
+    X = _f64(x)
+    lead = X.shape[:-1]
+    N = X.shape[-1]
+    X2 = np.ascontiguousarray(X.reshape(int(np.prod(lead)), N))
+    out = np.empty((X2.shape[0],), dtype=np.float64)
+    if X2.shape[0] > 0:
+        with np.errstate(invalid="ignore"):
+            _load().oracle_rowsum_f64(_ptr(X2), N, X2.shape[0], N, 1 if mean else 0, _ptr(out))
+    return out.reshape(lead)

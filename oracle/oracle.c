@@ -177,3 +177,20 @@ void oracle_sdpa_f64(const double *q, const int64_t *qs,
         free(num);
     }
 }
+
+/*
+ * Row reduction over the last dimension (README, section "Why MLX is not
+ * invariant": sum and mean are among the ops a batch-invariant stack relies
+ * on):  out[m] = sum_{n=0}^{N-1} x[m * ldx + n], or that sum divided by N
+ * when mean != 0.  A plain ascending loop in double; N == 0 gives 0 (sum)
+ * or NaN (mean, 0 / 0).
+ */
+void oracle_rowsum_f64(const double *x, int64_t ldx, int64_t M, int64_t N, int mean, double *out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        const double *row = x + m * ldx;
+        double s = 0.0;
+        for (int64_t n = 0; n < N; ++n) s = s + row[n];
+        out[m] = mean ? s / (double)N : s;
+    }
+}

@@ -188,3 +188,12 @@ def test_kernel_name_queries(lib):
     assert lib.bi_gemm_kernel_name(1, 4096, 4096, BF16, 0).decode().startswith("gemm16_strip_nk/")
     assert lib.bi_gemm_kernel_name(4096, 4096, 4096, BF16, 0).decode().startswith("gemm16_ring_nk/")
     assert lib.bi_gemm_kernel_name(0, 4096, 4096, BF16, 0).decode() == "none"
+
+
+def test_rowsum_validation(lib):
+    assert lib.bi_rowsum(P16, 64, P16b, 4, 64, 0, 9, None) == INVALID           # dtype
+    assert lib.bi_rowsum(P16, 64, P16b, -1, 64, 0, BF16, None) == INVALID
+    assert lib.bi_rowsum(P16, 32, P16b, 4, 64, 0, BF16, None) == INVALID         # ldx < N
+    assert lib.bi_rowsum(None, 64, P16b, 4, 64, 1, F32, None) == INVALID         # null input
+    assert lib.bi_rowsum(P16, 64, None, 4, 64, 1, F32, None) == INVALID          # null output
+    assert lib.bi_rowsum(None, 0, None, 0, 64, 0, F32, None) == OK               # nothing to do

@@ -275,7 +275,36 @@ SDPA_PINS = [pin_sdpa_bruteforce, pin_sdpa_default_scale, pin_sdpa_closed_forms,
              pin_sdpa_invariants, pin_sdpa_golden]
 
 
-@pytest.mark.parametrize("pin", GEMM_PINS + SDPA_PINS, ids=lambda f: f.__name__)
+def pin_rowsum_exact():
+    # integers: every order of summation is exact
+    x = synthetic.randint((7, 300), 111, -50, 50, torch.float32)
+    xi = x.to(torch.int64).numpy()
+    assert np.array_equal(oracle.rowsum(x), xi.sum(axis=1).astype(np.float64))
+    assert np.array_equal(oracle.rowsum(x, mean=True), xi.sum(axis=1) / 300.0)
+    # correctly rounded sums of random doubles (math.fsum)
+    y = synthetic.randn((5, 1000), 112, 1.0, torch.float32)
+    got = oracle.rowsum(y)
+    for r in range(5):
+        exact = math.fsum(float(v) for v in _vals(y)[r])
+        assert abs(got[r] - exact) <= 1e-12 * np.abs(_vals(y)[r]).sum()
+    # closed forms: constant rows, one nonzero element, empty rows
+    c = torch.full((3, 17), 0.25)
+    assert np.array_equal(oracle.rowsum(c, mean=True), np.full(3, 0.25))
+    one = torch.zeros(2, 9)
+    one[0, 8] = 3.0
+    one[1, 0] = -2.0
+    assert np.array_equal(oracle.rowsum(one), np.array([3.0, -2.0]))
+    assert np.array_equal(oracle.rowsum(torch.zeros(4, 0)), np.zeros(4))
+    assert np.isnan(oracle.rowsum(torch.zeros(2, 0), mean=True)).all()
+    # leading dims are batch: (2, 3, N) reduces to (2, 3)
+    z = synthetic.randint((2, 3, 11), 113, -9, 9, torch.float32)
+    assert np.array_equal(oracle.rowsum(z), z.to(torch.int64).sum(-1).numpy().astype(np.float64))
+
+
+ROWSUM_PINS = [pin_rowsum_exact]
+
+
+@pytest.mark.parametrize("pin", GEMM_PINS + SDPA_PINS + ROWSUM_PINS, ids=lambda f: f.__name__)
 def test_oracle_pin(pin):
     pin()
 
@@ -299,12 +328,16 @@ MUTANTS = {
     "sdpa_mask_polarity": ("ms[3]] != 0;", "ms[3]] == 0;", SDPA_PINS),
     "sdpa_value_from_key": ("const double *vrow = v + b * vs[0] + g * vs[1] + j * vs[2];",
                             "const double *vrow = k + b * ks[0] + g * ks[1] + j * ks[2];", SDPA_PINS),
+    "rowsum_last_dropped": ("for (int64_t n = 0; n < N; ++n) s = s + row[n];",
+                            "for (int64_t n = 0; n + 1 < N; ++n) s = s + row[n];", ROWSUM_PINS),
+    "rowsum_mean_undivided": ("out[m] = mean ? s / (double)N : s;", "out[m] = s;", ROWSUM_PINS),
+    "rowsum_row_pitch": ("const double *row = x + m * ldx;", "const double *row = x + m;", ROWSUM_PINS),
 }
 
 
 def _run_pins_with(lib_path: str, group: str) -> list:
     """Run one pin group against another build of oracle.c; return the pins that failed."""
-    pins = GEMM_PINS if group == "gemm" else SDPA_PINS
+    pins = {"gemm": GEMM_PINS, "sdpa": SDPA_PINS, "rowsum": ROWSUM_PINS}[group]
     failed = []
     with oracle.use_library(lib_path):
         for pin in pins:
@@ -318,7 +351,7 @@ def _run_pins_with(lib_path: str, group: str) -> list:
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_pins_catch_planted_mistake(name, tmp_path):
     old, new, pins = MUTANTS[name]
-    group = "gemm" if pins is GEMM_PINS else "sdpa"
+    group = "gemm" if pins is GEMM_PINS else ("sdpa" if pins is SDPA_PINS else "rowsum")
     root = os.path.dirname(HERE)
     src = open(os.path.join(root, "oracle", "oracle.c")).read()
     assert src.count(old) == 1, f"mutation anchor not unique in oracle.c: {old!r}"
