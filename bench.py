@@ -351,7 +351,7 @@ def _time_graph(torch, fn, reps=20, iters=10):
 
 def measure_cells(bi, lib, torch, dev, synthetic, data, launches, groups, names, group_ms):
     cells = {"decode_gemm": [], "large_m_gemm": [], "decode_attention": [], "prefill_attention": [],
-             "comparator": {}}
+             "comparator": {}, "e2e_decode": {}}
     K = 4096
     # decode GEMM: weights rotate through copies inside one graph, so reads are cold
     logits = synthetic.cfg5_inputs(torch.bfloat16, M_max=8)
@@ -431,7 +431,61 @@ def measure_cells(bi, lib, torch, dev, synthetic, data, launches, groups, names,
     cells["comparator"] = {"invariant_ms": round(inv_ms, 4), "variant_ms": round(var_ms, 4),
                            "invariant_over_variant_time": round(inv_ms / var_ms, 4),
                            "variant_rows_differing_from_M256": diff}
+    cells["e2e_decode"] = e2e_decode(torch, bi, dev, synthetic)
     return cells
+
+
+def e2e_decode(torch, bi, dev, synthetic):
+    """A random-weight 4-layer decoder (hidden 2048, 16 / 4 heads of 128, SwiGLU 5632, vocab 32000),
+    batch 8, 128-token prompts, 32 greedy decode steps: time per decode step under
+    batch_invariant_mode and with stock PyTorch (the batch-variant comparator), and how many of the
+    32000 last-position logits of one sequence move between batch 1 and batch 8 in each."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import tiny_transformer as tt
+    cfg = tt.TinyConfig(layers=4)
+    W = tt.make_weights(cfg, 0x5EEDE5, dev)
+    prompts = synthetic.randint((8, 128), 0x5EEDE6, 0, cfg.vocab, torch.int64).to(dev)
+    steps = 32
+
+    def run(invariant: bool, p):
+        ctx = bi.batch_invariant_mode() if invariant else _nullcontext()
+        with torch.no_grad(), ctx:
+            logits, cache = tt.forward(cfg, W, p, None, 0)
+            tok = logits[:, -1].float().argmax(-1, keepdim=True)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            pos = p.shape[1]
+            for _ in range(steps):
+                logits, cache = tt.forward(cfg, W, tok, cache, pos)
+                tok = logits[:, -1].float().argmax(-1, keepdim=True)
+                pos += 1
+            b.record()
+            b.synchronize()
+            return a.elapsed_time(b) / steps, logits[:, -1]
+
+    for inv in (True, False):               # warm-up both paths
+        run(inv, prompts)
+    out = {"model": "4 layers, hidden 2048, 16/4 heads x 128, SwiGLU 5632, vocab 32000, bf16, random weights",
+           "batch": 8, "prompt": 128, "decode_steps": steps}
+    for name, inv in (("invariant", True), ("stock", False)):
+        ms, last8 = run(inv, prompts)
+        _, last1 = run(inv, prompts[:1])
+        # decode logits of sequence 0 after 32 steps, alone vs in the batch of 8
+        n = int((last1[0].view(torch.int16) != last8[0].view(torch.int16)).sum())
+        out[name] = {"ms_per_decode_step": round(ms, 3), "tokens_per_s": round(8 * 1e3 / ms, 1),
+                     "logits_differing_batch1_vs_batch8": n}
+    out["invariant_over_stock_time"] = round(out["invariant"]["ms_per_decode_step"] /
+                                             out["stock"]["ms_per_decode_step"], 4)
+    return out
+
+
+class _nullcontext:
+    def __enter__(self):
+        return None
+
+    def __exit__(self, *a):
+        return False
 
 
 def cpu_baseline(torch, synthetic, args):
