@@ -329,37 +329,51 @@ __device__ __forceinline__ void rows16_load(const SdpaParams &p, int tile, int b
     for (int c = 0; c < 4; ++c) r.qf[c] = ldg16(qrow + (32 * c + 8 * g) * 2);
 }
 
-// One 64-key block [kb, kb + 64) of the online softmax for a wavefront's 16
-// rows; K and V blocks in LDS (256-byte key rows, K chunk c at slot
-// c ^ (r mod 16), V chunk c at slot c ^ 2 (r mod 8); V rows of keys past S
-// must read as zero by the time v_ready() returns).  k_done() runs once every
-// K read of the block is complete, v_ready() before the first V read.
-template <int dt, class KDone, class VReady>
-__device__ __forceinline__ void attn_block16(const SdpaParams &p, const Rows16 &r, const char *Ks, const char *Vs,
-                                             int kb, float &m_run, float &l_run, f32x4 (&o)[8], KDone k_done,
-                                             VReady v_ready) {
+// Scores of one 64-key block for a wavefront's 16 rows (K block in LDS, 256-byte key rows, chunk c of
+// key r at slot c ^ (r mod 16)): lane holds S^T[key 16 kt + 4 g + i][row r16].  All K fragments are
+// read first; the four chains (one per kt) each accumulate d chunks c = 0 .. 3 in order.  The K reads
+// may still be in flight on return.
+template <int dt>
+__device__ __forceinline__ void attn_scores16(const Rows16 &r, const char *Ks, f32x4 (&st)[4]) {
     constexpr int ROWB = 256;
-    constexpr float NEG_INF = -__builtin_huge_valf();
     const int lane = threadIdx.x & 63;
     const int r16 = lane & 15, g = lane >> 4;
-    // ---- scores: lane holds S^T[key 16 kt + 4 g + i][row r16].  All K fragments are read first; the four
-    // chains (one per kt) each accumulate d chunks c = 0 .. 3 in order.
     u32x4 kf[4][4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int c = 0; c < 4; ++c)
             kf[kt][c] = *reinterpret_cast<const u32x4 *>(Ks + (16 * kt + r16) * ROWB + (((4 * c + g) ^ r16) << 4));
-    f32x4 st[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) st[kt] = zero4();
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) st[kt] = Mfma<dt>::step(kf[kt][c], r.qf[c], st[kt]);
-    __builtin_amdgcn_s_waitcnt(0xc07f);               // every K read of this block done
-    k_done();
+}
+
+// The rest of one block [kb, kb + 64) given its scores: visibility, the online-softmax update of
+// (m, l, O) and O += P . V from the V block in LDS (chunk c of key r at slot c ^ 2 (r mod 8); rows of
+// keys past S must read as zero by the time v_ready() returns, which is before the first V read).
+template <int dt, class VReady>
+__device__ __forceinline__ void attn_update16(const SdpaParams &p, const Rows16 &r, const f32x4 (&st)[4],
+                                              const char *Vs, int kb, float &m_run, float &l_run, f32x4 (&o)[8],
+                                              VReady v_ready) {
+    constexpr int ROWB = 256;
+    constexpr float NEG_INF = -__builtin_huge_valf();
+    const int lane = threadIdx.x & 63;
+    const int r16 = lane & 15, g = lane >> 4;
     float s[4][4];
+    // block maximum of the row (exact in any order): a tree over the lane's 16 scores, then the lane
+    // groups; taken in each branch next to the products it reads, which the compiler then knows to be
+    // canonical (no quieting step before each maximum)
+    auto lane_max = [&]() {
+        float mk[4];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) mk[kt] = fmaxf(fmaxf(s[kt][0], s[kt][1]), fmaxf(s[kt][2], s[kt][3]));
+        return fmaxf(NEG_INF, fmaxf(fmaxf(mk[0], mk[1]), fmaxf(mk[2], mk[3])));   // all-NaN -> -inf
+    };
+    float mb;
     const bool visible = p.mask == nullptr && kb + KV_BLOCK <= p.S && (!p.causal || kb + KV_BLOCK - 1 <= r.pos_first);
     if (visible) {
         // rows past R get real scores too: they are per-row, never stored, and touch no other row
@@ -367,6 +381,7 @@ __device__ __forceinline__ void attn_block16(const SdpaParams &p, const Rows16 &
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) s[kt][i] = st[kt][i] * p.c;
+        mb = lane_max();
     } else {
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
@@ -379,35 +394,37 @@ __device__ __forceinline__ void attn_block16(const SdpaParams &p, const Rows16 &
                 const float sv = st[kt][i] * p.c;
                 s[kt][i] = ok ? sv : NEG_INF;
             }
+        mb = lane_max();
     }
-    // block maximum of the row (exact in any order): a tree over the lane's 16 scores, then the lane groups
-    float mk[4];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) mk[kt] = fmaxf(fmaxf(s[kt][0], s[kt][1]), fmaxf(s[kt][2], s[kt][3]));
-    float mb = fmaxf(NEG_INF, fmaxf(fmaxf(mk[0], mk[1]), fmaxf(mk[2], mk[3])));   // all-NaN -> -inf, as a scan from -inf
     mb = fmaxf(mb, __shfl_xor(mb, 16));
     mb = fmaxf(mb, __shfl_xor(mb, 32));
     const bool empty = mb == NEG_INF;
     const float m_new = empty ? m_run : fmaxf(m_run, mb);
     const float alpha = empty ? 1.0f : exp2_hw(m_run - m_new);
+    // p = exp2(s - m_new), and 0 for an invisible key: exp2(-inf) is exactly +0, so only a block with no
+    // visible key (m_new possibly -inf, where -inf - -inf would be NaN) needs a different reference
+    const float mref = empty ? 0.0f : m_new;
     float pr[4][4];
     float rs = 0.0f;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            pr[kt][i] = s[kt][i] == NEG_INF ? 0.0f : exp2_hw(s[kt][i] - m_new);
+            pr[kt][i] = exp2_hw(s[kt][i] - mref);
             rs = rs + pr[kt][i];
         }
     rs = rs + __shfl_xor(rs, 16);
     rs = rs + __shfl_xor(rs, 32);
     l_run = __builtin_fmaf(l_run, alpha, rs);
     m_run = m_new;
+    // O * 1 = O: the rescale is skipped when no row's maximum moved
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float ai = __shfl(alpha, 4 * g + i);
+        for (int i = 0; i < 4; ++i) {
+            const float ai = __shfl(alpha, 4 * g + i);
 #pragma unroll
-        for (int t = 0; t < 8; ++t) o[t][i] = o[t][i] * ai;
+            for (int t = 0; t < 8; ++t) o[t][i] = o[t][i] * ai;
+        }
     }
     v_ready();
     // ---- O += P . V: k slot 8 g + j <-> key 32 c + 4 g + j (j < 4), 32 c + 16 + 4 g + (j - 4) (j >= 4).
@@ -431,6 +448,22 @@ __device__ __forceinline__ void attn_block16(const SdpaParams &p, const Rows16 &
 #pragma unroll
         for (int t = 0; t < 8; ++t) o[t] = Mfma<dt>::step(pf, vf[t], o[t]);
     }
+}
+
+
+// One 64-key block [kb, kb + 64) of the online softmax for a wavefront's 16
+// rows, K and V blocks in LDS as attn_scores16 and attn_update16 take them.
+// k_done() runs once every K read of the block is complete, v_ready() before
+// the first V read.
+template <int dt, class KDone, class VReady>
+__device__ __forceinline__ void attn_block16(const SdpaParams &p, const Rows16 &r, const char *Ks, const char *Vs,
+                                             int kb, float &m_run, float &l_run, f32x4 (&o)[8], KDone k_done,
+                                             VReady v_ready) {
+    f32x4 st[4];
+    attn_scores16<dt>(r, Ks, st);
+    __builtin_amdgcn_s_waitcnt(0xc07f);               // every K read of this block done
+    k_done();
+    attn_update16<dt>(p, r, st, Vs, kb, m_run, l_run, o, v_ready);
 }
 
 // One wavefront's share: split `sp` of row tile `tile` of (b, gk), its K / V
@@ -674,7 +707,9 @@ __global__ __launch_bounds__(64 * W) void sdpa_prefill16(SdpaParams p) {
     constexpr int BPS = KV_SPLIT / KV_BLOCK;           // blocks per split
     constexpr float NEG_INF = -__builtin_huge_valf();
     static_assert(QBLK % W == 0, "every wavefront issues the same number of loads");
+    static_assert(16 % W == 0, "load q = wave + W j is a K load exactly when j < 16 / W");
     static_assert(NB >= 2 && QW * (NB - 2) <= 63, "vmcnt range");
+    constexpr int QK = 16 / W;                         // K loads per wavefront per block
     __shared__ __attribute__((aligned(1024))) char lds[NB * 2 * KBYTES];  // [buffer][K block | V block]
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -697,23 +732,41 @@ __global__ __launch_bounds__(64 * W) void sdpa_prefill16(SdpaParams p) {
     // load q = wave + W j of a block: q < 16 -> K key rows 4 q .. 4 q + 3, else V key rows 4 (q - 16) ..;
     // lane L row 4 (q mod 16) + L / 16, slot L mod 16 (K chunk slot ^ (row mod 16), V chunk slot ^ 2 (row mod 8))
     const int lrow = lane >> 4, lslot = lane & 15;
+    // per load j: this lane's key row within a block and its byte offset from the block's first key row.
+    // A block inside S is a uniform base pointer plus these 32-bit offsets (no per-lane 64-bit
+    // arithmetic); the block crossing S clamps its rows to S - 1 in 64-bit arithmetic, as does every
+    // block when a key row stride is too large for 32-bit offsets.
+    const bool off32 = (uint64_t)max(kstr, vstr) * KV_BLOCK + ROWB <= 0xffffffffull;
+    uint32_t loff[QW];
+    int lrowj[QW];
+#pragma unroll
+    for (int j = 0; j < QW; ++j) {
+        const int row = 4 * ((wave + W * j) & 15) + lrow;
+        lrowj[j] = row;
+        loff[j] = j < QK ? (uint32_t)(row * kstr) + ((lslot ^ (row & 15)) << 4)
+                         : (uint32_t)(row * vstr) + ((lslot ^ ((row & 7) << 1)) << 4);
+    }
     auto issue = [&](int blk) {
         const int kb = blk * KV_BLOCK;
         char *buf = lds + (blk % NB) * 2 * KBYTES;
+        if (off32 && kb + KV_BLOCK <= p.S) {
+            const char *kblk = kbase + (int64_t)kb * kstr;
+            const char *vblk = vbase + (int64_t)kb * vstr;
 #pragma unroll
-        for (int j = 0; j < QW; ++j) {
-            const int q = wave + W * j;
-            const int qq = q & 15;
-            const int row = 4 * qq + lrow;
-            const int key = min(kb + row, p.S - 1);
-            if (q < 16) {
-                const int ch = lslot ^ (row & 15);
-                __builtin_amdgcn_global_load_lds(static_cast<const void *>(kbase + key * kstr + ch * 16),
-                                                 BI_LDS_PTR(buf + qq * 1024), 16, 0, 0);
-            } else {
-                const int ch = lslot ^ ((row & 7) << 1);
-                __builtin_amdgcn_global_load_lds(static_cast<const void *>(vbase + key * vstr + ch * 16),
-                                                 BI_LDS_PTR(buf + KBYTES + qq * 1024), 16, 0, 0);
+            for (int j = 0; j < QW; ++j)
+                __builtin_amdgcn_global_load_lds(static_cast<const void *>((j < QK ? kblk : vblk) + loff[j]),
+                                                 BI_LDS_PTR(buf + (j < QK ? 0 : KBYTES) + ((wave + W * j) & 15) * 1024),
+                                                 16, 0, 0);
+        } else {
+#pragma unroll
+            for (int j = 0; j < QW; ++j) {
+                const int row = lrowj[j];
+                const int64_t key = min(kb + row, p.S - 1);
+                const char *src = j < QK ? kbase + key * kstr + ((lslot ^ (row & 15)) << 4)
+                                         : vbase + key * vstr + ((lslot ^ ((row & 7) << 1)) << 4);
+                __builtin_amdgcn_global_load_lds(static_cast<const void *>(src),
+                                                 BI_LDS_PTR(buf + (j < QK ? 0 : KBYTES) + ((wave + W * j) & 15) * 1024),
+                                                 16, 0, 0);
             }
         }
     };
@@ -754,8 +807,8 @@ __global__ __launch_bounds__(64 * W) void sdpa_prefill16(SdpaParams p) {
             const float a_i = __shfl(a, src), b_i = __shfl(bs, src);
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
-                if (first_i) ot[t][i] = o[t][i];
-                else if (!skip_i) ot[t][i] = __builtin_fmaf(ot[t][i], a_i, o[t][i] * b_i);
+                const float f = __builtin_fmaf(ot[t][i], a_i, o[t][i] * b_i);
+                ot[t][i] = first_i ? o[t][i] : skip_i ? ot[t][i] : f;
             }
         }
         have = have || !skip;
