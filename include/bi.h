@@ -227,9 +227,9 @@ bi_status bi_rowsum(const void *x, int64_t ldx, void *y, int64_t M, int64_t N, i
  * Returns "none" for empty or oversized shapes. */
 const char *bi_gemm_kernel_name(int64_t M, int64_t N, int64_t K, bi_dtype in_dt, int b_kn);
 
-/* Which attention kernels a bi_sdpa call of these sizes runs: "sdpa_fused16"
- * (16-bit, D = 128, S <= 1024), "sdpa_prefill16" (16-bit, D = 128, S > 1024,
- * Lq >= 384), "sdpa_split16+combine" (other 16-bit D = 128 calls) or
+/* Which attention kernels a bi_sdpa call of these sizes runs: "sdpa_prefill16"
+ * (16-bit, D = 128, Lq >= 384), "sdpa_fused16" (16-bit, D = 128, Lq < 384,
+ * S <= 1024), "sdpa_split16+combine" (other 16-bit D = 128 calls) or
  * "sdpa_split+combine" (fp32, D = 64).  Informational: the split / block
  * structure, and with it every output bit, is the same whichever runs.
  * Returns "none" for empty, oversized or unsupported sizes. */

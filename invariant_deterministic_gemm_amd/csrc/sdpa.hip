@@ -66,6 +66,26 @@ __device__ __forceinline__ f32x4 attn_mfma_chunk(u32x4 a, u32x4 b, f32x4 c) {
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// x op x[lane ^ 16] and x op x[lane ^ 32] for a commutative op, through the VALU lane swaps (no
+// LDS round trip): a swap of x with itself leaves one lane of each pair holding both values, the
+// other lane the same two in the other order, which a commutative op does not see.
+__device__ __forceinline__ float max_xor16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float add_xor16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float add_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Work item of a one-dimensional grid of `ntile` query-row tiles times
 // `ngroup` (split, batch, KV head) groups.  Workgroups are dealt to the eight
 // XCDs in turn, so when the grid size is a multiple of 8 the ids are permuted
@@ -185,8 +205,7 @@ __global__ __launch_bounds__(64) void sdpa_split(SdpaParams p) {
                 s[kt][i] = ok ? sv : NEG_INF;
                 mb = fmaxf(mb, s[kt][i]);
             }
-        mb = fmaxf(mb, __shfl_xor(mb, 16));
-        mb = fmaxf(mb, __shfl_xor(mb, 32));
+        mb = max_xor32(max_xor16(mb));
         const bool empty = mb == NEG_INF;
         const float m_new = empty ? m_run : fmaxf(m_run, mb);
         const float alpha = empty ? 1.0f : exp2_hw(m_run - m_new);
@@ -199,8 +218,7 @@ __global__ __launch_bounds__(64) void sdpa_split(SdpaParams p) {
                 pr[kt][i] = s[kt][i] == NEG_INF ? 0.0f : exp2_hw(s[kt][i] - m_new);
                 rs = rs + pr[kt][i];
             }
-        rs = rs + __shfl_xor(rs, 16);
-        rs = rs + __shfl_xor(rs, 32);
+        rs = add_xor32(add_xor16(rs));
         l_run = __builtin_fmaf(l_run, alpha, rs);
         m_run = m_new;
         // ---- rescale O: lane holds O rows 4 g + i
@@ -396,8 +414,7 @@ __device__ __forceinline__ void attn_update16(const SdpaParams &p, const Rows16 
             }
         mb = lane_max();
     }
-    mb = fmaxf(mb, __shfl_xor(mb, 16));
-    mb = fmaxf(mb, __shfl_xor(mb, 32));
+    mb = max_xor32(max_xor16(mb));
     const bool empty = mb == NEG_INF;
     const float m_new = empty ? m_run : fmaxf(m_run, mb);
     const float alpha = empty ? 1.0f : exp2_hw(m_run - m_new);
@@ -413,8 +430,7 @@ __device__ __forceinline__ void attn_update16(const SdpaParams &p, const Rows16 
             pr[kt][i] = exp2_hw(s[kt][i] - mref);
             rs = rs + pr[kt][i];
         }
-    rs = rs + __shfl_xor(rs, 16);
-    rs = rs + __shfl_xor(rs, 32);
+    rs = add_xor32(add_xor16(rs));
     l_run = __builtin_fmaf(l_run, alpha, rs);
     m_run = m_new;
     // O * 1 = O: the rescale is skipped when no row's maximum moved
@@ -922,8 +938,8 @@ constexpr int64_t PREFILL_MIN_LQ = 384;
 
 SdpaPath sdpa_path(int64_t Lq, int64_t S, int64_t D, int dt) {
     if (dt == DT_F32 || D != 128 || S <= 0) return SDPA_SPLIT;
-    if ((S + KV_SPLIT - 1) / KV_SPLIT <= FUSED_MAXW) return SDPA_FUSED16;
     if (Lq >= PREFILL_MIN_LQ) return SDPA_PREFILL16;
+    if ((S + KV_SPLIT - 1) / KV_SPLIT <= FUSED_MAXW) return SDPA_FUSED16;
     return SDPA_SPLIT;
 }
 

@@ -179,7 +179,8 @@ def test_kernel_name_queries(lib):
     assert lib.bi_sdpa_kernel_name(1, 32, 64, 1025, 128, F16).decode() == "sdpa_split16+combine"
     assert lib.bi_sdpa_kernel_name(1, 32, 384, 1025, 128, F16).decode() == "sdpa_prefill16"
     assert lib.bi_sdpa_kernel_name(1, 32, 383, 1025, 128, F16).decode() == "sdpa_split16+combine"
-    assert lib.bi_sdpa_kernel_name(1, 32, 384, 1024, 128, BF16).decode() == "sdpa_fused16"
+    assert lib.bi_sdpa_kernel_name(1, 32, 384, 1024, 128, BF16).decode() == "sdpa_prefill16"
+    assert lib.bi_sdpa_kernel_name(1, 32, 383, 1024, 128, BF16).decode() == "sdpa_fused16"
     assert lib.bi_sdpa_kernel_name(1, 32, 1, 300, 128, F32).decode() == "sdpa_split+combine"
     assert lib.bi_sdpa_kernel_name(1, 32, 1, 300, 64, BF16).decode() == "sdpa_split+combine"
     for bad in ((0, 32, 1, 10, 128, BF16), (1, 32, 1, 0, 128, BF16), (1, 32, 1, 10, 96, BF16),

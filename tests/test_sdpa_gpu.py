@@ -263,17 +263,18 @@ def test_readme_style_call():
 
 @pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16], ids=_ids)
 def test_prefill_path_matches_split_path_and_decode(dt):
-    """Query chunks of >= 384 rows against caches of more than 1024 keys run the workspace-free
-    prefill kernel; chunks of 383 run the split + combine kernels.  The tokens two such chunks share
-    must have the same bits, and sampled tokens must equal their own decode call."""
+    """Query chunks of >= 384 rows run the workspace-free prefill kernel; chunks of 383 run the split +
+    combine kernels (more than 1024 keys) or the fused kernel (up to 1024 keys).  The tokens two such
+    chunks share must have the same bits, and sampled tokens must equal their own decode call."""
     lib = bi._native.load()
     BI = bi.BI_BF16 if dt == torch.bfloat16 else bi.BI_F16
-    for (B, Hq, Hkv, S) in [(2, 32, 8, 2085), (1, 16, 8, 1500), (1, 8, 8, 1100)]:
+    for (B, Hq, Hkv, S) in [(2, 32, 8, 2085), (1, 16, 8, 1500), (1, 8, 8, 1100), (1, 32, 8, 1000), (2, 8, 8, 700)]:
         q = synthetic.randn((B, Hq, 500, 128), 0x5EED50 + S, 1.0, dt).to(DEV)
         k = synthetic.randn((B, Hkv, S, 128), 0x5EED51 + S, 1.0, dt).to(DEV)
         v = synthetic.randn((B, Hkv, S, 128), 0x5EED52 + S, 1.0, dt).to(DEV)
         assert lib.bi_sdpa_kernel_name(B, Hq, 384, S, 128, BI).decode() == "sdpa_prefill16"
-        assert lib.bi_sdpa_kernel_name(B, Hq, 383, S, 128, BI).decode() == "sdpa_split16+combine"
+        assert lib.bi_sdpa_kernel_name(B, Hq, 383, S, 128, BI).decode() == (
+            "sdpa_fused16" if S <= 1024 else "sdpa_split16+combine")
         split = bi.bi_sdpa(q[:, :, -383:], k, v, causal=True)
         for L in (384, 390, 500):
             pre = bi.bi_sdpa(q[:, :, -L:], k, v, causal=True)
