@@ -8,7 +8,9 @@ The definitions follow the mlx-batch-invariant README:
   * section "Use" -- linear(x, w, bias) with w in (N, K), matmul(a, b) with
     b in (K, N), addmm(c, a, b, alpha, beta) and
     scaled_dot_product_attention(q, k, v, mask="causal");
-  * section "Accuracy" -- results are judged against a float64 reference.
+  * section "Accuracy" -- results are judged against a float64 reference;
+  * section "Quantized models" -- 2, 4 and 8-bit group-wise affine weights
+    (dequantize, quantized_linear).
 Inputs may be torch tensors (any dtype, any device-less CPU tensor) or numpy
 arrays; they are converted exactly to float64 before the C code sees them.
 Outputs are unrounded float64 numpy arrays.
@@ -67,6 +69,8 @@ def _bind(lib):
     lib.oracle_sdpa_f64.restype = None
     lib.oracle_rowsum_f64.argtypes = [p, i64, i64, i64, ctypes.c_int, p]
     lib.oracle_rowsum_f64.restype = None
+    lib.oracle_dequant_f64.argtypes = [p, i64, p, p, i64, ctypes.c_int, i64, i64, i64, p]
+    lib.oracle_dequant_f64.restype = None
     lib.oracle_threads.restype = ctypes.c_int
     lib.oracle_set_threads.argtypes = [ctypes.c_int]
     return lib
@@ -202,3 +206,44 @@ def rowsum(x, mean: bool = False) -> np.ndarray:
         with np.errstate(invalid="ignore"):
             _load().oracle_rowsum_f64(_ptr(X2), N, X2.shape[0], N, 1 if mean else 0, _ptr(out))
     return out.reshape(lead)
+
+
+def _u32(w) -> np.ndarray:
+    """Packed weight words as C-contiguous uint32 (torch int32 / uint32 or numpy), bits unchanged."""
+    if hasattr(w, "detach"):
+        import torch
+        w = w.detach().to("cpu")
+        if w.dtype == torch.int32:
+            w = w.numpy().view(np.uint32)
+        else:
+            w = w.numpy()
+    return np.ascontiguousarray(np.asarray(w).astype(np.uint32, copy=False))
+
+
+def dequantize(wq, scales, biases, bits: int, group_size: int, K: int | None = None) -> np.ndarray:
+    """(N, K) float64 weights from group-wise affine quantisation (README, section "Quantized models"):
+    w[n, k] = scale[n, k // group_size] * q[n, k] + bias[n, k // group_size], q the bits-wide field
+    k mod (32 / bits) of word k // (32 / bits) of row n, lowest bits first.  Exact in float64."""
+    if bits not in (2, 4, 8):
+        raise ValueError("bits must be 2, 4 or 8")
+    W = _u32(wq)
+    Sc, Bi = _f64(scales), _f64(biases)
+    N = W.shape[0]
+    if K is None:
+        K = W.shape[1] * (32 // bits)
+    if Sc.shape != Bi.shape or Sc.shape[0] != N or Sc.shape[1] * group_size < K:
+        raise ValueError("scales / biases must be (N, >= K / group_size)")
+    out = np.empty((N, K), dtype=np.float64)
+    if N and K:
+        _load().oracle_dequant_f64(_ptr(W), W.shape[1], _ptr(Sc), _ptr(Bi), Sc.shape[1], int(bits),
+                                   int(group_size), N, K, _ptr(out))
+    return out
+
+
+def quantized_linear(x, wq, scales, biases, bits: int, group_size: int, bias=None) -> np.ndarray:
+    """y = x @ dequantize(w).T + bias in float64 (README, section "Quantized models": the quantized
+    layer is a linear layer on the dequantised weight)."""
+    X = _f64(x)
+    Wd = dequantize(wq, scales, biases, bits, group_size, X.shape[1])
+    return gemm(X, Wd, True, bias, 1.0, 1.0)
+

@@ -24,7 +24,8 @@
  *   - section "Why MLX is not invariant", attention bullets: the query
  *     length is q.shape[2] and the grouped-query factor is H / Hkv;
  *   - section "Accuracy": the float64 reference that accuracy is judged
- *     against.
+ *     against;
+ *   - section "Quantized models": 2, 4 and 8-bit group-wise affine weights.
  * Readings where the page is silent (all documented with the library):
  *   causal alignment is bottom-right (query i sits at key position
  *   S - Lq + i); query head h reads KV head floor(h * Hkv / Hq); a boolean
@@ -192,5 +193,34 @@ void oracle_rowsum_f64(const double *x, int64_t ldx, int64_t M, int64_t N, int m
         double s = 0.0;
         for (int64_t n = 0; n < N; ++n) s = s + row[n];
         out[m] = mean ? s / (double)N : s;
+    }
+}
+
+/*
+ * Group-wise affine dequantisation (README, section "Quantized models": 2, 4
+ * and 8-bit affine weights, one scale and one bias per group of k values).
+ * The packing follows the layout the page's quantized checkpoints use: along
+ * k, consecutive values share a 32-bit word, 32 / bits of them per word,
+ * value j of a word in bits [j * bits, (j + 1) * bits).
+ *
+ *   q[n, k] = (wq[n * ldwq + k / per] >> ((k mod per) * bits)) & (2^bits - 1),
+ *             per = 32 / bits
+ *   w[n, k] = scales[n * ldsb + k / gs] * q[n, k] + biases[n * ldsb + k / gs]
+ *
+ * evaluated exactly in double (the scale and bias are bf16 / fp16 values and
+ * q < 256, so the product and the sum are exact); out[n * K + k] = w[n, k].
+ */
+void oracle_dequant_f64(const uint32_t *wq, int64_t ldwq, const double *scales, const double *biases, int64_t ldsb,
+                        int bits, int64_t gs, int64_t N, int64_t K, double *out) {
+    const int64_t per = 32 / bits;
+    const uint32_t fieldmask = (bits == 32) ? 0xffffffffu : ((1u << bits) - 1u);
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t k = 0; k < K; k++) {
+            const uint32_t word = wq[n * ldwq + k / per];
+            const uint32_t q = (word >> ((k % per) * bits)) & fieldmask;
+            const int64_t grp = k / gs;
+            out[n * K + k] = scales[n * ldsb + grp] * (double)q + biases[n * ldsb + grp];
+        }
     }
 }

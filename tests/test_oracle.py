@@ -304,7 +304,72 @@ def pin_rowsum_exact():
 ROWSUM_PINS = [pin_rowsum_exact]
 
 
-@pytest.mark.parametrize("pin", GEMM_PINS + SDPA_PINS + ROWSUM_PINS, ids=lambda f: f.__name__)
+# ------------------------------------------------------------ quantized weights
+def _pack(q, bits):
+    """Pack integer fields (N, K) into uint32 words, 32 / bits per word, lowest bits first (plain
+    Python integers: an independent inverse of the oracle's unpacking)."""
+    per = 32 // bits
+    N, K = q.shape
+    words = np.zeros((N, K // per), dtype=np.uint32)
+    for n in range(N):
+        for w in range(K // per):
+            v = 0
+            for j in range(per):
+                v |= int(q[n, w * per + j]) << (j * bits)
+            words[n, w] = v
+    return words
+
+
+def pin_dequant_golden():
+    with open(GOLDEN) as f:
+        cases = json.load(f)["quantized"]
+    for c in cases:
+        got = oracle.dequantize(np.array(c["words"], dtype=np.uint32), np.array(c["scales"], float),
+                                np.array(c["biases"], float), c["bits"], c["group_size"], c["K"])
+        assert np.array_equal(got, np.array(c["expected"], float)), c["name"]
+
+
+def pin_dequant_roundtrip():
+    rng = np.random.default_rng(7)
+    for bits in (2, 4, 8):
+        for gs in (32, 64, 128):
+            N, K = 3, 256
+            q = rng.integers(0, 1 << bits, size=(N, K))
+            words = _pack(q, bits)
+            ones, zeros = np.ones((N, K // gs)), np.zeros((N, K // gs))
+            # scale 1, bias 0: the fields come back unchanged
+            assert np.array_equal(oracle.dequantize(words, ones, zeros, bits, gs), q.astype(float))
+            # every field 1: w = scale + bias of the field's own group
+            words1 = _pack(np.ones((N, K), dtype=np.int64), bits)
+            sc = rng.integers(1, 9, size=(N, K // gs)) / 4.0
+            bi = rng.integers(-9, 9, size=(N, K // gs)) / 2.0
+            want = np.repeat(sc + bi, gs, axis=1)
+            assert np.array_equal(oracle.dequantize(words1, sc, bi, bits, gs), want)
+            # largest field: w = (2^bits - 1) * scale + bias
+            wordsmax = _pack(np.full((N, K), (1 << bits) - 1), bits)
+            want = np.repeat(((1 << bits) - 1) * sc + bi, gs, axis=1)
+            assert np.array_equal(oracle.dequantize(wordsmax, sc, bi, bits, gs), want)
+
+
+def pin_qlinear_integer_exact():
+    rng = np.random.default_rng(8)
+    for bits, gs in ((4, 64), (8, 32), (2, 128)):
+        M, N, K = 5, 7, 256
+        q = rng.integers(0, 1 << bits, size=(N, K))
+        sc = rng.integers(1, 4, size=(N, K // gs)).astype(float)
+        bi = rng.integers(-5, 5, size=(N, K // gs)).astype(float)
+        x = rng.integers(-6, 7, size=(M, K))
+        bias = rng.integers(-9, 9, size=N)
+        w_int = q * np.repeat(sc.astype(np.int64), gs, axis=1) + np.repeat(bi.astype(np.int64), gs, axis=1)
+        want = (x @ w_int.T + bias).astype(float)          # int64 arithmetic: exact
+        got = oracle.quantized_linear(x.astype(float), _pack(q, bits), sc, bi, bits, gs, bias.astype(float))
+        assert np.array_equal(got, want)
+
+
+QUANT_PINS = [pin_dequant_golden, pin_dequant_roundtrip, pin_qlinear_integer_exact]
+
+
+@pytest.mark.parametrize("pin", GEMM_PINS + SDPA_PINS + ROWSUM_PINS + QUANT_PINS, ids=lambda f: f.__name__)
 def test_oracle_pin(pin):
     pin()
 
@@ -332,12 +397,19 @@ MUTANTS = {
                             "for (int64_t n = 0; n + 1 < N; ++n) s = s + row[n];", ROWSUM_PINS),
     "rowsum_mean_undivided": ("out[m] = mean ? s / (double)N : s;", "out[m] = s;", ROWSUM_PINS),
     "rowsum_row_pitch": ("const double *row = x + m * ldx;", "const double *row = x + m;", ROWSUM_PINS),
+    "dequant_bit_order": ("(word >> ((k % per) * bits))", "(word >> ((per - 1 - k % per) * bits))", QUANT_PINS),
+    "dequant_group_off_by_one": ("const int64_t grp = k / gs;", "const int64_t grp = (k + 1) / gs % (K / gs);",
+                                 QUANT_PINS),
+    "dequant_scale_bias_swapped": ("scales[n * ldsb + grp] * (double)q + biases[n * ldsb + grp]",
+                                   "biases[n * ldsb + grp] * (double)q + scales[n * ldsb + grp]", QUANT_PINS),
+    "dequant_word_index": ("const uint32_t word = wq[n * ldwq + k / per];",
+                           "const uint32_t word = wq[n * ldwq + k / bits % ldwq];", QUANT_PINS),
 }
 
 
 def _run_pins_with(lib_path: str, group: str) -> list:
     """Run one pin group against another build of oracle.c; return the pins that failed."""
-    pins = {"gemm": GEMM_PINS, "sdpa": SDPA_PINS, "rowsum": ROWSUM_PINS}[group]
+    pins = {"gemm": GEMM_PINS, "sdpa": SDPA_PINS, "rowsum": ROWSUM_PINS, "quant": QUANT_PINS}[group]
     failed = []
     with oracle.use_library(lib_path):
         for pin in pins:
@@ -351,7 +423,7 @@ def _run_pins_with(lib_path: str, group: str) -> list:
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_pins_catch_planted_mistake(name, tmp_path):
     old, new, pins = MUTANTS[name]
-    group = "gemm" if pins is GEMM_PINS else ("sdpa" if pins is SDPA_PINS else "rowsum")
+    group = {id(GEMM_PINS): "gemm", id(SDPA_PINS): "sdpa", id(ROWSUM_PINS): "rowsum", id(QUANT_PINS): "quant"}[id(pins)]
     root = os.path.dirname(HERE)
     src = open(os.path.join(root, "oracle", "oracle.c")).read()
     assert src.count(old) == 1, f"mutation anchor not unique in oracle.c: {old!r}"
