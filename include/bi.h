@@ -221,6 +221,39 @@ int bi_variant_splits(int64_t M);
 bi_status bi_rowsum(const void *x, int64_t ldx, void *y, int64_t M, int64_t N, int mean, bi_dtype dt,
                     void *stream);
 
+/*
+ * Quantized linear (README, section "Quantized models": 2, 4 and 8-bit
+ * group-wise affine weights, unpacked inside the K loop of the invariant
+ * kernel, with no narrower kernel for small batches).
+ *
+ *   y (M,N) = x (M,K) . W^T + bias,   W[n, k] = round_dt(fmaf(s, q[n, k], b))
+ *
+ * with s = scales[n, k / group_size], b = biases[n, k / group_size] (fp32
+ * fma of the two 16-bit values and the integer field, one rounding to dt) and
+ * q[n, k] the bits-wide field k mod (32 / bits) of word k / (32 / bits) of
+ * row n of wq, lowest bits first.  The MFMA chain and the epilogue are those
+ * of bi_linear, so y equals bi_linear(x, W, bias) bit for bit, and row m of y
+ * does not depend on M or on the other rows.
+ *
+ * x: M rows of K elements of dt at x + m * ldx (16-byte aligned, ldx >= K and
+ * a multiple of 8).  wq: N rows of ldwq uint32 words (ldwq >= K * bits / 32;
+ * 8-byte aligned with ldwq even when bits == 8).  scales, biases: N rows of
+ * ldsb elements of dt (ldsb >= K / group_size).  bias: N elements of dt or
+ * NULL.  y: M rows of N elements of dt at y + m * ldy (ldy >= N).
+ * dt: BI_BF16 or BI_F16.  bits: 2, 4 or 8 (3, 5 and 6-bit packings and
+ * anything else are refused with BI_ERR_UNSUPPORTED).  group_size: 32, 64 or
+ * 128, and K a multiple of it.  All device memory; enqueued on `stream`.
+ * M == 0 or N == 0 enqueues nothing; K == 0 writes the bias (or zeros).
+ */
+bi_status bi_quantized_linear(const void *x, int64_t ldx,
+                              const uint32_t *wq, int64_t ldwq,
+                              const void *scales, const void *biases, int64_t ldsb,
+                              int bits, int64_t group_size,
+                              const void *bias,
+                              void *y, int64_t ldy,
+                              int64_t M, int64_t N, int64_t K,
+                              bi_dtype dt, void *stream);
+
 /* Which kernel configuration a GEMM of this shape runs on ("gemm_skinny_nk/fm1",
  * "gemm_tiled_kn/128x128", ...; b_kn != 0 for a row-major (K, N) operand of
  * bi_matmul / bi_addmm, 0 for bi_linear and for column-major operands).  Informational: every configuration computes the same bits.

@@ -26,6 +26,7 @@ from . import _native
 from ._native import BI_BF16, BI_F16, BI_F32
 
 __all__ = ["bi_linear", "bi_matmul", "bi_addmm", "bi_sdpa", "bi_rowsum", "bi_variant_linear",
+           "bi_quantized_linear", "quantize",
            "linear", "matmul", "addmm", "scaled_dot_product_attention",
            "abi_version", "library_path", "BiError"]
 
@@ -315,6 +316,64 @@ def bi_variant_linear(x: torch.Tensor, w: torch.Tensor, bias: torch.Tensor | Non
 linear = bi_linear
 matmul = bi_matmul
 addmm = bi_addmm
+
+
+def quantize(w: torch.Tensor, bits: int = 4, group_size: int = 64):
+    """Group-wise affine quantisation of an (N, K) weight (offline weight preparation in plain torch, not
+    part of the kernel path): per group of group_size values along K, scale = (max - min) / (2^bits - 1)
+    and bias = min, both rounded to w's dtype; q = round((w - bias) / scale) clamped to [0, 2^bits - 1].
+    Returns (wq, scales, biases): wq is (N, K * bits / 32) int32 holding the packed uint32 words (32 / bits
+    fields per word, lowest bits first), scales / biases are (N, K / group_size) in w's dtype."""
+    if bits not in (2, 4, 8):
+        raise ValueError("bits must be 2, 4 or 8")
+    N, K = w.shape
+    if K % group_size or K % 32:
+        raise ValueError("K must be a multiple of group_size and of 32")
+    g = w.float().reshape(N, K // group_size, group_size)
+    lo, hi = g.amin(dim=-1), g.amax(dim=-1)
+    levels = (1 << bits) - 1
+    scale = ((hi - lo) / levels).clamp_min(1e-8).to(w.dtype)
+    bias = lo.to(w.dtype)
+    q = torch.round((g - bias.float()[..., None]) / scale.float()[..., None]).clamp_(0, levels).to(torch.int64)
+    per = 32 // bits
+    q = q.reshape(N, K // per, per)
+    shifts = torch.arange(per, device=w.device, dtype=torch.int64) * bits
+    words = (q << shifts).sum(dim=-1)                            # < 2^32
+    words = torch.where(words >= 2**31, words - 2**32, words).to(torch.int32)
+    return words.contiguous(), scale.contiguous(), bias.contiguous()
+
+
+def bi_quantized_linear(x: torch.Tensor, wq: torch.Tensor, scales: torch.Tensor, biases: torch.Tensor,
+                        bits: int, group_size: int, bias: torch.Tensor | None = None) -> torch.Tensor:
+    """y = x W^T + bias with W the group-wise affine dequantisation of wq (see `quantize` and bi.h):
+    equal bit for bit to bi_linear(x, W, bias) with W[n, k] = round(fmaf(scale, q, bias_group))."""
+    dev = _on_gpu(x, wq, scales, biases, bias)
+    if x.dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError("x must be bf16 or fp16")
+    if scales.dtype != x.dtype or biases.dtype != x.dtype:
+        raise ValueError("scales / biases must share x's dtype")
+    if wq.dtype not in (torch.int32, getattr(torch, "uint32", torch.int32)):
+        raise ValueError("wq must hold 32-bit words (int32 or uint32)")
+    lead = x.shape[:-1]
+    x2 = _aligned_ld(_rows(x))
+    M, K = x2.shape
+    N = wq.shape[0]
+    w2 = wq.contiguous()
+    s2, b2 = scales.contiguous(), biases.contiguous()
+    if s2.shape != b2.shape or s2.shape[0] != N:
+        raise ValueError("scales / biases must be (N, K / group_size)")
+    bb = None
+    if bias is not None:
+        if bias.shape != (N,) or bias.dtype != x.dtype:
+            raise ValueError("bias must be (N,) in x's dtype")
+        bb = bias.contiguous()
+    y = torch.empty((M, N), dtype=x.dtype, device=dev)
+    lib = _native.load()
+    st = lib.bi_quantized_linear(_ptr(x2), _ld(x2), _ptr(w2), w2.shape[1], _ptr(s2), _ptr(b2), s2.shape[1],
+                                 int(bits), int(group_size), _ptr(bb), _ptr(y), max(N, 1), M, N, K,
+                                 _dt(x2, "bi_quantized_linear"), _stream(dev))
+    _check(st, "bi_quantized_linear")
+    return y.reshape(*lead, N)
 
 
 def scaled_dot_product_attention(q, k, v, mask=None, scale=None):

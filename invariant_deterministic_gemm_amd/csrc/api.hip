@@ -19,6 +19,7 @@
 #include "device.h"
 #include "gemm.h"
 #include "rowsum.h"
+#include "qgemm.h"
 #include "sdpa.h"
 
 namespace {
@@ -320,6 +321,55 @@ bi_status bi_rowsum(const void *x, int64_t ldx, void *y, int64_t M, int64_t N, i
     if (M > 1 && ldx < N) return fail(BI_ERR_INVALID, "%s: ldx=%lld < N=%lld", fn, (long long)ldx, (long long)N);
     return device_status(bi::launch_rowsum(x, M > 1 ? ldx : N, y, M, N, mean ? 1 : 0, (int)dt, (hipStream_t)stream),
                          fn);
+}
+
+bi_status bi_quantized_linear(const void *x, int64_t ldx, const uint32_t *wq, int64_t ldwq, const void *scales,
+                              const void *biases, int64_t ldsb, int bits, int64_t group_size, const void *bias,
+                              void *y, int64_t ldy, int64_t M, int64_t N, int64_t K, bi_dtype dt, void *stream) {
+    const char *fn = "bi_quantized_linear";
+    if (!dtype_known(dt)) return fail(BI_ERR_INVALID, "%s: unknown dtype code %d", fn, (int)dt);
+    if (dt != BI_BF16 && dt != BI_F16) return fail(BI_ERR_UNSUPPORTED, "%s: dtype must be bf16 or fp16", fn);
+    if (bits != 2 && bits != 4 && bits != 8)
+        return fail(BI_ERR_UNSUPPORTED, "%s: %d-bit weights are not supported (2, 4 or 8)", fn, bits);
+    if (group_size != 32 && group_size != 64 && group_size != 128)
+        return fail(BI_ERR_UNSUPPORTED, "%s: group_size %lld is not supported (32, 64 or 128)", fn,
+                    (long long)group_size);
+    if (M < 0 || N < 0 || K < 0) return fail(BI_ERR_INVALID, "%s: negative size", fn);
+    if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return fail(BI_ERR_UNSUPPORTED, "%s: sizes must be below 2^31", fn);
+    if (K % group_size != 0)
+        return fail(BI_ERR_INVALID, "%s: K=%lld is not a multiple of group_size %lld", fn, (long long)K,
+                    (long long)group_size);
+    if (M == 0 || N == 0) return ok();
+    if (y == nullptr) return fail(BI_ERR_INVALID, "%s: output pointer is null", fn);
+    if (K > 0 && (x == nullptr || wq == nullptr || scales == nullptr || biases == nullptr))
+        return fail(BI_ERR_INVALID, "%s: input pointer is null", fn);
+    if (ldy < N) return fail(BI_ERR_INVALID, "%s: ldy=%lld < N=%lld", fn, (long long)ldy, (long long)N);
+    if (K > 0) {
+        if (ldx < K) return fail(BI_ERR_INVALID, "%s: ldx=%lld < K=%lld", fn, (long long)ldx, (long long)K);
+        if (ldwq < K * bits / 32)
+            return fail(BI_ERR_INVALID, "%s: ldwq=%lld < K*bits/32=%lld", fn, (long long)ldwq, (long long)(K * bits / 32));
+        if (ldsb < K / group_size)
+            return fail(BI_ERR_INVALID, "%s: ldsb=%lld < K/group_size=%lld", fn, (long long)ldsb,
+                        (long long)(K / group_size));
+        if (!aligned16(x) || ldx % 8 != 0)
+            return fail(BI_ERR_UNSUPPORTED, "%s: x must be 16-byte aligned with ldx a multiple of 8", fn);
+        if (!aligned_to(wq, bits == 8 ? 8 : 4) || (bits == 8 && ldwq % 2 != 0))
+            return fail(BI_ERR_UNSUPPORTED, "%s: wq must be 4-byte aligned (8-byte, ldwq even, for 8 bits)", fn);
+        if (!aligned_to(scales, 2) || !aligned_to(biases, 2))
+            return fail(BI_ERR_UNSUPPORTED, "%s: scales / biases misaligned", fn);
+    }
+    if (bias != nullptr && !aligned_to(bias, 2)) return fail(BI_ERR_UNSUPPORTED, "%s: bias pointer misaligned", fn);
+    if (!aligned_to(y, 2)) return fail(BI_ERR_UNSUPPORTED, "%s: output pointer misaligned", fn);
+    bi::QGemmParams q{};
+    q.g = make_params(x, ldx, nullptr, 0, bias, 0, y, ldy, M, N, K, 1.0f, 1.0f);
+    q.wq = wq;
+    q.ldwq = ldwq;
+    q.scales = scales;
+    q.biases = biases;
+    q.ldsb = ldsb;
+    q.bits = bits;
+    q.group_size = (int)group_size;
+    return device_status(bi::launch_qgemm(q, (int)dt, (hipStream_t)stream), fn);
 }
 
 const char *bi_gemm_kernel_name(int64_t M, int64_t N, int64_t K, bi_dtype in_dt, int b_kn) {

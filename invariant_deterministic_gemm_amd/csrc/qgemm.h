@@ -1,0 +1,28 @@
+// Host-visible launch interface of the quantized linear kernel (internal to libbi).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gemm.h"
+
+namespace bi {
+
+struct QGemmParams {
+    GemmParams g;           // A = x (M, K), C = bias row (ldc 0) or null, Y = y; alpha = beta = 1
+    const uint32_t *wq;     // (N, K * bits / 32) packed words, rows of ldwq words
+    int64_t ldwq;
+    const void *scales;     // (N, K / group_size) in the input dtype, rows of ldsb elements
+    const void *biases;     // same layout as scales
+    int64_t ldsb;
+    int bits;               // 2, 4 or 8
+    int group_size;         // 32, 64 or 128
+    int group_shift;        // log2(group_size), set by the launcher
+};
+
+hipError_t launch_qgemm(const QGemmParams &p, int dt, hipStream_t stream);
+
+// Rows of x one workgroup takes (16, 32 or 64): an arithmetic-identical tile choice.
+int qgemm_tile_rows(int M);
+
+}  // namespace bi

@@ -198,3 +198,53 @@ def test_rowsum_validation(lib):
     assert lib.bi_rowsum(None, 64, P16b, 4, 64, 1, F32, None) == INVALID         # null input
     assert lib.bi_rowsum(P16, 64, None, 4, 64, 1, F32, None) == INVALID          # null output
     assert lib.bi_rowsum(None, 0, None, 0, 64, 0, F32, None) == OK               # nothing to do
+
+
+def qlinear(lib, M=4, N=32, K=128, bits=4, gs=64, dt=BF16, x=P16, wq=P16b, sc=P16, sb=P16b, ldx=None, ldwq=None,
+            ldsb=None, ldy=None, bias=None, y=P16):
+    return lib.bi_quantized_linear(x, K if ldx is None else ldx, wq, K * bits // 32 if ldwq is None else ldwq,
+                                   sc, sb, K // gs if ldsb is None else ldsb, bits, gs, bias, y,
+                                   N if ldy is None else ldy, M, N, K, dt, None)
+
+
+def test_quantized_linear_validation(lib):
+    for bits in (1, 3, 5, 6, 16):
+        assert qlinear(lib, bits=bits) == UNSUPPORTED, bits
+    assert "not supported" in lib.bi_last_error().decode()
+    for gs in (16, 48, 256):
+        assert qlinear(lib, gs=gs, K=768) == UNSUPPORTED, gs
+    assert qlinear(lib, dt=F32) == UNSUPPORTED
+    assert qlinear(lib, dt=9) == INVALID
+    assert qlinear(lib, K=96, gs=64) == INVALID                  # K not a multiple of the group size
+    assert qlinear(lib, M=-1) == INVALID
+    assert qlinear(lib, x=None) == INVALID
+    assert qlinear(lib, wq=None) == INVALID
+    assert qlinear(lib, sc=None) == INVALID
+    assert qlinear(lib, y=None) == INVALID
+    assert qlinear(lib, ldx=64) == INVALID                       # ldx < K
+    assert qlinear(lib, ldwq=8) == INVALID                       # < K * bits / 32 = 16
+    assert qlinear(lib, ldsb=1) == INVALID                       # < K / gs = 2
+    assert qlinear(lib, ldy=16) == INVALID                       # ldy < N
+    assert qlinear(lib, x=P_MIS) == UNSUPPORTED                  # x not 16-byte aligned
+    assert qlinear(lib, ldx=132) == UNSUPPORTED                  # ldx not a multiple of 8
+    assert qlinear(lib, bits=8, ldwq=33) == UNSUPPORTED          # 8-bit rows need an even word pitch
+    assert qlinear(lib, M=0) == OK and qlinear(lib, N=0) == OK   # nothing to do
+
+
+def test_quantize_helper_round_trip():
+    """The offline quantiser's packing and groups, read back by the oracle: every weight within half a
+    step of its group's grid, and the extreme values of each group exact up to the 16-bit scale."""
+    import numpy as np
+    import torch
+    import oracle
+    import invariant_deterministic_gemm_amd as bi
+    g = torch.Generator().manual_seed(5)
+    w = (torch.randn(24, 256, generator=g) * 0.02).to(torch.bfloat16)
+    for bits, gs in ((2, 32), (4, 64), (8, 128)):
+        wq, sc, sb = bi.quantize(w, bits, gs)
+        assert wq.shape == (24, 256 * bits // 32) and wq.dtype == torch.int32
+        assert sc.shape == (24, 256 // gs) and sc.dtype == torch.bfloat16
+        deq = oracle.dequantize(wq, sc, sb, bits, gs)
+        step = np.repeat(sc.double().numpy(), gs, axis=1)
+        err = np.abs(deq - w.double().numpy())
+        assert (err <= 0.5 * step + 2e-3 * np.abs(w.double().numpy()) + 1e-6).all(), (bits, gs, err.max())

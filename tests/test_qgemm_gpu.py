@@ -1,0 +1,85 @@
+"""GPU tests of the quantized linear (bi_quantized_linear), README section "Quantized models".
+
+* bitwise identity with bi_linear on the dequantised weight: the weight is dequantised on the host in
+  float64 (exact), rounded once to fp32 (what one fmaf gives) and once to the input dtype, and the
+  result of bi_linear on it must equal the quantized kernel bit for bit -- the same chain, only the
+  weight's storage differs;
+* oracle tolerance (bf16 / fp16 outputs: 2e-2) against the float64 oracle's quantized_linear;
+* invariance on raw bit patterns across batch size and batch neighbours;
+* shapes with ragged N, a partial last 128-k stage, every bit width and group size.
+"""
+import numpy as np
+import pytest
+import torch
+
+import invariant_deterministic_gemm_amd as bi
+import oracle
+import synthetic
+from helpers import assert_bits_equal, assert_close_to_oracle
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def make(N, K, bits, gs, dt, seed):
+    w = synthetic.randn((N, K), seed, 0.02, dt)
+    wq, sc, sb = bi.quantize(w, bits, gs)
+    return wq, sc, sb
+
+
+def host_dequant(wq, sc, sb, bits, gs, K, dt):
+    """The kernel's weight, built on the host: exact float64 value -> fp32 -> dt (each step RNE)."""
+    exact = oracle.dequantize(wq, sc, sb, bits, gs, K)
+    return torch.from_numpy(exact.astype(np.float32)).to(dt)
+
+
+CASES = [  # M, N, K, bits, gs
+    (1, 4096, 4096, 4, 64), (4, 300, 384, 4, 128), (7, 513, 256, 8, 32), (16, 257, 96, 2, 32),
+    (33, 1000, 1024, 4, 32), (64, 128, 640, 8, 128), (100, 96, 512, 2, 64), (200, 72, 4096, 4, 64),
+]
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16], ids=["bf16", "fp16"])
+@pytest.mark.parametrize("M,N,K,bits,gs", CASES)
+def test_equals_linear_on_dequantised_weight_and_oracle(M, N, K, bits, gs, dt):
+    seed = M * 7 + N * 13 + K + bits
+    wq, sc, sb = make(N, K, bits, gs, dt, seed)
+    x = synthetic.randn((M, K), seed + 1, 1.0, dt)
+    bias = synthetic.randn((N,), seed + 2, 1.0, dt)
+    wd = host_dequant(wq, sc, sb, bits, gs, K, dt)
+    y = bi.bi_quantized_linear(x.to(DEV), wq.to(DEV), sc.to(DEV), sb.to(DEV), bits, gs, bias.to(DEV))
+    ref = bi.bi_linear(x.to(DEV), wd.to(DEV), bias.to(DEV))
+    assert_bits_equal(y, ref, f"M={M} N={N} K={K} bits={bits} gs={gs}: quantized vs linear on dequantised W")
+    want = oracle.quantized_linear(x, wq, sc, sb, bits, gs, bias)
+    assert_close_to_oracle(y, want, f"M={M} N={N} K={K} bits={bits} gs={gs}")
+
+
+@pytest.mark.parametrize("bits,gs", [(4, 64), (8, 32), (2, 128)])
+def test_rows_do_not_depend_on_batch(bits, gs):
+    dt = torch.bfloat16
+    N, K, Mmax = 1536, 2048, 200
+    wq, sc, sb = (t.to(DEV) for t in make(N, K, bits, gs, dt, 99 + bits))
+    x = synthetic.randn((Mmax, K), 98, 1.0, dt).to(DEV)
+    full = bi.bi_quantized_linear(x, wq, sc, sb, bits, gs)
+    for M in (1, 2, 3, 15, 16, 17, 32, 33, 63, 64, 65, 129):
+        part = bi.bi_quantized_linear(x[:M], wq, sc, sb, bits, gs)
+        assert_bits_equal(part, full[:M], f"bits={bits} gs={gs} M={M} vs M={Mmax}")
+    # batch neighbours: the other rows replaced by NaN
+    noisy = x.clone()
+    noisy[1:] = float("nan")
+    one = bi.bi_quantized_linear(noisy[:40], wq, sc, sb, bits, gs)
+    assert_bits_equal(one[:1], full[:1], "row 0 with NaN neighbours")
+
+
+def test_zero_k_gives_bias_and_errors_raise():
+    dt = torch.bfloat16
+    bias = synthetic.randn((40,), 5, 1.0, dt).to(DEV)
+    x = torch.empty((3, 0), dtype=dt, device=DEV)
+    wq = torch.empty((40, 0), dtype=torch.int32, device=DEV)
+    sc = torch.empty((40, 0), dtype=dt, device=DEV)
+    y = bi.bi_quantized_linear(x, wq, sc, sc, 4, 64, bias)
+    assert_bits_equal(y, bias[None].expand(3, 40).contiguous(), "K = 0")
+    wq3, sc3, sb3 = (t.to(DEV) for t in make(16, 256, 4, 64, dt, 6))
+    with pytest.raises(NotImplementedError):                      # 3-bit packings are refused, never guessed
+        bi.bi_quantized_linear(torch.zeros((2, 256), dtype=dt, device=DEV), wq3, sc3, sb3, 3, 64)
