@@ -244,6 +244,12 @@ bi_status bi_rowsum(const void *x, int64_t ldx, void *y, int64_t M, int64_t N, i
  * anything else are refused with BI_ERR_UNSUPPORTED).  group_size: 32, 64 or
  * 128, and K a multiple of it.  All device memory; enqueued on `stream`.
  * M == 0 or N == 0 enqueues nothing; K == 0 writes the bias (or zeros).
+ * ws: bi_quantized_linear_workspace_bytes(M, N, K, dt) bytes of 256-byte
+ * aligned device memory, or NULL when that is 0 (M <= 64: the weights are
+ * unpacked inside the kernel's K loop).  Above 64 rows, chunks of at most 8192
+ * columns are dequantised into ws with the same arithmetic and bi_linear's
+ * kernels run on them; the result is the same bits either way.  Too small a
+ * workspace is refused with BI_ERR_WORKSPACE.
  */
 bi_status bi_quantized_linear(const void *x, int64_t ldx,
                               const uint32_t *wq, int64_t ldwq,
@@ -252,7 +258,8 @@ bi_status bi_quantized_linear(const void *x, int64_t ldx,
                               const void *bias,
                               void *y, int64_t ldy,
                               int64_t M, int64_t N, int64_t K,
-                              bi_dtype dt, void *stream);
+                              bi_dtype dt, void *ws, size_t ws_bytes, void *stream);
+size_t bi_quantized_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, bi_dtype dt);
 
 /* Which kernel configuration a GEMM of this shape runs on ("gemm_skinny_nk/fm1",
  * "gemm_tiled_kn/128x128", ...; b_kn != 0 for a row-major (K, N) operand of

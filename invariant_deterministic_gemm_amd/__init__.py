@@ -369,9 +369,12 @@ def bi_quantized_linear(x: torch.Tensor, wq: torch.Tensor, scales: torch.Tensor,
         bb = bias.contiguous()
     y = torch.empty((M, N), dtype=x.dtype, device=dev)
     lib = _native.load()
+    dt = _dt(x2, "bi_quantized_linear")
+    need = lib.bi_quantized_linear_workspace_bytes(M, N, K, dt)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev) if need > 0 else None
     st = lib.bi_quantized_linear(_ptr(x2), _ld(x2), _ptr(w2), w2.shape[1], _ptr(s2), _ptr(b2), s2.shape[1],
-                                 int(bits), int(group_size), _ptr(bb), _ptr(y), max(N, 1), M, N, K,
-                                 _dt(x2, "bi_quantized_linear"), _stream(dev))
+                                 int(bits), int(group_size), _ptr(bb), _ptr(y), max(N, 1), M, N, K, dt,
+                                 _ptr(ws), need, _stream(dev))
     _check(st, "bi_quantized_linear")
     return y.reshape(*lead, N)
 

@@ -30,7 +30,8 @@ SIGNATURES = {
     "bi_sdpa_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64, _i]),
     "bi_rowsum": (_i, [_p, _i64, _p, _i64, _i64, _i, _i, _p]),
     "bi_quantized_linear": (_i, [_p, _i64, _p, _i64, _p, _p, _i64, _i, _i64, _p, _p, _i64, _i64, _i64, _i64, _i,
-                                 _p]),
+                                 _p, _sz, _p]),
+    "bi_quantized_linear_workspace_bytes": (_sz, [_i64, _i64, _i64, _i]),
     "bi_variant_linear": (_i, [_p, _i64, _p, _i64, _p, _p, _i64, _i64, _i64, _i64, _i, _i, _i, _p, _sz, _p]),
     "bi_variant_workspace_bytes": (_sz, [_i64, _i64, _i]),
     "bi_variant_splits": (_i, [_i64]),

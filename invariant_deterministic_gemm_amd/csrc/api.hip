@@ -325,7 +325,8 @@ bi_status bi_rowsum(const void *x, int64_t ldx, void *y, int64_t M, int64_t N, i
 
 bi_status bi_quantized_linear(const void *x, int64_t ldx, const uint32_t *wq, int64_t ldwq, const void *scales,
                               const void *biases, int64_t ldsb, int bits, int64_t group_size, const void *bias,
-                              void *y, int64_t ldy, int64_t M, int64_t N, int64_t K, bi_dtype dt, void *stream) {
+                              void *y, int64_t ldy, int64_t M, int64_t N, int64_t K, bi_dtype dt, void *ws,
+                              size_t ws_bytes, void *stream) {
     const char *fn = "bi_quantized_linear";
     if (!dtype_known(dt)) return fail(BI_ERR_INVALID, "%s: unknown dtype code %d", fn, (int)dt);
     if (dt != BI_BF16 && dt != BI_F16) return fail(BI_ERR_UNSUPPORTED, "%s: dtype must be bf16 or fp16", fn);
@@ -360,6 +361,13 @@ bi_status bi_quantized_linear(const void *x, int64_t ldx, const uint32_t *wq, in
     }
     if (bias != nullptr && !aligned_to(bias, 2)) return fail(BI_ERR_UNSUPPORTED, "%s: bias pointer misaligned", fn);
     if (!aligned_to(y, 2)) return fail(BI_ERR_UNSUPPORTED, "%s: output pointer misaligned", fn);
+    const size_t need = bi::qgemm_workspace_bytes(M, N, K);
+    if (need > 0) {
+        if (ws == nullptr || ws_bytes < need)
+            return fail(BI_ERR_WORKSPACE, "%s: workspace of %zu bytes needed (got %zu%s)", fn, need, ws_bytes,
+                        ws == nullptr ? ", null" : "");
+        if (!aligned_to(ws, 256)) return fail(BI_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);
+    }
     bi::QGemmParams q{};
     q.g = make_params(x, ldx, nullptr, 0, bias, 0, y, ldy, M, N, K, 1.0f, 1.0f);
     q.wq = wq;
@@ -369,7 +377,13 @@ bi_status bi_quantized_linear(const void *x, int64_t ldx, const uint32_t *wq, in
     q.ldsb = ldsb;
     q.bits = bits;
     q.group_size = (int)group_size;
-    return device_status(bi::launch_qgemm(q, (int)dt, (hipStream_t)stream), fn);
+    return device_status(bi::launch_qgemm(q, (int)dt, need > 0 ? ws : nullptr, (hipStream_t)stream), fn);
+}
+
+size_t bi_quantized_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, bi_dtype dt) {
+    if (dt != BI_BF16 && dt != BI_F16) return 0;
+    if (M <= 0 || N <= 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return 0;
+    return bi::qgemm_workspace_bytes(M, N, K);
 }
 
 const char *bi_gemm_kernel_name(int64_t M, int64_t N, int64_t K, bi_dtype in_dt, int b_kn) {

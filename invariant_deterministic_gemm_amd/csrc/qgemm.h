@@ -20,7 +20,15 @@ struct QGemmParams {
     int group_shift;        // log2(group_size), set by the launcher
 };
 
-hipError_t launch_qgemm(const QGemmParams &p, int dt, hipStream_t stream);
+// Rows up to this many run the fused kernel; more rows dequantise chunks of at most QGEMM_CHUNK_N
+// columns into a workspace and run the tile GEMM kernels on them.
+constexpr int64_t QGEMM_FUSED_MAX_M = 64;
+constexpr int64_t QGEMM_CHUNK_N = 8192;
+bool qgemm_uses_workspace(int64_t M);
+size_t qgemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+// ws: qgemm_workspace_bytes(M, N, K) bytes of device memory (unused, may be null, when that is 0).
+hipError_t launch_qgemm(const QGemmParams &p, int dt, void *ws, hipStream_t stream);
 
 // Rows of x one workgroup takes (16, 32 or 64): an arithmetic-identical tile choice.
 int qgemm_tile_rows(int M);

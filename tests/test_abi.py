@@ -201,10 +201,10 @@ def test_rowsum_validation(lib):
 
 
 def qlinear(lib, M=4, N=32, K=128, bits=4, gs=64, dt=BF16, x=P16, wq=P16b, sc=P16, sb=P16b, ldx=None, ldwq=None,
-            ldsb=None, ldy=None, bias=None, y=P16):
+            ldsb=None, ldy=None, bias=None, y=P16, ws=None, ws_bytes=0):
     return lib.bi_quantized_linear(x, K if ldx is None else ldx, wq, K * bits // 32 if ldwq is None else ldwq,
                                    sc, sb, K // gs if ldsb is None else ldsb, bits, gs, bias, y,
-                                   N if ldy is None else ldy, M, N, K, dt, None)
+                                   N if ldy is None else ldy, M, N, K, dt, ws, ws_bytes, None)
 
 
 def test_quantized_linear_validation(lib):
@@ -229,6 +229,14 @@ def test_quantized_linear_validation(lib):
     assert qlinear(lib, ldx=132) == UNSUPPORTED                  # ldx not a multiple of 8
     assert qlinear(lib, bits=8, ldwq=33) == UNSUPPORTED          # 8-bit rows need an even word pitch
     assert qlinear(lib, M=0) == OK and qlinear(lib, N=0) == OK   # nothing to do
+    # more than 64 rows need the dequantisation workspace: min(N, 8192) * K * 2 bytes
+    assert lib.bi_quantized_linear_workspace_bytes(64, 32, 128, BF16) == 0
+    assert lib.bi_quantized_linear_workspace_bytes(65, 32, 128, BF16) == 32 * 128 * 2
+    assert lib.bi_quantized_linear_workspace_bytes(1000, 20000, 4096, F16) == 8192 * 4096 * 2
+    assert lib.bi_quantized_linear_workspace_bytes(65, 32, 128, F32) == 0
+    assert qlinear(lib, M=65) == WORKSPACE
+    assert qlinear(lib, M=65, ws=P16, ws_bytes=32 * 128 * 2 - 1) == WORKSPACE
+    assert qlinear(lib, M=65, ws=P_MIS, ws_bytes=1 << 20) == WORKSPACE     # not 256-byte aligned
 
 
 def test_quantize_helper_round_trip():
