@@ -412,6 +412,33 @@ def measure_cells(bi, lib, torch, dev, synthetic, data, launches, groups, names,
                                            "frac_mfma": round(tf / BF16_PEAK_TFLOPS, 4),
                                            "kernel": lib.bi_sdpa_kernel_name(1, 32, S, S, 128, bi.BI_BF16).decode()})
         del q, k, v
+    # quantized linear (4-bit, groups of 64): packed weights rotate through copies so reads are cold;
+    # bytes = packed words + scales + biases + x + y; rows checked against M = 256 on raw bits
+    cells["quantized_gemm"] = []
+    for N in (4096, 14336):
+        wq, sc, sb = bi.quantize(data[N]["w"][0], 4, 64)
+        qbytes = wq.numel() * 4 + sc.numel() * 2 * 2
+        qs = [(wq, sc, sb)] + [(wq.clone(), sc.clone(), sb.clone()) for _ in range(max(1, -(-512 * 2**20 // qbytes)) - 1)]
+        xq = data[N]["x"]
+        full = bi.bi_quantized_linear(xq, wq, sc, sb, 4, 64)
+        differing = 0
+        for M in (1, 4, 16, 64, 256):
+            it = iter(range(10 ** 9))
+            ms = _time_graph(torch, lambda: bi.bi_quantized_linear(xq[:M], *qs[next(it) % len(qs)], 4, 64),
+                             reps=len(qs), iters=5)
+            nbytes = qbytes + 2.0 * (M * K + M * N)
+            gbps = nbytes / (ms * 1e-3) / 1e9
+            tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+            lin = next((c["us"] for c in cells["decode_gemm"] if c["M"] == M and c["N"] == N), None)
+            part = bi.bi_quantized_linear(xq[:M], wq, sc, sb, 4, 64)
+            differing += int((part.view(torch.int16) != full[:M].view(torch.int16)).any(dim=1).sum().item())
+            cells["quantized_gemm"].append({"M": M, "N": N, "bits": 4, "group_size": 64, "us": round(ms * 1e3, 2),
+                                            "GBps": round(gbps, 1), "frac_hbm": round(gbps / HBM_PEAK_GBPS, 4),
+                                            "TFLOPs": round(tf, 1),
+                                            "over_bf16_linear": round(ms * 1e3 / lin, 3) if lin else None})
+        cells.setdefault("quantized_rows_differing_from_M256", 0)
+        cells["quantized_rows_differing_from_M256"] += differing
+        del qs
     # batch-variant comparator on the linear half of the step: cost ratio and negative control
     inv_ms = var_ms = 0.0
     diff = 0
