@@ -237,8 +237,11 @@ bi_status bi_rowsum(const void *x, int64_t ldx, void *y, int64_t M, int64_t N, i
  *
  * x: M rows of K elements of dt at x + m * ldx (16-byte aligned, ldx >= K and
  * a multiple of 8).  wq: N rows of ldwq uint32 words (ldwq >= K * bits / 32;
- * 8-byte aligned with ldwq even when bits == 8).  scales, biases: N rows of
- * ldsb elements of dt (ldsb >= K / group_size).  bias: N elements of dt or
+ * 4-byte aligned for 2 bits; 16-byte aligned with ldwq a multiple of 4 for 4
+ * and 8 bits, which every contiguous packing satisfies).  scales, biases: N
+ * rows of ldsb elements of dt (ldsb >= K / group_size).  Row pitches of 2^24
+ * (x), 2^25 (wq) or 2^26 (scales, biases) elements or more are refused with
+ * BI_ERR_UNSUPPORTED.  bias: N elements of dt or
  * NULL.  y: M rows of N elements of dt at y + m * ldy (ldy >= N).
  * dt: BI_BF16 or BI_F16.  bits: 2, 4 or 8 (3, 5 and 6-bit packings and
  * anything else are refused with BI_ERR_UNSUPPORTED).  group_size: 32, 64 or

@@ -354,8 +354,12 @@ bi_status bi_quantized_linear(const void *x, int64_t ldx, const uint32_t *wq, in
                         (long long)(K / group_size));
         if (!aligned16(x) || ldx % 8 != 0)
             return fail(BI_ERR_UNSUPPORTED, "%s: x must be 16-byte aligned with ldx a multiple of 8", fn);
-        if (!aligned_to(wq, bits == 8 ? 8 : 4) || (bits == 8 && ldwq % 2 != 0))
-            return fail(BI_ERR_UNSUPPORTED, "%s: wq must be 4-byte aligned (8-byte, ldwq even, for 8 bits)", fn);
+        if (bits == 2 ? !aligned_to(wq, 4) : (!aligned16(wq) || ldwq % 4 != 0))
+            return fail(BI_ERR_UNSUPPORTED,
+                        "%s: wq must be 4-byte aligned (4 and 8 bits: 16-byte aligned, ldwq a multiple of 4)", fn);
+        // the fused kernel addresses 64 rows of x and 16 rows of wq / scales with 32-bit byte offsets
+        if (ldx >= (int64_t(1) << 24) || ldwq >= (int64_t(1) << 25) || ldsb >= (int64_t(1) << 26))
+            return fail(BI_ERR_UNSUPPORTED, "%s: row pitches must be below 2^24 (x), 2^25 (wq), 2^26 (scales)", fn);
         if (!aligned_to(scales, 2) || !aligned_to(biases, 2))
             return fail(BI_ERR_UNSUPPORTED, "%s: scales / biases misaligned", fn);
     }

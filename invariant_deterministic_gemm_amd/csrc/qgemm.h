@@ -24,6 +24,8 @@ struct QGemmParams {
 // columns into a workspace and run the tile GEMM kernels on them.
 constexpr int64_t QGEMM_FUSED_MAX_M = 64;
 constexpr int64_t QGEMM_CHUNK_N = 8192;
+// Up to this many rows the fused kernel's consumer loads x itself (x in registers, not LDS).
+constexpr int64_t QGEMM_XREG_MAX_M = 1;
 bool qgemm_uses_workspace(int64_t M);
 size_t qgemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 

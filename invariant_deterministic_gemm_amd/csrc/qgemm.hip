@@ -11,15 +11,20 @@
 // the bias, one rounding), so the result equals bi_linear on the dequantised
 // weight bit for bit, and like it does not depend on M.
 //
-// Up to 64 rows: one workgroup of four wavefronts per (strip of 16 output
-// columns, tile of 16 FM rows of x).  A 128-k stage is 256 units of 8 weights: each thread
-// unpacks one unit (its packed word(s), the group's scale and bias) into the
-// LDS stage in the strip kernel's layout (256-byte rows, chunk c of row r at
-// slot c ^ (r mod 16)) together with its share of the x rows; wavefront 0
-// then runs every row's chain for the stage.  Packed weights and x are
-// prefetched several stages ahead through register rings; the LDS stage is
-// double-buffered with one barrier per stage.  Only ordinary loads
-// are in flight, so the compiler's waits are exact.  More rows: chunks of
+// Up to 64 rows: one workgroup of five wavefronts per (strip of 16 output
+// columns, tile of 16 FM rows of x).  Wavefronts 1-4 unpack: a stage of 256 k
+// (128 k for four row fragments) is 256 units, each thread loading its unit's
+// packed words, scale and bias with one buffer load each and unpacking it into
+// a double-buffered LDS stage (256 or 512-byte rows; the slot of a 16-byte
+// chunk is swizzled by row and by chunk so both the strided unpacking writes
+// and the consumer's 16-row reads are free of bank conflicts), several stages
+// ahead through a register ring.  Wavefront 0 only consumes: it requests a
+// stage's fragments together and runs every row fragment's chain.  x goes
+// through the LDS stages as well, except for a single row, which the consumer
+// loads itself.  Buffer resources end at the last byte of each operand's rows,
+// so rows past N or M, k past K and stages past the end read as zeros with no
+// clamping arithmetic.  Only ordinary loads are in flight and no branch
+// surrounds them, so the compiler's waits are exact.  More rows: chunks of
 // columns are dequantised into a workspace with the same arithmetic and the
 // tile GEMM kernels of bi_linear run on them (the same chain, so the same
 // bits; the choice of path depends on M only as a tile choice does).
@@ -30,12 +35,6 @@
 namespace bi {
 
 namespace {
-
-constexpr int QDEPTH = 8;                // packed-weight stages in flight per thread
-// x stages in flight per thread (divides QDEPTH): deep for one row fragment, where x latency paces the
-// stage loop; one stage ahead for more rows, where the registers cost occupancy
-template <int FM> struct XDepth { static constexpr int value = FM == 1 ? 4 : 1; };
-constexpr int QSTAGE_K = 128;
 
 template <int BITS> struct Packed;
 template <> struct Packed<2> { using T = uint32_t; };   // 8 values = half a word
@@ -63,149 +62,327 @@ __device__ __forceinline__ void lds_barrier() {
 
 }  // namespace
 
-template <int dt, int FM, int BITS>
-__global__ __launch_bounds__(256) void qgemm16_strip(QGemmParams q) {
-    constexpr int ROWB = 256;                    // 128 k of 16-bit values
+// Byte b of x as an fp32 value (v_cvt_f32_ubyte<b>).
+template <int B> __device__ __forceinline__ float byte_f32(uint32_t x) { return (float)((x >> (8 * B)) & 0xFFu); }
+// Hides x's known bits from the optimiser, so that masked fields are converted with the byte-select
+// converts above instead of being re-extracted one at a time.
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+    asm("" : "+v"(x));
+    return x;
+}
+
+// Stage geometry of the fused kernel: k per stage, values each producer thread unpacks per stage (one
+// load of VPT * BITS / 8 bytes, one scale and one bias: VPT never exceeds a group), packed words per
+// unit, weight stages in flight per thread.
+template <int FM, int BITS, bool XREG_> struct QStrip {
+    static constexpr int KS = FM == 4 ? 128 : 256;
+    static constexpr int VPT = KS / 16;                          // 16 rows x KS values over 256 threads
+    static constexpr int WPU = VPT * BITS >= 32 ? VPT * BITS / 32 : 1;
+    static constexpr bool HALF = VPT * BITS < 32;              // 2 bits, 8 values: half a word
+    static constexpr int DEPTH = WPU >= 4 ? 4 : 8;
+    // x: with XREG (one fragment of few rows) the consumer loads its fragments straight into registers
+    // one stage ahead; otherwise x goes through LDS, XU 16-byte chunks per producer thread per stage,
+    // XD stages ahead
+    static constexpr bool XREG = XREG_;
+    static constexpr int XR = 1;
+    static constexpr int XU = XREG ? 0 : 16 * FM * KS / 2048;
+    static constexpr int XD = FM == 1 ? 4 : 1;
+};
+
+// LDS slot of weight chunk c (16 bytes) in strip row r: the row bits keep the consumer's 16-row reads
+// conflict-free, the chunk-index bits (c / CPT, CPT chunks per producer thread) do the same for the
+// producers' strided writes; a bijection on the chunks of a row.
+template <int CPT> __device__ __forceinline__ int wslot(int c, int r) {
+    if constexpr (CPT == 1) return c ^ (r & 15);
+    else return c ^ (r & 15) ^ ((c / CPT) & 7);
+}
+
+struct u32x8 {
+    u32x4 lo, hi;
+};
+template <int N> struct Words;
+template <> struct Words<1> { using T = uint32_t; };
+template <> struct Words<2> { using T = u32x2; };
+template <> struct Words<4> { using T = u32x4; };
+template <> struct Words<8> { using T = u32x8; };
+
+__device__ __forceinline__ int sat_off(uint32_t lane_off, uint32_t st_off) {
+    return (int)__builtin_elementwise_add_sat(lane_off, st_off);
+}
+// packed words of one unit at lane_off + st_off (saturating: an offset marked out of range stays so)
+template <int WPU>
+__device__ __forceinline__ typename Words<WPU>::T load_words(__amdgpu_buffer_rsrc_t r, uint32_t lane_off,
+                                                             uint32_t st_off) {
+    if constexpr (WPU == 1) {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, sat_off(lane_off, st_off), 0, 0);
+    } else if constexpr (WPU == 2) {
+        return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, sat_off(lane_off, st_off), 0, 0));
+    } else if constexpr (WPU == 4) {
+        return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, sat_off(lane_off, st_off), 0, 0));
+    } else {
+        u32x8 w;
+        w.lo = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, sat_off(lane_off, st_off), 0, 0));
+        w.hi = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, sat_off(lane_off + 16u, st_off), 0, 0));
+        return w;
+    }
+}
+template <int WPU> __device__ __forceinline__ uint32_t word_at(const typename Words<WPU>::T &w, int i) {
+    if constexpr (WPU == 1) return w;
+    else if constexpr (WPU == 8) return i < 4 ? w.lo[i] : w.hi[i - 4];
+    else return w[i];
+}
+
+// Fields 8 h .. 8 h + 7 of a unit as fp32 values in k order (fields lowest bits first).  hshift
+// selects the half word of a 2-bit unit of 8 values.
+template <int BITS, int WPU>
+__device__ __forceinline__ void unpack8(const typename Words<WPU>::T &w, int h, uint32_t hshift, float (&f)[8]) {
+    if constexpr (BITS == 8) {
+        const uint32_t x0 = word_at<WPU>(w, 2 * h), x1 = word_at<WPU>(w, 2 * h + 1);
+        f[0] = byte_f32<0>(x0);
+        f[1] = byte_f32<1>(x0);
+        f[2] = byte_f32<2>(x0);
+        f[3] = byte_f32<3>(x0);
+        f[4] = byte_f32<0>(x1);
+        f[5] = byte_f32<1>(x1);
+        f[6] = byte_f32<2>(x1);
+        f[7] = byte_f32<3>(x1);
+    } else if constexpr (BITS == 4) {
+        const uint32_t x = word_at<WPU>(w, h);
+        const uint32_t lo = opaque(x & 0x0F0F0F0Fu), hi = opaque((x >> 4) & 0x0F0F0F0Fu);
+        f[0] = byte_f32<0>(lo);
+        f[1] = byte_f32<0>(hi);
+        f[2] = byte_f32<1>(lo);
+        f[3] = byte_f32<1>(hi);
+        f[4] = byte_f32<2>(lo);
+        f[5] = byte_f32<2>(hi);
+        f[6] = byte_f32<3>(lo);
+        f[7] = byte_f32<3>(hi);
+    } else {
+        const uint32_t x = word_at<WPU>(w, h / 2) >> (hshift + 16u * (uint32_t)(h & 1));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t t = opaque((x >> (2 * j)) & 0x03030303u);   // byte b: field 4 b + j
+            f[j] = byte_f32<0>(t);
+            f[4 + j] = byte_f32<1>(t);
+        }
+    }
+}
+
+template <int dt, int FM, int BITS, bool XREG_>
+__global__ __launch_bounds__(320) void qgemm16_strip(QGemmParams q) {
+    static_assert(FM == 1 || !XREG_, "x in registers for one fragment only");
+    using G = QStrip<FM, BITS, XREG_>;
+    constexpr int KS = G::KS, VPT = G::VPT, WPU = G::WPU, QD = G::DEPTH, XU = G::XU, XD = G::XD, XR = G::XR;
+    constexpr bool XREG = G::XREG;
+    constexpr int ROWB = KS * 2;                 // bytes of one LDS row (KS values of 16 bits)
+    constexpr int CH = ROWB / 16;                // 16-byte chunks per LDS row
     constexpr int AR = 16 * FM;                  // x rows per workgroup
-    constexpr int STAGE = (16 + AR) * ROWB;
-    constexpr int PER = 32 / BITS;               // values per packed word
-    constexpr uint32_t FIELD = (1u << BITS) - 1u;
-    using P = typename Packed<BITS>::T;
-    constexpr int XD = XDepth<FM>::value;
+    constexpr int STAGE = (XREG ? 16 : 16 + AR) * ROWB;
+    constexpr int SPS = KS / 32;                 // chain steps per stage
+    constexpr int HS = FM == 1 ? (SPS < 8 ? SPS : 8) : (SPS < 4 ? SPS : 4);   // steps read together
+    constexpr uint32_t OOB = 0x80000000u;        // offset past every resource: the load returns zeros
+    using W = typename Words<WPU>::T;
+    static_assert(QD % XD == 0 && QD % 2 == 0 && (XR == 1 || XR % 2 == 0), "ring geometry");
     __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
 
     const GemmParams &p = q.g;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
     const int nstrip = (p.N + 15) / 16;
     const int n0 = (blockIdx.x % nstrip) * 16;
     const int m0 = (blockIdx.x / nstrip) * AR;
-    const int nst = (p.K + QSTAGE_K - 1) / QSTAGE_K;
+    const int nst = (p.K + KS - 1) / KS;
+    const int nround = (nst + QD - 1) / QD * QD;     // stages the loops run (whole rounds of QD)
+    const int rows = min(16, p.N - n0), xrows = min(AR, p.M - m0);
 
-    // this thread's weight unit: row wr of the strip, 8 values at chunk wc of each stage
-    const int wr = tid >> 4, wc = tid & 15;
-    const int wn = min(n0 + wr, p.N - 1);
-    const uint32_t *wrow = q.wq + (int64_t)wn * q.ldwq;
-    const void *srow = static_cast<const char *>(q.scales) + (int64_t)wn * q.ldsb * 2;
-    const void *brow = static_cast<const char *>(q.biases) + (int64_t)wn * q.ldsb * 2;
-    const int wslot = ((wc ^ (wr & 15)) << 4);
+    // Buffer resources of this workgroup's rows, each ending at the last byte of its last row's K
+    // values (none at all when K = 0, where the tensors may be empty).  Offsets are 32-bit and
+    // combined with saturating adds, so an offset marked out of range stays out of range; anything
+    // past a resource (rows past N or M, k past K, stages past the end) reads as zero.  The host keeps
+    // each resource below 2^31 bytes.
+    const uint32_t kb = p.K > 0 ? 1u : 0u;
+    const uint32_t xrow_b = (uint32_t)p.lda * 2u;
+    const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char *>(static_cast<const char *>(p.A) + (int64_t)m0 * p.lda * 2), 0,
+        (int)(kb * ((uint32_t)(xrows - 1) * xrow_b + (uint32_t)p.K * 2u)), 0x00020000);
+    auto stage_off = [&](int s, uint32_t per) { return s < nst ? (uint32_t)s * per : OOB; };
 
-    // register ring: packed values, raw 16-bit scale and bias of the unit for DEPTH stages (converted
-    // only when unpacked, so nothing waits for a load before its stage comes up)
-    P raw[QDEPTH];
-    uint32_t rsc[QDEPTH], rbi[QDEPTH];
-    const uint16_t *sp16 = static_cast<const uint16_t *>(srow);
-    const uint16_t *bp16 = static_cast<const uint16_t *>(brow);
-    auto loadW = [&](int s, P &r, uint32_t &sc, uint32_t &bi) {
-        const int k = min(s * QSTAGE_K + 8 * wc, p.K - 8);        // k < K: clamped, unused past K
-        if constexpr (BITS == 8) r = *reinterpret_cast<const u32x2 *>(wrow + k / PER);
-        else r = wrow[k / PER];
-        const int grp = k >> q.group_shift;
-        sc = sp16[grp];
-        bi = bp16[grp];
-    };
-    auto storeW = [&](int s, const P &r, uint32_t scr, uint32_t bir, char *buf) {
-        const int k = s * QSTAGE_K + 8 * wc;
-        const float sc = half_to_f32<dt>(scr), bi = half_to_f32<dt>(bir);
-        float w[8];
+    if (wave == 0) {
+        // consumer: FM row fragments against the strip's 16 columns; every fragment of a stage is
+        // requested before its first step, so the steps wait on LDS once per stage; k past K is never read
+        const int r16 = lane & 15, g = lane >> 4;
+        f32x4 acc[FM];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            uint32_t f;
-            if constexpr (BITS == 8) f = (r[j >> 2] >> (8 * (j & 3))) & FIELD;
-            else if constexpr (BITS == 4) f = (r >> (4 * j)) & FIELD;
-            else f = (r >> (16 * ((k >> 3) & 1) + 2 * j)) & FIELD;
-            w[j] = __builtin_fmaf(sc, (float)f, bi);
+        for (int f = 0; f < FM; ++f) acc[f] = zero4();
+        // one fragment: x rows (row r16 clamped to the last row) straight from memory, XR stages ahead
+        const uint32_t xa_lane = (uint32_t)min(r16, xrows - 1) * xrow_b + (uint32_t)g * 16u;
+        u32x4 xa[XR][SPS];
+        auto loadX = [&](int s, u32x4 (&a)[SPS]) {
+            const uint32_t so = stage_off(s, (uint32_t)ROWB);
+#pragma unroll
+            for (int u = 0; u < SPS; ++u)
+                a[u] = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres, sat_off(xa_lane + 64u * u, so), 0, 0));
+        };
+        if constexpr (XREG) {
+#pragma unroll
+            for (int j = 0; j < XR; ++j) loadX(j, xa[j]);
         }
-        u32x4 v = u32x4{round_pack<dt>(w[0], w[1]), round_pack<dt>(w[2], w[3]), round_pack<dt>(w[4], w[5]),
-                        round_pack<dt>(w[6], w[7])};
-        if (k >= p.K) v = zero_u4();
-        *reinterpret_cast<u32x4 *>(buf + wr * ROWB + wslot) = v;
-    };
-    // x rows: FM units of 16 bytes per thread per stage, in a ring of XD stages
-    u32x4 araw[XD][FM];
-    auto loadA = [&](int s, u32x4 (&a)[FM]) {    // clamped to k < K; chunks past K are zeroed when stored
+        lds_barrier();                                   // stage 0 unpacked
+        constexpr int CU = XR == 1 ? 2 : XR;            // consumer unroll: buffer parity and x ring slot constant
+        for (int s0 = 0; s0 < nround; s0 += CU) {
 #pragma unroll
-        for (int f = 0; f < FM; ++f) {
-            const int u = tid + 256 * f, r = u >> 4, c = u & 15;
-            const int k = min(s * QSTAGE_K + 8 * c, p.K - 8);
-            const int m = min(m0 + r, p.M - 1);
-            a[f] = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(p.A) + ((int64_t)m * p.lda + k) * 2);
-        }
-    };
-    auto storeA = [&](int s, const u32x4 (&a)[FM], char *buf) {
+            for (int j = 0; j < CU; ++j) {
+                const int s = s0 + j;
+                const char *buf = lds + (j & 1) * STAGE;
 #pragma unroll
-        for (int f = 0; f < FM; ++f) {
-            const int u = tid + 256 * f, r = u >> 4, c = u & 15;
-            const int row = 16 + r;
-            const u32x4 v = s * QSTAGE_K + 8 * c < p.K ? a[f] : zero_u4();
-            *reinterpret_cast<u32x4 *>(buf + row * ROWB + ((c ^ (row & 15)) << 4)) = v;
-        }
-    };
-
-    // consumer (wavefront 0): FM row fragments against the strip's 16 columns
-    const int r16 = lane & 15, g = lane >> 4;
-    f32x4 acc[FM];
+                for (int h = 0; h < SPS / HS; ++h) {          // HS steps at a time
+                    u32x4 b[HS], a[HS][FM];
 #pragma unroll
-    for (int f = 0; f < FM; ++f) acc[f] = zero4();
-    auto consume = [&](int s, const char *buf) {
+                    for (int v = 0; v < HS; ++v) {
+                        const int u = h * HS + v, c = 4 * u + g;
+                        b[v] = *reinterpret_cast<const u32x4 *>(buf + r16 * ROWB + (wslot<VPT / 8>(c, r16) << 4));
+                        if constexpr (XREG) {
+                            a[v][0] = xa[j % XR][u];
+                        } else {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            if (s * 4 + u < p.total_steps) {             // uniform: the chain's steps, none past K
-                const int c = 4 * u + g;
-                const u32x4 b = *reinterpret_cast<const u32x4 *>(buf + r16 * ROWB + ((c ^ r16) << 4));
+                            for (int f = 0; f < FM; ++f) {
+                                const int row = 16 + 16 * f + r16;
+                                a[v][f] = *reinterpret_cast<const u32x4 *>(buf + row * ROWB + ((c ^ (row & 15)) << 4));
+                            }
+                        }
+                    }
+                    const int u0 = s * SPS + h * HS;
+                    if (u0 + HS <= p.total_steps) {           // uniform: whole steps of the chain
 #pragma unroll
-                for (int f = 0; f < FM; ++f) {
-                    const int row = 16 + 16 * f + r16;
-                    const u32x4 a = *reinterpret_cast<const u32x4 *>(buf + row * ROWB + ((c ^ (row & 15)) << 4));
-                    acc[f] = Mfma<dt>::step(a, b, acc[f]);
+                        for (int v = 0; v < HS; ++v)
+#pragma unroll
+                            for (int f = 0; f < FM; ++f) acc[f] = Mfma<dt>::step(a[v][f], b[v], acc[f]);
+                    } else {                                  // the end of K: its steps before K only
+#pragma unroll
+                        for (int v = 0; v < HS; ++v)
+                            if (u0 + v < p.total_steps)
+#pragma unroll
+                                for (int f = 0; f < FM; ++f) acc[f] = Mfma<dt>::step(a[v][f], b[v], acc[f]);
+                    }
                 }
+                if constexpr (XREG) loadX(s + XR, xa[j % XR]);
+                lds_barrier();                           // stage s read; stage s + 1 unpacked
             }
         }
+        const int n = n0 + r16;
+        if (n >= p.N) return;
+#pragma unroll
+        for (int f = 0; f < FM; ++f)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = m0 + 16 * f + 4 * g + i;
+                if (m < p.M) epilogue<dt>(p, m, n, acc[f][i]);
+            }
+        return;
+    }
+
+    // producers (wavefronts 1-4): unpack the weights (and copy x, several fragments) into the LDS stages
+    if (nst == 0) {                                      // K = 0: nothing to load
+        lds_barrier();
+        return;
+    }
+    const int tid = threadIdx.x - 64;
+    const uint32_t wrow_b = (uint32_t)q.ldwq * 4u, srow_b = (uint32_t)q.ldsb * 2u;
+    const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint32_t *>(q.wq + (int64_t)n0 * q.ldwq), 0,
+        (int)((uint32_t)(rows - 1) * wrow_b + (uint32_t)p.K / 8u * (uint32_t)BITS), 0x00020000);
+    const uint32_t sb_records = (uint32_t)(rows - 1) * srow_b + ((uint32_t)p.K >> q.group_shift) * 2u;
+    const __amdgpu_buffer_rsrc_t sres = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char *>(static_cast<const char *>(q.scales) + (int64_t)n0 * q.ldsb * 2), 0, (int)sb_records,
+        0x00020000);
+    const __amdgpu_buffer_rsrc_t bres = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char *>(static_cast<const char *>(q.biases) + (int64_t)n0 * q.ldsb * 2), 0, (int)sb_records,
+        0x00020000);
+
+    // this thread's weight unit: row wr of the strip, VPT values at k = KS s + VPT wc of stage s
+    const int wr = tid >> 4, wc = tid & 15;
+    const uint32_t w_lane = wr < rows ? (uint32_t)wr * wrow_b + (uint32_t)(VPT * wc * BITS / 8) / 4u * 4u : OOB;
+    const uint32_t s_lane = wr < rows ? (uint32_t)wr * srow_b + (uint32_t)((VPT * wc) >> q.group_shift) * 2u : OOB;
+    const uint32_t hshift = G::HALF ? 16u * (uint32_t)(wc & 1) : 0u;
+    constexpr uint32_t W_STAGE = KS * BITS / 8;                        // packed bytes of a row per stage
+    const uint32_t S_STAGE = (uint32_t)(KS >> q.group_shift) * 2u;     // scale bytes of a row per stage
+
+    W raw[QD];
+    uint32_t rsc[QD], rbi[QD];
+    auto loadW = [&](int s, W &r, uint32_t &sc, uint32_t &bi) {
+        r = load_words<WPU>(wres, w_lane, stage_off(s, W_STAGE));
+        const int so = sat_off(s_lane, stage_off(s, S_STAGE));
+        sc = __builtin_amdgcn_raw_buffer_load_b16(sres, so, 0, 0);
+        bi = __builtin_amdgcn_raw_buffer_load_b16(bres, so, 0, 0);
+    };
+    // unpack into LDS: chunk c of strip row r at slot wslot(c, r)
+    auto storeW = [&](const W &r, uint32_t scr, uint32_t bir, char *buf) {
+        const float sc = half_to_f32<dt>(scr), bi = half_to_f32<dt>(bir);
+#pragma unroll
+        for (int h = 0; h < VPT / 8; ++h) {
+            float w[8];
+            unpack8<BITS, WPU>(r, h, hshift, w);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) w[j] = __builtin_fmaf(sc, w[j], bi);
+            const int c = (VPT / 8) * wc + h;
+            *reinterpret_cast<u32x4 *>(buf + wr * ROWB + (wslot<VPT / 8>(c, wr) << 4)) =
+                u32x4{round_pack<dt>(w[0], w[1]), round_pack<dt>(w[2], w[3]), round_pack<dt>(w[4], w[5]),
+                      round_pack<dt>(w[6], w[7])};
+        }
+    };
+    // several x fragments: XU chunks of 16 bytes per thread per stage, in a ring of XD stages
+    constexpr int XUA = XU > 0 ? XU : 1;
+    uint32_t x_lane[XUA];
+#pragma unroll
+    for (int f = 0; f < XUA; ++f) {
+        const int u = tid + 256 * f, r = u / CH, c = u % CH;
+        x_lane[f] = r < xrows ? (uint32_t)r * xrow_b + (uint32_t)c * 16u : OOB;
+    }
+    u32x4 araw[XD][XUA];
+    auto loadA = [&](int s, u32x4 (&a)[XUA]) {
+        const uint32_t so = stage_off(s, (uint32_t)ROWB);
+#pragma unroll
+        for (int f = 0; f < XU; ++f)
+            a[f] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres, sat_off(x_lane[f], so), 0, 0));
+    };
+    auto storeA = [&](const u32x4 (&a)[XUA], char *buf) {
+#pragma unroll
+        for (int f = 0; f < XU; ++f) {
+            const int u = tid + 256 * f, r = u / CH, c = u % CH;
+            const int row = 16 + r;
+            *reinterpret_cast<u32x4 *>(buf + row * ROWB + ((c ^ (row & 15)) << 4)) = a[f];
+        }
     };
 
-    // prologue: rings filled with stages 0 .. DEPTH-1, stage 0 unpacked, stage DEPTH requested
-    if (nst > 0) {
+    // prologue: rings filled with stages 0 .. depth-1, stage 0 unpacked, the freed slots refilled
 #pragma unroll
-        for (int j = 0; j < XD; ++j) loadA(j, araw[j]);
+    for (int j = 0; j < XD; ++j) loadA(j, araw[j]);
 #pragma unroll
-        for (int j = 0; j < QDEPTH; ++j) loadW(j, raw[j], rsc[j], rbi[j]);
-        storeA(0, araw[0], lds);
-        loadA(XD, araw[0]);
-        storeW(0, raw[0], rsc[0], rbi[0], lds);
-        loadW(QDEPTH, raw[0], rsc[0], rbi[0]);
-        lds_barrier();
-    }
-    // stage s: consume it; store x of stage s + 1 (x ring slot (s + 1) mod XD) and refill that slot
-    // with stage s + 1 + XD; unpack stage s + 1 (weight ring slot (s + 1) mod DEPTH) into the other
-    // buffer and refill that slot with stage s + 1 + DEPTH.  The body has no branch
-    // around loads (stages past the end load clamped addresses and store zeros; the stage count is
-    // rounded up to whole rounds of DEPTH), so the compiler counts each wait exactly.
-    for (int s0 = 0; s0 < nst; s0 += QDEPTH) {
+    for (int j = 0; j < QD; ++j) loadW(j, raw[j], rsc[j], rbi[j]);
+    storeA(araw[0], lds);
+    loadA(XD, araw[0]);
+    storeW(raw[0], rsc[0], rbi[0], lds);
+    loadW(QD, raw[0], rsc[0], rbi[0]);
+    lds_barrier();
+    // while the consumer reads stage s: store x of stage s + 1 and refill its ring slot with stage
+    // s + 1 + XD; unpack the weights of stage s + 1 into the other buffer and refill that slot with
+    // stage s + 1 + QD.  No branch around loads (stages past the end read as zeros and are never
+    // consumed), so the compiler counts each wait exactly.
+    for (int s0 = 0; s0 < nround; s0 += QD) {
 #pragma unroll
-        for (int j = 0; j < QDEPTH; ++j) {
+        for (int j = 0; j < QD; ++j) {
             const int s = s0 + j;
-            const int jn = (j + 1) % QDEPTH;               // constants once the loop is unrolled
+            const int jn = (j + 1) % QD;                  // constants once the loop is unrolled
             const int xn = (j + 1) % XD;
-            char *cur = lds + (s & 1) * STAGE;
-            char *nxt = lds + ((s + 1) & 1) * STAGE;
-            if (wave == 0) consume(s, cur);
-            storeA(s + 1, araw[xn], nxt);
+            char *nxt = lds + ((j + 1) & 1) * STAGE;     // s0 is a multiple of QD (even)
+            storeA(araw[xn], nxt);
             loadA(s + 1 + XD, araw[xn]);
-            storeW(s + 1, raw[jn], rsc[jn], rbi[jn], nxt);
-            loadW(s + 1 + QDEPTH, raw[jn], rsc[jn], rbi[jn]);
+            storeW(raw[jn], rsc[jn], rbi[jn], nxt);
+            loadW(s + 1 + QD, raw[jn], rsc[jn], rbi[jn]);
             lds_barrier();
         }
     }
-
-    if (wave != 0) return;
-    const int n = n0 + r16;
-    if (n >= p.N) return;
-#pragma unroll
-    for (int f = 0; f < FM; ++f)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int m = m0 + 16 * f + 4 * g + i;
-            if (m < p.M) epilogue<dt>(p, m, n, acc[f][i]);
-        }
 }
 
 // Large batches: the weights of columns [n0, n0 + nc) dequantised into an (nc, K) buffer of the input
@@ -252,15 +429,15 @@ size_t qgemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     return (size_t)(nc * K * 2);
 }
 
-template <int dt, int FM>
+template <int dt, int FM, bool XREG = false>
 static hipError_t launch_fm(const QGemmParams &q, hipStream_t st) {
     const int64_t nstrip = (q.g.N + 15) / 16, ntile = (q.g.M + 16 * FM - 1) / (16 * FM);
     const int64_t nwg = nstrip * ntile;
     if (nwg > INT32_MAX) return hipErrorInvalidConfiguration;
-    const dim3 grid((unsigned)nwg), block(256);
-    if (q.bits == 2) hipLaunchKernelGGL((qgemm16_strip<dt, FM, 2>), grid, block, 0, st, q);
-    else if (q.bits == 4) hipLaunchKernelGGL((qgemm16_strip<dt, FM, 4>), grid, block, 0, st, q);
-    else if (q.bits == 8) hipLaunchKernelGGL((qgemm16_strip<dt, FM, 8>), grid, block, 0, st, q);
+    const dim3 grid((unsigned)nwg), block(320);
+    if (q.bits == 2) hipLaunchKernelGGL((qgemm16_strip<dt, FM, 2, XREG>), grid, block, 0, st, q);
+    else if (q.bits == 4) hipLaunchKernelGGL((qgemm16_strip<dt, FM, 4, XREG>), grid, block, 0, st, q);
+    else if (q.bits == 8) hipLaunchKernelGGL((qgemm16_strip<dt, FM, 8, XREG>), grid, block, 0, st, q);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }
@@ -268,7 +445,10 @@ static hipError_t launch_fm(const QGemmParams &q, hipStream_t st) {
 template <int dt>
 static hipError_t launch_dt(const QGemmParams &q, hipStream_t st) {
     const int rows = qgemm_tile_rows(q.g.M);
-    if (rows == 16) return launch_fm<dt, 1>(q, st);
+    if (rows == 16) {
+        if (q.g.M <= QGEMM_XREG_MAX_M) return launch_fm<dt, 1, true>(q, st);
+        return launch_fm<dt, 1>(q, st);
+    }
     if (rows == 32) return launch_fm<dt, 2>(q, st);
     return launch_fm<dt, 4>(q, st);
 }

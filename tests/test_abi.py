@@ -227,7 +227,14 @@ def test_quantized_linear_validation(lib):
     assert qlinear(lib, ldy=16) == INVALID                       # ldy < N
     assert qlinear(lib, x=P_MIS) == UNSUPPORTED                  # x not 16-byte aligned
     assert qlinear(lib, ldx=132) == UNSUPPORTED                  # ldx not a multiple of 8
-    assert qlinear(lib, bits=8, ldwq=33) == UNSUPPORTED          # 8-bit rows need an even word pitch
+    assert qlinear(lib, bits=8, ldwq=33) == UNSUPPORTED          # 8-bit rows: a pitch of 4k words
+    assert qlinear(lib, bits=4, ldwq=18) == UNSUPPORTED          # 4-bit rows: a pitch of 4k words
+    assert qlinear(lib, bits=4, wq=ctypes.c_void_p(0x7f0000000008)) == UNSUPPORTED   # 16-byte alignment
+    # 2-bit rows need 4 bytes only (stopped by the missing workspace, after the alignment checks)
+    assert qlinear(lib, M=65, bits=2, ldwq=9, wq=ctypes.c_void_p(0x7f0000000004)) == WORKSPACE
+    assert qlinear(lib, ldx=1 << 24) == UNSUPPORTED              # 32-bit offsets inside the kernel
+    assert qlinear(lib, ldwq=1 << 25) == UNSUPPORTED
+    assert qlinear(lib, ldsb=1 << 26) == UNSUPPORTED
     assert qlinear(lib, M=0) == OK and qlinear(lib, N=0) == OK   # nothing to do
     # more than 64 rows need the dequantisation workspace: min(N, 8192) * K * 2 bytes
     assert lib.bi_quantized_linear_workspace_bytes(64, 32, 128, BF16) == 0

@@ -6,7 +6,7 @@
   weight's storage differs;
 * oracle tolerance (bf16 / fp16 outputs: 2e-2) against the float64 oracle's quantized_linear;
 * invariance on raw bit patterns across batch size and batch neighbours;
-* shapes with ragged N, a partial last 128-k stage, every bit width and group size, and both paths
+* shapes with ragged N, a partial last stage of the K loop, every bit width and group size, and both paths
   (up to 64 rows: unpacked inside the kernel's K loop; more: dequantised by chunks into a workspace
   for bi_linear's kernels), whose rows must agree bit for bit.
 """
@@ -40,6 +40,8 @@ CASES = [  # M, N, K, bits, gs
     (1, 4096, 4096, 4, 64), (4, 300, 384, 4, 128), (7, 513, 256, 8, 32), (16, 257, 96, 2, 32),
     (33, 1000, 1024, 4, 32), (64, 128, 640, 8, 128), (100, 96, 512, 2, 64), (200, 72, 4096, 4, 64),
     (70, 8200, 256, 4, 64),   # more than 64 rows: dequantised in two chunks of columns (8192 + 8)
+    # one row (x loaded by the consumer itself) and few rows, with partial last stages
+    (1, 100, 352, 8, 32), (1, 33, 160, 2, 32), (2, 77, 4160, 4, 64), (5, 200, 800, 2, 32),
 ]
 
 
