@@ -65,7 +65,7 @@ def _bind(lib):
     lib.oracle_gemm_f64.argtypes = [p, i64, p, i64, ctypes.c_int, p, i64, d, d, p, i64, i64, i64, i64]
     lib.oracle_gemm_f64.restype = None
     lib.oracle_sdpa_f64.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, d,
-                                    ctypes.c_int, p, p]
+                                    ctypes.c_int, p, p, p, p, p]
     lib.oracle_sdpa_f64.restype = None
     lib.oracle_rowsum_f64.argtypes = [p, i64, i64, i64, ctypes.c_int, p]
     lib.oracle_rowsum_f64.restype = None
@@ -147,12 +147,14 @@ def addmm(c, a, b, alpha: float = 1.0, beta: float = 1.0) -> np.ndarray:
     return gemm(a, b, False, c, alpha, beta)
 
 
-def sdpa(q, k, v, causal: bool = False, mask=None, scale: float | None = None) -> np.ndarray:
+def sdpa(q, k, v, causal: bool = False, mask=None, scale: float | None = None, sinks=None) -> np.ndarray:
     """Softmax attention over (B, Hq, Lq, D) queries and (B, Hkv, S, D) keys / values.
 
-    Bottom-right causal alignment, query head h reads KV head floor(h*Hkv/Hq),
-    mask is boolean (True = attend) and broadcastable to (B, Hq, Lq, S).
-    scale defaults to 1/sqrt(D).
+    Bottom-right causal alignment, query head h reads KV head floor(h*Hkv/Hq).
+    mask is broadcastable to (B, Hq, Lq, S): boolean or integer (nonzero = attend), or floating
+    point, added to the scaled scores (-inf removes a key) -- the README's mask forms (section
+    "How the kernels work", attention paragraph).  sinks: None or Hq logits, one extra softmax
+    term per query head that carries no value (section "Limitations").  scale defaults to 1/sqrt(D).
     """
     Q, Kt, V = _f64(q), _f64(k), _f64(v)
     B, Hq, Lq, D = Q.shape
@@ -169,28 +171,43 @@ def sdpa(q, k, v, causal: bool = False, mask=None, scale: float | None = None) -
     def strides(a):
         return i64x4(*[s // a.itemsize for s in a.strides])
 
-    mptr, mstr = None, i64x4(0, 0, 0, 0)
-    M8 = None
-    if mask is not None:
-        if hasattr(mask, "detach"):
-            mask = mask.detach().to("cpu").numpy()
-        M8 = np.asarray(mask).astype(np.uint8)
-        while M8.ndim < 4:
-            M8 = M8[None]
-        M8 = np.ascontiguousarray(M8)
+    def bcast(a, name):
+        while a.ndim < 4:
+            a = a[None]
+        a = np.ascontiguousarray(a)
         st = []
         for dim, want in zip(range(4), (B, Hq, Lq, S)):
-            if M8.shape[dim] == want:
-                st.append(M8.strides[dim])
-            elif M8.shape[dim] == 1:
+            if a.shape[dim] == want:
+                st.append(a.strides[dim] // a.itemsize)
+            elif a.shape[dim] == 1:
                 st.append(0)
             else:
-                raise ValueError(f"mask dim {dim} is {M8.shape[dim]}, expected 1 or {want}")
-        mstr = i64x4(*st)
-        mptr = _ptr(M8)
+                raise ValueError(f"{name} dim {dim} is {a.shape[dim]}, expected 1 or {want}")
+        return a, i64x4(*st)
+
+    mptr, mstr = None, i64x4(0, 0, 0, 0)
+    aptr, astr = None, i64x4(0, 0, 0, 0)
+    M8 = A64 = None
+    if mask is not None:
+        if hasattr(mask, "detach"):
+            mask = mask.detach().to("cpu")
+            mask = mask.float().numpy() if mask.is_floating_point() else mask.numpy()
+        mask = np.asarray(mask)
+        if np.issubdtype(mask.dtype, np.floating):
+            A64, astr = bcast(mask.astype(np.float64), "mask")
+            aptr = _ptr(A64)
+        else:
+            M8, mstr = bcast(mask.astype(np.uint8), "mask")
+            mptr = _ptr(M8)
+    sptr, S64 = None, None
+    if sinks is not None:
+        S64 = np.ascontiguousarray(_f64(sinks).reshape(-1))
+        if S64.shape != (Hq,):
+            raise ValueError(f"sinks must hold Hq={Hq} values")
+        sptr = _ptr(S64)
     _load().oracle_sdpa_f64(_ptr(Q), strides(Q), _ptr(Kt), strides(Kt), _ptr(V), strides(V),
                             _ptr(out), B, Hq, Hkv, Lq, S, D, float(scale), 1 if causal else 0,
-                            mptr, mstr)
+                            mptr, mstr, aptr, astr, sptr)
     return out
 
 

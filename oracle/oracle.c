@@ -99,7 +99,9 @@ void oracle_gemm_f64(const double *A, int64_t lda,
 
 /*
  * Scaled dot-product attention with grouped-query heads, an optional
- * bottom-right causal mask and an optional boolean mask.
+ * bottom-right causal mask, an optional boolean mask, an optional additive
+ * mask and optional attention sinks (README, section "How the kernels work",
+ * attention paragraph: the three mask forms; section "Limitations": sinks).
  *
  * q : (B, Hq,  Lq, D), element strides qs[0..3]
  * k : (B, Hkv, S,  D), element strides ks[0..3]
@@ -107,15 +109,23 @@ void oracle_gemm_f64(const double *A, int64_t lda,
  * o : (B, Hq,  Lq, D), contiguous, written in float64
  * mask : NULL, or uint8 with element strides ms[0..3] over (B, Hq, Lq, S);
  *        a stride of 0 broadcasts that dimension; nonzero = may attend.
+ * amask: NULL, or float64 with element strides as[0..3] over (B, Hq, Lq, S),
+ *        added to the scaled scores; -inf removes the key.
+ * sinks: NULL, or Hq float64 logits, one per query head: an extra softmax
+ *        term on the scale of the scaled scores that carries no value.
  *
  * For query row (b, h, i):
  *   position   p   = S - Lq + i
  *   KV head    g   = floor(h * Hkv / Hq)
+ *   added      a_j = amask[b,h,i,j] (0 without one)
  *   visible    j   : (causal == 0 or j <= p) and (mask == NULL or mask[b,h,i,j])
- *   score      s_j = scale * sum_d q[b,h,i,d] * k[b,g,j,d]
- *   weight     w_j = exp(s_j - max_visible s)
- *   output     o[b,h,i,:] = sum_visible w_j v[b,g,j,:] / sum_visible w_j
- *   a row with no visible key is 0.
+ *                    and a_j != -inf
+ *   score      s_j = scale * sum_d q[b,h,i,d] * k[b,g,j,d] + a_j
+ *   max        m   = max(max_visible s_j, sinks[h])
+ *   weight     w_j = exp(s_j - m)
+ *   output     o[b,h,i,:] = sum_visible w_j v[b,g,j,:]
+ *                           / (sum_visible w_j + exp(sinks[h] - m))
+ *   (the sink terms absent without sinks); a row with no visible key is 0.
  */
 void oracle_sdpa_f64(const double *q, const int64_t *qs,
                      const double *k, const int64_t *ks,
@@ -123,7 +133,8 @@ void oracle_sdpa_f64(const double *q, const int64_t *qs,
                      double *o,
                      int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq,
                      int64_t S, int64_t D, double scale, int causal,
-                     const uint8_t *mask, const int64_t *ms)
+                     const uint8_t *mask, const int64_t *ms,
+                     const double *amask, const int64_t *as, const double *sinks)
 {
     const int64_t rows = B * Hq * Lq;
     #pragma omp parallel
@@ -149,12 +160,17 @@ void oracle_sdpa_f64(const double *q, const int64_t *qs,
                 if (ok && mask != NULL) {
                     ok = mask[b * ms[0] + h * ms[1] + i * ms[2] + j * ms[3]] != 0;
                 }
+                double add = 0.0;
+                if (ok && amask != NULL) {
+                    add = amask[b * as[0] + h * as[1] + i * as[2] + j * as[3]];
+                    if (add == -INFINITY) ok = 0;
+                }
                 vis[j] = (unsigned char)ok;
                 if (!ok) continue;
                 const double *krow = k + b * ks[0] + g * ks[1] + j * ks[2];
                 double dot = 0.0;
                 for (int64_t d = 0; d < D; ++d) dot = dot + qrow[d * qs[3]] * krow[d * ks[3]];
-                s[j] = scale * dot;
+                s[j] = scale * dot + add;
                 if (!any || s[j] > m) m = s[j];
                 any = 1;
             }
@@ -163,6 +179,11 @@ void oracle_sdpa_f64(const double *q, const int64_t *qs,
                 continue;
             }
             double den = 0.0;
+            if (sinks != NULL) {
+                const double sk = sinks[h];
+                if (sk > m) m = sk;
+                den = den + exp(sk - m);
+            }
             for (int64_t d = 0; d < D; ++d) num[d] = 0.0;
             for (int64_t j = 0; j < S; ++j) {
                 if (!vis[j]) continue;

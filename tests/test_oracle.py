@@ -140,8 +140,9 @@ GEMM_PINS = [pin_gemm_fraction, pin_gemm_fsum_medium, pin_gemm_integer_exact,
 
 
 # ------------------------------------------------------------------ SDPA pins
-def brute_sdpa(q, k, v, causal, mask, scale):
-    """Plain-Python attention: exact dot products, math.exp, math.fsum."""
+def brute_sdpa(q, k, v, causal, mask, scale, amask=None, sinks=None):
+    """Plain-Python attention: exact dot products, math.exp, math.fsum.  amask (full shape) is added
+    to the scaled scores, -inf dropping the key; sinks[h] is an extra softmax term with no value."""
     B, Hq, Lq, D = q.shape
     _, Hkv, S, _ = k.shape
     out = np.zeros((B, Hq, Lq, D))
@@ -151,14 +152,21 @@ def brute_sdpa(q, k, v, causal, mask, scale):
             for i in range(Lq):
                 p = S - Lq + i
                 vis = [j for j in range(S)
-                       if (not causal or j <= p) and (mask is None or mask[b, h, i, j])]
+                       if (not causal or j <= p) and (mask is None or mask[b, h, i, j])
+                       and (amask is None or amask[b, h, i, j] != -math.inf)]
                 if not vis:
                     continue
                 s = {j: float(Fraction(scale) * sum(Fraction(float(q[b, h, i, d])) * Fraction(float(k[b, g, j, d]))
                                                    for d in range(D))) for j in vis}
+                if amask is not None:
+                    s = {j: s[j] + float(amask[b, h, i, j]) for j in vis}
                 m = max(s.values())
+                extra = []
+                if sinks is not None:
+                    m = max(m, float(sinks[h]))
+                    extra = [math.exp(float(sinks[h]) - m)]
                 w = {j: math.exp(s[j] - m) for j in vis}
-                den = math.fsum(w.values())
+                den = math.fsum(list(w.values()) + extra)
                 for d in range(D):
                     out[b, h, i, d] = math.fsum(w[j] * float(v[b, g, j, d]) for j in vis) / den
     return out
@@ -258,12 +266,81 @@ def pin_sdpa_invariants():
     assert np.array_equal(oracle.sdpa(q, k, v, mask=mfull), m1)
 
 
+def pin_sdpa_additive_mask():
+    B, Hq, Hkv, Lq, S, D = 2, 4, 2, 3, 7, 5
+    q = synthetic.randn((B, Hq, Lq, D), 121)
+    k = synthetic.randn((B, Hkv, S, D), 122)
+    v = synthetic.randn((B, Hkv, S, D), 123)
+    qn, kn, vn = map(_vals, (q, k, v))
+    g = torch.Generator().manual_seed(124)
+    amask = (torch.randn((B, Hq, Lq, S), generator=g, dtype=torch.float64) * 2).numpy()
+    amask[0, 1, 2, [0, 3]] = -math.inf
+    amask[1, :, 0, :] = -math.inf                      # rows with no visible key
+    for causal in (False, True):
+        got = oracle.sdpa(q, k, v, causal=causal, mask=amask, scale=0.37)
+        ref = brute_sdpa(qn, kn, vn, causal, None, 0.37, amask=amask)
+        np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
+    assert np.array_equal(oracle.sdpa(q, k, v, mask=amask)[1, :, 0], np.zeros((Hq, D)))
+    # a mask of zeros is no mask; -inf where a boolean mask says no is that boolean mask
+    base = oracle.sdpa(q, k, v, causal=True)
+    assert np.array_equal(oracle.sdpa(q, k, v, causal=True, mask=np.zeros((1, 1, Lq, S))), base)
+    bm = (torch.rand((B, 1, Lq, S), generator=g) > 0.4).numpy()
+    assert np.array_equal(oracle.sdpa(q, k, v, mask=np.where(bm, 0.0, -math.inf)), oracle.sdpa(q, k, v, mask=bm))
+    # q = 0: every scaled score is 0, so the weights are exp(mask); with mask = log(w) they are w
+    w = synthetic.randint((1, 1, Lq, S), 125, 1, 9, torch.float64).numpy()
+    q0 = torch.zeros(1, Hq, Lq, D)
+    got = oracle.sdpa(q0, k[:1], v[:1], mask=np.log(w))
+    for h in range(Hq):
+        gk = (h * Hkv) // Hq
+        for i in range(Lq):
+            want = (w[0, 0, i][:, None] * vn[0, gk]).sum(axis=0) / w[0, 0, i].sum()
+            np.testing.assert_allclose(got[0, h, i], want, rtol=1e-13, atol=1e-14)
+    # a constant added to a whole row changes nothing; the mask broadcasts like the boolean one
+    shifted = amask + 5.25
+    np.testing.assert_allclose(oracle.sdpa(q, k, v, mask=shifted), oracle.sdpa(q, k, v, mask=amask),
+                               rtol=1e-12, atol=1e-13)
+    row = amask[:1, :1]
+    assert np.array_equal(oracle.sdpa(q, k, v, mask=row),
+                          oracle.sdpa(q, k, v, mask=np.broadcast_to(row, (B, Hq, Lq, S)).copy()))
+
+
+def pin_sdpa_sinks():
+    B, Hq, Hkv, Lq, S, D = 2, 4, 2, 3, 6, 5
+    q = synthetic.randn((B, Hq, Lq, D), 131)
+    k = synthetic.randn((B, Hkv, S, D), 132)
+    v = synthetic.randn((B, Hkv, S, D), 133)
+    qn, kn, vn = map(_vals, (q, k, v))
+    sinks = np.array([-0.5, 1.25, 0.0, 2.5])            # one per query head, all different
+    for causal in (False, True):
+        got = oracle.sdpa(q, k, v, causal=causal, scale=0.41, sinks=sinks)
+        ref = brute_sdpa(qn, kn, vn, causal, None, 0.41, sinks=sinks)
+        np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
+    # -inf sinks are no sinks
+    base = oracle.sdpa(q, k, v, causal=True)
+    assert np.array_equal(oracle.sdpa(q, k, v, causal=True, sinks=np.full(Hq, -math.inf)), base)
+    # q = 0, causal: row i sees n = S - Lq + i + 1 keys of weight 1 and the sink of weight e^sink
+    q0 = torch.zeros(1, Hq, Lq, D)
+    got = oracle.sdpa(q0, k[:1], v[:1], causal=True, sinks=sinks)
+    for h in range(Hq):
+        gk = (h * Hkv) // Hq
+        for i in range(Lq):
+            n = S - Lq + i + 1
+            want = vn[0, gk, :n].sum(axis=0) / (n + math.exp(sinks[h]))
+            np.testing.assert_allclose(got[0, h, i], want, rtol=1e-13, atol=1e-14)
+    # a dominant sink takes all the weight (exp(-1000) is 0 in float64); no visible key stays 0
+    assert np.array_equal(oracle.sdpa(q0, k[:1], v[:1], sinks=np.full(Hq, 1000.0)), np.zeros((1, Hq, Lq, D)))
+    none = np.zeros((1, 1, Lq, S), dtype=bool)
+    assert np.array_equal(oracle.sdpa(q, k, v, mask=none, sinks=sinks), np.zeros((B, Hq, Lq, D)))
+
+
 def pin_sdpa_golden():
     with open(GOLDEN) as f:
         cases = json.load(f)["sdpa"]
     for c in cases:
         got = oracle.sdpa(np.array(c["q"], float), np.array(c["k"], float), np.array(c["v"], float),
-                          causal=c["causal"], scale=c["scale"])
+                          causal=c["causal"], scale=c["scale"],
+                          mask=np.array(c["mask"], float) if "mask" in c else None,
+                          sinks=np.array(c["sinks"], float) if "sinks" in c else None)
         exp = np.array(c["expected"], float)
         if "rtol" in c:
             np.testing.assert_allclose(got, exp, rtol=c["rtol"], atol=0, err_msg=c["name"])
@@ -272,7 +349,7 @@ def pin_sdpa_golden():
 
 
 SDPA_PINS = [pin_sdpa_bruteforce, pin_sdpa_default_scale, pin_sdpa_closed_forms,
-             pin_sdpa_invariants, pin_sdpa_golden]
+             pin_sdpa_invariants, pin_sdpa_additive_mask, pin_sdpa_sinks, pin_sdpa_golden]
 
 
 def pin_rowsum_exact():
@@ -389,7 +466,12 @@ MUTANTS = {
     "sdpa_gqa_interleaved": ("const int64_t g = (h * Hkv) / Hq;", "const int64_t g = h % Hkv;", SDPA_PINS),
     "sdpa_unnormalised": ("orow[d] = num[d] / den;", "orow[d] = num[d];", SDPA_PINS),
     "sdpa_no_max_shift": ("exp(s[j] - m)", "exp(s[j])", SDPA_PINS),
-    "sdpa_scale_dropped": ("s[j] = scale * dot;", "s[j] = dot;", SDPA_PINS),
+    "sdpa_scale_dropped": ("s[j] = scale * dot + add;", "s[j] = dot + add;", SDPA_PINS),
+    "sdpa_additive_sign": ("s[j] = scale * dot + add;", "s[j] = scale * dot - add;", SDPA_PINS),
+    "sdpa_additive_key_index": ("i * as[2] + j * as[3]]", "i * as[2] + 0 * as[3]]", SDPA_PINS),
+    "sdpa_additive_inf_visible": ("if (add == -INFINITY) ok = 0;", "if (add != add) ok = 0;", SDPA_PINS),
+    "sdpa_sink_dropped": ("den = den + exp(sk - m);", "den = den;", SDPA_PINS),
+    "sdpa_sink_kv_head": ("const double sk = sinks[h];", "const double sk = sinks[g];", SDPA_PINS),
     "sdpa_mask_polarity": ("ms[3]] != 0;", "ms[3]] == 0;", SDPA_PINS),
     "sdpa_value_from_key": ("const double *vrow = v + b * vs[0] + g * vs[1] + j * vs[2];",
                             "const double *vrow = k + b * ks[0] + g * ks[1] + j * ks[2];", SDPA_PINS),
