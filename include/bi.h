@@ -152,7 +152,8 @@ bi_status bi_addmm(const void *cin, int64_t ldcin,
  *   is rounded once to dt.  For 16-bit dt the softmax weights are rounded
  *   to dt before the P.V product; fp32 keeps them in fp32.
  *
- * Supported: D in {64, 128}; Hq % Hkv == 0; Lq <= S when causal; every
+ * Supported: D a multiple of 32 up to 256 (README, section "Limitations":
+ * head dimensions must be multiples of 32); Hq % Hkv == 0; Lq <= S when causal; every
  * base pointer 16-byte aligned and every stride except the last a multiple
  * of 8 (16-bit) or 4 (fp32) elements.
  * Workspace: ws must hold bi_sdpa_workspace_bytes(B, Hq, Lq, S, D, dt) bytes,
@@ -177,6 +178,39 @@ bi_status bi_sdpa(const void *q, const int64_t q_str[4],
 /* Bytes of workspace bi_sdpa needs for these sizes and dtype (0 when there is
  * nothing to do, when the path taken needs none, or for an unknown dtype). */
 size_t bi_sdpa_workspace_bytes(int64_t B, int64_t Hq, int64_t Lq, int64_t S, int64_t D, bi_dtype dt);
+
+/*
+ * bi_sdpa with every mask form and attention sinks (README, section "How the
+ * kernels work", attention paragraph: the mask forms of the single-pass
+ * kernel; section "Limitations": attention sinks).  Arguments as bi_sdpa,
+ * plus:
+ *   mask_kind: BI_MASK_NONE (mask ignored), BI_MASK_BOOL (uint8, nonzero =
+ *     may attend) or BI_MASK_ADD (elements of dt, added to the scaled scores;
+ *     -inf removes the key, a finite value weights it by exp(value));
+ *     element strides mask_str[0..3] over (B, Hq, Lq, S), 0 broadcasts.
+ *   sinks: NULL, or Hq fp32 logits in device memory, one per query head: an
+ *     extra softmax term on the scale of the scaled scores that carries no
+ *     value, so a query's weights sum to less than one.
+ * Arithmetic, in the exp2 domain of the bi_sdpa contract: an additive value
+ * a turns a key's score into fmaf(a, log2e, S * c) (c = scale * log2e,
+ * log2e rounded to fp32); a sink enters every fold of split partials as its
+ * first partial, (m, l, O) = (sink * log2e, 1, 0), before split 0.  Keys
+ * masked with -inf, like keys masked by a boolean mask, are identity steps,
+ * so appending them never changes an earlier result.  A query that sees no
+ * key produces zeros, with or without a sink.  Workspace as bi_sdpa.
+ */
+typedef enum { BI_MASK_NONE = 0, BI_MASK_BOOL = 1, BI_MASK_ADD = 2 } bi_mask_kind;
+bi_status bi_sdpa_ex(const void *q, const int64_t q_str[4],
+                     const void *k, const int64_t k_str[4],
+                     const void *v, const int64_t v_str[4],
+                     void *o, const int64_t o_str[4],
+                     int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t S, int64_t D,
+                     float scale, int causal,
+                     int mask_kind, const void *mask, const int64_t mask_str[4],
+                     const float *sinks,
+                     bi_dtype dt,
+                     void *ws, size_t ws_bytes,
+                     void *stream);
 
 /*
  * Batch-VARIANT comparator, for measurement only.  It runs the same
@@ -273,7 +307,7 @@ const char *bi_gemm_kernel_name(int64_t M, int64_t N, int64_t K, bi_dtype in_dt,
 /* Which attention kernels a bi_sdpa call of these sizes runs: "sdpa_prefill16"
  * (16-bit, D = 128, Lq >= 384), "sdpa_fused16" (16-bit, D = 128, Lq < 384,
  * S <= 1024), "sdpa_split16+combine" (other 16-bit D = 128 calls) or
- * "sdpa_split+combine" (fp32, D = 64).  Informational: the split / block
+ * "sdpa_split+combine" (fp32, and every other head dim).  Informational: the split / block
  * structure, and with it every output bit, is the same whichever runs.
  * Returns "none" for empty, oversized or unsupported sizes. */
 const char *bi_sdpa_kernel_name(int64_t B, int64_t Hq, int64_t Lq, int64_t S, int64_t D, bi_dtype dt);

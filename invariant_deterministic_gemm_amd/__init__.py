@@ -234,10 +234,17 @@ def _mask_strides(mask: torch.Tensor, shape) -> tuple:
     return m, st
 
 
+MASK_NONE, MASK_BOOL, MASK_ADD = 0, 1, 2
+
+
 def bi_sdpa(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
             mask: torch.Tensor | None = None, scale: float | None = None,
-            workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """Softmax attention, q (B, Hq, Lq, D), k / v (B, Hkv, S, D), bottom-right causal, bool mask."""
+            workspace: torch.Tensor | None = None, sinks: torch.Tensor | None = None) -> torch.Tensor:
+    """Softmax attention, q (B, Hq, Lq, D), k / v (B, Hkv, S, D), bottom-right causal.
+
+    mask: boolean (True = attend) or additive in q's dtype (added to the scaled scores, -inf removes
+    a key), broadcastable to (B, Hq, Lq, S).  sinks: None or Hq logits, one extra softmax term per
+    query head that carries no value (bi.h, bi_sdpa_ex)."""
     dev = _on_gpu(q, k, v, mask)
     if not (q.dtype == k.dtype == v.dtype):
         raise ValueError("q, k, v must share a dtype")
@@ -253,24 +260,34 @@ def bi_sdpa(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fa
     ks = k if k.stride(-1) == 1 else k.contiguous()
     vs = v if v.stride(-1) == 1 else v.contiguous()
     o = torch.empty((B, Hq, Lq, D), dtype=q.dtype, device=dev)
-    mptr, mstr = None, None
+    mptr, mstr, kind = None, None, MASK_NONE
     m8 = None
     if mask is not None:
-        if mask.dtype not in (torch.bool, torch.uint8):
-            raise NotImplementedError("only boolean masks are supported")
-        m8, st = _mask_strides(mask.to(torch.uint8) if mask.dtype == torch.bool else mask, (B, Hq, Lq, S))
+        if mask.dtype in (torch.bool, torch.uint8):
+            m8, st = _mask_strides(mask.to(torch.uint8) if mask.dtype == torch.bool else mask, (B, Hq, Lq, S))
+            kind = MASK_BOOL
+        elif mask.dtype == q.dtype:
+            m8, st = _mask_strides(mask, (B, Hq, Lq, S))
+            kind = MASK_ADD
+        else:
+            raise ValueError("an additive mask must have q's dtype (or use a boolean mask)")
         mptr, mstr = _ptr(m8), _native.i64x4(st)
+    sk = None
+    if sinks is not None:
+        if torch.as_tensor(sinks).numel() != Hq:
+            raise ValueError("sinks must hold one logit per query head")
+        sk = torch.as_tensor(sinks).reshape(Hq).to(device=dev, dtype=torch.float32).contiguous()
     lib = _native.load()
     need = int(lib.bi_sdpa_workspace_bytes(B, Hq, Lq, S, D, _dt(q, "bi_sdpa")))
     ws = workspace
     if need > 0 and (ws is None or ws.numel() * ws.element_size() < need):
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
-    st = lib.bi_sdpa(_ptr(qs), _native.i64x4(qs.stride()), _ptr(ks), _native.i64x4(ks.stride()),
-                     _ptr(vs), _native.i64x4(vs.stride()), _ptr(o), _native.i64x4(o.stride()),
-                     B, Hq, Hkv, Lq, S, D, float(scale), 1 if causal else 0, mptr, mstr,
-                     _dt(q, "bi_sdpa"), _ptr(ws) if ws is not None else None,
-                     need if ws is not None else 0, _stream(dev))
-    _check(st, "bi_sdpa")
+    st = lib.bi_sdpa_ex(_ptr(qs), _native.i64x4(qs.stride()), _ptr(ks), _native.i64x4(ks.stride()),
+                        _ptr(vs), _native.i64x4(vs.stride()), _ptr(o), _native.i64x4(o.stride()),
+                        B, Hq, Hkv, Lq, S, D, float(scale), 1 if causal else 0, kind, mptr, mstr, _ptr(sk),
+                        _dt(q, "bi_sdpa"), _ptr(ws) if ws is not None else None,
+                        need if ws is not None else 0, _stream(dev))
+    _check(st, "bi_sdpa_ex")
     return o
 
 
@@ -379,13 +396,14 @@ def bi_quantized_linear(x: torch.Tensor, wq: torch.Tensor, scales: torch.Tensor,
     return y.reshape(*lead, N)
 
 
-def scaled_dot_product_attention(q, k, v, mask=None, scale=None):
-    """README-style call: mask is None, "causal" or a boolean tensor."""
+def scaled_dot_product_attention(q, k, v, mask=None, scale=None, sinks=None):
+    """README-style call: mask is None, "causal", a boolean tensor or an additive tensor; sinks
+    optional (one logit per query head)."""
     if isinstance(mask, str):
         if mask != "causal":
-            raise ValueError("mask must be None, 'causal' or a boolean tensor")
-        return bi_sdpa(q, k, v, causal=True, scale=scale)
-    return bi_sdpa(q, k, v, causal=False, mask=mask, scale=scale)
+            raise ValueError("mask must be None, 'causal' or a tensor")
+        return bi_sdpa(q, k, v, causal=True, scale=scale, sinks=sinks)
+    return bi_sdpa(q, k, v, causal=False, mask=mask, scale=scale, sinks=sinks)
 
 
 # README, section "Use": route the framework's matmul and attention through these kernels.

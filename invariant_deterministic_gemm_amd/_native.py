@@ -27,6 +27,8 @@ SIGNATURES = {
     "bi_addmm": (_i, [_p, _i64, _p, _i64, _p, _i64, _i64, _p, _i64, _i64, _i64, _i64, _f, _f, _i, _i, _p]),
     "bi_sdpa": (_i, [_p, _i64p, _p, _i64p, _p, _i64p, _p, _i64p, _i64, _i64, _i64, _i64, _i64, _i64,
                      _f, _i, _p, _i64p, _i, _p, _sz, _p]),
+    "bi_sdpa_ex": (_i, [_p, _i64p, _p, _i64p, _p, _i64p, _p, _i64p, _i64, _i64, _i64, _i64, _i64, _i64,
+                        _f, _i, _i, _p, _i64p, _p, _i, _p, _sz, _p]),
     "bi_sdpa_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64, _i]),
     "bi_rowsum": (_i, [_p, _i64, _p, _i64, _i64, _i, _i, _p]),
     "bi_quantized_linear": (_i, [_p, _i64, _p, _i64, _p, _p, _i64, _i, _i64, _p, _p, _i64, _i64, _i64, _i64, _i,

@@ -208,12 +208,18 @@ size_t bi_sdpa_workspace_bytes(int64_t B, int64_t Hq, int64_t Lq, int64_t S, int
     return bi::sdpa_workspace_bytes(B, Hq, Lq, S, D, (int)dt);
 }
 
-bi_status bi_sdpa(const void *q, const int64_t q_str[4], const void *k, const int64_t k_str[4], const void *v,
-                  const int64_t v_str[4], void *o, const int64_t o_str[4], int64_t B, int64_t Hq, int64_t Hkv,
-                  int64_t Lq, int64_t S, int64_t D, float scale, int causal, const uint8_t *mask,
-                  const int64_t mask_str[4], bi_dtype dt, void *ws, size_t ws_bytes, void *stream) {
-    const char *fn = "bi_sdpa";
+static bi_status sdpa_impl(const char *fn, const void *q, const int64_t q_str[4], const void *k,
+                           const int64_t k_str[4], const void *v, const int64_t v_str[4], void *o,
+                           const int64_t o_str[4], int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t S,
+                           int64_t D, float scale, int causal, int mask_kind, const void *mask,
+                           const int64_t mask_str[4], const float *sinks, bi_dtype dt, void *ws, size_t ws_bytes,
+                           void *stream) {
     if (!dtype_known(dt)) return fail(BI_ERR_INVALID, "%s: unknown dtype code %d", fn, (int)dt);
+    if (mask_kind != BI_MASK_NONE && mask_kind != BI_MASK_BOOL && mask_kind != BI_MASK_ADD)
+        return fail(BI_ERR_INVALID, "%s: unknown mask kind %d", fn, mask_kind);
+    if (mask_kind == BI_MASK_NONE) mask = nullptr;
+    if (mask_kind != BI_MASK_NONE && mask == nullptr)
+        return fail(BI_ERR_INVALID, "%s: mask kind %d with a null mask", fn, mask_kind);
     if (B < 0 || Hq < 0 || Hkv <= 0 || Lq < 0 || S < 0 || D <= 0)
         return fail(BI_ERR_INVALID, "%s: bad sizes B=%lld Hq=%lld Hkv=%lld Lq=%lld S=%lld D=%lld", fn,
                     (long long)B, (long long)Hq, (long long)Hkv, (long long)Lq, (long long)S, (long long)D);
@@ -222,8 +228,9 @@ bi_status bi_sdpa(const void *q, const int64_t q_str[4], const void *k, const in
     if (causal && Lq > S)
         return fail(BI_ERR_INVALID, "%s: causal attention needs Lq <= S (Lq=%lld, S=%lld)", fn, (long long)Lq,
                     (long long)S);
-    if (D != 64 && D != 128)
-        return fail(BI_ERR_UNSUPPORTED, "%s: head dim %lld not supported (64 or 128)", fn, (long long)D);
+    if (D % 32 != 0 || D > 256)
+        return fail(BI_ERR_UNSUPPORTED, "%s: head dim %lld not supported (a multiple of 32 up to 256)", fn,
+                    (long long)D);
     if (!std::isfinite(scale)) return fail(BI_ERR_INVALID, "%s: scale must be finite", fn);
     if (B == 0 || Hq == 0 || Lq == 0) return ok();
     if (!q_str || !k_str || !v_str || !o_str) return fail(BI_ERR_INVALID, "%s: stride array is null", fn);
@@ -250,7 +257,10 @@ bi_status bi_sdpa(const void *q, const int64_t q_str[4], const void *k, const in
         if (!mask_str) return fail(BI_ERR_INVALID, "%s: mask strides are null", fn);
         for (int d = 0; d < 4; ++d)
             if (mask_str[d] < 0) return fail(BI_ERR_INVALID, "%s: negative mask stride", fn);
+        if (mask_kind == BI_MASK_ADD && !aligned_to(mask, esize(dt)))
+            return fail(BI_ERR_UNSUPPORTED, "%s: additive mask misaligned for its dtype", fn);
     }
+    if (sinks != nullptr && !aligned_to(sinks, 4)) return fail(BI_ERR_UNSUPPORTED, "%s: sinks misaligned", fn);
     const size_t need = bi::sdpa_workspace_bytes(B, Hq, Lq, S, D, (int)dt);
     if (need > 0 && (ws == nullptr || ws_bytes < need))
         return fail(BI_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
@@ -269,7 +279,9 @@ bi_status bi_sdpa(const void *q, const int64_t q_str[4], const void *k, const in
         p.os[d] = o_str[d];
     }
     p.mask = mask;
+    p.mask_add = mask_kind == BI_MASK_ADD ? 1 : 0;
     for (int d = 0; d < 4; ++d) p.ms[d] = mask ? mask_str[d] : 0;
+    p.sinks = sinks;
     p.B = (int)B;
     p.Hq = (int)Hq;
     p.Hkv = (int)Hkv;
@@ -281,6 +293,23 @@ bi_status bi_sdpa(const void *q, const int64_t q_str[4], const void *k, const in
     p.nsplit = (int)((S + bi::KV_SPLIT - 1) / bi::KV_SPLIT);
     if (need > 0) bi::sdpa_bind_workspace(p, ws);
     return device_status(bi::launch_sdpa(p, dt, (int)D, (hipStream_t)stream), fn);
+}
+
+bi_status bi_sdpa(const void *q, const int64_t q_str[4], const void *k, const int64_t k_str[4], const void *v,
+                  const int64_t v_str[4], void *o, const int64_t o_str[4], int64_t B, int64_t Hq, int64_t Hkv,
+                  int64_t Lq, int64_t S, int64_t D, float scale, int causal, const uint8_t *mask,
+                  const int64_t mask_str[4], bi_dtype dt, void *ws, size_t ws_bytes, void *stream) {
+    return sdpa_impl("bi_sdpa", q, q_str, k, k_str, v, v_str, o, o_str, B, Hq, Hkv, Lq, S, D, scale, causal,
+                     mask ? BI_MASK_BOOL : BI_MASK_NONE, mask, mask_str, nullptr, dt, ws, ws_bytes, stream);
+}
+
+bi_status bi_sdpa_ex(const void *q, const int64_t q_str[4], const void *k, const int64_t k_str[4], const void *v,
+                     const int64_t v_str[4], void *o, const int64_t o_str[4], int64_t B, int64_t Hq, int64_t Hkv,
+                     int64_t Lq, int64_t S, int64_t D, float scale, int causal, int mask_kind, const void *mask,
+                     const int64_t mask_str[4], const float *sinks, bi_dtype dt, void *ws, size_t ws_bytes,
+                     void *stream) {
+    return sdpa_impl("bi_sdpa_ex", q, q_str, k, k_str, v, v_str, o, o_str, B, Hq, Hkv, Lq, S, D, scale, causal,
+                     mask_kind, mask, mask_str, sinks, dt, ws, ws_bytes, stream);
 }
 
 int bi_variant_splits(int64_t M) {
@@ -398,7 +427,7 @@ const char *bi_gemm_kernel_name(int64_t M, int64_t N, int64_t K, bi_dtype in_dt,
 
 const char *bi_sdpa_kernel_name(int64_t B, int64_t Hq, int64_t Lq, int64_t S, int64_t D, bi_dtype dt) {
     if (B <= 0 || Hq <= 0 || Lq <= 0 || S <= 0 || B > kMaxDim || Hq > kMaxDim || Lq > kMaxDim || S > kMaxDim ||
-        (D != 64 && D != 128) || !dtype_known(dt))
+        (D <= 0 || D % 32 != 0 || D > 256) || !dtype_known(dt))
         return "none";
     return bi::sdpa_kernel_name(Lq, S, D, (int)dt);
 }

@@ -15,8 +15,10 @@ struct SdpaParams {
     const void *q, *k, *v;
     void *o;
     int64_t qs[3], ks[3], vs[3], os[3];   // element strides of dims 0..2 (dim 3 is contiguous)
-    const uint8_t *mask;                  // nullable
-    int64_t ms[4];
+    const void *mask;                     // nullable: uint8 (nonzero = attend) or, with mask_add, dt values
+    int64_t ms[4];                        // element strides of the mask
+    int mask_add;                         // the mask is additive (dt, added to the scaled scores)
+    const float *sinks;                   // nullable: Hq logits, one extra softmax term per query head
     int B, Hq, Hkv, Lq, S, G;             // G = Hq / Hkv
     int causal;
     float c;                              // scale * log2(e), rounded once to fp32

@@ -66,6 +66,32 @@ __device__ __forceinline__ f32x4 attn_mfma_chunk(u32x4 a, u32x4 b, f32x4 c) {
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// log2(e) rounded to fp32: additive mask values and sink logits move to the exp2 domain with it
+constexpr float LOG2E_F = 1.44269504088896340736f;
+
+// The mask row of query row (b, h, iq): byte pointer to its element for key 0, or null.
+__device__ __forceinline__ const char *mask_row(const SdpaParams &p, int b, int h, int iq, int eb) {
+    if (p.mask == nullptr) return nullptr;
+    const int64_t e = (int64_t)b * p.ms[0] + (int64_t)h * p.ms[1] + (int64_t)iq * p.ms[2];
+    return static_cast<const char *>(p.mask) + e * (p.mask_add ? eb : 1);
+}
+// Score of one key in the exp2 domain: s = S * c, or fmaf(a, log2 e, S * c) with the additive mask
+// value a of the key (-inf removes it); ok: the key passes causality, the end of the cache and a
+// boolean mask.  Invisible keys score -inf.
+template <int dt>
+__device__ __forceinline__ float masked_score(const SdpaParams &p, const char *mrow, int key, bool ok, float sdot) {
+    const float sv = sdot * p.c;
+    if (mrow == nullptr) return ok ? sv : -__builtin_huge_valf();
+    if (p.mask_add) {
+        const float a = load_as_f32<dt>(mrow, (int64_t)key * p.ms[3]);
+        return ok ? __builtin_fmaf(a, LOG2E_F, sv) : -__builtin_huge_valf();
+    }
+    return ok && reinterpret_cast<const uint8_t *>(mrow)[(int64_t)key * p.ms[3]] != 0 ? sv : -__builtin_huge_valf();
+}
+// The sink of query head h in the exp2 domain, as the first partial of every fold: (m, l, O) =
+// (sink * log2 e, 1, 0).
+__device__ __forceinline__ float sink2(const SdpaParams &p, int h) { return p.sinks[h] * LOG2E_F; }
+
 // x op x[lane ^ 16] and x op x[lane ^ 32] for a commutative op, through the VALU lane swaps (no
 // LDS round trip): a swap of x with itself leaves one lane of each pair holding both values, the
 // other lane the same two in the other order, which a commutative op does not see.
@@ -137,8 +163,7 @@ __global__ __launch_bounds__(64) void sdpa_split(SdpaParams p) {
                        ((int64_t)b * p.qs[0] + (int64_t)h * p.qs[1] + (int64_t)iq * p.qs[2]) * A::EB;
     const char *kbase = static_cast<const char *>(p.k) + ((int64_t)b * p.ks[0] + (int64_t)gk * p.ks[1]) * A::EB;
     const char *vbase = static_cast<const char *>(p.v) + ((int64_t)b * p.vs[0] + (int64_t)gk * p.vs[1]) * A::EB;
-    const uint8_t *mrow = p.mask ? p.mask + (int64_t)b * p.ms[0] + (int64_t)h * p.ms[1] + (int64_t)iq * p.ms[2]
-                                 : nullptr;
+    const char *mrow = mask_row(p, b, h, iq, A::EB);
 
     u32x4 qf[A::NCH];
 #pragma unroll
@@ -200,9 +225,7 @@ __global__ __launch_bounds__(64) void sdpa_split(SdpaParams p) {
                 const int key = kb + 16 * kt + 4 * g + i;
                 bool ok = row_ok && key < p.S;
                 if (p.causal) ok = ok && key <= pos;
-                if (mrow) ok = ok && mrow[(int64_t)key * p.ms[3]] != 0;
-                const float sv = st[kt][i] * p.c;
-                s[kt][i] = ok ? sv : NEG_INF;
+                s[kt][i] = masked_score<dt>(p, mrow, min(key, p.S - 1), ok, st[kt][i]);
                 mb = fmaxf(mb, s[kt][i]);
             }
         mb = max_xor32(max_xor16(mb));
@@ -324,7 +347,7 @@ struct Rows16 {
     bool row_ok;            // score row r16 is a real row (rows past R are computed and never stored)
     int pos;                // its key position (bottom-right alignment)
     int pos_first;          // key position of the tile's first row, the smallest in the tile
-    const uint8_t *mrow;    // its mask row, or null
+    const char *mrow;       // its mask row, or null
     u32x4 qf[4];            // its q fragments (d chunks 32 c + 8 g .. + 7)
 };
 
@@ -340,7 +363,7 @@ __device__ __forceinline__ void rows16_load(const SdpaParams &p, int tile, int b
     const int h = gk * p.G + rgc % p.G;
     r.pos = p.S - p.Lq + iq;
     r.pos_first = p.S - p.Lq + (tile * 16) / p.G;
-    r.mrow = p.mask ? p.mask + (int64_t)b * p.ms[0] + (int64_t)h * p.ms[1] + (int64_t)iq * p.ms[2] : nullptr;
+    r.mrow = mask_row(p, b, h, iq, 2);
     const char *qrow = static_cast<const char *>(p.q) +
                        ((int64_t)b * p.qs[0] + (int64_t)h * p.qs[1] + (int64_t)iq * p.qs[2]) * 2;
 #pragma unroll
@@ -408,9 +431,7 @@ __device__ __forceinline__ void attn_update16(const SdpaParams &p, const Rows16 
                 const int key = kb + 16 * kt + 4 * g + i;
                 bool ok = r.row_ok && key < p.S;
                 if (p.causal) ok = ok && key <= r.pos;
-                if (r.mrow) ok = ok && r.mrow[(int64_t)key * p.ms[3]] != 0;
-                const float sv = st[kt][i] * p.c;
-                s[kt][i] = ok ? sv : NEG_INF;
+                s[kt][i] = masked_score<dt>(p, r.mrow, min(key, p.S - 1), ok, st[kt][i]);
             }
         mb = lane_max();
     }
@@ -673,8 +694,14 @@ __global__ __launch_bounds__(64 * FUSED_MAXW) void sdpa_fused16(SdpaParams p) {
         const int row = e / D, d = e % D;
         const int ro = tile * 16 + row;
         if (ro >= R) continue;
+        const int iq = ro / p.G, h = gk * p.G + ro % p.G;
         bool have = false;
         float m = 0.0f, l = 0.0f, acc = 0.0f;
+        if (p.sinks) {                               // the sink is the fold's first partial
+            m = sink2(p, h);
+            l = 1.0f;
+            have = true;
+        }
         for (int sp = 0; sp < nw; ++sp) {
             const float ms = pml[(sp * 16 + row) * 2], ls = pml[(sp * 16 + row) * 2 + 1];
             if (ms == NEG_INF) continue;
@@ -695,7 +722,6 @@ __global__ __launch_bounds__(64 * FUSED_MAXW) void sdpa_fused16(SdpaParams p) {
         }
         float r = have ? acc / l : 0.0f;
         r = r + 0.0f;                                // -0 -> +0
-        const int iq = ro / p.G, h = gk * p.G + ro % p.G;
         char *orow = static_cast<char *>(p.o) +
                      ((int64_t)b * p.os[0] + (int64_t)h * p.os[1] + (int64_t)iq * p.os[2]) * Elem<dt>::bytes;
         store_from_f32<dt>(orow, d, r);
@@ -789,9 +815,16 @@ __global__ __launch_bounds__(64 * W) void sdpa_prefill16(SdpaParams p) {
 
     Rows16 r;
     rows16_load<dt>(p, tile, b, gk, r);
-    // running fold over splits (per score row in lane r16) and the current split's state
+    // running fold over splits (per score row in lane r16) and the current split's state; the sink,
+    // if any, is the fold's first partial
     bool have = false;
     float mt = 0.0f, lt = 0.0f;
+    if (p.sinks) {
+        const int rgc = min(tile * 16 + r16, R - 1);
+        mt = sink2(p, gk * p.G + rgc % p.G);
+        lt = 1.0f;
+        have = true;
+    }
     f32x4 ot[8];
     float m_run = NEG_INF, l_run = 0.0f;
     f32x4 o[8];
@@ -897,6 +930,11 @@ __global__ __launch_bounds__(D) void sdpa_combine(SdpaParams p) {
 
     bool have = false;
     float m = 0.0f, l = 0.0f, o = 0.0f;
+    if (p.sinks) {                                 // the sink is the fold's first partial
+        m = sink2(p, h);
+        l = 1.0f;
+        have = true;
+    }
     for (int s0 = 0; s0 < p.nsplit; s0 += CH) {
         float ms[CH], ls[CH], os[CH];
 #pragma unroll
@@ -1005,13 +1043,25 @@ const char *sdpa_kernel_name(int64_t Lq, int64_t S, int64_t D, int dt) {
     }
 }
 
+template <int dt>
+static hipError_t launch_d(const SdpaParams &p, int D, hipStream_t st) {
+    switch (D) {
+        case 32: return launch_typed<dt, 32>(p, st);
+        case 64: return launch_typed<dt, 64>(p, st);
+        case 96: return launch_typed<dt, 96>(p, st);
+        case 128: return launch_typed<dt, 128>(p, st);
+        case 160: return launch_typed<dt, 160>(p, st);
+        case 192: return launch_typed<dt, 192>(p, st);
+        case 224: return launch_typed<dt, 224>(p, st);
+        case 256: return launch_typed<dt, 256>(p, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 hipError_t launch_sdpa(const SdpaParams &p, int dt, int D, hipStream_t st) {
-    if (dt == DT_BF16 && D == 128) return launch_typed<DT_BF16, 128>(p, st);
-    if (dt == DT_BF16 && D == 64) return launch_typed<DT_BF16, 64>(p, st);
-    if (dt == DT_F16 && D == 128) return launch_typed<DT_F16, 128>(p, st);
-    if (dt == DT_F16 && D == 64) return launch_typed<DT_F16, 64>(p, st);
-    if (dt == DT_F32 && D == 128) return launch_typed<DT_F32, 128>(p, st);
-    if (dt == DT_F32 && D == 64) return launch_typed<DT_F32, 64>(p, st);
+    if (dt == DT_BF16) return launch_d<DT_BF16>(p, D, st);
+    if (dt == DT_F16) return launch_d<DT_F16>(p, D, st);
+    if (dt == DT_F32) return launch_d<DT_F32>(p, D, st);
     return hipErrorInvalidValue;
 }
 

@@ -29,8 +29,9 @@ Not routed (raises NotImplementedError when strict; runs stock PyTorch and
 is counted otherwise): dtypes other than fp32 / fp16 / bf16, mixed dtypes,
 inputs that require gradients while grad mode is on (the kernels are
 forward-only), out= arguments, broadcast batch dims in a matmul, attention
-with dropout, a float (additive) mask, head dims other than 64 / 128, a
-causal flag together with a mask, and anything the library itself refuses
+with dropout, a float mask of another dtype than the query, head dims that
+are not a multiple of 32 up to 256, a causal flag together with a mask, and
+anything the library itself refuses
 (for example K not a multiple of 8 for 16-bit inputs).  torch's is_causal
 aligns the mask to the top-left corner; it is passed on as the library's
 causal flag when the query and key lengths are equal (the two alignments
@@ -153,13 +154,15 @@ def _sdpa(query, key, value, attn_mask=None, dropout_p=0.0, is_causal=False, sca
     _check_tensors(q, k, v)
     _need(dropout_p == 0.0, "dropout")
     _need(q.dim() == 4 and k.dim() == 4 and v.dim() == 4, "q, k, v must be 4-D")
-    _need(q.shape[-1] in (64, 128) and k.shape[-1] == q.shape[-1] and v.shape[-1] == q.shape[-1], "head dim")
+    D = q.shape[-1]
+    _need(D % 32 == 0 and 0 < D <= 256 and k.shape[-1] == D and v.shape[-1] == D, "head dim")
     Hq, Hkv = q.shape[1], k.shape[1]
     _need(Hq == Hkv or (enable_gqa and Hq % Hkv == 0), "query / key head counts")
     Lq, S = q.shape[2], k.shape[2]
     if attn_mask is not None:
         _need(not is_causal, "causal flag together with a mask")
-        _need(attn_mask.dtype == torch.bool, "float (additive) mask")
+        # torch adds a float mask to the scaled scores, as the library's additive form does
+        _need(attn_mask.dtype == torch.bool or attn_mask.dtype == q.dtype, "mask of another dtype than q")
         return bi_sdpa(q, k, v, mask=attn_mask, scale=scale)
     if is_causal:
         if Lq == S:

@@ -114,8 +114,11 @@ def sdpa(lib, B=1, Hq=4, Hkv=2, Lq=1, S=16, D=128, dt=BF16, causal=1, ws=P16, ws
 def test_sdpa_validation(lib):
     assert sdpa(lib, Hq=6, Hkv=4) == INVALID
     assert sdpa(lib, Hkv=0) == INVALID
-    assert sdpa(lib, D=96) == UNSUPPORTED               # head dims 64 and 128 only
-    assert sdpa(lib, D=32) == UNSUPPORTED
+    assert sdpa(lib, D=48) == UNSUPPORTED               # head dims: multiples of 32 up to 256
+    assert sdpa(lib, D=288) == UNSUPPORTED
+    assert sdpa(lib, D=0) == INVALID
+    for D in (32, 96, 160, 256):                          # accepted: they stop at the missing workspace
+        assert sdpa(lib, D=D, ws=None) == WORKSPACE, D
     assert sdpa(lib, Lq=17, S=16, causal=1) == INVALID  # causal needs Lq <= S
     assert sdpa(lib, dt=9) == INVALID
     assert sdpa(lib, scale=float("inf")) == INVALID
@@ -133,6 +136,28 @@ def test_sdpa_validation(lib):
     assert sdpa(lib, qstr=bad) == UNSUPPORTED
     assert sdpa(lib, B=0) == OK
     assert sdpa(lib, Lq=0) == OK
+
+
+def sdpa_ex(lib, kind=0, mask=None, mstr=None, sinks=None, dt=BF16, ws=None, D=64):
+    B, Hq, Hkv, Lq, S = 1, 4, 2, 1, 16
+    qs, kv = strides((B, Hq, Lq, D)), strides((B, Hkv, S, D))
+    return lib.bi_sdpa_ex(P16, qs, P16b, kv, P16b, kv, P16, strides((B, Hq, Lq, D)), B, Hq, Hkv, Lq, S, D,
+                          0.125, 1, kind, mask, mstr, sinks, dt, ws, 0, None)
+
+
+def test_sdpa_ex_validation(lib):
+    m4 = strides((1, 1, 1, 16))
+    assert sdpa_ex(lib, kind=3, mask=P16, mstr=m4) == INVALID                   # unknown mask kind
+    assert sdpa_ex(lib, kind=1, mask=None, mstr=m4) == INVALID                  # kind without a mask
+    assert sdpa_ex(lib, kind=2, mask=ctypes.c_void_p(0x7f0000000001), mstr=m4) == UNSUPPORTED   # bf16 alignment
+    assert sdpa_ex(lib, sinks=ctypes.c_void_p(0x7f0000000002)) == UNSUPPORTED  # fp32 sinks alignment
+    neg = strides((1, 1, 1, 16))
+    neg[3] = -1
+    assert sdpa_ex(lib, kind=2, mask=P16, mstr=neg) == INVALID
+    # every form accepted together (D = 64 runs the split path: stops at the missing workspace)
+    assert sdpa_ex(lib, kind=2, mask=P16, mstr=m4, sinks=P16b) == WORKSPACE
+    assert sdpa_ex(lib, kind=1, mask=P16, mstr=m4, sinks=P16b, dt=F32) == WORKSPACE
+    assert sdpa_ex(lib, kind=0, mask=ctypes.c_void_p(0x7f0000000001), mstr=None) == WORKSPACE   # mask ignored
 
 
 def test_sdpa_workspace_formula(lib):
@@ -183,8 +208,9 @@ def test_kernel_name_queries(lib):
     assert lib.bi_sdpa_kernel_name(1, 32, 383, 1024, 128, BF16).decode() == "sdpa_fused16"
     assert lib.bi_sdpa_kernel_name(1, 32, 1, 300, 128, F32).decode() == "sdpa_split+combine"
     assert lib.bi_sdpa_kernel_name(1, 32, 1, 300, 64, BF16).decode() == "sdpa_split+combine"
-    for bad in ((0, 32, 1, 10, 128, BF16), (1, 32, 1, 0, 128, BF16), (1, 32, 1, 10, 96, BF16),
-                (1, 32, 1, 10, 128, 7)):
+    assert lib.bi_sdpa_kernel_name(1, 32, 1, 300, 96, BF16).decode() == "sdpa_split+combine"
+    for bad in ((0, 32, 1, 10, 128, BF16), (1, 32, 1, 0, 128, BF16), (1, 32, 1, 10, 80, BF16),
+                (1, 32, 1, 10, 288, BF16), (1, 32, 1, 10, 128, 7)):
         assert lib.bi_sdpa_kernel_name(*bad).decode() == "none"
     assert lib.bi_gemm_kernel_name(1, 4096, 4096, BF16, 0).decode().startswith("gemm16_strip_nk/")
     assert lib.bi_gemm_kernel_name(4096, 4096, 4096, BF16, 0).decode().startswith("gemm16_ring_nk/")

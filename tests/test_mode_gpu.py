@@ -89,12 +89,26 @@ def test_sdpa_routing_keeps_torch_semantics():
     kr, vr = k.float().repeat_interleave(4, 1), v.float().repeat_interleave(4, 1)
     ref = F.scaled_dot_product_attention(q[:, :, :9].float(), kr, vr, attn_mask=tri, scale=0.1)
     assert (tl.float() - ref).abs().max() / ref.abs().max() < 2e-2
+    # a float mask of q's dtype is added to the scaled scores, torch's meaning and the library's
+    # additive form; other head dims that are multiples of 32 are routed too
+    amask = (torch.randn(2, 1, 40, 40, device=DEV) * 2).to(torch.bfloat16)
+    amask[..., 5] = float("-inf")
+    q96, k96, v96 = _r((1, 4, 12, 96), 24), _r((1, 2, 40, 96), 25), _r((1, 2, 40, 96), 26)
+    with bi.batch_invariant_mode() as m:
+        added = F.scaled_dot_product_attention(q, k, v, attn_mask=amask, enable_gqa=True)
+        d96 = F.scaled_dot_product_attention(q96, k96, v96, enable_gqa=True)
+    assert not m.fallbacks, dict(m.fallbacks)
+    assert_bits_equal(added, bi.bi_sdpa(q, k, v, mask=amask), "additive mask")
+    assert_bits_equal(d96, bi.bi_sdpa(q96, k96, v96), "head dim 96")
+    ref = F.scaled_dot_product_attention(q.float(), k.float().repeat_interleave(4, 1),
+                                         v.float().repeat_interleave(4, 1), attn_mask=amask.float())
+    assert (added.float() - ref).abs().max() / ref.abs().max() < 2e-2
 
 
 def test_strict_mode_raises_and_lenient_mode_falls_back():
     x64 = torch.randn(4, 16, dtype=torch.float64, device=DEV)
     xb, wb = _r((4, 64), 31), _r((8, 64), 32)
-    q = _r((1, 4, 8, 64), 33)
+    q = _r((1, 4, 8, 48), 33)                                 # head dim not a multiple of 32
     fmask = torch.zeros(1, 1, 8, 8, device=DEV, dtype=torch.bfloat16)
     with bi.batch_invariant_mode():
         with pytest.raises(NotImplementedError):

@@ -1,0 +1,179 @@
+"""GPU tests of the attention forms beyond the boolean mask: additive masks, attention sinks, and head
+dims that are multiples of 32 (README, section "How the kernels work", attention paragraph: the mask
+forms of the single-pass kernel; section "Limitations": sinks, head dims).
+
+* oracle tolerance (fp32 1e-5, bf16 / fp16 2e-2) against the float64 oracle on every kernel path:
+  one launch for short caches, split + combine for long ones, the prefill kernel for long query
+  chunks, and the generic split kernel for fp32 and every head dim other than 128;
+* equivalences on raw bits: an additive mask of 0 / -inf equals the boolean mask, -inf sinks equal
+  no sinks;
+* invariance on raw bits: every token of a prefill chunk equals its own decode call (K / V truncated
+  after it, its mask row), batch neighbours do not matter, and keys appended with -inf (or masked
+  off) leave every result unchanged as the cache grows past split boundaries.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import invariant_deterministic_gemm_amd as bi
+import oracle
+import synthetic
+from helpers import assert_bits_equal, assert_close_to_oracle, round_ref
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+DTS = [torch.float32, torch.bfloat16, torch.float16]
+# (B, Hq, Hkv, Lq, S): one launch (S <= 1024), split + combine (S > 1024), prefill (Lq >= 384)
+PATHS = [(2, 8, 2, 5, 700), (1, 8, 2, 3, 2085), (1, 4, 2, 400, 900)]
+
+
+def _ids(d):
+    return str(d).split(".")[-1]
+
+
+def _qkv(B, Hq, Hkv, Lq, S, D, dt, seed):
+    q = synthetic.randn((B, Hq, Lq, D), seed, 1.0, dt)
+    k = synthetic.randn((B, Hkv, S, D), seed + 1, 1.0, dt)
+    v = synthetic.randn((B, Hkv, S, D), seed + 2, 1.0, dt)
+    return q, k, v
+
+
+def _gpu(*ts):
+    return [None if t is None else t.to(DEV) for t in ts]
+
+
+def _additive(shape, seed, dt, frac_inf=0.2):
+    g = torch.Generator().manual_seed(seed)
+    a = torch.randn(shape, generator=g) * 2
+    a[torch.rand(shape, generator=g) < frac_inf] = float("-inf")
+    return a.to(dt)
+
+
+@pytest.mark.parametrize("shape", PATHS, ids=["fused", "split", "prefill"])
+@pytest.mark.parametrize("dt", DTS, ids=_ids)
+def test_additive_mask_against_oracle_and_boolean(dt, shape):
+    B, Hq, Hkv, Lq, S = shape
+    q, k, v = _qkv(B, Hq, Hkv, Lq, S, 128, dt, 300 + Lq)
+    amask = _additive((B, 1, Lq, S), 301 + Lq, dt)
+    amask[..., S - Lq] = 0.0                            # every row keeps at least one key
+    qg, kg, vg, ag = _gpu(q, k, v, amask)
+    o = bi.bi_sdpa(qg, kg, vg, causal=True, mask=ag)
+    want = oracle.sdpa(q, k, v, causal=True, mask=amask.to(torch.float64))
+    assert_close_to_oracle(o, want, f"additive mask {dt} {shape}")
+    # 0 / -inf is the boolean mask, bit for bit
+    bm = torch.isfinite(amask)
+    zero_inf = torch.where(bm, torch.zeros((), dtype=dt), torch.full((), float("-inf"), dtype=dt))
+    assert_bits_equal(bi.bi_sdpa(qg, kg, vg, causal=True, mask=zero_inf.to(DEV)),
+                      bi.bi_sdpa(qg, kg, vg, causal=True, mask=bm.to(DEV)), "0 / -inf vs boolean")
+
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16], ids=_ids)
+def test_additive_mask_tokens_equal_their_decode_and_ignore_neighbours(dt):
+    B, Hq, Hkv, Lq, S, D = 3, 8, 2, 24, 1300, 128
+    q, k, v = _gpu(*_qkv(B, Hq, Hkv, Lq, S, D, dt, 310))
+    amask = _additive((B, Hq, Lq, S), 311, dt).to(DEV)
+    amask[..., :8] = 0.0
+    full = bi.bi_sdpa(q, k, v, causal=True, mask=amask)
+    for i in (0, 7, 23):
+        p = S - Lq + i
+        dec = bi.bi_sdpa(q[:, :, i:i + 1], k[:, :, :p + 1], v[:, :, :p + 1], causal=True,
+                         mask=amask[:, :, i:i + 1, :p + 1])
+        assert_bits_equal(dec[:, :, 0], full[:, :, i], f"token {i} vs its decode")
+    one = bi.bi_sdpa(q[1:2], k[1:2], v[1:2], causal=True, mask=amask[1:2])
+    assert_bits_equal(one, full[1:2], "batch element alone")
+
+
+@pytest.mark.parametrize("dt", DTS, ids=_ids)
+def test_keys_appended_with_minus_inf_change_nothing(dt):
+    B, Hq, Hkv, Lq, S0, D = 1, 8, 2, 4, 1000, 128
+    q, k, v = _qkv(B, Hq, Hkv, Lq, S0 + 600, D, dt, 320)
+    amask = _additive((B, Hq, Lq, S0 + 600), 321, dt, frac_inf=0.1)
+    amask[..., :4] = 0.0
+    q, k, v, amask = _gpu(q, k, v, amask)
+    base = bi.bi_sdpa(q, k[:, :, :S0], v[:, :, :S0], mask=amask[..., :S0])
+    for S in (S0 + 24, S0 + 300, S0 + 600):            # 4 -> 5, 6, 7 splits
+        grown = amask[..., :S].clone()
+        grown[..., S0:] = float("-inf")
+        o = bi.bi_sdpa(q, k[:, :, :S], v[:, :, :S], mask=grown)
+        assert_bits_equal(o, base, f"cache {S0} -> {S}, new keys at -inf")
+
+
+@pytest.mark.parametrize("shape", PATHS, ids=["fused", "split", "prefill"])
+@pytest.mark.parametrize("dt", DTS, ids=_ids)
+def test_sinks_against_oracle_and_minus_inf(dt, shape):
+    B, Hq, Hkv, Lq, S = shape
+    q, k, v = _qkv(B, Hq, Hkv, Lq, S, 128, dt, 330 + Lq)
+    sinks = synthetic.randn((Hq,), 331, 2.0)
+    qg, kg, vg = _gpu(q, k, v)
+    o = bi.bi_sdpa(qg, kg, vg, causal=True, sinks=sinks.to(DEV))
+    want = oracle.sdpa(q, k, v, causal=True, sinks=sinks)
+    assert_close_to_oracle(o, want, f"sinks {dt} {shape}")
+    none = torch.full((Hq,), float("-inf"), device=DEV)
+    assert_bits_equal(bi.bi_sdpa(qg, kg, vg, causal=True, sinks=none), bi.bi_sdpa(qg, kg, vg, causal=True),
+                      "-inf sinks vs no sinks")
+
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16], ids=_ids)
+def test_sinks_invariance(dt):
+    B, Hq, Hkv, Lq, S, D = 2, 8, 2, 20, 1100, 128
+    q, k, v = _gpu(*_qkv(B, Hq, Hkv, Lq, S + 400, D, dt, 340))
+    sinks = synthetic.randn((Hq,), 341, 2.0).to(DEV)
+    full = bi.bi_sdpa(q, k[:, :, :S], v[:, :, :S], causal=True, sinks=sinks)
+    for i in (0, 19):
+        p = S - Lq + i
+        dec = bi.bi_sdpa(q[:, :, i:i + 1], k[:, :, :p + 1], v[:, :, :p + 1], causal=True, sinks=sinks)
+        assert_bits_equal(dec[:, :, 0], full[:, :, i], f"token {i} vs its decode, sinks")
+    assert_bits_equal(bi.bi_sdpa(q[:1], k[:1, :, :S], v[:1, :, :S], causal=True, sinks=sinks), full[:1],
+                      "batch element alone, sinks")
+    # the cache grows by masked keys: the sink's place in the fold (first) does not move
+    m = torch.ones(1, 1, Lq, S + 400, dtype=torch.bool, device=DEV)
+    m[..., S:] = False
+    qd = q[:, :, :1]
+    base = bi.bi_sdpa(qd, k[:, :, :S], v[:, :, :S], sinks=sinks)
+    grown = bi.bi_sdpa(qd, k, v, mask=m[:, :, :1], sinks=sinks)
+    assert_bits_equal(grown, base, "cache growth with masked keys, sinks")
+    # a query that sees no key gives zeros, sink or not
+    none = torch.zeros(1, 1, 1, S, dtype=torch.bool, device=DEV)
+    z = bi.bi_sdpa(qd, k[:, :, :S], v[:, :, :S], mask=none, sinks=sinks)
+    assert_bits_equal(z, torch.zeros_like(z), "no visible key with a sink")
+
+
+@pytest.mark.parametrize("D", [32, 96, 160, 192, 224, 256])
+@pytest.mark.parametrize("dt", DTS, ids=_ids)
+def test_head_dims_multiple_of_32(dt, D):
+    B, Hq, Hkv, Lq, S = 2, 4, 2, 9, 300              # two splits, ragged last block
+    q, k, v = _qkv(B, Hq, Hkv, Lq, S, D, dt, 350 + D)
+    qg, kg, vg = _gpu(q, k, v)
+    o = bi.bi_sdpa(qg, kg, vg, causal=True)
+    assert_close_to_oracle(o, oracle.sdpa(q, k, v, causal=True), f"D={D} {dt}")
+    for i in (0, Lq - 1):
+        p = S - Lq + i
+        dec = bi.bi_sdpa(qg[:, :, i:i + 1], kg[:, :, :p + 1], vg[:, :, :p + 1], causal=True)
+        assert_bits_equal(dec[:, :, 0], o[:, :, i], f"D={D}: token {i} vs its decode")
+    assert_bits_equal(bi.bi_sdpa(qg[1:], kg[1:], vg[1:], causal=True), o[1:], f"D={D}: batch element alone")
+    # zero queries: weights exp2(0) = 1, integer values -> the correctly rounded mean
+    q0 = torch.zeros(1, Hq, S, D, dtype=dt)
+    vi = synthetic.randint((1, Hkv, S, D), 352, -8, 8, dt)
+    z = bi.bi_sdpa(q0.to(DEV), kg[:1], vi.to(DEV), causal=True).cpu()
+    assert_bits_equal(z, round_ref(oracle.sdpa(q0, k[:1], vi, causal=True), dt), f"D={D}: zero-query means")
+
+
+def test_forms_together_and_bad_arguments():
+    B, Hq, Hkv, Lq, S, D = 1, 8, 4, 6, 520, 64
+    dt = torch.bfloat16
+    q, k, v = _qkv(B, Hq, Hkv, Lq, S, D, dt, 360)
+    amask = _additive((1, 1, Lq, S), 361, dt)
+    amask[..., 0] = 0.0
+    sinks = synthetic.randn((Hq,), 362, 2.0)
+    qg, kg, vg, ag = _gpu(q, k, v, amask)
+    o = bi.bi_sdpa(qg, kg, vg, causal=True, mask=ag, sinks=sinks)
+    want = oracle.sdpa(q, k, v, causal=True, mask=amask.to(torch.float64), sinks=sinks)
+    assert_close_to_oracle(o, want, "additive mask, causal and sinks together")
+    with pytest.raises(ValueError):                     # an additive mask must share q's dtype
+        bi.bi_sdpa(qg, kg, vg, mask=ag.float())
+    with pytest.raises(ValueError):                     # one sink per query head
+        bi.bi_sdpa(qg, kg, vg, sinks=sinks[:3])
+    with pytest.raises(NotImplementedError):            # head dims are multiples of 32
+        bi.bi_sdpa(qg[..., :48], kg[..., :48], vg[..., :48])
