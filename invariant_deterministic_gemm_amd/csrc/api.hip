@@ -280,6 +280,12 @@ static bi_status sdpa_impl(const char *fn, const void *q, const int64_t q_str[4]
     }
     p.mask = mask;
     p.mask_add = mask_kind == BI_MASK_ADD ? 1 : 0;
+    if (mask != nullptr) {
+        // four consecutive keys per load: unit key stride, S a multiple of 4, every mask row 4-key aligned
+        const int eb = p.mask_add ? (int)esize(dt) : 1;
+        p.mask_vec = mask_str[3] == 1 && S % 4 == 0 && aligned_to(mask, 4 * eb) && mask_str[0] % 4 == 0 &&
+                     mask_str[1] % 4 == 0 && mask_str[2] % 4 == 0;
+    }
     for (int d = 0; d < 4; ++d) p.ms[d] = mask ? mask_str[d] : 0;
     p.sinks = sinks;
     p.B = (int)B;

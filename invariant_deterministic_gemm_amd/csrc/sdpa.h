@@ -18,6 +18,7 @@ struct SdpaParams {
     const void *mask;                     // nullable: uint8 (nonzero = attend) or, with mask_add, dt values
     int64_t ms[4];                        // element strides of the mask
     int mask_add;                         // the mask is additive (dt, added to the scaled scores)
+    int mask_vec;                         // keys contiguous, S % 4 == 0, rows 4-key aligned: 4 keys per load
     const float *sinks;                   // nullable: Hq logits, one extra softmax term per query head
     int B, Hq, Hkv, Lq, S, G;             // G = Hq / Hkv
     int causal;

@@ -88,6 +88,72 @@ __device__ __forceinline__ float masked_score(const SdpaParams &p, const char *m
     }
     return ok && reinterpret_cast<const uint8_t *>(mrow)[(int64_t)key * p.ms[3]] != 0 ? sv : -__builtin_huge_valf();
 }
+// Scores of a lane's 16 keys kb + 16 kt + 4 g + i of one block (exp2 domain, -inf when invisible), from
+// the block's raw scores st: key past S, causality (pos) and the mask.  With mask_vec the lane reads its
+// mask values as four 4-key vectors, all requested before the first is used (one wait for the four;
+// S % 4 == 0, so a 4-key group is entirely before S or entirely past it and is then read clamped).
+template <int dt>
+__device__ __forceinline__ void block_scores(const SdpaParams &p, const char *mrow, int kb, int g, bool row_ok,
+                                             int pos, const f32x4 (&st)[4], float (&s)[4][4]) {
+    constexpr int EB = Elem<dt>::bytes;
+    constexpr float NEG_INF = -__builtin_huge_valf();
+    if (mrow != nullptr && p.mask_vec) {
+        // the four loads of a mask kind are issued together, with no branch between them
+        auto vis = [&](int kt, int i) {
+            const int key = kb + 16 * kt + 4 * g + i;
+            bool ok = row_ok && key < p.S;
+            if (p.causal) ok = ok && key <= pos;
+            return ok;
+        };
+        if (!p.mask_add) {
+            uint32_t raw[4];
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+                raw[kt] = *reinterpret_cast<const uint32_t *>(mrow + min(kb + 16 * kt + 4 * g, p.S - 4));
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const bool ok = vis(kt, i) && ((raw[kt] >> (8 * i)) & 0xffu) != 0;
+                    s[kt][i] = ok ? st[kt][i] * p.c : NEG_INF;
+                }
+        } else if constexpr (EB == 2) {
+            u32x2 raw[4];
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+                raw[kt] = *reinterpret_cast<const u32x2 *>(mrow + (int64_t)min(kb + 16 * kt + 4 * g, p.S - 4) * 2);
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t h16 = (raw[kt][i >> 1] >> (16 * (i & 1))) & 0xffffu;
+                    const float a = dt == DT_BF16 ? bf16_to_f32(h16) : f16_to_f32(h16);
+                    s[kt][i] = vis(kt, i) ? __builtin_fmaf(a, LOG2E_F, st[kt][i] * p.c) : NEG_INF;
+                }
+        } else {
+            u32x4 raw[4];
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+                raw[kt] = *reinterpret_cast<const u32x4 *>(mrow + (int64_t)min(kb + 16 * kt + 4 * g, p.S - 4) * 4);
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    s[kt][i] = vis(kt, i) ? __builtin_fmaf(__uint_as_float(raw[kt][i]), LOG2E_F, st[kt][i] * p.c) : NEG_INF;
+        }
+        return;
+    }
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int key = kb + 16 * kt + 4 * g + i;
+            bool ok = row_ok && key < p.S;
+            if (p.causal) ok = ok && key <= pos;
+            s[kt][i] = masked_score<dt>(p, mrow, min(key, p.S - 1), ok, st[kt][i]);
+        }
+}
+
 // The sink of query head h in the exp2 domain, as the first partial of every fold: (m, l, O) =
 // (sink * log2 e, 1, 0).
 __device__ __forceinline__ float sink2(const SdpaParams &p, int h) { return p.sinks[h] * LOG2E_F; }
@@ -218,16 +284,11 @@ __global__ __launch_bounds__(64) void sdpa_split(SdpaParams p) {
         }
         float s[4][4];
         float mb = NEG_INF;
+        block_scores<dt>(p, mrow, kb, g, row_ok, pos, st, s);
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int key = kb + 16 * kt + 4 * g + i;
-                bool ok = row_ok && key < p.S;
-                if (p.causal) ok = ok && key <= pos;
-                s[kt][i] = masked_score<dt>(p, mrow, min(key, p.S - 1), ok, st[kt][i]);
-                mb = fmaxf(mb, s[kt][i]);
-            }
+            for (int i = 0; i < 4; ++i) mb = fmaxf(mb, s[kt][i]);
         mb = max_xor32(max_xor16(mb));
         const bool empty = mb == NEG_INF;
         const float m_new = empty ? m_run : fmaxf(m_run, mb);
@@ -424,15 +485,7 @@ __device__ __forceinline__ void attn_update16(const SdpaParams &p, const Rows16 
             for (int i = 0; i < 4; ++i) s[kt][i] = st[kt][i] * p.c;
         mb = lane_max();
     } else {
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int key = kb + 16 * kt + 4 * g + i;
-                bool ok = r.row_ok && key < p.S;
-                if (p.causal) ok = ok && key <= r.pos;
-                s[kt][i] = masked_score<dt>(p, r.mrow, min(key, p.S - 1), ok, st[kt][i]);
-            }
+        block_scores<dt>(p, r.mrow, kb, g, r.row_ok, r.pos, st, s);
         mb = lane_max();
     }
     mb = max_xor32(max_xor16(mb));
