@@ -398,6 +398,57 @@ def measure_cells(bi, lib, torch, dev, synthetic, data, launches, groups, names,
         cells["decode_attention"].append({"B": B, "S": S, "us": round(ms * 1e3, 1), "GBps": round(gbps, 1),
                                           "frac_hbm": round(gbps / HBM_PEAK_GBPS, 4)})
         del q, k, v, ws
+    # the other attention forms on the decode shape: sinks, a boolean (uint8) and an additive (bf16)
+    # padding mask over (B, 1, 1, S), each as a ratio to the plain call; head dims 64 and 256
+    cells["attention_forms"] = []
+    for B, S in ((8, 8192), (32, 8192)):
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(0x5EED91 + B * 100000 + S)
+        q = torch.randn((B, 32, 1, 128), generator=gen, device=dev).to(torch.bfloat16)
+        k = torch.randn((B, 8, S, 128), generator=gen, device=dev).to(torch.bfloat16)
+        v = torch.randn((B, 8, S, 128), generator=gen, device=dev).to(torch.bfloat16)
+        ws = torch.empty(lib.bi_sdpa_workspace_bytes(B, 32, 1, S, 128, bi.BI_BF16), dtype=torch.uint8, device=dev)
+        sinks = torch.randn((32,), generator=gen, device=dev)
+        keep = torch.rand((B, 1, 1, S), generator=gen, device=dev) > 0.1
+        m8 = keep.to(torch.uint8)
+        madd = torch.where(keep, torch.randn((B, 1, 1, S), generator=gen, device=dev),
+                           torch.full((), float("-inf"), device=dev)).to(torch.bfloat16)
+        forms = (("causal", lambda: bi.bi_sdpa(q, k, v, causal=True, workspace=ws)),
+                 ("causal+sinks", lambda: bi.bi_sdpa(q, k, v, causal=True, workspace=ws, sinks=sinks)),
+                 ("bool mask", lambda: bi.bi_sdpa(q, k, v, mask=m8, workspace=ws)),
+                 ("additive mask", lambda: bi.bi_sdpa(q, k, v, mask=madd, workspace=ws)))
+        base = None
+        for name, fn in forms:
+            ms = _time_graph(torch, fn, reps=4, iters=6)
+            base = base or ms
+            gbps = 2.0 * (B * 8 * S * 128 * 2) / (ms * 1e-3) / 1e9
+            cells["attention_forms"].append({"B": B, "S": S, "D": 128, "form": name, "us": round(ms * 1e3, 1),
+                                             "GBps": round(gbps, 1), "frac_hbm": round(gbps / HBM_PEAK_GBPS, 4),
+                                             "over_causal": round(ms / base, 3)})
+        del q, k, v, ws
+    for D in (64, 256):
+        B, S = 8, 8192
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(0x5EED92 + D)
+        q = torch.randn((B, 32, 1, D), generator=gen, device=dev).to(torch.bfloat16)
+        k = torch.randn((B, 8, S, D), generator=gen, device=dev).to(torch.bfloat16)
+        v = torch.randn((B, 8, S, D), generator=gen, device=dev).to(torch.bfloat16)
+        ws = torch.empty(lib.bi_sdpa_workspace_bytes(B, 32, 1, S, D, bi.BI_BF16), dtype=torch.uint8, device=dev)
+        ms = _time_graph(torch, lambda: bi.bi_sdpa(q, k, v, causal=True, workspace=ws), reps=4, iters=6)
+        gbps = 2.0 * (B * 8 * S * D * 2) / (ms * 1e-3) / 1e9
+        cells["attention_forms"].append({"B": B, "S": S, "D": D, "form": "causal decode", "us": round(ms * 1e3, 1),
+                                         "GBps": round(gbps, 1), "frac_hbm": round(gbps / HBM_PEAK_GBPS, 4),
+                                         "kernel": lib.bi_sdpa_kernel_name(B, 32, 1, S, D, bi.BI_BF16).decode()})
+        qp = torch.randn((1, 32, 2048, D), generator=gen, device=dev).to(torch.bfloat16)
+        kp = torch.randn((1, 8, 2048, D), generator=gen, device=dev).to(torch.bfloat16)
+        wsp = torch.empty(lib.bi_sdpa_workspace_bytes(1, 32, 2048, 2048, D, bi.BI_BF16), dtype=torch.uint8, device=dev)
+        ms = _time_graph(torch, lambda: bi.bi_sdpa(qp, kp, kp, causal=True, workspace=wsp), reps=2, iters=4)
+        tf = 4.0 * 32 * D * (2048 * 2049 / 2) / (ms * 1e-3) / 1e12
+        cells["attention_forms"].append({"B": 1, "Lq": 2048, "S": 2048, "D": D, "form": "causal prefill",
+                                         "us": round(ms * 1e3, 1), "TFLOPs": round(tf, 1),
+                                         "frac_mfma": round(tf / BF16_PEAK_TFLOPS, 4),
+                                         "kernel": lib.bi_sdpa_kernel_name(1, 32, 2048, 2048, D, bi.BI_BF16).decode()})
+        del q, k, v, ws, qp, kp, wsp
     # long causal prefill (query chunk = whole cache): workspace-free kernel, flops of visible pairs
     for S in (4096, 8192):
         gen = torch.Generator(device=dev)
