@@ -84,7 +84,7 @@ template <int FM, int BITS, bool XREG_> struct QStrip {
     // one stage ahead; otherwise x goes through LDS, XU 16-byte chunks per producer thread per stage,
     // XD stages ahead
     static constexpr bool XREG = XREG_;
-    static constexpr int XR = 1;
+    static constexpr int XR = 2;
     static constexpr int XU = XREG ? 0 : 16 * FM * KS / 2048;
     static constexpr int XD = FM == 1 ? 4 : 1;
 };
@@ -95,6 +95,23 @@ template <int FM, int BITS, bool XREG_> struct QStrip {
 template <int CPT> __device__ __forceinline__ int wslot(int c, int r) {
     if constexpr (CPT == 1) return c ^ (r & 15);
     else return c ^ (r & 15) ^ ((c / CPT) & 7);
+}
+
+// Lane u of each 16-lane row, broadcast to the whole row (DPP row_newbcast; u a constant once unrolled).
+__device__ __forceinline__ uint32_t row_bcast1(uint32_t x, int u) {
+    switch (u & 7) {
+        case 0: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x150, 0xf, 0xf, false);
+        case 1: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x151, 0xf, 0xf, false);
+        case 2: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x152, 0xf, 0xf, false);
+        case 3: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x153, 0xf, 0xf, false);
+        case 4: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x154, 0xf, 0xf, false);
+        case 5: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x155, 0xf, 0xf, false);
+        case 6: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x156, 0xf, 0xf, false);
+        default: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x157, 0xf, 0xf, false);
+    }
+}
+__device__ __forceinline__ u32x4 row_bcast(const u32x4 &x, int u) {
+    return u32x4{row_bcast1(x[0], u), row_bcast1(x[1], u), row_bcast1(x[2], u), row_bcast1(x[3], u)};
 }
 
 struct u32x8 {
@@ -214,15 +231,15 @@ __global__ __launch_bounds__(320) void qgemm16_strip(QGemmParams q) {
         f32x4 acc[FM];
 #pragma unroll
         for (int f = 0; f < FM; ++f) acc[f] = zero4();
-        // one fragment: x rows (row r16 clamped to the last row) straight from memory, XR stages ahead
-        const uint32_t xa_lane = (uint32_t)min(r16, xrows - 1) * xrow_b + (uint32_t)g * 16u;
-        u32x4 xa[XR][SPS];
-        auto loadX = [&](int s, u32x4 (&a)[SPS]) {
-            const uint32_t so = stage_off(s, (uint32_t)ROWB);
-#pragma unroll
-            for (int u = 0; u < SPS; ++u)
-                a[u] = __builtin_bit_cast(
-                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres, sat_off(xa_lane + 64u * u, so), 0, 0));
+        // one row of x (the host takes this path for M = 1 only): one load per stage, XR stages ahead,
+        // lane (r16, g) holding the 16 bytes of step r16 mod 8 and k group g; step u's fragment (row 0 in
+        // every lane) is then lane u of each 16-lane row, spread with a DPP row broadcast
+        static_assert(!XREG || SPS == 8, "one load per stage covers the stage's eight steps");
+        const uint32_t xa_lane = 64u * (uint32_t)(r16 & 7) + 16u * (uint32_t)g;
+        u32x4 xa[XR];
+        auto loadX = [&](int s, u32x4 &a) {
+            a = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              xres, sat_off(xa_lane, stage_off(s, (uint32_t)ROWB)), 0, 0));
         };
         if constexpr (XREG) {
 #pragma unroll
@@ -243,7 +260,7 @@ __global__ __launch_bounds__(320) void qgemm16_strip(QGemmParams q) {
                         const int u = h * HS + v, c = 4 * u + g;
                         b[v] = *reinterpret_cast<const u32x4 *>(buf + r16 * ROWB + (wslot<VPT / 8>(c, r16) << 4));
                         if constexpr (XREG) {
-                            a[v][0] = xa[j % XR][u];
+                            a[v][0] = row_bcast(xa[j % XR], u);
                         } else {
 #pragma unroll
                             for (int f = 0; f < FM; ++f) {
