@@ -160,7 +160,7 @@ bi_status bi_addmm(const void *cin, int64_t ldcin,
  * 256-byte aligned, device memory owned by the caller; its contents on entry
  * do not matter and on return are unspecified.  Two calls that run at the
  * same time must not share a workspace.  The query returns 0 (ws may then be
- * NULL) for the shapes served without a workspace: 16-bit dt with D = 128
+ * NULL) for the shapes served without a workspace: 16-bit dt with D <= 128
  * and either S <= 1024 (one launch, splits folded in LDS) or Lq >= 384
  * (prefill: splits folded in registers).  Every path computes the same bits.
  */
@@ -305,9 +305,11 @@ size_t bi_quantized_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, bi_d
 const char *bi_gemm_kernel_name(int64_t M, int64_t N, int64_t K, bi_dtype in_dt, int b_kn);
 
 /* Which attention kernels a bi_sdpa call of these sizes runs: "sdpa_prefill16"
- * (16-bit, D = 128, Lq >= 384), "sdpa_fused16" (16-bit, D = 128, Lq < 384,
+ * (16-bit, D <= 128, Lq >= 384), "sdpa_fused16" (16-bit, D <= 128, Lq < 384,
  * S <= 1024), "sdpa_split16+combine" (other 16-bit D = 128 calls) or
- * "sdpa_split+combine" (fp32, and every other head dim).  Informational: the split / block
+ * "sdpa_split+combine" (fp32, and every other 16-bit call).  16-bit D < 128
+ * runs the prefill and one-launch kernels on rows zero-padded to 128 (the
+ * padding adds exact zeros, so the bits are the split kernel's).  Informational: the split / block
  * structure, and with it every output bit, is the same whichever runs.
  * Returns "none" for empty, oversized or unsupported sizes. */
 const char *bi_sdpa_kernel_name(int64_t B, int64_t Hq, int64_t Lq, int64_t S, int64_t D, bi_dtype dt);

@@ -295,6 +295,7 @@ static bi_status sdpa_impl(const char *fn, const void *q, const int64_t q_str[4]
     p.S = (int)S;
     p.G = (int)G;
     p.causal = causal ? 1 : 0;
+    p.dr = (int)D;
     p.c = (float)((double)scale * 1.4426950408889634);   // log2(e), rounded once to fp32
     p.nsplit = (int)((S + bi::KV_SPLIT - 1) / bi::KV_SPLIT);
     if (need > 0) bi::sdpa_bind_workspace(p, ws);

@@ -22,6 +22,7 @@ struct SdpaParams {
     const float *sinks;                   // nullable: Hq logits, one extra softmax term per query head
     int B, Hq, Hkv, Lq, S, G;             // G = Hq / Hkv
     int causal;
+    int dr;                               // head dim; the 16-bit kernels run D <= 128 as 128 with zero padding
     float c;                              // scale * log2(e), rounded once to fp32
     int nsplit;                           // ceil(S / KV_SPLIT)
     float *ws_ml;                         // [rows][nsplit][2]  (m, l)
@@ -31,8 +32,8 @@ struct SdpaParams {
 // Which kernels serve a call.  Every path computes the same bits; only the
 // split path uses a workspace.
 enum SdpaPath {
-    SDPA_FUSED16,     // 16-bit, D = 128, at most four splits: one launch, fold in LDS
-    SDPA_PREFILL16,   // 16-bit, D = 128, long caches with many query rows: fold in registers
+    SDPA_FUSED16,     // 16-bit, D <= 128, at most four splits: one launch, fold in LDS
+    SDPA_PREFILL16,   // 16-bit, D <= 128, long caches with many query rows: fold in registers
     SDPA_SPLIT        // split kernel + combine kernel through the workspace
 };
 SdpaPath sdpa_path(int64_t Lq, int64_t S, int64_t D, int dt);

@@ -69,6 +69,11 @@ __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2
 // log2(e) rounded to fp32: additive mask values and sink logits move to the exp2 domain with it
 constexpr float LOG2E_F = 1.44269504088896340736f;
 
+// 16-bit head dims below 128 run the D = 128 kernels on zero-padded rows: the loads of 16-byte chunks at
+// d >= D read this zero page instead of memory, so the padding costs no HBM traffic; its zero products
+// add exact zeros to the q.k chain and its output columns are never stored.
+__device__ __attribute__((aligned(256))) uint32_t g_zero_page[64];
+
 // The mask row of query row (b, h, iq): byte pointer to its element for key 0, or null.
 __device__ __forceinline__ const char *mask_row(const SdpaParams &p, int b, int h, int iq, int eb) {
     if (p.mask == nullptr) return nullptr;
@@ -428,7 +433,10 @@ __device__ __forceinline__ void rows16_load(const SdpaParams &p, int tile, int b
     const char *qrow = static_cast<const char *>(p.q) +
                        ((int64_t)b * p.qs[0] + (int64_t)h * p.qs[1] + (int64_t)iq * p.qs[2]) * 2;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) r.qf[c] = ldg16(qrow + (32 * c + 8 * g) * 2);
+    for (int c = 0; c < 4; ++c) {
+        r.qf[c] = zero_u4();
+        if (32 * c < p.dr) r.qf[c] = ldg16(qrow + (32 * c + 8 * g) * 2);
+    }
 }
 
 // Scores of one 64-key block for a wavefront's 16 rows (K block in LDS, 256-byte key rows, chunk c of
@@ -592,17 +600,27 @@ __device__ __forceinline__ void split16_body(const SdpaParams &p, int sp, int ti
     const char *klane = kbase + lrow * kstr;
     const char *vlane = vbase + lrow * vstr;
     int kch[4], vch[2];
+    bool kz[4], vz[2];                                // chunk at d >= D: read the zero page
 #pragma unroll
-    for (int r = 0; r < 4; ++r) kch[r] = (lslot ^ ((4 * r + lrow) & 15)) << 4;
+    for (int r = 0; r < 4; ++r) {
+        const int c = lslot ^ ((4 * r + lrow) & 15);
+        kch[r] = c << 4;
+        kz[r] = 8 * c >= p.dr;
+    }
 #pragma unroll
-    for (int r = 0; r < 2; ++r) vch[r] = (lslot ^ (((4 * r + lrow) & 7) << 1)) << 4;
+    for (int r = 0; r < 2; ++r) {
+        const int c = lslot ^ (((4 * r + lrow) & 7) << 1);
+        vch[r] = c << 4;
+        vz[r] = 8 * c >= p.dr;
+    }
+    const char *zp = reinterpret_cast<const char *>(g_zero_page);
     auto issueK = [&](int blk) {
         const int kb = kbeg + blk * KV_BLOCK;
         if (kb + KV_BLOCK <= p.S) {
             const char *bp = klane + (int64_t)kb * kstr;
 #pragma unroll
             for (int q = 0; q < QB; ++q) {
-                __builtin_amdgcn_global_load_lds(static_cast<const void *>(bp + kch[q & 3]),
+                __builtin_amdgcn_global_load_lds(static_cast<const void *>(kz[q & 3] ? zp : bp + kch[q & 3]),
                                                  BI_LDS_PTR(lds + q * 1024), 16, 0, 0);
                 bp += 4 * kstr;
             }
@@ -610,8 +628,9 @@ __device__ __forceinline__ void split16_body(const SdpaParams &p, int sp, int ti
 #pragma unroll
             for (int q = 0; q < QB; ++q) {
                 const int key = min(kb + 4 * q + lrow, p.S - 1);
-                __builtin_amdgcn_global_load_lds(static_cast<const void *>(kbase + key * kstr + kch[q & 3]),
-                                                 BI_LDS_PTR(lds + q * 1024), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(
+                    static_cast<const void *>(kz[q & 3] ? zp : kbase + key * kstr + kch[q & 3]),
+                    BI_LDS_PTR(lds + q * 1024), 16, 0, 0);
             }
         }
     };
@@ -621,7 +640,7 @@ __device__ __forceinline__ void split16_body(const SdpaParams &p, int sp, int ti
             const char *bp = vlane + (int64_t)kb * vstr;
 #pragma unroll
             for (int q = 0; q < QB; ++q) {
-                __builtin_amdgcn_global_load_lds(static_cast<const void *>(bp + vch[q & 1]),
+                __builtin_amdgcn_global_load_lds(static_cast<const void *>(vz[q & 1] ? zp : bp + vch[q & 1]),
                                                  BI_LDS_PTR(lds + KBYTES + q * 1024), 16, 0, 0);
                 bp += 4 * vstr;
             }
@@ -629,8 +648,9 @@ __device__ __forceinline__ void split16_body(const SdpaParams &p, int sp, int ti
 #pragma unroll
             for (int q = 0; q < QB; ++q) {
                 const int key = min(kb + 4 * q + lrow, p.S - 1);
-                __builtin_amdgcn_global_load_lds(static_cast<const void *>(vbase + key * vstr + vch[q & 1]),
-                                                 BI_LDS_PTR(lds + KBYTES + q * 1024), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(
+                    static_cast<const void *>(vz[q & 1] ? zp : vbase + key * vstr + vch[q & 1]),
+                    BI_LDS_PTR(lds + KBYTES + q * 1024), 16, 0, 0);
             }
         }
     };
@@ -702,9 +722,10 @@ __global__ __launch_bounds__(64 * W) void sdpa_split16(SdpaParams p) {
         const int ro = tile * 16 + 4 * g + i;
         if (ro < R) {
             const int64_t rowid = ((int64_t)b * p.Hq + gk * p.G + ro % p.G) * p.Lq + ro / p.G;
-            float *dst = p.ws_o + (rowid * p.nsplit + sp) * 128;
+            float *dst = p.ws_o + (rowid * p.nsplit + sp) * p.dr;
 #pragma unroll
-            for (int t = 0; t < 8; ++t) dst[16 * t + r16] = o[t][i];
+            for (int t = 0; t < 8; ++t)
+                if (16 * t < p.dr) dst[16 * t + r16] = o[t][i];
         }
     }
 }
@@ -743,8 +764,8 @@ __global__ __launch_bounds__(64 * FUSED_MAXW) void sdpa_fused16(SdpaParams p) {
 #pragma unroll
         for (int t = 0; t < 8; ++t) po[(wave * 16 + 4 * g + i) * D + 16 * t + r16] = o[t][i];
     __syncthreads();
-    for (int e = tid; e < 16 * D; e += 64 * nw) {
-        const int row = e / D, d = e % D;
+    for (int e = tid; e < 16 * p.dr; e += 64 * nw) {
+        const int row = e / p.dr, d = e % p.dr;
         const int ro = tile * 16 + row;
         if (ro >= R) continue;
         const int iq = ro / p.G, h = gk * p.G + ro % p.G;
@@ -834,13 +855,16 @@ __global__ __launch_bounds__(64 * W) void sdpa_prefill16(SdpaParams p) {
     const bool off32 = (uint64_t)max(kstr, vstr) * KV_BLOCK + ROWB <= 0xffffffffull;
     uint32_t loff[QW];
     int lrowj[QW];
+    bool lz[QW];                                       // chunk at d >= D: read the zero page
 #pragma unroll
     for (int j = 0; j < QW; ++j) {
         const int row = 4 * ((wave + W * j) & 15) + lrow;
+        const int c = j < QK ? lslot ^ (row & 15) : lslot ^ ((row & 7) << 1);
         lrowj[j] = row;
-        loff[j] = j < QK ? (uint32_t)(row * kstr) + ((lslot ^ (row & 15)) << 4)
-                         : (uint32_t)(row * vstr) + ((lslot ^ ((row & 7) << 1)) << 4);
+        lz[j] = 8 * c >= p.dr;
+        loff[j] = (uint32_t)(row * (j < QK ? kstr : vstr)) + (c << 4);
     }
+    const char *zp = reinterpret_cast<const char *>(g_zero_page);
     auto issue = [&](int blk) {
         const int kb = blk * KV_BLOCK;
         char *buf = lds + (blk % NB) * 2 * KBYTES;
@@ -849,7 +873,7 @@ __global__ __launch_bounds__(64 * W) void sdpa_prefill16(SdpaParams p) {
             const char *vblk = vbase + (int64_t)kb * vstr;
 #pragma unroll
             for (int j = 0; j < QW; ++j)
-                __builtin_amdgcn_global_load_lds(static_cast<const void *>((j < QK ? kblk : vblk) + loff[j]),
+                __builtin_amdgcn_global_load_lds(static_cast<const void *>(lz[j] ? zp : (j < QK ? kblk : vblk) + loff[j]),
                                                  BI_LDS_PTR(buf + (j < QK ? 0 : KBYTES) + ((wave + W * j) & 15) * 1024),
                                                  16, 0, 0);
         } else {
@@ -857,8 +881,9 @@ __global__ __launch_bounds__(64 * W) void sdpa_prefill16(SdpaParams p) {
             for (int j = 0; j < QW; ++j) {
                 const int row = lrowj[j];
                 const int64_t key = min(kb + row, p.S - 1);
-                const char *src = j < QK ? kbase + key * kstr + ((lslot ^ (row & 15)) << 4)
-                                         : vbase + key * vstr + ((lslot ^ ((row & 7) << 1)) << 4);
+                const char *src = lz[j] ? zp
+                                  : j < QK ? kbase + key * kstr + ((lslot ^ (row & 15)) << 4)
+                                           : vbase + key * vstr + ((lslot ^ ((row & 7) << 1)) << 4);
                 __builtin_amdgcn_global_load_lds(static_cast<const void *>(src),
                                                  BI_LDS_PTR(buf + (j < QK ? 0 : KBYTES) + ((wave + W * j) & 15) * 1024),
                                                  16, 0, 0);
@@ -960,7 +985,7 @@ __global__ __launch_bounds__(64 * W) void sdpa_prefill16(SdpaParams p) {
         for (int t = 0; t < 8; ++t) {
             float v = have_i ? ot[t][i] / l_i : 0.0f;
             v = v + 0.0f;                                // -0 -> +0
-            store_from_f32<dt>(orow, 16 * t + r16, v);
+            if (16 * t < p.dr) store_from_f32<dt>(orow, 16 * t + r16, v);
         }
     }
 }
@@ -1028,7 +1053,7 @@ __global__ __launch_bounds__(D) void sdpa_combine(SdpaParams p) {
 constexpr int64_t PREFILL_MIN_LQ = 384;
 
 SdpaPath sdpa_path(int64_t Lq, int64_t S, int64_t D, int dt) {
-    if (dt == DT_F32 || D != 128 || S <= 0) return SDPA_SPLIT;
+    if (dt == DT_F32 || D > 128 || S <= 0) return SDPA_SPLIT;
     if (Lq >= PREFILL_MIN_LQ) return SDPA_PREFILL16;
     if ((S + KV_SPLIT - 1) / KV_SPLIT <= FUSED_MAXW) return SDPA_FUSED16;
     return SDPA_SPLIT;
@@ -1054,7 +1079,7 @@ template <int dt, int D>
 static hipError_t launch_typed(const SdpaParams &p, hipStream_t st) {
     const int R = p.G * p.Lq;
     const SdpaPath path = sdpa_path(p.Lq, p.S, D, dt);
-    if constexpr (dt != DT_F32 && D == 128) {
+    if constexpr (dt != DT_F32 && D <= 128) {
         if (path == SDPA_PREFILL16) {
             constexpr int W = 4;                         // row tiles per workgroup sharing each K / V block
             const int64_t nwg = (int64_t)(((R + 15) / 16 + W - 1) / W) * p.B * p.Hkv;
@@ -1070,7 +1095,7 @@ static hipError_t launch_typed(const SdpaParams &p, hipStream_t st) {
         }
     }
     if (p.nsplit > 0) {
-        if constexpr (dt != DT_F32 && D == 128) {
+        if constexpr (dt != DT_F32 && D == 128) {     // (below 128 the generic kernel decodes faster)
             constexpr int W = 2;                         // splits per workgroup (measured best for long caches)
             const int64_t nwg = (int64_t)((p.nsplit + W - 1) / W) * ((R + 15) / 16) * p.B * p.Hkv;
             if (nwg > INT32_MAX) return hipErrorInvalidConfiguration;

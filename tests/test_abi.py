@@ -117,8 +117,8 @@ def test_sdpa_validation(lib):
     assert sdpa(lib, D=48) == UNSUPPORTED               # head dims: multiples of 32 up to 256
     assert sdpa(lib, D=288) == UNSUPPORTED
     assert sdpa(lib, D=0) == INVALID
-    for D in (32, 96, 160, 256):                          # accepted: they stop at the missing workspace
-        assert sdpa(lib, D=D, ws=None) == WORKSPACE, D
+    for D in (32, 96, 160, 256):                          # accepted: fp32 stops at the missing workspace
+        assert sdpa(lib, D=D, ws=None, dt=F32) == WORKSPACE, D
     assert sdpa(lib, Lq=17, S=16, causal=1) == INVALID  # causal needs Lq <= S
     assert sdpa(lib, dt=9) == INVALID
     assert sdpa(lib, scale=float("inf")) == INVALID
@@ -154,10 +154,11 @@ def test_sdpa_ex_validation(lib):
     neg = strides((1, 1, 1, 16))
     neg[3] = -1
     assert sdpa_ex(lib, kind=2, mask=P16, mstr=neg) == INVALID
-    # every form accepted together (D = 64 runs the split path: stops at the missing workspace)
-    assert sdpa_ex(lib, kind=2, mask=P16, mstr=m4, sinks=P16b) == WORKSPACE
+    # every form accepted together: fp32 always runs the split path, so each call stops at the missing
+    # workspace, after every other check and before anything is launched
+    assert sdpa_ex(lib, kind=2, mask=P16, mstr=m4, sinks=P16b, dt=F32) == WORKSPACE
     assert sdpa_ex(lib, kind=1, mask=P16, mstr=m4, sinks=P16b, dt=F32) == WORKSPACE
-    assert sdpa_ex(lib, kind=0, mask=ctypes.c_void_p(0x7f0000000001), mstr=None) == WORKSPACE   # mask ignored
+    assert sdpa_ex(lib, kind=0, mask=ctypes.c_void_p(0x7f0000000001), mstr=None, dt=F32) == WORKSPACE  # ignored
 
 
 def test_sdpa_workspace_formula(lib):
@@ -166,7 +167,9 @@ def test_sdpa_workspace_formula(lib):
         rows, nsplit = B * Hq * Lq, (S + 255) // 256
         return (rows * nsplit * 8 + 255) // 256 * 256 + rows * nsplit * D * 4
     assert lib.bi_sdpa_workspace_bytes(2, 32, 3, 1000, 128, F32) == split_bytes(2, 32, 3, 1000, 128)
-    assert lib.bi_sdpa_workspace_bytes(2, 32, 3, 1000, 64, BF16) == split_bytes(2, 32, 3, 1000, 64)
+    assert lib.bi_sdpa_workspace_bytes(2, 32, 3, 2000, 64, BF16) == split_bytes(2, 32, 3, 2000, 64)
+    assert lib.bi_sdpa_workspace_bytes(2, 32, 3, 1000, 64, BF16) == 0           # one launch, as D = 128
+    assert lib.bi_sdpa_workspace_bytes(2, 32, 3, 1000, 160, BF16) == split_bytes(2, 32, 3, 1000, 160)
     assert lib.bi_sdpa_workspace_bytes(2, 32, 3, 2000, 128, F16) == split_bytes(2, 32, 3, 2000, 128)
     # 16-bit D = 128: S <= 1024 (fused) and Lq >= 128 (prefill) need none
     assert lib.bi_sdpa_workspace_bytes(2, 32, 3, 1000, 128, BF16) == 0
@@ -207,8 +210,10 @@ def test_kernel_name_queries(lib):
     assert lib.bi_sdpa_kernel_name(1, 32, 384, 1024, 128, BF16).decode() == "sdpa_prefill16"
     assert lib.bi_sdpa_kernel_name(1, 32, 383, 1024, 128, BF16).decode() == "sdpa_fused16"
     assert lib.bi_sdpa_kernel_name(1, 32, 1, 300, 128, F32).decode() == "sdpa_split+combine"
-    assert lib.bi_sdpa_kernel_name(1, 32, 1, 300, 64, BF16).decode() == "sdpa_split+combine"
-    assert lib.bi_sdpa_kernel_name(1, 32, 1, 300, 96, BF16).decode() == "sdpa_split+combine"
+    assert lib.bi_sdpa_kernel_name(1, 32, 1, 300, 64, BF16).decode() == "sdpa_fused16"    # D <= 128: padded
+    assert lib.bi_sdpa_kernel_name(1, 32, 1, 3000, 96, BF16).decode() == "sdpa_split+combine"
+    assert lib.bi_sdpa_kernel_name(1, 32, 1, 300, 160, BF16).decode() == "sdpa_split+combine"
+    assert lib.bi_sdpa_kernel_name(1, 32, 1, 300, 64, F32).decode() == "sdpa_split+combine"
     for bad in ((0, 32, 1, 10, 128, BF16), (1, 32, 1, 0, 128, BF16), (1, 32, 1, 10, 80, BF16),
                 (1, 32, 1, 10, 288, BF16), (1, 32, 1, 10, 128, 7)):
         assert lib.bi_sdpa_kernel_name(*bad).decode() == "none"

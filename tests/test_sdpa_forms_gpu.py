@@ -160,6 +160,34 @@ def test_head_dims_multiple_of_32(dt, D):
     assert_bits_equal(z, round_ref(oracle.sdpa(q0, k[:1], vi, causal=True), dt), f"D={D}: zero-query means")
 
 
+@pytest.mark.parametrize("D", [64, 96])
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16], ids=_ids)
+def test_small_head_dims_agree_across_kernels(dt, D):
+    """16-bit D < 128: the one-launch and prefill kernels run on rows zero-padded to 128, the split
+    kernel on the real rows; the zero products only add exact zeros, so every path gives the same
+    bits.  Prefill chunk (prefill kernel) vs the decode of its tokens (one launch at S <= 1024, split
+    kernel above)."""
+    B, Hq, Hkv, Lq, S = 1, 8, 2, 400, 1500
+    q, k, v = _gpu(*_qkv(B, Hq, Hkv, Lq, S, D, dt, 370 + D))
+    lib = bi._native.load()
+    assert lib.bi_sdpa_kernel_name(B, Hq, Lq, S, D, bi.BI_BF16).decode() == "sdpa_prefill16"
+    full = bi.bi_sdpa(q, k, v, causal=True)
+    for i in (0, 150, 399):
+        p = S - Lq + i
+        dec = bi.bi_sdpa(q[:, :, i:i + 1], k[:, :, :p + 1], v[:, :, :p + 1], causal=True)
+        assert_bits_equal(dec[:, :, 0], full[:, :, i], f"D={D}: prefill token {i} vs its split-kernel decode")
+    short = bi.bi_sdpa(q[:, :, :3], k[:, :, :900], v[:, :, :900], causal=True)      # one launch, padded
+    for i in range(3):
+        p = 900 - 3 + i
+        dec = bi.bi_sdpa(q[:, :, i:i + 1], k[:, :, :p + 1], v[:, :, :p + 1], causal=True)
+        assert_bits_equal(dec[:, :, 0], short[:, :, i], f"D={D}: one-launch row {i} vs its decode")
+    m = torch.ones(1, 1, 1, S, dtype=torch.bool, device=DEV)
+    m[..., 900:] = False                               # 900 keys through the split kernel (S = 1500)
+    qd = q[:, :, :1]
+    assert_bits_equal(bi.bi_sdpa(qd, k, v, mask=m), bi.bi_sdpa(qd, k[:, :, :900], v[:, :, :900]),
+                      f"D={D}: split kernel with masked keys vs one launch")
+
+
 def test_forms_together_and_bad_arguments():
     B, Hq, Hkv, Lq, S, D = 1, 8, 4, 6, 520, 64
     dt = torch.bfloat16
