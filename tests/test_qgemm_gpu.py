@@ -88,3 +88,29 @@ def test_zero_k_gives_bias_and_errors_raise():
     wq3, sc3, sb3 = (t.to(DEV) for t in make(16, 256, 4, 64, dt, 6))
     with pytest.raises(NotImplementedError):                      # 3-bit packings are refused, never guessed
         bi.bi_quantized_linear(torch.zeros((2, 256), dtype=dt, device=DEV), wq3, sc3, sb3, 3, 64)
+
+
+@pytest.mark.parametrize("M", [1, 16, 100])
+def test_graph_replay_equals_eager(M):
+    """Eager vs graph-captured launch (the workspace of the M > 64 path allocated inside the capture):
+    every replay, with eager calls and synchronisations in between, gives the eager bits."""
+    dt = torch.bfloat16
+    wq, sc, sb = (t.to(DEV) for t in make(1000, 768, 4, 64, dt, 390 + M))
+    x = synthetic.randn((M, 768), 391, 1.0, dt).to(DEV)
+    fn = lambda: bi.bi_quantized_linear(x, wq, sc, sb, 4, 64)
+    eager = fn()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out = fn()
+    for rep in range(4):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert_bits_equal(out, eager, f"M={M}: graph replay {rep}")
+        fn()
+        torch.cuda.synchronize()

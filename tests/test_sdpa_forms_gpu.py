@@ -205,3 +205,40 @@ def test_forms_together_and_bad_arguments():
         bi.bi_sdpa(qg, kg, vg, sinks=sinks[:3])
     with pytest.raises(NotImplementedError):            # head dims are multiples of 32
         bi.bi_sdpa(qg[..., :48], kg[..., :48], vg[..., :48])
+
+
+def _graph_replays_equal_eager(fn, eager, what, reps=4):
+    """Capture fn in a graph, replay it several times with eager work and synchronisations in between,
+    and compare every replay with the eager result on raw bits (the output is poisoned before each)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out = fn()
+    for rep in range(reps):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert_bits_equal(out, eager, f"{what}: graph replay {rep}")
+        fn()
+        torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("shape", [(1, 8, 2, 9, 1500), (1, 8, 2, 400, 900)], ids=["split", "prefill"])
+def test_forms_graph_replay_equals_eager(shape):
+    """The benchmark spec's eager vs graph-captured launch, for the additive mask, sinks and a padded
+    head dim (workspace, when the path needs one, allocated inside the captured call)."""
+    B, Hq, Hkv, Lq, S = shape
+    dt = torch.bfloat16
+    q, k, v = _gpu(*_qkv(B, Hq, Hkv, Lq, S, 128, dt, 380 + Lq))
+    amask = _additive((B, 1, Lq, S), 381, dt).to(DEV)
+    amask[..., 0] = 0.0
+    sinks = synthetic.randn((Hq,), 382, 2.0).to(DEV)
+    fn = lambda: bi.bi_sdpa(q, k, v, causal=True, mask=amask, sinks=sinks)
+    _graph_replays_equal_eager(fn, fn(), f"additive mask + sinks {shape}")
+    q64, k64, v64 = _gpu(*_qkv(B, Hq, Hkv, Lq, S, 64, dt, 383 + Lq))
+    fn64 = lambda: bi.bi_sdpa(q64, k64, v64, causal=True)
+    _graph_replays_equal_eager(fn64, fn64(), f"D=64 {shape}")
