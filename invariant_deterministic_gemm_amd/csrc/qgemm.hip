@@ -74,9 +74,10 @@ __device__ __forceinline__ uint32_t opaque(uint32_t x) {
 // Stage geometry of the fused kernel: k per stage, values each producer thread unpacks per stage (one
 // load of VPT * BITS / 8 bytes, one scale and one bias: VPT never exceeds a group), packed words per
 // unit, weight stages in flight per thread.
-template <int FM, int BITS, bool XREG_> struct QStrip {
+template <int FM, int BITS, bool XREG_, int NB> struct QStrip {
     static constexpr int KS = FM == 4 ? 128 : 256;
-    static constexpr int VPT = KS / 16;                          // 16 rows x KS values over 256 threads
+    static constexpr int VPT = NB * KS / 16;                     // 16 NB rows x KS values over 256 threads
+    static constexpr int TPR = 16 / NB;                          // producer threads per weight row
     static constexpr int WPU = VPT * BITS >= 32 ? VPT * BITS / 32 : 1;
     static constexpr bool HALF = VPT * BITS < 32;              // 2 bits, 8 values: half a word
     static constexpr int DEPTH = WPU >= 4 ? 4 : 8;
@@ -185,16 +186,18 @@ __device__ __forceinline__ void unpack8(const typename Words<WPU>::T &w, int h, 
     }
 }
 
-template <int dt, int FM, int BITS, bool XREG_>
-__global__ __launch_bounds__(320) void qgemm16_strip(QGemmParams q) {
+template <int dt, int FM, int BITS, bool XREG_, int NB>
+__global__ __launch_bounds__(64 * (NB + 4)) void qgemm16_strip(QGemmParams q) {
     static_assert(FM == 1 || !XREG_, "x in registers for one fragment only");
-    using G = QStrip<FM, BITS, XREG_>;
+    static_assert(NB == 1 || !XREG_, "x in registers for one strip only");
+    using G = QStrip<FM, BITS, XREG_, NB>;
     constexpr int KS = G::KS, VPT = G::VPT, WPU = G::WPU, QD = G::DEPTH, XU = G::XU, XD = G::XD, XR = G::XR;
     constexpr bool XREG = G::XREG;
     constexpr int ROWB = KS * 2;                 // bytes of one LDS row (KS values of 16 bits)
     constexpr int CH = ROWB / 16;                // 16-byte chunks per LDS row
     constexpr int AR = 16 * FM;                  // x rows per workgroup
-    constexpr int STAGE = (XREG ? 16 : 16 + AR) * ROWB;
+    constexpr int WROWS = 16 * NB;               // weight rows (output columns) per workgroup
+    constexpr int STAGE = (XREG ? WROWS : WROWS + AR) * ROWB;
     constexpr int SPS = KS / 32;                 // chain steps per stage
     constexpr int HS = FM == 1 ? (SPS < 8 ? SPS : 8) : (SPS < 4 ? SPS : 4);   // steps read together
     constexpr uint32_t OOB = 0x80000000u;        // offset past every resource: the load returns zeros
@@ -205,12 +208,12 @@ __global__ __launch_bounds__(320) void qgemm16_strip(QGemmParams q) {
     const GemmParams &p = q.g;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int nstrip = (p.N + 15) / 16;
-    const int n0 = (blockIdx.x % nstrip) * 16;
+    const int nstrip = (p.N + WROWS - 1) / WROWS;
+    const int n0 = (blockIdx.x % nstrip) * WROWS;
     const int m0 = (blockIdx.x / nstrip) * AR;
     const int nst = (p.K + KS - 1) / KS;
     const int nround = (nst + QD - 1) / QD * QD;     // stages the loops run (whole rounds of QD)
-    const int rows = min(16, p.N - n0), xrows = min(AR, p.M - m0);
+    const int rows = min(WROWS, p.N - n0), xrows = min(AR, p.M - m0);
 
     // Buffer resources of this workgroup's rows, each ending at the last byte of its last row's K
     // values (none at all when K = 0, where the tensors may be empty).  Offsets are 32-bit and
@@ -224,9 +227,11 @@ __global__ __launch_bounds__(320) void qgemm16_strip(QGemmParams q) {
         (int)(kb * ((uint32_t)(xrows - 1) * xrow_b + (uint32_t)p.K * 2u)), 0x00020000);
     auto stage_off = [&](int s, uint32_t per) { return s < nst ? (uint32_t)s * per : OOB; };
 
-    if (wave == 0) {
-        // consumer: FM row fragments against the strip's 16 columns; every fragment of a stage is
-        // requested before its first step, so the steps wait on LDS once per stage; k past K is never read
+    if (wave < NB) {
+        // consumer of 16-column strip cb: FM row fragments against its columns; every fragment of a
+        // stage is requested before its first step, so the steps wait on LDS once per stage; k past K
+        // is never read
+        const int cb = wave;
         const int r16 = lane & 15, g = lane >> 4;
         f32x4 acc[FM];
 #pragma unroll
@@ -258,13 +263,14 @@ __global__ __launch_bounds__(320) void qgemm16_strip(QGemmParams q) {
 #pragma unroll
                     for (int v = 0; v < HS; ++v) {
                         const int u = h * HS + v, c = 4 * u + g;
-                        b[v] = *reinterpret_cast<const u32x4 *>(buf + r16 * ROWB + (wslot<VPT / 8>(c, r16) << 4));
+                        b[v] = *reinterpret_cast<const u32x4 *>(buf + (16 * cb + r16) * ROWB +
+                                                                 (wslot<VPT / 8>(c, r16) << 4));
                         if constexpr (XREG) {
                             a[v][0] = row_bcast(xa[j % XR], u);
                         } else {
 #pragma unroll
                             for (int f = 0; f < FM; ++f) {
-                                const int row = 16 + 16 * f + r16;
+                                const int row = WROWS + 16 * f + r16;
                                 a[v][f] = *reinterpret_cast<const u32x4 *>(buf + row * ROWB + ((c ^ (row & 15)) << 4));
                             }
                         }
@@ -287,7 +293,7 @@ __global__ __launch_bounds__(320) void qgemm16_strip(QGemmParams q) {
                 lds_barrier();                           // stage s read; stage s + 1 unpacked
             }
         }
-        const int n = n0 + r16;
+        const int n = n0 + 16 * cb + r16;
         if (n >= p.N) return;
 #pragma unroll
         for (int f = 0; f < FM; ++f)
@@ -299,12 +305,13 @@ __global__ __launch_bounds__(320) void qgemm16_strip(QGemmParams q) {
         return;
     }
 
-    // producers (wavefronts 1-4): unpack the weights (and copy x, several fragments) into the LDS stages
+    // producers (the four wavefronts after the consumers): unpack the weights (and copy x, several
+    // fragments) into the LDS stages
     if (nst == 0) {                                      // K = 0: nothing to load
         lds_barrier();
         return;
     }
-    const int tid = threadIdx.x - 64;
+    const int tid = threadIdx.x - 64 * NB;
     const uint32_t wrow_b = (uint32_t)q.ldwq * 4u, srow_b = (uint32_t)q.ldsb * 2u;
     const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint32_t *>(q.wq + (int64_t)n0 * q.ldwq), 0,
@@ -317,8 +324,8 @@ __global__ __launch_bounds__(320) void qgemm16_strip(QGemmParams q) {
         const_cast<char *>(static_cast<const char *>(q.biases) + (int64_t)n0 * q.ldsb * 2), 0, (int)sb_records,
         0x00020000);
 
-    // this thread's weight unit: row wr of the strip, VPT values at k = KS s + VPT wc of stage s
-    const int wr = tid >> 4, wc = tid & 15;
+    // this thread's weight unit: row wr of the workgroup's rows, VPT values at k = KS s + VPT wc of stage s
+    const int wr = tid / G::TPR, wc = tid % G::TPR;
     const uint32_t w_lane = wr < rows ? (uint32_t)wr * wrow_b + (uint32_t)(VPT * wc * BITS / 8) / 4u * 4u : OOB;
     const uint32_t s_lane = wr < rows ? (uint32_t)wr * srow_b + (uint32_t)((VPT * wc) >> q.group_shift) * 2u : OOB;
     const uint32_t hshift = G::HALF ? 16u * (uint32_t)(wc & 1) : 0u;
@@ -367,7 +374,7 @@ __global__ __launch_bounds__(320) void qgemm16_strip(QGemmParams q) {
 #pragma unroll
         for (int f = 0; f < XU; ++f) {
             const int u = tid + 256 * f, r = u / CH, c = u % CH;
-            const int row = 16 + r;
+            const int row = WROWS + r;
             *reinterpret_cast<u32x4 *>(buf + row * ROWB + ((c ^ (row & 15)) << 4)) = a[f];
         }
     };
@@ -446,15 +453,15 @@ size_t qgemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     return (size_t)(nc * K * 2);
 }
 
-template <int dt, int FM, bool XREG = false>
+template <int dt, int FM, bool XREG = false, int NB = 1>
 static hipError_t launch_fm(const QGemmParams &q, hipStream_t st) {
-    const int64_t nstrip = (q.g.N + 15) / 16, ntile = (q.g.M + 16 * FM - 1) / (16 * FM);
+    const int64_t nstrip = (q.g.N + 16 * NB - 1) / (16 * NB), ntile = (q.g.M + 16 * FM - 1) / (16 * FM);
     const int64_t nwg = nstrip * ntile;
     if (nwg > INT32_MAX) return hipErrorInvalidConfiguration;
-    const dim3 grid((unsigned)nwg), block(320);
-    if (q.bits == 2) hipLaunchKernelGGL((qgemm16_strip<dt, FM, 2, XREG>), grid, block, 0, st, q);
-    else if (q.bits == 4) hipLaunchKernelGGL((qgemm16_strip<dt, FM, 4, XREG>), grid, block, 0, st, q);
-    else if (q.bits == 8) hipLaunchKernelGGL((qgemm16_strip<dt, FM, 8, XREG>), grid, block, 0, st, q);
+    const dim3 grid((unsigned)nwg), block(64 * (NB + 4));
+    if (q.bits == 2) hipLaunchKernelGGL((qgemm16_strip<dt, FM, 2, XREG, NB>), grid, block, 0, st, q);
+    else if (q.bits == 4) hipLaunchKernelGGL((qgemm16_strip<dt, FM, 4, XREG, NB>), grid, block, 0, st, q);
+    else if (q.bits == 8) hipLaunchKernelGGL((qgemm16_strip<dt, FM, 8, XREG, NB>), grid, block, 0, st, q);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }
@@ -462,12 +469,14 @@ static hipError_t launch_fm(const QGemmParams &q, hipStream_t st) {
 template <int dt>
 static hipError_t launch_dt(const QGemmParams &q, hipStream_t st) {
     const int rows = qgemm_tile_rows(q.g.M);
+    // two 16-column strips per workgroup once N is wide: x is then read half as often
+    const bool wide = (q.g.N + 15) / 16 > QGEMM_WIDE_STRIPS;
     if (rows == 16) {
         if (q.g.M <= QGEMM_XREG_MAX_M) return launch_fm<dt, 1, true>(q, st);
-        return launch_fm<dt, 1>(q, st);
+        return wide ? launch_fm<dt, 1, false, 2>(q, st) : launch_fm<dt, 1>(q, st);
     }
-    if (rows == 32) return launch_fm<dt, 2>(q, st);
-    return launch_fm<dt, 4>(q, st);
+    if (rows == 32) return wide ? launch_fm<dt, 2, false, 2>(q, st) : launch_fm<dt, 2>(q, st);
+    return wide ? launch_fm<dt, 4, false, 2>(q, st) : launch_fm<dt, 4>(q, st);
 }
 
 template <int dt>

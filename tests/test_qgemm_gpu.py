@@ -42,6 +42,9 @@ CASES = [  # M, N, K, bits, gs
     (70, 8200, 256, 4, 64),   # more than 64 rows: dequantised in two chunks of columns (8192 + 8)
     # one row (x loaded by the consumer itself) and few rows, with partial last stages
     (1, 100, 352, 8, 32), (1, 33, 160, 2, 32), (2, 77, 4160, 4, 64), (5, 200, 800, 2, 32),
+    # wide N (more than 256 strips of 16 columns): two strips per workgroup, ragged last pair
+    (2, 4200, 512, 4, 64), (16, 4113, 288, 8, 32), (17, 5000, 384, 2, 128), (40, 4500, 640, 4, 32),
+    (64, 4104, 256, 8, 64),
 ]
 
 
@@ -60,10 +63,10 @@ def test_equals_linear_on_dequantised_weight_and_oracle(M, N, K, bits, gs, dt):
     assert_close_to_oracle(y, want, f"M={M} N={N} K={K} bits={bits} gs={gs}")
 
 
-@pytest.mark.parametrize("bits,gs", [(4, 64), (8, 32), (2, 128)])
-def test_rows_do_not_depend_on_batch(bits, gs):
+@pytest.mark.parametrize("bits,gs,N", [(4, 64, 1536), (8, 32, 1536), (2, 128, 1536), (4, 64, 4500)])
+def test_rows_do_not_depend_on_batch(bits, gs, N):
     dt = torch.bfloat16
-    N, K, Mmax = 1536, 2048, 200
+    K, Mmax = 2048, 200
     wq, sc, sb = (t.to(DEV) for t in make(N, K, bits, gs, dt, 99 + bits))
     x = synthetic.randn((Mmax, K), 98, 1.0, dt).to(DEV)
     full = bi.bi_quantized_linear(x, wq, sc, sb, bits, gs)
