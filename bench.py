@@ -129,8 +129,8 @@ def build_step(torch, bi, lib, _native, synthetic, dev):
                 flops = 2.0 * M * N * K + M * N
                 nbytes = 2.0 * (M * K + N * K + M * N + N)
                 launches.append((kname, "gemm", fn, flops, nbytes, dict(N=N, M=M, form=form)))
-    sname = lib.bi_sdpa_kernel_name(1, 32, 1, S3, 128, _native.BI_BF16).decode()
     for L in Lqs:
+        sname = lib.bi_sdpa_kernel_name(1, 32, 8, L, S3, 128, _native.BI_BF16).decode()
         fn = (lambda L=L: bi.bi_sdpa(q3[:, :, S3 - L:], k3, v3, causal=True))
         nbytes = 2.0 * (2 * 8 * S3 * 128 + 2 * 32 * L * 128)
         vis = sum(S3 - L + i + 1 for i in range(L))
@@ -141,7 +141,7 @@ def build_step(torch, bi, lib, _native, synthetic, dev):
     for rec in launches:
         groups.setdefault(rec[0], []).append(rec)
     return dict(K=K, Ms=Ms, Ns=Ns, data=data, q3=q3, k3=k3, v3=v3, S3=S3, launches=launches,
-                groups=groups, names=list(groups), sdpa_group=sname)
+                groups=groups, names=list(groups))
 
 
 def main():
@@ -251,7 +251,7 @@ def main():
                     diff_rows += int(neq.sum().item())
                     checked_rows += M
     ref_o = bi.bi_sdpa(q3[:, :, S3 - 64:], k3, v3, causal=True)
-    for rec, out in zip(groups[st["sdpa_group"]], outs[st["sdpa_group"]]):
+    for rec, out in ((r, o) for g in names for r, o in zip(groups[g], outs[g]) if r[1] == "sdpa"):
         L = rec[5]["Lq"]
         neq = (out.view(torch.int16) != ref_o[:, :, 64 - L:].view(torch.int16)).any(dim=-1)
         diff_rows += int(neq.sum().item())
@@ -391,7 +391,7 @@ def measure_cells(bi, lib, torch, dev, synthetic, data, launches, groups, names,
         q = torch.randn((B, 32, 1, 128), generator=gen, device=dev).to(torch.bfloat16)
         k = torch.randn((B, 8, S, 128), generator=gen, device=dev).to(torch.bfloat16)
         v = torch.randn((B, 8, S, 128), generator=gen, device=dev).to(torch.bfloat16)
-        ws = torch.empty(bi.sdpa_workspace_bytes(B, 32, 1, S, 128, torch.bfloat16), dtype=torch.uint8, device=dev)
+        ws = torch.empty(bi.sdpa_workspace_bytes(B, 32, 8, 1, S, 128, torch.bfloat16), dtype=torch.uint8, device=dev)
         ms = _time_graph(torch, lambda: bi.bi_sdpa(q, k, v, causal=True, workspace=ws), reps=4, iters=6)
         nbytes = 2.0 * (B * 8 * S * 128 * 2 + 2 * B * 32 * 128)
         gbps = nbytes / (ms * 1e-3) / 1e9
@@ -407,7 +407,7 @@ def measure_cells(bi, lib, torch, dev, synthetic, data, launches, groups, names,
         q = torch.randn((B, 32, 1, 128), generator=gen, device=dev).to(torch.bfloat16)
         k = torch.randn((B, 8, S, 128), generator=gen, device=dev).to(torch.bfloat16)
         v = torch.randn((B, 8, S, 128), generator=gen, device=dev).to(torch.bfloat16)
-        ws = torch.empty(lib.bi_sdpa_workspace_bytes(B, 32, 1, S, 128, bi.BI_BF16), dtype=torch.uint8, device=dev)
+        ws = torch.empty(lib.bi_sdpa_workspace_bytes(B, 32, 8, 1, S, 128, bi.BI_BF16), dtype=torch.uint8, device=dev)
         sinks = torch.randn((32,), generator=gen, device=dev)
         keep = torch.rand((B, 1, 1, S), generator=gen, device=dev) > 0.1
         m8 = keep.to(torch.uint8)
@@ -433,21 +433,21 @@ def measure_cells(bi, lib, torch, dev, synthetic, data, launches, groups, names,
         q = torch.randn((B, 32, 1, D), generator=gen, device=dev).to(torch.bfloat16)
         k = torch.randn((B, 8, S, D), generator=gen, device=dev).to(torch.bfloat16)
         v = torch.randn((B, 8, S, D), generator=gen, device=dev).to(torch.bfloat16)
-        ws = torch.empty(lib.bi_sdpa_workspace_bytes(B, 32, 1, S, D, bi.BI_BF16), dtype=torch.uint8, device=dev)
+        ws = torch.empty(lib.bi_sdpa_workspace_bytes(B, 32, 8, 1, S, D, bi.BI_BF16), dtype=torch.uint8, device=dev)
         ms = _time_graph(torch, lambda: bi.bi_sdpa(q, k, v, causal=True, workspace=ws), reps=4, iters=6)
         gbps = 2.0 * (B * 8 * S * D * 2) / (ms * 1e-3) / 1e9
         cells["attention_forms"].append({"B": B, "S": S, "D": D, "form": "causal decode", "us": round(ms * 1e3, 1),
                                          "GBps": round(gbps, 1), "frac_hbm": round(gbps / HBM_PEAK_GBPS, 4),
-                                         "kernel": lib.bi_sdpa_kernel_name(B, 32, 1, S, D, bi.BI_BF16).decode()})
+                                         "kernel": lib.bi_sdpa_kernel_name(B, 32, 8, 1, S, D, bi.BI_BF16).decode()})
         qp = torch.randn((1, 32, 2048, D), generator=gen, device=dev).to(torch.bfloat16)
         kp = torch.randn((1, 8, 2048, D), generator=gen, device=dev).to(torch.bfloat16)
-        wsp = torch.empty(lib.bi_sdpa_workspace_bytes(1, 32, 2048, 2048, D, bi.BI_BF16), dtype=torch.uint8, device=dev)
+        wsp = torch.empty(lib.bi_sdpa_workspace_bytes(1, 32, 8, 2048, 2048, D, bi.BI_BF16), dtype=torch.uint8, device=dev)
         ms = _time_graph(torch, lambda: bi.bi_sdpa(qp, kp, kp, causal=True, workspace=wsp), reps=2, iters=4)
         tf = 4.0 * 32 * D * (2048 * 2049 / 2) / (ms * 1e-3) / 1e12
         cells["attention_forms"].append({"B": 1, "Lq": 2048, "S": 2048, "D": D, "form": "causal prefill",
                                          "us": round(ms * 1e3, 1), "TFLOPs": round(tf, 1),
                                          "frac_mfma": round(tf / BF16_PEAK_TFLOPS, 4),
-                                         "kernel": lib.bi_sdpa_kernel_name(1, 32, 2048, 2048, D, bi.BI_BF16).decode()})
+                                         "kernel": lib.bi_sdpa_kernel_name(1, 32, 8, 2048, 2048, D, bi.BI_BF16).decode()})
         del q, k, v, ws, qp, kp, wsp
     # long causal prefill (query chunk = whole cache): workspace-free kernel, flops of visible pairs
     for S in (4096, 8192):
@@ -461,7 +461,7 @@ def measure_cells(bi, lib, torch, dev, synthetic, data, launches, groups, names,
         tf = flops / (ms * 1e-3) / 1e12
         cells["prefill_attention"].append({"B": 1, "Lq": S, "S": S, "us": round(ms * 1e3, 1), "TFLOPs": round(tf, 1),
                                            "frac_mfma": round(tf / BF16_PEAK_TFLOPS, 4),
-                                           "kernel": lib.bi_sdpa_kernel_name(1, 32, S, S, 128, bi.BI_BF16).decode()})
+                                           "kernel": lib.bi_sdpa_kernel_name(1, 32, 8, S, S, 128, bi.BI_BF16).decode()})
         del q, k, v
     # quantized linear (4-bit, groups of 64): packed weights rotate through copies so reads are cold;
     # bytes = packed words + scales + biases + x + y; rows checked against M = 256 on raw bits

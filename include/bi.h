@@ -156,13 +156,14 @@ bi_status bi_addmm(const void *cin, int64_t ldcin,
  * head dimensions must be multiples of 32); Hq % Hkv == 0; Lq <= S when causal; every
  * base pointer 16-byte aligned and every stride except the last a multiple
  * of 8 (16-bit) or 4 (fp32) elements.
- * Workspace: ws must hold bi_sdpa_workspace_bytes(B, Hq, Lq, S, D, dt) bytes,
- * 256-byte aligned, device memory owned by the caller; its contents on entry
- * do not matter and on return are unspecified.  Two calls that run at the
- * same time must not share a workspace.  The query returns 0 (ws may then be
- * NULL) for the shapes served without a workspace: 16-bit dt with D <= 128
- * and either S <= 1024 (one launch, splits folded in LDS) or Lq >= 384
- * (prefill: splits folded in registers).  Every path computes the same bits.
+ * Workspace: ws must hold bi_sdpa_workspace_bytes(B, Hq, Hkv, Lq, S, D, dt)
+ * bytes, 256-byte aligned, device memory owned by the caller; its contents on
+ * entry do not matter and on return are unspecified.  Two calls that run at
+ * the same time must not share a workspace.  The query returns 0 (ws may then
+ * be NULL) for the shapes served without a workspace: 16-bit dt with D <= 128
+ * and either Lq >= 384 (prefill: splits folded in registers) or S <= 1024 with
+ * more than 256 (row tile, split) workgroups (one launch, splits folded in
+ * LDS); see bi_sdpa_kernel_name.  Every path computes the same bits.
  */
 bi_status bi_sdpa(const void *q, const int64_t q_str[4],
                   const void *k, const int64_t k_str[4],
@@ -176,8 +177,9 @@ bi_status bi_sdpa(const void *q, const int64_t q_str[4],
                   void *stream);
 
 /* Bytes of workspace bi_sdpa needs for these sizes and dtype (0 when there is
- * nothing to do, when the path taken needs none, or for an unknown dtype). */
-size_t bi_sdpa_workspace_bytes(int64_t B, int64_t Hq, int64_t Lq, int64_t S, int64_t D, bi_dtype dt);
+ * nothing to do, when the path taken needs none, for Hkv <= 0 or Hq not a
+ * multiple of Hkv, or for an unknown dtype). */
+size_t bi_sdpa_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t S, int64_t D, bi_dtype dt);
 
 /*
  * bi_sdpa with every mask form and attention sinks (README, section "How the
@@ -304,15 +306,19 @@ size_t bi_quantized_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, bi_d
  * Returns "none" for empty or oversized shapes. */
 const char *bi_gemm_kernel_name(int64_t M, int64_t N, int64_t K, bi_dtype in_dt, int b_kn);
 
-/* Which attention kernels a bi_sdpa call of these sizes runs: "sdpa_prefill16"
- * (16-bit, D <= 128, Lq >= 384), "sdpa_fused16" (16-bit, D <= 128, Lq < 384,
- * S <= 1024), "sdpa_split16+combine" (other 16-bit D = 128 calls) or
- * "sdpa_split+combine" (fp32, and every other 16-bit call).  16-bit D < 128
- * runs the prefill and one-launch kernels on rows zero-padded to 128 (the
- * padding adds exact zeros, so the bits are the split kernel's).  Informational: the split / block
- * structure, and with it every output bit, is the same whichever runs.
- * Returns "none" for empty, oversized or unsupported sizes. */
-const char *bi_sdpa_kernel_name(int64_t B, int64_t Hq, int64_t Lq, int64_t S, int64_t D, bi_dtype dt);
+/* Which attention kernels a bi_sdpa call of these sizes runs.  For 16-bit dt
+ * and D <= 128: "sdpa_prefill16" when Lq >= 384; else "sdpa_quad16+combine"
+ * when the quad grid, ceil(S / 256) splits x ceil((Hq / Hkv) Lq / 16) row
+ * tiles x B x Hkv workgroups, is at most 256 (one workgroup per CU: every
+ * split's K / V requested at once); else "sdpa_fused16" when S <= 1024, and
+ * "sdpa_split16+combine" (D = 128) or "sdpa_split+combine" (D < 128)
+ * otherwise.  fp32 and D > 128 run "sdpa_split+combine".  16-bit D < 128 runs
+ * the prefill, quad and one-launch kernels on rows zero-padded to 128 (the
+ * padding adds exact zeros, so the bits are the split kernel's).
+ * Informational: the split / block structure, and with it every output bit,
+ * is the same whichever runs.  Returns "none" for empty, oversized or
+ * unsupported sizes. */
+const char *bi_sdpa_kernel_name(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t S, int64_t D, bi_dtype dt);
 
 /* Name of a status code ("BI_OK", ...); never NULL. */
 const char *bi_status_name(bi_status s);

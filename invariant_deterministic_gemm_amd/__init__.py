@@ -214,9 +214,9 @@ def bi_addmm(c: torch.Tensor | None, a: torch.Tensor, b: torch.Tensor, alpha: fl
     return y
 
 
-def sdpa_workspace_bytes(B: int, Hq: int, Lq: int, S: int, D: int, dtype: torch.dtype) -> int:
+def sdpa_workspace_bytes(B: int, Hq: int, Hkv: int, Lq: int, S: int, D: int, dtype: torch.dtype) -> int:
     """Bytes of workspace bi_sdpa needs for these sizes and dtype (0 when the path taken needs none)."""
-    return int(_native.load().bi_sdpa_workspace_bytes(B, Hq, Lq, S, D, _DT[dtype]))
+    return int(_native.load().bi_sdpa_workspace_bytes(B, Hq, Hkv, Lq, S, D, _DT[dtype]))
 
 
 def _mask_strides(mask: torch.Tensor, shape) -> tuple:
@@ -278,7 +278,7 @@ def bi_sdpa(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fa
             raise ValueError("sinks must hold one logit per query head")
         sk = torch.as_tensor(sinks).reshape(Hq).to(device=dev, dtype=torch.float32).contiguous()
     lib = _native.load()
-    need = int(lib.bi_sdpa_workspace_bytes(B, Hq, Lq, S, D, _dt(q, "bi_sdpa")))
+    need = int(lib.bi_sdpa_workspace_bytes(B, Hq, Hkv, Lq, S, D, _dt(q, "bi_sdpa")))
     ws = workspace
     if need > 0 and (ws is None or ws.numel() * ws.element_size() < need):
         ws = torch.empty(need, dtype=torch.uint8, device=dev)

@@ -24,7 +24,8 @@
 
 namespace {
 
-constexpr int kAbiMajor = 1;
+// Major 2: the attention path queries take Hkv (the kernel choice depends on the grid size).
+constexpr int kAbiMajor = 2;
 // Bump when a compile-time constant that shapes arithmetic changes
 // (k-step order, MFMA shapes, KV_SPLIT / KV_BLOCK, combine order).
 // 3: 16-bit GEMM chain on v_mfma_f32_16x16x32 again (2 used 32x32x16).
@@ -203,9 +204,9 @@ bi_status bi_addmm(const void *cin, int64_t ldcin, const void *a, int64_t lda, c
     return device_status(bi::launch_gemm(p, in_dt, out_dt, b_kn, (hipStream_t)stream), "bi_addmm");
 }
 
-size_t bi_sdpa_workspace_bytes(int64_t B, int64_t Hq, int64_t Lq, int64_t S, int64_t D, bi_dtype dt) {
+size_t bi_sdpa_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t S, int64_t D, bi_dtype dt) {
     if (!dtype_known(dt)) return 0;
-    return bi::sdpa_workspace_bytes(B, Hq, Lq, S, D, (int)dt);
+    return bi::sdpa_workspace_bytes(B, Hq, Hkv, Lq, S, D, (int)dt);
 }
 
 static bi_status sdpa_impl(const char *fn, const void *q, const int64_t q_str[4], const void *k,
@@ -261,7 +262,7 @@ static bi_status sdpa_impl(const char *fn, const void *q, const int64_t q_str[4]
             return fail(BI_ERR_UNSUPPORTED, "%s: additive mask misaligned for its dtype", fn);
     }
     if (sinks != nullptr && !aligned_to(sinks, 4)) return fail(BI_ERR_UNSUPPORTED, "%s: sinks misaligned", fn);
-    const size_t need = bi::sdpa_workspace_bytes(B, Hq, Lq, S, D, (int)dt);
+    const size_t need = bi::sdpa_workspace_bytes(B, Hq, Hkv, Lq, S, D, (int)dt);
     if (need > 0 && (ws == nullptr || ws_bytes < need))
         return fail(BI_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
                     ws == nullptr ? (size_t)0 : ws_bytes);
@@ -432,11 +433,11 @@ const char *bi_gemm_kernel_name(int64_t M, int64_t N, int64_t K, bi_dtype in_dt,
     return bi::gemm_kernel_name((int)M, (int)N, (int)K, (int)in_dt, b_kn != 0);
 }
 
-const char *bi_sdpa_kernel_name(int64_t B, int64_t Hq, int64_t Lq, int64_t S, int64_t D, bi_dtype dt) {
-    if (B <= 0 || Hq <= 0 || Lq <= 0 || S <= 0 || B > kMaxDim || Hq > kMaxDim || Lq > kMaxDim || S > kMaxDim ||
-        (D <= 0 || D % 32 != 0 || D > 256) || !dtype_known(dt))
+const char *bi_sdpa_kernel_name(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t S, int64_t D, bi_dtype dt) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || Lq <= 0 || S <= 0 || B > kMaxDim || Hq > kMaxDim ||
+        Lq > kMaxDim || S > kMaxDim || (D <= 0 || D % 32 != 0 || D > 256) || !dtype_known(dt))
         return "none";
-    return bi::sdpa_kernel_name(Lq, S, D, (int)dt);
+    return bi::sdpa_kernel_name(B, Hq, Hkv, Lq, S, D, (int)dt);
 }
 
 const char *bi_status_name(bi_status s) {

@@ -29,19 +29,21 @@ struct SdpaParams {
     float *ws_o;                          // [rows][nsplit][D]
 };
 
-// Which kernels serve a call.  Every path computes the same bits; only the
-// split path uses a workspace.
+// Which kernels serve a call.  Every path computes the same bits; the split
+// and quad paths use a workspace.
 enum SdpaPath {
     SDPA_FUSED16,     // 16-bit, D <= 128, at most four splits: one launch, fold in LDS
     SDPA_PREFILL16,   // 16-bit, D <= 128, long caches with many query rows: fold in registers
+    SDPA_QUAD16,      // 16-bit, D <= 128, small grids: one wavefront per block, combine kernel
     SDPA_SPLIT        // split kernel + combine kernel through the workspace
 };
-SdpaPath sdpa_path(int64_t Lq, int64_t S, int64_t D, int dt);
-size_t sdpa_workspace_bytes(int64_t B, int64_t Hq, int64_t Lq, int64_t S, int64_t D, int dt);
+// Hkv >= 1 and Hq % Hkv == 0 (the callers validate).
+SdpaPath sdpa_path(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t S, int64_t D, int dt);
+size_t sdpa_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t S, int64_t D, int dt);
 // Carves ws into ws_ml / ws_o (p.nsplit must be set).
 void sdpa_bind_workspace(SdpaParams &p, void *ws);
 hipError_t launch_sdpa(const SdpaParams &p, int dt, int D, hipStream_t stream);
 // Names of the kernels launch_sdpa runs ("sdpa_fused16", ...).
-const char *sdpa_kernel_name(int64_t Lq, int64_t S, int64_t D, int dt);
+const char *sdpa_kernel_name(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t S, int64_t D, int dt);
 
 }  // namespace bi

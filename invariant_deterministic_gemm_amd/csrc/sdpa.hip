@@ -802,6 +802,198 @@ __global__ __launch_bounds__(64 * FUSED_MAXW) void sdpa_fused16(SdpaParams p) {
     }
 }
 
+// Few query rows: one workgroup per (row tile, split, batch, KV head) with
+// one wavefront per 64-key block of the split, so the whole split (K and V,
+// 128 KiB) is requested at once instead of one block at a time.  The
+// online-softmax recurrence of split16_body is then evaluated in stages that
+// keep every operation and operand of it:
+//   1. wavefront j computes block j's scores and their row maximum;
+//   2. each wavefront rebuilds the running maximum before its block from the
+//      earlier blocks' maxima (the same select / fmaxf sequence), then its
+//      alpha, P (rounded as in split16_body) and row sum;
+//   3. l = fmaf(l, alpha, sum) runs over the blocks in order, and
+//      O = O * alpha, O += P . V over the blocks in order, each wavefront for
+//      two of the eight 16-wide column tiles (columns are independent chains).
+// The split's (m, l, O) goes to the workspace like sdpa_split16's, and the
+// combine kernel folds the splits, so the bits are those of the split path.
+template <int dt>
+__global__ __launch_bounds__(64 * 4) void sdpa_quad16(SdpaParams p) {
+    constexpr int ROWB = 256;
+    constexpr int KBYTES = KV_BLOCK * ROWB;           // one K (or V) block
+    constexpr int QB = KBYTES / 1024;                 // 1 KiB load instructions per block half
+    constexpr int BPS = KV_SPLIT / KV_BLOCK;          // blocks per split = wavefronts
+    constexpr float NEG_INF = -__builtin_huge_valf();
+    static_assert(BPS == 4 && QB == 16, "four wavefronts, four key rows per load instruction");
+    __shared__ __attribute__((aligned(1024))) char lds[BPS * 2 * KBYTES];   // [block][K block | V block]
+    __shared__ u32x4 pbuf[BPS][2][64];                 // P fragments: block, half c, lane
+    __shared__ float xm[BPS][16], xa[BPS][16], xr[BPS][16];   // per block and row: maximum, alpha, sum
+
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int r16 = lane & 15, g = lane >> 4;
+    const int R = p.G * p.Lq;
+    int tile, grp;
+    attn_work((R + 15) / 16, p.nsplit * p.B * p.Hkv, tile, grp);
+    const int sp = grp % p.nsplit;
+    const int b = grp / p.nsplit / p.Hkv, gk = grp / p.nsplit % p.Hkv;
+
+    const int kbeg = sp * KV_SPLIT;
+    const int kend = min(kbeg + KV_SPLIT, p.S);
+    int nblk = (kend - kbeg + KV_BLOCK - 1) / KV_BLOCK;
+    if (p.causal) {
+        const int rlast = min(tile * 16 + 15, R - 1);
+        const int pos_last = p.S - p.Lq + rlast / p.G;
+        nblk = pos_last < kbeg ? 0 : min(nblk, (pos_last - kbeg) / KV_BLOCK + 1);
+    }
+    const int kb = kbeg + w * KV_BLOCK;               // this wavefront's block
+    const bool active = w < nblk;
+    char *Ks = lds + w * 2 * KBYTES;
+    char *Vs = Ks + KBYTES;
+
+    // ---- stage 1: q, then the block's K and V (direct to LDS, layout as split16_body), then scores
+    Rows16 r;
+    float mb = NEG_INF;
+    float s[4][4];
+    const int lrow = lane >> 4, lslot = lane & 15;
+    if (active) {
+        rows16_load<dt>(p, tile, b, gk, r);
+        const char *kbase = static_cast<const char *>(p.k) + ((int64_t)b * p.ks[0] + (int64_t)gk * p.ks[1]) * 2;
+        const char *vbase = static_cast<const char *>(p.v) + ((int64_t)b * p.vs[0] + (int64_t)gk * p.vs[1]) * 2;
+        const int64_t kstr = p.ks[2] * 2, vstr = p.vs[2] * 2;
+        const char *zp = reinterpret_cast<const char *>(g_zero_page);
+#pragma unroll
+        for (int q = 0; q < QB; ++q) {
+            const int row = 4 * q + lrow;
+            const int c = lslot ^ (row & 15);
+            const int64_t key = min(kb + row, p.S - 1);          // rows past S read row S - 1
+            __builtin_amdgcn_global_load_lds(static_cast<const void *>(8 * c >= p.dr ? zp : kbase + key * kstr + (c << 4)),
+                                             BI_LDS_PTR(Ks + q * 1024), 16, 0, 0);
+        }
+#pragma unroll
+        for (int q = 0; q < QB; ++q) {
+            const int row = 4 * q + lrow;
+            const int c = lslot ^ ((row & 7) << 1);
+            const int64_t key = min(kb + row, p.S - 1);
+            __builtin_amdgcn_global_load_lds(static_cast<const void *>(8 * c >= p.dr ? zp : vbase + key * vstr + (c << 4)),
+                                             BI_LDS_PTR(Vs + q * 1024), 16, 0, 0);
+        }
+        BI_WAIT_VMCNT(QB);                            // q and the K block landed (V may be in flight)
+        f32x4 st[4];
+        attn_scores16<dt>(r, Ks, st);
+        const bool visible = p.mask == nullptr && kb + KV_BLOCK <= p.S && (!p.causal || kb + KV_BLOCK - 1 <= r.pos_first);
+        if (visible) {
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s[kt][i] = st[kt][i] * p.c;
+        } else {
+            block_scores<dt>(p, r.mrow, kb, g, r.row_ok, r.pos, st, s);
+        }
+        float mk[4];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) mk[kt] = fmaxf(fmaxf(s[kt][0], s[kt][1]), fmaxf(s[kt][2], s[kt][3]));
+        mb = fmaxf(NEG_INF, fmaxf(fmaxf(mk[0], mk[1]), fmaxf(mk[2], mk[3])));   // all-NaN -> -inf
+        mb = max_xor32(max_xor16(mb));
+        if (g == 0) xm[w][r16] = mb;
+    }
+    __syncthreads();
+
+    // ---- stage 2: the running maximum before this block, alpha, P and the row sum
+    if (active) {
+        float m_run = NEG_INF;
+        for (int u = 0; u < w; ++u) {
+            const float mu = xm[u][r16];
+            m_run = mu == NEG_INF ? m_run : fmaxf(m_run, mu);
+        }
+        const bool empty = mb == NEG_INF;
+        const float m_new = empty ? m_run : fmaxf(m_run, mb);
+        const float alpha = empty ? 1.0f : exp2_hw(m_run - m_new);
+        const float mref = empty ? 0.0f : m_new;
+        float pr[4][4];
+        float rs = 0.0f;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                pr[kt][i] = exp2_hw(s[kt][i] - mref);
+                rs = rs + pr[kt][i];
+            }
+        rs = add_xor32(add_xor16(rs));
+        if (g == 0) {
+            xa[w][r16] = alpha;
+            xr[w][r16] = rs;
+        }
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+            pbuf[w][c][lane] = u32x4{pack_p<dt>(pr[2 * c][0], pr[2 * c][1]), pack_p<dt>(pr[2 * c][2], pr[2 * c][3]),
+                                     pack_p<dt>(pr[2 * c + 1][0], pr[2 * c + 1][1]),
+                                     pack_p<dt>(pr[2 * c + 1][2], pr[2 * c + 1][3])};
+        BI_WAIT_VMCNT(0);                             // the V block landed
+        if (kb + KV_BLOCK > p.S) {                    // V rows past S read as zero
+            for (int row = max(p.S - kb, 0) + lrow; row < KV_BLOCK; row += 4)
+                *reinterpret_cast<u32x4 *>(Vs + row * ROWB + lslot * 16) = zero_u4();
+        }
+    }
+    __syncthreads();
+
+    // ---- stage 3: l and m over the blocks in order; O for column tiles 2 w, 2 w + 1
+    float l_run = 0.0f, m_run = NEG_INF;
+    f32x4 o[2] = {zero4(), zero4()};
+    for (int u = 0; u < nblk; ++u) {
+        const float alpha = xa[u][r16];
+        const float mu = xm[u][r16];
+        m_run = mu == NEG_INF ? m_run : fmaxf(m_run, mu);
+        l_run = __builtin_fmaf(l_run, alpha, xr[u][r16]);
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float ai = xa[u][4 * g + i];
+                o[0][i] = o[0][i] * ai;
+                o[1][i] = o[1][i] * ai;
+            }
+        }
+        const char *Vu = lds + u * 2 * KBYTES + KBYTES;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const u32x4 pf = pbuf[u][c][lane];
+            const int row0 = 32 * c + 4 * g + (r16 >> 2);
+            const int row1 = row0 + 16;
+            u32x4 vf[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int ch = 2 * (2 * w + j) + ((r16 & 3) >> 1);
+                const int off = 8 * (r16 & 1);
+                const u32x2 lo = lds_read_tr16(Vu + row0 * ROWB + ((ch ^ ((row0 & 7) << 1)) << 4) + off);
+                const u32x2 hi = lds_read_tr16(Vu + row1 * ROWB + ((ch ^ ((row1 & 7) << 1)) << 4) + off);
+                vf[j] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) o[j] = Mfma<dt>::step(pf, vf[j], o[j]);
+        }
+    }
+
+    // ---- the split's partial, as sdpa_split16 stores it
+    const int rg = tile * 16 + r16;
+    if (w == 0 && g == 0 && rg < R) {
+        const int64_t rowid = ((int64_t)b * p.Hq + gk * p.G + rg % p.G) * p.Lq + rg / p.G;
+        float *ml = p.ws_ml + (rowid * p.nsplit + sp) * 2;
+        ml[0] = m_run;
+        ml[1] = l_run;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int ro = tile * 16 + 4 * g + i;
+        if (ro < R) {
+            const int64_t rowid = ((int64_t)b * p.Hq + gk * p.G + ro % p.G) * p.Lq + ro / p.G;
+            float *dst = p.ws_o + (rowid * p.nsplit + sp) * p.dr;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int t = 2 * w + j;
+                if (16 * t < p.dr) dst[16 * t + r16] = o[j][i];
+            }
+        }
+    }
+}
+
 // Long prefill without a workspace: a workgroup of W wavefronts takes W
 // consecutive row tiles of one (batch, KV head) and walks all key blocks in
 // ascending order, each block loaded once into LDS for all W tiles (NB
@@ -1051,17 +1243,30 @@ __global__ __launch_bounds__(D) void sdpa_combine(SdpaParams p) {
 // splits take the workspace-free prefill kernel (measured: below ~300 rows the
 // split kernel's extra parallelism wins, above it the shared K / V blocks do).
 constexpr int64_t PREFILL_MIN_LQ = 384;
+// Calls whose quad grid (one workgroup per row tile and split) holds at most
+// one workgroup per CU take the quad kernel, which requests a whole split at
+// once (measured at 32 query heads, 8 KV heads, D = 128: one decode row at
+// 1024 keys 14.5 -> 12.5 us, 16 rows 19.3 -> 14.1 us, one row at 8192 keys
+// 21.2 -> 17.3 us; with 512 workgroups or more the one-launch and split
+// kernels are faster).
+constexpr int64_t QUAD_MAX_WG = 256;
 
-SdpaPath sdpa_path(int64_t Lq, int64_t S, int64_t D, int dt) {
+SdpaPath sdpa_path(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t S, int64_t D, int dt) {
     if (dt == DT_F32 || D > 128 || S <= 0) return SDPA_SPLIT;
     if (Lq >= PREFILL_MIN_LQ) return SDPA_PREFILL16;
-    if ((S + KV_SPLIT - 1) / KV_SPLIT <= FUSED_MAXW) return SDPA_FUSED16;
+    const int64_t nsplit = (S + KV_SPLIT - 1) / KV_SPLIT;
+    const int64_t tiles = (Hq / Hkv * Lq + 15) / 16;
+    if (B * Hkv <= QUAD_MAX_WG && tiles <= QUAD_MAX_WG && nsplit <= QUAD_MAX_WG &&
+        nsplit * tiles * B * Hkv <= QUAD_MAX_WG)
+        return SDPA_QUAD16;
+    if (nsplit <= FUSED_MAXW) return SDPA_FUSED16;
     return SDPA_SPLIT;
 }
 
-size_t sdpa_workspace_bytes(int64_t B, int64_t Hq, int64_t Lq, int64_t S, int64_t D, int dt) {
-    if (B <= 0 || Hq <= 0 || Lq <= 0 || S <= 0 || D <= 0) return 0;
-    if (sdpa_path(Lq, S, D, dt) != SDPA_SPLIT) return 0;
+size_t sdpa_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t S, int64_t D, int dt) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || Lq <= 0 || S <= 0 || D <= 0) return 0;
+    const SdpaPath path = sdpa_path(B, Hq, Hkv, Lq, S, D, dt);
+    if (path != SDPA_SPLIT && path != SDPA_QUAD16) return 0;
     const int64_t rows = B * Hq * Lq;
     const int64_t nsplit = (S + KV_SPLIT - 1) / KV_SPLIT;
     const int64_t ml = (rows * nsplit * 2 * 4 + 255) / 256 * 256;
@@ -1078,7 +1283,7 @@ void sdpa_bind_workspace(SdpaParams &p, void *ws) {
 template <int dt, int D>
 static hipError_t launch_typed(const SdpaParams &p, hipStream_t st) {
     const int R = p.G * p.Lq;
-    const SdpaPath path = sdpa_path(p.Lq, p.S, D, dt);
+    const SdpaPath path = sdpa_path(p.B, p.Hq, p.Hkv, p.Lq, p.S, D, dt);
     if constexpr (dt != DT_F32 && D <= 128) {
         if (path == SDPA_PREFILL16) {
             constexpr int W = 4;                         // row tiles per workgroup sharing each K / V block
@@ -1094,7 +1299,15 @@ static hipError_t launch_typed(const SdpaParams &p, hipStream_t st) {
             return hipGetLastError();
         }
     }
-    if (p.nsplit > 0) {
+    if (p.nsplit > 0 && path == SDPA_QUAD16) {
+        if constexpr (dt != DT_F32 && D <= 128) {
+            const int64_t nwg = (int64_t)p.nsplit * ((R + 15) / 16) * p.B * p.Hkv;
+            if (nwg > INT32_MAX) return hipErrorInvalidConfiguration;
+            hipLaunchKernelGGL((sdpa_quad16<dt>), dim3((unsigned)nwg), dim3(64 * 4), 0, st, p);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+    } else if (p.nsplit > 0) {
         if constexpr (dt != DT_F32 && D == 128) {     // (below 128 the generic kernel decodes faster)
             constexpr int W = 2;                         // splits per workgroup (measured best for long caches)
             const int64_t nwg = (int64_t)((p.nsplit + W - 1) / W) * ((R + 15) / 16) * p.B * p.Hkv;
@@ -1113,10 +1326,11 @@ static hipError_t launch_typed(const SdpaParams &p, hipStream_t st) {
     return hipGetLastError();
 }
 
-const char *sdpa_kernel_name(int64_t Lq, int64_t S, int64_t D, int dt) {
-    switch (sdpa_path(Lq, S, D, dt)) {
+const char *sdpa_kernel_name(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t S, int64_t D, int dt) {
+    switch (sdpa_path(B, Hq, Hkv, Lq, S, D, dt)) {
         case SDPA_FUSED16: return "sdpa_fused16";
         case SDPA_PREFILL16: return "sdpa_prefill16";
+        case SDPA_QUAD16: return "sdpa_quad16+combine";
         default: return dt != DT_F32 && D == 128 ? "sdpa_split16+combine" : "sdpa_split+combine";
     }
 }

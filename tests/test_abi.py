@@ -52,7 +52,7 @@ def test_exported_symbols_with_nm():
 
 def test_abi_version_and_status_names(lib):
     v = lib.bi_abi_version()
-    assert v >> 16 == 1 and (v & 0xffff) >= 1
+    assert v >> 16 == 2 and (v & 0xffff) >= 1
     names = [lib.bi_status_name(s).decode() for s in range(5)]
     assert names == ["BI_OK", "BI_ERR_INVALID", "BI_ERR_UNSUPPORTED", "BI_ERR_WORKSPACE", "BI_ERR_DEVICE"]
     assert lib.bi_status_name(99).decode() == "BI_UNKNOWN_STATUS"
@@ -124,7 +124,7 @@ def test_sdpa_validation(lib):
     assert sdpa(lib, scale=float("inf")) == INVALID
     # fp32 runs the split path, which needs a workspace
     assert sdpa(lib, dt=F32, ws=None) == WORKSPACE
-    need = lib.bi_sdpa_workspace_bytes(1, 4, 1, 16, 128, F32)
+    need = lib.bi_sdpa_workspace_bytes(1, 4, 2, 1, 16, 128, F32)
     assert need > 0
     assert sdpa(lib, dt=F32, wsb=need - 4) == WORKSPACE
     assert sdpa(lib, dt=F32, ws=ctypes.c_void_p(0x7f0000000010)) == UNSUPPORTED   # workspace 256-byte aligned
@@ -162,23 +162,31 @@ def test_sdpa_ex_validation(lib):
 
 
 def test_sdpa_workspace_formula(lib):
-    # split path: (rows * nsplit * 2 floats, padded to 256 B) + rows * nsplit * D floats
+    # split and quad paths: (rows * nsplit * 2 floats, padded to 256 B) + rows * nsplit * D floats
     def split_bytes(B, Hq, Lq, S, D):
         rows, nsplit = B * Hq * Lq, (S + 255) // 256
         return (rows * nsplit * 8 + 255) // 256 * 256 + rows * nsplit * D * 4
-    assert lib.bi_sdpa_workspace_bytes(2, 32, 3, 1000, 128, F32) == split_bytes(2, 32, 3, 1000, 128)
-    assert lib.bi_sdpa_workspace_bytes(2, 32, 3, 2000, 64, BF16) == split_bytes(2, 32, 3, 2000, 64)
-    assert lib.bi_sdpa_workspace_bytes(2, 32, 3, 1000, 64, BF16) == 0           # one launch, as D = 128
-    assert lib.bi_sdpa_workspace_bytes(2, 32, 3, 1000, 160, BF16) == split_bytes(2, 32, 3, 1000, 160)
-    assert lib.bi_sdpa_workspace_bytes(2, 32, 3, 2000, 128, F16) == split_bytes(2, 32, 3, 2000, 128)
-    # 16-bit D = 128: S <= 1024 (fused) and Lq >= 128 (prefill) need none
-    assert lib.bi_sdpa_workspace_bytes(2, 32, 3, 1000, 128, BF16) == 0
-    assert lib.bi_sdpa_workspace_bytes(2, 32, 3, 1024, 128, BF16) == 0
-    assert lib.bi_sdpa_workspace_bytes(2, 32, 3, 1025, 128, BF16) == split_bytes(2, 32, 3, 1025, 128)
-    assert lib.bi_sdpa_workspace_bytes(1, 32, 384, 32768, 128, BF16) == 0
-    assert lib.bi_sdpa_workspace_bytes(1, 32, 383, 32768, 128, BF16) == split_bytes(1, 32, 383, 32768, 128)
-    assert lib.bi_sdpa_workspace_bytes(1, 1, 1, 0, 128, BF16) == 0
-    assert lib.bi_sdpa_workspace_bytes(1, 1, 1, 10, 128, 7) == 0
+    ws = lib.bi_sdpa_workspace_bytes
+    assert ws(2, 32, 8, 3, 1000, 128, F32) == split_bytes(2, 32, 3, 1000, 128)
+    assert ws(2, 32, 8, 3, 2000, 64, BF16) == split_bytes(2, 32, 3, 2000, 64)     # quad, as D = 128
+    assert ws(2, 32, 8, 3, 1000, 160, BF16) == split_bytes(2, 32, 3, 1000, 160)
+    assert ws(2, 32, 8, 3, 2000, 128, F16) == split_bytes(2, 32, 3, 2000, 128)
+    # 16-bit D <= 128: the quad grid (splits x row tiles x B x Hkv) decides between the quad kernel
+    # (<= 256 workgroups, workspace) and the one-launch kernel (S <= 1024, none) or the split kernel
+    assert ws(8, 32, 8, 1, 1024, 128, BF16) == split_bytes(8, 32, 1, 1024, 128)    # 4 x 1 x 8 x 8 = 256
+    assert ws(9, 32, 8, 1, 1024, 128, BF16) == 0                                   # 288: one launch
+    assert ws(2, 32, 8, 3, 1000, 64, BF16) == split_bytes(2, 32, 3, 1000, 64)
+    assert ws(16, 32, 8, 3, 1000, 64, BF16) == 0
+    assert ws(16, 32, 8, 3, 1024, 128, BF16) == 0
+    assert ws(16, 32, 8, 3, 1025, 128, BF16) == split_bytes(16, 32, 3, 1025, 128)
+    assert ws(1, 32, 8, 1, 8192, 128, BF16) == split_bytes(1, 32, 1, 8192, 128)    # 256: quad
+    # Lq >= 384 (prefill) needs none
+    assert ws(1, 32, 8, 384, 32768, 128, BF16) == 0
+    assert ws(1, 32, 8, 383, 32768, 128, BF16) == split_bytes(1, 32, 383, 32768, 128)
+    assert ws(1, 1, 1, 1, 0, 128, BF16) == 0
+    assert ws(1, 1, 1, 1, 10, 128, 7) == 0
+    assert ws(1, 32, 0, 1, 10, 128, BF16) == 0
+    assert ws(1, 32, 5, 1, 10, 128, BF16) == 0
 
 
 def test_variant_policy_and_validation(lib):
@@ -203,20 +211,28 @@ def test_python_binding_rejects_cpu_tensors_and_dtypes():
 
 
 def test_kernel_name_queries(lib):
-    assert lib.bi_sdpa_kernel_name(1, 32, 1, 1024, 128, BF16).decode() == "sdpa_fused16"
-    assert lib.bi_sdpa_kernel_name(1, 32, 64, 1025, 128, F16).decode() == "sdpa_split16+combine"
-    assert lib.bi_sdpa_kernel_name(1, 32, 384, 1025, 128, F16).decode() == "sdpa_prefill16"
-    assert lib.bi_sdpa_kernel_name(1, 32, 383, 1025, 128, F16).decode() == "sdpa_split16+combine"
-    assert lib.bi_sdpa_kernel_name(1, 32, 384, 1024, 128, BF16).decode() == "sdpa_prefill16"
-    assert lib.bi_sdpa_kernel_name(1, 32, 383, 1024, 128, BF16).decode() == "sdpa_fused16"
-    assert lib.bi_sdpa_kernel_name(1, 32, 1, 300, 128, F32).decode() == "sdpa_split+combine"
-    assert lib.bi_sdpa_kernel_name(1, 32, 1, 300, 64, BF16).decode() == "sdpa_fused16"    # D <= 128: padded
-    assert lib.bi_sdpa_kernel_name(1, 32, 1, 3000, 96, BF16).decode() == "sdpa_split+combine"
-    assert lib.bi_sdpa_kernel_name(1, 32, 1, 300, 160, BF16).decode() == "sdpa_split+combine"
-    assert lib.bi_sdpa_kernel_name(1, 32, 1, 300, 64, F32).decode() == "sdpa_split+combine"
-    for bad in ((0, 32, 1, 10, 128, BF16), (1, 32, 1, 0, 128, BF16), (1, 32, 1, 10, 80, BF16),
-                (1, 32, 1, 10, 288, BF16), (1, 32, 1, 10, 128, 7)):
-        assert lib.bi_sdpa_kernel_name(*bad).decode() == "none"
+    name = lambda *a: lib.bi_sdpa_kernel_name(*a).decode()
+    assert name(1, 32, 8, 1, 1024, 128, BF16) == "sdpa_quad16+combine"
+    assert name(8, 32, 8, 1, 1024, 128, BF16) == "sdpa_quad16+combine"        # 256 workgroups
+    assert name(9, 32, 8, 1, 1024, 128, BF16) == "sdpa_fused16"
+    assert name(1, 32, 8, 1, 8192, 128, BF16) == "sdpa_quad16+combine"
+    assert name(1, 32, 8, 1, 8193, 128, BF16) == "sdpa_split16+combine"
+    assert name(1, 32, 8, 64, 1025, 128, F16) == "sdpa_split16+combine"
+    assert name(1, 32, 8, 384, 1025, 128, F16) == "sdpa_prefill16"
+    assert name(1, 32, 8, 383, 1025, 128, F16) == "sdpa_split16+combine"
+    assert name(1, 32, 8, 384, 1024, 128, BF16) == "sdpa_prefill16"
+    assert name(1, 32, 8, 383, 1024, 128, BF16) == "sdpa_fused16"
+    assert name(1, 32, 8, 1, 300, 128, F32) == "sdpa_split+combine"
+    assert name(1, 32, 8, 1, 300, 64, BF16) == "sdpa_quad16+combine"           # D <= 128: padded
+    assert name(64, 32, 8, 1, 300, 64, BF16) == "sdpa_fused16"
+    assert name(1, 32, 8, 1, 3000, 96, BF16) == "sdpa_quad16+combine"
+    assert name(8, 32, 8, 1, 3000, 96, BF16) == "sdpa_split+combine"
+    assert name(1, 32, 8, 1, 300, 160, BF16) == "sdpa_split+combine"
+    assert name(1, 32, 8, 1, 300, 64, F32) == "sdpa_split+combine"
+    for bad in ((0, 32, 8, 1, 10, 128, BF16), (1, 32, 8, 1, 0, 128, BF16), (1, 32, 8, 1, 10, 80, BF16),
+                (1, 32, 8, 1, 10, 288, BF16), (1, 32, 8, 1, 10, 128, 7), (1, 32, 0, 1, 10, 128, BF16),
+                (1, 32, 5, 1, 10, 128, BF16)):
+        assert name(*bad) == "none"
     assert lib.bi_gemm_kernel_name(1, 4096, 4096, BF16, 0).decode().startswith("gemm16_strip_nk/")
     assert lib.bi_gemm_kernel_name(4096, 4096, 4096, BF16, 0).decode().startswith("gemm16_ring_nk/")
     assert lib.bi_gemm_kernel_name(0, 4096, 4096, BF16, 0).decode() == "none"

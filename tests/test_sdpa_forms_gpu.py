@@ -3,8 +3,9 @@ dims that are multiples of 32 (README, section "How the kernels work", attention
 forms of the single-pass kernel; section "Limitations": sinks, head dims).
 
 * oracle tolerance (fp32 1e-5, bf16 / fp16 2e-2) against the float64 oracle on every kernel path:
-  one launch for short caches, split + combine for long ones, the prefill kernel for long query
-  chunks, and the generic split kernel for fp32 and every head dim other than 128;
+  the quad kernel for small grids, one launch for other short caches, split + combine for long ones,
+  the prefill kernel for long query chunks, and the generic split kernel for fp32 and head dims above
+  128;
 * equivalences on raw bits: an additive mask of 0 / -inf equals the boolean mask, -inf sinks equal
   no sinks;
 * invariance on raw bits: every token of a prefill chunk equals its own decode call (K / V truncated
@@ -25,8 +26,10 @@ from helpers import assert_bits_equal, assert_close_to_oracle, round_ref
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
 DTS = [torch.float32, torch.bfloat16, torch.float16]
-# (B, Hq, Hkv, Lq, S): one launch (S <= 1024), split + combine (S > 1024), prefill (Lq >= 384)
-PATHS = [(2, 8, 2, 5, 700), (1, 8, 2, 3, 2085), (1, 4, 2, 400, 900)]
+# (B, Hq, Hkv, Lq, S) for 16-bit D = 128: quad + combine (at most 256 workgroups of one split and row
+# tile), one launch (more, S <= 1024), split + combine (more, S > 1024), prefill (Lq >= 384)
+PATHS = [(2, 8, 2, 5, 700), (4, 32, 8, 9, 900), (4, 32, 8, 3, 2085), (1, 4, 2, 400, 900)]
+PATH_IDS = ["quad", "fused", "split", "prefill"]
 
 
 def _ids(d):
@@ -51,7 +54,7 @@ def _additive(shape, seed, dt, frac_inf=0.2):
     return a.to(dt)
 
 
-@pytest.mark.parametrize("shape", PATHS, ids=["fused", "split", "prefill"])
+@pytest.mark.parametrize("shape", PATHS, ids=PATH_IDS)
 @pytest.mark.parametrize("dt", DTS, ids=_ids)
 def test_additive_mask_against_oracle_and_boolean(dt, shape):
     B, Hq, Hkv, Lq, S = shape
@@ -100,7 +103,7 @@ def test_keys_appended_with_minus_inf_change_nothing(dt):
         assert_bits_equal(o, base, f"cache {S0} -> {S}, new keys at -inf")
 
 
-@pytest.mark.parametrize("shape", PATHS, ids=["fused", "split", "prefill"])
+@pytest.mark.parametrize("shape", PATHS, ids=PATH_IDS)
 @pytest.mark.parametrize("dt", DTS, ids=_ids)
 def test_sinks_against_oracle_and_minus_inf(dt, shape):
     B, Hq, Hkv, Lq, S = shape
@@ -163,29 +166,31 @@ def test_head_dims_multiple_of_32(dt, D):
 @pytest.mark.parametrize("D", [64, 96])
 @pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16], ids=_ids)
 def test_small_head_dims_agree_across_kernels(dt, D):
-    """16-bit D < 128: the one-launch and prefill kernels run on rows zero-padded to 128, the split
-    kernel on the real rows; the zero products only add exact zeros, so every path gives the same
-    bits.  Prefill chunk (prefill kernel) vs the decode of its tokens (one launch at S <= 1024, split
-    kernel above)."""
+    """16-bit D < 128: the prefill, quad and one-launch kernels run on rows zero-padded to 128, the
+    generic split kernel on the real rows; the zero products only add exact zeros, so every path gives
+    the same bits.  Prefill chunk (prefill kernel) vs the decode of its tokens (quad kernel), and one
+    batch element alone (quad kernel) vs inside a batch of 40 (one launch at S <= 1024, the generic
+    split kernel above)."""
     B, Hq, Hkv, Lq, S = 1, 8, 2, 400, 1500
+    BI = bi.BI_BF16 if dt == torch.bfloat16 else bi.BI_F16
     q, k, v = _gpu(*_qkv(B, Hq, Hkv, Lq, S, D, dt, 370 + D))
     lib = bi._native.load()
-    assert lib.bi_sdpa_kernel_name(B, Hq, Lq, S, D, bi.BI_BF16).decode() == "sdpa_prefill16"
+    name = lambda *a: lib.bi_sdpa_kernel_name(*a, D, BI).decode()
+    assert name(B, Hq, Hkv, Lq, S) == "sdpa_prefill16"
     full = bi.bi_sdpa(q, k, v, causal=True)
     for i in (0, 150, 399):
         p = S - Lq + i
+        assert name(B, Hq, Hkv, 1, p + 1) == "sdpa_quad16+combine"
         dec = bi.bi_sdpa(q[:, :, i:i + 1], k[:, :, :p + 1], v[:, :, :p + 1], causal=True)
-        assert_bits_equal(dec[:, :, 0], full[:, :, i], f"D={D}: prefill token {i} vs its split-kernel decode")
-    short = bi.bi_sdpa(q[:, :, :3], k[:, :, :900], v[:, :, :900], causal=True)      # one launch, padded
-    for i in range(3):
-        p = 900 - 3 + i
-        dec = bi.bi_sdpa(q[:, :, i:i + 1], k[:, :, :p + 1], v[:, :, :p + 1], causal=True)
-        assert_bits_equal(dec[:, :, 0], short[:, :, i], f"D={D}: one-launch row {i} vs its decode")
-    m = torch.ones(1, 1, 1, S, dtype=torch.bool, device=DEV)
-    m[..., 900:] = False                               # 900 keys through the split kernel (S = 1500)
-    qd = q[:, :, :1]
-    assert_bits_equal(bi.bi_sdpa(qd, k, v, mask=m), bi.bi_sdpa(qd, k[:, :, :900], v[:, :, :900]),
-                      f"D={D}: split kernel with masked keys vs one launch")
+        assert_bits_equal(dec[:, :, 0], full[:, :, i], f"D={D}: prefill token {i} vs its quad-kernel decode")
+    for S2, big_kernel in ((900, "sdpa_fused16"), (1500, "sdpa_split+combine")):
+        qd, kd, vd = q[:, :, :2], k[:, :, :S2], v[:, :, :S2]
+        assert name(1, Hq, Hkv, 2, S2) == "sdpa_quad16+combine" and name(40, Hq, Hkv, 2, S2) == big_kernel
+        one = bi.bi_sdpa(qd, kd, vd, causal=True)
+        rep = lambda t: t.expand(40, -1, -1, -1).contiguous()
+        big = bi.bi_sdpa(rep(qd), rep(kd), rep(vd), causal=True)
+        assert_bits_equal(big[:1], one, f"D={D} S={S2}: {big_kernel} vs the quad kernel")
+        assert_bits_equal(big[39:], one, f"D={D} S={S2}: last batch element, {big_kernel} vs the quad kernel")
 
 
 def test_forms_together_and_bad_arguments():

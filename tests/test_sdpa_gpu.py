@@ -218,6 +218,49 @@ def test_accuracy_small_shapes(dt, D):
         assert_close_to_oracle(o.cpu(), oracle.sdpa(q, k, v, causal=causal), f"{dt} D={D} causal={causal}")
 
 
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16], ids=_ids)
+def test_quad_fused_and_split_kernels_agree(dt):
+    """16-bit D = 128: the kernel follows the size of the grid (splits x row tiles x B x KV heads), so
+    the same batch element runs the quad kernel alone and the one-launch (S <= 1024) or split kernel
+    (S > 1024) inside a batch of 48.  Every mask form, sinks, ragged S and several query lengths give
+    the same bits either way, and the quad results match the oracle."""
+    lib = bi._native.load()
+    BI = bi.BI_BF16 if dt == torch.bfloat16 else bi.BI_F16
+    Hq, Hkv, NB = 8, 2, 48
+    for S, Lq, big in ((700, 1, "sdpa_fused16"), (1024, 5, "sdpa_fused16"), (1000, 17, "sdpa_fused16"),
+                       (2085, 2, "sdpa_split16+combine"), (4100, 9, "sdpa_split16+combine")):
+        seed = 0x5EED70 + S + Lq
+        q = synthetic.randn((1, Hq, Lq, 128), seed, 1.0, dt)
+        k = synthetic.randn((1, Hkv, S, 128), seed + 1, 1.0, dt)
+        v = synthetic.randn((1, Hkv, S, 128), seed + 2, 1.0, dt)
+        g = torch.Generator().manual_seed(seed + 3)
+        bmask = torch.rand((1, Hq, Lq, S), generator=g) > 0.25
+        bmask[..., 0] = True
+        amask = (torch.randn((1, 1, Lq, S), generator=g) * 2).to(dt)
+        amask[torch.rand((1, 1, Lq, S), generator=g) < 0.2] = float("-inf")
+        amask[..., 0] = 0.0
+        sinks = synthetic.randn((Hq,), seed + 4, 2.0)
+        assert lib.bi_sdpa_kernel_name(1, Hq, Hkv, Lq, S, 128, BI).decode() == "sdpa_quad16+combine"
+        assert lib.bi_sdpa_kernel_name(NB, Hq, Hkv, Lq, S, 128, BI).decode() == big
+        rep = lambda t: t.expand(NB, *t.shape[1:]).contiguous()
+        qg, kg, vg = q.to(DEV), k.to(DEV), v.to(DEV)
+        qb, kb, vb = rep(qg), rep(kg), rep(vg)
+        forms = {"causal": dict(causal=True), "bool": dict(mask=bmask.to(DEV)),
+                 "additive+causal": dict(mask=amask.to(DEV), causal=True),
+                 "sinks+causal": dict(causal=True, sinks=sinks.to(DEV))}
+        for fname, kw in forms.items():
+            one = bi.bi_sdpa(qg, kg, vg, **kw)
+            kwb = dict(kw)
+            if "mask" in kw:
+                kwb["mask"] = kw["mask"].expand(NB, *kw["mask"].shape[1:]).contiguous()
+            many = bi.bi_sdpa(qb, kb, vb, **kwb)
+            for e in (0, 17, NB - 1):
+                assert_bits_equal(many[e:e + 1], one, f"S={S} Lq={Lq} {fname}: {big} element {e} vs quad")
+            if fname in ("causal", "sinks+causal"):
+                want = oracle.sdpa(q, k, v, causal=True, sinks=sinks if fname == "sinks+causal" else None)
+                assert_close_to_oracle(one.cpu(), want, f"S={S} Lq={Lq} {fname}: quad vs oracle")
+
+
 def test_strided_qkv_views():
     S, D = 512, 128
     qkv = synthetic.randn((1, 300, 3 * 4, D), 95, 1.0, torch.bfloat16).to(DEV)   # (B, L, 3H, D)
@@ -272,8 +315,8 @@ def test_prefill_path_matches_split_path_and_decode(dt):
         q = synthetic.randn((B, Hq, 500, 128), 0x5EED50 + S, 1.0, dt).to(DEV)
         k = synthetic.randn((B, Hkv, S, 128), 0x5EED51 + S, 1.0, dt).to(DEV)
         v = synthetic.randn((B, Hkv, S, 128), 0x5EED52 + S, 1.0, dt).to(DEV)
-        assert lib.bi_sdpa_kernel_name(B, Hq, 384, S, 128, BI).decode() == "sdpa_prefill16"
-        assert lib.bi_sdpa_kernel_name(B, Hq, 383, S, 128, BI).decode() == (
+        assert lib.bi_sdpa_kernel_name(B, Hq, Hkv, 384, S, 128, BI).decode() == "sdpa_prefill16"
+        assert lib.bi_sdpa_kernel_name(B, Hq, Hkv, 383, S, 128, BI).decode() == (
             "sdpa_fused16" if S <= 1024 else "sdpa_split16+combine")
         split = bi.bi_sdpa(q[:, :, -383:], k, v, causal=True)
         for L in (384, 390, 500):
@@ -300,7 +343,7 @@ def test_long_causal_prefill_needs_no_workspace():
     q = synthetic.randn((1, 32, S, 128), 0x5EED60, 1.0, torch.bfloat16).to(DEV)
     k = synthetic.randn((1, 8, S, 128), 0x5EED61, 1.0, torch.bfloat16).to(DEV)
     v = synthetic.randn((1, 8, S, 128), 0x5EED62, 1.0, torch.bfloat16).to(DEV)
-    assert bi.sdpa_workspace_bytes(1, 32, S, S, 128, torch.bfloat16) == 0
+    assert bi.sdpa_workspace_bytes(1, 32, 8, S, S, 128, torch.bfloat16) == 0
     o = bi.bi_sdpa(q, k, v, causal=True)
     qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
     for p in (0, 1, 255, 256, 1000, 2047, 4095):
