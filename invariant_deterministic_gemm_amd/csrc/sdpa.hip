@@ -409,16 +409,19 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const char *lds_addr) {
 
 // The 16 query rows of one row tile as one wavefront sees them: lane r16
 // carries score row r16 (column r16 of S^T); lanes hold O rows 4 g + i.
-struct Rows16 {
+// NC = 4 for rows of 128 (or zero-padded to 128), 8 for rows of 256.
+template <int NC>
+struct Rows16T {
     bool row_ok;            // score row r16 is a real row (rows past R are computed and never stored)
     int pos;                // its key position (bottom-right alignment)
     int pos_first;          // key position of the tile's first row, the smallest in the tile
     const char *mrow;       // its mask row, or null
-    u32x4 qf[4];            // its q fragments (d chunks 32 c + 8 g .. + 7)
+    u32x4 qf[NC];           // its q fragments (d chunks 32 c + 8 g .. + 7)
 };
+using Rows16 = Rows16T<4>;
 
-template <int dt>
-__device__ __forceinline__ void rows16_load(const SdpaParams &p, int tile, int b, int gk, Rows16 &r) {
+template <int dt, int NC>
+__device__ __forceinline__ void rows16_load(const SdpaParams &p, int tile, int b, int gk, Rows16T<NC> &r) {
     const int lane = threadIdx.x & 63;
     const int r16 = lane & 15, g = lane >> 4;
     const int R = p.G * p.Lq;
@@ -433,40 +436,44 @@ __device__ __forceinline__ void rows16_load(const SdpaParams &p, int tile, int b
     const char *qrow = static_cast<const char *>(p.q) +
                        ((int64_t)b * p.qs[0] + (int64_t)h * p.qs[1] + (int64_t)iq * p.qs[2]) * 2;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < NC; ++c) {
         r.qf[c] = zero_u4();
         if (32 * c < p.dr) r.qf[c] = ldg16(qrow + (32 * c + 8 * g) * 2);
     }
 }
 
-// Scores of one 64-key block for a wavefront's 16 rows (K block in LDS, 256-byte key rows, chunk c of
-// key r at slot c ^ (r mod 16)): lane holds S^T[key 16 kt + 4 g + i][row r16].  All K fragments are
-// read first; the four chains (one per kt) each accumulate d chunks c = 0 .. 3 in order.  The K reads
-// may still be in flight on return.
-template <int dt>
-__device__ __forceinline__ void attn_scores16(const Rows16 &r, const char *Ks, f32x4 (&st)[4]) {
-    constexpr int ROWB = 256;
+// Scores of one 64-key block for a wavefront's 16 rows (K block in LDS, 64 NC-byte key rows, chunk c
+// of key r at slot c ^ (r mod 16)): lane holds S^T[key 16 kt + 4 g + i][row r16].  The K fragments of
+// four d chunks are read first; the four chains (one per kt) each accumulate d chunks c = 0 .. NC - 1
+// in order.  The K reads may still be in flight on return.
+template <int dt, int NC>
+__device__ __forceinline__ void attn_scores16(const Rows16T<NC> &r, const char *Ks, f32x4 (&st)[4]) {
+    constexpr int ROWB = 64 * NC;
     const int lane = threadIdx.x & 63;
     const int r16 = lane & 15, g = lane >> 4;
-    u32x4 kf[4][4];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-            kf[kt][c] = *reinterpret_cast<const u32x4 *>(Ks + (16 * kt + r16) * ROWB + (((4 * c + g) ^ r16) << 4));
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) st[kt] = zero4();
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int h = 0; h < NC / 4; ++h) {
+        u32x4 kf[4][4];
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) st[kt] = Mfma<dt>::step(kf[kt][c], r.qf[c], st[kt]);
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                kf[kt][c] = *reinterpret_cast<const u32x4 *>(Ks + (16 * kt + r16) * ROWB +
+                                                             (((4 * (4 * h + c) + g) ^ r16) << 4));
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) st[kt] = Mfma<dt>::step(kf[kt][c], r.qf[4 * h + c], st[kt]);
+    }
 }
 
 // The rest of one block [kb, kb + 64) given its scores: visibility, the online-softmax update of
 // (m, l, O) and O += P . V from the V block in LDS (chunk c of key r at slot c ^ 2 (r mod 8); rows of
 // keys past S must read as zero by the time v_ready() returns, which is before the first V read).
-template <int dt, class VReady>
-__device__ __forceinline__ void attn_update16(const SdpaParams &p, const Rows16 &r, const f32x4 (&st)[4],
+template <int dt, class VReady, int NC>
+__device__ __forceinline__ void attn_update16(const SdpaParams &p, const Rows16T<NC> &r, const f32x4 (&st)[4],
                                               const char *Vs, int kb, float &m_run, float &l_run, f32x4 (&o)[8],
                                               VReady v_ready) {
     constexpr int ROWB = 256;
@@ -553,8 +560,8 @@ __device__ __forceinline__ void attn_update16(const SdpaParams &p, const Rows16 
 // rows, K and V blocks in LDS as attn_scores16 and attn_update16 take them.
 // k_done() runs once every K read of the block is complete, v_ready() before
 // the first V read.
-template <int dt, class KDone, class VReady>
-__device__ __forceinline__ void attn_block16(const SdpaParams &p, const Rows16 &r, const char *Ks, const char *Vs,
+template <int dt, class KDone, class VReady, int NC>
+__device__ __forceinline__ void attn_block16(const SdpaParams &p, const Rows16T<NC> &r, const char *Ks, const char *Vs,
                                              int kb, float &m_run, float &l_run, f32x4 (&o)[8], KDone k_done,
                                              VReady v_ready) {
     f32x4 st[4];
@@ -1182,6 +1189,177 @@ __global__ __launch_bounds__(64 * W) void sdpa_prefill16(SdpaParams p) {
     }
 }
 
+// Long prefill for 16-bit head dims 160 ... 256: rows zero-padded to 256 (chunks at d >= D read the zero
+// page), and each workgroup produces one half of the output columns.  Both halves compute the full
+// scores and P of their rows, then apply P to their 128 columns of V; every output column is therefore
+// the same chain as in the split kernel (scores over all d chunks in order, P rounded once, P . V over
+// each block's keys).  Otherwise as sdpa_prefill16: W row tiles of one (batch, KV head) walk the key
+// blocks in ascending order with NB LDS buffers, restart (m, l, O) at every 256-key split and fold the
+// split partials in registers with the combine's operations.  A buffer holds the K block with 512-byte
+// rows (load q covers key rows 2 q and 2 q + 1, lane L row 2 q + L / 32, slot L mod 32, chunk
+// slot ^ (row mod 16)) and the V block's half with 256-byte rows (as sdpa_prefill16 lays out V).
+template <int dt, int W, int NB>
+__global__ __launch_bounds__(64 * W) void sdpa_prefill16w(SdpaParams p) {
+    constexpr int NC = 8;                              // 32-wide d chunks of a padded row
+    constexpr int KROWB = 512, VROWB = 256;
+    constexpr int KBYTES = KV_BLOCK * KROWB;           // one K block
+    constexpr int VBYTES = KV_BLOCK * VROWB;           // one half of a V block
+    constexpr int BUF = KBYTES + VBYTES;
+    constexpr int QKB = KBYTES / 1024, QVB = VBYTES / 1024;
+    constexpr int QBLK = QKB + QVB;                    // 1 KiB loads per block
+    constexpr int QW = QBLK / W;                       // loads per wavefront per block
+    constexpr int QKW = QKB / W;                       // of which K loads (j < QKW)
+    constexpr int BPS = KV_SPLIT / KV_BLOCK;
+    constexpr float NEG_INF = -__builtin_huge_valf();
+    static_assert(QBLK % W == 0 && QKB % W == 0, "every wavefront issues the same loads");
+    static_assert(NB >= 2 && QW * (NB - 2) <= 63, "vmcnt range");
+    __shared__ __attribute__((aligned(1024))) char lds[NB * BUF];   // [buffer][K block | V half]
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r16 = lane & 15, g = lane >> 4;
+    const int R = p.G * p.Lq;
+    const int ntile = (R + 15) / 16;
+    int wt, grp;
+    attn_work((ntile + W - 1) / W, p.B * p.Hkv * 2, wt, grp);
+    const int half = grp & 1;                          // output columns 128 half .. + 127
+    const int b = (grp >> 1) / p.Hkv, gk = (grp >> 1) % p.Hkv;
+    const int tile = wt * W + wave;
+
+    const int rlast = min(wt * W * 16 + W * 16 - 1, R - 1);
+    const int nkeys = p.causal ? min(p.S - p.Lq + rlast / p.G + 1, p.S) : p.S;
+    const int nblk = (nkeys + KV_BLOCK - 1) / KV_BLOCK;
+
+    const char *kbase = static_cast<const char *>(p.k) + ((int64_t)b * p.ks[0] + (int64_t)gk * p.ks[1]) * 2;
+    const char *vbase = static_cast<const char *>(p.v) + ((int64_t)b * p.vs[0] + (int64_t)gk * p.vs[1]) * 2 +
+                        256 * half;
+    const int64_t kstr = p.ks[2] * 2, vstr = p.vs[2] * 2;
+    // per load j of this wavefront: its key row in the block, LDS byte offset, source chunk byte offset
+    int lrowj[QW], ldst[QW], lcb[QW];
+    bool lz[QW];
+#pragma unroll
+    for (int j = 0; j < QW; ++j) {
+        const int q = wave + W * j;
+        if (j < QKW) {
+            const int row = 2 * q + (lane >> 5), slot = lane & 31;
+            const int c = slot ^ (row & 15);
+            lrowj[j] = row;
+            ldst[j] = q * 1024;
+            lcb[j] = c << 4;
+            lz[j] = 8 * c >= p.dr;
+        } else {
+            const int qv = q - QKB;
+            const int row = 4 * qv + (lane >> 4), slot = lane & 15;
+            const int c = slot ^ ((row & 7) << 1);
+            lrowj[j] = row;
+            ldst[j] = KBYTES + qv * 1024;
+            lcb[j] = c << 4;
+            lz[j] = 128 * half + 8 * c >= p.dr;
+        }
+    }
+    const char *zp = reinterpret_cast<const char *>(g_zero_page);
+    auto issue = [&](int blk) {
+        const int kb = blk * KV_BLOCK;
+        char *buf = lds + (blk % NB) * BUF;
+#pragma unroll
+        for (int j = 0; j < QW; ++j) {
+            const int64_t key = min(kb + lrowj[j], p.S - 1);   // rows past S read row S - 1
+            const char *src = lz[j] ? zp : (j < QKW ? kbase + key * kstr : vbase + key * vstr) + lcb[j];
+            __builtin_amdgcn_global_load_lds(static_cast<const void *>(src), BI_LDS_PTR(buf + ldst[j]), 16, 0, 0);
+        }
+    };
+
+    Rows16T<NC> r;
+    rows16_load<dt>(p, tile, b, gk, r);
+    bool have = false;
+    float mt = 0.0f, lt = 0.0f;
+    if (p.sinks) {
+        const int rgc = min(tile * 16 + r16, R - 1);
+        mt = sink2(p, gk * p.G + rgc % p.G);
+        lt = 1.0f;
+        have = true;
+    }
+    f32x4 ot[8];
+    float m_run = NEG_INF, l_run = 0.0f;
+    f32x4 o[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        ot[t] = zero4();
+        o[t] = zero4();
+    }
+    auto fold_split = [&]() {                          // sdpa_combine's step, as in sdpa_prefill16
+        const bool skip = m_run == NEG_INF;
+        const bool first = !skip && !have;
+        const float m2 = fmaxf(mt, m_run);
+        const float a = exp2_hw(mt - m2);
+        const float bs = exp2_hw(m_run - m2);
+        if (first) {
+            mt = m_run;
+            lt = l_run;
+        } else if (!skip) {
+            lt = __builtin_fmaf(lt, a, l_run * bs);
+            mt = m2;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int src = 4 * g + i;
+            const bool skip_i = __shfl((int)skip, src) != 0;
+            const bool first_i = __shfl((int)first, src) != 0;
+            const float a_i = __shfl(a, src), b_i = __shfl(bs, src);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const float f = __builtin_fmaf(ot[t][i], a_i, o[t][i] * b_i);
+                ot[t][i] = first_i ? o[t][i] : skip_i ? ot[t][i] : f;
+            }
+        }
+        have = have || !skip;
+        m_run = NEG_INF;
+        l_run = 0.0f;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) o[t] = zero4();
+    };
+
+    for (int j = 0; j < NB - 1 && j < nblk; ++j) issue(j);
+    for (int blk = 0; blk < nblk; ++blk) {
+        const int kb = blk * KV_BLOCK;
+        char *Ks = lds + (blk % NB) * BUF;
+        char *Vs = Ks + KBYTES;
+        if (blk + NB - 2 < nblk) BI_WAIT_VMCNT(QW * (NB - 2));   // this wavefront's loads of block blk landed
+        else BI_WAIT_VMCNT(0);
+        if (kb + KV_BLOCK > p.S) {
+            // V rows past S read as zero; each wavefront clears the rows its own loads filled
+#pragma unroll
+            for (int j = QKW; j < QW; ++j) {
+                const int row = lrowj[j];
+                if (kb + row >= p.S) *reinterpret_cast<u32x4 *>(Vs + row * VROWB + (lane & 15) * 16) = zero_u4();
+            }
+            __builtin_amdgcn_s_waitcnt(0xc07f);
+        }
+        __syncthreads();                                 // block blk visible to all; block blk - 1 no longer read
+        if (blk + NB - 1 < nblk) issue(blk + NB - 1);
+        attn_block16<dt>(p, r, Ks, Vs, kb, m_run, l_run, o, []() {}, []() {});
+        if ((blk + 1) % BPS == 0 || blk + 1 == nblk) fold_split();
+    }
+
+    const float lrow_l = lt;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int ro = tile * 16 + 4 * g + i;
+        const bool have_i = __shfl((int)have, 4 * g + i) != 0;
+        const float l_i = __shfl(lrow_l, 4 * g + i);
+        if (ro >= R) continue;
+        const int iq = ro / p.G, h = gk * p.G + ro % p.G;
+        char *orow = static_cast<char *>(p.o) +
+                     ((int64_t)b * p.os[0] + (int64_t)h * p.os[1] + (int64_t)iq * p.os[2]) * Elem<dt>::bytes;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            float v = have_i ? ot[t][i] / l_i : 0.0f;
+            v = v + 0.0f;                                // -0 -> +0
+            const int col = 128 * half + 16 * t + r16;
+            if (col < p.dr) store_from_f32<dt>(orow, col, v);
+        }
+    }
+}
+
 // Fold the split partials of one query row left to right, normalise, round.
 // One thread per output column; the partials of CH splits are loaded together
 // (independent loads in flight at once), then folded one split at a time in
@@ -1252,8 +1430,9 @@ constexpr int64_t PREFILL_MIN_LQ = 384;
 constexpr int64_t QUAD_MAX_WG = 256;
 
 SdpaPath sdpa_path(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t S, int64_t D, int dt) {
-    if (dt == DT_F32 || D > 128 || S <= 0) return SDPA_SPLIT;
+    if (dt == DT_F32 || S <= 0) return SDPA_SPLIT;
     if (Lq >= PREFILL_MIN_LQ) return SDPA_PREFILL16;
+    if (D > 128) return SDPA_SPLIT;
     const int64_t nsplit = (S + KV_SPLIT - 1) / KV_SPLIT;
     const int64_t tiles = (Hq / Hkv * Lq + 15) / 16;
     if (B * Hkv <= QUAD_MAX_WG && tiles <= QUAD_MAX_WG && nsplit <= QUAD_MAX_WG &&
@@ -1299,6 +1478,15 @@ static hipError_t launch_typed(const SdpaParams &p, hipStream_t st) {
             return hipGetLastError();
         }
     }
+    if constexpr (dt != DT_F32 && D > 128) {
+        if (path == SDPA_PREFILL16) {
+            constexpr int W = 4;                         // row tiles per workgroup sharing each K / V block
+            const int64_t nwg = (int64_t)(((R + 15) / 16 + W - 1) / W) * p.B * p.Hkv * 2;
+            if (nwg > INT32_MAX) return hipErrorInvalidConfiguration;
+            hipLaunchKernelGGL((sdpa_prefill16w<dt, W, 2>), dim3((unsigned)nwg), dim3(64 * W), 0, st, p);
+            return hipGetLastError();
+        }
+    }
     if (p.nsplit > 0 && path == SDPA_QUAD16) {
         if constexpr (dt != DT_F32 && D <= 128) {
             const int64_t nwg = (int64_t)p.nsplit * ((R + 15) / 16) * p.B * p.Hkv;
@@ -1329,7 +1517,7 @@ static hipError_t launch_typed(const SdpaParams &p, hipStream_t st) {
 const char *sdpa_kernel_name(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t S, int64_t D, int dt) {
     switch (sdpa_path(B, Hq, Hkv, Lq, S, D, dt)) {
         case SDPA_FUSED16: return "sdpa_fused16";
-        case SDPA_PREFILL16: return "sdpa_prefill16";
+        case SDPA_PREFILL16: return D > 128 ? "sdpa_prefill16w" : "sdpa_prefill16";
         case SDPA_QUAD16: return "sdpa_quad16+combine";
         default: return dt != DT_F32 && D == 128 ? "sdpa_split16+combine" : "sdpa_split+combine";
     }

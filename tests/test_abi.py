@@ -180,8 +180,10 @@ def test_sdpa_workspace_formula(lib):
     assert ws(16, 32, 8, 3, 1024, 128, BF16) == 0
     assert ws(16, 32, 8, 3, 1025, 128, BF16) == split_bytes(16, 32, 3, 1025, 128)
     assert ws(1, 32, 8, 1, 8192, 128, BF16) == split_bytes(1, 32, 1, 8192, 128)    # 256: quad
-    # Lq >= 384 (prefill) needs none
+    # Lq >= 384 (prefill) needs none, at every 16-bit head dim
     assert ws(1, 32, 8, 384, 32768, 128, BF16) == 0
+    assert ws(1, 32, 8, 384, 4096, 256, BF16) == 0
+    assert ws(1, 32, 8, 384, 4096, 256, F32) == split_bytes(1, 32, 384, 4096, 256)
     assert ws(1, 32, 8, 383, 32768, 128, BF16) == split_bytes(1, 32, 383, 32768, 128)
     assert ws(1, 1, 1, 1, 0, 128, BF16) == 0
     assert ws(1, 1, 1, 1, 10, 128, 7) == 0
@@ -228,6 +230,10 @@ def test_kernel_name_queries(lib):
     assert name(1, 32, 8, 1, 3000, 96, BF16) == "sdpa_quad16+combine"
     assert name(8, 32, 8, 1, 3000, 96, BF16) == "sdpa_split+combine"
     assert name(1, 32, 8, 1, 300, 160, BF16) == "sdpa_split+combine"
+    assert name(1, 32, 8, 384, 2048, 160, BF16) == "sdpa_prefill16w"          # D > 128: two column halves
+    assert name(1, 32, 8, 384, 2048, 256, F16) == "sdpa_prefill16w"
+    assert name(1, 32, 8, 383, 2048, 256, F16) == "sdpa_split+combine"
+    assert name(1, 32, 8, 384, 2048, 256, F32) == "sdpa_split+combine"
     assert name(1, 32, 8, 1, 300, 64, F32) == "sdpa_split+combine"
     for bad in ((0, 32, 8, 1, 10, 128, BF16), (1, 32, 8, 1, 0, 128, BF16), (1, 32, 8, 1, 10, 80, BF16),
                 (1, 32, 8, 1, 10, 288, BF16), (1, 32, 8, 1, 10, 128, 7), (1, 32, 0, 1, 10, 128, BF16),

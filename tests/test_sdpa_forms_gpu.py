@@ -193,6 +193,44 @@ def test_small_head_dims_agree_across_kernels(dt, D):
         assert_bits_equal(big[39:], one, f"D={D} S={S2}: last batch element, {big_kernel} vs the quad kernel")
 
 
+@pytest.mark.parametrize("D", [160, 192, 256])
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16], ids=_ids)
+def test_wide_head_dims_prefill(dt, D):
+    """16-bit D > 128 with query chunks of >= 384 rows: the wide prefill kernel (rows zero-padded to
+    256, two workgroups per row tile, one per half of the output columns).  Oracle tolerance on sampled
+    rows; every sampled token equals its own decode (generic split kernel) on raw bits, also under an
+    additive mask with sinks; eager and graph-captured launches agree."""
+    B, Hq, Hkv, Lq, S = 1, 8, 2, 400, 1300
+    BI = bi.BI_BF16 if dt == torch.bfloat16 else bi.BI_F16
+    q, k, v = _qkv(B, Hq, Hkv, Lq, S, D, dt, 390 + D)
+    qg, kg, vg = _gpu(q, k, v)
+    lib = bi._native.load()
+    assert lib.bi_sdpa_kernel_name(B, Hq, Hkv, Lq, S, D, BI).decode() == "sdpa_prefill16w"
+    assert lib.bi_sdpa_kernel_name(B, Hq, Hkv, 1, S, D, BI).decode() == "sdpa_split+combine"
+    assert bi.sdpa_workspace_bytes(B, Hq, Hkv, Lq, S, D, dt) == 0
+    full = bi.bi_sdpa(qg, kg, vg, causal=True)
+    rows = [0, 1, 200, 399]
+    want = oracle.sdpa(q[:, :, rows[-1:]], k, v, causal=True)
+    assert_close_to_oracle(full[:, :, rows[-1:]], want, f"D={D}: last row vs oracle")
+    for i in rows:
+        p = S - Lq + i
+        ref = oracle.sdpa(q[:, :, i:i + 1], k[:, :, :p + 1], v[:, :, :p + 1], causal=True)
+        assert_close_to_oracle(full[:, :, i:i + 1], ref, f"D={D}: row {i} vs oracle")
+        dec = bi.bi_sdpa(qg[:, :, i:i + 1], kg[:, :, :p + 1], vg[:, :, :p + 1], causal=True)
+        assert_bits_equal(dec[:, :, 0], full[:, :, i], f"D={D}: prefill token {i} vs its split-kernel decode")
+    amask = _additive((B, Hq, Lq, S), 391 + D, dt).to(DEV)
+    amask[..., 0] = 0.0
+    sinks = synthetic.randn((Hq,), 392 + D, 2.0).to(DEV)
+    fm = bi.bi_sdpa(qg, kg, vg, causal=True, mask=amask, sinks=sinks)
+    for i in rows:
+        p = S - Lq + i
+        dec = bi.bi_sdpa(qg[:, :, i:i + 1], kg[:, :, :p + 1], vg[:, :, :p + 1], causal=True,
+                         mask=amask[:, :, i:i + 1, :p + 1], sinks=sinks)
+        assert_bits_equal(dec[:, :, 0], fm[:, :, i], f"D={D}: masked prefill token {i} vs its decode")
+    fn = lambda: bi.bi_sdpa(qg, kg, vg, causal=True, mask=amask, sinks=sinks)
+    _graph_replays_equal_eager(fn, fm, f"D={D} wide prefill")
+
+
 def test_forms_together_and_bad_arguments():
     B, Hq, Hkv, Lq, S, D = 1, 8, 4, 6, 520, 64
     dt = torch.bfloat16
@@ -232,9 +270,9 @@ def _graph_replays_equal_eager(fn, eager, what, reps=4):
         torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("shape", [(1, 8, 2, 9, 1500), (1, 8, 2, 400, 900)], ids=["split", "prefill"])
+@pytest.mark.parametrize("shape", [(1, 8, 2, 9, 1500), (1, 8, 2, 400, 900)], ids=["quad", "prefill"])
 def test_forms_graph_replay_equals_eager(shape):
-    """The benchmark spec's eager vs graph-captured launch, for the additive mask, sinks and a padded
+    """Eager vs graph-captured launch give the same bits, for the additive mask, sinks and a padded
     head dim (workspace, when the path needs one, allocated inside the captured call)."""
     B, Hq, Hkv, Lq, S = shape
     dt = torch.bfloat16
