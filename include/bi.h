@@ -160,8 +160,8 @@ bi_status bi_addmm(const void *cin, int64_t ldcin,
  * bytes, 256-byte aligned, device memory owned by the caller; its contents on
  * entry do not matter and on return are unspecified.  Two calls that run at
  * the same time must not share a workspace.  The query returns 0 (ws may then
- * be NULL) for the shapes served without a workspace: 16-bit dt with D <= 128
- * and either Lq >= 384 (prefill: splits folded in registers) or S <= 1024 with
+ * be NULL) for the shapes served without a workspace: 16-bit dt with either
+ * Lq >= 384 (prefill: splits folded in registers) or D <= 128, S <= 1024 and
  * more than 256 (row tile, split) workgroups (one launch, splits folded in
  * LDS); see bi_sdpa_kernel_name.  Every path computes the same bits.
  */
@@ -312,9 +312,12 @@ const char *bi_gemm_kernel_name(int64_t M, int64_t N, int64_t K, bi_dtype in_dt,
  * tiles x B x Hkv workgroups, is at most 256 (one workgroup per CU: every
  * split's K / V requested at once); else "sdpa_fused16" when S <= 1024, and
  * "sdpa_split16+combine" (D = 128) or "sdpa_split+combine" (D < 128)
- * otherwise.  fp32 and D > 128 run "sdpa_split+combine".  16-bit D < 128 runs
- * the prefill, quad and one-launch kernels on rows zero-padded to 128 (the
- * padding adds exact zeros, so the bits are the split kernel's).
+ * otherwise.  For 16-bit dt and D > 128: "sdpa_prefill16w" when Lq >= 384
+ * (two workgroups per row tile group, one per half of the output columns),
+ * else "sdpa_split+combine".  fp32 runs "sdpa_split+combine".  16-bit D < 128
+ * runs the prefill, quad and one-launch kernels on rows zero-padded to 128,
+ * D = 160 ... 224 the wide prefill on rows zero-padded to 256 (the padding
+ * adds exact zeros, so the bits are the split kernel's).
  * Informational: the split / block structure, and with it every output bit,
  * is the same whichever runs.  Returns "none" for empty, oversized or
  * unsupported sizes. */
