@@ -470,13 +470,14 @@ __device__ __forceinline__ void attn_scores16(const Rows16T<NC> &r, const char *
 }
 
 // The rest of one block [kb, kb + 64) given its scores: visibility, the online-softmax update of
-// (m, l, O) and O += P . V from the V block in LDS (chunk c of key r at slot c ^ 2 (r mod 8); rows of
-// keys past S must read as zero by the time v_ready() returns, which is before the first V read).
-template <int dt, class VReady, int NC>
+// (m, l, O) and O += P . V from the V block in LDS (NT 16-column tiles, 32 NT-byte rows, chunk c of key
+// r at slot c ^ 2 (r mod 8); rows of keys past S must read as zero by the time v_ready() returns, which
+// is before the first V read).
+template <int dt, class VReady, int NC, int NT>
 __device__ __forceinline__ void attn_update16(const SdpaParams &p, const Rows16T<NC> &r, const f32x4 (&st)[4],
-                                              const char *Vs, int kb, float &m_run, float &l_run, f32x4 (&o)[8],
+                                              const char *Vs, int kb, float &m_run, float &l_run, f32x4 (&o)[NT],
                                               VReady v_ready) {
-    constexpr int ROWB = 256;
+    constexpr int ROWB = 32 * NT;
     constexpr float NEG_INF = -__builtin_huge_valf();
     const int lane = threadIdx.x & 63;
     const int r16 = lane & 15, g = lane >> 4;
@@ -528,12 +529,12 @@ __device__ __forceinline__ void attn_update16(const SdpaParams &p, const Rows16T
         for (int i = 0; i < 4; ++i) {
             const float ai = __shfl(alpha, 4 * g + i);
 #pragma unroll
-            for (int t = 0; t < 8; ++t) o[t][i] = o[t][i] * ai;
+            for (int t = 0; t < NT; ++t) o[t][i] = o[t][i] * ai;
         }
     }
     v_ready();
     // ---- O += P . V: k slot 8 g + j <-> key 32 c + 4 g + j (j < 4), 32 c + 16 + 4 g + (j - 4) (j >= 4).
-    // The V fragments of a half (c) are read before its eight MFMAs; o[t] takes c = 0 then c = 1.
+    // The V fragments of a half (c) are read before its NT MFMAs; o[t] takes c = 0 then c = 1.
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
         const u32x4 pf = u32x4{pack_p<dt>(pr[2 * c][0], pr[2 * c][1]), pack_p<dt>(pr[2 * c][2], pr[2 * c][3]),
@@ -541,9 +542,9 @@ __device__ __forceinline__ void attn_update16(const SdpaParams &p, const Rows16T
                                pack_p<dt>(pr[2 * c + 1][2], pr[2 * c + 1][3])};
         const int row0 = 32 * c + 4 * g + (r16 >> 2);
         const int row1 = row0 + 16;
-        u32x4 vf[8];
+        u32x4 vf[NT];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
+        for (int t = 0; t < NT; ++t) {
             const int ch = 2 * t + ((r16 & 3) >> 1);
             const int off = 8 * (r16 & 1);
             const u32x2 lo = lds_read_tr16(Vs + row0 * ROWB + ((ch ^ ((row0 & 7) << 1)) << 4) + off);
@@ -551,7 +552,7 @@ __device__ __forceinline__ void attn_update16(const SdpaParams &p, const Rows16T
             vf[t] = u32x4{lo[0], lo[1], hi[0], hi[1]};
         }
 #pragma unroll
-        for (int t = 0; t < 8; ++t) o[t] = Mfma<dt>::step(pf, vf[t], o[t]);
+        for (int t = 0; t < NT; ++t) o[t] = Mfma<dt>::step(pf, vf[t], o[t]);
     }
 }
 
@@ -560,9 +561,9 @@ __device__ __forceinline__ void attn_update16(const SdpaParams &p, const Rows16T
 // rows, K and V blocks in LDS as attn_scores16 and attn_update16 take them.
 // k_done() runs once every K read of the block is complete, v_ready() before
 // the first V read.
-template <int dt, class KDone, class VReady, int NC>
+template <int dt, class KDone, class VReady, int NC, int NT>
 __device__ __forceinline__ void attn_block16(const SdpaParams &p, const Rows16T<NC> &r, const char *Ks, const char *Vs,
-                                             int kb, float &m_run, float &l_run, f32x4 (&o)[8], KDone k_done,
+                                             int kb, float &m_run, float &l_run, f32x4 (&o)[NT], KDone k_done,
                                              VReady v_ready) {
     f32x4 st[4];
     attn_scores16<dt>(r, Ks, st);
@@ -572,16 +573,20 @@ __device__ __forceinline__ void attn_block16(const SdpaParams &p, const Rows16T<
 }
 
 // One wavefront's share: split `sp` of row tile `tile` of (b, gk), its K / V
-// blocks staged in `lds` (2 * KV_BLOCK * 256 bytes); leaves the split's
-// (m, l) of row r16 and its O fragment (rows 4 g + i, columns 16 t + r16).
-template <int dt>
+// blocks staged in `lds` (2 * KV_BLOCK * 64 NC bytes: rows of 32 NC elements,
+// NC = 4 for D <= 128 and 8 for D = 160 ... 256, zero-padded); leaves the
+// split's (m, l) of row r16 and its O fragment (rows 4 g + i, columns 16 t + r16).
+template <int dt, int NC = 4>
 __device__ __forceinline__ void split16_body(const SdpaParams &p, int sp, int tile, int b, int gk, char *lds,
-                                             float &m_out, float &l_out, f32x4 (&o)[8]) {
-    constexpr int D = 128;
+                                             float &m_out, float &l_out, f32x4 (&o)[2 * NC]) {
+    constexpr int D = 32 * NC;
     constexpr int ROWB = D * 2;                       // bytes per key row
     constexpr int KBYTES = KV_BLOCK * ROWB;           // one K (or V) block
     constexpr int QB = KBYTES / 1024;                 // 1 KiB load instructions per block half
-    static_assert(QB == 16, "four key rows per load instruction");
+    constexpr int RPQ = 1024 / ROWB;                  // key rows per load instruction
+    constexpr int SPR = ROWB / 16;                    // 16-byte slots per key row
+    constexpr int KP = 16 / RPQ, VP = 8 / RPQ;        // periods (in q) of the K and V chunk patterns
+    static_assert(QB == 16 * NC / 4 && QB <= 63, "load count per block half");
     constexpr float NEG_INF = -__builtin_huge_valf();
     const int lane = threadIdx.x & 63;
     const int R = p.G * p.Lq;
@@ -599,99 +604,141 @@ __device__ __forceinline__ void split16_body(const SdpaParams &p, int sp, int ti
     const char *kbase = static_cast<const char *>(p.k) + ((int64_t)b * p.ks[0] + (int64_t)gk * p.ks[1]) * 2;
     const char *vbase = static_cast<const char *>(p.v) + ((int64_t)b * p.vs[0] + (int64_t)gk * p.vs[1]) * 2;
 
-    // load side: instruction q covers key rows 4 q .. 4 q + 3 of the block; lane L row 4 q + L / 16,
-    // slot L mod 16.  The swizzled chunk depends on q only through q mod 4 (K) and q mod 2 (V), so the
-    // per-lane parts are computed once and a block's addresses are one base plus multiples of the stride.
-    const int lrow = lane >> 4, lslot = lane & 15;
+    // load side: instruction q covers key rows RPQ q .. RPQ q + RPQ - 1 of the block; lane L row
+    // RPQ q + L / SPR, slot L mod SPR.  The swizzled chunk depends on q only through q mod KP (K) and
+    // q mod VP (V), so the per-lane parts are computed once and a block's addresses are one base plus
+    // multiples of the stride.
+    const int lrow = lane / SPR, lslot = lane % SPR;
     const int64_t kstr = p.ks[2] * 2, vstr = p.vs[2] * 2;      // bytes between key rows
     const char *klane = kbase + lrow * kstr;
     const char *vlane = vbase + lrow * vstr;
-    int kch[4], vch[2];
-    bool kz[4], vz[2];                                // chunk at d >= D: read the zero page
+    int kch[KP], vch[VP];
+    bool kz[KP], vz[VP];                              // chunk at d >= D: read the zero page
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int c = lslot ^ ((4 * r + lrow) & 15);
+    for (int r = 0; r < KP; ++r) {
+        const int c = lslot ^ ((RPQ * r + lrow) & 15);
         kch[r] = c << 4;
         kz[r] = 8 * c >= p.dr;
     }
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        const int c = lslot ^ (((4 * r + lrow) & 7) << 1);
+    for (int r = 0; r < VP; ++r) {
+        const int c = lslot ^ (((RPQ * r + lrow) & 7) << 1);
         vch[r] = c << 4;
         vz[r] = 8 * c >= p.dr;
     }
     const char *zp = reinterpret_cast<const char *>(g_zero_page);
-    auto issueK = [&](int blk) {
+    // instructions q0 .. q1 - 1 of a block half
+    auto issueK = [&](int blk, int q0, int q1) {
         const int kb = kbeg + blk * KV_BLOCK;
         if (kb + KV_BLOCK <= p.S) {
-            const char *bp = klane + (int64_t)kb * kstr;
+            const char *bp = klane + (int64_t)kb * kstr + (int64_t)q0 * RPQ * kstr;
 #pragma unroll
-            for (int q = 0; q < QB; ++q) {
-                __builtin_amdgcn_global_load_lds(static_cast<const void *>(kz[q & 3] ? zp : bp + kch[q & 3]),
+            for (int q = q0; q < q1; ++q) {
+                __builtin_amdgcn_global_load_lds(static_cast<const void *>(kz[q % KP] ? zp : bp + kch[q % KP]),
                                                  BI_LDS_PTR(lds + q * 1024), 16, 0, 0);
-                bp += 4 * kstr;
+                bp += RPQ * kstr;
             }
         } else {                                       // the block crosses S: rows past it read row S - 1
 #pragma unroll
-            for (int q = 0; q < QB; ++q) {
-                const int key = min(kb + 4 * q + lrow, p.S - 1);
+            for (int q = q0; q < q1; ++q) {
+                const int key = min(kb + RPQ * q + lrow, p.S - 1);
                 __builtin_amdgcn_global_load_lds(
-                    static_cast<const void *>(kz[q & 3] ? zp : kbase + key * kstr + kch[q & 3]),
+                    static_cast<const void *>(kz[q % KP] ? zp : kbase + key * kstr + kch[q % KP]),
                     BI_LDS_PTR(lds + q * 1024), 16, 0, 0);
             }
         }
     };
-    auto issueV = [&](int blk) {
+    auto issueV = [&](int blk, int q0, int q1) {
         const int kb = kbeg + blk * KV_BLOCK;
         if (kb + KV_BLOCK <= p.S) {
-            const char *bp = vlane + (int64_t)kb * vstr;
+            const char *bp = vlane + (int64_t)kb * vstr + (int64_t)q0 * RPQ * vstr;
 #pragma unroll
-            for (int q = 0; q < QB; ++q) {
-                __builtin_amdgcn_global_load_lds(static_cast<const void *>(vz[q & 1] ? zp : bp + vch[q & 1]),
+            for (int q = q0; q < q1; ++q) {
+                __builtin_amdgcn_global_load_lds(static_cast<const void *>(vz[q % VP] ? zp : bp + vch[q % VP]),
                                                  BI_LDS_PTR(lds + KBYTES + q * 1024), 16, 0, 0);
-                bp += 4 * vstr;
+                bp += RPQ * vstr;
             }
         } else {
 #pragma unroll
-            for (int q = 0; q < QB; ++q) {
-                const int key = min(kb + 4 * q + lrow, p.S - 1);
+            for (int q = q0; q < q1; ++q) {
+                const int key = min(kb + RPQ * q + lrow, p.S - 1);
                 __builtin_amdgcn_global_load_lds(
-                    static_cast<const void *>(vz[q & 1] ? zp : vbase + key * vstr + vch[q & 1]),
+                    static_cast<const void *>(vz[q % VP] ? zp : vbase + key * vstr + vch[q % VP]),
                     BI_LDS_PTR(lds + KBYTES + q * 1024), 16, 0, 0);
             }
         }
     };
 
-    Rows16 r;
+    Rows16T<NC> r;
     rows16_load<dt>(p, tile, b, gk, r);
     float m_run = NEG_INF, l_run = 0.0f;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) o[t] = zero4();
+    for (int t = 0; t < 2 * NC; ++t) o[t] = zero4();
 
-    if (nblk > 0) {
-        issueK(0);
-        issueV(0);
-    }
-    for (int blk = 0; blk < nblk; ++blk) {
-        const int kb = kbeg + blk * KV_BLOCK;
-        char *Vs = lds + KBYTES;
-        BI_WAIT_VMCNT(QB);                            // K of this block landed (its V may be in flight)
-        attn_block16<dt>(
-            p, r, lds, Vs, kb, m_run, l_run, o,
-            [&]() {
-                if (blk + 1 < nblk) issueK(blk + 1);
-            },
-            [&]() {
-                if (blk + 1 < nblk) BI_WAIT_VMCNT(QB);     // V of this block landed (next K may be in flight)
-                else BI_WAIT_VMCNT(0);
-                if (kb + KV_BLOCK > p.S) {
-                    for (int row = max(p.S - kb, 0) + lrow; row < KV_BLOCK; row += 4)
-                        *reinterpret_cast<u32x4 *>(Vs + row * ROWB + lslot * 16) = zero_u4();
-                    __builtin_amdgcn_s_waitcnt(0xc07f);
-                }
-            });
-        __builtin_amdgcn_s_waitcnt(0xc07f);           // every V read of this block done
-        if (blk + 1 < nblk) issueV(blk + 1);
+    if constexpr (NC == 4) {
+        // at most one K block and one V block (32 loads) in flight
+        if (nblk > 0) {
+            issueK(0, 0, QB);
+            issueV(0, 0, QB);
+        }
+        for (int blk = 0; blk < nblk; ++blk) {
+            const int kb = kbeg + blk * KV_BLOCK;
+            char *Vs = lds + KBYTES;
+            BI_WAIT_VMCNT(QB);                        // K of this block landed (its V may be in flight)
+            attn_block16<dt>(
+                p, r, lds, Vs, kb, m_run, l_run, o,
+                [&]() {
+                    if (blk + 1 < nblk) issueK(blk + 1, 0, QB);
+                },
+                [&]() {
+                    if (blk + 1 < nblk) BI_WAIT_VMCNT(QB);     // V of this block landed (next K may be in flight)
+                    else BI_WAIT_VMCNT(0);
+                    if (kb + KV_BLOCK > p.S) {
+                        for (int row = max(p.S - kb, 0) + lrow; row < KV_BLOCK; row += RPQ)
+                            *reinterpret_cast<u32x4 *>(Vs + row * ROWB + lslot * 16) = zero_u4();
+                        __builtin_amdgcn_s_waitcnt(0xc07f);
+                    }
+                });
+            __builtin_amdgcn_s_waitcnt(0xc07f);       // every V read of this block done
+            if (blk + 1 < nblk) issueV(blk + 1, 0, QB);
+        }
+    } else {
+        // 32 loads per block half: each half goes out in two pieces of H = 16 so that at most 48 loads
+        // are in flight (the vector-memory counter holds 63).  Sequence per block: K landed -> second
+        // piece of V; scores -> first piece of the next K; V landed -> its second piece; P . V -> first
+        // piece of the next V.
+        constexpr int H = QB / 2;
+        static_assert(H == 16, "two pieces of 16 loads");
+        if (nblk > 0) {
+            issueK(0, 0, QB);
+            issueV(0, 0, H);
+        }
+        for (int blk = 0; blk < nblk; ++blk) {
+            const int kb = kbeg + blk * KV_BLOCK;
+            char *Vs = lds + KBYTES;
+            BI_WAIT_VMCNT(H);                         // K of this block landed (first piece of V in flight)
+            issueV(blk, H, QB);
+            attn_block16<dt>(
+                p, r, lds, Vs, kb, m_run, l_run, o,
+                [&]() {
+                    if (blk + 1 < nblk) issueK(blk + 1, 0, H);
+                },
+                [&]() {
+                    if (blk + 1 < nblk) {
+                        BI_WAIT_VMCNT(H);             // V of this block landed (a piece of the next K in flight)
+                        issueK(blk + 1, H, QB);
+                    } else {
+                        BI_WAIT_VMCNT(0);
+                    }
+                    if (kb + KV_BLOCK > p.S) {
+                        for (int row = max(p.S - kb, 0) + lrow; row < KV_BLOCK; row += RPQ)
+                            *reinterpret_cast<u32x4 *>(Vs + row * ROWB + lslot * 16) = zero_u4();
+                        __builtin_amdgcn_s_waitcnt(0xc07f);
+                    }
+                });
+            __builtin_amdgcn_s_waitcnt(0xc07f);       // every V read of this block done
+            if (blk + 1 < nblk) issueV(blk + 1, 0, H);
+        }
     }
 
     m_out = m_run;
@@ -701,10 +748,11 @@ __device__ __forceinline__ void split16_body(const SdpaParams &p, int sp, int ti
 // W wavefronts per workgroup take W consecutive splits of one (batch, KV
 // head, row tile): neighbouring wavefronts stream neighbouring K / V ranges.
 // Each wavefront writes its own split's partial; the work split never changes
-// the arithmetic.
-template <int dt, int W>
+// the arithmetic.  NC = 8 serves rows of 256 (D = 256).
+template <int dt, int W, int NC = 4>
 __global__ __launch_bounds__(64 * W) void sdpa_split16(SdpaParams p) {
-    __shared__ __attribute__((aligned(1024))) char lds[W * 2 * KV_BLOCK * 256];   // per wave: K block, V block
+    constexpr int PER_WAVE = 2 * KV_BLOCK * 64 * NC;
+    __shared__ __attribute__((aligned(1024))) char lds[W * PER_WAVE];   // per wave: K block, V block
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r16 = lane & 15, g = lane >> 4;
     const int R = p.G * p.Lq;
@@ -715,8 +763,8 @@ __global__ __launch_bounds__(64 * W) void sdpa_split16(SdpaParams p) {
     const int b = grp / nsg / p.Hkv, gk = grp / nsg % p.Hkv;
     if (sp >= p.nsplit) return;
     float m_run, l_run;
-    f32x4 o[8];
-    split16_body<dt>(p, sp, tile, b, gk, lds + wave * 2 * KV_BLOCK * 256, m_run, l_run, o);
+    f32x4 o[2 * NC];
+    split16_body<dt, NC>(p, sp, tile, b, gk, lds + wave * PER_WAVE, m_run, l_run, o);
     const int rg = tile * 16 + r16;
     if (g == 0 && rg < R) {
         const int64_t rowid = ((int64_t)b * p.Hq + gk * p.G + rg % p.G) * p.Lq + rg / p.G;
@@ -731,7 +779,7 @@ __global__ __launch_bounds__(64 * W) void sdpa_split16(SdpaParams p) {
             const int64_t rowid = ((int64_t)b * p.Hq + gk * p.G + ro % p.G) * p.Lq + ro / p.G;
             float *dst = p.ws_o + (rowid * p.nsplit + sp) * p.dr;
 #pragma unroll
-            for (int t = 0; t < 8; ++t)
+            for (int t = 0; t < 2 * NC; ++t)
                 if (16 * t < p.dr) dst[16 * t + r16] = o[t][i];
         }
     }
@@ -1428,11 +1476,22 @@ constexpr int64_t PREFILL_MIN_LQ = 384;
 // 21.2 -> 17.3 us; with 512 workgroups or more the one-launch and split
 // kernels are faster).
 constexpr int64_t QUAD_MAX_WG = 256;
+// 16-bit D = 256 decode takes the wide split kernel (two splits per workgroup) up to this many
+// workgroups (measured at 32 query heads, 8 KV heads: B = 1 at 8192 keys 35.6 -> 29.9 us, B = 8
+// 125.9 -> 117.5 us; at 4096 workgroups the generic kernel streams faster, and rows padded from 160
+// or 192 are faster on the generic kernel at every size tried).
+constexpr int64_t SPLIT16W_MAX_WG = 1024;
 
 SdpaPath sdpa_path(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t S, int64_t D, int dt) {
     if (dt == DT_F32 || S <= 0) return SDPA_SPLIT;
     if (Lq >= PREFILL_MIN_LQ) return SDPA_PREFILL16;
-    if (D > 128) return SDPA_SPLIT;
+    if (D > 128) {
+        const int64_t nsg = ((S + KV_SPLIT - 1) / KV_SPLIT + 1) / 2;
+        const int64_t tiles = (Hq / Hkv * Lq + 15) / 16;
+        const bool wide = D == 256 && B * Hkv <= SPLIT16W_MAX_WG && tiles <= SPLIT16W_MAX_WG &&
+                          nsg <= SPLIT16W_MAX_WG && nsg * tiles * B * Hkv <= SPLIT16W_MAX_WG;
+        return wide ? SDPA_SPLIT16W : SDPA_SPLIT;
+    }
     const int64_t nsplit = (S + KV_SPLIT - 1) / KV_SPLIT;
     const int64_t tiles = (Hq / Hkv * Lq + 15) / 16;
     if (B * Hkv <= QUAD_MAX_WG && tiles <= QUAD_MAX_WG && nsplit <= QUAD_MAX_WG &&
@@ -1445,7 +1504,7 @@ SdpaPath sdpa_path(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t S, in
 size_t sdpa_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t S, int64_t D, int dt) {
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || Lq <= 0 || S <= 0 || D <= 0) return 0;
     const SdpaPath path = sdpa_path(B, Hq, Hkv, Lq, S, D, dt);
-    if (path != SDPA_SPLIT && path != SDPA_QUAD16) return 0;
+    if (path != SDPA_SPLIT && path != SDPA_QUAD16 && path != SDPA_SPLIT16W) return 0;
     const int64_t rows = B * Hq * Lq;
     const int64_t nsplit = (S + KV_SPLIT - 1) / KV_SPLIT;
     const int64_t ml = (rows * nsplit * 2 * 4 + 255) / 256 * 256;
@@ -1501,6 +1560,13 @@ static hipError_t launch_typed(const SdpaParams &p, hipStream_t st) {
             const int64_t nwg = (int64_t)((p.nsplit + W - 1) / W) * ((R + 15) / 16) * p.B * p.Hkv;
             if (nwg > INT32_MAX) return hipErrorInvalidConfiguration;
             hipLaunchKernelGGL((sdpa_split16<dt, W>), dim3((unsigned)nwg), dim3(64 * W), 0, st, p);
+        } else if (dt != DT_F32 && D == 256 && path == SDPA_SPLIT16W) {
+            if constexpr (dt != DT_F32 && D == 256) {
+                constexpr int W = 2;
+                const int64_t nwg = (int64_t)((p.nsplit + W - 1) / W) * ((R + 15) / 16) * p.B * p.Hkv;
+                if (nwg > INT32_MAX) return hipErrorInvalidConfiguration;
+                hipLaunchKernelGGL((sdpa_split16<dt, W, 8>), dim3((unsigned)nwg), dim3(64 * W), 0, st, p);
+            }
         } else {
             const int64_t nwg = (int64_t)p.nsplit * ((R + 15) / 16) * p.B * p.Hkv;
             if (nwg > INT32_MAX) return hipErrorInvalidConfiguration;
@@ -1519,6 +1585,7 @@ const char *sdpa_kernel_name(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int
         case SDPA_FUSED16: return "sdpa_fused16";
         case SDPA_PREFILL16: return D > 128 ? "sdpa_prefill16w" : "sdpa_prefill16";
         case SDPA_QUAD16: return "sdpa_quad16+combine";
+        case SDPA_SPLIT16W: return "sdpa_split16w+combine";
         default: return dt != DT_F32 && D == 128 ? "sdpa_split16+combine" : "sdpa_split+combine";
     }
 }

@@ -180,6 +180,7 @@ def test_sdpa_workspace_formula(lib):
     assert ws(16, 32, 8, 3, 1024, 128, BF16) == 0
     assert ws(16, 32, 8, 3, 1025, 128, BF16) == split_bytes(16, 32, 3, 1025, 128)
     assert ws(1, 32, 8, 1, 8192, 128, BF16) == split_bytes(1, 32, 1, 8192, 128)    # 256: quad
+    assert ws(8, 32, 8, 1, 8192, 256, BF16) == split_bytes(8, 32, 1, 8192, 256)    # wide split
     # Lq >= 384 (prefill) needs none, at every 16-bit head dim
     assert ws(1, 32, 8, 384, 32768, 128, BF16) == 0
     assert ws(1, 32, 8, 384, 4096, 256, BF16) == 0
@@ -230,6 +231,9 @@ def test_kernel_name_queries(lib):
     assert name(1, 32, 8, 1, 3000, 96, BF16) == "sdpa_quad16+combine"
     assert name(8, 32, 8, 1, 3000, 96, BF16) == "sdpa_split+combine"
     assert name(1, 32, 8, 1, 300, 160, BF16) == "sdpa_split+combine"
+    assert name(8, 32, 8, 1, 8192, 256, BF16) == "sdpa_split16w+combine"       # 16 x 1 x 8 x 8 = 1024
+    assert name(9, 32, 8, 1, 8192, 256, BF16) == "sdpa_split+combine"
+    assert name(8, 32, 8, 1, 8192, 192, BF16) == "sdpa_split+combine"
     assert name(1, 32, 8, 384, 2048, 160, BF16) == "sdpa_prefill16w"          # D > 128: two column halves
     assert name(1, 32, 8, 384, 2048, 256, F16) == "sdpa_prefill16w"
     assert name(1, 32, 8, 383, 2048, 256, F16) == "sdpa_split+combine"

@@ -206,7 +206,8 @@ def test_wide_head_dims_prefill(dt, D):
     qg, kg, vg = _gpu(q, k, v)
     lib = bi._native.load()
     assert lib.bi_sdpa_kernel_name(B, Hq, Hkv, Lq, S, D, BI).decode() == "sdpa_prefill16w"
-    assert lib.bi_sdpa_kernel_name(B, Hq, Hkv, 1, S, D, BI).decode() == "sdpa_split+combine"
+    assert lib.bi_sdpa_kernel_name(B, Hq, Hkv, 1, S, D, BI).decode() == (
+        "sdpa_split16w+combine" if D == 256 else "sdpa_split+combine")
     assert bi.sdpa_workspace_bytes(B, Hq, Hkv, Lq, S, D, dt) == 0
     full = bi.bi_sdpa(qg, kg, vg, causal=True)
     rows = [0, 1, 200, 399]
@@ -229,6 +230,36 @@ def test_wide_head_dims_prefill(dt, D):
         assert_bits_equal(dec[:, :, 0], fm[:, :, i], f"D={D}: masked prefill token {i} vs its decode")
     fn = lambda: bi.bi_sdpa(qg, kg, vg, causal=True, mask=amask, sinks=sinks)
     _graph_replays_equal_eager(fn, fm, f"D={D} wide prefill")
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16], ids=_ids)
+def test_wide_split_matches_generic_split(dt):
+    """16-bit D = 256 decode: the wide split kernel (512-byte rows, moderate grids) and the generic split
+    kernel (larger grids) give the same bits: one batch element alone against the same element inside a
+    batch of 40, causal, with an additive mask and sinks, and with a ragged cache; the wide kernel also
+    matches the oracle."""
+    Hq, Hkv, D, NB = 8, 2, 256, 40
+    BI = bi.BI_BF16 if dt == torch.bfloat16 else bi.BI_F16
+    lib = bi._native.load()
+    for Lq, S in ((1, 7000), (3, 6500)):
+        q, k, v = _qkv(1, Hq, Hkv, Lq, S, D, dt, 400 + Lq)
+        amask = _additive((1, 1, Lq, S), 401 + Lq, dt)
+        amask[..., 0] = 0.0
+        sinks = synthetic.randn((Hq,), 402 + Lq, 2.0)
+        assert lib.bi_sdpa_kernel_name(1, Hq, Hkv, Lq, S, D, BI).decode() == "sdpa_split16w+combine"
+        assert lib.bi_sdpa_kernel_name(NB, Hq, Hkv, Lq, S, D, BI).decode() == "sdpa_split+combine"
+        qg, kg, vg, ag, sg = _gpu(q, k, v, amask, sinks)
+        rep = lambda t: t.expand(NB, *t.shape[1:]).contiguous()
+        for what, kw in (("causal", dict(causal=True)), ("additive+sinks", dict(causal=True, mask=ag, sinks=sg))):
+            one = bi.bi_sdpa(qg, kg, vg, **kw)
+            kwb = dict(kw)
+            if "mask" in kw:
+                kwb["mask"] = rep(kw["mask"])
+            many = bi.bi_sdpa(rep(qg), rep(kg), rep(vg), **kwb)
+            for e in (0, NB - 1):
+                assert_bits_equal(many[e:e + 1], one, f"Lq={Lq} S={S} {what}: generic element {e} vs wide")
+        want = oracle.sdpa(q, k, v, causal=True, mask=amask.to(torch.float64), sinks=sinks)
+        assert_close_to_oracle(bi.bi_sdpa(qg, kg, vg, causal=True, mask=ag, sinks=sg), want, f"Lq={Lq}: wide vs oracle")
 
 
 def test_forms_together_and_bad_arguments():
