@@ -69,6 +69,37 @@ def test_rows_without_visible_keys_are_zero():
     assert_bits_equal(o, torch.zeros_like(o), "empty cache")
 
 
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16], ids=_ids)
+def test_edge_rows_on_every_16bit_kernel(dt):
+    """A row that sees one key returns that key's value row, and a row that sees none returns zeros, on
+    the quad kernel (one batch element) and on the one-launch and split kernels (the same element
+    repeated 80 times), with and without sinks (a sink with no visible key still gives zeros)."""
+    lib = bi._native.load()
+    BI = bi.BI_BF16 if dt == torch.bfloat16 else bi.BI_F16
+    Hq, Hkv, D, NB = 8, 2, 128, 80
+    for S, big in ((300, "sdpa_fused16"), (2000, "sdpa_split16+combine")):
+        q = synthetic.randn((1, Hq, 3, D), 81 + S, 1.0, dt).to(DEV)
+        k = synthetic.randn((1, Hkv, S, D), 82 + S, 1.0, dt).to(DEV)
+        v = synthetic.randn((1, Hkv, S, D), 83 + S, 1.0, dt).to(DEV)
+        one_key = torch.zeros(1, 1, 3, S, dtype=torch.bool, device=DEV)
+        one_key[..., S - 7] = True
+        one_key[:, :, 2] = False                          # the third row sees nothing
+        sinks = synthetic.randn((Hq,), 84 + S, 2.0).to(DEV)
+        assert lib.bi_sdpa_kernel_name(1, Hq, Hkv, 3, S, D, BI).decode() == "sdpa_quad16+combine"
+        assert lib.bi_sdpa_kernel_name(NB, Hq, Hkv, 3, S, D, BI).decode() == big
+        rep = lambda t: t.expand(NB, *t.shape[1:]).contiguous()
+        for b_, (qq, kk, vv, mm) in (("quad", (q, k, v, one_key)), (big, (rep(q), rep(k), rep(v), rep(one_key)))):
+            o = bi.bi_sdpa(qq, kk, vv, mask=mm)
+            for h in range(Hq):
+                for i in range(2):
+                    assert_bits_equal(o[:, h, i], vv[:, h * Hkv // Hq, S - 7], f"{b_} S={S}: one visible key")
+            assert_bits_equal(o[:, :, 2], torch.zeros_like(o[:, :, 2]), f"{b_} S={S}: no visible key")
+            os_ = bi.bi_sdpa(qq, kk, vv, mask=mm, sinks=sinks)
+            assert_bits_equal(os_[:, :, 2], torch.zeros_like(os_[:, :, 2]), f"{b_} S={S}: no visible key, sinks")
+            # one key and a sink: weights e^(s - m) / (e^(s - m) + e^(sink - m)); only the key carries a value
+            assert torch.isfinite(os_.float()).all()
+
+
 @pytest.mark.parametrize("B", [1, 2])
 def test_config3_prefill_tokens_equal_their_decode(B):
     S = 1024
