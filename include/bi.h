@@ -308,9 +308,10 @@ const char *bi_gemm_kernel_name(int64_t M, int64_t N, int64_t K, bi_dtype in_dt,
 
 /* Which attention kernels a bi_sdpa call of these sizes runs.  For 16-bit dt
  * and D <= 128: "sdpa_prefill16" when Lq >= 384; else "sdpa_quad16+combine"
- * when the quad grid, ceil(S / 256) splits x ceil((Hq / Hkv) Lq / 16) row
- * tiles x B x Hkv workgroups, is at most 256 (one workgroup per CU: every
- * split's K / V requested at once); else "sdpa_fused16" when S <= 1024, and
+ * when the quad grid, ceil(S / 256) splits x ceil(ceil((Hq / Hkv) Lq / 16) / T)
+ * row-tile groups x B x Hkv workgroups with T = 1 or 2 row tiles per
+ * workgroup, is at most 256 (one workgroup per CU: every split's K / V
+ * requested at once); else "sdpa_fused16" when S <= 1024, and
  * "sdpa_split16+combine" (D = 128) or "sdpa_split+combine" (D < 128)
  * otherwise.  For 16-bit dt and D > 128: "sdpa_prefill16w" when Lq >= 384
  * (two workgroups per row tile group, one per half of the output columns);

@@ -857,66 +857,78 @@ __global__ __launch_bounds__(64 * FUSED_MAXW) void sdpa_fused16(SdpaParams p) {
     }
 }
 
-// Few query rows: one workgroup per (row tile, split, batch, KV head) with
-// one wavefront per 64-key block of the split, so the whole split (K and V,
-// 128 KiB) is requested at once instead of one block at a time.  The
-// online-softmax recurrence of split16_body is then evaluated in stages that
-// keep every operation and operand of it:
-//   1. wavefront j computes block j's scores and their row maximum;
-//   2. each wavefront rebuilds the running maximum before its block from the
-//      earlier blocks' maxima (the same select / fmaxf sequence), then its
-//      alpha, P (rounded as in split16_body) and row sum;
+// Few query rows: one workgroup per (T row tiles, split, batch, KV head) with
+// one wavefront per (64-key block of the split, row tile), so the whole split
+// (K and V, 128 KiB) is requested at once instead of one block at a time, and
+// with T = 2 two row tiles share it.  The online-softmax recurrence of
+// split16_body is then evaluated in stages that keep every operation and
+// operand of it, per row tile:
+//   1. wavefront (j, t) computes block j's scores for tile t and their row
+//      maximum;
+//   2. each rebuilds the running maximum before its block from the earlier
+//      blocks' maxima (the same select / fmaxf sequence), then its alpha, P
+//      (rounded as in split16_body) and row sum;
 //   3. l = fmaf(l, alpha, sum) runs over the blocks in order, and
 //      O = O * alpha, O += P . V over the blocks in order, each wavefront for
 //      two of the eight 16-wide column tiles (columns are independent chains).
-// The split's (m, l, O) goes to the workspace like sdpa_split16's, and the
-// combine kernel folds the splits, so the bits are those of the split path.
-template <int dt>
-__global__ __launch_bounds__(64 * 4) void sdpa_quad16(SdpaParams p) {
+// A tile only visits the blocks split16_body visits for it (its own causal
+// limit), so its bits never depend on the other tile.  The split's (m, l, O)
+// goes to the workspace like sdpa_split16's, and the combine kernel folds the
+// splits, so the bits are those of the split path.
+template <int dt, int T>
+__global__ __launch_bounds__(64 * 4 * T) void sdpa_quad16(SdpaParams p) {
     constexpr int ROWB = 256;
     constexpr int KBYTES = KV_BLOCK * ROWB;           // one K (or V) block
     constexpr int QB = KBYTES / 1024;                 // 1 KiB load instructions per block half
-    constexpr int BPS = KV_SPLIT / KV_BLOCK;          // blocks per split = wavefronts
+    constexpr int BPS = KV_SPLIT / KV_BLOCK;          // blocks per split
+    constexpr int QT = QB / T;                        // load instructions per wavefront per block half
     constexpr float NEG_INF = -__builtin_huge_valf();
-    static_assert(BPS == 4 && QB == 16, "four wavefronts, four key rows per load instruction");
+    static_assert(BPS == 4 && QB == 16 && QB % T == 0, "four blocks, four key rows per load instruction");
     __shared__ __attribute__((aligned(1024))) char lds[BPS * 2 * KBYTES];   // [block][K block | V block]
-    __shared__ u32x4 pbuf[BPS][2][64];                 // P fragments: block, half c, lane
-    __shared__ float xm[BPS][16], xa[BPS][16], xr[BPS][16];   // per block and row: maximum, alpha, sum
+    __shared__ u32x4 pbuf[T][BPS][2][64];              // P fragments: tile, block, half c, lane
+    __shared__ float xm[T][BPS][16], xa[T][BPS][16], xr[T][BPS][16];   // per block and row: max, alpha, sum
 
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int w = wave % BPS, wt = wave / BPS;        // block of the split, tile of the workgroup
     const int r16 = lane & 15, g = lane >> 4;
     const int R = p.G * p.Lq;
-    int tile, grp;
-    attn_work((R + 15) / 16, p.nsplit * p.B * p.Hkv, tile, grp);
+    const int ntile = (R + 15) / 16;
+    int tg, grp;
+    attn_work((ntile + T - 1) / T, p.nsplit * p.B * p.Hkv, tg, grp);
     const int sp = grp % p.nsplit;
     const int b = grp / p.nsplit / p.Hkv, gk = grp / p.nsplit % p.Hkv;
+    const int tile = tg * T + wt;                     // tiles past the last compute clamped rows, store nothing
 
     const int kbeg = sp * KV_SPLIT;
     const int kend = min(kbeg + KV_SPLIT, p.S);
-    int nblk = (kend - kbeg + KV_BLOCK - 1) / KV_BLOCK;
-    if (p.causal) {
-        const int rlast = min(tile * 16 + 15, R - 1);
+    const int nfull = (kend - kbeg + KV_BLOCK - 1) / KV_BLOCK;
+    // blocks split16_body visits for a tile (rows are ordered by query index, so its last row sees the most)
+    auto tile_blocks = [&](int t) {
+        if (!p.causal) return nfull;
+        const int rlast = min(t * 16 + 15, R - 1);
         const int pos_last = p.S - p.Lq + rlast / p.G;
-        nblk = pos_last < kbeg ? 0 : min(nblk, (pos_last - kbeg) / KV_BLOCK + 1);
-    }
+        return pos_last < kbeg ? 0 : min(nfull, (pos_last - kbeg) / KV_BLOCK + 1);
+    };
+    const int nblk = tile_blocks(tile);                               // this wavefront's tile
+    const int nload = tile_blocks(min(tg * T + T - 1, ntile - 1));    // the workgroup's (its last tile's)
     const int kb = kbeg + w * KV_BLOCK;               // this wavefront's block
-    const bool active = w < nblk;
     char *Ks = lds + w * 2 * KBYTES;
     char *Vs = Ks + KBYTES;
 
-    // ---- stage 1: q, then the block's K and V (direct to LDS, layout as split16_body), then scores
-    Rows16 r;
-    float mb = NEG_INF;
-    float s[4][4];
+    // ---- stage 1: q, then this wavefront's share of its block's K and V (direct to LDS, layout as
+    // split16_body: instruction q covers key rows 4 q .. 4 q + 3), then scores
     const int lrow = lane >> 4, lslot = lane & 15;
-    if (active) {
-        rows16_load<dt>(p, tile, b, gk, r);
+    const bool loads = w < nload;
+    Rows16 r;
+    rows16_load<dt>(p, tile, b, gk, r);
+    if (loads) {
         const char *kbase = static_cast<const char *>(p.k) + ((int64_t)b * p.ks[0] + (int64_t)gk * p.ks[1]) * 2;
         const char *vbase = static_cast<const char *>(p.v) + ((int64_t)b * p.vs[0] + (int64_t)gk * p.vs[1]) * 2;
         const int64_t kstr = p.ks[2] * 2, vstr = p.vs[2] * 2;
         const char *zp = reinterpret_cast<const char *>(g_zero_page);
 #pragma unroll
-        for (int q = 0; q < QB; ++q) {
+        for (int j = 0; j < QT; ++j) {
+            const int q = wt * QT + j;
             const int row = 4 * q + lrow;
             const int c = lslot ^ (row & 15);
             const int64_t key = min(kb + row, p.S - 1);          // rows past S read row S - 1
@@ -924,14 +936,23 @@ __global__ __launch_bounds__(64 * 4) void sdpa_quad16(SdpaParams p) {
                                              BI_LDS_PTR(Ks + q * 1024), 16, 0, 0);
         }
 #pragma unroll
-        for (int q = 0; q < QB; ++q) {
+        for (int j = 0; j < QT; ++j) {
+            const int q = wt * QT + j;
             const int row = 4 * q + lrow;
             const int c = lslot ^ ((row & 7) << 1);
             const int64_t key = min(kb + row, p.S - 1);
             __builtin_amdgcn_global_load_lds(static_cast<const void *>(8 * c >= p.dr ? zp : vbase + key * vstr + (c << 4)),
                                              BI_LDS_PTR(Vs + q * 1024), 16, 0, 0);
         }
-        BI_WAIT_VMCNT(QB);                            // q and the K block landed (V may be in flight)
+        BI_WAIT_VMCNT(QT);                            // q and this wavefront's part of K landed
+    } else {
+        BI_WAIT_VMCNT(0);                             // q landed
+    }
+    if constexpr (T > 1) __syncthreads();             // every part of every K block landed
+    const bool active = w < nblk;
+    float mb = NEG_INF;
+    float s[4][4];
+    if (active) {
         f32x4 st[4];
         attn_scores16<dt>(r, Ks, st);
         const bool visible = p.mask == nullptr && kb + KV_BLOCK <= p.S && (!p.causal || kb + KV_BLOCK - 1 <= r.pos_first);
@@ -948,7 +969,7 @@ __global__ __launch_bounds__(64 * 4) void sdpa_quad16(SdpaParams p) {
         for (int kt = 0; kt < 4; ++kt) mk[kt] = fmaxf(fmaxf(s[kt][0], s[kt][1]), fmaxf(s[kt][2], s[kt][3]));
         mb = fmaxf(NEG_INF, fmaxf(fmaxf(mk[0], mk[1]), fmaxf(mk[2], mk[3])));   // all-NaN -> -inf
         mb = max_xor32(max_xor16(mb));
-        if (g == 0) xm[w][r16] = mb;
+        if (g == 0) xm[wt][w][r16] = mb;
     }
     __syncthreads();
 
@@ -956,7 +977,7 @@ __global__ __launch_bounds__(64 * 4) void sdpa_quad16(SdpaParams p) {
     if (active) {
         float m_run = NEG_INF;
         for (int u = 0; u < w; ++u) {
-            const float mu = xm[u][r16];
+            const float mu = xm[wt][u][r16];
             m_run = mu == NEG_INF ? m_run : fmaxf(m_run, mu);
         }
         const bool empty = mb == NEG_INF;
@@ -974,34 +995,39 @@ __global__ __launch_bounds__(64 * 4) void sdpa_quad16(SdpaParams p) {
             }
         rs = add_xor32(add_xor16(rs));
         if (g == 0) {
-            xa[w][r16] = alpha;
-            xr[w][r16] = rs;
+            xa[wt][w][r16] = alpha;
+            xr[wt][w][r16] = rs;
         }
 #pragma unroll
         for (int c = 0; c < 2; ++c)
-            pbuf[w][c][lane] = u32x4{pack_p<dt>(pr[2 * c][0], pr[2 * c][1]), pack_p<dt>(pr[2 * c][2], pr[2 * c][3]),
-                                     pack_p<dt>(pr[2 * c + 1][0], pr[2 * c + 1][1]),
-                                     pack_p<dt>(pr[2 * c + 1][2], pr[2 * c + 1][3])};
-        BI_WAIT_VMCNT(0);                             // the V block landed
-        if (kb + KV_BLOCK > p.S) {                    // V rows past S read as zero
-            for (int row = max(p.S - kb, 0) + lrow; row < KV_BLOCK; row += 4)
-                *reinterpret_cast<u32x4 *>(Vs + row * ROWB + lslot * 16) = zero_u4();
+            pbuf[wt][w][c][lane] = u32x4{pack_p<dt>(pr[2 * c][0], pr[2 * c][1]), pack_p<dt>(pr[2 * c][2], pr[2 * c][3]),
+                                         pack_p<dt>(pr[2 * c + 1][0], pr[2 * c + 1][1]),
+                                         pack_p<dt>(pr[2 * c + 1][2], pr[2 * c + 1][3])};
+    }
+    if (loads) {
+        BI_WAIT_VMCNT(0);                             // this wavefront's part of the V block landed
+        if (kb + KV_BLOCK > p.S) {                    // V rows past S read as zero (the rows it loaded)
+#pragma unroll
+            for (int j = 0; j < QT; ++j) {
+                const int row = 4 * (wt * QT + j) + lrow;
+                if (kb + row >= p.S) *reinterpret_cast<u32x4 *>(Vs + row * ROWB + lslot * 16) = zero_u4();
+            }
         }
     }
     __syncthreads();
 
-    // ---- stage 3: l and m over the blocks in order; O for column tiles 2 w, 2 w + 1
+    // ---- stage 3: l and m over the tile's blocks in order; O for column tiles 2 w, 2 w + 1
     float l_run = 0.0f, m_run = NEG_INF;
     f32x4 o[2] = {zero4(), zero4()};
     for (int u = 0; u < nblk; ++u) {
-        const float alpha = xa[u][r16];
-        const float mu = xm[u][r16];
+        const float alpha = xa[wt][u][r16];
+        const float mu = xm[wt][u][r16];
         m_run = mu == NEG_INF ? m_run : fmaxf(m_run, mu);
-        l_run = __builtin_fmaf(l_run, alpha, xr[u][r16]);
+        l_run = __builtin_fmaf(l_run, alpha, xr[wt][u][r16]);
         if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float ai = xa[u][4 * g + i];
+                const float ai = xa[wt][u][4 * g + i];
                 o[0][i] = o[0][i] * ai;
                 o[1][i] = o[1][i] * ai;
             }
@@ -1009,7 +1035,7 @@ __global__ __launch_bounds__(64 * 4) void sdpa_quad16(SdpaParams p) {
         const char *Vu = lds + u * 2 * KBYTES + KBYTES;
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            const u32x4 pf = pbuf[u][c][lane];
+            const u32x4 pf = pbuf[wt][u][c][lane];
             const int row0 = 32 * c + 4 * g + (r16 >> 2);
             const int row1 = row0 + 16;
             u32x4 vf[2];
@@ -1469,13 +1495,25 @@ __global__ __launch_bounds__(D) void sdpa_combine(SdpaParams p) {
 // splits take the workspace-free prefill kernel (measured: below ~300 rows the
 // split kernel's extra parallelism wins, above it the shared K / V blocks do).
 constexpr int64_t PREFILL_MIN_LQ = 384;
-// Calls whose quad grid (one workgroup per row tile and split) holds at most
-// one workgroup per CU take the quad kernel, which requests a whole split at
-// once (measured at 32 query heads, 8 KV heads, D = 128: one decode row at
+// Calls whose quad grid (one workgroup per split and one or two row tiles)
+// holds at most one workgroup per CU take the quad kernel, which requests a
+// whole split at once (measured at 32 query heads, 8 KV heads, D = 128: one decode row at
 // 1024 keys 14.5 -> 12.5 us, 16 rows 19.3 -> 14.1 us, one row at 8192 keys
 // 21.2 -> 17.3 us; with 512 workgroups or more the one-launch and split
 // kernels are faster).
 constexpr int64_t QUAD_MAX_WG = 256;
+// Row tiles per quad workgroup: one when that grid fits, else two (sharing the split's K / V; measured:
+// 16 rows at 4096 keys 19.8 -> 16.7 us, 64 rows at 1024 keys 19.9 -> 17.0 us, while at grids that
+// already fit two tiles per workgroup cost 0.1-0.3 us), else 0: the quad kernel does not apply.
+static int64_t quad_tiles(int64_t B, int64_t Hkv, int64_t nsplit, int64_t ntile) {
+    auto fits = [&](int64_t groups) {
+        return B * Hkv <= QUAD_MAX_WG && groups <= QUAD_MAX_WG && nsplit <= QUAD_MAX_WG &&
+               nsplit * groups * B * Hkv <= QUAD_MAX_WG;
+    };
+    if (fits(ntile)) return 1;
+    if (ntile >= 2 && fits((ntile + 1) / 2)) return 2;
+    return 0;
+}
 // 16-bit D = 256 decode takes the wide split kernel (two splits per workgroup) up to this many
 // workgroups (measured at 32 query heads, 8 KV heads: B = 1 at 8192 keys 35.6 -> 29.9 us, B = 8
 // 125.9 -> 117.5 us; at 4096 workgroups the generic kernel streams faster, and rows padded from 160
@@ -1493,10 +1531,7 @@ SdpaPath sdpa_path(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t S, in
         return wide ? SDPA_SPLIT16W : SDPA_SPLIT;
     }
     const int64_t nsplit = (S + KV_SPLIT - 1) / KV_SPLIT;
-    const int64_t tiles = (Hq / Hkv * Lq + 15) / 16;
-    if (B * Hkv <= QUAD_MAX_WG && tiles <= QUAD_MAX_WG && nsplit <= QUAD_MAX_WG &&
-        nsplit * tiles * B * Hkv <= QUAD_MAX_WG)
-        return SDPA_QUAD16;
+    if (quad_tiles(B, Hkv, nsplit, (Hq / Hkv * Lq + 15) / 16) > 0) return SDPA_QUAD16;
     if (nsplit <= FUSED_MAXW) return SDPA_FUSED16;
     return SDPA_SPLIT;
 }
@@ -1548,9 +1583,12 @@ static hipError_t launch_typed(const SdpaParams &p, hipStream_t st) {
     }
     if (p.nsplit > 0 && path == SDPA_QUAD16) {
         if constexpr (dt != DT_F32 && D <= 128) {
-            const int64_t nwg = (int64_t)p.nsplit * ((R + 15) / 16) * p.B * p.Hkv;
+            const int64_t ntile = (R + 15) / 16;
+            const int64_t T = quad_tiles(p.B, p.Hkv, p.nsplit, ntile);
+            const int64_t nwg = (int64_t)p.nsplit * ((ntile + T - 1) / T) * p.B * p.Hkv;
             if (nwg > INT32_MAX) return hipErrorInvalidConfiguration;
-            hipLaunchKernelGGL((sdpa_quad16<dt>), dim3((unsigned)nwg), dim3(64 * 4), 0, st, p);
+            if (T == 2) hipLaunchKernelGGL((sdpa_quad16<dt, 2>), dim3((unsigned)nwg), dim3(64 * 4 * 2), 0, st, p);
+            else hipLaunchKernelGGL((sdpa_quad16<dt, 1>), dim3((unsigned)nwg), dim3(64 * 4), 0, st, p);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }

@@ -28,7 +28,7 @@ DEV = "cuda"
 DTS = [torch.float32, torch.bfloat16, torch.float16]
 # (B, Hq, Hkv, Lq, S) for 16-bit D = 128: quad + combine (at most 256 workgroups of one split and row
 # tile), one launch (more, S <= 1024), split + combine (more, S > 1024), prefill (Lq >= 384)
-PATHS = [(2, 8, 2, 5, 700), (4, 32, 8, 9, 900), (4, 32, 8, 3, 2085), (1, 4, 2, 400, 900)]
+PATHS = [(2, 8, 2, 5, 700), (4, 32, 8, 17, 900), (4, 32, 8, 3, 2085), (1, 4, 2, 400, 900)]
 PATH_IDS = ["quad", "fused", "split", "prefill"]
 
 
