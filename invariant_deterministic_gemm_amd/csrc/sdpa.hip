@@ -1438,10 +1438,9 @@ __global__ __launch_bounds__(64 * W) void sdpa_prefill16w(SdpaParams p) {
 // One thread per output column; the partials of CH splits are loaded together
 // (independent loads in flight at once), then folded one split at a time in
 // ascending order.
-template <int dt, int D>
+template <int dt, int D, int CH = 16>
 __global__ __launch_bounds__(D) void sdpa_combine(SdpaParams p) {
     constexpr float NEG_INF = -__builtin_huge_valf();
-    constexpr int CH = 16;
     const int64_t rowid = blockIdx.x;
     const int d = threadIdx.x;
     const int iq = (int)(rowid % p.Lq);
@@ -1614,7 +1613,10 @@ static hipError_t launch_typed(const SdpaParams &p, hipStream_t st) {
         if (e != hipSuccess) return e;
     }
     const dim3 g2((unsigned)((int64_t)p.B * p.Hq * p.Lq));
-    hipLaunchKernelGGL((sdpa_combine<dt, D>), g2, dim3(D), 0, st, p);
+    // the same fold with fewer loads in flight for short caches (measured 0.5-1.3 us less at four splits)
+    if (p.nsplit <= 4) hipLaunchKernelGGL((sdpa_combine<dt, D, 4>), g2, dim3(D), 0, st, p);
+    else if (p.nsplit <= 8) hipLaunchKernelGGL((sdpa_combine<dt, D, 8>), g2, dim3(D), 0, st, p);
+    else hipLaunchKernelGGL((sdpa_combine<dt, D>), g2, dim3(D), 0, st, p);
     return hipGetLastError();
 }
 
