@@ -161,8 +161,9 @@ bi_status bi_addmm(const void *cin, int64_t ldcin,
  * entry do not matter and on return are unspecified.  Two calls that run at
  * the same time must not share a workspace.  The query returns 0 (ws may then
  * be NULL) for the shapes served without a workspace: 16-bit dt with either
- * Lq >= 384 (prefill: splits folded in registers) or D <= 128, S <= 1024 and
- * more than 256 (row tile, split) workgroups (one launch, splits folded in
+ * Lq >= 384 (prefill: splits folded in registers), or D <= 128 and S <= 256
+ * on the quad kernel (one split, finished in the kernel), or D <= 128,
+ * S <= 1024 and more than 256 quad workgroups (one launch, splits folded in
  * LDS); see bi_sdpa_kernel_name.  Every path computes the same bits.
  */
 bi_status bi_sdpa(const void *q, const int64_t q_str[4],
@@ -308,6 +309,7 @@ const char *bi_gemm_kernel_name(int64_t M, int64_t N, int64_t K, bi_dtype in_dt,
 
 /* Which attention kernels a bi_sdpa call of these sizes runs.  For 16-bit dt
  * and D <= 128: "sdpa_prefill16" when Lq >= 384; else "sdpa_quad16+combine"
+ * ("sdpa_quad16" when S <= 256: one split, folded in the kernel)
  * when the quad grid, ceil(S / 256) splits x ceil(ceil((Hq / Hkv) Lq / 16) / T)
  * row-tile groups x B x Hkv workgroups with T = 1 or 2 row tiles per
  * workgroup, is at most 256 (one workgroup per CU: every split's K / V

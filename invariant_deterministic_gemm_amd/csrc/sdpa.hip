@@ -1052,6 +1052,50 @@ __global__ __launch_bounds__(64 * 4 * T) void sdpa_quad16(SdpaParams p) {
         }
     }
 
+    if (p.nsplit == 1) {
+        // one split: sdpa_combine's fold of a single partial (after the sink, if any), done here
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int ro = tile * 16 + 4 * g + i;
+            const float ms = __shfl(m_run, 4 * g + i), ls = __shfl(l_run, 4 * g + i);
+            if (ro >= R) continue;
+            const int iq = ro / p.G, h = gk * p.G + ro % p.G;
+            bool have = false;
+            float m = 0.0f, l = 0.0f;
+            if (p.sinks) {
+                m = sink2(p, h);
+                l = 1.0f;
+                have = true;
+            }
+            float a = 0.0f, bs = 0.0f;
+            bool first = false;
+            const bool skip = ms == NEG_INF;
+            if (!skip) {
+                if (!have) {
+                    first = true;
+                    l = ls;
+                } else {
+                    const float m2 = fmaxf(m, ms);
+                    a = exp2_hw(m - m2);
+                    bs = exp2_hw(ms - m2);
+                    l = __builtin_fmaf(l, a, ls * bs);
+                }
+                have = true;
+            }
+            char *orow = static_cast<char *>(p.o) +
+                         ((int64_t)b * p.os[0] + (int64_t)h * p.os[1] + (int64_t)iq * p.os[2]) * Elem<dt>::bytes;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int t = 2 * w + j;
+                const float acc = skip ? 0.0f : first ? o[j][i] : __builtin_fmaf(0.0f, a, o[j][i] * bs);
+                float v = have ? acc / l : 0.0f;
+                v = v + 0.0f;                        // -0 -> +0
+                if (16 * t < p.dr) store_from_f32<dt>(orow, 16 * t + r16, v);
+            }
+        }
+        return;
+    }
+
     // ---- the split's partial, as sdpa_split16 stores it
     const int rg = tile * 16 + r16;
     if (w == 0 && g == 0 && rg < R) {
@@ -1539,6 +1583,7 @@ size_t sdpa_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int6
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || Lq <= 0 || S <= 0 || D <= 0) return 0;
     const SdpaPath path = sdpa_path(B, Hq, Hkv, Lq, S, D, dt);
     if (path != SDPA_SPLIT && path != SDPA_QUAD16 && path != SDPA_SPLIT16W) return 0;
+    if (path == SDPA_QUAD16 && S <= KV_SPLIT) return 0;          // one split: the quad kernel finishes the rows
     const int64_t rows = B * Hq * Lq;
     const int64_t nsplit = (S + KV_SPLIT - 1) / KV_SPLIT;
     const int64_t ml = (rows * nsplit * 2 * 4 + 255) / 256 * 256;
@@ -1589,7 +1634,7 @@ static hipError_t launch_typed(const SdpaParams &p, hipStream_t st) {
             if (T == 2) hipLaunchKernelGGL((sdpa_quad16<dt, 2>), dim3((unsigned)nwg), dim3(64 * 4 * 2), 0, st, p);
             else hipLaunchKernelGGL((sdpa_quad16<dt, 1>), dim3((unsigned)nwg), dim3(64 * 4), 0, st, p);
             hipError_t e = hipGetLastError();
-            if (e != hipSuccess) return e;
+            if (e != hipSuccess || p.nsplit == 1) return e;      // one split: no combine
         }
     } else if (p.nsplit > 0) {
         if constexpr (dt != DT_F32 && D == 128) {     // (below 128 the generic kernel decodes faster)
@@ -1624,7 +1669,7 @@ const char *sdpa_kernel_name(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int
     switch (sdpa_path(B, Hq, Hkv, Lq, S, D, dt)) {
         case SDPA_FUSED16: return "sdpa_fused16";
         case SDPA_PREFILL16: return D > 128 ? "sdpa_prefill16w" : "sdpa_prefill16";
-        case SDPA_QUAD16: return "sdpa_quad16+combine";
+        case SDPA_QUAD16: return S <= KV_SPLIT ? "sdpa_quad16" : "sdpa_quad16+combine";
         case SDPA_SPLIT16W: return "sdpa_split16w+combine";
         default: return dt != DT_F32 && D == 128 ? "sdpa_split16+combine" : "sdpa_split+combine";
     }

@@ -70,6 +70,46 @@ def test_rows_without_visible_keys_are_zero():
 
 
 @pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16], ids=_ids)
+def test_single_split_finished_in_the_quad_kernel(dt):
+    """At most 256 keys (one split) the quad kernel applies the combine's fold itself (no workspace, no
+    second launch): the same bits as the one-launch kernel (the element inside a batch of 160), for every
+    mask form, sinks and ragged cache lengths, and the oracle's values."""
+    lib = bi._native.load()
+    BI = bi.BI_BF16 if dt == torch.bfloat16 else bi.BI_F16
+    Hq, Hkv, D, NB = 8, 2, 128, 160
+    for S, Lq in ((256, 1), (200, 3), (70, 17), (1, 1)):
+        q = synthetic.randn((1, Hq, Lq, D), 91 + S, 1.0, dt)
+        k = synthetic.randn((1, Hkv, S, D), 92 + S, 1.0, dt)
+        v = synthetic.randn((1, Hkv, S, D), 93 + S, 1.0, dt)
+        g = torch.Generator().manual_seed(94 + S)
+        bmask = torch.rand((1, Hq, Lq, S), generator=g) > 0.3
+        bmask[..., 0] = True
+        amask = (torch.randn((1, 1, Lq, S), generator=g) * 2).to(dt)
+        amask[..., S // 2:] = float("-inf")
+        amask[..., 0] = 0.0
+        sinks = synthetic.randn((Hq,), 95 + S, 2.0)
+        assert lib.bi_sdpa_kernel_name(1, Hq, Hkv, Lq, S, D, BI).decode() == "sdpa_quad16"
+        assert lib.bi_sdpa_kernel_name(NB, Hq, Hkv, Lq, S, D, BI).decode() == "sdpa_fused16"
+        assert bi.sdpa_workspace_bytes(1, Hq, Hkv, Lq, S, D, dt) == 0
+        rep = lambda t: t.expand(NB, *t.shape[1:]).contiguous()
+        qg, kg, vg = q.to(DEV), k.to(DEV), v.to(DEV)
+        forms = {"causal": dict(causal=True), "bool": dict(mask=bmask.to(DEV)),
+                 "additive+sinks": dict(mask=amask.to(DEV), causal=True, sinks=sinks.to(DEV)),
+                 "sinks": dict(sinks=sinks.to(DEV))}
+        for fname, kw in forms.items():
+            one = bi.bi_sdpa(qg, kg, vg, **kw)
+            kwb = dict(kw)
+            if "mask" in kw:
+                kwb["mask"] = rep(kw["mask"])
+            many = bi.bi_sdpa(rep(qg), rep(kg), rep(vg), **kwb)
+            for e in (0, NB - 1):
+                assert_bits_equal(many[e:e + 1], one, f"S={S} Lq={Lq} {fname}: one-launch element {e} vs quad")
+        want = oracle.sdpa(q, k, v, causal=True, mask=amask.to(torch.float64), sinks=sinks)
+        assert_close_to_oracle(bi.bi_sdpa(qg, kg, vg, causal=True, mask=amask.to(DEV), sinks=sinks.to(DEV)).cpu(),
+                               want, f"S={S} Lq={Lq}: quad vs oracle")
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16], ids=_ids)
 def test_edge_rows_on_every_16bit_kernel(dt):
     """A row that sees one key returns that key's value row, and a row that sees none returns zeros, on
     the quad kernel (one batch element) and on the one-launch and split kernels (the same element
