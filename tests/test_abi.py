@@ -180,6 +180,8 @@ def test_sdpa_workspace_formula(lib):
     assert ws(16, 32, 8, 3, 1024, 128, BF16) == 0
     assert ws(16, 32, 8, 3, 1025, 128, BF16) == split_bytes(16, 32, 3, 1025, 128)
     assert ws(1, 32, 8, 1, 8192, 128, BF16) == split_bytes(1, 32, 1, 8192, 128)    # 256: quad
+    assert ws(1, 32, 8, 1, 256, 128, BF16) == 0                                    # one split: finished in quad
+    assert ws(1, 32, 8, 1, 257, 128, BF16) == split_bytes(1, 32, 1, 257, 128)
     assert ws(8, 32, 8, 1, 8192, 256, BF16) == split_bytes(8, 32, 1, 8192, 256)    # wide split
     # Lq >= 384 (prefill) needs none, at every 16-bit head dim
     assert ws(1, 32, 8, 384, 32768, 128, BF16) == 0
@@ -216,6 +218,7 @@ def test_python_binding_rejects_cpu_tensors_and_dtypes():
 def test_kernel_name_queries(lib):
     name = lambda *a: lib.bi_sdpa_kernel_name(*a).decode()
     assert name(1, 32, 8, 1, 1024, 128, BF16) == "sdpa_quad16+combine"
+    assert name(1, 32, 8, 1, 256, 128, BF16) == "sdpa_quad16"
     assert name(8, 32, 8, 1, 1024, 128, BF16) == "sdpa_quad16+combine"        # 256 workgroups
     assert name(9, 32, 8, 1, 1024, 128, BF16) == "sdpa_fused16"
     assert name(1, 32, 8, 1, 8192, 128, BF16) == "sdpa_quad16+combine"
