@@ -316,7 +316,7 @@ const char *bi_gemm_kernel_name(int64_t M, int64_t N, int64_t K, bi_dtype in_dt,
  * requested at once); else "sdpa_fused16" when S <= 1024, and
  * "sdpa_split16+combine" (D = 128) or "sdpa_split+combine" (D < 128)
  * otherwise.  For 16-bit dt and D > 128: "sdpa_prefill16w" when Lq >= 384
- * (two workgroups per row tile group, one per half of the output columns);
+ * (rows of 256, all output columns in one workgroup);
  * else, for D = 256 with at most 1024 workgroups of two splits and one row
  * tile, "sdpa_split16w+combine"; else "sdpa_split+combine".  fp32 runs "sdpa_split+combine".  16-bit D < 128
  * runs the prefill, quad and one-launch kernels on rows zero-padded to 128,

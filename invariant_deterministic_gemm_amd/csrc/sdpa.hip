@@ -1308,20 +1308,24 @@ __global__ __launch_bounds__(64 * W) void sdpa_prefill16(SdpaParams p) {
 }
 
 // Long prefill for 16-bit head dims 160 ... 256: rows zero-padded to 256 (chunks at d >= D read the zero
-// page), and each workgroup produces one half of the output columns.  Both halves compute the full
-// scores and P of their rows, then apply P to their 128 columns of V; every output column is therefore
-// the same chain as in the split kernel (scores over all d chunks in order, P rounded once, P . V over
-// each block's keys).  Otherwise as sdpa_prefill16: W row tiles of one (batch, KV head) walk the key
-// blocks in ascending order with NB LDS buffers, restart (m, l, O) at every 256-key split and fold the
-// split partials in registers with the combine's operations.  A buffer holds the K block with 512-byte
-// rows (load q covers key rows 2 q and 2 q + 1, lane L row 2 q + L / 32, slot L mod 32, chunk
-// slot ^ (row mod 16)) and the V block's half with 256-byte rows (as sdpa_prefill16 lays out V).
-template <int dt, int W, int NB>
+// page).  A workgroup produces NT 16-wide output column tiles: all 16 (NT = 16, the launched form), or
+// one half (NT = 8: two workgroups per row tile group, each computing the full scores and P and
+// applying P to its 128 columns of V; measured 1.3-1.5x slower, as the scores are computed twice).
+// Every output column is the same chain as in the split kernel (scores over all d chunks in order, P
+// rounded once, P . V over each block's keys).  Otherwise as sdpa_prefill16: W row tiles of one (batch,
+// KV head) walk the key blocks in ascending order with NB LDS buffers, restart (m, l, O) at every
+// 256-key split and fold the split partials in registers with the combine's operations.  A buffer holds
+// the K block with 512-byte rows (load q covers key rows 2 q and 2 q + 1, lane L row 2 q + L / 32, slot
+// L mod 32, chunk slot ^ (row mod 16)) and the workgroup's V columns with 32 NT-byte rows (chunk c of
+// key r at slot c ^ 2 (r mod 8)).
+template <int dt, int W, int NB, int NT = 8>
 __global__ __launch_bounds__(64 * W) void sdpa_prefill16w(SdpaParams p) {
     constexpr int NC = 8;                              // 32-wide d chunks of a padded row
-    constexpr int KROWB = 512, VROWB = 256;
+    constexpr int NH = 16 / NT;                        // workgroups per row tile group (column halves)
+    constexpr int KROWB = 512, VROWB = 32 * NT;
+    constexpr int RPV = 1024 / VROWB, SPV = VROWB / 16;   // V rows per load instruction, slots per V row
     constexpr int KBYTES = KV_BLOCK * KROWB;           // one K block
-    constexpr int VBYTES = KV_BLOCK * VROWB;           // one half of a V block
+    constexpr int VBYTES = KV_BLOCK * VROWB;           // the V block's columns of this workgroup
     constexpr int BUF = KBYTES + VBYTES;
     constexpr int QKB = KBYTES / 1024, QVB = VBYTES / 1024;
     constexpr int QBLK = QKB + QVB;                    // 1 KiB loads per block
@@ -1338,9 +1342,9 @@ __global__ __launch_bounds__(64 * W) void sdpa_prefill16w(SdpaParams p) {
     const int R = p.G * p.Lq;
     const int ntile = (R + 15) / 16;
     int wt, grp;
-    attn_work((ntile + W - 1) / W, p.B * p.Hkv * 2, wt, grp);
-    const int half = grp & 1;                          // output columns 128 half .. + 127
-    const int b = (grp >> 1) / p.Hkv, gk = (grp >> 1) % p.Hkv;
+    attn_work((ntile + W - 1) / W, p.B * p.Hkv * NH, wt, grp);
+    const int half = grp % NH;                         // output columns 16 NT half .. + 16 NT - 1
+    const int b = (grp / NH) / p.Hkv, gk = (grp / NH) % p.Hkv;
     const int tile = wt * W + wave;
 
     const int rlast = min(wt * W * 16 + W * 16 - 1, R - 1);
@@ -1349,7 +1353,7 @@ __global__ __launch_bounds__(64 * W) void sdpa_prefill16w(SdpaParams p) {
 
     const char *kbase = static_cast<const char *>(p.k) + ((int64_t)b * p.ks[0] + (int64_t)gk * p.ks[1]) * 2;
     const char *vbase = static_cast<const char *>(p.v) + ((int64_t)b * p.vs[0] + (int64_t)gk * p.vs[1]) * 2 +
-                        256 * half;
+                        VROWB * half;
     const int64_t kstr = p.ks[2] * 2, vstr = p.vs[2] * 2;
     // per load j of this wavefront: its key row in the block, LDS byte offset, source chunk byte offset
     int lrowj[QW], ldst[QW], lcb[QW];
@@ -1366,12 +1370,12 @@ __global__ __launch_bounds__(64 * W) void sdpa_prefill16w(SdpaParams p) {
             lz[j] = 8 * c >= p.dr;
         } else {
             const int qv = q - QKB;
-            const int row = 4 * qv + (lane >> 4), slot = lane & 15;
+            const int row = RPV * qv + lane / SPV, slot = lane % SPV;
             const int c = slot ^ ((row & 7) << 1);
             lrowj[j] = row;
             ldst[j] = KBYTES + qv * 1024;
             lcb[j] = c << 4;
-            lz[j] = 128 * half + 8 * c >= p.dr;
+            lz[j] = 16 * NT * half + 8 * c >= p.dr;
         }
     }
     const char *zp = reinterpret_cast<const char *>(g_zero_page);
@@ -1396,11 +1400,11 @@ __global__ __launch_bounds__(64 * W) void sdpa_prefill16w(SdpaParams p) {
         lt = 1.0f;
         have = true;
     }
-    f32x4 ot[8];
+    f32x4 ot[NT];
     float m_run = NEG_INF, l_run = 0.0f;
-    f32x4 o[8];
+    f32x4 o[NT];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
+    for (int t = 0; t < NT; ++t) {
         ot[t] = zero4();
         o[t] = zero4();
     }
@@ -1424,7 +1428,7 @@ __global__ __launch_bounds__(64 * W) void sdpa_prefill16w(SdpaParams p) {
             const bool first_i = __shfl((int)first, src) != 0;
             const float a_i = __shfl(a, src), b_i = __shfl(bs, src);
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
+            for (int t = 0; t < NT; ++t) {
                 const float f = __builtin_fmaf(ot[t][i], a_i, o[t][i] * b_i);
                 ot[t][i] = first_i ? o[t][i] : skip_i ? ot[t][i] : f;
             }
@@ -1433,7 +1437,7 @@ __global__ __launch_bounds__(64 * W) void sdpa_prefill16w(SdpaParams p) {
         m_run = NEG_INF;
         l_run = 0.0f;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) o[t] = zero4();
+        for (int t = 0; t < NT; ++t) o[t] = zero4();
     };
 
     for (int j = 0; j < NB - 1 && j < nblk; ++j) issue(j);
@@ -1448,7 +1452,7 @@ __global__ __launch_bounds__(64 * W) void sdpa_prefill16w(SdpaParams p) {
 #pragma unroll
             for (int j = QKW; j < QW; ++j) {
                 const int row = lrowj[j];
-                if (kb + row >= p.S) *reinterpret_cast<u32x4 *>(Vs + row * VROWB + (lane & 15) * 16) = zero_u4();
+                if (kb + row >= p.S) *reinterpret_cast<u32x4 *>(Vs + row * VROWB + (lane % SPV) * 16) = zero_u4();
             }
             __builtin_amdgcn_s_waitcnt(0xc07f);
         }
@@ -1469,10 +1473,10 @@ __global__ __launch_bounds__(64 * W) void sdpa_prefill16w(SdpaParams p) {
         char *orow = static_cast<char *>(p.o) +
                      ((int64_t)b * p.os[0] + (int64_t)h * p.os[1] + (int64_t)iq * p.os[2]) * Elem<dt>::bytes;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
+        for (int t = 0; t < NT; ++t) {
             float v = have_i ? ot[t][i] / l_i : 0.0f;
             v = v + 0.0f;                                // -0 -> +0
-            const int col = 128 * half + 16 * t + r16;
+            const int col = 16 * NT * half + 16 * t + r16;
             if (col < p.dr) store_from_f32<dt>(orow, col, v);
         }
     }
@@ -1619,9 +1623,9 @@ static hipError_t launch_typed(const SdpaParams &p, hipStream_t st) {
     if constexpr (dt != DT_F32 && D > 128) {
         if (path == SDPA_PREFILL16) {
             constexpr int W = 4;                         // row tiles per workgroup sharing each K / V block
-            const int64_t nwg = (int64_t)(((R + 15) / 16 + W - 1) / W) * p.B * p.Hkv * 2;
+            const int64_t nwg = (int64_t)(((R + 15) / 16 + W - 1) / W) * p.B * p.Hkv;
             if (nwg > INT32_MAX) return hipErrorInvalidConfiguration;
-            hipLaunchKernelGGL((sdpa_prefill16w<dt, W, 2>), dim3((unsigned)nwg), dim3(64 * W), 0, st, p);
+            hipLaunchKernelGGL((sdpa_prefill16w<dt, W, 2, 16>), dim3((unsigned)nwg), dim3(64 * W), 0, st, p);
             return hipGetLastError();
         }
     }

@@ -197,7 +197,7 @@ def test_small_head_dims_agree_across_kernels(dt, D):
 @pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16], ids=_ids)
 def test_wide_head_dims_prefill(dt, D):
     """16-bit D > 128 with query chunks of >= 384 rows: the wide prefill kernel (rows zero-padded to
-    256, two workgroups per row tile, one per half of the output columns).  Oracle tolerance on sampled
+    256, all output columns of a row tile in one workgroup).  Oracle tolerance on sampled
     rows; every sampled token equals its own decode (generic split kernel) on raw bits, also under an
     additive mask with sinks; eager and graph-captured launches agree."""
     B, Hq, Hkv, Lq, S = 1, 8, 2, 400, 1300
