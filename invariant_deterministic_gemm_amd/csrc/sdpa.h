@@ -33,7 +33,7 @@ struct SdpaParams {
 // wide split and quad paths use a workspace.
 enum SdpaPath {
     SDPA_FUSED16,     // 16-bit, D <= 128, at most four splits: one launch, fold in LDS
-    SDPA_PREFILL16,   // 16-bit, long caches with many query rows: fold in registers (D > 128: two column halves)
+    SDPA_PREFILL16,   // 16-bit, long caches with many query rows: fold in registers (D > 128: rows of 256)
     SDPA_QUAD16,      // 16-bit, D <= 128, small grids: one wavefront per block, combine kernel
     SDPA_SPLIT16W,    // 16-bit, D = 256, moderate grids: 512-byte rows, combine kernel
     SDPA_SPLIT        // split kernel + combine kernel through the workspace

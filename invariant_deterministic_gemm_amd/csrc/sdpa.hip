@@ -1335,7 +1335,7 @@ __global__ __launch_bounds__(64 * W) void sdpa_prefill16w(SdpaParams p) {
     constexpr float NEG_INF = -__builtin_huge_valf();
     static_assert(QBLK % W == 0 && QKB % W == 0, "every wavefront issues the same loads");
     static_assert(NB >= 2 && QW * (NB - 2) <= 63, "vmcnt range");
-    __shared__ __attribute__((aligned(1024))) char lds[NB * BUF];   // [buffer][K block | V half]
+    __shared__ __attribute__((aligned(1024))) char lds[NB * BUF];   // [buffer][K block | V columns]
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r16 = lane & 15, g = lane >> 4;
