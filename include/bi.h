@@ -161,7 +161,8 @@ bi_status bi_addmm(const void *cin, int64_t ldcin,
  * entry do not matter and on return are unspecified.  Two calls that run at
  * the same time must not share a workspace.  The query returns 0 (ws may then
  * be NULL) for the shapes served without a workspace: 16-bit dt with either
- * Lq >= 384 (prefill: splits folded in registers), or D <= 128 and S <= 256
+ * Lq >= 384 (prefill: splits folded in registers; for D > 128 also Lq >= 64
+ * with B Lq >= 192), or D <= 128 and S <= 256
  * on the quad kernel (one split, finished in the kernel), or D <= 128,
  * S <= 1024 and more than 256 quad workgroups (one launch, splits folded in
  * LDS); see bi_sdpa_kernel_name.  Every path computes the same bits.
@@ -315,8 +316,8 @@ const char *bi_gemm_kernel_name(int64_t M, int64_t N, int64_t K, bi_dtype in_dt,
  * workgroup, is at most 256 (one workgroup per CU: every split's K / V
  * requested at once); else "sdpa_fused16" when S <= 1024, and
  * "sdpa_split16+combine" (D = 128) or "sdpa_split+combine" (D < 128)
- * otherwise.  For 16-bit dt and D > 128: "sdpa_prefill16w" when Lq >= 384
- * (rows of 256, all output columns in one workgroup);
+ * otherwise.  For 16-bit dt and D > 128: "sdpa_prefill16w" when Lq >= 384, or
+ * Lq >= 64 with B Lq >= 192 (rows of 256, all output columns in one workgroup);
  * else, for D = 256 with at most 1024 workgroups of two splits and one row
  * tile, "sdpa_split16w+combine"; else "sdpa_split+combine".  fp32 runs "sdpa_split+combine".  16-bit D < 128
  * runs the prefill, quad and one-launch kernels on rows zero-padded to 128,

@@ -1542,6 +1542,11 @@ __global__ __launch_bounds__(D) void sdpa_combine(SdpaParams p) {
 // splits take the workspace-free prefill kernel (measured: below ~300 rows the
 // split kernel's extra parallelism wins, above it the shared K / V blocks do).
 constexpr int64_t PREFILL_MIN_LQ = 384;
+// 16-bit head dims above 128 take the wide prefill kernel from 64 query rows on once the batch holds at
+// least 192 of them (measured at D = 256 and 192 against the generic split kernel: B = 1, 2048 keys,
+// 192 rows 132 -> 103 us; B = 4, 64 rows 173 -> 105 us; B = 1, 128 rows and B = 4, 32 rows stay
+// faster on the split kernel).
+constexpr int64_t WIDE_PREFILL_MIN_LQ = 64, WIDE_PREFILL_MIN_ROWS = 192;
 // Calls whose quad grid (one workgroup per split and one or two row tiles)
 // holds at most one workgroup per CU take the quad kernel, which requests a
 // whole split at once (measured at 32 query heads, 8 KV heads, D = 128: one decode row at
@@ -1570,6 +1575,7 @@ constexpr int64_t SPLIT16W_MAX_WG = 1024;
 SdpaPath sdpa_path(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t S, int64_t D, int dt) {
     if (dt == DT_F32 || S <= 0) return SDPA_SPLIT;
     if (Lq >= PREFILL_MIN_LQ) return SDPA_PREFILL16;
+    if (D > 128 && Lq >= WIDE_PREFILL_MIN_LQ && B * Lq >= WIDE_PREFILL_MIN_ROWS) return SDPA_PREFILL16;
     if (D > 128) {
         const int64_t nsg = ((S + KV_SPLIT - 1) / KV_SPLIT + 1) / 2;
         const int64_t tiles = (Hq / Hkv * Lq + 15) / 16;

@@ -239,7 +239,10 @@ def test_kernel_name_queries(lib):
     assert name(8, 32, 8, 1, 8192, 192, BF16) == "sdpa_split+combine"
     assert name(1, 32, 8, 384, 2048, 160, BF16) == "sdpa_prefill16w"          # D > 128: two column halves
     assert name(1, 32, 8, 384, 2048, 256, F16) == "sdpa_prefill16w"
-    assert name(1, 32, 8, 383, 2048, 256, F16) == "sdpa_split+combine"
+    assert name(1, 32, 8, 383, 2048, 256, F16) == "sdpa_prefill16w"            # >= 64 rows, >= 192 in the batch
+    assert name(4, 32, 8, 64, 2048, 256, F16) == "sdpa_prefill16w"
+    assert name(1, 32, 8, 128, 2048, 256, F16) == "sdpa_split16w+combine"
+    assert name(4, 32, 8, 32, 2048, 192, BF16) == "sdpa_split+combine"
     assert name(1, 32, 8, 384, 2048, 256, F32) == "sdpa_split+combine"
     assert name(1, 32, 8, 1, 300, 64, F32) == "sdpa_split+combine"
     for bad in ((0, 32, 8, 1, 10, 128, BF16), (1, 32, 8, 1, 0, 128, BF16), (1, 32, 8, 1, 10, 80, BF16),
