@@ -301,7 +301,8 @@ def _graph_replays_equal_eager(fn, eager, what, reps=4):
         torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("shape", [(1, 8, 2, 9, 1500), (1, 8, 2, 400, 900)], ids=["quad", "prefill"])
+@pytest.mark.parametrize("shape", [(1, 8, 2, 9, 1500), (1, 32, 8, 64, 1024), (1, 8, 2, 5, 200), (1, 8, 2, 400, 900)],
+                         ids=["quad", "quad-two-tiles", "quad-one-split", "prefill"])
 def test_forms_graph_replay_equals_eager(shape):
     """Eager vs graph-captured launch give the same bits, for the additive mask, sinks and a padded
     head dim (workspace, when the path needs one, allocated inside the captured call)."""
