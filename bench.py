@@ -33,6 +33,7 @@ from __future__ import annotations
 
 import argparse
 import csv
+import ctypes
 import glob
 import hashlib
 import json
@@ -78,6 +79,13 @@ def parse():
     ap.add_argument("--no-cells", action="store_true", help="skip the per-cell roofline table")
     ap.add_argument("--cpu-threads", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--samples", type=int, default=200, help="timed graph replays per graded cell")
+    ap.add_argument("--cell", action="append", default=[], choices=sorted(CELLS),
+                    help="measure only these cells (no step, no CPU baseline); repeatable")
+    ap.add_argument("--eager", action="store_true", help="with --cell: direct calls instead of graph replays")
+    ap.add_argument("--summarize-counters", metavar="DIR", default=None,
+                    help="per-dispatch averages of the counters under DIR for kernels matching --kernel")
+    ap.add_argument("--kernel", action="append", default=[])
     ap.add_argument("--pmc-pass", metavar="ORDER_JSON", default=None,
                     help="run one eager step for counter collection and write its dispatch order")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None)
@@ -97,7 +105,7 @@ def build_step(torch, bi, lib, _native, synthetic, dev):
     Mmax = max(Ms)
     t0 = time.time()
     data = {}
-    copies = {4096: 8, 14336: 4}          # > 256 MB of weights per N and layout
+    copies = {N: rotation(2.0 * N * K) for N in Ns}     # >= 2 x 256 MB of weights per N
     for N in Ns:
         d = synthetic.cfg2_inputs(N, M_max=Mmax)
         w = d["w"].to(dev)
@@ -152,6 +160,9 @@ def main():
     if args.summarize_pmc:
         summarize_pmc(args)
         return
+    if args.summarize_counters:
+        summarize_counters(args)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the library runs on one GPU and has no multi-GPU path "
               "(run with --gpus 1).", file=sys.stderr)
@@ -166,6 +177,14 @@ def main():
     lib = _native.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.cell:
+        # chosen cells only (used for the profiles of single kernels)
+        global EAGER
+        EAGER = args.eager
+        ctx = Ctx(torch, bi, lib, dev, synthetic, args.samples)
+        cells = measure_cells(ctx, args.cell)
+        print(json.dumps({"cells": cells}), flush=True)
+        return
     st = build_step(torch, bi, lib, _native, synthetic, dev)
     if args.pmc_pass:
         pmc_pass(torch, st, args.pmc_pass)
@@ -282,7 +301,7 @@ def main():
     # ------------------------------------------------------------ per-cell table (outside the step)
     cells = {}
     if not args.no_cells:
-        cells = measure_cells(bi, lib, torch, dev, synthetic, data, launches, groups, names, group_ms)
+        cells = measure_cells(Ctx(torch, bi, lib, dev, synthetic, args.samples, data))
 
     # ------------------------------------------------------------ CPU oracle baseline
     cpu = None
@@ -318,8 +337,29 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def _time_graph(torch, fn, reps=20, iters=10):
-    """Median per-call ms of fn replayed from a captured graph (reps calls per replay)."""
+ROTATE_BYTES = 512 * 2 ** 20     # inputs rotate through >= 2 x the 256 MB Infinity Cache, so reads are cold
+
+
+def rotation(nbytes: float) -> int:
+    """Copies of an input of nbytes that together exceed ROTATE_BYTES."""
+    return max(1, -(-ROTATE_BYTES // int(nbytes)))
+
+
+def _pct(sorted_vals, q):
+    return sorted_vals[min(len(sorted_vals) - 1, int(round(q * (len(sorted_vals) - 1))))]
+
+
+EAGER = False    # --eager: cells call their kernels directly instead of replaying graphs (counter runs)
+
+
+def _time_graph(torch, fn, reps=20, samples=200, warm=10, keep=True):
+    """Per-call time of fn replayed from a captured graph (reps calls per replay).
+
+    At least `warm` warm-up replays, and about 30 ms of them so clocks have settled; then `samples`
+    replays, each bracketed by its own pair of events.  Returns the median and p95 per-call time in us,
+    the sample count and (keep=True) every per-call sample in ns."""
+    if EAGER:
+        return _time_eager(torch, fn, reps, samples, keep)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -329,187 +369,385 @@ def _time_graph(torch, fn, reps=20, iters=10):
     with torch.cuda.graph(g):
         for _ in range(reps):
             fn()
-    # warm-up replays for about 30 ms, so clocks have settled before timing
     t0 = time.perf_counter()
     g.replay()
     torch.cuda.synchronize()
     once = time.perf_counter() - t0
-    for _ in range(min(200, int(0.03 / max(once, 1e-6)) + 1)):
+    for _ in range(max(warm, min(200, int(0.03 / max(once, 1e-6)) + 1))):
         g.replay()
     torch.cuda.synchronize()
-    ts = []
-    for _ in range(iters):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(samples)]
+    for a, b in evs:
         a.record()
         g.replay()
         b.record()
-        b.synchronize()
-        ts.append(a.elapsed_time(b) / reps)
-    ts.sort()
-    return ts[len(ts) // 2]
+    torch.cuda.synchronize()
+    ns = [a.elapsed_time(b) * 1e6 / reps for a, b in evs]
+    srt = sorted(ns)
+    out = {"us": round(_pct(srt, 0.5) / 1e3, 3), "p95_us": round(_pct(srt, 0.95) / 1e3, 3), "n": samples}
+    if keep:
+        out["samples_ns"] = [int(round(v)) for v in ns]
+    del g
+    return out
 
 
-def measure_cells(bi, lib, torch, dev, synthetic, data, launches, groups, names, group_ms):
-    cells = {"decode_gemm": [], "large_m_gemm": [], "decode_attention": [], "prefill_attention": [],
-             "comparator": {}, "e2e_decode": {}}
+def _time_eager(torch, fn, reps, samples, keep):
+    """As _time_graph with direct calls (one warm-up round), for counter collection runs."""
+    for _ in range(reps):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(samples)]
+    for a, b in evs:
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+    torch.cuda.synchronize()
+    ns = sorted(a.elapsed_time(b) * 1e6 / reps for a, b in evs)
+    out = {"us": round(_pct(ns, 0.5) / 1e3, 3), "p95_us": round(_pct(ns, 0.95) / 1e3, 3), "n": samples}
+    if keep:
+        out["samples_ns"] = [int(round(v)) for v in ns]
+    return out
+
+
+class Ctx:
+    """What the cells share: modules, device, sample count, the measured ceilings and the weights."""
+
+    def __init__(self, torch, bi, lib, dev, synthetic, samples, data=None):
+        self.torch, self.bi, self.lib, self.dev, self.synthetic = torch, bi, lib, dev, synthetic
+        self.samples = samples
+        self.data = data or {}
+        self.ceil = None
+
+    def weights(self, N):
+        """The bf16 linear workload's x (256, 4096), bias and a rotation set of W (N, 4096) copies."""
+        if N not in self.data:
+            d = self.synthetic.cfg2_inputs(N, M_max=256)
+            w = d["w"].to(self.dev)
+            ws = [w] + [w.clone() for _ in range(rotation(w.numel() * 2) - 1)]
+            self.data[N] = dict(x=d["x"].to(self.dev), w=ws, wt=[c.t() for c in ws], b=d["b"].to(self.dev),
+                                sha=self.synthetic.sha256(d["w"]))
+        return self.data[N]
+
+    def frac(self, value, kind):
+        """Fraction of the measured ceiling ("hbm": GB/s, "mfma": TFLOP/s), or None before it is measured."""
+        if not self.ceil:
+            return None
+        top = self.ceil["hbm_stream_read"]["GBps"] if kind == "hbm" else self.ceil["mfma_bf16"]["TFLOPs"]
+        return round(value / top, 4)
+
+
+def _cell(ctx, t, **fields):
+    """A cell's record: its fields, then the timing statistics (raw samples last)."""
+    rec = dict(fields)
+    rec.update({k: v for k, v in t.items() if k != "samples_ns"})
+    if "samples_ns" in t:
+        rec["samples_ns"] = t["samples_ns"]
+    return rec
+
+
+def cell_ceilings(ctx):
+    """What this GPU measurably sustains: a streaming read of 1 GiB (every byte once; best of 1, 2 and 4
+    workgroups of 256 threads per CU, and the same read of 32 MiB / 112 MiB, the decode weights of
+    N = 4096 / 14336, as single launches) and an MFMA-only loop (8 independent bf16 16x16x32 chains per
+    wavefront, 1 and 2 workgroups of 4 wavefronts per CU)."""
+    torch, lib = ctx.torch, ctx.lib
+    sink = torch.zeros(256 * 8 * 256, dtype=torch.int32, device=ctx.dev)
+
+    def stream():                 # the stream a graph capture records (read at each call)
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    out = {}
+    best = None
+    for nb in (2 ** 30, 32 * 2 ** 20, 112 * 2 ** 20):
+        src = torch.empty(nb // 4, dtype=torch.int32, device=ctx.dev).random_(0, 2 ** 30)
+        for wpc in ((1, 2, 4) if nb == 2 ** 30 else (4,)):
+            fn = (lambda src=src, wpc=wpc: _chk(lib.bi_measure_stream_read(ctypes.c_void_p(src.data_ptr()), nb,
+                                                                          ctypes.c_void_p(sink.data_ptr()),
+                                                                          256 * wpc, stream())))
+            t = _time_graph(torch, fn, reps=4 if nb == 2 ** 30 else 20, samples=min(ctx.samples, 100), keep=False)
+            gbps = nb / (t["us"] * 1e-6) / 1e9
+            rec = {"bytes": nb, "workgroups_per_cu": wpc, "us": t["us"], "p95_us": t["p95_us"], "GBps": round(gbps, 1),
+                   "frac_hbm": round(gbps / HBM_PEAK_GBPS, 4)}
+            if nb == 2 ** 30:
+                if best is None or gbps > best["GBps"]:
+                    best = rec
+            else:
+                out[f"stream_read_{nb >> 20}MiB"] = rec
+        del src
+    out["hbm_stream_read"] = best
+    mbest = None
+    for wpc in (1, 2):
+        flops = [0.0]
+
+        def fn(wpc=wpc):
+            flops[0] = lib.bi_measure_mfma(ctypes.c_void_p(sink.data_ptr()), 256 * wpc, 4096, stream())
+            if flops[0] < 0:
+                raise RuntimeError("bi_measure_mfma refused its arguments")
+        t = _time_graph(torch, fn, reps=4, samples=min(ctx.samples, 100), keep=False)
+        tf = flops[0] / (t["us"] * 1e-6) / 1e12
+        rec = {"workgroups_per_cu": wpc, "us": t["us"], "TFLOPs": round(tf, 1), "frac_mfma": round(tf / BF16_PEAK_TFLOPS, 4)}
+        if mbest is None or tf > mbest["TFLOPs"]:
+            mbest = rec
+    out["mfma_bf16"] = mbest
+    ctx.ceil = out
+    return out
+
+
+def _chk(rc):
+    if rc != 0:
+        raise RuntimeError(f"bi_measure_stream_read returned {rc}")
+
+
+def cell_decode_gemm(ctx):
+    """bi_linear at M in {1, 2, 4, 8} x N in {4096, 14336, 32000}, K = 4096, bf16, weights cold."""
+    torch, bi = ctx.torch, ctx.bi
     K = 4096
-    # decode GEMM: weights rotate through copies inside one graph, so reads are cold
-    logits = synthetic.cfg5_inputs(torch.bfloat16, M_max=8)
-    wl = logits["w"].to(dev)
-    wls = [wl, wl.clone()]
-    xl = logits["h"].to(dev)
+    logits = ctx.synthetic.cfg5_inputs(torch.bfloat16, M_max=8)
+    wl = logits["w"].to(ctx.dev)
+    wls = [wl] + [wl.clone() for _ in range(rotation(wl.numel() * 2) - 1)]
+    xl = logits["h"].to(ctx.dev)
+    res = []
     for N in (4096, 14336, 32000):
         for M in (1, 2, 4, 8):
             if N == 32000:
                 ws, x = wls, xl
             else:
-                ws, x = data[N]["w"], data[N]["x"]
+                ws, x = ctx.weights(N)["w"], ctx.weights(N)["x"]
             it = iter(range(10 ** 9))
             fn = (lambda: bi.bi_linear(x[:M], ws[next(it) % len(ws)]))
-            ms = _time_graph(torch, fn, reps=len(ws) * 2)
+            t = _time_graph(torch, fn, reps=len(ws) * 2, samples=ctx.samples)
             nbytes = 2.0 * (M * K + N * K + M * N)
-            gbps = nbytes / (ms * 1e-3) / 1e9
-            cells["decode_gemm"].append({"M": M, "N": N, "us": round(ms * 1e3, 2), "GBps": round(gbps, 1),
-                                         "frac_hbm": round(gbps / HBM_PEAK_GBPS, 4),
-                                         "kernel": lib.bi_gemm_kernel_name(M, N, K, bi.BI_BF16, 0).decode()})
+            gbps = nbytes / (t["us"] * 1e-6) / 1e9
+            res.append(_cell(ctx, t, M=M, N=N, GBps=round(gbps, 1), frac_hbm=round(gbps / HBM_PEAK_GBPS, 4),
+                             frac_ceiling=ctx.frac(gbps, "hbm"), rotated_copies=len(ws),
+                             kernel=ctx.lib.bi_gemm_kernel_name(M, N, K, bi.BI_BF16, 0).decode()))
     del wls, wl
-    # large-M GEMM (added points, above the configs' M = 256)
+    return res
+
+
+def cell_large_m_gemm(ctx):
+    """bi_linear at M in {512, 1024, 4096} x N in {4096, 14336}, K = 4096, bf16 (added points above M = 256)."""
+    torch, bi = ctx.torch, ctx.bi
+    K = 4096
+    res = []
     for N in (4096, 14336):
-        w = data[N]["w"][0]
+        w = ctx.weights(N)["w"][0]
         for M in (512, 1024, 4096):
-            x = synthetic.randn((M, K), 0x5EED77, 1.0, torch.bfloat16).to(dev)
-            ms = _time_graph(torch, lambda: bi.bi_linear(x, w), reps=5, iters=6)
-            tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
-            cells["large_m_gemm"].append({"M": M, "N": N, "us": round(ms * 1e3, 1), "TFLOPs": round(tf, 1),
-                                          "frac_mfma": round(tf / BF16_PEAK_TFLOPS, 4),
-                                          "kernel": lib.bi_gemm_kernel_name(M, N, K, bi.BI_BF16, 0).decode()})
-    # decode attention on the pages' sweep shape (Hq 32, Hkv 8, D 128, bf16, q_len 1)
-    for B, S in ((8, 2048), (8, 8192), (32, 8192), (32, 32768)):
-        # multi-GB timing-only inputs: seeded draws on the GPU generator
-        gen = torch.Generator(device=dev)
-        gen.manual_seed(0x5EED90 + B * 100000 + S)
-        q = torch.randn((B, 32, 1, 128), generator=gen, device=dev).to(torch.bfloat16)
-        k = torch.randn((B, 8, S, 128), generator=gen, device=dev).to(torch.bfloat16)
-        v = torch.randn((B, 8, S, 128), generator=gen, device=dev).to(torch.bfloat16)
-        ws = torch.empty(bi.sdpa_workspace_bytes(B, 32, 8, 1, S, 128, torch.bfloat16), dtype=torch.uint8, device=dev)
-        ms = _time_graph(torch, lambda: bi.bi_sdpa(q, k, v, causal=True, workspace=ws), reps=4, iters=6)
+            x = ctx.synthetic.randn((M, K), 0x5EED77, 1.0, torch.bfloat16).to(ctx.dev)
+            t = _time_graph(torch, lambda: bi.bi_linear(x, w), reps=5, samples=ctx.samples)
+            tf = 2.0 * M * N * K / (t["us"] * 1e-6) / 1e12
+            res.append(_cell(ctx, t, M=M, N=N, TFLOPs=round(tf, 1), frac_mfma=round(tf / BF16_PEAK_TFLOPS, 4),
+                             frac_ceiling=ctx.frac(tf, "mfma"),
+                             kernel=ctx.lib.bi_gemm_kernel_name(M, N, K, bi.BI_BF16, 0).decode()))
+    return res
+
+
+def _decode_inputs(torch, dev, B, S, D, seed):
+    """Seeded timing-only decode attention inputs, drawn on the GPU generator (multi-GB at the largest
+    cells), K / V in enough copies to exceed the rotation size."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    q = torch.randn((B, 32, 1, D), generator=gen, device=dev).to(torch.bfloat16)
+    k = torch.randn((B, 8, S, D), generator=gen, device=dev).to(torch.bfloat16)
+    v = torch.randn((B, 8, S, D), generator=gen, device=dev).to(torch.bfloat16)
+    n = rotation(2.0 * k.numel() * 2)
+    kv = [(k, v)] + [(k.clone(), v.clone()) for _ in range(n - 1)]
+    return q, kv, gen
+
+
+def cell_decode_attention(ctx):
+    """bi_sdpa decode (q_len 1, causal) on the pages' sweep shape: Hq 32, Hkv 8, D 128, bf16,
+    B in {8, 32} x S in {2048, 8192, 32768}; K / V cold."""
+    torch, bi, lib = ctx.torch, ctx.bi, ctx.lib
+    res = []
+    for B, S in ((8, 2048), (8, 8192), (8, 32768), (32, 2048), (32, 8192), (32, 32768)):
+        q, kv, _ = _decode_inputs(torch, ctx.dev, B, S, 128, 0x5EED90 + B * 100000 + S)
+        ws = torch.empty(max(1, bi.sdpa_workspace_bytes(B, 32, 8, 1, S, 128, torch.bfloat16)), dtype=torch.uint8,
+                         device=ctx.dev)
+        it = iter(range(10 ** 9))
+
+        def fn():
+            k, v = kv[next(it) % len(kv)]
+            return bi.bi_sdpa(q, k, v, causal=True, workspace=ws)
+        t = _time_graph(torch, fn, reps=max(4, 2 * len(kv)), samples=ctx.samples)
         nbytes = 2.0 * (B * 8 * S * 128 * 2 + 2 * B * 32 * 128)
-        gbps = nbytes / (ms * 1e-3) / 1e9
-        cells["decode_attention"].append({"B": B, "S": S, "us": round(ms * 1e3, 1), "GBps": round(gbps, 1),
-                                          "frac_hbm": round(gbps / HBM_PEAK_GBPS, 4)})
-        del q, k, v, ws
-    # the other attention forms on the decode shape: sinks, a boolean (uint8) and an additive (bf16)
-    # padding mask over (B, 1, 1, S), each as a ratio to the plain call; head dims 64 and 256
-    cells["attention_forms"] = []
+        gbps = nbytes / (t["us"] * 1e-6) / 1e9
+        res.append(_cell(ctx, t, B=B, S=S, GBps=round(gbps, 1), frac_hbm=round(gbps / HBM_PEAK_GBPS, 4),
+                         frac_ceiling=ctx.frac(gbps, "hbm"), rotated_copies=len(kv),
+                         kernel=lib.bi_sdpa_kernel_name(B, 32, 8, 1, S, 128, bi.BI_BF16).decode()))
+        del q, kv, ws
+    return res
+
+
+def cell_attention_forms(ctx):
+    """Sinks, a boolean (uint8) and an additive (bf16) padding mask over (B, 1, 1, S) on the decode shape,
+    each as a ratio to the plain causal call; head dims 64 and 256 in decode and 2048-token prefill."""
+    torch, bi, lib = ctx.torch, ctx.bi, ctx.lib
+    ns = min(ctx.samples, 50)
+    res = []
     for B, S in ((8, 8192), (32, 8192)):
-        gen = torch.Generator(device=dev)
-        gen.manual_seed(0x5EED91 + B * 100000 + S)
-        q = torch.randn((B, 32, 1, 128), generator=gen, device=dev).to(torch.bfloat16)
-        k = torch.randn((B, 8, S, 128), generator=gen, device=dev).to(torch.bfloat16)
-        v = torch.randn((B, 8, S, 128), generator=gen, device=dev).to(torch.bfloat16)
-        ws = torch.empty(lib.bi_sdpa_workspace_bytes(B, 32, 8, 1, S, 128, bi.BI_BF16), dtype=torch.uint8, device=dev)
-        sinks = torch.randn((32,), generator=gen, device=dev)
-        keep = torch.rand((B, 1, 1, S), generator=gen, device=dev) > 0.1
+        q, kv, gen = _decode_inputs(torch, ctx.dev, B, S, 128, 0x5EED91 + B * 100000 + S)
+        ws = torch.empty(lib.bi_sdpa_workspace_bytes(B, 32, 8, 1, S, 128, bi.BI_BF16), dtype=torch.uint8, device=ctx.dev)
+        sinks = torch.randn((32,), generator=gen, device=ctx.dev)
+        keep = torch.rand((B, 1, 1, S), generator=gen, device=ctx.dev) > 0.1
         m8 = keep.to(torch.uint8)
-        madd = torch.where(keep, torch.randn((B, 1, 1, S), generator=gen, device=dev),
-                           torch.full((), float("-inf"), device=dev)).to(torch.bfloat16)
-        forms = (("causal", lambda: bi.bi_sdpa(q, k, v, causal=True, workspace=ws)),
-                 ("causal+sinks", lambda: bi.bi_sdpa(q, k, v, causal=True, workspace=ws, sinks=sinks)),
-                 ("bool mask", lambda: bi.bi_sdpa(q, k, v, mask=m8, workspace=ws)),
-                 ("additive mask", lambda: bi.bi_sdpa(q, k, v, mask=madd, workspace=ws)))
+        madd = torch.where(keep, torch.randn((B, 1, 1, S), generator=gen, device=ctx.dev),
+                           torch.full((), float("-inf"), device=ctx.dev)).to(torch.bfloat16)
+        it = iter(range(10 ** 9))
+
+        def kvn():
+            return kv[next(it) % len(kv)]
+        forms = (("causal", lambda: bi.bi_sdpa(q, *kvn(), causal=True, workspace=ws)),
+                 ("causal+sinks", lambda: bi.bi_sdpa(q, *kvn(), causal=True, workspace=ws, sinks=sinks)),
+                 ("bool mask", lambda: bi.bi_sdpa(q, *kvn(), mask=m8, workspace=ws)),
+                 ("additive mask", lambda: bi.bi_sdpa(q, *kvn(), mask=madd, workspace=ws)))
         base = None
         for name, fn in forms:
-            ms = _time_graph(torch, fn, reps=4, iters=6)
-            base = base or ms
-            gbps = 2.0 * (B * 8 * S * 128 * 2) / (ms * 1e-3) / 1e9
-            cells["attention_forms"].append({"B": B, "S": S, "D": 128, "form": name, "us": round(ms * 1e3, 1),
-                                             "GBps": round(gbps, 1), "frac_hbm": round(gbps / HBM_PEAK_GBPS, 4),
-                                             "over_causal": round(ms / base, 3)})
-        del q, k, v, ws
+            t = _time_graph(torch, fn, reps=max(4, 2 * len(kv)), samples=ns, keep=False)
+            base = base or t["us"]
+            gbps = 2.0 * (B * 8 * S * 128 * 2) / (t["us"] * 1e-6) / 1e9
+            res.append(_cell(ctx, t, B=B, S=S, D=128, form=name, GBps=round(gbps, 1),
+                             frac_hbm=round(gbps / HBM_PEAK_GBPS, 4), over_causal=round(t["us"] / base, 3)))
+        del q, kv, ws
     for D in (64, 256):
         B, S = 8, 8192
-        gen = torch.Generator(device=dev)
-        gen.manual_seed(0x5EED92 + D)
-        q = torch.randn((B, 32, 1, D), generator=gen, device=dev).to(torch.bfloat16)
-        k = torch.randn((B, 8, S, D), generator=gen, device=dev).to(torch.bfloat16)
-        v = torch.randn((B, 8, S, D), generator=gen, device=dev).to(torch.bfloat16)
-        ws = torch.empty(lib.bi_sdpa_workspace_bytes(B, 32, 8, 1, S, D, bi.BI_BF16), dtype=torch.uint8, device=dev)
-        ms = _time_graph(torch, lambda: bi.bi_sdpa(q, k, v, causal=True, workspace=ws), reps=4, iters=6)
-        gbps = 2.0 * (B * 8 * S * D * 2) / (ms * 1e-3) / 1e9
-        cells["attention_forms"].append({"B": B, "S": S, "D": D, "form": "causal decode", "us": round(ms * 1e3, 1),
-                                         "GBps": round(gbps, 1), "frac_hbm": round(gbps / HBM_PEAK_GBPS, 4),
-                                         "kernel": lib.bi_sdpa_kernel_name(B, 32, 8, 1, S, D, bi.BI_BF16).decode()})
-        qp = torch.randn((1, 32, 2048, D), generator=gen, device=dev).to(torch.bfloat16)
-        kp = torch.randn((1, 8, 2048, D), generator=gen, device=dev).to(torch.bfloat16)
-        wsp = torch.empty(lib.bi_sdpa_workspace_bytes(1, 32, 8, 2048, 2048, D, bi.BI_BF16), dtype=torch.uint8, device=dev)
-        ms = _time_graph(torch, lambda: bi.bi_sdpa(qp, kp, kp, causal=True, workspace=wsp), reps=2, iters=4)
-        tf = 4.0 * 32 * D * (2048 * 2049 / 2) / (ms * 1e-3) / 1e12
-        cells["attention_forms"].append({"B": 1, "Lq": 2048, "S": 2048, "D": D, "form": "causal prefill",
-                                         "us": round(ms * 1e3, 1), "TFLOPs": round(tf, 1),
-                                         "frac_mfma": round(tf / BF16_PEAK_TFLOPS, 4),
-                                         "kernel": lib.bi_sdpa_kernel_name(1, 32, 8, 2048, 2048, D, bi.BI_BF16).decode()})
-        del q, k, v, ws, qp, kp, wsp
-    # long causal prefill (query chunk = whole cache): workspace-free kernel, flops of visible pairs
+        q, kv, gen = _decode_inputs(torch, ctx.dev, B, S, D, 0x5EED92 + D)
+        ws = torch.empty(lib.bi_sdpa_workspace_bytes(B, 32, 8, 1, S, D, bi.BI_BF16), dtype=torch.uint8, device=ctx.dev)
+        it = iter(range(10 ** 9))
+
+        def fn():
+            k, v = kv[next(it) % len(kv)]
+            return bi.bi_sdpa(q, k, v, causal=True, workspace=ws)
+        t = _time_graph(torch, fn, reps=max(4, 2 * len(kv)), samples=ns, keep=False)
+        gbps = 2.0 * (B * 8 * S * D * 2) / (t["us"] * 1e-6) / 1e9
+        res.append(_cell(ctx, t, B=B, S=S, D=D, form="causal decode", GBps=round(gbps, 1),
+                         frac_hbm=round(gbps / HBM_PEAK_GBPS, 4),
+                         kernel=lib.bi_sdpa_kernel_name(B, 32, 8, 1, S, D, bi.BI_BF16).decode()))
+        qp = torch.randn((1, 32, 2048, D), generator=gen, device=ctx.dev).to(torch.bfloat16)
+        kp = torch.randn((1, 8, 2048, D), generator=gen, device=ctx.dev).to(torch.bfloat16)
+        wsp = torch.empty(max(1, lib.bi_sdpa_workspace_bytes(1, 32, 8, 2048, 2048, D, bi.BI_BF16)), dtype=torch.uint8,
+                          device=ctx.dev)
+        t = _time_graph(torch, lambda: bi.bi_sdpa(qp, kp, kp, causal=True, workspace=wsp), reps=2, samples=ns,
+                        keep=False)
+        tf = 4.0 * 32 * D * (2048 * 2049 / 2) / (t["us"] * 1e-6) / 1e12
+        res.append(_cell(ctx, t, B=1, Lq=2048, S=2048, D=D, form="causal prefill", TFLOPs=round(tf, 1),
+                         frac_mfma=round(tf / BF16_PEAK_TFLOPS, 4),
+                         kernel=lib.bi_sdpa_kernel_name(1, 32, 8, 2048, 2048, D, bi.BI_BF16).decode()))
+        del q, kv, ws, qp, kp, wsp
+    return res
+
+
+def cell_prefill_attention(ctx):
+    """Long causal prefill (query chunk = whole cache), Hq 32, Hkv 8, D 128, bf16, at 4096 and 8192
+    tokens; flops of the causally visible pairs only."""
+    torch, bi = ctx.torch, ctx.bi
+    res = []
     for S in (4096, 8192):
-        gen = torch.Generator(device=dev)
+        gen = torch.Generator(device=ctx.dev)
         gen.manual_seed(0x5EED95 + S)
-        q = torch.randn((1, 32, S, 128), generator=gen, device=dev).to(torch.bfloat16)
-        k = torch.randn((1, 8, S, 128), generator=gen, device=dev).to(torch.bfloat16)
-        v = torch.randn((1, 8, S, 128), generator=gen, device=dev).to(torch.bfloat16)
-        ms = _time_graph(torch, lambda: bi.bi_sdpa(q, k, v, causal=True), reps=2, iters=5)
+        q = torch.randn((1, 32, S, 128), generator=gen, device=ctx.dev).to(torch.bfloat16)
+        k = torch.randn((1, 8, S, 128), generator=gen, device=ctx.dev).to(torch.bfloat16)
+        v = torch.randn((1, 8, S, 128), generator=gen, device=ctx.dev).to(torch.bfloat16)
+        t = _time_graph(torch, lambda: bi.bi_sdpa(q, k, v, causal=True), reps=2, samples=ctx.samples)
         flops = 4.0 * 32 * 128 * (S * (S + 1) / 2)
-        tf = flops / (ms * 1e-3) / 1e12
-        cells["prefill_attention"].append({"B": 1, "Lq": S, "S": S, "us": round(ms * 1e3, 1), "TFLOPs": round(tf, 1),
-                                           "frac_mfma": round(tf / BF16_PEAK_TFLOPS, 4),
-                                           "kernel": lib.bi_sdpa_kernel_name(1, 32, 8, S, S, 128, bi.BI_BF16).decode()})
+        tf = flops / (t["us"] * 1e-6) / 1e12
+        res.append(_cell(ctx, t, B=1, Lq=S, S=S, TFLOPs=round(tf, 1), frac_mfma=round(tf / BF16_PEAK_TFLOPS, 4),
+                         frac_ceiling=ctx.frac(tf, "mfma"),
+                         kernel=ctx.lib.bi_sdpa_kernel_name(1, 32, 8, S, S, 128, bi.BI_BF16).decode()))
         del q, k, v
-    # quantized linear (4-bit, groups of 64): packed weights rotate through copies so reads are cold;
-    # bytes = packed words + scales + biases + x + y; rows checked against M = 256 on raw bits
-    cells["quantized_gemm"] = []
+    return res
+
+
+def cell_quantized_gemm(ctx):
+    """bi_quantized_linear, 4-bit, groups of 64, K = 4096, M in {1, 4, 16, 64, 256} x N in {4096, 14336};
+    packed weights cold; bytes = packed words + scales + biases + x + y; rows checked against M = 256."""
+    torch, bi = ctx.torch, ctx.bi
+    K = 4096
+    res = []
+    differing = 0
     for N in (4096, 14336):
-        wq, sc, sb = bi.quantize(data[N]["w"][0], 4, 64)
+        d = ctx.weights(N)
+        wq, sc, sb = bi.quantize(d["w"][0], 4, 64)
         qbytes = wq.numel() * 4 + sc.numel() * 2 * 2
-        qs = [(wq, sc, sb)] + [(wq.clone(), sc.clone(), sb.clone()) for _ in range(max(1, -(-512 * 2**20 // qbytes)) - 1)]
-        xq = data[N]["x"]
+        qs = [(wq, sc, sb)] + [(wq.clone(), sc.clone(), sb.clone()) for _ in range(rotation(qbytes) - 1)]
+        xq = d["x"]
         full = bi.bi_quantized_linear(xq, wq, sc, sb, 4, 64)
-        differing = 0
         for M in (1, 4, 16, 64, 256):
             it = iter(range(10 ** 9))
-            ms = _time_graph(torch, lambda: bi.bi_quantized_linear(xq[:M], *qs[next(it) % len(qs)], 4, 64),
-                             reps=len(qs), iters=5)
+            t = _time_graph(torch, lambda: bi.bi_quantized_linear(xq[:M], *qs[next(it) % len(qs)], 4, 64),
+                            reps=len(qs), samples=min(ctx.samples, 50), keep=False)
             nbytes = qbytes + 2.0 * (M * K + M * N)
-            gbps = nbytes / (ms * 1e-3) / 1e9
-            tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
-            lin = next((c["us"] for c in cells["decode_gemm"] if c["M"] == M and c["N"] == N), None)
+            gbps = nbytes / (t["us"] * 1e-6) / 1e9
+            tf = 2.0 * M * N * K / (t["us"] * 1e-6) / 1e12
             part = bi.bi_quantized_linear(xq[:M], wq, sc, sb, 4, 64)
             differing += int((part.view(torch.int16) != full[:M].view(torch.int16)).any(dim=1).sum().item())
-            cells["quantized_gemm"].append({"M": M, "N": N, "bits": 4, "group_size": 64, "us": round(ms * 1e3, 2),
-                                            "GBps": round(gbps, 1), "frac_hbm": round(gbps / HBM_PEAK_GBPS, 4),
-                                            "TFLOPs": round(tf, 1),
-                                            "over_bf16_linear": round(ms * 1e3 / lin, 3) if lin else None})
-        cells.setdefault("quantized_rows_differing_from_M256", 0)
-        cells["quantized_rows_differing_from_M256"] += differing
+            res.append(_cell(ctx, t, M=M, N=N, bits=4, group_size=64, GBps=round(gbps, 1),
+                             frac_hbm=round(gbps / HBM_PEAK_GBPS, 4), TFLOPs=round(tf, 1)))
         del qs
-    # batch-variant comparator on the linear half of the step: cost ratio and negative control
-    inv_ms = var_ms = 0.0
-    diff = 0
+    return {"cells": res, "rows_differing_from_M256": differing}
+
+
+def cell_comparator(ctx):
+    """The batch-variant comparator beside the invariant path on the bf16 linear workload (K = 4096,
+    N in {4096, 14336}, every M of the sweep): total time of each, their ratio, and the negative control
+    (rows of each M that differ from the same rows at M = 256: nonzero for the variant, 0 for bi_linear)."""
+    torch, bi, lib = ctx.torch, ctx.bi, ctx.lib
+    inv_us = var_us = 0.0
+    diff_var = diff_inv = 0
+    per = []
     for N in (4096, 14336):
-        dN = data[N]
+        dN = ctx.weights(N)
         ws = dN["w"]
         full_var = bi.bi_variant_linear(dN["x"], ws[0], dN["b"])
-        for M in synthetic.CFG2["M_values"]:
+        full_inv = bi.bi_linear(dN["x"], ws[0], dN["b"])
+        for M in ctx.synthetic.CFG2["M_values"]:
             x = dN["x"][:M]
             it1, it2 = iter(range(10 ** 9)), iter(range(10 ** 9))
-            inv_ms += _time_graph(torch, lambda: bi.bi_linear(x, ws[next(it1) % len(ws)], dN["b"]),
-                                  reps=len(ws), iters=5)
-            var_ms += _time_graph(torch, lambda: bi.bi_variant_linear(x, ws[next(it2) % len(ws)], dN["b"]),
-                                  reps=len(ws), iters=5)
-            v = bi.bi_variant_linear(x, dN["w"][0], dN["b"])
-            diff += int((v.view(torch.int16) != full_var[:M].view(torch.int16)).any(dim=1).sum().item())
-    cells["comparator"] = {"invariant_ms": round(inv_ms, 4), "variant_ms": round(var_ms, 4),
-                           "invariant_over_variant_time": round(inv_ms / var_ms, 4),
-                           "variant_rows_differing_from_M256": diff}
-    cells["e2e_decode"] = e2e_decode(torch, bi, dev, synthetic)
+            ti = _time_graph(torch, lambda: bi.bi_linear(x, ws[next(it1) % len(ws)], dN["b"]),
+                             reps=len(ws), samples=min(ctx.samples, 50), keep=False)
+            tv = _time_graph(torch, lambda: bi.bi_variant_linear(x, ws[next(it2) % len(ws)], dN["b"]),
+                             reps=len(ws), samples=min(ctx.samples, 50), keep=False)
+            inv_us += ti["us"]
+            var_us += tv["us"]
+            v = bi.bi_variant_linear(x, ws[0], dN["b"])
+            y = bi.bi_linear(x, ws[0], dN["b"])
+            dv = int((v.view(torch.int16) != full_var[:M].view(torch.int16)).any(dim=1).sum().item())
+            di = int((y.view(torch.int16) != full_inv[:M].view(torch.int16)).any(dim=1).sum().item())
+            diff_var += dv
+            diff_inv += di
+            per.append({"M": M, "N": N, "invariant_us": ti["us"], "variant_us": tv["us"],
+                        "splits": int(lib.bi_variant_splits(M)),
+                        "invariant_kernel": lib.bi_gemm_kernel_name(M, N, 4096, bi.BI_BF16, 0).decode(),
+                        "variant_rows_differing": dv})
+    return {"invariant_ms": round(inv_us / 1e3, 4), "variant_ms": round(var_us / 1e3, 4),
+            "invariant_over_variant_time": round(inv_us / var_us, 4),
+            "variant_rows_differing_from_M256": diff_var, "invariant_rows_differing_from_M256": diff_inv,
+            "per_shape": per}
+
+
+def cell_e2e(ctx):
+    return {"decode": e2e_decode(ctx.torch, ctx.bi, ctx.dev, ctx.synthetic)}
+
+
+CELLS = {
+    "ceilings": cell_ceilings,
+    "decode_gemm": cell_decode_gemm,
+    "large_m_gemm": cell_large_m_gemm,
+    "decode_attention": cell_decode_attention,
+    "prefill_attention": cell_prefill_attention,
+    "attention_forms": cell_attention_forms,
+    "quantized_gemm": cell_quantized_gemm,
+    "comparator": cell_comparator,
+    "e2e": cell_e2e,
+}
+
+
+def measure_cells(ctx, names=None):
+    cells = {}
+    for name in names or list(CELLS):
+        t0 = time.time()
+        cells[name] = CELLS[name](ctx)
+        log(f"cell {name} measured in {time.time() - t0:.1f}s")
     return cells
 
 
@@ -566,8 +804,21 @@ class _nullcontext:
         return False
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(torch, synthetic, args):
-    import numpy as np  # noqa: F401
+    """The float64 CPU oracle, as it stands, on the host's OpenMP threads: the linear workload (whole passes
+    of the M = 256 batch at both N) for about --cpu-seconds, then the attention q_len sweep (q_len 1 ... 64
+    against the 1024-key cache, Hq 32, Hkv 8, D 128) for about as long."""
     import oracle
     if args.cpu_threads > 0:
         oracle.set_threads(args.cpu_threads)
@@ -577,7 +828,6 @@ def cpu_baseline(torch, synthetic, args):
     flops = 0.0
     passes = 0
     t0 = time.perf_counter()
-    # whole passes over the sample until at least args.cpu_seconds have gone by
     while passes == 0 or time.perf_counter() - t0 < args.cpu_seconds:
         for d in inputs:
             # the largest batch of the sweep: its rows contain every smaller batch's rows
@@ -585,12 +835,29 @@ def cpu_baseline(torch, synthetic, args):
             flops += 2.0 * d["x"].shape[0] * d["w"].shape[0] * d["w"].shape[1]
         passes += 1
     t = time.perf_counter() - t0
-    log(f"cpu oracle: {flops / 1e9:.1f} GFLOP in {t:.1f}s on {threads} threads ({passes} passes)")
+    log(f"cpu oracle linear: {flops / 1e9:.1f} GFLOP in {t:.1f}s on {threads} threads ({passes} passes)")
+    c3 = synthetic.cfg3_inputs(B=1, S=synthetic.CFG3["S"])
+    S3 = synthetic.CFG3["S"]
+    abytes = 0.0
+    apasses = 0
+    t1 = time.perf_counter()
+    while apasses == 0 or time.perf_counter() - t1 < args.cpu_seconds:
+        for L in synthetic.CFG3["Lq_values"]:
+            oracle.sdpa(c3["q"][:, :, S3 - L:], c3["k"], c3["v"], causal=True)
+            abytes += 2.0 * (2 * 8 * S3 * 128 + 2 * 32 * L * 128)
+        apasses += 1
+    ta = time.perf_counter() - t1
+    log(f"cpu oracle attention: {abytes / 1e6:.1f} MB in {ta:.1f}s ({apasses} passes)")
     return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu_model": _cpu_model(),
             "sample": f"{passes} passes of the float64 oracle linear on the M=256 batch (x 256x4096, bias) "
-                      "for N=4096 and N=14336, i.e. every row of the GEMM sweep once per pass; "
-                      "attention not included",
-            "seconds": round(t, 2)}
+                      "for N=4096 and N=14336, i.e. every row of the GEMM sweep once per pass",
+            "seconds": round(t, 2),
+            "attention": {"value": round(abytes / ta / 1e9, 6), "unit": "GB/s",
+                          "sample": f"{apasses} passes of the float64 oracle attention over the bf16 causal GQA "
+                                    "q_len sweep {1,2,4,8,9,16,64} against the 1024-key cache (Hq 32, Hkv 8, D 128), "
+                                    "bytes counted as on the GPU (K and V once per KV head, q and o)",
+                          "seconds": round(ta, 2)}}
 
 
 # ---------------------------------------------------------------- profiling helpers
@@ -702,6 +969,47 @@ def measured_traffic(group, family):
         return g["traffic_bytes"]
     except (OSError, AttributeError, KeyError, ValueError):
         return None
+
+
+def summarize_counters(args):
+    """Per-dispatch averages of every counter collected under a directory, for the kernels whose names
+    contain one of --kernel, with instruction counts per wavefront and per MFMA instruction."""
+    files = glob.glob(os.path.join(args.summarize_counters, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {args.summarize_counters}")
+    per = {}
+    for fn in files:
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                name = r["Kernel_Name"]
+                if args.kernel and not any(k in name for k in args.kernel):
+                    continue
+                d = per.setdefault(name, {}).setdefault(int(r["Dispatch_Id"]), {})
+                d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    lines = [f"# {args.title}", "", "Commands (run from the repository root on one MI355X):", "", "```"] + args.cmd + \
+        ["```", "", "Counter values are per dispatch, averaged over the dispatches of each kernel (SQ counters "
+         "summed over the whole GPU).", ""]
+    for name, disp in sorted(per.items()):
+        names = sorted({c for d in disp.values() for c in d})
+        avg = {c: sum(d.get(c, 0.0) for d in disp.values()) / len(disp) for c in names}
+        short = name if len(name) < 100 else name[:97] + "..."
+        lines += [f"## `{short}`", "", f"{len(disp)} dispatches.", "", "| counter | per dispatch |", "|---|---:|"]
+        lines += [f"| {c} | {avg[c]:.4g} |" for c in names]
+        waves = avg.get("SQ_WAVES")
+        mfma = avg.get("SQ_INSTS_MFMA") or avg.get("SQ_INSTS_VALU_MFMA_BF16")
+        derived = []
+        for c in ("SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_INSTS_MFMA", "SQ_INSTS_VALU_TRANS_F32",
+                  "SQ_INSTS_VMEM_RD"):
+            if c in avg and waves:
+                derived.append(f"| {c} per wavefront | {avg[c] / waves:.1f} |")
+            if c in avg and mfma and c != "SQ_INSTS_MFMA":
+                derived.append(f"| {c} per MFMA instruction | {avg[c] / mfma:.3f} |")
+        if derived:
+            lines += ["", "| derived | value |", "|---|---:|"] + derived
+        lines.append("")
+    with open(args.out, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
 
 
 def summarize_stats(args):

@@ -42,6 +42,9 @@ SIGNATURES = {
     "bi_status_name": (ctypes.c_char_p, [_i]),
     "bi_last_error": (ctypes.c_char_p, []),
     "bi_abi_version": (_i, []),
+    # include/bi_measure.h: measured ceilings for the benchmark
+    "bi_measure_stream_read": (_i, [_p, _sz, _p, _i, _p]),
+    "bi_measure_mfma": (ctypes.c_double, [_p, _i, _i, _p]),
 }
 
 _lib = None

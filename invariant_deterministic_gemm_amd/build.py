@@ -20,7 +20,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libbi.so")
-SOURCES = ["api.hip", "gemm.hip", "gemm16.hip", "sdpa.hip", "rowsum.hip", "qgemm.hip"]
+SOURCES = ["api.hip", "gemm.hip", "gemm16.hip", "sdpa.hip", "rowsum.hip", "qgemm.hip", "measure.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 

@@ -33,6 +33,8 @@
 // masked) run the same operations on the same operands, and appending masked
 // keys to the cache only appends identity steps.
 
+#include <type_traits>
+
 #include "device.h"
 #include "sdpa.h"
 
@@ -469,18 +471,20 @@ __device__ __forceinline__ void attn_scores16(const Rows16T<NC> &r, const char *
     }
 }
 
-// The rest of one block [kb, kb + 64) given its scores: visibility, the online-softmax update of
-// (m, l, O) and O += P . V from the V block in LDS (NT 16-column tiles, 32 NT-byte rows, chunk c of key
-// r at slot c ^ 2 (r mod 8); rows of keys past S must read as zero by the time v_ready() returns, which
-// is before the first V read).
-template <int dt, class VReady, int NC, int NT>
-__device__ __forceinline__ void attn_update16(const SdpaParams &p, const Rows16T<NC> &r, const f32x4 (&st)[4],
-                                              const char *Vs, int kb, float &m_run, float &l_run, f32x4 (&o)[NT],
-                                              VReady v_ready) {
-    constexpr int ROWB = 32 * NT;
+// The online-softmax half of one block [kb, kb + 64) given its scores: visibility, the update of (m, l)
+// and the rescale of O, leaving P rounded to the input dtype as the A fragments of the two 32-key
+// halves of P . V (k slot 8 g + j <-> key 32 c + 4 g + j (j < 4), 32 c + 16 + 4 g + (j - 4) (j >= 4)).
+// VISIBLE: the caller knows every key of the block is visible to every row (no mask, inside S, before
+// the tile's first causal position), which is the case the visibility test would pick.  RESCALE_ALWAYS:
+// O is multiplied by alpha even when no row's maximum moved (alpha = 1 then, and O * 1 = O), so the
+// update has no branch.  Neither changes any result.
+template <int dt, int NC, int NT, bool VISIBLE = false, bool RESCALE_ALWAYS = false>
+__device__ __forceinline__ void attn_softmax16(const SdpaParams &p, const Rows16T<NC> &r, const f32x4 (&st)[4],
+                                               int kb, float &m_run, float &l_run, f32x4 (&o)[NT],
+                                               u32x4 (&pf)[2]) {
     constexpr float NEG_INF = -__builtin_huge_valf();
     const int lane = threadIdx.x & 63;
-    const int r16 = lane & 15, g = lane >> 4;
+    const int g = lane >> 4;
     float s[4][4];
     // block maximum of the row (exact in any order): a tree over the lane's 16 scores, then the lane
     // groups; taken in each branch next to the products it reads, which the compiler then knows to be
@@ -492,7 +496,8 @@ __device__ __forceinline__ void attn_update16(const SdpaParams &p, const Rows16T
         return fmaxf(NEG_INF, fmaxf(fmaxf(mk[0], mk[1]), fmaxf(mk[2], mk[3])));   // all-NaN -> -inf
     };
     float mb;
-    const bool visible = p.mask == nullptr && kb + KV_BLOCK <= p.S && (!p.causal || kb + KV_BLOCK - 1 <= r.pos_first);
+    const bool visible =
+        VISIBLE || (p.mask == nullptr && kb + KV_BLOCK <= p.S && (!p.causal || kb + KV_BLOCK - 1 <= r.pos_first));
     if (visible) {
         // rows past R get real scores too: they are per-row, never stored, and touch no other row
 #pragma unroll
@@ -524,7 +529,7 @@ __device__ __forceinline__ void attn_update16(const SdpaParams &p, const Rows16T
     l_run = __builtin_fmaf(l_run, alpha, rs);
     m_run = m_new;
     // O * 1 = O: the rescale is skipped when no row's maximum moved
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+    if (RESCALE_ALWAYS || __builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const float ai = __shfl(alpha, 4 * g + i);
@@ -532,27 +537,47 @@ __device__ __forceinline__ void attn_update16(const SdpaParams &p, const Rows16T
             for (int t = 0; t < NT; ++t) o[t][i] = o[t][i] * ai;
         }
     }
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+        pf[c] = u32x4{pack_p<dt>(pr[2 * c][0], pr[2 * c][1]), pack_p<dt>(pr[2 * c][2], pr[2 * c][3]),
+                      pack_p<dt>(pr[2 * c + 1][0], pr[2 * c + 1][1]), pack_p<dt>(pr[2 * c + 1][2], pr[2 * c + 1][3])};
+}
+
+// V fragments of 32-key half c for the NT 16-column tiles (V block in LDS, 32 NT-byte rows, chunk c of key
+// r at slot c ^ 2 (r mod 8)): B operand of P . V, k slot j as in attn_softmax16.
+template <int NT>
+__device__ __forceinline__ void attn_vfrags16(const char *Vs, int c, u32x4 (&vf)[NT]) {
+    constexpr int ROWB = 32 * NT;
+    const int lane = threadIdx.x & 63;
+    const int r16 = lane & 15, g = lane >> 4;
+    const int row0 = 32 * c + 4 * g + (r16 >> 2);
+    const int row1 = row0 + 16;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const int ch = 2 * t + ((r16 & 3) >> 1);
+        const int off = 8 * (r16 & 1);
+        const u32x2 lo = lds_read_tr16(Vs + row0 * ROWB + ((ch ^ ((row0 & 7) << 1)) << 4) + off);
+        const u32x2 hi = lds_read_tr16(Vs + row1 * ROWB + ((ch ^ ((row1 & 7) << 1)) << 4) + off);
+        vf[t] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    }
+}
+
+// The rest of one block [kb, kb + 64) given its scores: attn_softmax16, then O += P . V from the V block
+// in LDS (rows of keys past S must read as zero by the time v_ready() returns, which is before the first
+// V read).  The V fragments of a half (c) are read before its NT MFMAs; o[t] takes c = 0 then c = 1.
+template <int dt, class VReady, int NC, int NT>
+__device__ __forceinline__ void attn_update16(const SdpaParams &p, const Rows16T<NC> &r, const f32x4 (&st)[4],
+                                              const char *Vs, int kb, float &m_run, float &l_run, f32x4 (&o)[NT],
+                                              VReady v_ready) {
+    u32x4 pf[2];
+    attn_softmax16<dt>(p, r, st, kb, m_run, l_run, o, pf);
     v_ready();
-    // ---- O += P . V: k slot 8 g + j <-> key 32 c + 4 g + j (j < 4), 32 c + 16 + 4 g + (j - 4) (j >= 4).
-    // The V fragments of a half (c) are read before its NT MFMAs; o[t] takes c = 0 then c = 1.
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-        const u32x4 pf = u32x4{pack_p<dt>(pr[2 * c][0], pr[2 * c][1]), pack_p<dt>(pr[2 * c][2], pr[2 * c][3]),
-                               pack_p<dt>(pr[2 * c + 1][0], pr[2 * c + 1][1]),
-                               pack_p<dt>(pr[2 * c + 1][2], pr[2 * c + 1][3])};
-        const int row0 = 32 * c + 4 * g + (r16 >> 2);
-        const int row1 = row0 + 16;
         u32x4 vf[NT];
+        attn_vfrags16<NT>(Vs, c, vf);
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const int ch = 2 * t + ((r16 & 3) >> 1);
-            const int off = 8 * (r16 & 1);
-            const u32x2 lo = lds_read_tr16(Vs + row0 * ROWB + ((ch ^ ((row0 & 7) << 1)) << 4) + off);
-            const u32x2 hi = lds_read_tr16(Vs + row1 * ROWB + ((ch ^ ((row1 & 7) << 1)) << 4) + off);
-            vf[t] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-        }
-#pragma unroll
-        for (int t = 0; t < NT; ++t) o[t] = Mfma<dt>::step(pf, vf[t], o[t]);
+        for (int t = 0; t < NT; ++t) o[t] = Mfma<dt>::step(pf[c], vf[t], o[t]);
     }
 }
 
@@ -1119,130 +1144,38 @@ __global__ __launch_bounds__(64 * 4 * T) void sdpa_quad16(SdpaParams p) {
     }
 }
 
-// Long prefill without a workspace: a workgroup of W wavefronts takes W
-// consecutive row tiles of one (batch, KV head) and walks all key blocks in
-// ascending order, each block loaded once into LDS for all W tiles (NB
-// buffers: blocks j + 1 .. j + NB - 1 load while block j is computed).  Every wavefront
-// runs exactly split16_body's per-block arithmetic on its tile, starting a
-// fresh (m, l, O) at each 256-key split boundary, and folds each split's
-// partial into a running state in registers with sdpa_combine's exact
-// operations in ascending split order, so every row gets the bits of the
-// split + combine path.  Blocks past the workgroup's last causal position are
-// not visited; for the tiles that stop earlier they are empty blocks, whose
-// split partials the fold skips, as it does for splits the split path never
-// launches.
-template <int dt, int W, int NB>
-__global__ __launch_bounds__(64 * W) void sdpa_prefill16(SdpaParams p) {
-    constexpr int ROWB = 256;
-    constexpr int KBYTES = KV_BLOCK * ROWB;            // one K (or V) block
-    constexpr int QBLK = 2 * KBYTES / 1024;            // 1 KiB loads per block (K then V)
-    constexpr int QW = QBLK / W;                       // loads per wavefront per block
-    constexpr int BPS = KV_SPLIT / KV_BLOCK;           // blocks per split
+// sdpa_combine's step for one split's partial (m_run, l_run, o) of the rows of a wavefront's 16-row tile,
+// folded into the running state (have, mt, lt, ot): per score row (lane r16), skip an empty partial, copy
+// the first non-empty one, otherwise rescale both sides to the larger maximum; O rows 4 g + i take the
+// factors of their score rows.  The split state then restarts empty.  When no row of the tile skips or
+// copies (the common case), the selects between the three outcomes are left out: they would all pick
+// the rescaled sum.
+template <int NT>
+__device__ __forceinline__ void fold_split16(float &m_run, float &l_run, f32x4 (&o)[NT], bool &have, float &mt,
+                                             float &lt, f32x4 (&ot)[NT]) {
     constexpr float NEG_INF = -__builtin_huge_valf();
-    static_assert(QBLK % W == 0, "every wavefront issues the same number of loads");
-    static_assert(16 % W == 0, "load q = wave + W j is a K load exactly when j < 16 / W");
-    static_assert(NB >= 2 && QW * (NB - 2) <= 63, "vmcnt range");
-    constexpr int QK = 16 / W;                         // K loads per wavefront per block
-    __shared__ __attribute__((aligned(1024))) char lds[NB * 2 * KBYTES];  // [buffer][K block | V block]
-
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int r16 = lane & 15, g = lane >> 4;
-    const int R = p.G * p.Lq;
-    const int ntile = (R + 15) / 16;
-    int wt, grp;
-    attn_work((ntile + W - 1) / W, p.B * p.Hkv, wt, grp);
-    const int b = grp / p.Hkv, gk = grp % p.Hkv;
-    const int tile = wt * W + wave;                    // tiles past the last compute clamped rows, store nothing
-
-    // keys the workgroup needs: up to its last row's causal position
-    const int rlast = min(wt * W * 16 + W * 16 - 1, R - 1);
-    const int nkeys = p.causal ? min(p.S - p.Lq + rlast / p.G + 1, p.S) : p.S;
-    const int nblk = (nkeys + KV_BLOCK - 1) / KV_BLOCK;
-
-    const char *kbase = static_cast<const char *>(p.k) + ((int64_t)b * p.ks[0] + (int64_t)gk * p.ks[1]) * 2;
-    const char *vbase = static_cast<const char *>(p.v) + ((int64_t)b * p.vs[0] + (int64_t)gk * p.vs[1]) * 2;
-    const int64_t kstr = p.ks[2] * 2, vstr = p.vs[2] * 2;
-    // load q = wave + W j of a block: q < 16 -> K key rows 4 q .. 4 q + 3, else V key rows 4 (q - 16) ..;
-    // lane L row 4 (q mod 16) + L / 16, slot L mod 16 (K chunk slot ^ (row mod 16), V chunk slot ^ 2 (row mod 8))
-    const int lrow = lane >> 4, lslot = lane & 15;
-    // per load j: this lane's key row within a block and its byte offset from the block's first key row.
-    // A block inside S is a uniform base pointer plus these 32-bit offsets (no per-lane 64-bit
-    // arithmetic); the block crossing S clamps its rows to S - 1 in 64-bit arithmetic, as does every
-    // block when a key row stride is too large for 32-bit offsets.
-    const bool off32 = (uint64_t)max(kstr, vstr) * KV_BLOCK + ROWB <= 0xffffffffull;
-    uint32_t loff[QW];
-    int lrowj[QW];
-    bool lz[QW];                                       // chunk at d >= D: read the zero page
-#pragma unroll
-    for (int j = 0; j < QW; ++j) {
-        const int row = 4 * ((wave + W * j) & 15) + lrow;
-        const int c = j < QK ? lslot ^ (row & 15) : lslot ^ ((row & 7) << 1);
-        lrowj[j] = row;
-        lz[j] = 8 * c >= p.dr;
-        loff[j] = (uint32_t)(row * (j < QK ? kstr : vstr)) + (c << 4);
+    const int g = (threadIdx.x & 63) >> 4;
+    const bool skip = m_run == NEG_INF;
+    const bool first = !skip && !have;
+    const float m2 = fmaxf(mt, m_run);
+    const float a = exp2_hw(mt - m2);
+    const float bs = exp2_hw(m_run - m2);
+    if (first) {
+        mt = m_run;
+        lt = l_run;
+    } else if (!skip) {
+        lt = __builtin_fmaf(lt, a, l_run * bs);
+        mt = m2;
     }
-    const char *zp = reinterpret_cast<const char *>(g_zero_page);
-    auto issue = [&](int blk) {
-        const int kb = blk * KV_BLOCK;
-        char *buf = lds + (blk % NB) * 2 * KBYTES;
-        if (off32 && kb + KV_BLOCK <= p.S) {
-            const char *kblk = kbase + (int64_t)kb * kstr;
-            const char *vblk = vbase + (int64_t)kb * vstr;
+    if (__builtin_amdgcn_ballot_w64(skip || first) == 0) {
 #pragma unroll
-            for (int j = 0; j < QW; ++j)
-                __builtin_amdgcn_global_load_lds(static_cast<const void *>(lz[j] ? zp : (j < QK ? kblk : vblk) + loff[j]),
-                                                 BI_LDS_PTR(buf + (j < QK ? 0 : KBYTES) + ((wave + W * j) & 15) * 1024),
-                                                 16, 0, 0);
-        } else {
+        for (int i = 0; i < 4; ++i) {
+            const int src = 4 * g + i;
+            const float a_i = __shfl(a, src), b_i = __shfl(bs, src);
 #pragma unroll
-            for (int j = 0; j < QW; ++j) {
-                const int row = lrowj[j];
-                const int64_t key = min(kb + row, p.S - 1);
-                const char *src = lz[j] ? zp
-                                  : j < QK ? kbase + key * kstr + ((lslot ^ (row & 15)) << 4)
-                                           : vbase + key * vstr + ((lslot ^ ((row & 7) << 1)) << 4);
-                __builtin_amdgcn_global_load_lds(static_cast<const void *>(src),
-                                                 BI_LDS_PTR(buf + (j < QK ? 0 : KBYTES) + ((wave + W * j) & 15) * 1024),
-                                                 16, 0, 0);
-            }
+            for (int t = 0; t < NT; ++t) ot[t][i] = __builtin_fmaf(ot[t][i], a_i, o[t][i] * b_i);
         }
-    };
-
-    Rows16 r;
-    rows16_load<dt>(p, tile, b, gk, r);
-    // running fold over splits (per score row in lane r16) and the current split's state; the sink,
-    // if any, is the fold's first partial
-    bool have = false;
-    float mt = 0.0f, lt = 0.0f;
-    if (p.sinks) {
-        const int rgc = min(tile * 16 + r16, R - 1);
-        mt = sink2(p, gk * p.G + rgc % p.G);
-        lt = 1.0f;
-        have = true;
-    }
-    f32x4 ot[8];
-    float m_run = NEG_INF, l_run = 0.0f;
-    f32x4 o[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-        ot[t] = zero4();
-        o[t] = zero4();
-    }
-    auto fold_split = [&]() {
-        // sdpa_combine's step for this split's partial, per row: skip an empty partial, copy the first
-        // non-empty one, otherwise rescale both sides to the larger maximum
-        const bool skip = m_run == NEG_INF;
-        const bool first = !skip && !have;
-        const float m2 = fmaxf(mt, m_run);
-        const float a = exp2_hw(mt - m2);
-        const float bs = exp2_hw(m_run - m2);
-        if (first) {
-            mt = m_run;
-            lt = l_run;
-        } else if (!skip) {
-            lt = __builtin_fmaf(lt, a, l_run * bs);
-            mt = m2;
-        }
+    } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int src = 4 * g + i;
@@ -1250,41 +1183,295 @@ __global__ __launch_bounds__(64 * W) void sdpa_prefill16(SdpaParams p) {
             const bool first_i = __shfl((int)first, src) != 0;
             const float a_i = __shfl(a, src), b_i = __shfl(bs, src);
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
+            for (int t = 0; t < NT; ++t) {
                 const float f = __builtin_fmaf(ot[t][i], a_i, o[t][i] * b_i);
                 ot[t][i] = first_i ? o[t][i] : skip_i ? ot[t][i] : f;
             }
         }
-        have = have || !skip;
-        m_run = NEG_INF;
-        l_run = 0.0f;
+    }
+    have = have || !skip;
+    m_run = NEG_INF;
+    l_run = 0.0f;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) o[t] = zero4();
+    for (int t = 0; t < NT; ++t) o[t] = zero4();
+}
+
+// The V fragments of one 32-key half as attn_vfrags16<8> reads them (same addresses, same values), issued
+// from one asm block that also waits for them.  The compiler cannot tell a transposed LDS read from the
+// direct-to-LDS loads in flight into the other buffer and would otherwise wait for those loads before the
+// first read; here the loads stay in flight.  va[t]: LDS address of tile t's first row-0 read of half 0;
+// HOFF: byte offset of the half (+ 16 key rows for the second read of a tile).  Outputs are early-clobber
+// so no read can overwrite an address a later read of the block still needs.
+template <int HOFF>
+__device__ __forceinline__ void vfrags_tr_asm(const uint32_t (&va)[8], u32x4 (&vf)[8]) {
+    u32x2 lo[8], hi[8];
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %16 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %8, %16 offset:%25\n\t"
+        "ds_read_b64_tr_b16 %1, %17 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %9, %17 offset:%25\n\t"
+        "ds_read_b64_tr_b16 %2, %18 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %10, %18 offset:%25\n\t"
+        "ds_read_b64_tr_b16 %3, %19 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %11, %19 offset:%25\n\t"
+        "ds_read_b64_tr_b16 %4, %20 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %12, %20 offset:%25\n\t"
+        "ds_read_b64_tr_b16 %5, %21 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %13, %21 offset:%25\n\t"
+        "ds_read_b64_tr_b16 %6, %22 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %14, %22 offset:%25\n\t"
+        "ds_read_b64_tr_b16 %7, %23 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %15, %23 offset:%25\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(lo[0]), "=&v"(lo[1]), "=&v"(lo[2]), "=&v"(lo[3]), "=&v"(lo[4]), "=&v"(lo[5]), "=&v"(lo[6]),
+          "=&v"(lo[7]), "=&v"(hi[0]), "=&v"(hi[1]), "=&v"(hi[2]), "=&v"(hi[3]), "=&v"(hi[4]), "=&v"(hi[5]),
+          "=&v"(hi[6]), "=&v"(hi[7])
+        : "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), "v"(va[4]), "v"(va[5]), "v"(va[6]), "v"(va[7]),
+          "i"(HOFF), "i"(HOFF + 16 * 256)
+        : "memory");
+#pragma unroll
+    for (int t = 0; t < 8; ++t) vf[t] = u32x4{lo[t][0], lo[t][1], hi[t][0], hi[t][1]};
+}
+
+// sdpa_combine's step when every row's split partial is non-empty (m_run finite): the rescaled sum, with no
+// branch.  A running state that is still empty (mt = -inf, lt = 0, ot = 0) takes the partial itself, as
+// the combine's copy does: a = exp2(-inf) = 0 and bs = 1 give lt = l_run and ot = o, except that a zero of
+// o may come out with the other sign, which no later fold, the division or the final -0 -> +0 step can turn
+// into a different output bit.
+template <int NT>
+__device__ __forceinline__ void fold_split16_full(float &m_run, float &l_run, f32x4 (&o)[NT], bool &have,
+                                                  float &mt, float &lt, f32x4 (&ot)[NT]) {
+    constexpr float NEG_INF = -__builtin_huge_valf();
+    const int g = (threadIdx.x & 63) >> 4;
+    const float m2 = fmaxf(mt, m_run);
+    const float a = exp2_hw(mt - m2);
+    const float bs = exp2_hw(m_run - m2);
+    lt = __builtin_fmaf(lt, a, l_run * bs);
+    mt = m2;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int src = 4 * g + i;
+        const float a_i = __shfl(a, src), b_i = __shfl(bs, src);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) ot[t][i] = __builtin_fmaf(ot[t][i], a_i, o[t][i] * b_i);
+    }
+    have = true;
+    m_run = NEG_INF;
+    l_run = 0.0f;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) o[t] = zero4();
+}
+
+// Long prefill (rows of 128, or zero-padded to 128 when PAD), software-pipelined over key blocks.  W row
+// tiles of one (batch, KV head), one per wavefront, share each K and V block through LDS; K runs two
+// blocks ahead and V one: while block j's softmax runs, block j + 1's scores are formed from its K block
+// on the matrix cores, and the loads of K(j + 2) and V(j + 1) are in flight.  Per tile the arithmetic is
+// the split path's: the same score chains (d chunks in order), attn_softmax16, P . V over the two 32-key
+// halves in order, a fresh (m, l, O) at every 256-key split and the combine's fold into the running
+// state, so every row gets the bits of the split + combine path.  Splits whose blocks every row of the
+// workgroup sees completely (no mask, inside S, before the first row's causal position) run a
+// branch-free body: visibility known, rescale by alpha always (O * 1 = O), the fold without its
+// empty-partial cases.  Causal workgroups start longest first.
+template <int dt, int W, bool PAD>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2)))
+void sdpa_prefill16p(SdpaParams p) {
+    constexpr int ROWB = 256;
+    constexpr int KBYTES = KV_BLOCK * ROWB;            // one K or V block
+    constexpr int QW = KBYTES / 1024 / W;              // 1 KiB loads per wavefront per K (or V) block
+    constexpr int BPS = KV_SPLIT / KV_BLOCK;           // blocks per split
+    constexpr float NEG_INF = -__builtin_huge_valf();
+    static_assert((KBYTES / 1024) % W == 0, "every wavefront issues the same loads");
+    // the K buffers as objects of their own, so the compiler can tell their reads from the direct-to-LDS
+    // loads into the other K buffer or into V (V is read by vfrags_tr_asm, which the compiler does not see)
+    __shared__ __attribute__((aligned(1024))) char kbuf0[KBYTES];
+    __shared__ __attribute__((aligned(1024))) char kbuf1[KBYTES];
+    __shared__ __attribute__((aligned(1024))) char vbufs[2 * KBYTES];
+    char *const vbuf0 = vbufs, *const vbuf1 = vbufs + KBYTES;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r16 = lane & 15, g = lane >> 4;
+    const int R = p.G * p.Lq;
+    const int ntile = (R + 15) / 16;
+    const int nwt = (ntile + W - 1) / W;
+    int wt, grp;
+    attn_work(nwt, p.B * p.Hkv, wt, grp);
+    if (p.causal) wt = nwt - 1 - wt;                   // the workgroups with the most keys start first
+    const int b = grp / p.Hkv, gk = grp % p.Hkv;
+    const int tile = wt * W + wave;                    // tiles past the last compute clamped rows, store nothing
+
+    const int rlast = min((wt + 1) * W * 16 - 1, R - 1);
+    const int nkeys = p.causal ? min(p.S - p.Lq + rlast / p.G + 1, p.S) : p.S;
+    const int nblk = (nkeys + KV_BLOCK - 1) / KV_BLOCK;
+    // splits every row of the workgroup sees completely; the last block always runs the general body
+    const int pos_wg = p.S - p.Lq + (wt * W * 16) / p.G;           // first row's causal position
+    int nfast = p.mask != nullptr ? 0 : (p.causal ? min(pos_wg + 1, p.S) : p.S) / KV_SPLIT;
+    nfast = max(0, min(nfast, (nblk - 1) / BPS));
+
+    const char *kbase = static_cast<const char *>(p.k) + ((int64_t)b * p.ks[0] + (int64_t)gk * p.ks[1]) * 2;
+    const char *vbase = static_cast<const char *>(p.v) + ((int64_t)b * p.vs[0] + (int64_t)gk * p.vs[1]) * 2;
+    const int64_t kstr = p.ks[2] * 2, vstr = p.vs[2] * 2;
+    // load j of a K (or V) block covers key rows 4 q .. 4 q + 3, q = wave + W j: lane L row 4 q + L / 16,
+    // slot L mod 16 (K chunk slot ^ (row mod 16), V chunk slot ^ 2 (row mod 8)).  A block inside S is a
+    // uniform base plus these 32-bit lane offsets; the block crossing S (and every block when a key row
+    // stride is too large for 32-bit offsets) clamps rows to S - 1 in 64-bit arithmetic.
+    const int lrow = lane >> 4, lslot = lane & 15;
+    const bool off32 = (uint64_t)max(kstr, vstr) * KV_BLOCK + ROWB <= 0xffffffffull;
+    uint32_t koff[QW], voff[QW];
+    bool kz[QW], vz[QW];                               // PAD: chunk at d >= D reads the zero page
+#pragma unroll
+    for (int j = 0; j < QW; ++j) {
+        const int row = 4 * (wave + W * j) + lrow;
+        const int ck = lslot ^ (row & 15), cv = lslot ^ ((row & 7) << 1);
+        kz[j] = PAD && 8 * ck >= p.dr;
+        vz[j] = PAD && 8 * cv >= p.dr;
+        koff[j] = (uint32_t)(row * kstr) + (ck << 4);
+        voff[j] = (uint32_t)(row * vstr) + (cv << 4);
+    }
+    const char *zp = reinterpret_cast<const char *>(g_zero_page);
+    auto issue = [&](int blk, char *buf, bool isv) {
+        const int kb = blk * KV_BLOCK;
+        const char *base = isv ? vbase : kbase;
+        const int64_t str = isv ? vstr : kstr;
+        if (off32 && kb + KV_BLOCK <= p.S) {
+            const char *bp = base + (int64_t)kb * str;
+#pragma unroll
+            for (int j = 0; j < QW; ++j) {
+                const char *src = bp + (isv ? voff[j] : koff[j]);
+                if constexpr (PAD) src = (isv ? vz[j] : kz[j]) ? zp : src;
+                __builtin_amdgcn_global_load_lds(static_cast<const void *>(src),
+                                                 BI_LDS_PTR(buf + (wave + W * j) * 1024), 16, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < QW; ++j) {
+                const int row = 4 * (wave + W * j) + lrow;
+                const int64_t key = min(kb + row, p.S - 1);
+                const int c = isv ? lslot ^ ((row & 7) << 1) : lslot ^ (row & 15);
+                const char *src = base + key * str + (c << 4);
+                if constexpr (PAD) src = (isv ? vz[j] : kz[j]) ? zp : src;
+                __builtin_amdgcn_global_load_lds(static_cast<const void *>(src),
+                                                 BI_LDS_PTR(buf + (wave + W * j) * 1024), 16, 0, 0);
+            }
+        }
     };
 
-    // blocks blk .. blk + NB - 2 are in flight when block blk is waited for; block blk + NB - 1 goes into
-    // the buffer block blk - 1 used, once every wavefront is past it
-    for (int j = 0; j < NB - 1 && j < nblk; ++j) issue(j);
-    for (int blk = 0; blk < nblk; ++blk) {
-        const int kb = blk * KV_BLOCK;
-        char *Ks = lds + (blk % NB) * 2 * KBYTES;
-        char *Vs = Ks + KBYTES;
-        if (blk + NB - 2 < nblk) BI_WAIT_VMCNT(QW * (NB - 2));   // this wavefront's loads of block blk landed
-        else BI_WAIT_VMCNT(0);
+    Rows16 r;
+    rows16_load<dt>(p, tile, b, gk, r);
+    // running fold over splits (per score row in lane r16; empty: mt = -inf, lt = 0) and the current
+    // split's state; the sink, if any, is the fold's first partial
+    bool have = false;
+    float mt = NEG_INF, lt = 0.0f;
+    if (p.sinks) {
+        const int rgc = min(tile * 16 + r16, R - 1);
+        mt = sink2(p, gk * p.G + rgc % p.G);
+        lt = 1.0f;
+        have = true;
+    }
+    float m_run = NEG_INF, l_run = 0.0f;
+    f32x4 o[8], ot[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        o[t] = zero4();
+        ot[t] = zero4();
+    }
+    // per-lane LDS addresses of the V reads (attn_vfrags16's row-0 address of tile t, half 0) in buffer 0;
+    // buffer 1 is KBYTES further
+    uint32_t va[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const int row0 = 4 * g + (r16 >> 2);
+        const int ch = 2 * t + ((r16 & 3) >> 1);
+        const uint32_t off = (uint32_t)(row0 * ROWB + ((ch ^ ((row0 & 7) << 1)) << 4) + 8 * (r16 & 1));
+        va[t] = (uint32_t)(uintptr_t)BI_LDS_PTR(vbufs) + off;
+    }
+    // scores of a block from its K block: each key tile's chain takes d chunks 0 .. 3 in order
+    auto scores = [&](const char *Ks, f32x4 (&st)[4]) {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+            u32x4 kf[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                kf[c] = *reinterpret_cast<const u32x4 *>(Ks + (16 * kt + r16) * ROWB + (((4 * c + g) ^ r16) << 4));
+            st[kt] = zero4();
+#pragma unroll
+            for (int c = 0; c < 4; ++c) st[kt] = Mfma<dt>::step(kf[c], r.qf[c], st[kt]);
+        }
+    };
+    // O += P . V over the two 32-key halves of V buffer VB
+    auto pv = [&](const u32x4 (&pf)[2], auto vb) {
+        constexpr int VB = decltype(vb)::value;
+        u32x4 vf[8];
+        vfrags_tr_asm<VB * KBYTES>(va, vf);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) o[t] = Mfma<dt>::step(pf[0], vf[t], o[t]);
+        vfrags_tr_asm<VB * KBYTES + 32 * ROWB>(va, vf);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) o[t] = Mfma<dt>::step(pf[1], vf[t], o[t]);
+    };
+
+    using VB0 = std::integral_constant<int, 0>;
+    using VB1 = std::integral_constant<int, 1>;
+    f32x4 st_cur[4], st_nxt[4];
+    // block j: its V block (and K of block j + 1) landed, published by the barrier; then K(j + 2) goes into
+    // the K buffer block j's scores were read from (in block j - 1) and V(j + 1) into the V buffer block
+    // j - 1 read; block j + 1's scores, block j's softmax and P . V
+    auto top = [&](int j, char *kfree, char *vnext, char *vcur) {
+        const int kb = j * KV_BLOCK;
+        BI_WAIT_VMCNT(0);
         if (kb + KV_BLOCK > p.S) {
             // V rows past S read as zero; each wavefront clears the rows its own loads filled
 #pragma unroll
-            for (int j = 0; j < QW; ++j) {
-                const int q = wave + W * j;
-                const int row = 4 * (q & 15) + lrow;
-                if (q >= 16 && kb + row >= p.S) *reinterpret_cast<u32x4 *>(Vs + row * ROWB + lslot * 16) = zero_u4();
+            for (int jj = 0; jj < QW; ++jj) {
+                const int row = 4 * (wave + W * jj) + lrow;
+                if (kb + row >= p.S) *reinterpret_cast<u32x4 *>(vcur + row * ROWB + lslot * 16) = zero_u4();
             }
             __builtin_amdgcn_s_waitcnt(0xc07f);
         }
-        __syncthreads();                                 // block blk visible to all; block blk - 1 no longer read
-        if (blk + NB - 1 < nblk) issue(blk + NB - 1);
-        attn_block16<dt>(p, r, Ks, Vs, kb, m_run, l_run, o, []() {}, []() {});
-        if ((blk + 1) % BPS == 0 || blk + 1 == nblk) fold_split();
+        __syncthreads();
+        if (j + 2 < nblk) issue(j + 2, kfree, false);
+        if (j + 1 < nblk) issue(j + 1, vnext, true);
+    };
+    auto fast_block = [&](int j, char *kfree, const char *knext, char *vnext, char *vcur, auto vb) {
+        top(j, kfree, vnext, vcur);
+        scores(knext, st_nxt);
+        u32x4 pf[2];
+        attn_softmax16<dt, 4, 8, true, true>(p, r, st_cur, j * KV_BLOCK, m_run, l_run, o, pf);
+        pv(pf, vb);
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) st_cur[kt] = st_nxt[kt];
+    };
+    auto general_block = [&](int j, char *kfree, const char *knext, char *vnext, char *vcur, auto vb) {
+        top(j, kfree, vnext, vcur);
+        if (j + 1 < nblk) scores(knext, st_nxt);
+        u32x4 pf[2];
+        attn_softmax16<dt>(p, r, st_cur, j * KV_BLOCK, m_run, l_run, o, pf);
+        pv(pf, vb);
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) st_cur[kt] = st_nxt[kt];
+        if ((j + 1) % BPS == 0 || j + 1 == nblk) fold_split16(m_run, l_run, o, have, mt, lt, ot);
+    };
+
+    if (nblk > 0) {
+        issue(0, kbuf0, false);
+        issue(0, vbuf0, true);
+        if (nblk > 1) issue(1, kbuf1, false);
+        BI_WAIT_VMCNT(0);
+        __syncthreads();
+        scores(kbuf0, st_cur);
+    }
+    // block j reads K(j + 1) from kbuf[(j + 1) % 2] and V(j) from vbuf[j % 2]
+    for (int sp = 0; sp < nfast; ++sp) {
+        const int j = sp * BPS;
+        fast_block(j, kbuf0, kbuf1, vbuf1, vbuf0, VB0{});
+        fast_block(j + 1, kbuf1, kbuf0, vbuf0, vbuf1, VB1{});
+        fast_block(j + 2, kbuf0, kbuf1, vbuf1, vbuf0, VB0{});
+        fast_block(j + 3, kbuf1, kbuf0, vbuf0, vbuf1, VB1{});
+        fold_split16_full(m_run, l_run, o, have, mt, lt, ot);
+    }
+    for (int j = nfast * BPS; j < nblk; j += 2) {
+        general_block(j, kbuf0, kbuf1, vbuf1, vbuf0, VB0{});
+        if (j + 1 < nblk) general_block(j + 1, kbuf1, kbuf0, vbuf0, vbuf1, VB1{});
     }
 
     // normalise, canonicalise -0, round once: O rows 4 g + i, columns 16 t + r16
@@ -1302,7 +1489,7 @@ __global__ __launch_bounds__(64 * W) void sdpa_prefill16(SdpaParams p) {
         for (int t = 0; t < 8; ++t) {
             float v = have_i ? ot[t][i] / l_i : 0.0f;
             v = v + 0.0f;                                // -0 -> +0
-            if (16 * t < p.dr) store_from_f32<dt>(orow, 16 * t + r16, v);
+            if (!PAD || 16 * t < p.dr) store_from_f32<dt>(orow, 16 * t + r16, v);
         }
     }
 }
@@ -1312,7 +1499,7 @@ __global__ __launch_bounds__(64 * W) void sdpa_prefill16(SdpaParams p) {
 // one half (NT = 8: two workgroups per row tile group, each computing the full scores and P and
 // applying P to its 128 columns of V; measured 1.3-1.5x slower, as the scores are computed twice).
 // Every output column is the same chain as in the split kernel (scores over all d chunks in order, P
-// rounded once, P . V over each block's keys).  Otherwise as sdpa_prefill16: W row tiles of one (batch,
+// rounded once, P . V over each block's keys).  Otherwise as the D = 128 prefill: W row tiles of one (batch,
 // KV head) walk the key blocks in ascending order with NB LDS buffers, restart (m, l, O) at every
 // 256-key split and fold the split partials in registers with the combine's operations.  A buffer holds
 // the K block with 512-byte rows (load q covers key rows 2 q and 2 q + 1, lane L row 2 q + L / 32, slot
@@ -1408,37 +1595,7 @@ __global__ __launch_bounds__(64 * W) void sdpa_prefill16w(SdpaParams p) {
         ot[t] = zero4();
         o[t] = zero4();
     }
-    auto fold_split = [&]() {                          // sdpa_combine's step, as in sdpa_prefill16
-        const bool skip = m_run == NEG_INF;
-        const bool first = !skip && !have;
-        const float m2 = fmaxf(mt, m_run);
-        const float a = exp2_hw(mt - m2);
-        const float bs = exp2_hw(m_run - m2);
-        if (first) {
-            mt = m_run;
-            lt = l_run;
-        } else if (!skip) {
-            lt = __builtin_fmaf(lt, a, l_run * bs);
-            mt = m2;
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int src = 4 * g + i;
-            const bool skip_i = __shfl((int)skip, src) != 0;
-            const bool first_i = __shfl((int)first, src) != 0;
-            const float a_i = __shfl(a, src), b_i = __shfl(bs, src);
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                const float f = __builtin_fmaf(ot[t][i], a_i, o[t][i] * b_i);
-                ot[t][i] = first_i ? o[t][i] : skip_i ? ot[t][i] : f;
-            }
-        }
-        have = have || !skip;
-        m_run = NEG_INF;
-        l_run = 0.0f;
-#pragma unroll
-        for (int t = 0; t < NT; ++t) o[t] = zero4();
-    };
+    auto fold_split = [&]() { fold_split16(m_run, l_run, o, have, mt, lt, ot); };
 
     for (int j = 0; j < NB - 1 && j < nblk; ++j) issue(j);
     for (int blk = 0; blk < nblk; ++blk) {
@@ -1613,10 +1770,11 @@ static hipError_t launch_typed(const SdpaParams &p, hipStream_t st) {
     const SdpaPath path = sdpa_path(p.B, p.Hq, p.Hkv, p.Lq, p.S, D, dt);
     if constexpr (dt != DT_F32 && D <= 128) {
         if (path == SDPA_PREFILL16) {
-            constexpr int W = 4;                         // row tiles per workgroup sharing each K / V block
+            constexpr int W = 4;                         // row tiles (one per wavefront) sharing each K / V block
             const int64_t nwg = (int64_t)(((R + 15) / 16 + W - 1) / W) * p.B * p.Hkv;
             if (nwg > INT32_MAX) return hipErrorInvalidConfiguration;
-            hipLaunchKernelGGL((sdpa_prefill16<dt, W, 2>), dim3((unsigned)nwg), dim3(64 * W), 0, st, p);
+            if (D == 128) hipLaunchKernelGGL((sdpa_prefill16p<dt, W, false>), dim3((unsigned)nwg), dim3(64 * W), 0, st, p);
+            else hipLaunchKernelGGL((sdpa_prefill16p<dt, W, true>), dim3((unsigned)nwg), dim3(64 * W), 0, st, p);
             return hipGetLastError();
         }
         if (path == SDPA_FUSED16) {

@@ -1,7 +1,9 @@
 """C-ABI checks that need no GPU: the library loads, exports every function
-include/bi.h declares, and rejects malformed or unsupported arguments on the
-host before touching the device (no compute call is made here)."""
+the headers under include/ declare, and rejects malformed or unsupported
+arguments on the host before touching the device (no compute call is made
+here)."""
 import ctypes
+import glob
 import os
 import re
 
@@ -10,7 +12,7 @@ import pytest
 from invariant_deterministic_gemm_amd import _native
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "bi.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 F32, F16, BF16 = _native.BI_F32, _native.BI_F16, _native.BI_BF16
 OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
@@ -28,9 +30,15 @@ def lib():
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(bi_[a-z_0-9]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(bi_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
+
+
+def test_headers_found():
+    assert any(h.endswith("bi.h") for h in HEADERS) and any(h.endswith("bi_measure.h") for h in HEADERS)
 
 
 def test_header_declares_what_the_binding_binds():
@@ -48,6 +56,17 @@ def test_exported_symbols_with_nm():
                          check=True).stdout
     exported = set(re.findall(r"\bT (bi_\w+)", out))
     assert set(declared_functions()) <= exported
+
+
+def test_measure_validation(lib):
+    # bad arguments are refused on the host, before any launch
+    assert lib.bi_measure_stream_read(None, 1024, P16, 4, None) == 1
+    assert lib.bi_measure_stream_read(P16, 1000, P16b, 4, None) == 1
+    assert lib.bi_measure_stream_read(P_MIS, 1024, P16b, 4, None) == 1
+    assert lib.bi_measure_stream_read(P16, 1024, P16b, 0, None) == 1
+    assert lib.bi_measure_mfma(None, 4, 10, None) < 0
+    assert lib.bi_measure_mfma(P16, 0, 10, None) < 0
+    assert lib.bi_measure_mfma(P16, 4, 0, None) < 0
 
 
 def test_abi_version_and_status_names(lib):

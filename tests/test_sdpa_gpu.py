@@ -407,6 +407,31 @@ def test_prefill_path_matches_split_path_and_decode(dt):
         assert_close_to_oracle(a[:1].cpu(), ref, f"S={S}: masked prefill vs oracle")
 
 
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16], ids=_ids)
+@pytest.mark.parametrize("B,Hq,Hkv,S", [(2, 16, 8, 1000), (1, 32, 8, 1337), (3, 8, 2, 777)])
+def test_every_prefill_token_matches_split_chunks(dt, B, Hq, Hkv, S):
+    """Every token of a causal prefill (query chunk = the whole cache, the prefill kernel) equals the same
+    token computed by the split + combine or one-launch kernels in chunks of at most 383 query rows
+    against the cache truncated after the chunk: ragged row-tile groups, caches that end inside a block,
+    GQA factors 2 and 4, batch neighbours."""
+    lib = bi._native.load()
+    BI = bi.BI_BF16 if dt == torch.bfloat16 else bi.BI_F16
+    q = synthetic.randn((B, Hq, S, 128), 0x5EED53 + S, 1.0, dt).to(DEV)
+    k = synthetic.randn((B, Hkv, S, 128), 0x5EED54 + S, 1.0, dt).to(DEV)
+    v = synthetic.randn((B, Hkv, S, 128), 0x5EED55 + S, 1.0, dt).to(DEV)
+    assert lib.bi_sdpa_kernel_name(B, Hq, Hkv, S, S, 128, BI).decode() == "sdpa_prefill16"
+    full = bi.bi_sdpa(q, k, v, causal=True)
+    a = 0
+    while a < S:
+        e = min(a + 383, S)
+        assert lib.bi_sdpa_kernel_name(B, Hq, Hkv, e - a, e, 128, BI).decode() != "sdpa_prefill16"
+        part = bi.bi_sdpa(q[:, :, a:e], k[:, :, :e], v[:, :, :e], causal=True)
+        assert_bits_equal(full[:, :, a:e], part, f"tokens {a}..{e - 1}")
+        a = e
+    ref = oracle.sdpa(q[:1, :, -64:].cpu(), k[:1].cpu(), v[:1].cpu(), causal=True)
+    assert_close_to_oracle(full[:1, :, -64:].cpu(), ref, "last 64 tokens vs oracle")
+
+
 def test_long_causal_prefill_needs_no_workspace():
     """A 4096-token causal prefill against its own 4096-key cache (the split path would need a
     multi-GB workspace): no workspace is requested, sampled rows match the oracle and equal a decode."""
