@@ -217,6 +217,35 @@ bi_status bi_sdpa_ex(const void *q, const int64_t q_str[4],
                      void *stream);
 
 /*
+ * bi_sdpa_ex for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.
+ * Arguments, results and bits as bi_sdpa_ex, without ws / ws_bytes: the
+ * split partials (the bytes bi_sdpa_workspace_bytes reports) go to a
+ * scratch array of bi_sdpa_scratch_limit() bytes (64 MiB) that the library
+ * holds on each GPU it runs on until the process ends; this call allocates
+ * and frees nothing.  Sizes needing more return BI_ERR_UNSUPPORTED before
+ * anything is enqueued.  Every call on a GPU uses that GPU's one array (the
+ * device current on the calling thread), so calls that overlap on one GPU
+ * (other streams, other threads) race and must not be made; the array's
+ * contents on entry do not matter and are left as the last call wrote them.
+ * The first call that needs the array on a device looks up its address
+ * there (hipGetSymbolAddress), so make that first call outside graph
+ * capture.
+ */
+bi_status bi_sdpa_ex_noalloc(const void *q, const int64_t q_str[4],
+                             const void *k, const int64_t k_str[4],
+                             const void *v, const int64_t v_str[4],
+                             void *o, const int64_t o_str[4],
+                             int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t S, int64_t D,
+                             float scale, int causal,
+                             int mask_kind, const void *mask, const int64_t mask_str[4],
+                             const float *sinks,
+                             bi_dtype dt,
+                             void *stream);
+/* Bytes of the per-GPU scratch array bi_sdpa_ex_noalloc uses (its size limit). */
+size_t bi_sdpa_scratch_limit(void);
+
+/*
  * Batch-VARIANT comparator, for measurement only.  It runs the same
  * fragment loads, MFMA instruction and epilogue as bi_linear but cuts K
  * into `splits` contiguous ranges whose fp32 partial sums are added in a

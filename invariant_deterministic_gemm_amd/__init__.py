@@ -12,6 +12,7 @@ Entry points (same names as the C ABI, plus the README's short names):
     bi_matmul(a, b)                         y = a b, b is (K, N)
     bi_addmm(c, a, b, alpha=1, beta=1)      y = alpha a b + beta c
     bi_sdpa(q, k, v, causal=False, mask=None, scale=None)
+    bi_sdpa_noalloc(q, k, v, ...)           bi_sdpa with no workspace allocation (per-GPU scratch)
     bi_rowsum(x, mean=False)                row sum / mean over the last dim
     bi_variant_linear(x, w, bias=None, splits=None)   batch-VARIANT comparator
 """
@@ -25,7 +26,7 @@ import torch
 from . import _native
 from ._native import BI_BF16, BI_F16, BI_F32
 
-__all__ = ["bi_linear", "bi_matmul", "bi_addmm", "bi_sdpa", "bi_rowsum", "bi_variant_linear",
+__all__ = ["bi_linear", "bi_matmul", "bi_addmm", "bi_sdpa", "bi_sdpa_noalloc", "bi_rowsum", "bi_variant_linear",
            "bi_quantized_linear", "quantize",
            "linear", "matmul", "addmm", "scaled_dot_product_attention",
            "abi_version", "library_path", "BiError"]
@@ -245,6 +246,19 @@ def bi_sdpa(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fa
     mask: boolean (True = attend) or additive in q's dtype (added to the scaled scores, -inf removes
     a key), broadcastable to (B, Hq, Lq, S).  sinks: None or Hq logits, one extra softmax term per
     query head that carries no value (bi.h, bi_sdpa_ex)."""
+    return _sdpa(q, k, v, causal, mask, scale, workspace, sinks, noalloc=False)
+
+
+def bi_sdpa_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+                    mask: torch.Tensor | None = None, scale: float | None = None,
+                    sinks: torch.Tensor | None = None) -> torch.Tensor:
+    """bi_sdpa through bi_sdpa_ex_noalloc: no workspace is allocated; the library's per-GPU scratch array
+    holds the split partials (bi.h: calls that overlap on one GPU race; sizes above
+    bi_sdpa_scratch_limit() raise NotImplementedError).  The output tensor is still allocated here."""
+    return _sdpa(q, k, v, causal, mask, scale, None, sinks, noalloc=True)
+
+
+def _sdpa(q, k, v, causal, mask, scale, workspace, sinks, noalloc):
     dev = _on_gpu(q, k, v, mask)
     if not (q.dtype == k.dtype == v.dtype):
         raise ValueError("q, k, v must share a dtype")
@@ -278,6 +292,13 @@ def bi_sdpa(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fa
             raise ValueError("sinks must hold one logit per query head")
         sk = torch.as_tensor(sinks).reshape(Hq).to(device=dev, dtype=torch.float32).contiguous()
     lib = _native.load()
+    if noalloc:
+        st = lib.bi_sdpa_ex_noalloc(_ptr(qs), _native.i64x4(qs.stride()), _ptr(ks), _native.i64x4(ks.stride()),
+                                    _ptr(vs), _native.i64x4(vs.stride()), _ptr(o), _native.i64x4(o.stride()),
+                                    B, Hq, Hkv, Lq, S, D, float(scale), 1 if causal else 0, kind, mptr, mstr,
+                                    _ptr(sk), _dt(q, "bi_sdpa"), _stream(dev))
+        _check(st, "bi_sdpa_ex_noalloc")
+        return o
     need = int(lib.bi_sdpa_workspace_bytes(B, Hq, Hkv, Lq, S, D, _dt(q, "bi_sdpa")))
     ws = workspace
     if need > 0 and (ws is None or ws.numel() * ws.element_size() < need):

@@ -30,6 +30,9 @@ SIGNATURES = {
     "bi_sdpa_ex": (_i, [_p, _i64p, _p, _i64p, _p, _i64p, _p, _i64p, _i64, _i64, _i64, _i64, _i64, _i64,
                         _f, _i, _i, _p, _i64p, _p, _i, _p, _sz, _p]),
     "bi_sdpa_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64, _i64, _i]),
+    "bi_sdpa_ex_noalloc": (_i, [_p, _i64p, _p, _i64p, _p, _i64p, _p, _i64p, _i64, _i64, _i64, _i64, _i64, _i64,
+                                _f, _i, _i, _p, _i64p, _p, _i, _p]),
+    "bi_sdpa_scratch_limit": (_sz, []),
     "bi_rowsum": (_i, [_p, _i64, _p, _i64, _i64, _i, _i, _p]),
     "bi_quantized_linear": (_i, [_p, _i64, _p, _i64, _p, _p, _i64, _i, _i64, _p, _p, _i64, _i64, _i64, _i64, _i,
                                  _p, _sz, _p]),

@@ -13,6 +13,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdint>
+#include <mutex>
 #include <string>
 
 #include "bi.h"
@@ -330,6 +331,58 @@ int bi_variant_splits(int64_t M) {
 size_t bi_variant_workspace_bytes(int64_t M, int64_t N, int splits) {
     if (splits <= 1 || M <= 0 || N <= 0) return 0;
     return (size_t)splits * (size_t)M * (size_t)N * 4;
+}
+
+// ---------------------------------------------------------------- attention without a caller workspace
+// For callers that cannot allocate device memory (code under graph capture, serving loops, harnesses that
+// forbid it): the split partials go to one file-scope device array per GPU, set up once per device the
+// first time the entry point needs it, with that device current.  Host code uses the address
+// hipGetSymbolAddress returns for the current device, never the array's name (a host-side stand-in).
+constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr int kScratchDevices = 64;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+static std::mutex g_scratch_mu;
+static void *g_scratch_ptr[kScratchDevices];
+
+static bi_status scratch_for_current_device(const char *fn, void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return device_status(e, fn);
+    if (dev < 0 || dev >= kScratchDevices)
+        return fail(BI_ERR_UNSUPPORTED, "%s: device %d beyond the %d the library keeps scratch for", fn, dev,
+                    kScratchDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return device_status(e, fn);
+        if (ptr == nullptr) return fail(BI_ERR_DEVICE, "%s: no device address for the scratch array", fn);
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return BI_OK;
+}
+
+size_t bi_sdpa_scratch_limit(void) { return kScratchBytes; }
+
+bi_status bi_sdpa_ex_noalloc(const void *q, const int64_t q_str[4], const void *k, const int64_t k_str[4],
+                             const void *v, const int64_t v_str[4], void *o, const int64_t o_str[4], int64_t B,
+                             int64_t Hq, int64_t Hkv, int64_t Lq, int64_t S, int64_t D, float scale, int causal,
+                             int mask_kind, const void *mask, const int64_t mask_str[4], const float *sinks,
+                             bi_dtype dt, void *stream) {
+    const char *fn = "bi_sdpa_ex_noalloc";
+    const size_t need = dtype_known(dt) ? bi::sdpa_workspace_bytes(B, Hq, Hkv, Lq, S, D, (int)dt) : 0;
+    if (need > kScratchBytes)
+        return fail(BI_ERR_UNSUPPORTED, "%s: these sizes need %zu bytes of partials, above the %zu-byte scratch "
+                    "limit of this entry point (use bi_sdpa_ex with a workspace)", fn, need, kScratchBytes);
+    void *ws = nullptr;
+    if (need > 0) {
+        const bi_status st = scratch_for_current_device(fn, &ws);
+        if (st != BI_OK) return st;
+    }
+    return sdpa_impl(fn, q, q_str, k, k_str, v, v_str, o, o_str, B, Hq, Hkv, Lq, S, D, scale, causal, mask_kind,
+                     mask, mask_str, sinks, dt, ws, ws ? kScratchBytes : 0, stream);
 }
 
 bi_status bi_variant_linear(const void *x, int64_t ldx, const void *w, int64_t ldw, const void *bias, void *y,

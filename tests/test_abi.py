@@ -58,6 +58,23 @@ def test_exported_symbols_with_nm():
     assert set(declared_functions()) <= exported
 
 
+def test_sdpa_noalloc_host_checks(lib):
+    # sizes whose partials exceed the scratch limit are refused on the host, before any device call
+    lim = lib.bi_sdpa_scratch_limit()
+    assert lim == 64 * 2 ** 20
+    st4 = (ctypes.c_int64 * 4)(32 * 1 * 128, 1 * 128, 128, 1)
+    kv4 = (ctypes.c_int64 * 4)(8 * 65536 * 128, 65536 * 128, 128, 1)
+    need = lib.bi_sdpa_workspace_bytes(64, 32, 8, 1, 65536, 128, BF16)
+    assert need > lim
+    s = lib.bi_sdpa_ex_noalloc(P16, st4, P16b, kv4, P16b, kv4, P16, st4, 64, 32, 8, 1, 65536, 128, 0.088, 1,
+                               0, None, None, None, BF16, None)
+    assert s == UNSUPPORTED and b"scratch" in lib.bi_last_error()
+    # malformed arguments that need no scratch are refused as by bi_sdpa_ex
+    s = lib.bi_sdpa_ex_noalloc(P16, st4, P16b, kv4, P16b, kv4, P16, st4, 1, 30, 8, 1, 64, 128, 0.088, 1,
+                               0, None, None, None, BF16, None)
+    assert s == INVALID
+
+
 def test_measure_validation(lib):
     # bad arguments are refused on the host, before any launch
     assert lib.bi_measure_stream_read(None, 1024, P16, 4, None) == 1
