@@ -688,10 +688,15 @@ def cell_quantized_gemm(ctx):
 
 
 def cell_comparator(ctx):
-    """The batch-variant comparator beside the invariant path on the bf16 linear workload (K = 4096,
-    N in {4096, 14336}, every M of the sweep): total time of each, their ratio, and the negative control
-    (rows of each M that differ from the same rows at M = 256: nonzero for the variant, 0 for bi_linear)."""
+    """The batch-variant comparators beside the invariant path (the cost of invariance and the negative
+    control).  GEMM: the bf16 linear workload (K = 4096, N in {4096, 14336}, every M of the sweep), where
+    bi_variant_linear runs the same kernel as bi_linear for each M with M-keyed split-K; rows of each M
+    that differ from the same rows at M = 256 (nonzero for the variant, 0 for bi_linear).  Attention:
+    bi_variant_sdpa (split length from G * q_len and S) against bi_sdpa on the q_len sweep at a 1024-key
+    cache and on decode at B = 8, S = 8192; elements of single-token decodes (Hq 16, Hkv 8) that change
+    when the cache grows from 4000 to 4200 keys with the new keys masked."""
     torch, bi, lib = ctx.torch, ctx.bi, ctx.lib
+    ns = min(ctx.samples, 50)
     inv_us = var_us = 0.0
     diff_var = diff_inv = 0
     per = []
@@ -704,9 +709,9 @@ def cell_comparator(ctx):
             x = dN["x"][:M]
             it1, it2 = iter(range(10 ** 9)), iter(range(10 ** 9))
             ti = _time_graph(torch, lambda: bi.bi_linear(x, ws[next(it1) % len(ws)], dN["b"]),
-                             reps=len(ws), samples=min(ctx.samples, 50), keep=False)
+                             reps=len(ws), samples=ns, keep=False)
             tv = _time_graph(torch, lambda: bi.bi_variant_linear(x, ws[next(it2) % len(ws)], dN["b"]),
-                             reps=len(ws), samples=min(ctx.samples, 50), keep=False)
+                             reps=len(ws), samples=ns, keep=False)
             inv_us += ti["us"]
             var_us += tv["us"]
             v = bi.bi_variant_linear(x, ws[0], dN["b"])
@@ -717,16 +722,58 @@ def cell_comparator(ctx):
             diff_inv += di
             per.append({"M": M, "N": N, "invariant_us": ti["us"], "variant_us": tv["us"],
                         "splits": int(lib.bi_variant_splits(M)),
-                        "invariant_kernel": lib.bi_gemm_kernel_name(M, N, 4096, bi.BI_BF16, 0).decode(),
+                        "kernel": lib.bi_gemm_kernel_name(M, N, 4096, bi.BI_BF16, 0).decode(),
                         "variant_rows_differing": dv})
-    return {"invariant_ms": round(inv_us / 1e3, 4), "variant_ms": round(var_us / 1e3, 4),
+    gemm = {"invariant_ms": round(inv_us / 1e3, 4), "variant_ms": round(var_us / 1e3, 4),
             "invariant_over_variant_time": round(inv_us / var_us, 4),
             "variant_rows_differing_from_M256": diff_var, "invariant_rows_differing_from_M256": diff_inv,
             "per_shape": per}
+    # attention: cost on the q_len sweep and on a decode batch
+    c3 = ctx.synthetic.cfg3_inputs(B=1, S=1024)
+    q3, k3, v3 = (c3[n].to(ctx.dev) for n in ("q", "k", "v"))
+    att = {"qlen_sweep": []}
+    tot_i = tot_v = 0.0
+    for L in ctx.synthetic.CFG3["Lq_values"]:
+        qq = q3[:, :, 1024 - L:]
+        ti = _time_graph(torch, lambda: bi.bi_sdpa(qq, k3, v3, causal=True), reps=10, samples=ns, keep=False)
+        tv = _time_graph(torch, lambda: bi.bi_variant_sdpa(qq, k3, v3, causal=True), reps=10, samples=ns, keep=False)
+        tot_i += ti["us"]
+        tot_v += tv["us"]
+        att["qlen_sweep"].append({"Lq": L, "invariant_us": ti["us"], "variant_us": tv["us"]})
+    att["qlen_sweep_invariant_over_variant_time"] = round(tot_i / tot_v, 4)
+    q, kv, _ = _decode_inputs(torch, ctx.dev, 8, 8192, 128, 0x5EED93)
+    wsd = torch.empty(max(1, bi.sdpa_workspace_bytes(8, 32, 8, 1, 8192, 128, torch.bfloat16)), dtype=torch.uint8,
+                      device=ctx.dev)
+    it1, it2 = iter(range(10 ** 9)), iter(range(10 ** 9))
+    ti = _time_graph(torch, lambda: bi.bi_sdpa(q, *kv[next(it1) % len(kv)], causal=True, workspace=wsd),
+                     reps=2 * len(kv), samples=ns, keep=False)
+    tv = _time_graph(torch, lambda: bi.bi_variant_sdpa(q, *kv[next(it2) % len(kv)], causal=True),
+                     reps=2 * len(kv), samples=ns, keep=False)
+    att["decode_B8_S8192"] = {"invariant_us": ti["us"], "variant_us": tv["us"],
+                              "invariant_over_variant_time": round(ti["us"] / tv["us"], 4)}
+    del q, kv, wsd
+    # negative control: context growth with the new keys masked (config 4 shapes)
+    c4 = ctx.synthetic.cfg4_inputs(torch.bfloat16)
+    q4, k4, v4 = (c4[n].to(ctx.dev) for n in ("q", "k", "v"))
+    dv = di = 0
+    for n0 in (4000, 4096):
+        base_v = bi.bi_variant_sdpa(q4, k4[:, :, :n0], v4[:, :, :n0])
+        base_i = bi.bi_sdpa(q4, k4[:, :, :n0], v4[:, :, :n0])
+        for n in range(n0 + 1, 4201, 25):
+            mask = torch.zeros(1, 1, 1, n, dtype=torch.bool, device=ctx.dev)
+            mask[..., :n0] = True
+            dv += int((bi.bi_variant_sdpa(q4, k4[:, :, :n], v4[:, :, :n], mask=mask).view(torch.int16)
+                       != base_v.view(torch.int16)).sum())
+            di += int((bi.bi_sdpa(q4, k4[:, :, :n], v4[:, :, :n], mask=mask).view(torch.int16)
+                       != base_i.view(torch.int16)).sum())
+    att["context_growth_elements_differing"] = {"variant": dv, "invariant": di}
+    return {"gemm": gemm, "attention": att}
 
 
 def cell_e2e(ctx):
-    return {"decode": e2e_decode(ctx.torch, ctx.bi, ctx.dev, ctx.synthetic)}
+    """The random-weight decoder end to end: decode steps and a 256-token prefill, each under
+    batch_invariant_mode, under the batch-variant comparator kernels and with stock PyTorch."""
+    return e2e_run(ctx.torch, ctx.bi, ctx.dev, ctx.synthetic)
 
 
 CELLS = {
@@ -751,21 +798,48 @@ def measure_cells(ctx, names=None):
     return cells
 
 
-def e2e_decode(torch, bi, dev, synthetic):
-    """A random-weight 4-layer decoder (hidden 2048, 16 / 4 heads of 128, SwiGLU 5632, vocab 32000),
-    batch 8, 128-token prompts, 32 greedy decode steps: time per decode step under
-    batch_invariant_mode and with stock PyTorch (the batch-variant comparator), and how many of the
-    32000 last-position logits of one sequence move between batch 1 and batch 8 in each."""
+def _variant_mode(torch, bi):
+    """F.linear and F.scaled_dot_product_attention on the batch-variant comparator kernels
+    (bi_variant_linear with its M-keyed split-K, bi_variant_sdpa with its shape-keyed splits); every
+    other op runs stock.  The end-to-end analogue of the kernels' comparator."""
+    import torch.nn.functional as F
+    from torch.overrides import TorchFunctionMode
+
+    class VariantMode(TorchFunctionMode):
+        def __torch_function__(self, func, types, args=(), kwargs=None):
+            kwargs = kwargs or {}
+            if func is F.linear:
+                x, w = args[0], args[1]
+                b = args[2] if len(args) > 2 else kwargs.get("bias")
+                return bi.bi_variant_linear(x, w, b)
+            if func is F.scaled_dot_product_attention:
+                q, k, v = args[:3]
+                causal = kwargs.get("is_causal", False)
+                assert not causal or q.shape[2] == k.shape[2]
+                return bi.bi_variant_sdpa(q, k, v, causal=causal, scale=kwargs.get("scale"))
+            return func(*args, **kwargs)
+
+    return VariantMode()
+
+
+def e2e_run(torch, bi, dev, synthetic):
+    """A random-weight 4-layer decoder (hidden 2048, 16 / 4 heads of 128, SwiGLU 5632, vocab 32000):
+    batch 8 with 128-token prompts and 32 greedy decode steps (time per decode step), and a prefill of
+    8 x 256 tokens (time per prefill), each under batch_invariant_mode, under the batch-variant comparator
+    kernels and with stock PyTorch; how many of the 32000 last-position logits of one sequence move
+    between batch 1 and batch 8 in each."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     import tiny_transformer as tt
     cfg = tt.TinyConfig(layers=4)
     W = tt.make_weights(cfg, 0x5EEDE5, dev)
     prompts = synthetic.randint((8, 128), 0x5EEDE6, 0, cfg.vocab, torch.int64).to(dev)
+    long_prompts = synthetic.randint((8, 256), 0x5EEDE7, 0, cfg.vocab, torch.int64).to(dev)
     steps = 32
+    modes = {"invariant": lambda: bi.batch_invariant_mode(), "variant": lambda: _variant_mode(torch, bi),
+             "stock": lambda: _nullcontext()}
 
-    def run(invariant: bool, p):
-        ctx = bi.batch_invariant_mode() if invariant else _nullcontext()
-        with torch.no_grad(), ctx:
+    def decode(name, p):
+        with torch.no_grad(), modes[name]():
             logits, cache = tt.forward(cfg, W, p, None, 0)
             tok = logits[:, -1].float().argmax(-1, keepdim=True)
             torch.cuda.synchronize()
@@ -780,19 +854,38 @@ def e2e_decode(torch, bi, dev, synthetic):
             b.synchronize()
             return a.elapsed_time(b) / steps, logits[:, -1]
 
-    for inv in (True, False):               # warm-up both paths
-        run(inv, prompts)
+    def prefill(name, p, reps=5):
+        with torch.no_grad(), modes[name]():
+            tt.forward(cfg, W, p, None, 0)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(reps):
+                logits, _ = tt.forward(cfg, W, p, None, 0)
+            b.record()
+            b.synchronize()
+            return a.elapsed_time(b) / reps, logits[:, -1]
+
+    for name in modes:                      # warm-up every path
+        decode(name, prompts)
     out = {"model": "4 layers, hidden 2048, 16/4 heads x 128, SwiGLU 5632, vocab 32000, bf16, random weights",
-           "batch": 8, "prompt": 128, "decode_steps": steps}
-    for name, inv in (("invariant", True), ("stock", False)):
-        ms, last8 = run(inv, prompts)
-        _, last1 = run(inv, prompts[:1])
-        # decode logits of sequence 0 after 32 steps, alone vs in the batch of 8
+           "decode": {"batch": 8, "prompt": 128, "decode_steps": steps},
+           "prefill": {"batch": 8, "tokens": 256}}
+    for name in modes:
+        ms, last8 = decode(name, prompts)
+        _, last1 = decode(name, prompts[:1])
         n = int((last1[0].view(torch.int16) != last8[0].view(torch.int16)).sum())
-        out[name] = {"ms_per_decode_step": round(ms, 3), "tokens_per_s": round(8 * 1e3 / ms, 1),
-                     "logits_differing_batch1_vs_batch8": n}
-    out["invariant_over_stock_time"] = round(out["invariant"]["ms_per_decode_step"] /
-                                             out["stock"]["ms_per_decode_step"], 4)
+        out["decode"][name] = {"ms_per_decode_step": round(ms, 3), "tokens_per_s": round(8 * 1e3 / ms, 1),
+                               "logits_differing_batch1_vs_batch8": n}
+        ms, l8 = prefill(name, long_prompts)
+        _, l1 = prefill(name, long_prompts[:1], reps=1)
+        n = int((l1[0].view(torch.int16) != l8[0].view(torch.int16)).sum())
+        out["prefill"][name] = {"ms_per_prefill": round(ms, 3), "tokens_per_s": round(8 * 256 * 1e3 / ms, 1),
+                                "logits_differing_batch1_vs_batch8": n}
+    for ph, key in (("decode", "ms_per_decode_step"), ("prefill", "ms_per_prefill")):
+        inv = out[ph]["invariant"][key]
+        out[ph]["invariant_over_stock_time"] = round(inv / out[ph]["stock"][key], 4)
+        out[ph]["invariant_over_variant_time"] = round(inv / out[ph]["variant"][key], 4)
     return out
 
 

@@ -247,13 +247,16 @@ size_t bi_sdpa_scratch_limit(void);
 
 /*
  * Batch-VARIANT comparator, for measurement only.  It runs the same
- * fragment loads, MFMA instruction and epilogue as bi_linear but cuts K
- * into `splits` contiguous ranges whose fp32 partial sums are added in a
- * second pass -- the M-dependent split-K tuning that the README (section
- * "Why MLX is not invariant", matmul paragraph) identifies as the source of
- * batch variance.  Its results are NOT batch-invariant by design.
- * splits must be in 1..16; K is cut into that many ranges of whole k-groups,
- * as even as possible.  ws must hold bi_variant_workspace_bytes(M, N, splits)
+ * kernels bi_linear picks for this M (the strip, pipelined and ring tile
+ * kernels, or the generic ones where bi_linear uses those), with the same
+ * fragment loads, MFMA instruction and epilogue, but cuts K into `splits`
+ * contiguous ranges (a grid dimension) whose fp32 partial sums are added in
+ * ascending order in a second pass -- the M-dependent split-K tuning that the
+ * README (section "Why MLX is not invariant", matmul paragraph) identifies
+ * as the source of batch variance.  Its results are NOT batch-invariant by
+ * design.  splits must be in 1..16; K is cut into that many ranges of whole
+ * LDS stages (128 k in the strip kernel, 64 or 128 k in the tile kernels) or
+ * k-groups (generic kernels), as even as possible.  ws must hold bi_variant_workspace_bytes(M, N, splits)
  * bytes (256-byte aligned device memory); same dtype / alignment rules as
  * bi_linear.
  * bi_variant_splits(M) is the M-keyed policy: 8 for M <= 16, 4 for M <= 64,
@@ -269,6 +272,33 @@ bi_status bi_variant_linear(const void *x, int64_t ldx,
                             void *stream);
 size_t bi_variant_workspace_bytes(int64_t M, int64_t N, int splits);
 int bi_variant_splits(int64_t M);
+
+/*
+ * Batch-VARIANT attention comparator, for measurement only (README, section
+ * "Why MLX is not invariant", attention: the split-KV count follows the GQA
+ * factor times the query count, and growing the cache past 4096 keys switches
+ * from one pass to two).  Arguments as bi_sdpa.  The generic split kernel and
+ * the combine run with a split length taken from the call's shape,
+ * bi_variant_sdpa_split_len(G = Hq / Hkv, Lq, S): the whole cache (rounded up
+ * to 64 keys) as one split up to S = 4096, above that ceil(S / n) rounded up
+ * to 64 keys with n = 64 splits when G * Lq >= 4, else 32.  A token's bits
+ * therefore move with the query count and the cache length, while every
+ * result stays within the oracle tolerance.  ws must hold
+ * bi_variant_sdpa_workspace_bytes(B, Hq, Hkv, Lq, S, D) bytes, 256-byte
+ * aligned.
+ */
+bi_status bi_variant_sdpa(const void *q, const int64_t q_str[4],
+                          const void *k, const int64_t k_str[4],
+                          const void *v, const int64_t v_str[4],
+                          void *o, const int64_t o_str[4],
+                          int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t S, int64_t D,
+                          float scale, int causal,
+                          const uint8_t *mask, const int64_t mask_str[4],
+                          bi_dtype dt,
+                          void *ws, size_t ws_bytes,
+                          void *stream);
+size_t bi_variant_sdpa_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t S, int64_t D);
+int64_t bi_variant_sdpa_split_len(int64_t G, int64_t Lq, int64_t S);
 
 /*
  * Row sum / row mean over the last dimension (README, section "Why MLX is not

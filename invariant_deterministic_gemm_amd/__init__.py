@@ -15,6 +15,7 @@ Entry points (same names as the C ABI, plus the README's short names):
     bi_sdpa_noalloc(q, k, v, ...)           bi_sdpa with no workspace allocation (per-GPU scratch)
     bi_rowsum(x, mean=False)                row sum / mean over the last dim
     bi_variant_linear(x, w, bias=None, splits=None)   batch-VARIANT comparator
+    bi_variant_sdpa(q, k, v, causal=False, mask=None)  batch-VARIANT attention comparator
 """
 from __future__ import annotations
 
@@ -27,7 +28,7 @@ from . import _native
 from ._native import BI_BF16, BI_F16, BI_F32
 
 __all__ = ["bi_linear", "bi_matmul", "bi_addmm", "bi_sdpa", "bi_sdpa_noalloc", "bi_rowsum", "bi_variant_linear",
-           "bi_quantized_linear", "quantize",
+           "bi_variant_sdpa", "bi_quantized_linear", "quantize",
            "linear", "matmul", "addmm", "scaled_dot_product_attention",
            "abi_version", "library_path", "BiError"]
 
@@ -348,6 +349,36 @@ def bi_variant_linear(x: torch.Tensor, w: torch.Tensor, bias: torch.Tensor | Non
                                int(splits), _ptr(ws), need, _stream(dev))
     _check(st, "bi_variant_linear")
     return y.reshape(*x.shape[:-1], N)
+
+
+def bi_variant_sdpa(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+                    mask: torch.Tensor | None = None, scale: float | None = None) -> torch.Tensor:
+    """Batch-VARIANT attention comparator (bi.h, bi_variant_sdpa): the split length follows the GQA factor
+    times the query count and the cache length, so bits move with them.  Measurement only."""
+    dev = _on_gpu(q, k, v, mask)
+    B, Hq, Lq, D = q.shape
+    _, Hkv, S, _ = k.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    qs = q if q.stride(-1) == 1 else q.contiguous()
+    ks = k if k.stride(-1) == 1 else k.contiguous()
+    vs = v if v.stride(-1) == 1 else v.contiguous()
+    o = torch.empty((B, Hq, Lq, D), dtype=q.dtype, device=dev)
+    mptr, mstr = None, None
+    if mask is not None:
+        if mask.dtype not in (torch.bool, torch.uint8):
+            raise ValueError("bi_variant_sdpa takes a boolean mask")
+        m8, st = _mask_strides(mask.to(torch.uint8) if mask.dtype == torch.bool else mask, (B, Hq, Lq, S))
+        mptr, mstr = _ptr(m8), _native.i64x4(st)
+    lib = _native.load()
+    need = int(lib.bi_variant_sdpa_workspace_bytes(B, Hq, Hkv, Lq, S, D))
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = lib.bi_variant_sdpa(_ptr(qs), _native.i64x4(qs.stride()), _ptr(ks), _native.i64x4(ks.stride()),
+                             _ptr(vs), _native.i64x4(vs.stride()), _ptr(o), _native.i64x4(o.stride()),
+                             B, Hq, Hkv, Lq, S, D, float(scale), 1 if causal else 0, mptr, mstr,
+                             _dt(q, "bi_variant_sdpa"), _ptr(ws), need, _stream(dev))
+    _check(st, "bi_variant_sdpa")
+    return o
 
 
 # README, section "Use": the short names.

@@ -40,6 +40,10 @@ SIGNATURES = {
     "bi_variant_linear": (_i, [_p, _i64, _p, _i64, _p, _p, _i64, _i64, _i64, _i64, _i, _i, _i, _p, _sz, _p]),
     "bi_variant_workspace_bytes": (_sz, [_i64, _i64, _i]),
     "bi_variant_splits": (_i, [_i64]),
+    "bi_variant_sdpa": (_i, [_p, _i64p, _p, _i64p, _p, _i64p, _p, _i64p, _i64, _i64, _i64, _i64, _i64, _i64,
+                             _f, _i, _p, _i64p, _i, _p, _sz, _p]),
+    "bi_variant_sdpa_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64, _i64]),
+    "bi_variant_sdpa_split_len": (_i64, [_i64, _i64, _i64]),
     "bi_gemm_kernel_name": (ctypes.c_char_p, [_i64, _i64, _i64, _i, _i]),
     "bi_sdpa_kernel_name": (ctypes.c_char_p, [_i64, _i64, _i64, _i64, _i64, _i64, _i]),
     "bi_status_name": (ctypes.c_char_p, [_i]),

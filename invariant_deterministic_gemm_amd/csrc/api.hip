@@ -215,7 +215,7 @@ static bi_status sdpa_impl(const char *fn, const void *q, const int64_t q_str[4]
                            const int64_t o_str[4], int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t S,
                            int64_t D, float scale, int causal, int mask_kind, const void *mask,
                            const int64_t mask_str[4], const float *sinks, bi_dtype dt, void *ws, size_t ws_bytes,
-                           void *stream) {
+                           void *stream, bool variant = false) {
     if (!dtype_known(dt)) return fail(BI_ERR_INVALID, "%s: unknown dtype code %d", fn, (int)dt);
     if (mask_kind != BI_MASK_NONE && mask_kind != BI_MASK_BOOL && mask_kind != BI_MASK_ADD)
         return fail(BI_ERR_INVALID, "%s: unknown mask kind %d", fn, mask_kind);
@@ -263,7 +263,8 @@ static bi_status sdpa_impl(const char *fn, const void *q, const int64_t q_str[4]
             return fail(BI_ERR_UNSUPPORTED, "%s: additive mask misaligned for its dtype", fn);
     }
     if (sinks != nullptr && !aligned_to(sinks, 4)) return fail(BI_ERR_UNSUPPORTED, "%s: sinks misaligned", fn);
-    const size_t need = bi::sdpa_workspace_bytes(B, Hq, Hkv, Lq, S, D, (int)dt);
+    const size_t need = variant ? bi::sdpa_variant_workspace_bytes(B, Hq, Hkv, Lq, S, D)
+                                : bi::sdpa_workspace_bytes(B, Hq, Hkv, Lq, S, D, (int)dt);
     if (need > 0 && (ws == nullptr || ws_bytes < need))
         return fail(BI_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
                     ws == nullptr ? (size_t)0 : ws_bytes);
@@ -299,8 +300,10 @@ static bi_status sdpa_impl(const char *fn, const void *q, const int64_t q_str[4]
     p.causal = causal ? 1 : 0;
     p.dr = (int)D;
     p.c = (float)((double)scale * 1.4426950408889634);   // log2(e), rounded once to fp32
-    p.nsplit = (int)((S + bi::KV_SPLIT - 1) / bi::KV_SPLIT);
+    p.split_len = variant ? (int)bi::sdpa_variant_split_len(G, Lq, S) : bi::KV_SPLIT;
+    p.nsplit = (int)((S + p.split_len - 1) / p.split_len);
     if (need > 0) bi::sdpa_bind_workspace(p, ws);
+    if (variant) return device_status(bi::launch_sdpa_variant(p, dt, (int)D, (hipStream_t)stream), fn);
     return device_status(bi::launch_sdpa(p, dt, (int)D, (hipStream_t)stream), fn);
 }
 
@@ -332,6 +335,22 @@ size_t bi_variant_workspace_bytes(int64_t M, int64_t N, int splits) {
     if (splits <= 1 || M <= 0 || N <= 0) return 0;
     return (size_t)splits * (size_t)M * (size_t)N * 4;
 }
+
+bi_status bi_variant_sdpa(const void *q, const int64_t q_str[4], const void *k, const int64_t k_str[4],
+                          const void *v, const int64_t v_str[4], void *o, const int64_t o_str[4], int64_t B,
+                          int64_t Hq, int64_t Hkv, int64_t Lq, int64_t S, int64_t D, float scale, int causal,
+                          const uint8_t *mask, const int64_t mask_str[4], bi_dtype dt, void *ws, size_t ws_bytes,
+                          void *stream) {
+    return sdpa_impl("bi_variant_sdpa", q, q_str, k, k_str, v, v_str, o, o_str, B, Hq, Hkv, Lq, S, D, scale,
+                     causal, mask ? BI_MASK_BOOL : BI_MASK_NONE, mask, mask_str, nullptr, dt, ws, ws_bytes, stream,
+                     true);
+}
+
+size_t bi_variant_sdpa_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t S, int64_t D) {
+    return bi::sdpa_variant_workspace_bytes(B, Hq, Hkv, Lq, S, D);
+}
+
+int64_t bi_variant_sdpa_split_len(int64_t G, int64_t Lq, int64_t S) { return bi::sdpa_variant_split_len(G, Lq, S); }
 
 // ---------------------------------------------------------------- attention without a caller workspace
 // For callers that cannot allocate device memory (code under graph capture, serving loops, harnesses that

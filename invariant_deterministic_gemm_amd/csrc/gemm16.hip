@@ -14,8 +14,11 @@
 //   gemm16_pipe   M above the strip range up to the thousands: the same
 //                 loads with fragments read several steps ahead and one
 //                 barrier per stage.
-// Everything else (row-major (K, N) weights, other K, the split-K comparator)
-// runs the generic kernels of gemm.hip, which implement the same chain.
+// Everything else (row-major (K, N) weights, other K) runs the generic
+// kernels of gemm.hip, which implement the same chain.  The batch-variant
+// split-K comparator runs these same kernels with the stage loop cut into
+// ranges (grid dimension y) whose raw sums go to a workspace; with one split
+// (the invariant path) every workgroup runs the whole chain.
 #include <cstdio>
 
 #include "gemm16.h"
@@ -54,7 +57,9 @@ __global__ __launch_bounds__(64 * (1 + NL)) void gemm16_strip(GemmParams p) {
     const int lane = tid & 63, wave = tid >> 6;
     const int n0 = blockIdx.x * SW;
     const int nchunk = p.K >> 3;                 // 16-byte chunks per row
-    const int nstages = (p.K + 127) >> 7;
+    int sbase, send;                             // this split's stages (all of them without split-K)
+    split_stages(p, (p.K + 127) >> 7, sbase, send);
+    const int nstages = send - sbase;
     const int total_steps = p.total_steps;
     const bool consumer = wave == 0;
     const int lw = consumer ? 0 : wave - 1;      // loader index
@@ -79,7 +84,7 @@ __global__ __launch_bounds__(64 * (1 + NL)) void gemm16_strip(GemmParams p) {
         for (int j = 0; j < QHI; ++j) {
             if (j < myq) {
                 const int q = lw + NL * j;
-                const int gc = min(stage * 16 + cl[j], nchunk - 1);
+                const int gc = min((sbase + stage) * 16 + cl[j], nchunk - 1);
                 __builtin_amdgcn_global_load_lds(static_cast<const void *>(src[j] + (int64_t)gc * 16),
                                                  BI_LDS_PTR(buf + q * 1024), 16, 0, 0);
             }
@@ -140,8 +145,8 @@ __global__ __launch_bounds__(64 * (1 + NL)) void gemm16_strip(GemmParams p) {
     auto mma_last = [&](int stage, const u32x4 (&a)[4][FM], const u32x4 (&b)[4][NB]) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            if (stage * 4 + u < total_steps) {
-                const bool past = stage * 16 + 4 * u + g >= nchunk;
+            if ((sbase + stage) * 4 + u < total_steps) {
+                const bool past = (sbase + stage) * 16 + 4 * u + g >= nchunk;
 #pragma unroll
                 for (int j = 0; j < NB; ++j)
 #pragma unroll
@@ -219,7 +224,7 @@ __global__ __launch_bounds__(64 * (1 + NL)) void gemm16_strip(GemmParams p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int m = 16 * f + 4 * g + i;
-                if (m < p.M) epilogue<odt>(p, m, n, acc[j][f][i]);
+                if (m < p.M) finish<odt>(p, blockIdx.y, m, n, acc[j][f][i]);
             }
     }
 }
@@ -261,7 +266,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm16_ring(GemmParams p) {
     int tm, tn;
     tile_coords(blockIdx.x, ntm, ntn, 8, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
-    const int nstages = p.K / 64;
+    int sbase, send;                                 // this split's stages (all of them without split-K)
+    split_stages(p, p.K / 64, sbase, send);
+    const int nstages = send - sbase;
 
     const char *src[QW];
 #pragma unroll
@@ -275,7 +282,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm16_ring(GemmParams p) {
             src[j] = static_cast<const char *>(p.B) + (int64_t)min(n0 + rloc, p.N - 1) * p.ldb * 2 + c * 16;
     }
     auto issue = [&](int stage) {
-        const int64_t koff = (int64_t)stage * ROWB;
+        const int64_t koff = (int64_t)(sbase + stage) * ROWB;
         char *buf = lds + (stage % NS) * STAGE;
 #pragma unroll
         for (int j = 0; j < QW; ++j) {
@@ -346,21 +353,23 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm16_ring(GemmParams p) {
         mma(a1, b1);
     }
     if constexpr (BM * BN * Elem<odt>::bytes <= NS * STAGE) {
-        store_tile16<odt, BM, BN, WGM, WGN>(p, acc, m0, n0, lds);     // the ring's LDS holds the whole tile
-    } else {
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int n = n0 + wn * WN + 16 * j + r16;
-                if (n >= p.N) continue;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int m = m0 + wm * WM + 16 * i + 4 * g + e;
-                    if (m < p.M) epilogue<odt>(p, m, n, acc[i][j][e]);
-                }
-            }
+        if (p.splits == 1) {
+            store_tile16<odt, BM, BN, WGM, WGN>(p, acc, m0, n0, lds);     // the ring's LDS holds the whole tile
+            return;
+        }
     }
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int n = n0 + wn * WN + 16 * j + r16;
+            if (n >= p.N) continue;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int m = m0 + wm * WM + 16 * i + 4 * g + e;
+                if (m < p.M) finish<odt>(p, blockIdx.y, m, n, acc[i][j][e]);
+            }
+        }
 }
 
 // ============================================================ pipelined ring kernel
@@ -412,7 +421,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm16_pipe(GemmParams p) {
     int tm, tn;
     tile_coords(blockIdx.x, ntm, ntn, 8, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
-    const int nstages = p.K / KS;
+    int sbase, send;                                 // this split's stages (all of them without split-K)
+    split_stages(p, p.K / KS, sbase, send);
+    const int nstages = send - sbase;
     const int nsteps = nstages * SPS;
 
     // load side: instruction q covers stage rows RPI q .. RPI q + RPI - 1; lane L row RPI q + L / CPR,
@@ -429,7 +440,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm16_pipe(GemmParams p) {
             src[j] = static_cast<const char *>(p.B) + (int64_t)min(n0 + rloc - BM, p.N - 1) * p.ldb * 2 + c * 16;
     }
     auto issue = [&](int stage) {
-        const int64_t koff = (int64_t)stage * ROWB;
+        const int64_t koff = (int64_t)(sbase + stage) * ROWB;
         char *buf = lds + (stage % NS) * STAGE;
 #pragma unroll
         for (int j = 0; j < QW; ++j) {
@@ -498,21 +509,23 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm16_pipe(GemmParams p) {
         }
     }
     if constexpr (BM * BN * Elem<odt>::bytes <= NS * STAGE) {
-        store_tile16<odt, BM, BN, WGM, WGN>(p, acc, m0, n0, lds);
-    } else {
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int n = n0 + wn * WN + 16 * j + r16;
-                if (n >= p.N) continue;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int m = m0 + wm * WM + 16 * i + 4 * g + e;
-                    if (m < p.M) epilogue<odt>(p, m, n, acc[i][j][e]);
-                }
-            }
+        if (p.splits == 1) {
+            store_tile16<odt, BM, BN, WGM, WGN>(p, acc, m0, n0, lds);
+            return;
+        }
     }
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int n = n0 + wn * WN + 16 * j + r16;
+            if (n >= p.N) continue;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int m = m0 + wm * WM + 16 * i + 4 * g + e;
+                if (m < p.M) finish<odt>(p, blockIdx.y, m, n, acc[i][j][e]);
+            }
+        }
 }
 
 // ============================================================ plan + launch
@@ -566,7 +579,8 @@ static TileCfg tile_cfg(int M, int N, int K) {
 
 bool gemm16_applies(int M, int N, int K, bool b_kn, int splits) {
     (void)N;
-    if (b_kn || splits != 1) return false;
+    (void)splits;                                // split-K ranges run on the same kernels
+    if (b_kn) return false;
     return M <= 64 || K % 64 == 0;
 }
 
@@ -574,7 +588,7 @@ template <int idt, int odt>
 static hipError_t launch16_typed(const GemmParams &p, hipStream_t st) {
     if (use_strip(p.M, p.N, p.K)) {
         const StripCfg c = strip_cfg(p.M, p.N);
-        const dim3 grid((p.N + 16 * c.nb - 1) / (16 * c.nb)), block(64 * (1 + c.nl));
+        const dim3 grid((p.N + 16 * c.nb - 1) / (16 * c.nb), p.splits), block(64 * (1 + c.nl));
         if (c.ar == 4) hipLaunchKernelGGL((gemm16_strip<idt, odt, 1, 1, 4, 6, 3>), grid, block, 0, st, p);
         else if (c.ar == 16) hipLaunchKernelGGL((gemm16_strip<idt, odt, 1, 1, 16, 6, 3>), grid, block, 0, st, p);
         else if (c.ar == 32 && c.nb == 1) hipLaunchKernelGGL((gemm16_strip<idt, odt, 1, 2, 32, 4, 3>), grid, block, 0, st, p);
@@ -584,31 +598,31 @@ static hipError_t launch16_typed(const GemmParams &p, hipStream_t st) {
         return hipGetLastError();
     }
     const TileCfg c = tile_cfg(p.M, p.N, p.K);
-    const unsigned tiles = (unsigned)(((p.M + c.bm - 1) / c.bm) * ((p.N + c.bn - 1) / c.bn));
+    const dim3 tiles((unsigned)(((p.M + c.bm - 1) / c.bm) * ((p.N + c.bn - 1) / c.bn)), p.splits);
     switch (c.kind) {
         case RING256x256:
-            hipLaunchKernelGGL((gemm16_ring<idt, odt, 256, 256, 2, 4, 2>), dim3(tiles), dim3(512), 0, st, p);
+            hipLaunchKernelGGL((gemm16_ring<idt, odt, 256, 256, 2, 4, 2>), tiles, dim3(512), 0, st, p);
             break;
         case RING256x128:
-            hipLaunchKernelGGL((gemm16_ring<idt, odt, 256, 128, 4, 2, 3>), dim3(tiles), dim3(512), 0, st, p);
+            hipLaunchKernelGGL((gemm16_ring<idt, odt, 256, 128, 4, 2, 3>), tiles, dim3(512), 0, st, p);
             break;
         case PIPE128x128:
-            hipLaunchKernelGGL((gemm16_pipe<idt, odt, 128, 128, 2, 4, 4, 64, 2>), dim3(tiles), dim3(512), 0, st, p);
+            hipLaunchKernelGGL((gemm16_pipe<idt, odt, 128, 128, 2, 4, 4, 64, 2>), tiles, dim3(512), 0, st, p);
             break;
         case PIPE128x64:
-            hipLaunchKernelGGL((gemm16_pipe<idt, odt, 128, 64, 4, 2, 6, 64, 2>), dim3(tiles), dim3(512), 0, st, p);
+            hipLaunchKernelGGL((gemm16_pipe<idt, odt, 128, 64, 4, 2, 6, 64, 2>), tiles, dim3(512), 0, st, p);
             break;
         case PIPE64x64:
-            hipLaunchKernelGGL((gemm16_pipe<idt, odt, 64, 64, 2, 4, 4, 128, 2>), dim3(tiles), dim3(512), 0, st, p);
+            hipLaunchKernelGGL((gemm16_pipe<idt, odt, 64, 64, 2, 4, 4, 128, 2>), tiles, dim3(512), 0, st, p);
             break;
         case PIPE32x64:
-            hipLaunchKernelGGL((gemm16_pipe<idt, odt, 32, 64, 2, 4, 5, 128, 2>), dim3(tiles), dim3(512), 0, st, p);
+            hipLaunchKernelGGL((gemm16_pipe<idt, odt, 32, 64, 2, 4, 5, 128, 2>), tiles, dim3(512), 0, st, p);
             break;
         case RING128x64:
-            hipLaunchKernelGGL((gemm16_ring<idt, odt, 128, 64, 2, 2, 4>), dim3(tiles), dim3(256), 0, st, p);
+            hipLaunchKernelGGL((gemm16_ring<idt, odt, 128, 64, 2, 2, 4>), tiles, dim3(256), 0, st, p);
             break;
         case RING64x64:
-            hipLaunchKernelGGL((gemm16_ring<idt, odt, 64, 64, 2, 2, 4>), dim3(tiles), dim3(256), 0, st, p);
+            hipLaunchKernelGGL((gemm16_ring<idt, odt, 64, 64, 2, 2, 4>), tiles, dim3(256), 0, st, p);
             break;
     }
     return hipGetLastError();

@@ -52,6 +52,14 @@ __device__ __forceinline__ void split_range(const GemmParams &p, int split, int 
     se = (int)((int64_t)p.total_steps * (split + 1) / p.splits);
 }
 
+// Stages [s0, s1) of nst covered by this workgroup's split (blockIdx.y of splits; all of them when
+// splits == 1).  Comparator only: the invariant path always runs one split.
+__device__ __forceinline__ void split_stages(const GemmParams &p, int nst, int &s0, int &s1) {
+    const int s = (int)blockIdx.y;
+    s0 = (int)((int64_t)nst * s / p.splits);
+    s1 = (int)((int64_t)nst * (s + 1) / p.splits);
+}
+
 __device__ __forceinline__ void tile_coords(int b, int ntm, int ntn, int gm, int &tm, int &tn) {
     const int T = ntm * ntn;
     int L = b;

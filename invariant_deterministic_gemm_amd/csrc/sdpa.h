@@ -24,7 +24,8 @@ struct SdpaParams {
     int causal;
     int dr;                               // head dim; the 16-bit kernels run D <= 128 as 128 with zero padding
     float c;                              // scale * log2(e), rounded once to fp32
-    int nsplit;                           // ceil(S / KV_SPLIT)
+    int nsplit;                           // ceil(S / split_len)
+    int split_len;                        // KV_SPLIT; other values only in the batch-variant comparator
     float *ws_ml;                         // [rows][nsplit][2]  (m, l)
     float *ws_o;                          // [rows][nsplit][D]
 };
@@ -44,6 +45,12 @@ size_t sdpa_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int6
 // Carves ws into ws_ml / ws_o (p.nsplit must be set).
 void sdpa_bind_workspace(SdpaParams &p, void *ws);
 hipError_t launch_sdpa(const SdpaParams &p, int dt, int D, hipStream_t stream);
+// Batch-variant comparator: the generic split kernel + combine with a split length chosen from the call's
+// shape (sdpa_variant_split_len), so that the reduction order moves with the query count and the cache
+// length.  Not invariant; measurement only.
+int64_t sdpa_variant_split_len(int64_t G, int64_t Lq, int64_t S);
+size_t sdpa_variant_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t S, int64_t D);
+hipError_t launch_sdpa_variant(const SdpaParams &p, int dt, int D, hipStream_t stream);
 // Names of the kernels launch_sdpa runs ("sdpa_fused16", ...).
 const char *sdpa_kernel_name(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t S, int64_t D, int dt);
 

@@ -222,8 +222,8 @@ __global__ __launch_bounds__(64) void sdpa_split(SdpaParams p) {
     const int h = gk * p.G + rgc % p.G;
     const int pos = p.S - p.Lq + iq;
 
-    const int kbeg = sp * KV_SPLIT;
-    const int kend = min(kbeg + KV_SPLIT, p.S);
+    const int kbeg = sp * p.split_len;          // KV_SPLIT except in the comparator
+    const int kend = min(kbeg + p.split_len, p.S);
     int nblk = (kend - kbeg + KV_BLOCK - 1) / KV_BLOCK;
     if (p.causal) {
         // rows are ordered by query index, so the tile's last row sees the most keys
@@ -1831,6 +1831,61 @@ static hipError_t launch_typed(const SdpaParams &p, hipStream_t st) {
     else if (p.nsplit <= 8) hipLaunchKernelGGL((sdpa_combine<dt, D, 8>), g2, dim3(D), 0, st, p);
     else hipLaunchKernelGGL((sdpa_combine<dt, D>), g2, dim3(D), 0, st, p);
     return hipGetLastError();
+}
+
+// The comparator's split length, following the page's account of the batch-variant library (README,
+// "Why MLX is not invariant", attention): one pass over the whole cache up to 4096 keys, two passes
+// above; the second pass's split count is 64 when G times the query count is at least 4, else 32.
+int64_t sdpa_variant_split_len(int64_t G, int64_t Lq, int64_t S) {
+    const int64_t s = S > 0 ? S : 1;
+    if (s <= 4096) return (s + KV_BLOCK - 1) / KV_BLOCK * KV_BLOCK;
+    const int64_t nsplit = G * Lq >= 4 ? 64 : 32;
+    const int64_t len = (s + nsplit - 1) / nsplit;
+    return (len + KV_BLOCK - 1) / KV_BLOCK * KV_BLOCK;
+}
+
+size_t sdpa_variant_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t S, int64_t D) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || Lq <= 0 || S <= 0 || D <= 0) return 0;
+    const int64_t len = sdpa_variant_split_len(Hq / Hkv, Lq, S);
+    const int64_t rows = B * Hq * Lq;
+    const int64_t nsplit = (S + len - 1) / len;
+    const int64_t ml = (rows * nsplit * 2 * 4 + 255) / 256 * 256;
+    return (size_t)(ml + rows * nsplit * D * 4);
+}
+
+template <int dt, int D>
+static hipError_t launch_variant_typed(const SdpaParams &p, hipStream_t st) {
+    const int R = p.G * p.Lq;
+    const int64_t nwg = (int64_t)p.nsplit * ((R + 15) / 16) * p.B * p.Hkv;
+    if (nwg > INT32_MAX) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((sdpa_split<dt, D>), dim3((unsigned)nwg), dim3(64), 0, st, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((sdpa_combine<dt, D>), dim3((unsigned)((int64_t)p.B * p.Hq * p.Lq)), dim3(D), 0, st, p);
+    return hipGetLastError();
+}
+
+template <int dt>
+static hipError_t launch_variant_d(const SdpaParams &p, int D, hipStream_t st) {
+    switch (D) {
+        case 32: return launch_variant_typed<dt, 32>(p, st);
+        case 64: return launch_variant_typed<dt, 64>(p, st);
+        case 96: return launch_variant_typed<dt, 96>(p, st);
+        case 128: return launch_variant_typed<dt, 128>(p, st);
+        case 160: return launch_variant_typed<dt, 160>(p, st);
+        case 192: return launch_variant_typed<dt, 192>(p, st);
+        case 224: return launch_variant_typed<dt, 224>(p, st);
+        case 256: return launch_variant_typed<dt, 256>(p, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_sdpa_variant(const SdpaParams &p, int dt, int D, hipStream_t st) {
+    if (p.nsplit <= 0) return hipSuccess;
+    if (dt == DT_BF16) return launch_variant_d<DT_BF16>(p, D, st);
+    if (dt == DT_F16) return launch_variant_d<DT_F16>(p, D, st);
+    if (dt == DT_F32) return launch_variant_d<DT_F32>(p, D, st);
+    return hipErrorInvalidValue;
 }
 
 const char *sdpa_kernel_name(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t S, int64_t D, int dt) {

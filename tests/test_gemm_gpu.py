@@ -274,6 +274,44 @@ def test_splitk_comparator_is_correct_but_batch_variant():
     assert_bits_equal(bi.bi_variant_linear(x[:8], w, b, splits=1), bi.bi_linear(x[:8], w, b), "splits=1")
 
 
+@pytest.mark.parametrize("K", [1024, 960])
+def test_splitk_comparator_runs_the_invariant_kernels_exactly(K):
+    """The comparator cuts K into ranges on the very kernels bi_linear picks (strip, pipelined and ring
+    tiles).  With integer inputs every summation order is exact, so any split count must give the oracle
+    rounded once, bit for bit: no stage of K may be dropped or counted twice at any split boundary."""
+    lib = bi._native.load()
+    Ns = (72, 4100)
+    Ms = (1, 5, 16, 33, 64, 65, 128, 129, 256, 300, 1024)
+    x = ints((max(Ms), K), 71, torch.bfloat16)
+    w = ints((max(Ns), K), 72, torch.bfloat16)
+    b = ints((max(Ns),), 73, torch.bfloat16, -5, 5)
+    xg, wg, bg = x.to(DEV), w.to(DEV), b.to(DEV)
+    seen = set()
+    for n in Ns:
+        ref = round_ref(oracle.linear(x, w[:n], b[:n]), torch.bfloat16)
+        for m in Ms:
+            seen.add(lib.bi_gemm_kernel_name(m, n, K, bi.BI_BF16, 0).decode())
+            for sp in (1, 2, 3, 8):
+                v = bi.bi_variant_linear(xg[:m], wg[:n], bg[:n], splits=sp)
+                assert_bits_equal(v.cpu(), ref[:m], f"K={K} N={n} M={m} splits={sp}")
+    assert any(k.startswith("gemm16_strip") for k in seen) and any(k.startswith("gemm16_ring") for k in seen)
+    assert any(k.startswith("gemm16_pipe") for k in seen) or K % 128 != 0, seen
+
+
+def test_splitk_comparator_cost_shapes_match_oracle():
+    """The bf16 linear workload's shapes (K = 4096, N = 14336) through the comparator's default M-keyed
+    split counts: within the oracle gate, and different bits from bi_linear at every M that splits."""
+    d = synthetic.cfg2_inputs(14336, M_max=256)
+    x, w, b = (d[k].to(DEV) for k in ("x", "w", "b"))
+    ref = oracle.linear(d["x"][:8], d["w"], d["b"])
+    lib = bi._native.load()
+    for m in (8, 33, 128):
+        assert lib.bi_variant_splits(m) > 1
+        v = bi.bi_variant_linear(x[:m], w, b)
+        assert_close_to_oracle(v[:8].cpu(), ref[:min(m, 8)], f"variant M={m}")
+        assert n_bit_diff(v, bi.bi_linear(x[:m], w, b)) > 0, f"M={m}: split-K changed no bit"
+
+
 @pytest.mark.parametrize("N", [4096, 14336])
 def test_large_m_rows_match_small_m_calls(N):
     """Rows of big-M calls (256x256 / 256x224 / 128x128 / 64x64 tiles) equal the same rows computed

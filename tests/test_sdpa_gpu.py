@@ -19,7 +19,7 @@ import torch
 import invariant_deterministic_gemm_amd as bi
 import oracle
 import synthetic
-from helpers import assert_bits_equal, assert_close_to_oracle, round_ref
+from helpers import assert_bits_equal, assert_close_to_oracle, n_bit_diff, round_ref
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -447,3 +447,37 @@ def test_long_causal_prefill_needs_no_workspace():
         assert_close_to_oracle(o[:, :, p:p + 1].cpu(), ref, f"row {p}")
         dec = bi.bi_sdpa(q[:, :, p:p + 1], k[:, :, :p + 1], v[:, :, :p + 1], causal=True)
         assert_bits_equal(o[:, :, p:p + 1], dec, f"row {p} vs its decode")
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32], ids=_ids)
+def test_variant_attention_is_accurate_but_batch_variant(dt):
+    """The batch-variant attention comparator (split length from G * q_len and S, one pass up to 4096 keys):
+    within the oracle gate, but a token's bits move with its query count (GQA factor 2: decode runs 32
+    splits, a chunk of two tokens 64) and when a fully masked key takes the cache past 4096 keys -- the
+    three switches the page lists -- while the invariant path does not move."""
+    lib = bi._native.load()
+    assert lib.bi_variant_sdpa_split_len(2, 1, 8192) == 256 and lib.bi_variant_sdpa_split_len(2, 2, 8192) == 128
+    assert lib.bi_variant_sdpa_split_len(4, 1, 4096) == 4096 and lib.bi_variant_sdpa_split_len(4, 1, 4097) == 128
+    S = 6000
+    q = synthetic.randn((1, 16, 2, 128), 0x5EEDB0, 1.0, dt).to(DEV)
+    k = synthetic.randn((1, 8, S, 128), 0x5EEDB1, 1.0, dt).to(DEV)
+    v = synthetic.randn((1, 8, S, 128), 0x5EEDB2, 1.0, dt).to(DEV)
+    chunk = bi.bi_variant_sdpa(q, k, v, causal=True)
+    dec = bi.bi_variant_sdpa(q[:, :, 1:], k, v, causal=True)
+    ref = oracle.sdpa(q.cpu(), k.cpu(), v.cpu(), causal=True)
+    assert_close_to_oracle(chunk.cpu(), ref, "variant chunk vs oracle")
+    assert_close_to_oracle(dec.cpu(), ref[:, :, 1:], "variant decode vs oracle")
+    assert n_bit_diff(chunk[:, :, 1:], dec) > 0, "q_len 2 vs 1 changed no bit"
+    assert_bits_equal(bi.bi_sdpa(q, k, v, causal=True)[:, :, 1:], bi.bi_sdpa(q[:, :, 1:], k, v, causal=True),
+                      "invariant path, q_len 2 vs 1")
+    # context growth: 4096 keys vs 4097 with the newest fully masked
+    qd = q[:, :, 1:]
+    base = bi.bi_variant_sdpa(qd, k[:, :, :4096], v[:, :, :4096])
+    mask = torch.ones(1, 1, 1, 4097, dtype=torch.bool, device=DEV)
+    mask[..., 4096] = False
+    grown = bi.bi_variant_sdpa(qd, k[:, :, :4097], v[:, :, :4097], mask=mask)
+    assert n_bit_diff(base, grown) > 0, "crossing 4096 keys changed no bit"
+    assert_close_to_oracle(grown.cpu(), oracle.sdpa(qd.cpu(), k[:, :, :4096].cpu(), v[:, :, :4096].cpu()),
+                           "variant grown vs oracle")
+    assert_bits_equal(bi.bi_sdpa(qd, k[:, :, :4097], v[:, :, :4097], mask=mask),
+                      bi.bi_sdpa(qd, k[:, :, :4096], v[:, :, :4096]), "invariant path across 4096")
