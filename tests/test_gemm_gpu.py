@@ -258,6 +258,32 @@ def test_graph_replay_matches_eager():
         assert outs_prev is not None
 
 
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16], ids=lambda d: str(d).split(".")[-1])
+@pytest.mark.parametrize("K", [1000, 136])
+def test_ragged_k_random_rows_across_kernel_families(dt, K):
+    """K not a multiple of 64: 16-bit linear runs the strip kernel up to M = 64 and the generic tiled kernel
+    from M = 65.  Random N(0, 1) inputs (every summation order gives different bits, unlike integer
+    inputs), so the two families must run the same chain and treat the ragged tail alike: every row of
+    each M equals the same row of the M = 300 call, for the (N, K) weight and for the (K, N) layout."""
+    lib = bi._native.load()
+    BI = bi.BI_BF16 if dt == torch.bfloat16 else bi.BI_F16
+    N = 200
+    x = synthetic.randn((300, K), 0x5EED3D + K, 1.0, dt).to(DEV)
+    w = synthetic.randn((N, K), 0x5EED3E + K, 1.0, dt).to(DEV)
+    b = synthetic.randn((N,), 0x5EED3F + K, 1.0, dt).to(DEV)
+    wkn = w.t().contiguous()
+    names = {lib.bi_gemm_kernel_name(m, N, K, BI, 0).decode() for m in (64, 65)}
+    assert any(n.startswith("gemm16_strip") for n in names) and any(n.startswith("gemm_tiled") for n in names), names
+    full = bi.bi_linear(x, w, b)
+    full_kn = bi.bi_matmul(x, wkn)
+    for m in (1, 16, 63, 64, 65, 129, 300):
+        assert_bits_equal(bi.bi_linear(x[:m], w, b), full[:m], f"K={K} linear M={m}")
+        assert_bits_equal(bi.bi_matmul(x[:m], wkn), full_kn[:m], f"K={K} (K, N) matmul M={m}")
+        assert_bits_equal(bi.bi_matmul(x[:m], w.t()), bi.bi_linear(x[:m], w), f"K={K} transposed view M={m}")
+    ref = oracle.linear(x[:8].cpu(), w.cpu(), b.cpu())
+    assert_close_to_oracle(full[:8].cpu(), ref, f"K={K} vs oracle")
+
+
 def test_splitk_comparator_is_correct_but_batch_variant():
     d = synthetic.cfg2_inputs(4096, M_max=256)
     x, w, b = (d[k].to(DEV) for k in ("x", "w", "b"))

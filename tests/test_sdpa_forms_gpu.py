@@ -232,6 +232,41 @@ def test_wide_head_dims_prefill(dt, D):
     _graph_replays_equal_eager(fn, fm, f"D={D} wide prefill")
 
 
+@pytest.mark.parametrize("D", [160, 192, 224, 256])
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16], ids=_ids)
+def test_wide_prefill_batch_switch_keeps_bits(dt, D):
+    """The wide prefill kernel takes 16-bit D > 128 calls from 64 query rows once the batch holds 192 rows
+    or more, so whether a row runs there or on the split kernels depends on the batch: B = 4 x 64 rows
+    (wide prefill) against each element alone (split kernels), and B = 3 (192 rows, wide prefill) against
+    B = 2 (128 rows, split kernels); causal, with an additive mask, and with sinks; raw bits, plus the
+    oracle on one element."""
+    Hq, Hkv, Lq, S = 8, 2, 64, 700
+    BI = bi.BI_BF16 if dt == torch.bfloat16 else bi.BI_F16
+    lib = bi._native.load()
+    assert lib.bi_sdpa_kernel_name(4, Hq, Hkv, Lq, S, D, BI).decode() == "sdpa_prefill16w"
+    assert lib.bi_sdpa_kernel_name(3, Hq, Hkv, Lq, S, D, BI).decode() == "sdpa_prefill16w"
+    assert lib.bi_sdpa_kernel_name(2, Hq, Hkv, Lq, S, D, BI).decode() != "sdpa_prefill16w"
+    assert lib.bi_sdpa_kernel_name(1, Hq, Hkv, Lq, S, D, BI).decode() != "sdpa_prefill16w"
+    q, k, v = _qkv(4, Hq, Hkv, Lq, S, D, dt, 410 + D)
+    amask = _additive((4, 1, Lq, S), 411 + D, dt)
+    amask[..., 0] = 0.0
+    sinks = synthetic.randn((Hq,), 412 + D, 2.0)
+    qg, kg, vg, ag, sg = _gpu(q, k, v, amask, sinks)
+    forms = (("causal", lambda b0, b1: dict(causal=True)),
+             ("additive", lambda b0, b1: dict(mask=ag[b0:b1])),
+             ("causal+sinks", lambda b0, b1: dict(causal=True, sinks=sg)))
+    for what, kw in forms:
+        four = bi.bi_sdpa(qg, kg, vg, **kw(0, 4))
+        for e in range(4):
+            one = bi.bi_sdpa(qg[e:e + 1], kg[e:e + 1], vg[e:e + 1], **kw(e, e + 1))
+            assert_bits_equal(four[e:e + 1], one, f"D={D} {what}: element {e} in B=4 vs alone")
+        three = bi.bi_sdpa(qg[:3], kg[:3], vg[:3], **kw(0, 3))
+        two = bi.bi_sdpa(qg[:2], kg[:2], vg[:2], **kw(0, 2))
+        assert_bits_equal(three[:2], two, f"D={D} {what}: B=3 vs B=2")
+    want = oracle.sdpa(q[:1], k[:1], v[:1], causal=True, sinks=sinks)
+    assert_close_to_oracle(bi.bi_sdpa(qg[:1], kg[:1], vg[:1], causal=True, sinks=sg), want, f"D={D}: vs oracle")
+
+
 @pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16], ids=_ids)
 def test_wide_split_matches_generic_split(dt):
     """16-bit D = 256 decode: the wide split kernel (512-byte rows, moderate grids) and the generic split
