@@ -159,7 +159,11 @@ bi_status bi_addmm(const void *cin, int64_t ldcin,
  * Workspace: ws must hold bi_sdpa_workspace_bytes(B, Hq, Hkv, Lq, S, D, dt)
  * bytes, 256-byte aligned, device memory owned by the caller; its contents on
  * entry do not matter and on return are unspecified.  Two calls that run at
- * the same time must not share a workspace.  The query returns 0 (ws may then
+ * the same time must not share a workspace.  The query stays at or below
+ * 256 MiB (or the partials of one query row per head, if more): a call whose
+ * partials would need more runs in chunks of query rows, one after the other
+ * on `stream`, each with the keys up to its last row when causal; no row's
+ * arithmetic changes.  The query returns 0 (ws may then
  * be NULL) for the shapes served without a workspace: 16-bit dt with either
  * Lq >= 384 (prefill: splits folded in registers; for D > 128 also Lq >= 64
  * with B Lq >= 192), or D <= 128 and S <= 256

@@ -9,6 +9,7 @@
 // environment.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -302,9 +303,33 @@ static bi_status sdpa_impl(const char *fn, const void *q, const int64_t q_str[4]
     p.c = (float)((double)scale * 1.4426950408889634);   // log2(e), rounded once to fp32
     p.split_len = variant ? (int)bi::sdpa_variant_split_len(G, Lq, S) : bi::KV_SPLIT;
     p.nsplit = (int)((S + p.split_len - 1) / p.split_len);
-    if (need > 0) bi::sdpa_bind_workspace(p, ws);
-    if (variant) return device_status(bi::launch_sdpa_variant(p, dt, (int)D, (hipStream_t)stream), fn);
-    return device_status(bi::launch_sdpa(p, dt, (int)D, (hipStream_t)stream), fn);
+    if (variant) {
+        if (need > 0) bi::sdpa_bind_workspace(p, ws);
+        return device_status(bi::launch_sdpa_variant(p, dt, (int)D, (hipStream_t)stream), fn);
+    }
+    const int64_t Lc = bi::sdpa_chunk_rows(B, Hq, Hkv, Lq, S, D, (int)dt);
+    if (Lc >= Lq) {
+        if (need > 0) bi::sdpa_bind_workspace(p, ws);
+        return device_status(bi::launch_sdpa(p, dt, (int)D, (hipStream_t)stream), fn);
+    }
+    // query rows c0 .. c0 + Lc - 1 as calls of their own: q, o and the mask start at row c0, and a causal
+    // chunk sees the keys up to its last row (bottom-right alignment keeps every row's position)
+    const int64_t eb = esize(dt);
+    for (int64_t c0 = 0; c0 < Lq; c0 += Lc) {
+        bi::SdpaParams pc = p;
+        const int64_t lc = std::min(Lc, Lq - c0);
+        pc.q = static_cast<const char *>(q) + c0 * q_str[2] * eb;
+        pc.o = static_cast<char *>(o) + c0 * o_str[2] * eb;
+        if (mask != nullptr) pc.mask = static_cast<const char *>(mask) + c0 * mask_str[2] * (pc.mask_add ? eb : 1);
+        pc.Lq = (int)lc;
+        pc.S = causal ? (int)(S - Lq + c0 + lc) : (int)S;
+        pc.nsplit = (pc.S + bi::KV_SPLIT - 1) / bi::KV_SPLIT;
+        pc.mask_vec = p.mask_vec && pc.S % 4 == 0;    // 4-key mask groups need S % 4 == 0
+        if (bi::sdpa_workspace_bytes(B, Hq, Hkv, lc, pc.S, D, (int)dt) > 0) bi::sdpa_bind_workspace(pc, ws);
+        const bi_status st = device_status(bi::launch_sdpa(pc, dt, (int)D, (hipStream_t)stream), fn);
+        if (st != BI_OK) return st;
+    }
+    return ok();
 }
 
 bi_status bi_sdpa(const void *q, const int64_t q_str[4], const void *k, const int64_t k_str[4], const void *v,

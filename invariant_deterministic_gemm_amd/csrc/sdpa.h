@@ -42,6 +42,11 @@ enum SdpaPath {
 // Hkv >= 1 and Hq % Hkv == 0 (the callers validate).
 SdpaPath sdpa_path(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t S, int64_t D, int dt);
 size_t sdpa_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t S, int64_t D, int dt);
+// Calls whose split partials would exceed SDPA_WS_CAP bytes run in chunks of this many query rows (each a
+// call of its own with the keys up to its last row when causal: every row's arithmetic is unchanged), so
+// the workspace stays bounded as Lq and S grow; Lq when the call runs whole.
+constexpr int64_t SDPA_WS_CAP = int64_t(256) << 20;
+int64_t sdpa_chunk_rows(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t S, int64_t D, int dt);
 // Carves ws into ws_ml / ws_o (p.nsplit must be set).
 void sdpa_bind_workspace(SdpaParams &p, void *ws);
 hipError_t launch_sdpa(const SdpaParams &p, int dt, int D, hipStream_t stream);

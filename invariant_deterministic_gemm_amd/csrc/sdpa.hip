@@ -33,6 +33,7 @@
 // masked) run the same operations on the same operands, and appending masked
 // keys to the cache only appends identity steps.
 
+#include <algorithm>
 #include <type_traits>
 
 #include "device.h"
@@ -1746,15 +1747,31 @@ SdpaPath sdpa_path(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t S, in
     return SDPA_SPLIT;
 }
 
-size_t sdpa_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t S, int64_t D, int dt) {
-    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || Lq <= 0 || S <= 0 || D <= 0) return 0;
-    const SdpaPath path = sdpa_path(B, Hq, Hkv, Lq, S, D, dt);
-    if (path != SDPA_SPLIT && path != SDPA_QUAD16 && path != SDPA_SPLIT16W) return 0;
-    if (path == SDPA_QUAD16 && S <= KV_SPLIT) return 0;          // one split: the quad kernel finishes the rows
+// Bytes of split partials for Lq query rows: the (m, l) pairs padded to 256 bytes, then the O rows.
+static int64_t partial_bytes(int64_t B, int64_t Hq, int64_t Lq, int64_t S, int64_t D) {
     const int64_t rows = B * Hq * Lq;
     const int64_t nsplit = (S + KV_SPLIT - 1) / KV_SPLIT;
     const int64_t ml = (rows * nsplit * 2 * 4 + 255) / 256 * 256;
-    return (size_t)(ml + rows * nsplit * D * 4);
+    return ml + rows * nsplit * D * 4;
+}
+
+int64_t sdpa_chunk_rows(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t S, int64_t D, int dt) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || Lq <= 0 || S <= 0 || D <= 0) return Lq;
+    const SdpaPath path = sdpa_path(B, Hq, Hkv, Lq, S, D, dt);
+    if (path != SDPA_SPLIT && path != SDPA_QUAD16 && path != SDPA_SPLIT16W) return Lq;
+    if (partial_bytes(B, Hq, Lq, S, D) <= SDPA_WS_CAP) return Lq;
+    const int64_t per_row = partial_bytes(B, Hq, 1, S, D) + 256;
+    return std::max<int64_t>(1, std::min<int64_t>(Lq, SDPA_WS_CAP / per_row));
+}
+
+size_t sdpa_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t S, int64_t D, int dt) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || Lq <= 0 || S <= 0 || D <= 0) return 0;
+    const int64_t Lc = sdpa_chunk_rows(B, Hq, Hkv, Lq, S, D, dt);
+    if (Lc < Lq) return (size_t)partial_bytes(B, Hq, Lc, S, D);  // bounds every chunk's path
+    const SdpaPath path = sdpa_path(B, Hq, Hkv, Lq, S, D, dt);
+    if (path != SDPA_SPLIT && path != SDPA_QUAD16 && path != SDPA_SPLIT16W) return 0;
+    if (path == SDPA_QUAD16 && S <= KV_SPLIT) return 0;          // one split: the quad kernel finishes the rows
+    return (size_t)partial_bytes(B, Hq, Lq, S, D);
 }
 
 void sdpa_bind_workspace(SdpaParams &p, void *ws) {

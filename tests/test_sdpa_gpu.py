@@ -481,3 +481,45 @@ def test_variant_attention_is_accurate_but_batch_variant(dt):
                            "variant grown vs oracle")
     assert_bits_equal(bi.bi_sdpa(qd, k[:, :, :4097], v[:, :, :4097], mask=mask),
                       bi.bi_sdpa(qd, k[:, :, :4096], v[:, :, :4096]), "invariant path across 4096")
+
+
+def test_workspace_stays_bounded_for_long_calls():
+    """Calls whose split partials would exceed 256 MiB (fp32 long prefill, 16-bit multi-row calls against
+    long caches) run in query-row chunks, so the workspace query stays bounded; every sampled row keeps the
+    bits of its own single-row call and the oracle gate holds."""
+    lib = bi._native.load()
+    cap = 256 * 2 ** 20
+    # fp32 causal prefill, 4096 tokens (the whole-call partials would need ~1.1 GB)
+    S = 4096
+    q = synthetic.randn((1, 32, S, 128), 0x5EEDC0, 1.0, torch.float32).to(DEV)
+    k = synthetic.randn((1, 8, S, 128), 0x5EEDC1, 1.0, torch.float32).to(DEV)
+    v = synthetic.randn((1, 8, S, 128), 0x5EEDC2, 1.0, torch.float32).to(DEV)
+    assert 0 < bi.sdpa_workspace_bytes(1, 32, 8, S, S, 128, torch.float32) <= cap
+    o = bi.bi_sdpa(q, k, v, causal=True)
+    qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
+    for p in (0, 1000, 2047, 2048, 3333, 4095):
+        dec = bi.bi_sdpa(q[:, :, p:p + 1], k[:, :, :p + 1], v[:, :, :p + 1], causal=True)
+        assert_bits_equal(o[:, :, p:p + 1], dec, f"fp32 row {p} vs its decode")
+        ref = oracle.sdpa(qc[:, :, p:p + 1], kc[:, :, :p + 1], vc[:, :, :p + 1], causal=True)
+        assert_close_to_oracle(o[:, :, p:p + 1].cpu(), ref, f"fp32 row {p}")
+    # fp32 with a boolean mask, not causal: chunks keep every key and start their mask rows at the chunk
+    Lq, S2 = 2048, 3000
+    gen = torch.Generator(device="cpu").manual_seed(0x5EEDC3)
+    mask = (torch.rand((1, 1, Lq, S2), generator=gen) > 0.3).to(DEV)
+    assert 0 < bi.sdpa_workspace_bytes(1, 32, 8, Lq, S2, 128, torch.float32) <= cap
+    om = bi.bi_sdpa(q[:, :, :Lq], k[:, :, :S2], v[:, :, :S2], mask=mask)
+    for i in (0, 700, 1500, 2047):
+        one = bi.bi_sdpa(q[:, :, i:i + 1], k[:, :, :S2], v[:, :, :S2], mask=mask[:, :, i:i + 1])
+        assert_bits_equal(om[:, :, i:i + 1], one, f"fp32 masked row {i} vs alone")
+    # bf16: 300 query rows per sequence against a 20000-key cache, batch 4
+    B, L3, S3 = 4, 300, 20000
+    assert lib.bi_sdpa_kernel_name(B, 32, 8, L3, S3, 128, bi.BI_BF16).decode() == "sdpa_split16+combine"
+    assert 0 < bi.sdpa_workspace_bytes(B, 32, 8, L3, S3, 128, torch.bfloat16) <= cap
+    q3 = synthetic.randn((B, 32, L3, 128), 0x5EEDC4, 1.0, torch.bfloat16).to(DEV)
+    k3 = synthetic.randn((B, 8, S3, 128), 0x5EEDC5, 1.0, torch.bfloat16).to(DEV)
+    v3 = synthetic.randn((B, 8, S3, 128), 0x5EEDC6, 1.0, torch.bfloat16).to(DEV)
+    o3 = bi.bi_sdpa(q3, k3, v3, causal=True)
+    for i in (0, 150, 299):
+        p = S3 - L3 + i
+        dec = bi.bi_sdpa(q3[:, :, i:i + 1], k3[:, :, :p + 1], v3[:, :, :p + 1], causal=True)
+        assert_bits_equal(o3[:, :, i:i + 1], dec, f"bf16 row {i} vs its decode")
