@@ -223,7 +223,12 @@ def test_sdpa_workspace_formula(lib):
     assert ws(1, 32, 8, 384, 32768, 128, BF16) == 0
     assert ws(1, 32, 8, 384, 4096, 256, BF16) == 0
     assert ws(1, 32, 8, 384, 4096, 256, F32) == split_bytes(1, 32, 384, 4096, 256)
-    assert ws(1, 32, 8, 383, 32768, 128, BF16) == split_bytes(1, 32, 383, 32768, 128)
+    # partials above 256 MiB: the call runs in query-row chunks and the query reports one chunk's need
+    cap = 256 * 2 ** 20
+    assert split_bytes(1, 32, 383, 32768, 128) > cap
+    lc = cap // (split_bytes(1, 32, 1, 32768, 128) + 256)
+    assert ws(1, 32, 8, 383, 32768, 128, BF16) == split_bytes(1, 32, lc, 32768, 128) <= cap
+    assert ws(1, 32, 8, 8192, 8192, 128, F32) <= cap
     assert ws(1, 1, 1, 1, 0, 128, BF16) == 0
     assert ws(1, 1, 1, 1, 10, 128, 7) == 0
     assert ws(1, 32, 0, 1, 10, 128, BF16) == 0
