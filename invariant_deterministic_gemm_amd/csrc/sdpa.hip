@@ -1263,6 +1263,36 @@ __device__ __forceinline__ void fold_split16_full(float &m_run, float &l_run, f3
     for (int t = 0; t < NT; ++t) o[t] = zero4();
 }
 
+// Direct-to-LDS loads written as asm, so that the compiler does not know about them: it would otherwise
+// wait for every such load in flight before any transposed LDS read (it cannot tell which buffer a
+// transposed read touches).  The kernel that issues them waits for them itself (asm_wait_vmcnt0, then a
+// barrier) before any wavefront reads the bytes; they write no register.  saddr form: a uniform 64-bit
+// base plus this lane's 32-bit offset; vaddr form: this lane's 64-bit address.
+__device__ __forceinline__ void dma16_saddr(const char *base, uint32_t voff, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_addr), "v"(voff), "s"(base)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void dma16_vaddr(const char *src, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_addr), "v"(src) : "memory", "m0");
+}
+__device__ __forceinline__ void asm_wait_vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// The V fragments of one 32-key half as attn_vfrags16<8> reads them: va[t] is the LDS address of tile t's
+// first row-0 read of half 0 in the buffer, HOFF the byte offset of the half (+ 16 key rows for the second
+// read of a tile).
+__device__ __forceinline__ u32x2 lds_tr16_at(uint32_t addr) {
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(size_t)addr);
+    return __builtin_bit_cast(u32x2, v);
+}
+template <int HOFF>
+__device__ __forceinline__ void vfrags_tr(const uint32_t (&va)[8], u32x4 (&vf)[8]) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const u32x2 lo = lds_tr16_at(va[t] + HOFF), hi = lds_tr16_at(va[t] + HOFF + 16 * 256);
+        vf[t] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    }
+}
+
 // Long prefill (rows of 128, or zero-padded to 128 when PAD), software-pipelined over key blocks.  W row
 // tiles of one (batch, KV head), one per wavefront, share each K and V block through LDS; K runs two
 // blocks ahead and V one: while block j's softmax runs, block j + 1's scores are formed from its K block
@@ -1282,8 +1312,7 @@ void sdpa_prefill16p(SdpaParams p) {
     constexpr int BPS = KV_SPLIT / KV_BLOCK;           // blocks per split
     constexpr float NEG_INF = -__builtin_huge_valf();
     static_assert((KBYTES / 1024) % W == 0, "every wavefront issues the same loads");
-    // the K buffers as objects of their own, so the compiler can tell their reads from the direct-to-LDS
-    // loads into the other K buffer or into V (V is read by vfrags_tr_asm, which the compiler does not see)
+    // LDS: K block buffers and V block buffers, two of each
     __shared__ __attribute__((aligned(1024))) char kbuf0[KBYTES];
     __shared__ __attribute__((aligned(1024))) char kbuf1[KBYTES];
     __shared__ __attribute__((aligned(1024))) char vbufs[2 * KBYTES];
@@ -1318,41 +1347,30 @@ void sdpa_prefill16p(SdpaParams p) {
     // stride is too large for 32-bit offsets) clamps rows to S - 1 in 64-bit arithmetic.
     const int lrow = lane >> 4, lslot = lane & 15;
     const bool off32 = (uint64_t)max(kstr, vstr) * KV_BLOCK + ROWB <= 0xffffffffull;
-    uint32_t koff[QW], voff[QW];
-    bool kz[QW], vz[QW];                               // PAD: chunk at d >= D reads the zero page
-#pragma unroll
-    for (int j = 0; j < QW; ++j) {
-        const int row = 4 * (wave + W * j) + lrow;
-        const int ck = lslot ^ (row & 15), cv = lslot ^ ((row & 7) << 1);
-        kz[j] = PAD && 8 * ck >= p.dr;
-        vz[j] = PAD && 8 * cv >= p.dr;
-        koff[j] = (uint32_t)(row * kstr) + (ck << 4);
-        voff[j] = (uint32_t)(row * vstr) + (cv << 4);
-    }
+    // the chunk slots do not depend on j (4 W j is a multiple of 16), so load j is load 0 plus 4 W j rows
+    static_assert((4 * W) % 16 == 0, "row period of the chunk swizzles");
+    const int row0 = 4 * wave + lrow;
+    const int ck = lslot ^ (row0 & 15), cv = lslot ^ ((row0 & 7) << 1);
+    const bool kz = PAD && 8 * ck >= p.dr, vz = PAD && 8 * cv >= p.dr;   // PAD: chunk at d >= D: zero page
+    const uint32_t koff = (uint32_t)(row0 * kstr) + (ck << 4), voff = (uint32_t)(row0 * vstr) + (cv << 4);
     const char *zp = reinterpret_cast<const char *>(g_zero_page);
     auto issue = [&](int blk, char *buf, bool isv) {
         const int kb = blk * KV_BLOCK;
         const char *base = isv ? vbase : kbase;
         const int64_t str = isv ? vstr : kstr;
-        if (off32 && kb + KV_BLOCK <= p.S) {
-            const char *bp = base + (int64_t)kb * str;
+        const uint32_t lbase = (uint32_t)(uintptr_t)BI_LDS_PTR(buf) + wave * 1024;
+        if (!PAD && off32 && kb + KV_BLOCK <= p.S) {
 #pragma unroll
-            for (int j = 0; j < QW; ++j) {
-                const char *src = bp + (isv ? voff[j] : koff[j]);
-                if constexpr (PAD) src = (isv ? vz[j] : kz[j]) ? zp : src;
-                __builtin_amdgcn_global_load_lds(static_cast<const void *>(src),
-                                                 BI_LDS_PTR(buf + (wave + W * j) * 1024), 16, 0, 0);
-            }
+            for (int j = 0; j < QW; ++j)
+                dma16_saddr(base + (int64_t)(kb + 4 * W * j) * str, isv ? voff : koff, lbase + W * j * 1024);
         } else {
 #pragma unroll
             for (int j = 0; j < QW; ++j) {
-                const int row = 4 * (wave + W * j) + lrow;
+                const int row = row0 + 4 * W * j;
                 const int64_t key = min(kb + row, p.S - 1);
-                const int c = isv ? lslot ^ ((row & 7) << 1) : lslot ^ (row & 15);
-                const char *src = base + key * str + (c << 4);
-                if constexpr (PAD) src = (isv ? vz[j] : kz[j]) ? zp : src;
-                __builtin_amdgcn_global_load_lds(static_cast<const void *>(src),
-                                                 BI_LDS_PTR(buf + (wave + W * j) * 1024), 16, 0, 0);
+                const char *src = base + key * str + ((isv ? cv : ck) << 4);
+                if constexpr (PAD) src = (isv ? vz : kz) ? zp : src;
+                dma16_vaddr(src, lbase + W * j * 1024);
             }
         }
     };
@@ -1399,16 +1417,17 @@ void sdpa_prefill16p(SdpaParams p) {
             for (int c = 0; c < 4; ++c) st[kt] = Mfma<dt>::step(kf[c], r.qf[c], st[kt]);
         }
     };
-    // O += P . V over the two 32-key halves of V buffer VB
-    auto pv = [&](const u32x4 (&pf)[2], auto vb) {
+    // the V fragments of V buffer VB (both 32-key halves), and O += P . V from them
+    auto vread = [&](auto vb, u32x4 (&vf)[2][8]) {
         constexpr int VB = decltype(vb)::value;
-        u32x4 vf[8];
-        vfrags_tr_asm<VB * KBYTES>(va, vf);
+        vfrags_tr<VB * KBYTES>(va, vf[0]);
+        vfrags_tr<VB * KBYTES + 32 * ROWB>(va, vf[1]);
+    };
+    auto pv = [&](const u32x4 (&pf)[2], const u32x4 (&vf)[2][8]) {
 #pragma unroll
-        for (int t = 0; t < 8; ++t) o[t] = Mfma<dt>::step(pf[0], vf[t], o[t]);
-        vfrags_tr_asm<VB * KBYTES + 32 * ROWB>(va, vf);
+        for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int t = 0; t < 8; ++t) o[t] = Mfma<dt>::step(pf[1], vf[t], o[t]);
+            for (int t = 0; t < 8; ++t) o[t] = Mfma<dt>::step(pf[c], vf[c][t], o[t]);
     };
 
     using VB0 = std::integral_constant<int, 0>;
@@ -1419,7 +1438,7 @@ void sdpa_prefill16p(SdpaParams p) {
     // j - 1 read; block j + 1's scores, block j's softmax and P . V
     auto top = [&](int j, char *kfree, char *vnext, char *vcur) {
         const int kb = j * KV_BLOCK;
-        BI_WAIT_VMCNT(0);
+        asm_wait_vmcnt0();                               // this wavefront's loads of K(j + 1) and V(j) landed
         if (kb + KV_BLOCK > p.S) {
             // V rows past S read as zero; each wavefront clears the rows its own loads filled
 #pragma unroll
@@ -1438,7 +1457,9 @@ void sdpa_prefill16p(SdpaParams p) {
         scores(knext, st_nxt);
         u32x4 pf[2];
         attn_softmax16<dt, 4, 8, true, true>(p, r, st_cur, j * KV_BLOCK, m_run, l_run, o, pf);
-        pv(pf, vb);
+        u32x4 vf[2][8];
+        vread(vb, vf);
+        pv(pf, vf);
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) st_cur[kt] = st_nxt[kt];
     };
@@ -1447,7 +1468,9 @@ void sdpa_prefill16p(SdpaParams p) {
         if (j + 1 < nblk) scores(knext, st_nxt);
         u32x4 pf[2];
         attn_softmax16<dt>(p, r, st_cur, j * KV_BLOCK, m_run, l_run, o, pf);
-        pv(pf, vb);
+        u32x4 vf[2][8];
+        vread(vb, vf);
+        pv(pf, vf);
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) st_cur[kt] = st_nxt[kt];
         if ((j + 1) % BPS == 0 || j + 1 == nblk) fold_split16(m_run, l_run, o, have, mt, lt, ot);
@@ -1457,7 +1480,7 @@ void sdpa_prefill16p(SdpaParams p) {
         issue(0, kbuf0, false);
         issue(0, vbuf0, true);
         if (nblk > 1) issue(1, kbuf1, false);
-        BI_WAIT_VMCNT(0);
+        asm_wait_vmcnt0();
         __syncthreads();
         scores(kbuf0, st_cur);
     }
