@@ -83,7 +83,7 @@ def parse():
     ap.add_argument("--cell", action="append", default=[], choices=sorted(CELLS),
                     help="measure only these cells (no step, no CPU baseline); repeatable")
     ap.add_argument("--eager", action="store_true", help="with --cell: direct calls instead of graph replays")
-    ap.add_argument("--summarize-counters", metavar="DIR", default=None,
+    ap.add_argument("--summarize-counters", metavar="DIR", action="append", default=[],
                     help="per-dispatch averages of the counters under DIR for kernels matching --kernel")
     ap.add_argument("--kernel", action="append", default=[])
     ap.add_argument("--pmc-pass", metavar="ORDER_JSON", default=None,
@@ -181,6 +181,8 @@ def main():
         # chosen cells only (used for the profiles of single kernels)
         global EAGER
         EAGER = args.eager
+        if EAGER:
+            _calibration_copy(torch)
         ctx = Ctx(torch, bi, lib, dev, synthetic, args.samples)
         cells = measure_cells(ctx, args.cell)
         print(json.dumps({"cells": cells}), flush=True)
@@ -954,6 +956,17 @@ def cpu_baseline(torch, synthetic, args):
 
 
 # ---------------------------------------------------------------- profiling helpers
+def _calibration_copy(torch):
+    """An elementwise copy that reads and writes CALIB_BYTES each, dispatched before any library kernel, so
+    counter summaries can scale FETCH_SIZE / WRITE_SIZE to bytes."""
+    src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device="cuda").uniform_()
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.mul(src, 2.0, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def pmc_pass(torch, st, order_path):
     """One eager pass for counter collection: a calibration copy of known size, then every launch
     of the step once, in order; writes which kernel group each of our dispatches belongs to."""
@@ -1065,38 +1078,79 @@ def measured_traffic(group, family):
 
 
 def summarize_counters(args):
-    """Per-dispatch averages of every counter collected under a directory, for the kernels whose names
-    contain one of --kernel, with instruction counts per wavefront and per MFMA instruction."""
-    files = glob.glob(os.path.join(args.summarize_counters, "**", "*counter_collection.csv"), recursive=True)
-    if not files:
-        raise SystemExit(f"no counter_collection.csv under {args.summarize_counters}")
+    """Per-dispatch averages of the counters collected under one or more directories (a run per counter
+    pass), for the kernels whose names contain one of --kernel, grouped by kernel and grid size; derived:
+    instructions per wavefront and per MFMA instruction, busy fractions of the matrix cores, the vector ALUs
+    and the LDS over the dispatch's duration at the 2.4 GHz nominal clock (1024 SIMDs, 256 CUs), and HBM
+    bytes from FETCH_SIZE / WRITE_SIZE scaled by the calibration copy run first (--cell with --eager)."""
+    rows = []
+    for d in args.summarize_counters:
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        for fn in files:
+            with open(fn) as f:
+                rows += [dict(r, _dir=d) for r in csv.DictReader(f)]
+    # calibration: per directory, the largest FETCH_SIZE / WRITE_SIZE of a non-library dispatch before the
+    # first library dispatch (the CALIB_BYTES copy of --eager cell runs)
+    scale = {}
+    for d in args.summarize_counters:
+        first = min((int(r["Dispatch_Id"]) for r in rows if r["_dir"] == d and "bi::" in r["Kernel_Name"]), default=None)
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            per = {}
+            for r in rows:
+                if r["_dir"] == d and r["Counter_Name"] == c and "bi::" not in r["Kernel_Name"] and \
+                        (first is None or int(r["Dispatch_Id"]) < first):
+                    per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+            if per and max(per.values()) * 1024 > 0.5 * CALIB_BYTES:
+                scale[c] = CALIB_BYTES / (max(per.values()) * 1024)
     per = {}
-    for fn in files:
-        with open(fn) as f:
-            for r in csv.DictReader(f):
-                name = r["Kernel_Name"]
-                if args.kernel and not any(k in name for k in args.kernel):
-                    continue
-                d = per.setdefault(name, {}).setdefault(int(r["Dispatch_Id"]), {})
-                d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    for r in rows:
+        name = r["Kernel_Name"]
+        if args.kernel and not any(k in name for k in args.kernel):
+            continue
+        key = (name, int(r["Grid_Size"]))
+        disp = per.setdefault(key, {}).setdefault((r["_dir"], int(r["Dispatch_Id"])), {})
+        disp[r["Counter_Name"]] = disp.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        disp["_ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
     lines = [f"# {args.title}", "", "Commands (run from the repository root on one MI355X):", "", "```"] + args.cmd + \
-        ["```", "", "Counter values are per dispatch, averaged over the dispatches of each kernel (SQ counters "
-         "summed over the whole GPU).", ""]
-    for name, disp in sorted(per.items()):
-        names = sorted({c for d in disp.values() for c in d})
-        avg = {c: sum(d.get(c, 0.0) for d in disp.values()) / len(disp) for c in names}
+        ["```", "", "Counter values are per dispatch, averaged over the dispatches of each kernel and grid size (SQ "
+         "counters summed over the whole GPU).  Busy fractions divide by the dispatch's duration under counter "
+         "collection at the nominal 2.4 GHz clock and are estimates.", ""]
+    if scale:
+        lines += ["Calibration (a copy of %d bytes each way): " % CALIB_BYTES +
+                  ", ".join(f"{c} scale {v:.3f}" for c, v in sorted(scale.items())), ""]
+    for (name, grid), disp in sorted(per.items()):
+        names = sorted({c for dd in disp.values() for c in dd if not c.startswith("_")})
+        cnt = {c: [dd[c] for dd in disp.values() if c in dd] for c in names}
+        avg = {c: sum(v) / len(v) for c, v in cnt.items()}
+        ns = sorted(dd["_ns"] for dd in disp.values())[len(disp) // 2]
         short = name if len(name) < 100 else name[:97] + "..."
-        lines += [f"## `{short}`", "", f"{len(disp)} dispatches.", "", "| counter | per dispatch |", "|---|---:|"]
+        lines += [f"## `{short}`, grid {grid}", "", f"{max(len(v) for v in cnt.values())} dispatches per counter pass; "
+                  f"median duration under collection {ns / 1e3:.1f} us.", "", "| counter | per dispatch |", "|---|---:|"]
         lines += [f"| {c} | {avg[c]:.4g} |" for c in names]
         waves = avg.get("SQ_WAVES")
-        mfma = avg.get("SQ_INSTS_MFMA") or avg.get("SQ_INSTS_VALU_MFMA_BF16")
+        mfma = avg.get("SQ_INSTS_MFMA")
+        cyc = ns * 2.4
         derived = []
-        for c in ("SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_INSTS_MFMA", "SQ_INSTS_VALU_TRANS_F32",
-                  "SQ_INSTS_VMEM_RD"):
+        for c in ("SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_INSTS_MFMA", "SQ_INSTS_VALU_TRANS_F32"):
             if c in avg and waves:
                 derived.append(f"| {c} per wavefront | {avg[c] / waves:.1f} |")
             if c in avg and mfma and c != "SQ_INSTS_MFMA":
                 derived.append(f"| {c} per MFMA instruction | {avg[c] / mfma:.3f} |")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in avg and cyc:
+            derived.append(f"| matrix cores busy (SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs / cycles) | "
+                           f"{avg['SQ_VALU_MFMA_BUSY_CYCLES'] / 1024 / cyc:.3f} |")
+        if "SQ_ACTIVE_INST_VALU" in avg and cyc:
+            derived.append(f"| vector ALU issue (4 x SQ_ACTIVE_INST_VALU / 1024 SIMDs / cycles) | "
+                           f"{4 * avg['SQ_ACTIVE_INST_VALU'] / 1024 / cyc:.3f} |")
+        if "SQ_LDS_IDX_ACTIVE" in avg and cyc:
+            derived.append(f"| LDS busy (SQ_LDS_IDX_ACTIVE / 256 CUs / cycles) | {avg['SQ_LDS_IDX_ACTIVE'] / 256 / cyc:.3f} |")
+        if "SQ_WAIT_ANY" in avg and "SQ_WAVE_CYCLES" in avg:
+            derived.append(f"| wave time waiting (SQ_WAIT_ANY / SQ_WAVE_CYCLES) | {avg['SQ_WAIT_ANY'] / avg['SQ_WAVE_CYCLES']:.3f} |")
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            if c in avg and c in scale:
+                derived.append(f"| HBM {c.split('_')[0].lower()} MB (scaled) | {avg[c] * 1024 * scale[c] / 1e6:.2f} |")
         if derived:
             lines += ["", "| derived | value |", "|---|---:|"] + derived
         lines.append("")
@@ -1106,6 +1160,8 @@ def summarize_counters(args):
 
 
 def summarize_stats(args):
+    """The rocprofv3 kernel statistics as a table, plus (from the kernel trace beside them) the duration of
+    every library kernel by grid shape: the cells launch one kernel at several shapes."""
     with open(args.summarize_stats) as f:
         rows = list(csv.DictReader(f))
     lines = [f"# {args.title}", "", "Command (run from the repository root on one MI355X):", "", "```"] + \
@@ -1122,10 +1178,28 @@ def summarize_stats(args):
         lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                      f"{float(r['Percentage']):.1f} |")
+    trace = args.summarize_stats.replace("kernel_stats.csv", "kernel_trace.csv")
+    if trace != args.summarize_stats and os.path.exists(trace):
+        by = {}
+        with open(trace) as f:
+            for r in csv.DictReader(f):
+                if "bi::" not in r["Kernel_Name"]:
+                    continue
+                key = (r["Kernel_Name"], int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]),
+                       int(r["Workgroup_Size_X"]))
+                by.setdefault(key, []).append((float(r["End_Timestamp"]) - float(r["Start_Timestamp"])) / 1e3)
+        lines += ["", "Library kernels by launch shape (threads in the grid, workgroup size):", "",
+                  "| kernel | grid threads | workgroup | calls | median us | min us | p95 us |",
+                  "|---|---:|---:|---:|---:|---:|---:|"]
+        for (name, grid, wg), d in sorted(by.items(), key=lambda kv: (kv[0][0], kv[0][1])):
+            d.sort()
+            short = name.replace("|", "/")
+            short = short if len(short) <= 90 else short[:87] + "..."
+            lines.append(f"| `{short}` | {grid} | {wg} | {len(d)} | {d[len(d) // 2]:.2f} | {d[0]:.2f} | "
+                         f"{d[min(len(d) - 1, int(round(0.95 * (len(d) - 1))))]:.2f} |")
     with open(args.out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
-
 
 if __name__ == "__main__":
     main()
