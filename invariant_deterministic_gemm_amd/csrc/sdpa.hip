@@ -1719,6 +1719,85 @@ __global__ __launch_bounds__(D) void sdpa_combine(SdpaParams p) {
     store_from_f32<dt>(orow, d, r);
 }
 
+// The same fold for rows with many splits: one workgroup of 256 threads per query row stages the partials
+// of up to CHUNK splits in LDS, every load requested before any is used, and its first D threads fold them
+// in ascending split order while the next chunk's loads are in flight.  The fold is sdpa_combine's written
+// without branches: the empty state is m = -inf, l = o = 0, so a first partial enters through the ordinary
+// step (a = exp2(-inf) = 0, bs = exp2(0) = 1, hence l = ls and o = os, exactly) and an empty split's step is
+// computed and then discarded by a select.  The two forms give the same bits up to the sign of a zero o,
+// which the final o / l + 0 removes.  Without branches the eight steps of a group share one basic block, so
+// their exponentials overlap and only the max / fma chains are serial.
+template <int dt, int D, int CHUNK>
+__global__ __launch_bounds__(256) void sdpa_combine_lds(SdpaParams p) {
+    constexpr float NEG_INF = -__builtin_huge_valf();
+    constexpr int PER = CHUNK * D / 4 / 256;           // 16-byte loads of O partials per thread per chunk
+    static_assert(CHUNK * D % 1024 == 0 && 2 * CHUNK <= 256 && CHUNK % 8 == 0, "chunk layout");
+    __shared__ float sml[2 * CHUNK];
+    __shared__ __attribute__((aligned(16))) float so[CHUNK * D];
+    const int64_t rowid = blockIdx.x;
+    const int tid = threadIdx.x, d = tid;
+    const int iq = (int)(rowid % p.Lq);
+    const int h = (int)((rowid / p.Lq) % p.Hq);
+    const int b = (int)(rowid / ((int64_t)p.Lq * p.Hq));
+    const float *ml = p.ws_ml + rowid * p.nsplit * 2;
+    const float *po = p.ws_o + rowid * p.nsplit * D;
+
+    f32x4 v[PER];
+    float mlv;
+    auto fetch = [&](int s0) {
+        const int n = min(CHUNK, p.nsplit - s0);
+        const f32x4 *src = reinterpret_cast<const f32x4 *>(po + (int64_t)s0 * D);
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int i = tid + 256 * k;
+            v[k] = i < n * D / 4 ? src[i] : zero4();
+        }
+        mlv = tid < 2 * n ? ml[2 * s0 + tid] : NEG_INF;
+    };
+
+    // the sink is the fold's first partial
+    float m = p.sinks ? sink2(p, h) : NEG_INF, l = p.sinks ? 1.0f : 0.0f, o = 0.0f;
+    fetch(0);
+    for (int s0 = 0; s0 < p.nsplit; s0 += CHUNK) {
+        const int n = min(CHUNK, p.nsplit - s0);
+#pragma unroll
+        for (int k = 0; k < PER; ++k) reinterpret_cast<f32x4 *>(so)[tid + 256 * k] = v[k];
+        if (tid < 2 * CHUNK) sml[tid] = mlv;
+        __syncthreads();
+        if (s0 + CHUNK < p.nsplit) fetch(s0 + CHUNK);
+        if (d < D) {
+            for (int u0 = 0; u0 < n; u0 += 8) {
+                float ms[8], ls[8], os[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    ms[j] = sml[2 * (u0 + j)];             // -inf past the end: skipped like an empty split
+                    ls[j] = sml[2 * (u0 + j) + 1];
+                    os[j] = so[(u0 + j) * D + d];
+                }
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const bool skip = ms[j] == NEG_INF;     // split saw no key of this row
+                    const float m2 = fmaxf(m, ms[j]);
+                    const float a = exp2_hw(m - m2);
+                    const float bs = exp2_hw(ms[j] - m2);
+                    const float l2 = __builtin_fmaf(l, a, ls[j] * bs);
+                    const float o2 = __builtin_fmaf(o, a, os[j] * bs);
+                    l = skip ? l : l2;
+                    o = skip ? o : o2;
+                    m = m2;
+                }
+            }
+        }
+        __syncthreads();
+    }
+    if (d >= D) return;
+    char *orow = static_cast<char *>(p.o) +
+                 ((int64_t)b * p.os[0] + (int64_t)h * p.os[1] + (int64_t)iq * p.os[2]) * Elem<dt>::bytes;
+    float r = m != NEG_INF ? o / l : 0.0f;
+    r = r + 0.0f;                                  // -0 -> +0
+    store_from_f32<dt>(orow, d, r);
+}
+
 // Query chunks of at least this many rows against caches longer than four
 // splits take the workspace-free prefill kernel (measured: below ~300 rows the
 // split kernel's extra parallelism wins, above it the shared K / V blocks do).
@@ -1866,10 +1945,12 @@ static hipError_t launch_typed(const SdpaParams &p, hipStream_t st) {
         if (e != hipSuccess) return e;
     }
     const dim3 g2((unsigned)((int64_t)p.B * p.Hq * p.Lq));
-    // the same fold with fewer loads in flight for short caches (measured 0.5-1.3 us less at four splits)
+    // the same fold with fewer loads in flight for short caches (measured 0.5-1.3 us less at four splits),
+    // and through LDS, 64 KiB of partials per memory round trip, for long ones
     if (p.nsplit <= 4) hipLaunchKernelGGL((sdpa_combine<dt, D, 4>), g2, dim3(D), 0, st, p);
     else if (p.nsplit <= 8) hipLaunchKernelGGL((sdpa_combine<dt, D, 8>), g2, dim3(D), 0, st, p);
-    else hipLaunchKernelGGL((sdpa_combine<dt, D>), g2, dim3(D), 0, st, p);
+    else if (p.nsplit <= 16) hipLaunchKernelGGL((sdpa_combine<dt, D>), g2, dim3(D), 0, st, p);
+    else hipLaunchKernelGGL((sdpa_combine_lds<dt, D, (D <= 128 ? 128 : 64)>), g2, dim3(256), 0, st, p);
     return hipGetLastError();
 }
 

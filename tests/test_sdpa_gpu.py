@@ -523,3 +523,35 @@ def test_workspace_stays_bounded_for_long_calls():
         p = S3 - L3 + i
         dec = bi.bi_sdpa(q3[:, :, i:i + 1], k3[:, :, :p + 1], v3[:, :, :p + 1], causal=True)
         assert_bits_equal(o3[:, :, i:i + 1], dec, f"bf16 row {i} vs its decode")
+
+
+@pytest.mark.parametrize("dt", DTS, ids=_ids)
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_many_split_fold_matches_aligned_windows(dt, D):
+    """Decode rows over caches of 17 to 129 splits (the fold of many partials runs through LDS, 64 splits
+    at a time): a row whose visible keys all lie in a window starting at a multiple of 256 equals, bit
+    for bit, the same window called as a short cache of its own -- every split before and after it is
+    empty and skipped; the first visible split may sit in the second or third 64-split chunk.  With a
+    sink, and against the oracle."""
+    Hq, Hkv = 8, 2
+    S_max = 33000
+    q = synthetic.randn((1, Hq, 1, D), 0x5EEDD0 + D, 1.0, dt).to(DEV)
+    k = synthetic.randn((1, Hkv, S_max, D), 0x5EEDD1 + D, 1.0, dt).to(DEV)
+    v = synthetic.randn((1, Hkv, S_max, D), 0x5EEDD2 + D, 1.0, dt).to(DEV)
+    sinks = synthetic.randn((Hq,), 0x5EEDD3, 2.0).to(DEV)
+    for S, lo, hi in ((4097, 256, 700), (4352, 4096, 4352), (16385, 0, 300), (16385, 16384, 16385),
+                      (20000, 16384 + 100, 16384 + 500), (33000, 32768 - 256, 33000), (33000, 5000, 30000)):
+        w0 = lo // 256 * 256
+        m = torch.zeros(1, 1, 1, S, dtype=torch.bool, device=DEV)
+        m[..., lo:hi] = True
+        mw = m[..., w0:hi].contiguous()
+        for sk in (None, sinks):
+            o = bi.bi_sdpa(q, k[:, :, :S], v[:, :, :S], mask=m, sinks=sk)
+            ow = bi.bi_sdpa(q, k[:, :, w0:hi], v[:, :, w0:hi], mask=mw, sinks=sk)
+            assert_bits_equal(o, ow, f"{dt} D={D} S={S} keys [{lo}, {hi}) sinks={sk is not None}")
+    S, lo, hi = 33000, 5000, 30000
+    m = torch.zeros(1, 1, 1, S, dtype=torch.bool)
+    m[..., lo:hi] = True
+    o = bi.bi_sdpa(q, k[:, :, :S], v[:, :, :S], mask=m.to(DEV), sinks=sinks)
+    ref = oracle.sdpa(q.cpu(), k[:, :, :S].cpu(), v[:, :, :S].cpu(), mask=m, sinks=sinks.cpu())
+    assert_close_to_oracle(o.cpu(), ref, f"{dt} D={D} S={S}")
