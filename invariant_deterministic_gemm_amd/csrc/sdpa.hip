@@ -1197,43 +1197,6 @@ __device__ __forceinline__ void fold_split16(float &m_run, float &l_run, f32x4 (
     for (int t = 0; t < NT; ++t) o[t] = zero4();
 }
 
-// The V fragments of one 32-key half as attn_vfrags16<8> reads them (same addresses, same values), issued
-// from one asm block that also waits for them.  The compiler cannot tell a transposed LDS read from the
-// direct-to-LDS loads in flight into the other buffer and would otherwise wait for those loads before the
-// first read; here the loads stay in flight.  va[t]: LDS address of tile t's first row-0 read of half 0;
-// HOFF: byte offset of the half (+ 16 key rows for the second read of a tile).  Outputs are early-clobber
-// so no read can overwrite an address a later read of the block still needs.
-template <int HOFF>
-__device__ __forceinline__ void vfrags_tr_asm(const uint32_t (&va)[8], u32x4 (&vf)[8]) {
-    u32x2 lo[8], hi[8];
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %16 offset:%24\n\t"
-        "ds_read_b64_tr_b16 %8, %16 offset:%25\n\t"
-        "ds_read_b64_tr_b16 %1, %17 offset:%24\n\t"
-        "ds_read_b64_tr_b16 %9, %17 offset:%25\n\t"
-        "ds_read_b64_tr_b16 %2, %18 offset:%24\n\t"
-        "ds_read_b64_tr_b16 %10, %18 offset:%25\n\t"
-        "ds_read_b64_tr_b16 %3, %19 offset:%24\n\t"
-        "ds_read_b64_tr_b16 %11, %19 offset:%25\n\t"
-        "ds_read_b64_tr_b16 %4, %20 offset:%24\n\t"
-        "ds_read_b64_tr_b16 %12, %20 offset:%25\n\t"
-        "ds_read_b64_tr_b16 %5, %21 offset:%24\n\t"
-        "ds_read_b64_tr_b16 %13, %21 offset:%25\n\t"
-        "ds_read_b64_tr_b16 %6, %22 offset:%24\n\t"
-        "ds_read_b64_tr_b16 %14, %22 offset:%25\n\t"
-        "ds_read_b64_tr_b16 %7, %23 offset:%24\n\t"
-        "ds_read_b64_tr_b16 %15, %23 offset:%25\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(lo[0]), "=&v"(lo[1]), "=&v"(lo[2]), "=&v"(lo[3]), "=&v"(lo[4]), "=&v"(lo[5]), "=&v"(lo[6]),
-          "=&v"(lo[7]), "=&v"(hi[0]), "=&v"(hi[1]), "=&v"(hi[2]), "=&v"(hi[3]), "=&v"(hi[4]), "=&v"(hi[5]),
-          "=&v"(hi[6]), "=&v"(hi[7])
-        : "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), "v"(va[4]), "v"(va[5]), "v"(va[6]), "v"(va[7]),
-          "i"(HOFF), "i"(HOFF + 16 * 256)
-        : "memory");
-#pragma unroll
-    for (int t = 0; t < 8; ++t) vf[t] = u32x4{lo[t][0], lo[t][1], hi[t][0], hi[t][1]};
-}
-
 // sdpa_combine's step when every row's split partial is non-empty (m_run finite): the rescaled sum, with no
 // branch.  A running state that is still empty (mt = -inf, lt = 0, ot = 0) takes the partial itself, as
 // the combine's copy does: a = exp2(-inf) = 0 and bs = 1 give lt = l_run and ot = o, except that a zero of
@@ -1277,23 +1240,23 @@ __device__ __forceinline__ void dma16_vaddr(const char *src, uint32_t lds_addr) 
 }
 __device__ __forceinline__ void asm_wait_vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// The V fragments of one 32-key half as attn_vfrags16<8> reads them: va[t] is the LDS address of tile t's
-// first row-0 read of half 0 in the buffer, HOFF the byte offset of the half (+ 16 key rows for the second
-// read of a tile).
+// The V fragments of one 32-key half as attn_vfrags16 reads them, for output column tiles t < NT: va[t] is
+// the LDS address of tile t's first row-0 read of half 0 in the buffer, HOFF the byte offset of the half
+// (+ 16 key rows for the second read of a tile).
 __device__ __forceinline__ u32x2 lds_tr16_at(uint32_t addr) {
     const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(size_t)addr);
     return __builtin_bit_cast(u32x2, v);
 }
-template <int HOFF>
-__device__ __forceinline__ void vfrags_tr(const uint32_t (&va)[8], u32x4 (&vf)[8]) {
+template <int HOFF, int NT>
+__device__ __forceinline__ void vfrags_tr(const uint32_t (&va)[NT], u32x4 (&vf)[NT]) {
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
+    for (int t = 0; t < NT; ++t) {
         const u32x2 lo = lds_tr16_at(va[t] + HOFF), hi = lds_tr16_at(va[t] + HOFF + 16 * 256);
         vf[t] = u32x4{lo[0], lo[1], hi[0], hi[1]};
     }
 }
 
-// Long prefill (rows of 128, or zero-padded to 128 when PAD), software-pipelined over key blocks.  W row
+// Long prefill for 16-bit head dims D = 32, 64, 96, 128, software-pipelined over key blocks.  W row
 // tiles of one (batch, KV head), one per wavefront, share each K and V block through LDS; K runs two
 // blocks ahead and V one: while block j's softmax runs, block j + 1's scores are formed from its K block
 // on the matrix cores, and the loads of K(j + 2) and V(j + 1) are in flight.  Per tile the arithmetic is
@@ -1302,10 +1265,15 @@ __device__ __forceinline__ void vfrags_tr(const uint32_t (&va)[8], u32x4 (&vf)[8
 // state, so every row gets the bits of the split + combine path.  Splits whose blocks every row of the
 // workgroup sees completely (no mask, inside S, before the first row's causal position) run a
 // branch-free body: visibility known, rescale by alpha always (O * 1 = O), the fold without its
-// empty-partial cases.  Causal workgroups start longest first.
-template <int dt, int W, bool PAD>
+// empty-partial cases.  Causal workgroups start longest first.  Below D = 128 the kernel takes only the
+// head dim's D / 32 score chunks and D / 16 output column tiles (the LDS rows keep the 256-byte layout;
+// chunks at d >= D are neither loaded nor read), which are the split kernel's chains for that D.
+template <int dt, int W, int D>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2)))
 void sdpa_prefill16p(SdpaParams p) {
+    constexpr int NC = D / 32;                         // d chunks of the score chains
+    constexpr int NT = D / 16;                         // output column tiles
+    static_assert(D % 32 == 0 && D <= 128, "head dims 32, 64, 96, 128");
     constexpr int ROWB = 256;
     constexpr int KBYTES = KV_BLOCK * ROWB;            // one K or V block
     constexpr int QW = KBYTES / 1024 / W;              // 1 KiB loads per wavefront per K (or V) block
@@ -1351,31 +1319,30 @@ void sdpa_prefill16p(SdpaParams p) {
     static_assert((4 * W) % 16 == 0, "row period of the chunk swizzles");
     const int row0 = 4 * wave + lrow;
     const int ck = lslot ^ (row0 & 15), cv = lslot ^ ((row0 & 7) << 1);
-    const bool kz = PAD && 8 * ck >= p.dr, vz = PAD && 8 * cv >= p.dr;   // PAD: chunk at d >= D: zero page
+    const bool kin = 8 * ck < D, vin = 8 * cv < D;     // this lane's chunk lies inside the head dim
     const uint32_t koff = (uint32_t)(row0 * kstr) + (ck << 4), voff = (uint32_t)(row0 * vstr) + (cv << 4);
-    const char *zp = reinterpret_cast<const char *>(g_zero_page);
     auto issue = [&](int blk, char *buf, bool isv) {
         const int kb = blk * KV_BLOCK;
         const char *base = isv ? vbase : kbase;
         const int64_t str = isv ? vstr : kstr;
         const uint32_t lbase = (uint32_t)(uintptr_t)BI_LDS_PTR(buf) + wave * 1024;
-        if (!PAD && off32 && kb + KV_BLOCK <= p.S) {
+        if (D == 128 || (isv ? vin : kin)) {
+            if (off32 && kb + KV_BLOCK <= p.S) {
 #pragma unroll
-            for (int j = 0; j < QW; ++j)
-                dma16_saddr(base + (int64_t)(kb + 4 * W * j) * str, isv ? voff : koff, lbase + W * j * 1024);
-        } else {
+                for (int j = 0; j < QW; ++j)
+                    dma16_saddr(base + (int64_t)(kb + 4 * W * j) * str, isv ? voff : koff, lbase + W * j * 1024);
+            } else {
 #pragma unroll
-            for (int j = 0; j < QW; ++j) {
-                const int row = row0 + 4 * W * j;
-                const int64_t key = min(kb + row, p.S - 1);
-                const char *src = base + key * str + ((isv ? cv : ck) << 4);
-                if constexpr (PAD) src = (isv ? vz : kz) ? zp : src;
-                dma16_vaddr(src, lbase + W * j * 1024);
+                for (int j = 0; j < QW; ++j) {
+                    const int row = row0 + 4 * W * j;
+                    const int64_t key = min(kb + row, p.S - 1);
+                    dma16_vaddr(base + key * str + ((isv ? cv : ck) << 4), lbase + W * j * 1024);
+                }
             }
         }
     };
 
-    Rows16 r;
+    Rows16T<NC> r;
     rows16_load<dt>(p, tile, b, gk, r);
     // running fold over splits (per score row in lane r16; empty: mt = -inf, lt = 0) and the current
     // split's state; the sink, if any, is the fold's first partial
@@ -1388,46 +1355,46 @@ void sdpa_prefill16p(SdpaParams p) {
         have = true;
     }
     float m_run = NEG_INF, l_run = 0.0f;
-    f32x4 o[8], ot[8];
+    f32x4 o[NT], ot[NT];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
+    for (int t = 0; t < NT; ++t) {
         o[t] = zero4();
         ot[t] = zero4();
     }
     // per-lane LDS addresses of the V reads (attn_vfrags16's row-0 address of tile t, half 0) in buffer 0;
     // buffer 1 is KBYTES further
-    uint32_t va[8];
+    uint32_t va[NT];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
+    for (int t = 0; t < NT; ++t) {
         const int row0 = 4 * g + (r16 >> 2);
         const int ch = 2 * t + ((r16 & 3) >> 1);
         const uint32_t off = (uint32_t)(row0 * ROWB + ((ch ^ ((row0 & 7) << 1)) << 4) + 8 * (r16 & 1));
         va[t] = (uint32_t)(uintptr_t)BI_LDS_PTR(vbufs) + off;
     }
-    // scores of a block from its K block: each key tile's chain takes d chunks 0 .. 3 in order
+    // scores of a block from its K block: each key tile's chain takes d chunks 0 .. NC - 1 in order
     auto scores = [&](const char *Ks, f32x4 (&st)[4]) {
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
-            u32x4 kf[4];
+            u32x4 kf[NC];
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
+            for (int c = 0; c < NC; ++c)
                 kf[c] = *reinterpret_cast<const u32x4 *>(Ks + (16 * kt + r16) * ROWB + (((4 * c + g) ^ r16) << 4));
             st[kt] = zero4();
 #pragma unroll
-            for (int c = 0; c < 4; ++c) st[kt] = Mfma<dt>::step(kf[c], r.qf[c], st[kt]);
+            for (int c = 0; c < NC; ++c) st[kt] = Mfma<dt>::step(kf[c], r.qf[c], st[kt]);
         }
     };
     // the V fragments of V buffer VB (both 32-key halves), and O += P . V from them
-    auto vread = [&](auto vb, u32x4 (&vf)[2][8]) {
+    auto vread = [&](auto vb, u32x4 (&vf)[2][NT]) {
         constexpr int VB = decltype(vb)::value;
         vfrags_tr<VB * KBYTES>(va, vf[0]);
         vfrags_tr<VB * KBYTES + 32 * ROWB>(va, vf[1]);
     };
-    auto pv = [&](const u32x4 (&pf)[2], const u32x4 (&vf)[2][8]) {
+    auto pv = [&](const u32x4 (&pf)[2], const u32x4 (&vf)[2][NT]) {
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
-            for (int t = 0; t < 8; ++t) o[t] = Mfma<dt>::step(pf[c], vf[c][t], o[t]);
+            for (int t = 0; t < NT; ++t) o[t] = Mfma<dt>::step(pf[c], vf[c][t], o[t]);
     };
 
     using VB0 = std::integral_constant<int, 0>;
@@ -1456,8 +1423,8 @@ void sdpa_prefill16p(SdpaParams p) {
         top(j, kfree, vnext, vcur);
         scores(knext, st_nxt);
         u32x4 pf[2];
-        attn_softmax16<dt, 4, 8, true, true>(p, r, st_cur, j * KV_BLOCK, m_run, l_run, o, pf);
-        u32x4 vf[2][8];
+        attn_softmax16<dt, NC, NT, true, true>(p, r, st_cur, j * KV_BLOCK, m_run, l_run, o, pf);
+        u32x4 vf[2][NT];
         vread(vb, vf);
         pv(pf, vf);
 #pragma unroll
@@ -1468,7 +1435,7 @@ void sdpa_prefill16p(SdpaParams p) {
         if (j + 1 < nblk) scores(knext, st_nxt);
         u32x4 pf[2];
         attn_softmax16<dt>(p, r, st_cur, j * KV_BLOCK, m_run, l_run, o, pf);
-        u32x4 vf[2][8];
+        u32x4 vf[2][NT];
         vread(vb, vf);
         pv(pf, vf);
 #pragma unroll
@@ -1510,10 +1477,10 @@ void sdpa_prefill16p(SdpaParams p) {
         char *orow = static_cast<char *>(p.o) +
                      ((int64_t)b * p.os[0] + (int64_t)h * p.os[1] + (int64_t)iq * p.os[2]) * Elem<dt>::bytes;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
+        for (int t = 0; t < NT; ++t) {
             float v = have_i ? ot[t][i] / l_i : 0.0f;
             v = v + 0.0f;                                // -0 -> +0
-            if (!PAD || 16 * t < p.dr) store_from_f32<dt>(orow, 16 * t + r16, v);
+            store_from_f32<dt>(orow, 16 * t + r16, v);
         }
     }
 }
@@ -1892,8 +1859,7 @@ static hipError_t launch_typed(const SdpaParams &p, hipStream_t st) {
             constexpr int W = 4;                         // row tiles (one per wavefront) sharing each K / V block
             const int64_t nwg = (int64_t)(((R + 15) / 16 + W - 1) / W) * p.B * p.Hkv;
             if (nwg > INT32_MAX) return hipErrorInvalidConfiguration;
-            if (D == 128) hipLaunchKernelGGL((sdpa_prefill16p<dt, W, false>), dim3((unsigned)nwg), dim3(64 * W), 0, st, p);
-            else hipLaunchKernelGGL((sdpa_prefill16p<dt, W, true>), dim3((unsigned)nwg), dim3(64 * W), 0, st, p);
+            hipLaunchKernelGGL((sdpa_prefill16p<dt, W, D>), dim3((unsigned)nwg), dim3(64 * W), 0, st, p);
             return hipGetLastError();
         }
         if (path == SDPA_FUSED16) {

@@ -8,13 +8,16 @@
 * invariance on raw bit patterns across batch size and batch neighbours;
 * shapes with ragged N, a partial last stage of the K loop, every bit width and group size, and both paths
   (up to 64 rows: unpacked inside the kernel's K loop; more: dequantised by chunks into a workspace
-  for bi_linear's kernels), whose rows must agree bit for bit.
+  for bi_linear's kernels), whose rows must agree bit for bit;
+* scale / bias rows padded past K / group_size (through the C ABI), and scales of 2^118 and 2^119 beside
+  ordinary ones.
 """
 import numpy as np
 import pytest
 import torch
 
 import invariant_deterministic_gemm_amd as bi
+from invariant_deterministic_gemm_amd import _native
 import oracle
 import synthetic
 from helpers import assert_bits_equal, assert_close_to_oracle
@@ -45,6 +48,9 @@ CASES = [  # M, N, K, bits, gs
     # wide N (more than 256 strips of 16 columns): two strips per workgroup, ragged last pair
     (2, 4200, 512, 4, 64), (16, 4113, 288, 8, 32), (17, 5000, 384, 2, 128), (40, 4500, 640, 4, 32),
     (64, 4104, 256, 8, 64),
+    # few rows of 4-bit weights at every group size, ragged N, K past a 1024-k boundary
+    (3, 1000, 1024, 4, 32), (4, 300, 1280, 4, 128), (2, 4113, 2048, 4, 64), (4, 4096, 4096, 4, 64),
+    (1, 16, 256, 4, 32),
 ]
 
 
@@ -117,3 +123,50 @@ def test_graph_replay_equals_eager(M):
         assert_bits_equal(out, eager, f"M={M}: graph replay {rep}")
         fn()
         torch.cuda.synchronize()
+
+
+def _qlinear_raw(x, wq, sc, sb, ldsb, gs, N, K):
+    """bi_quantized_linear through the C ABI with an explicit scale / bias row pitch (4-bit, bf16)."""
+    lib = _native.load()
+    M = x.shape[0]
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    st = lib.bi_quantized_linear(x.data_ptr(), x.stride(0), wq.data_ptr(), wq.stride(0), sc.data_ptr(),
+                                 sb.data_ptr(), ldsb, 4, gs, None, y.data_ptr(), N, M, N, K, _native.BI_BF16,
+                                 None, 0, torch.cuda.current_stream().cuda_stream)
+    assert st == _native.BI_OK, lib.bi_last_error().decode()
+    return y
+
+
+def test_padded_scale_rows_and_huge_scales():
+    """Few rows of 4-bit weights, equal bit for bit to bi_linear on the host's dequantised weight: (a)
+    scale / bias rows padded to 8 entries for 3 groups (K = 96, a partial stage); (b) groups whose scale
+    is 2^119 or 2^118 beside ordinary ones, with x small on those groups so every product stays finite."""
+    dt = torch.bfloat16
+    N, K, gs = 50, 96, 32
+    wq, sc, sb = make(N, K, 4, gs, dt, 7)
+    scp = torch.zeros((N, 8), dtype=dt)
+    sbp = torch.zeros((N, 8), dtype=dt)
+    scp[:, :3] = sc
+    sbp[:, :3] = sb
+    wd = host_dequant(wq, sc, sb, 4, gs, K, dt).to(DEV)
+    for M in (1, 3, 4):
+        x = synthetic.randn((M, K), 8 + M, 1.0, dt).to(DEV)
+        y = _qlinear_raw(x, wq.to(DEV), scp.to(DEV), sbp.to(DEV), 8, gs, N, K)
+        assert_bits_equal(y, bi.bi_linear(x, wd), f"padded scale rows, M={M}")
+    N, K, gs = 64, 1024, 64
+    wq, sc, sb = make(N, K, 4, gs, dt, 11)
+    sc, sb = sc.clone(), sb.clone()
+    sc[0::2, 1] = 2.0 ** 119
+    sb[0::2, 1] = 0.0
+    sc[0::3, 9] = 2.0 ** 118
+    sb[0::3, 9] = 1.0
+    x = synthetic.randn((4, K), 12, 1.0, dt)
+    x[:, 64:128] *= 2.0 ** -124
+    x[:, 576:640] *= 2.0 ** -123
+    wd = host_dequant(wq, sc, sb, 4, gs, K, dt).to(DEV)
+    for M in (1, 2, 4):
+        xm = x[:M].contiguous().to(DEV)
+        y = bi.bi_quantized_linear(xm, wq.to(DEV), sc.to(DEV), sb.to(DEV), 4, gs)
+        ref = bi.bi_linear(xm, wd)
+        assert torch.isfinite(ref.float()).all()
+        assert_bits_equal(y, ref, f"scales of 2^118 and 2^119, M={M}")

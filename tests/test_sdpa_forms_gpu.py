@@ -163,17 +163,19 @@ def test_head_dims_multiple_of_32(dt, D):
     assert_bits_equal(z, round_ref(oracle.sdpa(q0, k[:1], vi, causal=True), dt), f"D={D}: zero-query means")
 
 
-@pytest.mark.parametrize("D", [64, 96])
+@pytest.mark.parametrize("D", [32, 64, 96])
 @pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16], ids=_ids)
 def test_small_head_dims_agree_across_kernels(dt, D):
-    """16-bit D < 128: the prefill, quad and one-launch kernels run on rows zero-padded to 128, the
-    generic split kernel on the real rows; the zero products only add exact zeros, so every path gives
-    the same bits.  Prefill chunk (prefill kernel) vs the decode of its tokens (quad kernel), and one
-    batch element alone (quad kernel) vs inside a batch of 40 (one launch at S <= 1024, the generic
-    split kernel above)."""
+    """16-bit D < 128: the prefill kernel and the generic split kernel take the head dim's own D / 32
+    score chunks and D / 16 output tiles, the quad and one-launch kernels run on rows zero-padded to 128
+    (the zero products only add exact zeros), so every path gives the same bits.  Prefill chunk (prefill
+    kernel) vs the decode of its tokens (quad kernel) and vs the oracle, a masked prefill vs the same
+    rows called few at a time (split kernel), and one batch element alone (quad kernel) vs inside a
+    batch of 40 (one launch at S <= 1024, the generic split kernel above)."""
     B, Hq, Hkv, Lq, S = 1, 8, 2, 400, 1500
     BI = bi.BI_BF16 if dt == torch.bfloat16 else bi.BI_F16
-    q, k, v = _gpu(*_qkv(B, Hq, Hkv, Lq, S, D, dt, 370 + D))
+    qc, kc, vc = _qkv(B, Hq, Hkv, Lq, S, D, dt, 370 + D)
+    q, k, v = _gpu(qc, kc, vc)
     lib = bi._native.load()
     name = lambda *a: lib.bi_sdpa_kernel_name(*a, D, BI).decode()
     assert name(B, Hq, Hkv, Lq, S) == "sdpa_prefill16"
@@ -183,6 +185,16 @@ def test_small_head_dims_agree_across_kernels(dt, D):
         assert name(B, Hq, Hkv, 1, p + 1) == "sdpa_quad16+combine"
         dec = bi.bi_sdpa(q[:, :, i:i + 1], k[:, :, :p + 1], v[:, :, :p + 1], causal=True)
         assert_bits_equal(dec[:, :, 0], full[:, :, i], f"D={D}: prefill token {i} vs its quad-kernel decode")
+    rows = slice(390, 400)
+    ref = oracle.sdpa(qc[:, :, rows], kc[:, :, :S - Lq + 400], vc[:, :, :S - Lq + 400], causal=True)
+    assert_close_to_oracle(full[:, :, rows], ref, f"D={D} prefill rows 390-399")
+    gen = torch.Generator(device="cpu").manual_seed(380 + D)
+    mask = (torch.rand((1, 1, Lq, S), generator=gen) > 0.2).to(DEV)
+    masked = bi.bi_sdpa(q, k, v, mask=mask)
+    for a in (0, 200, 396):
+        assert name(B, Hq, Hkv, 4, S) != "sdpa_prefill16"
+        part = bi.bi_sdpa(q[:, :, a:a + 4], k, v, mask=mask[:, :, a:a + 4])
+        assert_bits_equal(part, masked[:, :, a:a + 4], f"D={D}: masked prefill rows {a}.. vs four at a time")
     for S2, big_kernel in ((900, "sdpa_fused16"), (1500, "sdpa_split+combine")):
         qd, kd, vd = q[:, :, :2], k[:, :, :S2], v[:, :, :S2]
         assert name(1, Hq, Hkv, 2, S2) == "sdpa_quad16+combine" and name(40, Hq, Hkv, 2, S2) == big_kernel
