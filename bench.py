@@ -450,9 +450,11 @@ def _cell(ctx, t, **fields):
 
 def cell_ceilings(ctx):
     """What this GPU measurably sustains: a streaming read of 1 GiB (every byte once; best of 1, 2 and 4
-    workgroups of 256 threads per CU, and the same read of 32 MiB / 112 MiB, the decode weights of
-    N = 4096 / 14336, as single launches) and an MFMA-only loop (8 independent bf16 16x16x32 chains per
-    wavefront, 1 and 2 workgroups of 4 wavefronts per CU)."""
+    workgroups of 256 threads per CU), the same read of 32 MiB / 112 MiB (the decode weights of N = 4096 /
+    14336 at K = 4096) as single launches, once from one buffer read again and again (it stays in the
+    last-level cache: "hot") and once rotating through copies of at least 512 MiB as the decode cells do
+    ("cold"), and an MFMA-only loop (8 independent bf16 16x16x32 chains per wavefront, 1 and 2 workgroups
+    of 4 wavefronts per CU)."""
     torch, lib = ctx.torch, ctx.lib
     sink = torch.zeros(256 * 8 * 256, dtype=torch.int32, device=ctx.dev)
 
@@ -460,22 +462,30 @@ def cell_ceilings(ctx):
         return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     out = {}
     best = None
-    for nb in (2 ** 30, 32 * 2 ** 20, 112 * 2 ** 20):
-        src = torch.empty(nb // 4, dtype=torch.int32, device=ctx.dev).random_(0, 2 ** 30)
+    for nb, cold in ((2 ** 30, False), (32 * 2 ** 20, False), (112 * 2 ** 20, False), (32 * 2 ** 20, True),
+                     (112 * 2 ** 20, True)):
+        srcs = [torch.empty(nb // 4, dtype=torch.int32, device=ctx.dev).random_(0, 2 ** 30)
+                for _ in range(rotation(nb) if cold else 1)]
         for wpc in ((1, 2, 4) if nb == 2 ** 30 else (4,)):
-            fn = (lambda src=src, wpc=wpc: _chk(lib.bi_measure_stream_read(ctypes.c_void_p(src.data_ptr()), nb,
-                                                                          ctypes.c_void_p(sink.data_ptr()),
-                                                                          256 * wpc, stream())))
-            t = _time_graph(torch, fn, reps=4 if nb == 2 ** 30 else 20, samples=min(ctx.samples, 100), keep=False)
+            it = iter(range(10 ** 9))
+
+            def fn(wpc=wpc):
+                src = srcs[next(it) % len(srcs)]
+                _chk(lib.bi_measure_stream_read(ctypes.c_void_p(src.data_ptr()), nb, ctypes.c_void_p(sink.data_ptr()),
+                                                256 * wpc, stream()))
+            reps = 4 if nb == 2 ** 30 else (2 * len(srcs) if cold else 20)
+            t = _time_graph(torch, fn, reps=reps, samples=min(ctx.samples, 100), keep=False)
             gbps = nb / (t["us"] * 1e-6) / 1e9
             rec = {"bytes": nb, "workgroups_per_cu": wpc, "us": t["us"], "p95_us": t["p95_us"], "GBps": round(gbps, 1),
                    "frac_hbm": round(gbps / HBM_PEAK_GBPS, 4)}
+            if cold:
+                rec["rotated_copies"] = len(srcs)
             if nb == 2 ** 30:
                 if best is None or gbps > best["GBps"]:
                     best = rec
             else:
-                out[f"stream_read_{nb >> 20}MiB"] = rec
-        del src
+                out[f"stream_read_{'cold' if cold else 'hot'}_{nb >> 20}MiB"] = rec
+        del srcs
     out["hbm_stream_read"] = best
     mbest = None
     for wpc in (1, 2):
@@ -520,8 +530,11 @@ def cell_decode_gemm(ctx):
             t = _time_graph(torch, fn, reps=len(ws) * 2, samples=ctx.samples)
             nbytes = 2.0 * (M * K + N * K + M * N)
             gbps = nbytes / (t["us"] * 1e-6) / 1e9
+            same = (ctx.ceil or {}).get(f"stream_read_cold_{(N * K * 2) >> 20}MiB")
             res.append(_cell(ctx, t, M=M, N=N, GBps=round(gbps, 1), frac_hbm=round(gbps / HBM_PEAK_GBPS, 4),
-                             frac_ceiling=ctx.frac(gbps, "hbm"), rotated_copies=len(ws),
+                             frac_ceiling=ctx.frac(gbps, "hbm"),
+                             frac_cold_read_same_bytes=round(gbps / same["GBps"], 4) if same else None,
+                             rotated_copies=len(ws),
                              kernel=ctx.lib.bi_gemm_kernel_name(M, N, K, bi.BI_BF16, 0).decode()))
     del wls, wl
     return res
