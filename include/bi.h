@@ -350,10 +350,11 @@ bi_status bi_rowsum(const void *x, int64_t ldx, void *y, int64_t M, int64_t N, i
  * M == 0 or N == 0 enqueues nothing; K == 0 writes the bias (or zeros).
  * ws: bi_quantized_linear_workspace_bytes(M, N, K, dt) bytes of 256-byte
  * aligned device memory, or NULL when that is 0 (M <= 64: the weights are
- * unpacked inside the kernel's K loop).  Above 64 rows, chunks of at most 8192
- * columns are dequantised into ws with the same arithmetic and bi_linear's
- * kernels run on them; the result is the same bits either way.  Too small a
- * workspace is refused with BI_ERR_WORKSPACE.
+ * unpacked inside the strip kernel's K loop; more rows with K a multiple of
+ * 128: inside the tile kernel, on their way into LDS).  Above 64 rows with
+ * other K, chunks of at most 8192 columns are dequantised into ws with the
+ * same arithmetic and bi_linear's kernels run on them; the result is the same
+ * bits in every case.  Too small a workspace is refused with BI_ERR_WORKSPACE.
  */
 bi_status bi_quantized_linear(const void *x, int64_t ldx,
                               const uint32_t *wq, int64_t ldwq,
@@ -398,7 +399,8 @@ const char *bi_status_name(bi_status s);
 const char *bi_last_error(void);
 /* (ABI major << 16) | bits version.  The bits version changes whenever a
  * compile-time constant that shapes the arithmetic (k-group order, KV block
- * and split sizes) changes, i.e. whenever output bits may change. */
+ * and split sizes) or a rounding step changes, i.e. whenever output bits may
+ * change. */
 int bi_abi_version(void);
 
 #ifdef __cplusplus

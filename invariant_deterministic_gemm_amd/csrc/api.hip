@@ -31,7 +31,9 @@ constexpr int kAbiMajor = 2;
 // Bump when a compile-time constant that shapes arithmetic changes
 // (k-step order, MFMA shapes, KV_SPLIT / KV_BLOCK, combine order).
 // 3: 16-bit GEMM chain on v_mfma_f32_16x16x32 again (2 used 32x32x16).
-constexpr int kBitsVersion = 3;
+// 4: fp16 results (GEMM outputs, dequantised fp16 weights) rounded from the fp32 fmaf result in every
+//    kernel (some had fused the fmaf with the conversion and rounded once).
+constexpr int kBitsVersion = 4;
 
 thread_local std::string g_last_error;
 

@@ -38,8 +38,12 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
     u += 0x7fffu + ((u >> 16) & 1u);
     return u >> 16;
 }
-// v_cvt_f16_f32 in the default round-to-nearest-even mode.
+// v_cvt_f16_f32 in the default round-to-nearest-even mode, of the value f as an fp32 number.  The empty asm
+// hides where f came from: the compiler would otherwise fuse an fmaf producing f with this conversion into
+// one v_fma_mixlo_f16, which rounds the exact sum once to fp16 instead of to fp32 and then to fp16, and
+// does so in some kernels and not in others (their outputs then differ in rare elements).
 __device__ __forceinline__ uint32_t f32_to_f16(float f) {
+    asm("" : "+v"(f));
     return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
 }
 

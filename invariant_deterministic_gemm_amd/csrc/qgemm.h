@@ -20,15 +20,17 @@ struct QGemmParams {
     int group_shift;        // log2(group_size), set by the launcher
 };
 
-// Rows up to this many run the fused kernel; more rows dequantise chunks of at most QGEMM_CHUNK_N
-// columns into a workspace and run the tile GEMM kernels on them.
+// Rows up to this many run the strip kernel; more rows run the tile kernel, which dequantises the weight
+// tiles on their way into LDS, when K is a multiple of QGEMM_TILE_K, else dequantise chunks of at most
+// QGEMM_CHUNK_N columns into a workspace and run the tile GEMM kernels on them.
 constexpr int64_t QGEMM_FUSED_MAX_M = 64;
+constexpr int64_t QGEMM_TILE_K = 128;
 constexpr int64_t QGEMM_CHUNK_N = 8192;
 // Up to this many rows the fused kernel's consumer loads x itself (x in registers, not LDS).
 constexpr int64_t QGEMM_XREG_MAX_M = 1;
 // Above this many 16-column strips a workgroup of the fused kernel takes two strips (x read half as often).
 constexpr int64_t QGEMM_WIDE_STRIPS = 256;
-bool qgemm_uses_workspace(int64_t M);
+bool qgemm_uses_workspace(int64_t M, int64_t K);
 size_t qgemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 // ws: qgemm_workspace_bytes(M, N, K) bytes of device memory (unused, may be null, when that is 0).

@@ -30,7 +30,10 @@
 // bits; the choice of path depends on M only as a tile choice does).
 #include "device.h"
 #include "gemm_common.h"
+#include "gemm16_store.h"
 #include "qgemm.h"
+
+#include <type_traits>
 
 namespace bi {
 
@@ -46,7 +49,7 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 template <int dt> __device__ __forceinline__ uint32_t round_pack(float lo, float hi) {
     if constexpr (dt == DT_BF16) return __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)lo, (__bf16)hi});
-    else return __builtin_bit_cast(uint32_t, f16x2_t{(_Float16)lo, (_Float16)hi});
+    else return f32_to_f16(lo) | f32_to_f16(hi) << 16;        // each rounded from its fp32 value
 }
 template <int dt> __device__ __forceinline__ float half_to_f32(uint32_t h) {
     if constexpr (dt == DT_BF16) return bf16_to_f32(h);
@@ -409,6 +412,240 @@ __global__ __launch_bounds__(64 * (NB + 4)) void qgemm16_strip(QGemmParams q) {
     }
 }
 
+// More rows (M > 64, K a multiple of 128): the tile scheme of bi_linear's mid-M kernel (LDS stages of KS
+// k with 2 KS-byte rows, chunk c of row r at slot c ^ swz(r), fragments read DR chain steps ahead, one
+// barrier per stage whose buffer refill lags a stage behind) with the weight rows dequantised on their way
+// into LDS.  x arrives by direct-to-LDS loads as in the 16-bit kernel.  For its share of a stage's weight
+// rows, each thread owns one 16-byte chunk (8 values) per piece: direct-to-LDS loads bring the chunk's
+// packed words, scale and bias into a small staging area of its own, R stages ahead; when the stage's
+// buffer is handed over the thread reads them back, unpacks them with the arithmetic of the kernels above
+// and writes the chunk where the 16-bit kernel's direct-to-LDS load would have put it.  No load returns a
+// register and the loads are issued as asm, so every wait is one of the kernel's own counted waits.  The MFMA side is the 16-bit kernel's:
+// every element is bi_linear's chain on the dequantised weight.  No workspace.
+// Direct-to-LDS loads written as asm (M0 = the wave-uniform LDS address; lane L's 16 bytes at M0 + 16 L,
+// its 4 or 2 bytes at M0 + 4 L):
+// the compiler then neither reorders them nor adds waits of its own for them (it would wait for every
+// such load in flight before the next LDS read).  The kernel counts them itself; they write no register.
+__device__ __forceinline__ void qdma16(const void *src, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(src) : "memory", "m0");
+}
+__device__ __forceinline__ void qdma4(const void *src, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(src) : "memory", "m0");
+}
+__device__ __forceinline__ void qdma2(const void *src, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_ushort %1, off" ::"s"(lds), "v"(src) : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void *p) { return (uint32_t)(uintptr_t)BI_LDS_PTR(p); }
+
+template <int KS> __device__ __forceinline__ int qtile_swz(int row) {
+    if constexpr (KS == 128) return row & 15;
+    else return (row >> 1) & 7;
+}
+constexpr int qtile_gcd(int a, int b) { return b == 0 ? a : qtile_gcd(b, a % b); }
+
+template <int dt, int BITS, int BM, int BN, int WGM, int WGN, int NS, int KS, int DR>
+__global__ __launch_bounds__(64 * WGM * WGN) void qgemm16_tile(QGemmParams q) {
+    const GemmParams &p = q.g;
+    constexpr int NW = WGM * WGN;
+    constexpr int WM = BM / WGM, WN = BN / WGN;
+    constexpr int FM = WM / 16, FN = WN / 16;
+    constexpr int ROWB = 2 * KS, CPR = KS / 8, RPI = 64 / CPR;
+    constexpr int STAGE = (BM + BN) * ROWB;
+    constexpr int QA = BM / RPI, QB = BN / RPI;          // 1 KiB pieces of a stage: x rows, weight rows
+    constexpr int QAW = QA / NW, QBW = QB / NW;          // per wavefront
+    constexpr int SPS = KS / 32;                         // chain steps per stage
+    constexpr int NSET = DR + 1;
+    constexpr int R = NS - 2;                            // stages of packed weights staged ahead
+    constexpr int U = NSET * R * SPS / qtile_gcd(NSET, R * SPS);   // steps per unrolled iteration
+    constexpr int WPC = BITS == 8 ? 2 : 1;               // packed words per 8-value chunk
+    constexpr int L = QAW + QBW * (WPC + 2);             // loads a wavefront issues per stage
+    constexpr int PIECE = 64 * 4 * (WPC + 2);            // staging bytes of one piece: words, scales, biases
+    constexpr int SSTAGE = NW * QBW * PIECE;             // staging bytes of one stage
+    static_assert(KS == 64 || KS == 128, "stage width");
+    static_assert(WM % 16 == 0 && WN % 16 == 0 && QA % NW == 0 && QB % NW == 0, "tile geometry");
+    static_assert(NS >= 3 && L * (NS - 2) <= 63, "vmcnt range");
+    static_assert(DR >= 1 && DR <= SPS, "read-ahead");
+    __shared__ __attribute__((aligned(1024))) char lds[NS * STAGE];
+    __shared__ __attribute__((aligned(256))) char stg[R * SSTAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WGN, wn = wave % WGN;
+    const int r16 = lane & 15, g = lane >> 4;
+
+    const int ntm = (p.M + BM - 1) / BM, ntn = (p.N + BN - 1) / BN;
+    int tm, tn;
+    tile_coords(blockIdx.x, ntm, ntn, 8, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int nstages = p.K / KS;
+    const int nsteps = nstages * SPS;
+
+    // x: piece j of this wavefront covers stage rows RPI (wave + NW j) .. + RPI - 1 (as the 16-bit kernel)
+    const char *asrc[QAW];
+#pragma unroll
+    for (int j = 0; j < QAW; ++j) {
+        const int rloc = (wave + NW * j) * RPI + lane / CPR;
+        const int c = (lane % CPR) ^ qtile_swz<KS>(rloc);
+        asrc[j] = static_cast<const char *>(p.A) + (int64_t)min(m0 + rloc, p.M - 1) * p.lda * 2 + c * 16;
+    }
+    // weights: piece j covers stage rows BM + RPI (wave + NW j) ..; this lane's chunk c of weight row n
+    const char *wsrc[QBW];
+    const char *ssrc[QBW], *bsrc[QBW];
+    int bchunk[QBW];
+#pragma unroll
+    for (int j = 0; j < QBW; ++j) {
+        const int qb = wave + NW * j;
+        const int rloc = BM + qb * RPI + lane / CPR;
+        const int c = (lane % CPR) ^ qtile_swz<KS>(rloc);
+        const int n = min(n0 + qb * RPI + lane / CPR, p.N - 1);
+        bchunk[j] = c;
+        wsrc[j] = reinterpret_cast<const char *>(q.wq + (int64_t)n * q.ldwq) + (8 * c * BITS) / 32 * 4;
+        ssrc[j] = static_cast<const char *>(q.scales) + (int64_t)n * q.ldsb * 2;
+        bsrc[j] = static_cast<const char *>(q.biases) + (int64_t)n * q.ldsb * 2;
+    }
+    // staging of stage st (slot st mod R): piece j of this wavefront at wave, j: words [WPC][64], then
+    // scales [64], biases [64], each lane's in 4 bytes (a 2-byte direct-to-LDS load fills lane L's value
+    // into bytes 4 L, 4 L + 1 and zeroes the other two)
+    auto piece_at = [&](int slot, int j) { return stg + slot * SSTAGE + (wave * QBW + j) * PIECE; };
+    auto stage_packed = [&](int st, int slot) {
+        const int sc = min(st, nstages - 1);           // past the end: the last stage again, never read
+#pragma unroll
+        for (int j = 0; j < QBW; ++j) {
+            char *pc = piece_at(slot, j);
+            const int grp = (sc * KS + 8 * bchunk[j]) >> q.group_shift;
+            const char *w = wsrc[j] + (int64_t)sc * (KS * BITS / 8);
+#pragma unroll
+            for (int u = 0; u < WPC; ++u) qdma4(w + 4 * u, lds_addr(pc + 256 * u));
+            qdma2(ssrc[j] + 2 * grp, lds_addr(pc + 256 * WPC));
+            qdma2(bsrc[j] + 2 * grp, lds_addr(pc + 256 * WPC + 256));
+        }
+    };
+    // stage st: its weight chunks from the staging slot into its LDS buffer, then the packed loads of stage
+    // st + R into the slot just read, then its x pieces.  L loads per stage in every case (stages past the
+    // end load the last stage again into places nobody reads), so every count of loads in flight is exact.
+    auto fill = [&](int st, int slot) {
+        char *buf = lds + (st % NS) * STAGE;
+#pragma unroll
+        for (int j = 0; j < QBW; ++j) {
+            const char *pc = piece_at(slot, j);
+            const float sc = half_to_f32<dt>(*reinterpret_cast<const uint16_t *>(pc + 256 * WPC + 4 * lane));
+            const float bi = half_to_f32<dt>(*reinterpret_cast<const uint16_t *>(pc + 256 * WPC + 256 + 4 * lane));
+            float f[8];
+            if constexpr (BITS == 8) {
+                const u32x2 w = u32x2{*reinterpret_cast<const uint32_t *>(pc + 4 * lane),
+                                      *reinterpret_cast<const uint32_t *>(pc + 256 + 4 * lane)};
+                unpack8<8, 2>(w, 0, 0u, f);
+            } else {
+                const uint32_t w = *reinterpret_cast<const uint32_t *>(pc + 4 * lane);
+                if constexpr (BITS == 4) unpack8<4, 1>(w, 0, 0u, f);
+                else unpack8<2, 1>(w, 0, 16u * (uint32_t)(bchunk[j] & 1), f);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f[e] = __builtin_fmaf(sc, f[e], bi);
+            *reinterpret_cast<u32x4 *>(buf + (QA + wave + NW * j) * 1024 + lane * 16) =
+                u32x4{round_pack<dt>(f[0], f[1]), round_pack<dt>(f[2], f[3]), round_pack<dt>(f[4], f[5]),
+                      round_pack<dt>(f[6], f[7])};
+        }
+        stage_packed(st + R, slot);
+        const int64_t koff = (int64_t)min(st, nstages - 1) * ROWB;
+#pragma unroll
+        for (int j = 0; j < QAW; ++j) qdma16(asrc[j] + koff, lds_addr(buf + (wave + NW * j) * 1024));
+    };
+
+    int aoff[FM], boff[FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) aoff[i] = (wm * WM + 16 * i + r16) * ROWB;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) boff[j] = (BM + wn * WN + 16 * j + r16) * ROWB;
+    const int swz = qtile_swz<KS>(r16);
+    u32x4 fa[NSET][FM], fb[NSET][FN];
+    auto read_step = [&](int step, u32x4 (&a)[FM], u32x4 (&b)[FN]) {
+        const char *buf = lds + ((step / SPS) % NS) * STAGE;
+        const int c = 4 * (step % SPS) + g;
+        const int off = (c ^ swz) << 4;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) a[i] = *reinterpret_cast<const u32x4 *>(buf + aoff[i] + off);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) b[j] = *reinterpret_cast<const u32x4 *>(buf + boff[j] + off);
+    };
+    f32x4 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = zero4();
+
+    // prologue: packed stages 0 .. R - 1 staged; stages 0 .. NS - 2 filled (the fill of stage st first
+    // waits for its own staged data, issued before the x pieces of stage st - R); stage 0 landed
+    // everywhere; steps 0 .. DR - 1 read
+    if (nstages > 0) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) stage_packed(r, r);
+        BI_WAIT_VMCNT(0);
+#pragma unroll
+        for (int st = 0; st < NS - 1; ++st) {
+            if (st >= R) BI_WAIT_VMCNT(QAW + L * (R - 1));    // stage st's staged data (fill st - R) landed
+            fill(st, st % R);
+        }
+        BI_WAIT_VMCNT(L * (NS - 2));                  // this wavefront's x pieces of stage 0 landed
+        __builtin_amdgcn_s_waitcnt(0xc07f);           // and its chunk writes done
+        __builtin_amdgcn_s_barrier();
+#pragma unroll
+        for (int d = 0; d < DR; ++d)
+            if (d < nsteps) read_step(d, fa[d], fb[d]);
+    }
+    // step s: read step s + DR (entering stage tr first waits for it, which also covers the staged data of
+    // stage tr + NS - 2 = tr + R, issued in the fill of stage tr before its x pieces, and fills that stage
+    // into the buffer of stage tr - 2), then the MFMAs of step s.  s0 is a multiple of U (a multiple of R
+    // stages), so the staging slot of a stage is a constant in the unrolled body.  Whole iterations run
+    // without a condition; the rest runs with the checks.
+    auto step = [&](int s0, int d, auto checked) {
+        constexpr bool CHECK = decltype(checked)::value;
+        const int s = s0 + d;
+        if (CHECK && s >= nsteps) return;
+        const int sr_ = s + DR;
+        if (!CHECK || sr_ < nsteps) {
+            if ((d + DR) % SPS == 0) {
+                const int tr = sr_ / SPS;              // the stage being entered (>= 1)
+                BI_WAIT_VMCNT(L * (NS - 3));
+                __builtin_amdgcn_s_waitcnt(0xc07f);
+                __builtin_amdgcn_s_barrier();
+                fill(tr + NS - 2, ((d + DR) / SPS + NS - 2) % R);   // slot: a constant once unrolled
+            }
+            read_step(sr_, fa[(d + DR) % NSET], fb[(d + DR) % NSET]);
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) acc[i][j] = Mfma<dt>::step(fa[d % NSET][i], fb[d % NSET][j], acc[i][j]);
+    };
+    const int nfull = nsteps > DR ? (nsteps - DR) / U : 0;
+    for (int it = 0; it < nfull; ++it) {
+#pragma unroll
+        for (int d = 0; d < U; ++d) step(it * U, d, std::false_type{});
+    }
+    for (int s0 = nfull * U; s0 < nsteps; s0 += U) {
+#pragma unroll
+        for (int d = 0; d < U; ++d) step(s0, d, std::true_type{});
+    }
+    BI_WAIT_VMCNT(0);                                  // no load of this wavefront outlives the kernel's LDS
+    if constexpr (BM * BN * 2 <= NS * STAGE) {
+        store_tile16<dt, BM, BN, WGM, WGN>(p, acc, m0, n0, lds);
+    } else {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int n = n0 + wn * WN + 16 * j + r16;
+                if (n >= p.N) continue;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int m = m0 + wm * WM + 16 * i + 4 * g + e;
+                    if (m < p.M) epilogue<dt>(p, m, n, acc[i][j][e]);
+                }
+            }
+    }
+}
+
 // Large batches: the weights of columns [n0, n0 + nc) dequantised into an (nc, K) buffer of the input
 // dtype with exactly the arithmetic of storeW above (one fmaf, one rounding), for the tile GEMM kernels.
 // One thread per 8 values.
@@ -445,10 +682,10 @@ __global__ __launch_bounds__(256) void qdequant16(QGemmParams q, int n0, int nc,
 
 int qgemm_tile_rows(int M) { return M <= 16 ? 16 : (M <= 32 ? 32 : 64); }
 
-bool qgemm_uses_workspace(int64_t M) { return M > QGEMM_FUSED_MAX_M; }
+bool qgemm_uses_workspace(int64_t M, int64_t K) { return M > QGEMM_FUSED_MAX_M && K % QGEMM_TILE_K != 0; }
 
 size_t qgemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-    if (!qgemm_uses_workspace(M) || N <= 0 || K <= 0) return 0;
+    if (!qgemm_uses_workspace(M, K) || N <= 0 || K <= 0) return 0;
     const int64_t nc = N < QGEMM_CHUNK_N ? N : QGEMM_CHUNK_N;
     return (size_t)(nc * K * 2);
 }
@@ -477,6 +714,30 @@ static hipError_t launch_dt(const QGemmParams &q, hipStream_t st) {
     }
     if (rows == 32) return wide ? launch_fm<dt, 2, false, 2>(q, st) : launch_fm<dt, 2>(q, st);
     return wide ? launch_fm<dt, 4, false, 2>(q, st) : launch_fm<dt, 4>(q, st);
+}
+
+// More rows: 128 x 128 tiles when they give about one tile per CU, else 64 x 64 (the 16-bit plan's
+// thresholds); either way the chain of every element is bi_linear's.
+template <int dt, int BITS>
+static hipError_t launch_tile_bits(const QGemmParams &q, hipStream_t st) {
+    const int64_t t128 = ((q.g.M + 127) / 128) * ((q.g.N + 127) / 128);
+    if (t128 >= 192) {
+        const dim3 grid((unsigned)t128);
+        hipLaunchKernelGGL((qgemm16_tile<dt, BITS, 128, 128, 2, 4, 4, 64, 2>), grid, dim3(512), 0, st, q);
+    } else {
+        const int64_t t64 = ((q.g.M + 63) / 64) * ((q.g.N + 63) / 64);
+        if (t64 > INT32_MAX) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL((qgemm16_tile<dt, BITS, 64, 64, 2, 4, 4, 128, 2>), dim3((unsigned)t64), dim3(512), 0, st, q);
+    }
+    return hipGetLastError();
+}
+
+template <int dt>
+static hipError_t launch_tile(const QGemmParams &q, hipStream_t st) {
+    if (q.bits == 2) return launch_tile_bits<dt, 2>(q, st);
+    if (q.bits == 4) return launch_tile_bits<dt, 4>(q, st);
+    if (q.bits == 8) return launch_tile_bits<dt, 8>(q, st);
+    return hipErrorInvalidValue;
 }
 
 template <int dt>
@@ -510,7 +771,12 @@ hipError_t launch_qgemm(const QGemmParams &qin, int dt, void *ws, hipStream_t st
     q.g.total_steps = q.g.K / 32;
     q.group_shift = q.group_size == 32 ? 5 : (q.group_size == 64 ? 6 : 7);
     if ((1 << q.group_shift) != q.group_size) return hipErrorInvalidValue;
-    if (qgemm_uses_workspace(q.g.M) && q.g.K > 0) {
+    if (q.g.M > QGEMM_FUSED_MAX_M && q.g.K > 0 && !qgemm_uses_workspace(q.g.M, q.g.K)) {
+        if (dt == DT_BF16) return launch_tile<DT_BF16>(q, st);
+        if (dt == DT_F16) return launch_tile<DT_F16>(q, st);
+        return hipErrorInvalidValue;
+    }
+    if (qgemm_uses_workspace(q.g.M, q.g.K) && q.g.K > 0) {
         if (ws == nullptr) return hipErrorInvalidValue;
         if (dt == DT_BF16) return launch_chunks<DT_BF16>(q, ws, st);
         if (dt == DT_F16) return launch_chunks<DT_F16>(q, ws, st);

@@ -335,19 +335,22 @@ def test_quantized_linear_validation(lib):
     assert qlinear(lib, bits=4, ldwq=18) == UNSUPPORTED          # 4-bit rows: a pitch of 4k words
     assert qlinear(lib, bits=4, wq=ctypes.c_void_p(0x7f0000000008)) == UNSUPPORTED   # 16-byte alignment
     # 2-bit rows need 4 bytes only (stopped by the missing workspace, after the alignment checks)
-    assert qlinear(lib, M=65, bits=2, ldwq=9, wq=ctypes.c_void_p(0x7f0000000004)) == WORKSPACE
+    assert qlinear(lib, M=65, K=192, bits=2, ldwq=13, wq=ctypes.c_void_p(0x7f0000000004)) == WORKSPACE
     assert qlinear(lib, ldx=1 << 24) == UNSUPPORTED              # 32-bit offsets inside the kernel
     assert qlinear(lib, ldwq=1 << 25) == UNSUPPORTED
     assert qlinear(lib, ldsb=1 << 26) == UNSUPPORTED
     assert qlinear(lib, M=0) == OK and qlinear(lib, N=0) == OK   # nothing to do
-    # more than 64 rows need the dequantisation workspace: min(N, 8192) * K * 2 bytes
-    assert lib.bi_quantized_linear_workspace_bytes(64, 32, 128, BF16) == 0
-    assert lib.bi_quantized_linear_workspace_bytes(65, 32, 128, BF16) == 32 * 128 * 2
-    assert lib.bi_quantized_linear_workspace_bytes(1000, 20000, 4096, F16) == 8192 * 4096 * 2
-    assert lib.bi_quantized_linear_workspace_bytes(65, 32, 128, F32) == 0
-    assert qlinear(lib, M=65) == WORKSPACE
-    assert qlinear(lib, M=65, ws=P16, ws_bytes=32 * 128 * 2 - 1) == WORKSPACE
-    assert qlinear(lib, M=65, ws=P_MIS, ws_bytes=1 << 20) == WORKSPACE     # not 256-byte aligned
+    # more than 64 rows with K a multiple of 128 dequantise inside the tile kernel (no workspace); other K
+    # need the dequantisation workspace: min(N, 8192) * K * 2 bytes
+    assert lib.bi_quantized_linear_workspace_bytes(64, 32, 192, BF16) == 0
+    assert lib.bi_quantized_linear_workspace_bytes(65, 32, 128, BF16) == 0
+    assert lib.bi_quantized_linear_workspace_bytes(1000, 20000, 4096, F16) == 0
+    assert lib.bi_quantized_linear_workspace_bytes(65, 32, 192, BF16) == 32 * 192 * 2
+    assert lib.bi_quantized_linear_workspace_bytes(1000, 20000, 4032, F16) == 8192 * 4032 * 2
+    assert lib.bi_quantized_linear_workspace_bytes(65, 32, 192, F32) == 0
+    assert qlinear(lib, M=65, K=192) == WORKSPACE
+    assert qlinear(lib, M=65, K=192, ws=P16, ws_bytes=32 * 192 * 2 - 1) == WORKSPACE
+    assert qlinear(lib, M=65, K=192, ws=P_MIS, ws_bytes=1 << 20) == WORKSPACE     # not 256-byte aligned
 
 
 def test_quantize_helper_round_trip():

@@ -6,9 +6,10 @@
   weight's storage differs;
 * oracle tolerance (bf16 / fp16 outputs: 2e-2) against the float64 oracle's quantized_linear;
 * invariance on raw bit patterns across batch size and batch neighbours;
-* shapes with ragged N, a partial last stage of the K loop, every bit width and group size, and both paths
-  (up to 64 rows: unpacked inside the kernel's K loop; more: dequantised by chunks into a workspace
-  for bi_linear's kernels), whose rows must agree bit for bit;
+* shapes with ragged N, a partial last stage of the K loop, every bit width and group size, and the three
+  paths (up to 64 rows: unpacked inside the strip kernel's K loop; more rows with K a multiple of 128:
+  dequantised on the way into the tile kernel's LDS; other K: dequantised by chunks into a workspace for
+  bi_linear's kernels), whose rows must agree bit for bit;
 * scale / bias rows padded past K / group_size (through the C ABI), and scales of 2^118 and 2^119 beside
   ordinary ones.
 """
@@ -48,6 +49,10 @@ CASES = [  # M, N, K, bits, gs
     # wide N (more than 256 strips of 16 columns): two strips per workgroup, ragged last pair
     (2, 4200, 512, 4, 64), (16, 4113, 288, 8, 32), (17, 5000, 384, 2, 128), (40, 4500, 640, 4, 32),
     (64, 4104, 256, 8, 64),
+    # more than 64 rows, K a multiple of 128: the dequantising tile kernel (64 x 64 tiles; 128 x 128 tiles
+    # from 192 of them), every bit width; other K: the workspace path
+    (150, 500, 1024, 8, 128), (65, 33, 384, 4, 32), (200, 12288, 256, 4, 64), (300, 1000, 640, 2, 128),
+    (80, 300, 224, 4, 32), (130, 200, 352, 8, 32),
     # few rows of 4-bit weights at every group size, ragged N, K past a 1024-k boundary
     (3, 1000, 1024, 4, 32), (4, 300, 1280, 4, 128), (2, 4113, 2048, 4, 64), (4, 4096, 4096, 4, 64),
     (1, 16, 256, 4, 32),
