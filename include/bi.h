@@ -349,12 +349,13 @@ bi_status bi_rowsum(const void *x, int64_t ldx, void *y, int64_t M, int64_t N, i
  * 128, and K a multiple of it.  All device memory; enqueued on `stream`.
  * M == 0 or N == 0 enqueues nothing; K == 0 writes the bias (or zeros).
  * ws: bi_quantized_linear_workspace_bytes(M, N, K, dt) bytes of 256-byte
- * aligned device memory, or NULL when that is 0 (M <= 64: the weights are
- * unpacked inside the strip kernel's K loop; more rows with K a multiple of
- * 128: inside the tile kernel, on their way into LDS).  Above 64 rows with
- * other K, chunks of at most 8192 columns are dequantised into ws with the
- * same arithmetic and bi_linear's kernels run on them; the result is the same
- * bits in every case.  Too small a workspace is refused with BI_ERR_WORKSPACE.
+ * aligned device memory, or NULL when that is 0 (up to 64 rows, and any
+ * number of rows when K is a multiple of 128, the weights are unpacked inside
+ * the kernels: in the strip kernel's K loop, or in the tile kernel on their
+ * way into LDS).  Above 64 rows with other K, chunks of at most 8192 columns
+ * are dequantised into ws with the same arithmetic and bi_linear's kernels run
+ * on them; the result is the same bits in every case.  Too small a workspace
+ * is refused with BI_ERR_WORKSPACE.
  */
 bi_status bi_quantized_linear(const void *x, int64_t ldx,
                               const uint32_t *wq, int64_t ldwq,

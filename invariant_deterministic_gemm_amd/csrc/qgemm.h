@@ -20,9 +20,10 @@ struct QGemmParams {
     int group_shift;        // log2(group_size), set by the launcher
 };
 
-// Rows up to this many run the strip kernel; more rows run the tile kernel, which dequantises the weight
-// tiles on their way into LDS, when K is a multiple of QGEMM_TILE_K, else dequantise chunks of at most
-// QGEMM_CHUNK_N columns into a workspace and run the tile GEMM kernels on them.
+// Rows up to this many run the strip kernel (up to 32 when N > 4096); more rows run the tile kernel,
+// which dequantises the weight tiles on their way into LDS, when K is a multiple of QGEMM_TILE_K, else
+// (above 64 rows) dequantise chunks of at most QGEMM_CHUNK_N columns into a workspace and run the tile
+// GEMM kernels on them.
 constexpr int64_t QGEMM_FUSED_MAX_M = 64;
 constexpr int64_t QGEMM_TILE_K = 128;
 constexpr int64_t QGEMM_CHUNK_N = 8192;
