@@ -29,6 +29,21 @@
  *    back to a different (batch-variant) kernel.  (README, section "Use":
  *    anything that cannot be made invariant raises instead of silently
  *    falling back.)
+ *
+ * Where this interface differs from the plainest form of the four calls
+ * -------------------------------------------------------------------
+ *  - The GEMM calls take no workspace and have no workspace query: each
+ *    output element's whole K reduction is one chain inside one kernel (no
+ *    split-K and no fixed K-segment fold), so there is nothing to stage.
+ *    Only the batch-variant comparator (bi_variant_linear) and the
+ *    quantized linear above 64 rows with K not a multiple of 128 take one.
+ *  - bi_sdpa_workspace_bytes takes Hkv and the dtype besides (B, Hq, Lq, S,
+ *    D): which kernel runs, and whether the split partials go through a
+ *    workspace at all, follows the grid size (B x Hkv x row tiles) and the
+ *    dtype (fp32 always takes the split path).
+ *  - bi_matmul / bi_addmm describe B by a row and a column stride instead of
+ *    one leading dimension, so the transposed view of an (N, K) weight is
+ *    passed without a copy and runs the bi_linear kernels.
  */
 #ifndef BI_H
 #define BI_H
