@@ -478,8 +478,9 @@ __device__ __forceinline__ void attn_scores16(const Rows16T<NC> &r, const char *
 // VISIBLE: the caller knows every key of the block is visible to every row (no mask, inside S, before
 // the tile's first causal position), which is the case the visibility test would pick.  RESCALE_ALWAYS:
 // O is multiplied by alpha even when no row's maximum moved (alpha = 1 then, and O * 1 = O), so the
-// update has no branch.  Neither changes any result.
-template <int dt, int NC, int NT, bool VISIBLE = false, bool RESCALE_ALWAYS = false>
+// update has no branch.  Neither changes any result.  OT: the caller accumulates O transposed (lane
+// holds O[row r16][16 t + 4 g + i], see sdpa_prefill16p), so each lane rescales by its own row's alpha.
+template <int dt, int NC, int NT, bool VISIBLE = false, bool RESCALE_ALWAYS = false, bool OT = false>
 __device__ __forceinline__ void attn_softmax16(const SdpaParams &p, const Rows16T<NC> &r, const f32x4 (&st)[4],
                                                int kb, float &m_run, float &l_run, f32x4 (&o)[NT],
                                                u32x4 (&pf)[2]) {
@@ -533,7 +534,7 @@ __device__ __forceinline__ void attn_softmax16(const SdpaParams &p, const Rows16
     if (RESCALE_ALWAYS || __builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float ai = __shfl(alpha, 4 * g + i);
+            const float ai = OT ? alpha : __shfl(alpha, 4 * g + i);
 #pragma unroll
             for (int t = 0; t < NT; ++t) o[t][i] = o[t][i] * ai;
         }
@@ -566,19 +567,22 @@ __device__ __forceinline__ void attn_vfrags16(const char *Vs, int c, u32x4 (&vf)
 // The rest of one block [kb, kb + 64) given its scores: attn_softmax16, then O += P . V from the V block
 // in LDS (rows of keys past S must read as zero by the time v_ready() returns, which is before the first
 // V read).  The V fragments of a half (c) are read before its NT MFMAs; o[t] takes c = 0 then c = 1.
-template <int dt, class VReady, int NC, int NT>
+// OT: O is accumulated transposed, O^T += V^T . P^T (the V fragments as the A operand, P as the B
+// operand): every element gets the products and k order of P . V, and lane (r16, g) holds
+// O[row r16][16 t + 4 g + i] instead of O[row 4 g + i][16 t + r16].
+template <int dt, class VReady, int NC, int NT, bool OT = false>
 __device__ __forceinline__ void attn_update16(const SdpaParams &p, const Rows16T<NC> &r, const f32x4 (&st)[4],
                                               const char *Vs, int kb, float &m_run, float &l_run, f32x4 (&o)[NT],
                                               VReady v_ready) {
     u32x4 pf[2];
-    attn_softmax16<dt>(p, r, st, kb, m_run, l_run, o, pf);
+    attn_softmax16<dt, NC, NT, false, false, OT>(p, r, st, kb, m_run, l_run, o, pf);
     v_ready();
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
         u32x4 vf[NT];
         attn_vfrags16<NT>(Vs, c, vf);
 #pragma unroll
-        for (int t = 0; t < NT; ++t) o[t] = Mfma<dt>::step(pf[c], vf[t], o[t]);
+        for (int t = 0; t < NT; ++t) o[t] = OT ? Mfma<dt>::step(vf[t], pf[c], o[t]) : Mfma<dt>::step(pf[c], vf[t], o[t]);
     }
 }
 
@@ -587,7 +591,7 @@ __device__ __forceinline__ void attn_update16(const SdpaParams &p, const Rows16T
 // rows, K and V blocks in LDS as attn_scores16 and attn_update16 take them.
 // k_done() runs once every K read of the block is complete, v_ready() before
 // the first V read.
-template <int dt, class KDone, class VReady, int NC, int NT>
+template <int dt, bool OT = false, class KDone, class VReady, int NC, int NT>
 __device__ __forceinline__ void attn_block16(const SdpaParams &p, const Rows16T<NC> &r, const char *Ks, const char *Vs,
                                              int kb, float &m_run, float &l_run, f32x4 (&o)[NT], KDone k_done,
                                              VReady v_ready) {
@@ -595,14 +599,15 @@ __device__ __forceinline__ void attn_block16(const SdpaParams &p, const Rows16T<
     attn_scores16<dt>(r, Ks, st);
     __builtin_amdgcn_s_waitcnt(0xc07f);               // every K read of this block done
     k_done();
-    attn_update16<dt>(p, r, st, Vs, kb, m_run, l_run, o, v_ready);
+    attn_update16<dt, VReady, NC, NT, OT>(p, r, st, Vs, kb, m_run, l_run, o, v_ready);
 }
 
 // One wavefront's share: split `sp` of row tile `tile` of (b, gk), its K / V
 // blocks staged in `lds` (2 * KV_BLOCK * 64 NC bytes: rows of 32 NC elements,
 // NC = 4 for D <= 128 and 8 for D = 160 ... 256, zero-padded); leaves the
-// split's (m, l) of row r16 and its O fragment (rows 4 g + i, columns 16 t + r16).
-template <int dt, int NC = 4>
+// split's (m, l) of row r16 and its O fragment (rows 4 g + i, columns 16 t + r16;
+// with OT, row r16, columns 16 t + 4 g + i: see attn_update16).
+template <int dt, int NC = 4, bool OT = false>
 __device__ __forceinline__ void split16_body(const SdpaParams &p, int sp, int tile, int b, int gk, char *lds,
                                              float &m_out, float &l_out, f32x4 (&o)[2 * NC]) {
     constexpr int D = 32 * NC;
@@ -711,7 +716,7 @@ __device__ __forceinline__ void split16_body(const SdpaParams &p, int sp, int ti
             const int kb = kbeg + blk * KV_BLOCK;
             char *Vs = lds + KBYTES;
             BI_WAIT_VMCNT(QB);                        // K of this block landed (its V may be in flight)
-            attn_block16<dt>(
+            attn_block16<dt, OT>(
                 p, r, lds, Vs, kb, m_run, l_run, o,
                 [&]() {
                     if (blk + 1 < nblk) issueK(blk + 1, 0, QB);
@@ -744,7 +749,7 @@ __device__ __forceinline__ void split16_body(const SdpaParams &p, int sp, int ti
             char *Vs = lds + KBYTES;
             BI_WAIT_VMCNT(H);                         // K of this block landed (first piece of V in flight)
             issueV(blk, H, QB);
-            attn_block16<dt>(
+            attn_block16<dt, OT>(
                 p, r, lds, Vs, kb, m_run, l_run, o,
                 [&]() {
                     if (blk + 1 < nblk) issueK(blk + 1, 0, H);
@@ -790,24 +795,20 @@ __global__ __launch_bounds__(64 * W) void sdpa_split16(SdpaParams p) {
     if (sp >= p.nsplit) return;
     float m_run, l_run;
     f32x4 o[2 * NC];
-    split16_body<dt, NC>(p, sp, tile, b, gk, lds + wave * PER_WAVE, m_run, l_run, o);
+    split16_body<dt, NC, true>(p, sp, tile, b, gk, lds + wave * PER_WAVE, m_run, l_run, o);
+    // O accumulated transposed: lane (r16, g) holds row r16, columns 16 t + 4 g .. + 3 (one 16-byte store)
     const int rg = tile * 16 + r16;
-    if (g == 0 && rg < R) {
+    if (rg < R) {
         const int64_t rowid = ((int64_t)b * p.Hq + gk * p.G + rg % p.G) * p.Lq + rg / p.G;
-        float *ml = p.ws_ml + (rowid * p.nsplit + sp) * 2;
-        ml[0] = m_run;
-        ml[1] = l_run;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int ro = tile * 16 + 4 * g + i;
-        if (ro < R) {
-            const int64_t rowid = ((int64_t)b * p.Hq + gk * p.G + ro % p.G) * p.Lq + ro / p.G;
-            float *dst = p.ws_o + (rowid * p.nsplit + sp) * p.dr;
-#pragma unroll
-            for (int t = 0; t < 2 * NC; ++t)
-                if (16 * t < p.dr) dst[16 * t + r16] = o[t][i];
+        if (g == 0) {
+            float *ml = p.ws_ml + (rowid * p.nsplit + sp) * 2;
+            ml[0] = m_run;
+            ml[1] = l_run;
         }
+        float *dst = p.ws_o + (rowid * p.nsplit + sp) * p.dr;
+#pragma unroll
+        for (int t = 0; t < 2 * NC; ++t)
+            if (16 * t < p.dr) *reinterpret_cast<f32x4 *>(dst + 16 * t + 4 * g) = o[t];
     }
 }
 
@@ -1151,7 +1152,7 @@ __global__ __launch_bounds__(64 * 4 * T) void sdpa_quad16(SdpaParams p) {
 // factors of their score rows.  The split state then restarts empty.  When no row of the tile skips or
 // copies (the common case), the selects between the three outcomes are left out: they would all pick
 // the rescaled sum.
-template <int NT>
+template <int NT, bool OT = false>
 __device__ __forceinline__ void fold_split16(float &m_run, float &l_run, f32x4 (&o)[NT], bool &have, float &mt,
                                              float &lt, f32x4 (&ot)[NT]) {
     constexpr float NEG_INF = -__builtin_huge_valf();
@@ -1172,7 +1173,7 @@ __device__ __forceinline__ void fold_split16(float &m_run, float &l_run, f32x4 (
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int src = 4 * g + i;
-            const float a_i = __shfl(a, src), b_i = __shfl(bs, src);
+            const float a_i = OT ? a : __shfl(a, src), b_i = OT ? bs : __shfl(bs, src);
 #pragma unroll
             for (int t = 0; t < NT; ++t) ot[t][i] = __builtin_fmaf(ot[t][i], a_i, o[t][i] * b_i);
         }
@@ -1180,9 +1181,9 @@ __device__ __forceinline__ void fold_split16(float &m_run, float &l_run, f32x4 (
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int src = 4 * g + i;
-            const bool skip_i = __shfl((int)skip, src) != 0;
-            const bool first_i = __shfl((int)first, src) != 0;
-            const float a_i = __shfl(a, src), b_i = __shfl(bs, src);
+            const bool skip_i = OT ? skip : __shfl((int)skip, src) != 0;
+            const bool first_i = OT ? first : __shfl((int)first, src) != 0;
+            const float a_i = OT ? a : __shfl(a, src), b_i = OT ? bs : __shfl(bs, src);
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 const float f = __builtin_fmaf(ot[t][i], a_i, o[t][i] * b_i);
@@ -1202,7 +1203,7 @@ __device__ __forceinline__ void fold_split16(float &m_run, float &l_run, f32x4 (
 // the combine's copy does: a = exp2(-inf) = 0 and bs = 1 give lt = l_run and ot = o, except that a zero of
 // o may come out with the other sign, which no later fold, the division or the final -0 -> +0 step can turn
 // into a different output bit.
-template <int NT>
+template <int NT, bool OT = false>
 __device__ __forceinline__ void fold_split16_full(float &m_run, float &l_run, f32x4 (&o)[NT], bool &have,
                                                   float &mt, float &lt, f32x4 (&ot)[NT]) {
     constexpr float NEG_INF = -__builtin_huge_valf();
@@ -1215,7 +1216,7 @@ __device__ __forceinline__ void fold_split16_full(float &m_run, float &l_run, f3
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int src = 4 * g + i;
-        const float a_i = __shfl(a, src), b_i = __shfl(bs, src);
+        const float a_i = OT ? a : __shfl(a, src), b_i = OT ? bs : __shfl(bs, src);
 #pragma unroll
         for (int t = 0; t < NT; ++t) ot[t][i] = __builtin_fmaf(ot[t][i], a_i, o[t][i] * b_i);
     }
@@ -1265,7 +1266,9 @@ __device__ __forceinline__ void vfrags_tr(const uint32_t (&va)[NT], u32x4 (&vf)[
 // state, so every row gets the bits of the split + combine path.  Splits whose blocks every row of the
 // workgroup sees completely (no mask, inside S, before the first row's causal position) run a
 // branch-free body: visibility known, rescale by alpha always (O * 1 = O), the fold without its
-// empty-partial cases.  Causal workgroups start longest first.  Below D = 128 the kernel takes only the
+// empty-partial cases.  O is accumulated transposed (V^T . P^T on the matrix cores: each lane then holds
+// output columns of its own score row, so the rescale and the split fold need no lane exchange; the
+// products and their k order are those of P . V).  Causal workgroups start longest first.  Below D = 128 the kernel takes only the
 // head dim's D / 32 score chunks and D / 16 output column tiles (the LDS rows keep the 256-byte layout;
 // chunks at d >= D are neither loaded nor read), which are the split kernel's chains for that D.
 template <int dt, int W, int D>
@@ -1390,11 +1393,13 @@ void sdpa_prefill16p(SdpaParams p) {
         vfrags_tr<VB * KBYTES>(va, vf[0]);
         vfrags_tr<VB * KBYTES + 32 * ROWB>(va, vf[1]);
     };
+    // O^T += V^T . P^T: the V fragments as the A operand and P as the B operand give each element the
+    // products and k order of O += P . V, with rows and columns of the tile swapped
     auto pv = [&](const u32x4 (&pf)[2], const u32x4 (&vf)[2][NT]) {
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
-            for (int t = 0; t < NT; ++t) o[t] = Mfma<dt>::step(pf[c], vf[c][t], o[t]);
+            for (int t = 0; t < NT; ++t) o[t] = Mfma<dt>::step(vf[c][t], pf[c], o[t]);
     };
 
     using VB0 = std::integral_constant<int, 0>;
@@ -1423,7 +1428,7 @@ void sdpa_prefill16p(SdpaParams p) {
         top(j, kfree, vnext, vcur);
         scores(knext, st_nxt);
         u32x4 pf[2];
-        attn_softmax16<dt, NC, NT, true, true>(p, r, st_cur, j * KV_BLOCK, m_run, l_run, o, pf);
+        attn_softmax16<dt, NC, NT, true, true, true>(p, r, st_cur, j * KV_BLOCK, m_run, l_run, o, pf);
         u32x4 vf[2][NT];
         vread(vb, vf);
         pv(pf, vf);
@@ -1434,13 +1439,13 @@ void sdpa_prefill16p(SdpaParams p) {
         top(j, kfree, vnext, vcur);
         if (j + 1 < nblk) scores(knext, st_nxt);
         u32x4 pf[2];
-        attn_softmax16<dt>(p, r, st_cur, j * KV_BLOCK, m_run, l_run, o, pf);
+        attn_softmax16<dt, NC, NT, false, false, true>(p, r, st_cur, j * KV_BLOCK, m_run, l_run, o, pf);
         u32x4 vf[2][NT];
         vread(vb, vf);
         pv(pf, vf);
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) st_cur[kt] = st_nxt[kt];
-        if ((j + 1) % BPS == 0 || j + 1 == nblk) fold_split16(m_run, l_run, o, have, mt, lt, ot);
+        if ((j + 1) % BPS == 0 || j + 1 == nblk) fold_split16<NT, true>(m_run, l_run, o, have, mt, lt, ot);
     };
 
     if (nblk > 0) {
@@ -1458,30 +1463,27 @@ void sdpa_prefill16p(SdpaParams p) {
         fast_block(j + 1, kbuf1, kbuf0, vbuf0, vbuf1, VB1{});
         fast_block(j + 2, kbuf0, kbuf1, vbuf1, vbuf0, VB0{});
         fast_block(j + 3, kbuf1, kbuf0, vbuf0, vbuf1, VB1{});
-        fold_split16_full(m_run, l_run, o, have, mt, lt, ot);
+        fold_split16_full<NT, true>(m_run, l_run, o, have, mt, lt, ot);
     }
     for (int j = nfast * BPS; j < nblk; j += 2) {
         general_block(j, kbuf0, kbuf1, vbuf1, vbuf0, VB0{});
         if (j + 1 < nblk) general_block(j + 1, kbuf1, kbuf0, vbuf0, vbuf1, VB1{});
     }
 
-    // normalise, canonicalise -0, round once: O rows 4 g + i, columns 16 t + r16
-    const float lrow_l = lt;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int ro = tile * 16 + 4 * g + i;
-        const bool have_i = __shfl((int)have, 4 * g + i) != 0;
-        const float l_i = __shfl(lrow_l, 4 * g + i);
-        if (ro >= R) continue;
+    // normalise, canonicalise -0, round once: O row r16, columns 16 t + 4 g + i
+    const int ro = tile * 16 + r16;
+    if (ro < R) {
         const int iq = ro / p.G, h = gk * p.G + ro % p.G;
         char *orow = static_cast<char *>(p.o) +
                      ((int64_t)b * p.os[0] + (int64_t)h * p.os[1] + (int64_t)iq * p.os[2]) * Elem<dt>::bytes;
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            float v = have_i ? ot[t][i] / l_i : 0.0f;
-            v = v + 0.0f;                                // -0 -> +0
-            store_from_f32<dt>(orow, 16 * t + r16, v);
-        }
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float v = have ? ot[t][i] / lt : 0.0f;
+                v = v + 0.0f;                            // -0 -> +0
+                store_from_f32<dt>(orow, 16 * t + 4 * g + i, v);
+            }
     }
 }
 
