@@ -833,7 +833,7 @@ __global__ __launch_bounds__(64 * FUSED_MAXW) void sdpa_fused16(SdpaParams p) {
     const int b = grp / p.Hkv, gk = grp % p.Hkv;
     float m_run, l_run;
     f32x4 o[8];
-    split16_body<dt>(p, wave, tile, b, gk, lds + wave * PER_WAVE, m_run, l_run, o);
+    split16_body<dt, 4, true>(p, wave, tile, b, gk, lds + wave * PER_WAVE, m_run, l_run, o);
     __syncthreads();                                 // every wavefront is done with its K / V blocks
     float *pml = reinterpret_cast<float *>(lds);                     // [split][16 rows][2]
     float *po = pml + FUSED_MAXW * 16 * 2;                           // [split][16 rows][D]
@@ -841,10 +841,9 @@ __global__ __launch_bounds__(64 * FUSED_MAXW) void sdpa_fused16(SdpaParams p) {
         pml[(wave * 16 + r16) * 2] = m_run;
         pml[(wave * 16 + r16) * 2 + 1] = l_run;
     }
+    // O transposed: lane (r16, g) holds row r16, columns 16 t + 4 g .. + 3
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int t = 0; t < 8; ++t) po[(wave * 16 + 4 * g + i) * D + 16 * t + r16] = o[t][i];
+    for (int t = 0; t < 8; ++t) *reinterpret_cast<f32x4 *>(po + (wave * 16 + r16) * D + 16 * t + 4 * g) = o[t];
     __syncthreads();
     for (int e = tid; e < 16 * p.dr; e += 64 * nw) {
         const int row = e / p.dr, d = e % p.dr;
@@ -897,7 +896,8 @@ __global__ __launch_bounds__(64 * FUSED_MAXW) void sdpa_fused16(SdpaParams p) {
 //      (rounded as in split16_body) and row sum;
 //   3. l = fmaf(l, alpha, sum) runs over the blocks in order, and
 //      O = O * alpha, O += P . V over the blocks in order, each wavefront for
-//      two of the eight 16-wide column tiles (columns are independent chains).
+//      two of the eight 16-wide column tiles (columns are independent chains),
+//      accumulated transposed as in attn_update16.
 // A tile only visits the blocks split16_body visits for it (its own causal
 // limit), so its bits never depend on the other tile.  The split's (m, l, O)
 // goes to the workspace like sdpa_split16's, and the combine kernel folds the
@@ -1051,12 +1051,11 @@ __global__ __launch_bounds__(64 * 4 * T) void sdpa_quad16(SdpaParams p) {
         const float mu = xm[wt][u][r16];
         m_run = mu == NEG_INF ? m_run : fmaxf(m_run, mu);
         l_run = __builtin_fmaf(l_run, alpha, xr[wt][u][r16]);
-        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {      // O transposed: row r16 in every lane
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float ai = xa[wt][u][4 * g + i];
-                o[0][i] = o[0][i] * ai;
-                o[1][i] = o[1][i] * ai;
+                o[0][i] = o[0][i] * alpha;
+                o[1][i] = o[1][i] * alpha;
             }
         }
         const char *Vu = lds + u * 2 * KBYTES + KBYTES;
@@ -1075,18 +1074,18 @@ __global__ __launch_bounds__(64 * 4 * T) void sdpa_quad16(SdpaParams p) {
                 vf[j] = u32x4{lo[0], lo[1], hi[0], hi[1]};
             }
 #pragma unroll
-            for (int j = 0; j < 2; ++j) o[j] = Mfma<dt>::step(pf, vf[j], o[j]);
+            for (int j = 0; j < 2; ++j) o[j] = Mfma<dt>::step(vf[j], pf, o[j]);    // O^T += V^T . P^T
         }
     }
 
     if (p.nsplit == 1) {
-        // one split: sdpa_combine's fold of a single partial (after the sink, if any), done here
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int ro = tile * 16 + 4 * g + i;
-            const float ms = __shfl(m_run, 4 * g + i), ls = __shfl(l_run, 4 * g + i);
-            if (ro >= R) continue;
-            const int iq = ro / p.G, h = gk * p.G + ro % p.G;
+        // one split: sdpa_combine's fold of a single partial (after the sink, if any), done here; lane
+        // (r16, g) holds row r16, columns 16 t + 4 g + i
+        const int ro = tile * 16 + r16;
+        if (ro >= R) return;
+        const float ms = m_run, ls = l_run;
+        const int iq = ro / p.G, h = gk * p.G + ro % p.G;
+        {
             bool have = false;
             float m = 0.0f, l = 0.0f;
             if (p.sinks) {
@@ -1114,34 +1113,32 @@ __global__ __launch_bounds__(64 * 4 * T) void sdpa_quad16(SdpaParams p) {
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const int t = 2 * w + j;
-                const float acc = skip ? 0.0f : first ? o[j][i] : __builtin_fmaf(0.0f, a, o[j][i] * bs);
-                float v = have ? acc / l : 0.0f;
-                v = v + 0.0f;                        // -0 -> +0
-                if (16 * t < p.dr) store_from_f32<dt>(orow, 16 * t + r16, v);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float acc = skip ? 0.0f : first ? o[j][i] : __builtin_fmaf(0.0f, a, o[j][i] * bs);
+                    float v = have ? acc / l : 0.0f;
+                    v = v + 0.0f;                    // -0 -> +0
+                    if (16 * t < p.dr) store_from_f32<dt>(orow, 16 * t + 4 * g + i, v);
+                }
             }
         }
         return;
     }
 
-    // ---- the split's partial, as sdpa_split16 stores it
+    // ---- the split's partial, as sdpa_split16 stores it (row r16, columns 16 t + 4 g .. + 3 per lane)
     const int rg = tile * 16 + r16;
-    if (w == 0 && g == 0 && rg < R) {
+    if (rg < R) {
         const int64_t rowid = ((int64_t)b * p.Hq + gk * p.G + rg % p.G) * p.Lq + rg / p.G;
-        float *ml = p.ws_ml + (rowid * p.nsplit + sp) * 2;
-        ml[0] = m_run;
-        ml[1] = l_run;
-    }
+        if (w == 0 && g == 0) {
+            float *ml = p.ws_ml + (rowid * p.nsplit + sp) * 2;
+            ml[0] = m_run;
+            ml[1] = l_run;
+        }
+        float *dst = p.ws_o + (rowid * p.nsplit + sp) * p.dr;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int ro = tile * 16 + 4 * g + i;
-        if (ro < R) {
-            const int64_t rowid = ((int64_t)b * p.Hq + gk * p.G + ro % p.G) * p.Lq + ro / p.G;
-            float *dst = p.ws_o + (rowid * p.nsplit + sp) * p.dr;
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int t = 2 * w + j;
-                if (16 * t < p.dr) dst[16 * t + r16] = o[j][i];
-            }
+        for (int j = 0; j < 2; ++j) {
+            const int t = 2 * w + j;
+            if (16 * t < p.dr) *reinterpret_cast<f32x4 *>(dst + 16 * t + 4 * g) = o[j];
         }
     }
 }
