@@ -27,8 +27,6 @@ struct QGemmParams {
 constexpr int64_t QGEMM_FUSED_MAX_M = 64;
 constexpr int64_t QGEMM_TILE_K = 128;
 constexpr int64_t QGEMM_CHUNK_N = 8192;
-// Up to this many rows the fused kernel's consumer loads x itself (x in registers, not LDS).
-constexpr int64_t QGEMM_XREG_MAX_M = 1;
 // Above this many 16-column strips a workgroup of the fused kernel takes two strips (x read half as often).
 constexpr int64_t QGEMM_WIDE_STRIPS = 256;
 bool qgemm_uses_workspace(int64_t M, int64_t K);

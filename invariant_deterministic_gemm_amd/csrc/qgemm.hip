@@ -76,20 +76,17 @@ __device__ __forceinline__ uint32_t opaque(uint32_t x) {
 
 // Stage geometry of the fused kernel: k per stage, values each producer thread unpacks per stage (one
 // load of VPT * BITS / 8 bytes, one scale and one bias: VPT never exceeds a group), packed words per
-// unit, weight stages in flight per thread.
-template <int FM, int BITS, bool XREG_, int NB> struct QStrip {
-    static constexpr int KS = FM == 4 ? 128 : 256;
+// unit, weight stages in flight per thread.  One strip of one row fragment takes 512-k stages (half as
+// many barriers; measured 8.1 -> 7.8 us at N = 4096, M = 1, 4-bit), two strips keep 256 (faster there).
+template <int FM, int BITS, int NB> struct QStrip {
+    static constexpr int KS = FM == 4 ? 128 : (FM == 1 && NB == 1 ? 512 : 256);
     static constexpr int VPT = NB * KS / 16;                     // 16 NB rows x KS values over 256 threads
     static constexpr int TPR = 16 / NB;                          // producer threads per weight row
     static constexpr int WPU = VPT * BITS >= 32 ? VPT * BITS / 32 : 1;
     static constexpr bool HALF = VPT * BITS < 32;              // 2 bits, 8 values: half a word
     static constexpr int DEPTH = WPU >= 4 ? 4 : 8;
-    // x: with XREG (one fragment of few rows) the consumer loads its fragments straight into registers
-    // one stage ahead; otherwise x goes through LDS, XU 16-byte chunks per producer thread per stage,
-    // XD stages ahead
-    static constexpr bool XREG = XREG_;
-    static constexpr int XR = 2;
-    static constexpr int XU = XREG ? 0 : 16 * FM * KS / 2048;
+    // x goes through LDS, XU 16-byte chunks per producer thread per stage, XD stages ahead
+    static constexpr int XU = 16 * FM * KS / 2048;
     static constexpr int XD = FM == 1 ? 4 : 1;
 };
 
@@ -99,23 +96,6 @@ template <int FM, int BITS, bool XREG_, int NB> struct QStrip {
 template <int CPT> __device__ __forceinline__ int wslot(int c, int r) {
     if constexpr (CPT == 1) return c ^ (r & 15);
     else return c ^ (r & 15) ^ ((c / CPT) & 7);
-}
-
-// Lane u of each 16-lane row, broadcast to the whole row (DPP row_newbcast; u a constant once unrolled).
-__device__ __forceinline__ uint32_t row_bcast1(uint32_t x, int u) {
-    switch (u & 7) {
-        case 0: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x150, 0xf, 0xf, false);
-        case 1: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x151, 0xf, 0xf, false);
-        case 2: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x152, 0xf, 0xf, false);
-        case 3: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x153, 0xf, 0xf, false);
-        case 4: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x154, 0xf, 0xf, false);
-        case 5: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x155, 0xf, 0xf, false);
-        case 6: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x156, 0xf, 0xf, false);
-        default: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x157, 0xf, 0xf, false);
-    }
-}
-__device__ __forceinline__ u32x4 row_bcast(const u32x4 &x, int u) {
-    return u32x4{row_bcast1(x[0], u), row_bcast1(x[1], u), row_bcast1(x[2], u), row_bcast1(x[3], u)};
 }
 
 struct u32x8 {
@@ -189,23 +169,20 @@ __device__ __forceinline__ void unpack8(const typename Words<WPU>::T &w, int h, 
     }
 }
 
-template <int dt, int FM, int BITS, bool XREG_, int NB>
+template <int dt, int FM, int BITS, int NB>
 __global__ __launch_bounds__(64 * (NB + 4)) void qgemm16_strip(QGemmParams q) {
-    static_assert(FM == 1 || !XREG_, "x in registers for one fragment only");
-    static_assert(NB == 1 || !XREG_, "x in registers for one strip only");
-    using G = QStrip<FM, BITS, XREG_, NB>;
-    constexpr int KS = G::KS, VPT = G::VPT, WPU = G::WPU, QD = G::DEPTH, XU = G::XU, XD = G::XD, XR = G::XR;
-    constexpr bool XREG = G::XREG;
+    using G = QStrip<FM, BITS, NB>;
+    constexpr int KS = G::KS, VPT = G::VPT, WPU = G::WPU, QD = G::DEPTH, XU = G::XU, XD = G::XD;
     constexpr int ROWB = KS * 2;                 // bytes of one LDS row (KS values of 16 bits)
     constexpr int CH = ROWB / 16;                // 16-byte chunks per LDS row
     constexpr int AR = 16 * FM;                  // x rows per workgroup
     constexpr int WROWS = 16 * NB;               // weight rows (output columns) per workgroup
-    constexpr int STAGE = (XREG ? WROWS : WROWS + AR) * ROWB;
+    constexpr int STAGE = (WROWS + AR) * ROWB;
     constexpr int SPS = KS / 32;                 // chain steps per stage
     constexpr int HS = FM == 1 ? (SPS < 8 ? SPS : 8) : (SPS < 4 ? SPS : 4);   // steps read together
     constexpr uint32_t OOB = 0x80000000u;        // offset past every resource: the load returns zeros
     using W = typename Words<WPU>::T;
-    static_assert(QD % XD == 0 && QD % 2 == 0 && (XR == 1 || XR % 2 == 0), "ring geometry");
+    static_assert(QD % XD == 0 && QD % 2 == 0, "ring geometry");
     __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
 
     const GemmParams &p = q.g;
@@ -239,22 +216,8 @@ __global__ __launch_bounds__(64 * (NB + 4)) void qgemm16_strip(QGemmParams q) {
         f32x4 acc[FM];
 #pragma unroll
         for (int f = 0; f < FM; ++f) acc[f] = zero4();
-        // one row of x (the host takes this path for M = 1 only): one load per stage, XR stages ahead,
-        // lane (r16, g) holding the 16 bytes of step r16 mod 8 and k group g; step u's fragment (row 0 in
-        // every lane) is then lane u of each 16-lane row, spread with a DPP row broadcast
-        static_assert(!XREG || SPS == 8, "one load per stage covers the stage's eight steps");
-        const uint32_t xa_lane = 64u * (uint32_t)(r16 & 7) + 16u * (uint32_t)g;
-        u32x4 xa[XR];
-        auto loadX = [&](int s, u32x4 &a) {
-            a = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                              xres, sat_off(xa_lane, stage_off(s, (uint32_t)ROWB)), 0, 0));
-        };
-        if constexpr (XREG) {
-#pragma unroll
-            for (int j = 0; j < XR; ++j) loadX(j, xa[j]);
-        }
         lds_barrier();                                   // stage 0 unpacked
-        constexpr int CU = XR == 1 ? 2 : XR;            // consumer unroll: buffer parity and x ring slot constant
+        constexpr int CU = 2;                            // consumer unroll: buffer parity constant
         for (int s0 = 0; s0 < nround; s0 += CU) {
 #pragma unroll
             for (int j = 0; j < CU; ++j) {
@@ -268,14 +231,10 @@ __global__ __launch_bounds__(64 * (NB + 4)) void qgemm16_strip(QGemmParams q) {
                         const int u = h * HS + v, c = 4 * u + g;
                         b[v] = *reinterpret_cast<const u32x4 *>(buf + (16 * cb + r16) * ROWB +
                                                                  (wslot<VPT / 8>(c, r16) << 4));
-                        if constexpr (XREG) {
-                            a[v][0] = row_bcast(xa[j % XR], u);
-                        } else {
 #pragma unroll
-                            for (int f = 0; f < FM; ++f) {
-                                const int row = WROWS + 16 * f + r16;
-                                a[v][f] = *reinterpret_cast<const u32x4 *>(buf + row * ROWB + ((c ^ (row & 15)) << 4));
-                            }
+                        for (int f = 0; f < FM; ++f) {
+                            const int row = WROWS + 16 * f + r16;
+                            a[v][f] = *reinterpret_cast<const u32x4 *>(buf + row * ROWB + ((c ^ (row & 15)) << 4));
                         }
                     }
                     const int u0 = s * SPS + h * HS;
@@ -292,7 +251,6 @@ __global__ __launch_bounds__(64 * (NB + 4)) void qgemm16_strip(QGemmParams q) {
                                 for (int f = 0; f < FM; ++f) acc[f] = Mfma<dt>::step(a[v][f], b[v], acc[f]);
                     }
                 }
-                if constexpr (XREG) loadX(s + XR, xa[j % XR]);
                 lds_barrier();                           // stage s read; stage s + 1 unpacked
             }
         }
@@ -690,15 +648,15 @@ size_t qgemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     return (size_t)(nc * K * 2);
 }
 
-template <int dt, int FM, bool XREG = false, int NB = 1>
+template <int dt, int FM, int NB = 1>
 static hipError_t launch_fm(const QGemmParams &q, hipStream_t st) {
     const int64_t nstrip = (q.g.N + 16 * NB - 1) / (16 * NB), ntile = (q.g.M + 16 * FM - 1) / (16 * FM);
     const int64_t nwg = nstrip * ntile;
     if (nwg > INT32_MAX) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)nwg), block(64 * (NB + 4));
-    if (q.bits == 2) hipLaunchKernelGGL((qgemm16_strip<dt, FM, 2, XREG, NB>), grid, block, 0, st, q);
-    else if (q.bits == 4) hipLaunchKernelGGL((qgemm16_strip<dt, FM, 4, XREG, NB>), grid, block, 0, st, q);
-    else if (q.bits == 8) hipLaunchKernelGGL((qgemm16_strip<dt, FM, 8, XREG, NB>), grid, block, 0, st, q);
+    if (q.bits == 2) hipLaunchKernelGGL((qgemm16_strip<dt, FM, 2, NB>), grid, block, 0, st, q);
+    else if (q.bits == 4) hipLaunchKernelGGL((qgemm16_strip<dt, FM, 4, NB>), grid, block, 0, st, q);
+    else if (q.bits == 8) hipLaunchKernelGGL((qgemm16_strip<dt, FM, 8, NB>), grid, block, 0, st, q);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }
@@ -708,12 +666,9 @@ static hipError_t launch_dt(const QGemmParams &q, hipStream_t st) {
     const int rows = qgemm_tile_rows(q.g.M);
     // two 16-column strips per workgroup once N is wide: x is then read half as often
     const bool wide = (q.g.N + 15) / 16 > QGEMM_WIDE_STRIPS;
-    if (rows == 16) {
-        if (q.g.M <= QGEMM_XREG_MAX_M) return launch_fm<dt, 1, true>(q, st);
-        return wide ? launch_fm<dt, 1, false, 2>(q, st) : launch_fm<dt, 1>(q, st);
-    }
-    if (rows == 32) return wide ? launch_fm<dt, 2, false, 2>(q, st) : launch_fm<dt, 2>(q, st);
-    return wide ? launch_fm<dt, 4, false, 2>(q, st) : launch_fm<dt, 4>(q, st);
+    if (rows == 16) return wide ? launch_fm<dt, 1, 2>(q, st) : launch_fm<dt, 1>(q, st);
+    if (rows == 32) return wide ? launch_fm<dt, 2, 2>(q, st) : launch_fm<dt, 2>(q, st);
+    return wide ? launch_fm<dt, 4, 2>(q, st) : launch_fm<dt, 4>(q, st);
 }
 
 // More rows: 128 x 128 tiles when they give about one tile per CU, else 64 x 64 (the 16-bit plan's

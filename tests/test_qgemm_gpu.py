@@ -44,8 +44,9 @@ CASES = [  # M, N, K, bits, gs
     (1, 4096, 4096, 4, 64), (4, 300, 384, 4, 128), (7, 513, 256, 8, 32), (16, 257, 96, 2, 32),
     (33, 1000, 1024, 4, 32), (64, 128, 640, 8, 128), (100, 96, 512, 2, 64), (200, 72, 4096, 4, 64),
     (70, 8200, 256, 4, 64),   # more than 64 rows: dequantised in two chunks of columns (8192 + 8)
-    # one row (x loaded by the consumer itself) and few rows, with partial last stages
+    # one row and few rows, with partial last stages (512-k stages for one strip per workgroup)
     (1, 100, 352, 8, 32), (1, 33, 160, 2, 32), (2, 77, 4160, 4, 64), (5, 200, 800, 2, 32),
+    (9, 2000, 1536, 8, 128), (1, 4200, 768, 8, 64), (1, 4500, 1056, 2, 32),
     # wide N (more than 256 strips of 16 columns): two strips per workgroup, ragged last pair
     (2, 4200, 512, 4, 64), (16, 4113, 288, 8, 32), (17, 5000, 384, 2, 128), (40, 4500, 640, 4, 32),
     (64, 4104, 256, 8, 64),
