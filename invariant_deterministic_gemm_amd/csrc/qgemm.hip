@@ -76,17 +76,19 @@ __device__ __forceinline__ uint32_t opaque(uint32_t x) {
 
 // Stage geometry of the fused kernel: k per stage, values each producer thread unpacks per stage (one
 // load of VPT * BITS / 8 bytes, one scale and one bias: VPT never exceeds a group), packed words per
-// unit, weight stages in flight per thread.  One strip of one row fragment takes 512-k stages (half as
-// many barriers; measured 8.1 -> 7.8 us at N = 4096, M = 1, 4-bit), two strips keep 256 (faster there).
-template <int FM, int BITS, int NB> struct QStrip {
-    static constexpr int KS = FM == 4 ? 128 : (FM == 1 && NB == 1 ? 512 : 256);
+// unit, weight stages in flight per thread; x rows staged in LDS per stage (16 FM, or XS < 16 when the
+// call has at most XS rows).
+template <int FM, int BITS, int NB, int XS, int KS_> struct QStrip {
+    static constexpr int KS = KS_;
     static constexpr int VPT = NB * KS / 16;                     // 16 NB rows x KS values over 256 threads
     static constexpr int TPR = 16 / NB;                          // producer threads per weight row
     static constexpr int WPU = VPT * BITS >= 32 ? VPT * BITS / 32 : 1;
     static constexpr bool HALF = VPT * BITS < 32;              // 2 bits, 8 values: half a word
     static constexpr int DEPTH = WPU >= 4 ? 4 : 8;
-    // x goes through LDS, XU 16-byte chunks per producer thread per stage, XD stages ahead
-    static constexpr int XU = 16 * FM * KS / 2048;
+    // x goes through LDS, XS rows of KS values: XU 16-byte chunks per producer thread per stage (the last
+    // threads may have none), XD stages ahead
+    static constexpr int XCH = XS * KS / 8;
+    static constexpr int XU = (XCH + 255) / 256;
     static constexpr int XD = FM == 1 ? 4 : 1;
 };
 
@@ -169,15 +171,17 @@ __device__ __forceinline__ void unpack8(const typename Words<WPU>::T &w, int h, 
     }
 }
 
-template <int dt, int FM, int BITS, int NB>
+template <int dt, int FM, int BITS, int NB, int XS, int KS_>
 __global__ __launch_bounds__(64 * (NB + 4)) void qgemm16_strip(QGemmParams q) {
-    using G = QStrip<FM, BITS, NB>;
+    using G = QStrip<FM, BITS, NB, XS, KS_>;
     constexpr int KS = G::KS, VPT = G::VPT, WPU = G::WPU, QD = G::DEPTH, XU = G::XU, XD = G::XD;
+    constexpr int XCH = G::XCH;
+    static_assert(XS <= 16 * FM, "x rows staged");
     constexpr int ROWB = KS * 2;                 // bytes of one LDS row (KS values of 16 bits)
     constexpr int CH = ROWB / 16;                // 16-byte chunks per LDS row
     constexpr int AR = 16 * FM;                  // x rows per workgroup
     constexpr int WROWS = 16 * NB;               // weight rows (output columns) per workgroup
-    constexpr int STAGE = (WROWS + AR) * ROWB;
+    constexpr int STAGE = (WROWS + XS) * ROWB;
     constexpr int SPS = KS / 32;                 // chain steps per stage
     constexpr int HS = FM == 1 ? (SPS < 8 ? SPS : 8) : (SPS < 4 ? SPS : 4);   // steps read together
     constexpr uint32_t OOB = 0x80000000u;        // offset past every resource: the load returns zeros
@@ -233,7 +237,8 @@ __global__ __launch_bounds__(64 * (NB + 4)) void qgemm16_strip(QGemmParams q) {
                                                                  (wslot<VPT / 8>(c, r16) << 4));
 #pragma unroll
                         for (int f = 0; f < FM; ++f) {
-                            const int row = WROWS + 16 * f + r16;
+                            // rows past XS (never stored: the call has at most XS rows) read row XS - 1
+                            const int row = WROWS + min(16 * f + r16, XS - 1);
                             a[v][f] = *reinterpret_cast<const u32x4 *>(buf + row * ROWB + ((c ^ (row & 15)) << 4));
                         }
                     }
@@ -322,7 +327,7 @@ __global__ __launch_bounds__(64 * (NB + 4)) void qgemm16_strip(QGemmParams q) {
 #pragma unroll
     for (int f = 0; f < XUA; ++f) {
         const int u = tid + 256 * f, r = u / CH, c = u % CH;
-        x_lane[f] = r < xrows ? (uint32_t)r * xrow_b + (uint32_t)c * 16u : OOB;
+        x_lane[f] = (XCH % 256 == 0 || u < XCH) && r < xrows ? (uint32_t)r * xrow_b + (uint32_t)c * 16u : OOB;
     }
     u32x4 araw[XD][XUA];
     auto loadA = [&](int s, u32x4 (&a)[XUA]) {
@@ -336,7 +341,7 @@ __global__ __launch_bounds__(64 * (NB + 4)) void qgemm16_strip(QGemmParams q) {
         for (int f = 0; f < XU; ++f) {
             const int u = tid + 256 * f, r = u / CH, c = u % CH;
             const int row = WROWS + r;
-            *reinterpret_cast<u32x4 *>(buf + row * ROWB + ((c ^ (row & 15)) << 4)) = a[f];
+            if (XCH % 256 == 0 || u < XCH) *reinterpret_cast<u32x4 *>(buf + row * ROWB + ((c ^ (row & 15)) << 4)) = a[f];
         }
     };
 
@@ -638,6 +643,9 @@ __global__ __launch_bounds__(256) void qdequant16(QGemmParams q, int n0, int nc,
               round_pack<dt>(w[6], w[7])};
 }
 
+#ifndef KSW4
+#define KSW4 256
+#endif
 int qgemm_tile_rows(int M) { return M <= 16 ? 16 : (M <= 32 ? 32 : 64); }
 
 bool qgemm_uses_workspace(int64_t M, int64_t K) { return M > QGEMM_FUSED_MAX_M && K % QGEMM_TILE_K != 0; }
@@ -648,15 +656,15 @@ size_t qgemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     return (size_t)(nc * K * 2);
 }
 
-template <int dt, int FM, int NB = 1>
+template <int dt, int FM, int NB, int XS, int KS>
 static hipError_t launch_fm(const QGemmParams &q, hipStream_t st) {
     const int64_t nstrip = (q.g.N + 16 * NB - 1) / (16 * NB), ntile = (q.g.M + 16 * FM - 1) / (16 * FM);
     const int64_t nwg = nstrip * ntile;
     if (nwg > INT32_MAX) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)nwg), block(64 * (NB + 4));
-    if (q.bits == 2) hipLaunchKernelGGL((qgemm16_strip<dt, FM, 2, NB>), grid, block, 0, st, q);
-    else if (q.bits == 4) hipLaunchKernelGGL((qgemm16_strip<dt, FM, 4, NB>), grid, block, 0, st, q);
-    else if (q.bits == 8) hipLaunchKernelGGL((qgemm16_strip<dt, FM, 8, NB>), grid, block, 0, st, q);
+    if (q.bits == 2) hipLaunchKernelGGL((qgemm16_strip<dt, FM, 2, NB, XS, KS>), grid, block, 0, st, q);
+    else if (q.bits == 4) hipLaunchKernelGGL((qgemm16_strip<dt, FM, 4, NB, XS, KS>), grid, block, 0, st, q);
+    else if (q.bits == 8) hipLaunchKernelGGL((qgemm16_strip<dt, FM, 8, NB, XS, KS>), grid, block, 0, st, q);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }
@@ -666,9 +674,10 @@ static hipError_t launch_dt(const QGemmParams &q, hipStream_t st) {
     const int rows = qgemm_tile_rows(q.g.M);
     // two 16-column strips per workgroup once N is wide: x is then read half as often
     const bool wide = (q.g.N + 15) / 16 > QGEMM_WIDE_STRIPS;
-    if (rows == 16) return wide ? launch_fm<dt, 1, 2>(q, st) : launch_fm<dt, 1>(q, st);
-    if (rows == 32) return wide ? launch_fm<dt, 2, 2>(q, st) : launch_fm<dt, 2>(q, st);
-    return wide ? launch_fm<dt, 4, 2>(q, st) : launch_fm<dt, 4>(q, st);
+    if (rows == 16 && q.g.M <= 4) return wide ? launch_fm<dt, 1, 2, 4, KSW4>(q, st) : launch_fm<dt, 1, 1, 4, 512>(q, st);
+    if (rows == 16) return wide ? launch_fm<dt, 1, 2, 16, 256>(q, st) : launch_fm<dt, 1, 1, 16, 512>(q, st);
+    if (rows == 32) return wide ? launch_fm<dt, 2, 2, 32, 256>(q, st) : launch_fm<dt, 2, 1, 32, 256>(q, st);
+    return wide ? launch_fm<dt, 4, 2, 64, 128>(q, st) : launch_fm<dt, 4, 1, 64, 128>(q, st);
 }
 
 // More rows: 128 x 128 tiles when they give about one tile per CU, else 64 x 64 (the 16-bit plan's
