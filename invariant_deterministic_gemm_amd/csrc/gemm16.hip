@@ -538,8 +538,11 @@ struct StripCfg { int nb, fm, ar, ns, nl; };
 static bool wide_n(int N) { return (N + 15) / 16 > 256; }
 static StripCfg strip_cfg(int M, int N) {
     // 32-column strips halve the re-reads of A once N is wide
+    // A rows staged per stage follow M, and 16 of them take a 4-deep ring: the LDS per workgroup then
+    // lets every 16-column strip of N = 14336 be resident at once (M = 8: 27.1 -> 25.2 us there)
     if (M <= 4) return StripCfg{1, 1, 4, 6, 3};
-    if (M <= 16) return StripCfg{1, 1, 16, 6, 3};
+    if (M <= 8) return StripCfg{1, 1, 8, 6, 3};
+    if (M <= 16) return StripCfg{1, 1, 16, 4, 3};
     if (M <= 32) return wide_n(N) ? StripCfg{2, 2, 32, 4, 3} : StripCfg{1, 2, 32, 4, 3};
     return wide_n(N) ? StripCfg{2, 4, 64, 3, 3} : StripCfg{1, 4, 64, 4, 3};
 }
@@ -590,7 +593,8 @@ static hipError_t launch16_typed(const GemmParams &p, hipStream_t st) {
         const StripCfg c = strip_cfg(p.M, p.N);
         const dim3 grid((p.N + 16 * c.nb - 1) / (16 * c.nb), p.splits), block(64 * (1 + c.nl));
         if (c.ar == 4) hipLaunchKernelGGL((gemm16_strip<idt, odt, 1, 1, 4, 6, 3>), grid, block, 0, st, p);
-        else if (c.ar == 16) hipLaunchKernelGGL((gemm16_strip<idt, odt, 1, 1, 16, 6, 3>), grid, block, 0, st, p);
+        else if (c.ar == 8) hipLaunchKernelGGL((gemm16_strip<idt, odt, 1, 1, 8, 6, 3>), grid, block, 0, st, p);
+        else if (c.ar == 16) hipLaunchKernelGGL((gemm16_strip<idt, odt, 1, 1, 16, 4, 3>), grid, block, 0, st, p);
         else if (c.ar == 32 && c.nb == 1) hipLaunchKernelGGL((gemm16_strip<idt, odt, 1, 2, 32, 4, 3>), grid, block, 0, st, p);
         else if (c.ar == 32) hipLaunchKernelGGL((gemm16_strip<idt, odt, 2, 2, 32, 4, 3>), grid, block, 0, st, p);
         else if (c.nb == 1) hipLaunchKernelGGL((gemm16_strip<idt, odt, 1, 4, 64, 4, 3>), grid, block, 0, st, p);
