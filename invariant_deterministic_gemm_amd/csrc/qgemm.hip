@@ -643,9 +643,6 @@ __global__ __launch_bounds__(256) void qdequant16(QGemmParams q, int n0, int nc,
               round_pack<dt>(w[6], w[7])};
 }
 
-#ifndef KSW4
-#define KSW4 256
-#endif
 int qgemm_tile_rows(int M) { return M <= 16 ? 16 : (M <= 32 ? 32 : 64); }
 
 bool qgemm_uses_workspace(int64_t M, int64_t K) { return M > QGEMM_FUSED_MAX_M && K % QGEMM_TILE_K != 0; }
@@ -674,7 +671,10 @@ static hipError_t launch_dt(const QGemmParams &q, hipStream_t st) {
     const int rows = qgemm_tile_rows(q.g.M);
     // two 16-column strips per workgroup once N is wide: x is then read half as often
     const bool wide = (q.g.N + 15) / 16 > QGEMM_WIDE_STRIPS;
-    if (rows == 16 && q.g.M <= 4) return wide ? launch_fm<dt, 1, 2, 4, KSW4>(q, st) : launch_fm<dt, 1, 1, 4, 512>(q, st);
+    // one 16-row fragment: 512-k stages for one strip per workgroup (8.1 -> 7.8 us at N = 4096, M = 1),
+    // 256 for two (512 was slower there); calls of at most four rows stage four x rows (more workgroups
+    // per CU: M = 1 7.9 -> 7.0 us at N = 4096, 15.0 -> 13.8 at N = 14336)
+    if (rows == 16 && q.g.M <= 4) return wide ? launch_fm<dt, 1, 2, 4, 256>(q, st) : launch_fm<dt, 1, 1, 4, 512>(q, st);
     if (rows == 16) return wide ? launch_fm<dt, 1, 2, 16, 256>(q, st) : launch_fm<dt, 1, 1, 16, 512>(q, st);
     if (rows == 32) return wide ? launch_fm<dt, 2, 2, 32, 256>(q, st) : launch_fm<dt, 2, 1, 32, 256>(q, st);
     return wide ? launch_fm<dt, 4, 2, 64, 128>(q, st) : launch_fm<dt, 4, 1, 64, 128>(q, st);
