@@ -449,6 +449,8 @@ __device__ __forceinline__ void rows16_load(const SdpaParams &p, int tile, int b
 // of key r at slot c ^ (r mod 16)): lane holds S^T[key 16 kt + 4 g + i][row r16].  The K fragments of
 // four d chunks are read first; the four chains (one per kt) each accumulate d chunks c = 0 .. NC - 1
 // in order.  The K reads may still be in flight on return.
+// Rows of 64 values (D = 64) are 128 bytes: chunk c of key r at slot c ^ ((r / 2) mod 8) instead, which keeps
+// the 16 rows of one read pass on distinct bank groups.
 template <int dt, int NC>
 __device__ __forceinline__ void attn_scores16(const Rows16T<NC> &r, const char *Ks, f32x4 (&st)[4]) {
     constexpr int ROWB = 64 * NC;
@@ -456,6 +458,19 @@ __device__ __forceinline__ void attn_scores16(const Rows16T<NC> &r, const char *
     const int r16 = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) st[kt] = zero4();
+    if constexpr (NC == 2) {
+        u32x4 kf[4][2];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+                kf[kt][c] = *reinterpret_cast<const u32x4 *>(Ks + (16 * kt + r16) * ROWB +
+                                                             (((4 * c + g) ^ ((r16 >> 1) & 7)) << 4));
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) st[kt] = Mfma<dt>::step(kf[kt][c], r.qf[c], st[kt]);
+    }
 #pragma unroll
     for (int h = 0; h < NC / 4; ++h) {
         u32x4 kf[4][4];
@@ -547,6 +562,12 @@ __device__ __forceinline__ void attn_softmax16(const SdpaParams &p, const Rows16
 
 // V fragments of 32-key half c for the NT 16-column tiles (V block in LDS, 32 NT-byte rows, chunk c of key
 // r at slot c ^ 2 (r mod 8)): B operand of P . V, k slot j as in attn_softmax16.
+// Rows of 64 values (NT = 4) are 128 bytes: chunk c of key r at slot c ^ 2 ((r / 2) mod 4).
+template <int NT>
+__device__ __forceinline__ int vswz16(int row) {
+    if constexpr (NT == 4) return ((row >> 1) & 3) << 1;
+    else return (row & 7) << 1;
+}
 template <int NT>
 __device__ __forceinline__ void attn_vfrags16(const char *Vs, int c, u32x4 (&vf)[NT]) {
     constexpr int ROWB = 32 * NT;
@@ -558,8 +579,8 @@ __device__ __forceinline__ void attn_vfrags16(const char *Vs, int c, u32x4 (&vf)
     for (int t = 0; t < NT; ++t) {
         const int ch = 2 * t + ((r16 & 3) >> 1);
         const int off = 8 * (r16 & 1);
-        const u32x2 lo = lds_read_tr16(Vs + row0 * ROWB + ((ch ^ ((row0 & 7) << 1)) << 4) + off);
-        const u32x2 hi = lds_read_tr16(Vs + row1 * ROWB + ((ch ^ ((row1 & 7) << 1)) << 4) + off);
+        const u32x2 lo = lds_read_tr16(Vs + row0 * ROWB + ((ch ^ vswz16<NT>(row0)) << 4) + off);
+        const u32x2 hi = lds_read_tr16(Vs + row1 * ROWB + ((ch ^ vswz16<NT>(row1)) << 4) + off);
         vf[t] = u32x4{lo[0], lo[1], hi[0], hi[1]};
     }
 }
@@ -618,6 +639,7 @@ __device__ __forceinline__ void split16_body(const SdpaParams &p, int sp, int ti
     constexpr int SPR = ROWB / 16;                    // 16-byte slots per key row
     constexpr int KP = 16 / RPQ, VP = 8 / RPQ;        // periods (in q) of the K and V chunk patterns
     static_assert(QB == 16 * NC / 4 && QB <= 63, "load count per block half");
+    static_assert(NC == 2 || NC >= 4, "rows of 64 values or of at least 128");
     constexpr float NEG_INF = -__builtin_huge_valf();
     const int lane = threadIdx.x & 63;
     const int R = p.G * p.Lq;
@@ -647,13 +669,14 @@ __device__ __forceinline__ void split16_body(const SdpaParams &p, int sp, int ti
     bool kz[KP], vz[VP];                              // chunk at d >= D: read the zero page
 #pragma unroll
     for (int r = 0; r < KP; ++r) {
-        const int c = lslot ^ ((RPQ * r + lrow) & 15);
+        const int row = RPQ * r + lrow;
+        const int c = lslot ^ (NC == 2 ? (row >> 1) & 7 : row & 15);
         kch[r] = c << 4;
         kz[r] = 8 * c >= p.dr;
     }
 #pragma unroll
     for (int r = 0; r < VP; ++r) {
-        const int c = lslot ^ (((RPQ * r + lrow) & 7) << 1);
+        const int c = lslot ^ vswz16<2 * NC>(RPQ * r + lrow);
         vch[r] = c << 4;
         vz[r] = 8 * c >= p.dr;
     }
@@ -706,7 +729,7 @@ __device__ __forceinline__ void split16_body(const SdpaParams &p, int sp, int ti
 #pragma unroll
     for (int t = 0; t < 2 * NC; ++t) o[t] = zero4();
 
-    if constexpr (NC == 4) {
+    if constexpr (NC <= 4) {
         // at most one K block and one V block (32 loads) in flight
         if (nblk > 0) {
             issueK(0, 0, QB);
@@ -1889,11 +1912,11 @@ static hipError_t launch_typed(const SdpaParams &p, hipStream_t st) {
             if (e != hipSuccess || p.nsplit == 1) return e;      // one split: no combine
         }
     } else if (p.nsplit > 0) {
-        if constexpr (dt != DT_F32 && D == 128) {     // (below 128 the generic kernel decodes faster)
+        if constexpr (dt != DT_F32 && (D == 128 || D == 64)) {   // (D = 32, 96: the generic kernel)
             constexpr int W = 2;                         // splits per workgroup (measured best for long caches)
             const int64_t nwg = (int64_t)((p.nsplit + W - 1) / W) * ((R + 15) / 16) * p.B * p.Hkv;
             if (nwg > INT32_MAX) return hipErrorInvalidConfiguration;
-            hipLaunchKernelGGL((sdpa_split16<dt, W>), dim3((unsigned)nwg), dim3(64 * W), 0, st, p);
+            hipLaunchKernelGGL((sdpa_split16<dt, W, D / 32>), dim3((unsigned)nwg), dim3(64 * W), 0, st, p);
         } else if (dt != DT_F32 && D == 256 && path == SDPA_SPLIT16W) {
             if constexpr (dt != DT_F32 && D == 256) {
                 constexpr int W = 2;
@@ -1983,7 +2006,7 @@ const char *sdpa_kernel_name(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int
         case SDPA_PREFILL16: return D > 128 ? "sdpa_prefill16w" : "sdpa_prefill16";
         case SDPA_QUAD16: return S <= KV_SPLIT ? "sdpa_quad16" : "sdpa_quad16+combine";
         case SDPA_SPLIT16W: return "sdpa_split16w+combine";
-        default: return dt != DT_F32 && D == 128 ? "sdpa_split16+combine" : "sdpa_split+combine";
+        default: return dt != DT_F32 && (D == 128 || D == 64) ? "sdpa_split16+combine" : "sdpa_split+combine";
     }
 }
 

@@ -274,6 +274,8 @@ def test_kernel_name_queries(lib):
     assert name(64, 32, 8, 1, 300, 64, BF16) == "sdpa_fused16"
     assert name(1, 32, 8, 1, 3000, 96, BF16) == "sdpa_quad16+combine"
     assert name(8, 32, 8, 1, 3000, 96, BF16) == "sdpa_split+combine"
+    assert name(8, 32, 8, 1, 8192, 64, BF16) == "sdpa_split16+combine"         # 128-byte key rows
+    assert name(8, 32, 8, 1, 8192, 64, F32) == "sdpa_split+combine"
     assert name(1, 32, 8, 1, 300, 160, BF16) == "sdpa_split+combine"
     assert name(8, 32, 8, 1, 8192, 256, BF16) == "sdpa_split16w+combine"       # 16 x 1 x 8 x 8 = 1024
     assert name(9, 32, 8, 1, 8192, 256, BF16) == "sdpa_split+combine"

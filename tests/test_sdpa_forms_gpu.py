@@ -166,12 +166,13 @@ def test_head_dims_multiple_of_32(dt, D):
 @pytest.mark.parametrize("D", [32, 64, 96])
 @pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16], ids=_ids)
 def test_small_head_dims_agree_across_kernels(dt, D):
-    """16-bit D < 128: the prefill kernel and the generic split kernel take the head dim's own D / 32
-    score chunks and D / 16 output tiles, the quad and one-launch kernels run on rows zero-padded to 128
-    (the zero products only add exact zeros), so every path gives the same bits.  Prefill chunk (prefill
-    kernel) vs the decode of its tokens (quad kernel) and vs the oracle, a masked prefill vs the same
-    rows called few at a time (split kernel), and one batch element alone (quad kernel) vs inside a
-    batch of 40 (one launch at S <= 1024, the generic split kernel above)."""
+    """16-bit D < 128: the prefill kernel and the split kernels take the head dim's own D / 32 score
+    chunks and D / 16 output tiles (D = 64 on the 16-bit split kernel with 128-byte key rows, D = 32 and 96
+    on the generic one), the quad and one-launch kernels run on rows zero-padded to 128 (the zero
+    products only add exact zeros), so every path gives the same bits.  Prefill chunk (prefill kernel) vs
+    the decode of its tokens (quad kernel) and vs the oracle, a masked prefill vs the same rows called
+    few at a time (split kernel), and one batch element alone (quad kernel) vs inside a batch of 40 (one
+    launch at S <= 1024, a split kernel above)."""
     B, Hq, Hkv, Lq, S = 1, 8, 2, 400, 1500
     BI = bi.BI_BF16 if dt == torch.bfloat16 else bi.BI_F16
     qc, kc, vc = _qkv(B, Hq, Hkv, Lq, S, D, dt, 370 + D)
@@ -195,7 +196,8 @@ def test_small_head_dims_agree_across_kernels(dt, D):
         assert name(B, Hq, Hkv, 4, S) != "sdpa_prefill16"
         part = bi.bi_sdpa(q[:, :, a:a + 4], k, v, mask=mask[:, :, a:a + 4])
         assert_bits_equal(part, masked[:, :, a:a + 4], f"D={D}: masked prefill rows {a}.. vs four at a time")
-    for S2, big_kernel in ((900, "sdpa_fused16"), (1500, "sdpa_split+combine")):
+    split_kernel = "sdpa_split16+combine" if D == 64 else "sdpa_split+combine"
+    for S2, big_kernel in ((900, "sdpa_fused16"), (1500, split_kernel)):
         qd, kd, vd = q[:, :, :2], k[:, :, :S2], v[:, :, :S2]
         assert name(1, Hq, Hkv, 2, S2) == "sdpa_quad16+combine" and name(40, Hq, Hkv, 2, S2) == big_kernel
         one = bi.bi_sdpa(qd, kd, vd, causal=True)
