@@ -1268,11 +1268,11 @@ __device__ __forceinline__ u32x2 lds_tr16_at(uint32_t addr) {
     const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(size_t)addr);
     return __builtin_bit_cast(u32x2, v);
 }
-template <int HOFF, int NT>
+template <int HOFF, int NT, int ROWB = 256>
 __device__ __forceinline__ void vfrags_tr(const uint32_t (&va)[NT], u32x4 (&vf)[NT]) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-        const u32x2 lo = lds_tr16_at(va[t] + HOFF), hi = lds_tr16_at(va[t] + HOFF + 16 * 256);
+        const u32x2 lo = lds_tr16_at(va[t] + HOFF), hi = lds_tr16_at(va[t] + HOFF + 16 * ROWB);
         vf[t] = u32x4{lo[0], lo[1], hi[0], hi[1]};
     }
 }
@@ -1297,7 +1297,11 @@ void sdpa_prefill16p(SdpaParams p) {
     constexpr int NC = D / 32;                         // d chunks of the score chains
     constexpr int NT = D / 16;                         // output column tiles
     static_assert(D % 32 == 0 && D <= 128, "head dims 32, 64, 96, 128");
-    constexpr int ROWB = 256;
+    // key rows of 256 bytes (chunks at d >= D neither loaded nor read), or of 128 for D = 64, which halves
+    // the LDS per workgroup so that its ~150 registers per lane can run three wavefronts per SIMD
+    constexpr bool C128 = D == 64;
+    constexpr int ROWB = C128 ? 128 : 256;
+    constexpr int RPL = 1024 / ROWB;                   // key rows per 1 KiB load
     constexpr int KBYTES = KV_BLOCK * ROWB;            // one K or V block
     constexpr int QW = KBYTES / 1024 / W;              // 1 KiB loads per wavefront per K (or V) block
     constexpr int BPS = KV_SPLIT / KV_BLOCK;           // blocks per split
@@ -1332,16 +1336,19 @@ void sdpa_prefill16p(SdpaParams p) {
     const char *kbase = static_cast<const char *>(p.k) + ((int64_t)b * p.ks[0] + (int64_t)gk * p.ks[1]) * 2;
     const char *vbase = static_cast<const char *>(p.v) + ((int64_t)b * p.vs[0] + (int64_t)gk * p.vs[1]) * 2;
     const int64_t kstr = p.ks[2] * 2, vstr = p.vs[2] * 2;
-    // load j of a K (or V) block covers key rows 4 q .. 4 q + 3, q = wave + W j: lane L row 4 q + L / 16,
-    // slot L mod 16 (K chunk slot ^ (row mod 16), V chunk slot ^ 2 (row mod 8)).  A block inside S is a
-    // uniform base plus these 32-bit lane offsets; the block crossing S (and every block when a key row
-    // stride is too large for 32-bit offsets) clamps rows to S - 1 in 64-bit arithmetic.
-    const int lrow = lane >> 4, lslot = lane & 15;
+    // load j of a K (or V) block covers key rows RPL q .. RPL q + RPL - 1, q = wave + W j: lane L row
+    // RPL q + L / SPR, slot L mod SPR (K chunk slot ^ (row mod 16), V chunk slot ^ 2 (row mod 8); for
+    // 128-byte rows K slot ^ ((row / 2) mod 8), V slot ^ 2 ((row / 2) mod 4)).  A block
+    // inside S is a uniform base plus these 32-bit lane offsets; the block crossing S (and every block when
+    // a key row stride is too large for 32-bit offsets) clamps rows to S - 1 in 64-bit arithmetic.
+    constexpr int SPR = ROWB / 16;                     // slots per key row
+    const int lrow = lane / SPR, lslot = lane % SPR;
     const bool off32 = (uint64_t)max(kstr, vstr) * KV_BLOCK + ROWB <= 0xffffffffull;
-    // the chunk slots do not depend on j (4 W j is a multiple of 16), so load j is load 0 plus 4 W j rows
-    static_assert((4 * W) % 16 == 0, "row period of the chunk swizzles");
-    const int row0 = 4 * wave + lrow;
-    const int ck = lslot ^ (row0 & 15), cv = lslot ^ ((row0 & 7) << 1);
+    // the chunk slots do not depend on j (RPL W j is a multiple of 16), so load j is load 0 plus RPL W j rows
+    static_assert((RPL * W) % 16 == 0, "row period of the chunk swizzles");
+    const int row0 = RPL * wave + lrow;
+    const int ck = lslot ^ (C128 ? (row0 >> 1) & 7 : row0 & 15);
+    const int cv = lslot ^ (C128 ? ((row0 >> 1) & 3) << 1 : (row0 & 7) << 1);
     const bool kin = 8 * ck < D, vin = 8 * cv < D;     // this lane's chunk lies inside the head dim
     const uint32_t koff = (uint32_t)(row0 * kstr) + (ck << 4), voff = (uint32_t)(row0 * vstr) + (cv << 4);
     auto issue = [&](int blk, char *buf, bool isv) {
@@ -1353,11 +1360,11 @@ void sdpa_prefill16p(SdpaParams p) {
             if (off32 && kb + KV_BLOCK <= p.S) {
 #pragma unroll
                 for (int j = 0; j < QW; ++j)
-                    dma16_saddr(base + (int64_t)(kb + 4 * W * j) * str, isv ? voff : koff, lbase + W * j * 1024);
+                    dma16_saddr(base + (int64_t)(kb + RPL * W * j) * str, isv ? voff : koff, lbase + W * j * 1024);
             } else {
 #pragma unroll
                 for (int j = 0; j < QW; ++j) {
-                    const int row = row0 + 4 * W * j;
+                    const int row = row0 + RPL * W * j;
                     const int64_t key = min(kb + row, p.S - 1);
                     dma16_vaddr(base + key * str + ((isv ? cv : ck) << 4), lbase + W * j * 1024);
                 }
@@ -1391,7 +1398,8 @@ void sdpa_prefill16p(SdpaParams p) {
     for (int t = 0; t < NT; ++t) {
         const int row0 = 4 * g + (r16 >> 2);
         const int ch = 2 * t + ((r16 & 3) >> 1);
-        const uint32_t off = (uint32_t)(row0 * ROWB + ((ch ^ ((row0 & 7) << 1)) << 4) + 8 * (r16 & 1));
+        const int sw = C128 ? ((row0 >> 1) & 3) << 1 : (row0 & 7) << 1;      // same for row0 + 16, + 32
+        const uint32_t off = (uint32_t)(row0 * ROWB + ((ch ^ sw) << 4) + 8 * (r16 & 1));
         va[t] = (uint32_t)(uintptr_t)BI_LDS_PTR(vbufs) + off;
     }
     // scores of a block from its K block: each key tile's chain takes d chunks 0 .. NC - 1 in order
@@ -1401,7 +1409,8 @@ void sdpa_prefill16p(SdpaParams p) {
             u32x4 kf[NC];
 #pragma unroll
             for (int c = 0; c < NC; ++c)
-                kf[c] = *reinterpret_cast<const u32x4 *>(Ks + (16 * kt + r16) * ROWB + (((4 * c + g) ^ r16) << 4));
+                kf[c] = *reinterpret_cast<const u32x4 *>(Ks + (16 * kt + r16) * ROWB +
+                                                         (((4 * c + g) ^ (C128 ? (r16 >> 1) & 7 : r16)) << 4));
             st[kt] = zero4();
 #pragma unroll
             for (int c = 0; c < NC; ++c) st[kt] = Mfma<dt>::step(kf[c], r.qf[c], st[kt]);
@@ -1410,8 +1419,8 @@ void sdpa_prefill16p(SdpaParams p) {
     // the V fragments of V buffer VB (both 32-key halves), and O += P . V from them
     auto vread = [&](auto vb, u32x4 (&vf)[2][NT]) {
         constexpr int VB = decltype(vb)::value;
-        vfrags_tr<VB * KBYTES>(va, vf[0]);
-        vfrags_tr<VB * KBYTES + 32 * ROWB>(va, vf[1]);
+        vfrags_tr<VB * KBYTES, NT, ROWB>(va, vf[0]);
+        vfrags_tr<VB * KBYTES + 32 * ROWB, NT, ROWB>(va, vf[1]);
     };
     // O^T += V^T . P^T: the V fragments as the A operand and P as the B operand give each element the
     // products and k order of O += P . V, with rows and columns of the tile swapped
@@ -1435,7 +1444,7 @@ void sdpa_prefill16p(SdpaParams p) {
             // V rows past S read as zero; each wavefront clears the rows its own loads filled
 #pragma unroll
             for (int jj = 0; jj < QW; ++jj) {
-                const int row = 4 * (wave + W * jj) + lrow;
+                const int row = RPL * (wave + W * jj) + lrow;
                 if (kb + row >= p.S) *reinterpret_cast<u32x4 *>(vcur + row * ROWB + lslot * 16) = zero_u4();
             }
             __builtin_amdgcn_s_waitcnt(0xc07f);
