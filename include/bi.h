@@ -395,12 +395,13 @@ const char *bi_gemm_kernel_name(int64_t M, int64_t N, int64_t K, bi_dtype in_dt,
  * row-tile groups x B x Hkv workgroups with T = 1 or 2 row tiles per
  * workgroup, is at most 256 (one workgroup per CU: every split's K / V
  * requested at once); else "sdpa_fused16" when S <= 1024, and
- * "sdpa_split16+combine" (D = 128) or "sdpa_split+combine" (D < 128)
- * otherwise.  For 16-bit dt and D > 128: "sdpa_prefill16w" when Lq >= 384, or
+ * "sdpa_split16+combine" (D = 128, and D = 64 on 128-byte key rows) or
+ * "sdpa_split+combine" (D = 32, 96) otherwise.  For 16-bit dt and D > 128: "sdpa_prefill16w" when Lq >= 384, or
  * Lq >= 64 with B Lq >= 192 (rows of 256, all output columns in one workgroup);
  * else, for D = 256 with at most 1024 workgroups of two splits and one row
  * tile, "sdpa_split16w+combine"; else "sdpa_split+combine".  fp32 runs "sdpa_split+combine".  16-bit D < 128
- * runs the prefill, quad and one-launch kernels on rows zero-padded to 128,
+ * runs the quad and one-launch kernels on rows zero-padded to 128 (the prefill kernel computes only the
+ * head dim's chunks),
  * D = 160 ... 224 the wide prefill on rows zero-padded to 256 (the padding
  * adds exact zeros, so the bits are the split kernel's).
  * Informational: the split / block structure, and with it every output bit,
