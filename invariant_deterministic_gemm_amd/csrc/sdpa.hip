@@ -1943,14 +1943,13 @@ static hipError_t launch_typed(const SdpaParams &p, hipStream_t st) {
     }
     const dim3 g2((unsigned)((int64_t)p.B * p.Hq * p.Lq));
     // the same fold with fewer loads in flight for short caches (measured 0.5-1.3 us less at four splits),
-    // and through LDS for long ones: up to 64 KiB of partials per memory round trip, the staging sized to
-    // the split count so that short folds keep more workgroups per CU
+    // and through LDS for long ones, 32 partials per chunk: more workgroups per CU than with 128-partial
+    // staging, and the next chunk's loads overlap the fold (B = 32, 8192 keys: 198.6 -> 193.5 us; 32768
+    // keys: 742.6 -> 734.8)
     if (p.nsplit <= 4) hipLaunchKernelGGL((sdpa_combine<dt, D, 4>), g2, dim3(D), 0, st, p);
     else if (p.nsplit <= 8) hipLaunchKernelGGL((sdpa_combine<dt, D, 8>), g2, dim3(D), 0, st, p);
     else if (p.nsplit <= 16) hipLaunchKernelGGL((sdpa_combine<dt, D>), g2, dim3(D), 0, st, p);
-    else if (p.nsplit <= 32) hipLaunchKernelGGL((sdpa_combine_lds<dt, D, 32>), g2, dim3(256), 0, st, p);
-    else if (p.nsplit <= 64 || D > 128) hipLaunchKernelGGL((sdpa_combine_lds<dt, D, 64>), g2, dim3(256), 0, st, p);
-    else hipLaunchKernelGGL((sdpa_combine_lds<dt, D, 128>), g2, dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((sdpa_combine_lds<dt, D, 32>), g2, dim3(256), 0, st, p);
     return hipGetLastError();
 }
 
