@@ -311,6 +311,37 @@ def test_wide_split_matches_generic_split(dt):
         assert_close_to_oracle(bi.bi_sdpa(qg, kg, vg, causal=True, mask=ag, sinks=sg), want, f"Lq={Lq}: wide vs oracle")
 
 
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16], ids=_ids)
+def test_d64_split_matches_quad(dt):
+    """16-bit D = 64 decode: the 16-bit split kernel on 128-byte key rows (large grids) and the quad kernel
+    on rows zero-padded to 128 (small grids) give the same bits: one batch element alone against the same
+    element inside a batch of 40, causal, with an additive mask and sinks, with a ragged cache and three
+    query rows; the split kernel also matches the oracle."""
+    Hq, Hkv, D, NB = 8, 2, 64, 40
+    BI = bi.BI_BF16 if dt == torch.bfloat16 else bi.BI_F16
+    lib = bi._native.load()
+    for Lq, S in ((1, 7000), (3, 6500)):
+        q, k, v = _qkv(1, Hq, Hkv, Lq, S, D, dt, 410 + Lq)
+        amask = _additive((1, 1, Lq, S), 411 + Lq, dt)
+        amask[..., 0] = 0.0
+        sinks = synthetic.randn((Hq,), 412 + Lq, 2.0)
+        assert lib.bi_sdpa_kernel_name(1, Hq, Hkv, Lq, S, D, BI).decode() == "sdpa_quad16+combine"
+        assert lib.bi_sdpa_kernel_name(NB, Hq, Hkv, Lq, S, D, BI).decode() == "sdpa_split16+combine"
+        qg, kg, vg, ag, sg = _gpu(q, k, v, amask, sinks)
+        rep = lambda t: t.expand(NB, *t.shape[1:]).contiguous()
+        for what, kw in (("causal", dict(causal=True)), ("additive+sinks", dict(causal=True, mask=ag, sinks=sg))):
+            one = bi.bi_sdpa(qg, kg, vg, **kw)
+            kwb = dict(kw)
+            if "mask" in kw:
+                kwb["mask"] = rep(kw["mask"])
+            many = bi.bi_sdpa(rep(qg), rep(kg), rep(vg), **kwb)
+            for e in (0, NB - 1):
+                assert_bits_equal(many[e:e + 1], one, f"Lq={Lq} S={S} {what}: split element {e} vs quad")
+        want = oracle.sdpa(q, k, v, causal=True, mask=amask.to(torch.float64), sinks=sinks)
+        many = bi.bi_sdpa(rep(qg), rep(kg), rep(vg), causal=True, mask=rep(ag), sinks=sg)
+        assert_close_to_oracle(many[:1], want, f"Lq={Lq}: split vs oracle")
+
+
 def test_forms_together_and_bad_arguments():
     B, Hq, Hkv, Lq, S, D = 1, 8, 4, 6, 520, 64
     dt = torch.bfloat16
