@@ -32,6 +32,7 @@ when the counters were taken.
 from __future__ import annotations
 
 import argparse
+import contextlib
 import csv
 import ctypes
 import glob
@@ -813,28 +814,27 @@ def measure_cells(ctx, names=None):
     return cells
 
 
+@contextlib.contextmanager
 def _variant_mode(torch, bi):
     """F.linear and F.scaled_dot_product_attention on the batch-variant comparator kernels
     (bi_variant_linear with its M-keyed split-K, bi_variant_sdpa with its shape-keyed splits); every
-    other op runs stock.  The end-to-end analogue of the kernels' comparator."""
+    other op runs stock.  The end-to-end analogue of the kernels' comparator, installed the way
+    batch_invariant_mode installs its routes (the two functions replaced while the block runs)."""
     import torch.nn.functional as F
-    from torch.overrides import TorchFunctionMode
+    lin, att = F.linear, F.scaled_dot_product_attention
 
-    class VariantMode(TorchFunctionMode):
-        def __torch_function__(self, func, types, args=(), kwargs=None):
-            kwargs = kwargs or {}
-            if func is F.linear:
-                x, w = args[0], args[1]
-                b = args[2] if len(args) > 2 else kwargs.get("bias")
-                return bi.bi_variant_linear(x, w, b)
-            if func is F.scaled_dot_product_attention:
-                q, k, v = args[:3]
-                causal = kwargs.get("is_causal", False)
-                assert not causal or q.shape[2] == k.shape[2]
-                return bi.bi_variant_sdpa(q, k, v, causal=causal, scale=kwargs.get("scale"))
-            return func(*args, **kwargs)
+    def linear(x, w, bias=None):
+        return bi.bi_variant_linear(x, w, bias)
 
-    return VariantMode()
+    def sdpa(q, k, v, attn_mask=None, dropout_p=0.0, is_causal=False, scale=None, enable_gqa=False):
+        assert attn_mask is None and dropout_p == 0.0 and (not is_causal or q.shape[2] == k.shape[2])
+        return bi.bi_variant_sdpa(q, k, v, causal=is_causal, scale=scale)
+
+    F.linear, F.scaled_dot_product_attention = linear, sdpa
+    try:
+        yield
+    finally:
+        F.linear, F.scaled_dot_product_attention = lin, att
 
 
 def e2e_run(torch, bi, dev, synthetic):

@@ -9,7 +9,10 @@ that patches the framework's matmul and attention, strict by default).
         y = model(x)                      # unsupported calls run stock PyTorch
     m.fallbacks                           # how many did, by function name
 
-Intercepted at the Python API (a TorchFunctionMode), for GPU tensors:
+Intercepted at the Python API, for GPU tensors (while a mode is active the functions below are
+replaced by thin wrappers; a wrapper hands the call to the innermost mode of the calling thread, and
+with no mode active on that thread, or for calls made from inside a routed call, it calls PyTorch's
+function unchanged; the originals come back when the last mode exits):
     torch.nn.functional.linear, torch.mm, torch.addmm, torch.matmul, torch.bmm,
     the Tensor methods mm / addmm / matmul / bmm and the @ operator,
     torch.nn.functional.scaled_dot_product_attention,
@@ -23,7 +26,9 @@ Every routed call runs the library's kernels through the C ABI binding, so
 results equal bi_linear / bi_matmul / bi_addmm / bi_sdpa / bi_rowsum bit for
 bit and no row depends on the batch.  A batched matmul runs one GEMM per batch element.
 Calls whose tensors are all on the CPU are not the library's business and
-pass through untouched in either mode.
+pass through untouched in either mode.  Every call of these functions is routed, including calls
+made inside other PyTorch Python functions (nn.Linear.forward, for example); calls made from C++
+inside PyTorch, and references to the functions taken before the mode was entered, are not.
 
 Not routed (raises NotImplementedError when strict; runs stock PyTorch and
 is counted otherwise): dtypes other than fp32 / fp16 / bf16, mixed dtypes,
@@ -40,11 +45,12 @@ coincide) and as the equivalent boolean mask otherwise.
 from __future__ import annotations
 
 import contextlib
+import functools
+import threading
 from collections import Counter
 
 import torch
 import torch.nn.functional as F
-from torch.overrides import TorchFunctionMode
 
 from . import bi_addmm, bi_linear, bi_matmul, bi_rowsum, bi_sdpa
 
@@ -244,28 +250,94 @@ def _tensors_in(args, kwargs):
             yield x
 
 
-class _InvariantMode(TorchFunctionMode):
+# (owner, attribute) of every routed function; the wrappers replace these attributes while any mode is
+# active in any thread
+_TARGETS = ((F, "linear"), (torch, "mm"), (torch.Tensor, "mm"), (torch, "addmm"), (torch.Tensor, "addmm"),
+            (torch, "matmul"), (torch.Tensor, "matmul"), (torch.Tensor, "__matmul__"),
+            (torch.Tensor, "__rmatmul__"), (torch, "bmm"), (torch.Tensor, "bmm"),
+            (F, "scaled_dot_product_attention"), (torch, "sum"), (torch.Tensor, "sum"), (torch, "mean"),
+            (torch.Tensor, "mean"))
+# the route of each target, looked up once on the functions PyTorch defines
+_TARGET_ROUTES = tuple((owner, name, _ROUTES[getattr(owner, name)], getattr(getattr(owner, name), "__name__", name))
+                       for owner, name in _TARGETS)
+_tls = threading.local()               # .stack: this thread's active modes; .busy: inside a routed call
+_lock = threading.Lock()
+_active_count = 0                      # modes active over all threads
+_saved = []                            # (owner, name, original, owner held it in its own __dict__)
+
+
+def _wrapper(orig, route, name):
+    @functools.wraps(orig)
+    def call(*args, **kwargs):
+        stack = getattr(_tls, "stack", None)
+        if not stack or getattr(_tls, "busy", False):
+            return orig(*args, **kwargs)
+        return stack[-1]._dispatch(orig, route, name, args, kwargs)
+    return call
+
+
+def _install():
+    try:
+        for owner, name, route, fname in _TARGET_ROUTES:
+            orig = getattr(owner, name)
+            _saved.append((owner, name, orig, name in vars(owner)))
+            setattr(owner, name, _wrapper(orig, route, fname))
+    except BaseException:
+        _uninstall()
+        raise
+
+
+def _uninstall():
+    while _saved:
+        owner, name, orig, own = _saved.pop()
+        if own:
+            setattr(owner, name, orig)
+        else:
+            delattr(owner, name)       # the attribute is inherited again (Tensor methods of the C base)
+
+
+class _InvariantMode:
     def __init__(self, strict: bool):
-        super().__init__()
         self.strict = strict
         self.fallbacks = Counter()
         self.routed = Counter()
 
-    def __torch_function__(self, func, types, args=(), kwargs=None):
-        kwargs = kwargs or {}
-        route = _ROUTES.get(func)
-        if route is None or not any(t.is_cuda for t in _tensors_in(args, kwargs)):
-            return func(*args, **kwargs)
-        name = getattr(func, "__name__", str(func))
+    def __enter__(self):
+        global _active_count
+        with _lock:
+            if _active_count == 0:
+                _install()
+            _active_count += 1
+        if getattr(_tls, "stack", None) is None:
+            _tls.stack = []
+        _tls.stack.append(self)
+        return self
+
+    def __exit__(self, *exc):
+        global _active_count
+        _tls.stack.remove(self)
+        with _lock:
+            _active_count -= 1
+            if _active_count == 0:
+                _uninstall()
+        return False
+
+    def _dispatch(self, orig, route, name, args, kwargs):
+        if not any(t.is_cuda for t in _tensors_in(args, kwargs)):
+            return orig(*args, **kwargs)
+        _tls.busy = True
         try:
-            out = _call(route, args, kwargs)
-        except _NotOurs:
-            return func(*args, **kwargs)
-        except (Unsupported, NotImplementedError) as e:
-            if self.strict:
-                raise NotImplementedError(f"batch_invariant_mode: {name}: {e}") from None
-            self.fallbacks[name] += 1
-            return func(*args, **kwargs)
+            try:
+                out = _call(route, args, kwargs)
+            except _NotOurs:
+                return orig(*args, **kwargs)
+            except (Unsupported, NotImplementedError) as e:
+                if self.strict:
+                    raise NotImplementedError(f"batch_invariant_mode: {name}: {e}") from None
+                self.fallbacks[name] += 1
+                return orig(*args, **kwargs)
+        finally:
+            _tls.busy = False
         self.routed[name] += 1
         return out
 

@@ -171,3 +171,20 @@ def test_mode_makes_last_dim_sum_and_mean_invariant(dt):
     assert m.routed["sum"] >= 5 and m.routed["mean"] >= 4 and not m.fallbacks
     assert total.shape == () and cols.shape == (4099,)
 
+
+
+def test_other_threads_and_nested_calls_run_stock_pytorch():
+    """The mode belongs to the thread that entered it: a linear on another thread runs PyTorch's own kernel
+    (not counted), the same call on this thread is routed and equals the direct library call."""
+    import threading
+    x, w = _r((48, 256), 21), _r((80, 256), 22, 0.02)
+    other = []
+    with bi.batch_invariant_mode() as m:
+        t = threading.Thread(target=lambda: other.append(F.linear(x, w)))
+        t.start()
+        t.join()
+        assert not m.routed
+        y = F.linear(x, w)
+        assert m.routed["linear"] == 1
+    assert_bits_equal(y, bi.bi_linear(x, w), "routed linear vs direct call")
+    torch.testing.assert_close(other[0].float(), y.float(), rtol=2e-2, atol=2e-2)
