@@ -182,9 +182,10 @@ bi_status bi_addmm(const void *cin, int64_t ldcin,
  * be NULL) for the shapes served without a workspace: 16-bit dt with either
  * Lq >= 384 (prefill: splits folded in registers; for D > 128 also Lq >= 64
  * with B Lq >= 192), or D <= 128 and S <= 256
- * on the quad kernel (one split, finished in the kernel), or D <= 128,
- * S <= 1024 and more than 256 quad workgroups (one launch, splits folded in
- * LDS); see bi_sdpa_kernel_name.  Every path computes the same bits.
+ * on the quad kernel (one split, finished in the kernel), or D <= 128, more
+ * than 256 quad workgroups and either (Hq / Hkv) Lq >= 64 (prefill) or
+ * S <= 1024 (one launch, splits folded in LDS); see bi_sdpa_kernel_name.
+ * Every path computes the same bits.
  */
 bi_status bi_sdpa(const void *q, const int64_t q_str[4],
                   const void *k, const int64_t k_str[4],
@@ -394,7 +395,8 @@ const char *bi_gemm_kernel_name(int64_t M, int64_t N, int64_t K, bi_dtype in_dt,
  * when the quad grid, ceil(S / 256) splits x ceil(ceil((Hq / Hkv) Lq / 16) / T)
  * row-tile groups x B x Hkv workgroups with T = 1 or 2 row tiles per
  * workgroup, is at most 256 (one workgroup per CU: every split's K / V
- * requested at once); else "sdpa_fused16" when S <= 1024, and
+ * requested at once); else "sdpa_prefill16" when a KV head has at least 64
+ * query rows ((Hq / Hkv) Lq >= 64); else "sdpa_fused16" when S <= 1024, and
  * "sdpa_split16+combine" (D = 128, and D = 64 on 128-byte key rows) or
  * "sdpa_split+combine" (D = 32, 96) otherwise.  For 16-bit dt and D > 128: "sdpa_prefill16w" when Lq >= 384, or
  * Lq >= 64 with B Lq >= 192 (rows of 256, all output columns in one workgroup);

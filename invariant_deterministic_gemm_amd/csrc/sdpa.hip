@@ -839,14 +839,17 @@ __global__ __launch_bounds__(64 * W) void sdpa_split16(SdpaParams p) {
 // wavefront per split, the split partials exchanged through LDS and folded
 // in the workgroup with exactly sdpa_combine's arithmetic (ascending split
 // order, same operations), so the result is bit-identical to the two-kernel
-// path and needs no workspace round trip or second launch.
+// path and needs no workspace round trip or second launch.  The launch gives
+// each workgroup FUSED_LDS_PER_WAVE bytes of LDS per wavefront (a K and a V
+// block), so that workgroups of one or two splits share a CU.
 constexpr int FUSED_MAXW = 4;
+constexpr int FUSED_LDS_PER_WAVE = 2 * KV_BLOCK * 256;
 template <int dt>
 __global__ __launch_bounds__(64 * FUSED_MAXW) void sdpa_fused16(SdpaParams p) {
     constexpr float NEG_INF = -__builtin_huge_valf();
     constexpr int D = 128;
-    constexpr int PER_WAVE = 2 * KV_BLOCK * 256;
-    __shared__ __attribute__((aligned(1024))) char lds[FUSED_MAXW * PER_WAVE];
+    constexpr int PER_WAVE = FUSED_LDS_PER_WAVE;
+    extern __shared__ __attribute__((aligned(1024))) char lds[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nw = blockDim.x >> 6;                  // == nsplit
     const int r16 = lane & 15, g = lane >> 4;
@@ -858,6 +861,7 @@ __global__ __launch_bounds__(64 * FUSED_MAXW) void sdpa_fused16(SdpaParams p) {
     f32x4 o[8];
     split16_body<dt, 4, true>(p, wave, tile, b, gk, lds + wave * PER_WAVE, m_run, l_run, o);
     __syncthreads();                                 // every wavefront is done with its K / V blocks
+    // the partials reuse the K / V space: nw * (16 * 2 + 16 * D) floats + padding <= nw * PER_WAVE bytes
     float *pml = reinterpret_cast<float *>(lds);                     // [split][16 rows][2]
     float *po = pml + FUSED_MAXW * 16 * 2;                           // [split][16 rows][D]
     if (g == 0) {
@@ -1800,6 +1804,13 @@ __global__ __launch_bounds__(256) void sdpa_combine_lds(SdpaParams p) {
 // splits take the workspace-free prefill kernel (measured: below ~300 rows the
 // split kernel's extra parallelism wins, above it the shared K / V blocks do).
 constexpr int64_t PREFILL_MIN_LQ = 384;
+// Shorter chunks take it too when the quad kernel does not apply and a KV head has at least one full
+// workgroup of rows (four 16-row tiles), measured at D = 128, causal (one-launch / split kernel against
+// prefill): B = 8, 16 / 4 heads, 256 rows at 256 keys 51.3 -> 18.5 us, at 1024 keys 127.5 -> 35.0;
+// B = 4, 32 / 8 heads, 128 rows at 2048 keys 98.3 -> 42.7; B = 2, 256 rows at 4096 keys 180.4 -> 73.8;
+// B = 8, 64 rows at 1024 keys 70.2 -> 27.2; B = 16, 16 rows at 1024 keys 34.5 -> 27.8.  Decode rows
+// (four per KV head) stay on the other kernels, which were as fast or faster there.
+constexpr int64_t PREFILL_MIN_ROWS = 64;
 // 16-bit head dims above 128 take the wide prefill kernel from 64 query rows on once the batch holds at
 // least 192 of them (measured at D = 256 and 192 against the generic split kernel: B = 1, 2048 keys,
 // 192 rows 132 -> 103 us; B = 4, 64 rows 173 -> 105 us; B = 1, 128 rows and B = 4, 32 rows stay
@@ -1843,6 +1854,7 @@ SdpaPath sdpa_path(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t S, in
     }
     const int64_t nsplit = (S + KV_SPLIT - 1) / KV_SPLIT;
     if (quad_tiles(B, Hkv, nsplit, (Hq / Hkv * Lq + 15) / 16) > 0) return SDPA_QUAD16;
+    if (Hq / Hkv * Lq >= PREFILL_MIN_ROWS) return SDPA_PREFILL16;
     if (nsplit <= FUSED_MAXW) return SDPA_FUSED16;
     return SDPA_SPLIT;
 }
@@ -1896,7 +1908,8 @@ static hipError_t launch_typed(const SdpaParams &p, hipStream_t st) {
         if (path == SDPA_FUSED16) {
             const int64_t nwg = (int64_t)((R + 15) / 16) * p.B * p.Hkv;
             if (nwg > INT32_MAX) return hipErrorInvalidConfiguration;
-            hipLaunchKernelGGL((sdpa_fused16<dt>), dim3((unsigned)nwg), dim3(64 * p.nsplit), 0, st, p);
+            hipLaunchKernelGGL((sdpa_fused16<dt>), dim3((unsigned)nwg), dim3(64 * p.nsplit),
+                               (unsigned)(FUSED_LDS_PER_WAVE * p.nsplit), st, p);
             return hipGetLastError();
         }
     }

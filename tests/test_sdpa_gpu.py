@@ -72,8 +72,9 @@ def test_rows_without_visible_keys_are_zero():
 @pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16], ids=_ids)
 def test_single_split_finished_in_the_quad_kernel(dt):
     """At most 256 keys (one split) the quad kernel applies the combine's fold itself (no workspace, no
-    second launch): the same bits as the one-launch kernel (the element inside a batch of 160), for every
-    mask form, sinks and ragged cache lengths, and the oracle's values."""
+    second launch): the same bits as the one-launch kernel, or the prefill kernel once a KV head has 64
+    query rows (the element inside a batch of 160), for every mask form, sinks and ragged cache lengths,
+    and the oracle's values."""
     lib = bi._native.load()
     BI = bi.BI_BF16 if dt == torch.bfloat16 else bi.BI_F16
     Hq, Hkv, D, NB = 8, 2, 128, 160
@@ -89,7 +90,8 @@ def test_single_split_finished_in_the_quad_kernel(dt):
         amask[..., 0] = 0.0
         sinks = synthetic.randn((Hq,), 95 + S, 2.0)
         assert lib.bi_sdpa_kernel_name(1, Hq, Hkv, Lq, S, D, BI).decode() == "sdpa_quad16"
-        assert lib.bi_sdpa_kernel_name(NB, Hq, Hkv, Lq, S, D, BI).decode() == "sdpa_fused16"
+        assert lib.bi_sdpa_kernel_name(NB, Hq, Hkv, Lq, S, D, BI).decode() == (
+            "sdpa_prefill16" if Hq // Hkv * Lq >= 64 else "sdpa_fused16")
         assert bi.sdpa_workspace_bytes(1, Hq, Hkv, Lq, S, D, dt) == 0
         rep = lambda t: t.expand(NB, *t.shape[1:]).contiguous()
         qg, kg, vg = q.to(DEV), k.to(DEV), v.to(DEV)
@@ -292,13 +294,13 @@ def test_accuracy_small_shapes(dt, D):
 @pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16], ids=_ids)
 def test_quad_fused_and_split_kernels_agree(dt):
     """16-bit D = 128: the kernel follows the size of the grid (splits x row tiles x B x KV heads), so
-    the same batch element runs the quad kernel alone and the one-launch (S <= 1024) or split kernel
-    (S > 1024) inside a batch of 48.  Every mask form, sinks, ragged S and several query lengths give
+    the same batch element runs the quad kernel alone and the one-launch (S <= 1024), split (S > 1024)
+    or prefill (64 query rows per KV head) kernel inside a batch of 48.  Every mask form, sinks, ragged S and several query lengths give
     the same bits either way, and the quad results match the oracle."""
     lib = bi._native.load()
     BI = bi.BI_BF16 if dt == torch.bfloat16 else bi.BI_F16
     Hq, Hkv, NB = 8, 2, 48
-    for S, Lq, big in ((700, 1, "sdpa_fused16"), (1024, 5, "sdpa_fused16"), (1000, 17, "sdpa_fused16"),
+    for S, Lq, big in ((700, 1, "sdpa_fused16"), (1024, 5, "sdpa_fused16"), (1000, 17, "sdpa_prefill16"),
                        (2085, 2, "sdpa_split16+combine"), (4100, 9, "sdpa_split16+combine")):
         seed = 0x5EED70 + S + Lq
         q = synthetic.randn((1, Hq, Lq, 128), seed, 1.0, dt)
@@ -377,22 +379,26 @@ def test_readme_style_call():
 
 @pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16], ids=_ids)
 def test_prefill_path_matches_split_path_and_decode(dt):
-    """Query chunks of >= 384 rows run the workspace-free prefill kernel; chunks of 383 run the split +
-    combine kernels (more than 1024 keys) or the fused kernel (up to 1024 keys).  The tokens two such
-    chunks share must have the same bits, and sampled tokens must equal their own decode call."""
+    """Query chunks of >= 384 rows run the workspace-free prefill kernel, and so do chunks of 383 (at
+    least 64 rows per KV head); chunks of fewer than 64 rows per KV head run the quad, split + combine or
+    one-launch kernels.  The tokens such chunks share must have the same bits, and sampled tokens must
+    equal their own decode call."""
     lib = bi._native.load()
     BI = bi.BI_BF16 if dt == torch.bfloat16 else bi.BI_F16
     for (B, Hq, Hkv, S) in [(2, 32, 8, 2085), (1, 16, 8, 1500), (1, 8, 8, 1100), (1, 32, 8, 1000), (2, 8, 8, 700)]:
         q = synthetic.randn((B, Hq, 500, 128), 0x5EED50 + S, 1.0, dt).to(DEV)
         k = synthetic.randn((B, Hkv, S, 128), 0x5EED51 + S, 1.0, dt).to(DEV)
         v = synthetic.randn((B, Hkv, S, 128), 0x5EED52 + S, 1.0, dt).to(DEV)
+        Ls = 64 // (Hq // Hkv) - 1                       # rows of a chunk below the prefill kernel's range
         assert lib.bi_sdpa_kernel_name(B, Hq, Hkv, 384, S, 128, BI).decode() == "sdpa_prefill16"
-        assert lib.bi_sdpa_kernel_name(B, Hq, Hkv, 383, S, 128, BI).decode() == (
-            "sdpa_fused16" if S <= 1024 else "sdpa_split16+combine")
-        split = bi.bi_sdpa(q[:, :, -383:], k, v, causal=True)
+        assert lib.bi_sdpa_kernel_name(B, Hq, Hkv, 383, S, 128, BI).decode() == "sdpa_prefill16"
+        assert lib.bi_sdpa_kernel_name(B, Hq, Hkv, Ls, S, 128, BI).decode() != "sdpa_prefill16"
+        shifted = bi.bi_sdpa(q[:, :, -383:], k, v, causal=True)
+        split = bi.bi_sdpa(q[:, :, -Ls:], k, v, causal=True)
         for L in (384, 390, 500):
             pre = bi.bi_sdpa(q[:, :, -L:], k, v, causal=True)
-            assert_bits_equal(pre[:, :, -383:], split, f"S={S} Hq={Hq}: q_len {L} (prefill) vs 383 (split)")
+            assert_bits_equal(pre[:, :, -383:], shifted, f"S={S} Hq={Hq}: q_len {L} vs 383 (row tiles shifted)")
+            assert_bits_equal(pre[:, :, -Ls:], split, f"S={S} Hq={Hq}: q_len {L} (prefill) vs {Ls} (split)")
             for i in (0, L // 2, L - 1):
                 p = S - L + i
                 dec = bi.bi_sdpa(q[:, :, 500 - L + i:500 - L + i + 1], k[:, :, :p + 1], v[:, :, :p + 1], causal=True)
@@ -401,8 +407,8 @@ def test_prefill_path_matches_split_path_and_decode(dt):
         mask = torch.ones(1, 1, 1, S, dtype=torch.bool, device=DEV)
         mask[..., 50:300] = False
         a = bi.bi_sdpa(q[:, :, -384:], k, v, mask=mask)
-        c = bi.bi_sdpa(q[:, :, -383:], k, v, mask=mask)
-        assert_bits_equal(a[:, :, -383:], c, f"S={S}: masked, prefill vs split")
+        c = bi.bi_sdpa(q[:, :, -Ls:], k, v, mask=mask)
+        assert_bits_equal(a[:, :, -Ls:], c, f"S={S}: masked, prefill vs split")
         ref = oracle.sdpa(q[:1, :, -384:].cpu(), k[:1].cpu(), v[:1].cpu(), mask=mask.cpu())
         assert_close_to_oracle(a[:1].cpu(), ref, f"S={S}: masked prefill vs oracle")
 
@@ -411,9 +417,9 @@ def test_prefill_path_matches_split_path_and_decode(dt):
 @pytest.mark.parametrize("B,Hq,Hkv,S", [(2, 16, 8, 1000), (1, 32, 8, 1337), (3, 8, 2, 777)])
 def test_every_prefill_token_matches_split_chunks(dt, B, Hq, Hkv, S):
     """Every token of a causal prefill (query chunk = the whole cache, the prefill kernel) equals the same
-    token computed by the split + combine or one-launch kernels in chunks of at most 383 query rows
-    against the cache truncated after the chunk: ragged row-tile groups, caches that end inside a block,
-    GQA factors 2 and 4, batch neighbours."""
+    token computed by the quad, split + combine or one-launch kernels in chunks of fewer than 64 query
+    rows per KV head against the cache truncated after the chunk: ragged row-tile groups, caches that
+    end inside a block, GQA factors 2 and 4, batch neighbours."""
     lib = bi._native.load()
     BI = bi.BI_BF16 if dt == torch.bfloat16 else bi.BI_F16
     q = synthetic.randn((B, Hq, S, 128), 0x5EED53 + S, 1.0, dt).to(DEV)
@@ -421,9 +427,10 @@ def test_every_prefill_token_matches_split_chunks(dt, B, Hq, Hkv, S):
     v = synthetic.randn((B, Hkv, S, 128), 0x5EED55 + S, 1.0, dt).to(DEV)
     assert lib.bi_sdpa_kernel_name(B, Hq, Hkv, S, S, 128, BI).decode() == "sdpa_prefill16"
     full = bi.bi_sdpa(q, k, v, causal=True)
+    cs = 64 // (Hq // Hkv) - 1
     a = 0
     while a < S:
-        e = min(a + 383, S)
+        e = min(a + cs, S)
         assert lib.bi_sdpa_kernel_name(B, Hq, Hkv, e - a, e, 128, BI).decode() != "sdpa_prefill16"
         part = bi.bi_sdpa(q[:, :, a:e], k[:, :, :e], v[:, :, :e], causal=True)
         assert_bits_equal(full[:, :, a:e], part, f"tokens {a}..{e - 1}")
@@ -511,15 +518,15 @@ def test_workspace_stays_bounded_for_long_calls():
     for i in (0, 700, 1500, 2047):
         one = bi.bi_sdpa(q[:, :, i:i + 1], k[:, :, :S2], v[:, :, :S2], mask=mask[:, :, i:i + 1])
         assert_bits_equal(om[:, :, i:i + 1], one, f"fp32 masked row {i} vs alone")
-    # bf16: 300 query rows per sequence against a 20000-key cache, batch 4
-    B, L3, S3 = 4, 300, 20000
+    # bf16: 15 query rows per sequence (60 per KV head: the split kernel) against a 20000-key cache, batch 16
+    B, L3, S3 = 16, 15, 20000
     assert lib.bi_sdpa_kernel_name(B, 32, 8, L3, S3, 128, bi.BI_BF16).decode() == "sdpa_split16+combine"
     assert 0 < bi.sdpa_workspace_bytes(B, 32, 8, L3, S3, 128, torch.bfloat16) <= cap
     q3 = synthetic.randn((B, 32, L3, 128), 0x5EEDC4, 1.0, torch.bfloat16).to(DEV)
     k3 = synthetic.randn((B, 8, S3, 128), 0x5EEDC5, 1.0, torch.bfloat16).to(DEV)
     v3 = synthetic.randn((B, 8, S3, 128), 0x5EEDC6, 1.0, torch.bfloat16).to(DEV)
     o3 = bi.bi_sdpa(q3, k3, v3, causal=True)
-    for i in (0, 150, 299):
+    for i in (0, 7, 14):
         p = S3 - L3 + i
         dec = bi.bi_sdpa(q3[:, :, i:i + 1], k3[:, :, :p + 1], v3[:, :, :p + 1], causal=True)
         assert_bits_equal(o3[:, :, i:i + 1], dec, f"bf16 row {i} vs its decode")
