@@ -531,7 +531,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm16_pipe(GemmParams p) {
 // ============================================================ plan + launch
 // Strip instantiations by M (fragments, A rows per stage, stages, loader
 // waves) and ring tiles, largest first.  The ring plan takes the largest tile
-// that still yields about one tile per CU (192 of 256), else the smallest.
+// that still yields about one tile per CU (160 of 256), else the smallest.
 // Used only to pick a kernel, never changes bits.
 struct StripCfg { int nb, fm, ar, ns, nl; };
 // More than one 16-column strip per CU: A re-reads from L2 start to cost.
@@ -554,7 +554,7 @@ static bool use_strip(int M, int N, int K) {
     return false;
 }
 // Tiles for M above the strip range, largest first.  The plan takes the
-// largest tile that yields about one tile per CU (192 of 256), skipping tiles at
+// largest tile that yields about one tile per CU (160 of 256), skipping tiles at
 // least twice as tall as M (their rows would be mostly clamped copies), else the
 // smallest one allowed.  The 256-row tiles run the two-stage ring; the others
 // the pipelined kernel, except that the 128x64 tile runs the ring when it spans
@@ -565,7 +565,10 @@ enum TileKind { RING256x256, RING256x128, PIPE128x128, PIPE128x64, PIPE64x64, PI
 struct TileCfg { int bm, bn; TileKind kind; };
 static const TileCfg kTiles[] = {{256, 256, RING256x256}, {256, 128, RING256x128}, {128, 128, PIPE128x128},
                                  {128, 64, PIPE128x64},   {64, 64, PIPE64x64},     {32, 64, PIPE32x64}};
-constexpr long kMinTiles = 192;
+// 160 rather than a full round of 256: a larger tile that leaves some CUs idle beats a smaller one that
+// needs a second round (measured M = 2048, N = 5632, K = 2048: 176 tiles of 256x256 861 TFLOP/s against
+// 352 of 256x128 687; every shape with 192 or more tiles of some size keeps its tile).
+constexpr long kMinTiles = 160;
 
 static TileCfg tile_cfg(int M, int N, int K) {
     TileCfg pick = kTiles[0];

@@ -302,6 +302,11 @@ def test_kernel_name_queries(lib):
         assert name(*bad) == "none"
     assert lib.bi_gemm_kernel_name(1, 4096, 4096, BF16, 0).decode().startswith("gemm16_strip_nk/")
     assert lib.bi_gemm_kernel_name(4096, 4096, 4096, BF16, 0).decode().startswith("gemm16_ring_nk/")
+    # the largest tile with at least 160 tiles: 176 tiles of 256x256 rather than 352 of 256x128
+    assert lib.bi_gemm_kernel_name(2048, 5632, 2048, BF16, 0).decode() == "gemm16_ring_nk/256x256"
+    assert lib.bi_gemm_kernel_name(1280, 8192, 4096, BF16, 0).decode() == "gemm16_ring_nk/256x256"   # 160
+    assert lib.bi_gemm_kernel_name(1024, 8192, 4096, BF16, 0).decode() == "gemm16_ring_nk/256x128"   # 128 / 256
+    assert lib.bi_gemm_kernel_name(512, 14336, 4096, BF16, 0).decode() == "gemm16_ring_nk/256x128"   # 112 / 224
     assert lib.bi_gemm_kernel_name(0, 4096, 4096, BF16, 0).decode() == "none"
 
 

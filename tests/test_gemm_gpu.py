@@ -390,3 +390,24 @@ def test_every_tile_configuration_is_exact(K):
               "gemm16_pipe_nk/128x64", "gemm16_ring_nk/128x64"}
     expect |= {"gemm16_pipe_nk/64x64", "gemm16_pipe_nk/32x64"} if K % 128 == 0 else {"gemm16_ring_nk/64x64"}
     assert expect <= seen, (sorted(expect - seen), sorted(seen))
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16], ids=lambda d: str(d).split(".")[-1])
+def test_rows_across_the_tile_count_switch(dt):
+    """K = 2048, N = 5632: M = 2048 gives 176 tiles of 256x256 (the plan takes the largest tile with at
+    least 160), M = 1279 gives 5 x 44 = 220 tiles of 256x128 and smaller M smaller tiles or the strip
+    kernel: every row equals the same row of the M = 2048 call, and the oracle gate holds."""
+    K, N = 2048, 5632
+    x = synthetic.randn((2048, K), 0x5EED3D, 1.0, dt).to(DEV)
+    w = synthetic.randn((N, K), 0x5EED3E, 0.02, dt).to(DEV)
+    lib = bi._native.load()
+    BI = bi.BI_BF16 if dt == torch.bfloat16 else bi.BI_F16
+    assert lib.bi_gemm_kernel_name(2048, N, K, BI, 0).decode() == "gemm16_ring_nk/256x256"
+    full = bi.bi_linear(x, w)
+    seen = set()
+    for m in (2048, 1280, 1279, 1024, 300, 64, 3):
+        seen.add(lib.bi_gemm_kernel_name(m, N, K, BI, 0).decode())
+        assert_bits_equal(bi.bi_linear(x[:m], w), full[:m], f"{dt} M={m}")
+    assert len(seen) >= 4, seen
+    rows = [0, 1279, 2047]
+    assert_close_to_oracle(full[rows].cpu(), oracle.linear(x[rows].cpu(), w.cpu()), f"{dt} K=2048 N=5632")
