@@ -553,7 +553,8 @@ static bool use_strip(int M, int N, int K) {
     if (M <= 64) return !(wide_n(N) && K % 64 == 0);
     return false;
 }
-// Tiles for M above the strip range, largest first.  The plan takes the
+// Tiles for M above the strip range, largest first.  Up to 256 rows (where the
+// weight stream bounds the call) the plan takes the
 // largest tile that yields about one tile per CU (160 of 256), skipping tiles at
 // least twice as tall as M (their rows would be mostly clamped copies), else the
 // smallest one allowed.  The 256-row tiles run the two-stage ring; the others
@@ -570,7 +571,33 @@ static const TileCfg kTiles[] = {{256, 256, RING256x256}, {256, 128, RING256x128
 // 352 of 256x128 687; every shape with 192 or more tiles of some size keeps its tile).
 constexpr long kMinTiles = 160;
 
+// Above 256 rows the plan weighs wave quantisation instead: a tile kind costs ceil(tiles / 256) rounds of
+// its tile area at its measured full-chip rate (K = 4096 / 14336, TFLOP/s), and a smaller tile replaces a
+// larger one only when that cost is at least 5% lower.  Measured against every tile kernel on M in {384,
+// 768, 2048, 8192} x (N, K) in {(6144, 4096), (28672, 4096), (4096, 14336), (1024, 4096), (128256, 4096)}
+// and the large-M cells, this picks the fastest tile or one within 2% of it (M = 768, N = 6144: 256x128,
+// 668 TFLOP/s against 501 for the 128x128 tile the tile-count rule took; M = 384: 128x128, 478 against
+// 398; M = 768, N = 28672: 256x128, 943 against 884; M = 2048, N = 512: the 64x64 ring, 344 against 312).
+struct TileRate { int bm, bn; TileKind kind; int tflops; };
+static const TileRate kRates[] = {{256, 256, RING256x256, 1290}, {256, 128, RING256x128, 1060},
+                                  {128, 128, PIPE128x128, 860},  {128, 64, RING128x64, 690},
+                                  {64, 64, RING64x64, 650},      {32, 64, PIPE32x64, 270}};
+
 static TileCfg tile_cfg(int M, int N, int K) {
+    if (M > 256) {
+        TileCfg pick = {kRates[0].bm, kRates[0].bn, kRates[0].kind};
+        double best = 0.0;
+        for (const TileRate &c : kRates) {
+            if (c.kind == PIPE32x64 && K % 128 != 0) continue;
+            const long tiles = (long)((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
+            const double cost = (double)((tiles + 255) / 256) * c.bm * c.bn / c.tflops;
+            if (best == 0.0 || cost < 0.95 * best) {
+                best = cost;
+                pick = TileCfg{c.bm, c.bn, c.kind};
+            }
+        }
+        return pick;
+    }
     TileCfg pick = kTiles[0];
     for (const TileCfg &c : kTiles) {
         if (c.bm >= 2 * M && c.bm > 32) continue;
