@@ -180,11 +180,13 @@ bi_status bi_addmm(const void *cin, int64_t ldcin,
  * on `stream`, each with the keys up to its last row when causal; no row's
  * arithmetic changes.  The query returns 0 (ws may then
  * be NULL) for the shapes served without a workspace: 16-bit dt with either
- * Lq >= 384 (prefill: splits folded in registers; for D > 128 also Lq >= 64
- * with B Lq >= 192), or D <= 128 and S <= 256
+ * Lq >= 384 (prefill: splits folded in registers; for D <= 128 only on a
+ * prefill grid of more than 64 workgroups, for D > 128 also Lq >= 64 with
+ * B Lq >= 192), or D <= 128 and S <= 256
  * on the quad kernel (one split, finished in the kernel), or D <= 128, more
- * than 256 quad workgroups and either (Hq / Hkv) Lq >= 64 (prefill) or
- * S <= 1024 (one launch, splits folded in LDS); see bi_sdpa_kernel_name.
+ * than 256 quad workgroups and either (Hq / Hkv) Lq >= 64 on a prefill grid
+ * of more than 64 workgroups (prefill) or S <= 1024 (one launch, splits
+ * folded in LDS); see bi_sdpa_kernel_name.
  * Every path computes the same bits.
  */
 bi_status bi_sdpa(const void *q, const int64_t q_str[4],
@@ -390,13 +392,15 @@ size_t bi_quantized_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, bi_d
 const char *bi_gemm_kernel_name(int64_t M, int64_t N, int64_t K, bi_dtype in_dt, int b_kn);
 
 /* Which attention kernels a bi_sdpa call of these sizes runs.  For 16-bit dt
- * and D <= 128: "sdpa_prefill16" when Lq >= 384; else "sdpa_quad16+combine"
+ * and D <= 128: "sdpa_prefill16" when Lq >= 384 and its grid,
+ * ceil(ceil((Hq / Hkv) Lq / 16) / 4) x B x Hkv workgroups, exceeds 64; else "sdpa_quad16+combine"
  * ("sdpa_quad16" when S <= 256: one split, folded in the kernel)
  * when the quad grid, ceil(S / 256) splits x ceil(ceil((Hq / Hkv) Lq / 16) / T)
  * row-tile groups x B x Hkv workgroups with T = 1 or 2 row tiles per
  * workgroup, is at most 256 (one workgroup per CU: every split's K / V
  * requested at once); else "sdpa_prefill16" when a KV head has at least 64
- * query rows ((Hq / Hkv) Lq >= 64); else "sdpa_fused16" when S <= 1024, and
+ * query rows ((Hq / Hkv) Lq >= 64) and the prefill grid exceeds 64
+ * workgroups; else "sdpa_fused16" when S <= 1024, and
  * "sdpa_split16+combine" (D = 128, and D = 64 on 128-byte key rows) or
  * "sdpa_split+combine" (D = 32, 96) otherwise.  For 16-bit dt and D > 128: "sdpa_prefill16w" when Lq >= 384, or
  * Lq >= 64 with B Lq >= 192 (rows of 256, all output columns in one workgroup);

@@ -1811,6 +1811,17 @@ constexpr int64_t PREFILL_MIN_LQ = 384;
 // B = 8, 64 rows at 1024 keys 70.2 -> 27.2; B = 16, 16 rows at 1024 keys 34.5 -> 27.8.  Decode rows
 // (four per KV head) stay on the other kernels, which were as fast or faster there.
 constexpr int64_t PREFILL_MIN_ROWS = 64;
+// Either way (D <= 128) only when the prefill grid has more than this many workgroups: the split kernel
+// also spreads a row tile's keys over workgroups, and on small grids with long caches that wins (B = 1,
+// 32 / 32 heads, 64 rows at 2048 keys: 32 prefill workgroups 41.2 us, split 20.0; 384 rows of 8 / 8
+// heads at 8192 keys: 48 workgroups 133 against 75; 16 / 16 heads, 256 rows at 8192 keys: 64, 136
+// against 96), while from 96 workgroups on the prefill kernel was as fast or faster (16 / 16 heads, 384
+// rows at 2048 keys: 39.7 against 43.7; 128 workgroups of 8 / 2 heads, 1024 rows at 8192 keys: 134
+// against 179).
+constexpr int64_t PREFILL_MIN_WG = 64;
+static int64_t prefill_workgroups(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq) {
+    return ((Hq / Hkv * Lq + 15) / 16 + 3) / 4 * B * Hkv;
+}
 // 16-bit head dims above 128 take the wide prefill kernel from 64 query rows on once the batch holds at
 // least 192 of them (measured at D = 256 and 192 against the generic split kernel: B = 1, 2048 keys,
 // 192 rows 132 -> 103 us; B = 4, 64 rows 173 -> 105 us; B = 1, 128 rows and B = 4, 32 rows stay
@@ -1843,7 +1854,8 @@ constexpr int64_t SPLIT16W_MAX_WG = 1024;
 
 SdpaPath sdpa_path(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t S, int64_t D, int dt) {
     if (dt == DT_F32 || S <= 0) return SDPA_SPLIT;
-    if (Lq >= PREFILL_MIN_LQ) return SDPA_PREFILL16;
+    const bool prefill_grid = D > 128 || prefill_workgroups(B, Hq, Hkv, Lq) > PREFILL_MIN_WG;
+    if (Lq >= PREFILL_MIN_LQ && prefill_grid) return SDPA_PREFILL16;
     if (D > 128 && Lq >= WIDE_PREFILL_MIN_LQ && B * Lq >= WIDE_PREFILL_MIN_ROWS) return SDPA_PREFILL16;
     if (D > 128) {
         const int64_t nsg = ((S + KV_SPLIT - 1) / KV_SPLIT + 1) / 2;
@@ -1854,7 +1866,7 @@ SdpaPath sdpa_path(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t S, in
     }
     const int64_t nsplit = (S + KV_SPLIT - 1) / KV_SPLIT;
     if (quad_tiles(B, Hkv, nsplit, (Hq / Hkv * Lq + 15) / 16) > 0) return SDPA_QUAD16;
-    if (Hq / Hkv * Lq >= PREFILL_MIN_ROWS) return SDPA_PREFILL16;
+    if (Hq / Hkv * Lq >= PREFILL_MIN_ROWS && prefill_grid) return SDPA_PREFILL16;
     if (nsplit <= FUSED_MAXW) return SDPA_FUSED16;
     return SDPA_SPLIT;
 }

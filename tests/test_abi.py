@@ -230,7 +230,9 @@ def test_sdpa_workspace_formula(lib):
     assert ws(1, 32, 8, 383, 32768, 128, F32) == split_bytes(1, 32, lc, 32768, 128) <= cap
     # 16-bit D <= 128 with at least 64 query rows per KV head takes the prefill kernel below 384 rows too
     assert ws(1, 32, 8, 383, 32768, 128, BF16) == 0
-    assert ws(16, 16, 4, 16, 1024, 128, BF16) == 0                                 # 4 x 16 = 64 rows
+    assert ws(32, 16, 4, 16, 1024, 128, BF16) == 0                                 # 4 x 16 = 64 rows
+    # ... on a prefill grid of more than 64 workgroups; smaller grids keep the split kernel
+    assert ws(1, 8, 8, 384, 8192, 128, BF16) == split_bytes(1, 8, 384, 8192, 128)  # 6 x 8 = 48
     assert ws(16, 16, 4, 15, 2048, 128, BF16) == split_bytes(16, 16, 15, 2048, 128)  # 60 rows: split
     assert ws(1, 32, 8, 8192, 8192, 128, F32) <= cap
     assert ws(1, 1, 1, 1, 0, 128, BF16) == 0
@@ -271,10 +273,12 @@ def test_kernel_name_queries(lib):
     assert name(1, 32, 8, 384, 1025, 128, F16) == "sdpa_prefill16"
     assert name(1, 32, 8, 384, 1024, 128, BF16) == "sdpa_prefill16"
     # below 384 rows: prefill once a KV head has 64 query rows and the quad kernel does not apply
-    assert name(1, 32, 8, 64, 1025, 128, F16) == "sdpa_prefill16"
+    assert name(4, 32, 8, 64, 1025, 128, F16) == "sdpa_prefill16"                # 4 x 4 x 8 = 128 workgroups
+    assert name(1, 32, 8, 64, 1025, 128, F16) == "sdpa_split16+combine"          # 32: the split kernel
     assert name(1, 32, 8, 383, 1024, 128, BF16) == "sdpa_prefill16"
-    assert name(4, 32, 8, 16, 1025, 128, F16) == "sdpa_prefill16"                # 4 x 16 = 64 rows
-    assert name(4, 32, 8, 15, 1025, 128, F16) == "sdpa_split16+combine"          # 60 rows
+    assert name(1, 8, 8, 384, 8192, 128, BF16) == "sdpa_split16+combine"         # 48 workgroups
+    assert name(16, 32, 8, 16, 1025, 128, F16) == "sdpa_prefill16"               # 4 x 16 = 64 rows
+    assert name(16, 32, 8, 15, 1025, 128, F16) == "sdpa_split16+combine"         # 60 rows
     assert name(8, 32, 8, 15, 1024, 128, BF16) == "sdpa_fused16"
     assert name(4, 32, 8, 15, 1024, 128, BF16) == "sdpa_quad16+combine"          # 4 x 2 x 4 x 8 = 256"
     assert name(1, 32, 8, 1, 300, 128, F32) == "sdpa_split+combine"

@@ -173,7 +173,7 @@ def test_small_head_dims_agree_across_kernels(dt, D):
     the decode of its tokens (quad kernel) and vs the oracle, a masked prefill vs the same rows called
     few at a time (split kernel), and one batch element alone (quad kernel) vs inside a batch of 40 (one
     launch at S <= 1024, a split kernel above)."""
-    B, Hq, Hkv, Lq, S = 1, 8, 2, 400, 1500
+    B, Hq, Hkv, Lq, S = 1, 16, 4, 400, 1500
     BI = bi.BI_BF16 if dt == torch.bfloat16 else bi.BI_F16
     qc, kc, vc = _qkv(B, Hq, Hkv, Lq, S, D, dt, 370 + D)
     q, k, v = _gpu(qc, kc, vc)

@@ -385,7 +385,7 @@ def test_prefill_path_matches_split_path_and_decode(dt):
     equal their own decode call."""
     lib = bi._native.load()
     BI = bi.BI_BF16 if dt == torch.bfloat16 else bi.BI_F16
-    for (B, Hq, Hkv, S) in [(2, 32, 8, 2085), (1, 16, 8, 1500), (1, 8, 8, 1100), (1, 32, 8, 1000), (2, 8, 8, 700)]:
+    for (B, Hq, Hkv, S) in [(2, 32, 8, 2085), (1, 16, 8, 1500), (1, 16, 16, 1100), (1, 32, 8, 1000), (2, 8, 8, 700)]:
         q = synthetic.randn((B, Hq, 500, 128), 0x5EED50 + S, 1.0, dt).to(DEV)
         k = synthetic.randn((B, Hkv, S, 128), 0x5EED51 + S, 1.0, dt).to(DEV)
         v = synthetic.randn((B, Hkv, S, 128), 0x5EED52 + S, 1.0, dt).to(DEV)
