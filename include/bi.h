@@ -386,7 +386,7 @@ bi_status bi_quantized_linear(const void *x, int64_t ldx,
 size_t bi_quantized_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, bi_dtype dt);
 
 /* Which kernel configuration a GEMM of this shape runs on ("gemm_skinny_nk/fm1",
- * "gemm_tiled_kn/128x128", ...; b_kn != 0 for a row-major (K, N) operand of
+ * "gemm16_strip_kn/w16_a8", "gemm_tiled_kn/128x128", ...; b_kn != 0 for a row-major (K, N) operand of
  * bi_matmul / bi_addmm, 0 for bi_linear and for column-major operands).  Informational: every configuration computes the same bits.
  * Returns "none" for empty or oversized shapes. */
 const char *bi_gemm_kernel_name(int64_t M, int64_t N, int64_t K, bi_dtype in_dt, int b_kn);

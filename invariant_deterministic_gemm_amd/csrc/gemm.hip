@@ -441,7 +441,7 @@ static hipError_t launch_generic_dt(const GemmParams &p, int in_dt, int out_dt, 
 }
 
 const char *gemm_kernel_name(int M, int N, int K, int in_dt, bool b_kn) {
-    if (in_dt != DT_F32 && gemm16_applies(M, N, K, b_kn, 1)) return gemm16_kernel_name(M, N, K);
+    if (in_dt != DT_F32 && gemm16_applies(M, N, K, b_kn, 1)) return gemm16_kernel_name(M, N, K, b_kn);
     const GemmPlan16 pl = plan16(M, N);
     static thread_local char buf[64];
     if (pl.kind == 0) snprintf(buf, sizeof buf, "gemm_skinny_%s/fm%d", b_kn ? "kn" : "nk", pl.fm);
@@ -456,7 +456,7 @@ static hipError_t dispatch_dt(const GemmParams &p0, int in_dt, int out_dt, bool 
     p.splits = splits;
     p.partial = splits > 1 ? ws : nullptr;
     hipError_t e;
-    if (in_dt != DT_F32 && gemm16_applies(p.M, p.N, p.K, b_kn, splits)) e = launch_gemm16(p, in_dt, out_dt, st);
+    if (in_dt != DT_F32 && gemm16_applies(p.M, p.N, p.K, b_kn, splits)) e = launch_gemm16(p, in_dt, out_dt, b_kn, st);
     else e = launch_generic_dt(p, in_dt, out_dt, b_kn, st);
     if (e != hipSuccess || splits <= 1) return e;
     const int64_t total = (int64_t)p.M * p.N;

@@ -1,6 +1,6 @@
 // Batch-invariant GEMM kernels for 16-bit inputs (bf16 / fp16) on gfx950:
-// the cooperative strip kernel (small M) and the deep-ring tile kernel
-// (large M), both for B in the (N, K) layout.
+// the cooperative strip kernel (small M; B in the (N, K) layout or row-major
+// (K, N)) and the tile kernels (larger M, B in the (N, K) layout).
 //
 // Chain for 16-bit inputs (fixed; these kernels and the generic ones of
 // gemm.hip all run exactly this): one v_mfma_f32_16x16x32_{bf16,f16} per k
@@ -20,7 +20,7 @@ namespace bi {
 
 // Whether one of these kernels serves the call (else the generic kernels of gemm.hip do).
 bool gemm16_applies(int M, int N, int K, bool b_kn, int splits);
-hipError_t launch_gemm16(const GemmParams &p, int in_dt, int out_dt, hipStream_t st);
-const char *gemm16_kernel_name(int M, int N, int K);
+hipError_t launch_gemm16(const GemmParams &p, int in_dt, int out_dt, bool b_kn, hipStream_t st);
+const char *gemm16_kernel_name(int M, int N, int K, bool b_kn);
 
 }  // namespace bi

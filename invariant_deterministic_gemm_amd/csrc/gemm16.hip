@@ -14,8 +14,9 @@
 //   gemm16_pipe   M above the strip range up to the thousands: the same
 //                 loads with fragments read several steps ahead and one
 //                 barrier per stage.
-// Everything else (row-major (K, N) weights, other K) runs the generic
-// kernels of gemm.hip, which implement the same chain.  The batch-variant
+// The strip kernel also takes row-major (K, N) weights (M <= 64); everything
+// else with that layout, and other K, runs the generic kernels of gemm.hip,
+// which implement the same chain.  The batch-variant
 // split-K comparator runs these same kernels with the stage loop cut into
 // ranges (grid dimension y) whose raw sums go to a workspace; with one split
 // (the invariant path) every workgroup runs the whole chain.
@@ -42,7 +43,23 @@ namespace bi {
 // Q mod NL issue one more, and wait with their own vmcnt thresholds).  Chunks
 // past K are fetched from a clamped in-bounds address and replaced by zeros
 // when read, and steps past the end of the chain are not run.
-template <int idt, int odt, int NB, int FM, int AR, int NS, int NL>
+// KN (B row-major (K, N), 16-column strips): the stage's B part is its 128 k-rows of the strip, 32 bytes
+// each, row r at byte 32 r with bit 7 of the offset flipped by bit 8 (the four lane groups of a transposed
+// read then cover both halves of the banks); load instruction q moves k-rows 32 q .. 32 q + 31, each lane
+// the 16-byte piece that belongs at its slot.  The consumer reads column fragments with transposing LDS
+// reads (two per 32-k chunk: k-rows 8 g .. 8 g + 3 and 8 g + 4 .. 8 g + 7 of column r16), which hold the
+// same k as the (N, K) path's 16-byte chunks, in the same order.  The strips are dealt so that each
+// XCD (workgroup b runs on XCD b mod 8) gets a contiguous range: neighbouring strips read the same
+// 128-byte lines of a k-row and share them in that XCD's L2.
+__device__ __forceinline__ u32x2 lds_tr16(const char *lds_ptr) {
+    typedef short s16x4_t __attribute__((ext_vector_type(4)));
+    const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4_t *)(size_t)(uint32_t)(uintptr_t)BI_LDS_PTR(lds_ptr));
+    return __builtin_bit_cast(u32x2, v);
+}
+__device__ __forceinline__ int kn_swz(int off) { return off ^ (((off >> 8) & 1) << 7); }
+
+template <int idt, int odt, int NB, int FM, int AR, int NS, int NL, bool KN = false>
 __global__ __launch_bounds__(64 * (1 + NL)) void gemm16_strip(GemmParams p) {
     constexpr int ROWB = 256;
     constexpr int SW = 16 * NB;                  // strip width: NB 16-column fragments
@@ -51,11 +68,18 @@ __global__ __launch_bounds__(64 * (1 + NL)) void gemm16_strip(GemmParams p) {
     constexpr int STAGE = Q * 1024;
     static_assert(AR % 4 == 0 && AR >= 4 && AR <= 16 * FM, "A rows per stage");
     static_assert(NS >= 2 && QHI * (NS - 1) <= 63, "vmcnt range");
+    static_assert(!KN || NB == 1, "(K, N) weights take 16-column strips");
     __shared__ __attribute__((aligned(1024))) char lds[NS * STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int n0 = blockIdx.x * SW;
+    int strip = blockIdx.x;
+    if constexpr (KN) {
+        const int nstrip = (p.N + SW - 1) / SW, per = (nstrip + 7) / 8;
+        strip = (blockIdx.x % 8) * per + blockIdx.x / 8;
+        if (strip >= nstrip) return;                 // the whole workgroup, before any barrier
+    }
+    const int n0 = strip * SW;
     const int nchunk = p.K >> 3;                 // 16-byte chunks per row
     int sbase, send;                             // this split's stages (all of them without split-K)
     split_stages(p, (p.K + 127) >> 7, sbase, send);
@@ -73,10 +97,16 @@ __global__ __launch_bounds__(64 * (1 + NL)) void gemm16_strip(GemmParams p) {
         const int q = min(lw + NL * j, Q - 1);
         const int row = 4 * q + (lane >> 4);
         cl[j] = (lane & 15) ^ (row & 15);
-        if (row < SW)
+        if (KN && q < QB) {
+            // the piece stored at this lane's slot: k-row 32 q + o / 32, columns n0 + 8 ((o / 16) mod 2) ..
+            const int o = kn_swz(16 * lane);
+            cl[j] = 32 * q + (o >> 5);
+            src[j] = static_cast<const char *>(p.B) + (int64_t)min(n0 + 8 * ((o >> 4) & 1), p.N - 8) * 2;
+        } else if (row < SW) {
             src[j] = static_cast<const char *>(p.B) + (int64_t)min(n0 + row, p.N - 1) * p.ldb * 2;
-        else
+        } else {
             src[j] = static_cast<const char *>(p.A) + (int64_t)min(row - SW, p.M - 1) * p.lda * 2;
+        }
     }
     auto issue = [&](int stage) {
         char *buf = lds + (stage % NS) * STAGE;
@@ -84,9 +114,16 @@ __global__ __launch_bounds__(64 * (1 + NL)) void gemm16_strip(GemmParams p) {
         for (int j = 0; j < QHI; ++j) {
             if (j < myq) {
                 const int q = lw + NL * j;
-                const int gc = min((sbase + stage) * 16 + cl[j], nchunk - 1);
-                __builtin_amdgcn_global_load_lds(static_cast<const void *>(src[j] + (int64_t)gc * 16),
-                                                 BI_LDS_PTR(buf + q * 1024), 16, 0, 0);
+                const char *from;
+                if (KN && q < QB) {
+                    const int kr = min((sbase + stage) * 128 + cl[j], p.K - 1);
+                    from = src[j] + (int64_t)kr * p.ldb * 2;
+                } else {
+                    const int gc = min((sbase + stage) * 16 + cl[j], nchunk - 1);
+                    from = src[j] + (int64_t)gc * 16;
+                }
+                __builtin_amdgcn_global_load_lds(static_cast<const void *>(from), BI_LDS_PTR(buf + q * 1024), 16,
+                                                 0, 0);
             }
         }
     };
@@ -125,9 +162,16 @@ __global__ __launch_bounds__(64 * (1 + NL)) void gemm16_strip(GemmParams p) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int c = 4 * u + g;
+            if constexpr (KN) {
+                const int kr = 32 * u + 8 * g + (r16 >> 2);
+                const u32x2 lo = lds_tr16(buf + kn_swz(32 * kr + 8 * (r16 & 3)));
+                const u32x2 hi = lds_tr16(buf + kn_swz(32 * (kr + 4) + 8 * (r16 & 3)));
+                b[u][0] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+            } else {
 #pragma unroll
-            for (int j = 0; j < NB; ++j)
-                b[u][j] = *reinterpret_cast<const u32x4 *>(buf + (16 * j + r16) * ROWB + ((c ^ r16) << 4));
+                for (int j = 0; j < NB; ++j)
+                    b[u][j] = *reinterpret_cast<const u32x4 *>(buf + (16 * j + r16) * ROWB + ((c ^ r16) << 4));
+            }
 #pragma unroll
             for (int f = 0; f < FM; ++f)
                 a[u][f] = *reinterpret_cast<const u32x4 *>(buf + aoff[f] + ((c ^ aswz[f]) << 4));
@@ -613,12 +657,32 @@ static TileCfg tile_cfg(int M, int N, int K) {
 bool gemm16_applies(int M, int N, int K, bool b_kn, int splits) {
     (void)N;
     (void)splits;                                // split-K ranges run on the same kernels
-    if (b_kn) return false;
+    if (b_kn) return M <= 64;                    // the strip kernel's (K, N) form
     return M <= 64 || K % 64 == 0;
 }
 
+// (K, N) weights: 16-column strips (the strip configurations above with one fragment column)
+static StripCfg strip_cfg_kn(int M) {
+    if (M <= 4) return StripCfg{1, 1, 4, 6, 3};
+    if (M <= 8) return StripCfg{1, 1, 8, 6, 3};
+    if (M <= 16) return StripCfg{1, 1, 16, 4, 3};
+    if (M <= 32) return StripCfg{1, 2, 32, 4, 3};
+    return StripCfg{1, 4, 64, 4, 3};
+}
+
 template <int idt, int odt>
-static hipError_t launch16_typed(const GemmParams &p, hipStream_t st) {
+static hipError_t launch16_typed(const GemmParams &p, bool b_kn, hipStream_t st) {
+    if (b_kn) {
+        const StripCfg c = strip_cfg_kn(p.M);
+        const int per = ((p.N + 15) / 16 + 7) / 8;   // strips per XCD
+        const dim3 grid(8 * per, p.splits), block(64 * (1 + c.nl));
+        if (c.ar == 4) hipLaunchKernelGGL((gemm16_strip<idt, odt, 1, 1, 4, 6, 3, true>), grid, block, 0, st, p);
+        else if (c.ar == 8) hipLaunchKernelGGL((gemm16_strip<idt, odt, 1, 1, 8, 6, 3, true>), grid, block, 0, st, p);
+        else if (c.ar == 16) hipLaunchKernelGGL((gemm16_strip<idt, odt, 1, 1, 16, 4, 3, true>), grid, block, 0, st, p);
+        else if (c.ar == 32) hipLaunchKernelGGL((gemm16_strip<idt, odt, 1, 2, 32, 4, 3, true>), grid, block, 0, st, p);
+        else hipLaunchKernelGGL((gemm16_strip<idt, odt, 1, 4, 64, 4, 3, true>), grid, block, 0, st, p);
+        return hipGetLastError();
+    }
     if (use_strip(p.M, p.N, p.K)) {
         const StripCfg c = strip_cfg(p.M, p.N);
         const dim3 grid((p.N + 16 * c.nb - 1) / (16 * c.nb), p.splits), block(64 * (1 + c.nl));
@@ -662,16 +726,20 @@ static hipError_t launch16_typed(const GemmParams &p, hipStream_t st) {
     return hipGetLastError();
 }
 
-hipError_t launch_gemm16(const GemmParams &p, int in_dt, int out_dt, hipStream_t st) {
-    if (in_dt == DT_BF16 && out_dt == DT_BF16) return launch16_typed<DT_BF16, DT_BF16>(p, st);
-    if (in_dt == DT_F16 && out_dt == DT_F16) return launch16_typed<DT_F16, DT_F16>(p, st);
-    if (in_dt == DT_BF16 && out_dt == DT_F32) return launch16_typed<DT_BF16, DT_F32>(p, st);
-    if (in_dt == DT_F16 && out_dt == DT_F32) return launch16_typed<DT_F16, DT_F32>(p, st);
+hipError_t launch_gemm16(const GemmParams &p, int in_dt, int out_dt, bool b_kn, hipStream_t st) {
+    if (in_dt == DT_BF16 && out_dt == DT_BF16) return launch16_typed<DT_BF16, DT_BF16>(p, b_kn, st);
+    if (in_dt == DT_F16 && out_dt == DT_F16) return launch16_typed<DT_F16, DT_F16>(p, b_kn, st);
+    if (in_dt == DT_BF16 && out_dt == DT_F32) return launch16_typed<DT_BF16, DT_F32>(p, b_kn, st);
+    if (in_dt == DT_F16 && out_dt == DT_F32) return launch16_typed<DT_F16, DT_F32>(p, b_kn, st);
     return hipErrorInvalidValue;
 }
 
-const char *gemm16_kernel_name(int M, int N, int K) {
+const char *gemm16_kernel_name(int M, int N, int K, bool b_kn) {
     static thread_local char buf[64];
+    if (b_kn) {
+        snprintf(buf, sizeof buf, "gemm16_strip_kn/w16_a%d", strip_cfg_kn(M).ar);
+        return buf;
+    }
     if (use_strip(M, N, K)) {
         const StripCfg c = strip_cfg(M, N);
         snprintf(buf, sizeof buf, "gemm16_strip_nk/w%d_a%d", 16 * c.nb, c.ar);

@@ -411,3 +411,27 @@ def test_rows_across_the_tile_count_switch(dt):
     assert len(seen) >= 4, seen
     rows = [0, 1279, 2047]
     assert_close_to_oracle(full[rows].cpu(), oracle.linear(x[rows].cpu(), w.cpu()), f"{dt} K=2048 N=5632")
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16], ids=lambda d: str(d).split(".")[-1])
+def test_kn_strip_equals_nk_strip(dt):
+    """Row-major (K, N) weights up to M = 64 run the strip kernel's (K, N) form (16-column strips dealt
+    XCD by XCD, transposing LDS reads): every strip configuration, N ragged (strip counts not a multiple
+    of 8, a last strip of 8 columns), K ragged and tiny; random inputs, so the bits equal the (N, K) path
+    only if the chain is the same; matmul, addmm with a broadcast row and fp32 output."""
+    lib = bi._native.load()
+    BI = bi.BI_BF16 if dt == torch.bfloat16 else bi.BI_F16
+    for N, K in ((8, 8), (24, 136), (1000, 4104), (4104, 1000), (4096, 4096)):
+        x = synthetic.randn((64, K), 0x5EED40 + K, 1.0, dt).to(DEV)
+        w = synthetic.randn((N, K), 0x5EED41 + N, 0.05, dt).to(DEV)
+        c = synthetic.randn((N,), 0x5EED42 + N, 1.0, dt).to(DEV)
+        wkn = w.t().contiguous()
+        for m in (1, 4, 5, 8, 9, 16, 17, 32, 33, 64):
+            assert lib.bi_gemm_kernel_name(m, N, K, BI, 1).decode().startswith("gemm16_strip_kn/"), (m, N, K)
+            want = bi.bi_linear(x[:m], w)
+            assert_bits_equal(bi.bi_matmul(x[:m], wkn), want, f"N={N} K={K} M={m}: (K, N) vs (N, K)")
+            assert_bits_equal(bi.bi_addmm(c, x[:m], wkn), bi.bi_linear(x[:m], w, c), f"N={N} K={K} M={m}: addmm")
+            assert_bits_equal(bi.bi_matmul(x[:m], wkn, out_dtype=torch.float32),
+                              bi.bi_linear(x[:m], w, out_dtype=torch.float32), f"N={N} K={K} M={m}: fp32 out")
+    ref = oracle.linear(x[:4].cpu(), w.cpu())
+    assert_close_to_oracle(bi.bi_matmul(x[:4], wkn).cpu(), ref, "(K, N) strip vs oracle")
