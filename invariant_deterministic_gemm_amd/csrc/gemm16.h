@@ -1,6 +1,6 @@
 // Batch-invariant GEMM kernels for 16-bit inputs (bf16 / fp16) on gfx950:
-// the cooperative strip kernel (small M; B in the (N, K) layout or row-major
-// (K, N)) and the tile kernels (larger M, B in the (N, K) layout).
+// the cooperative strip kernel (small M) and the tile kernels (larger M), for
+// B in the (N, K) layout and (strip, 128x128 pipelined tile) row-major (K, N).
 //
 // Chain for 16-bit inputs (fixed; these kernels and the generic ones of
 // gemm.hip all run exactly this): one v_mfma_f32_16x16x32_{bf16,f16} per k

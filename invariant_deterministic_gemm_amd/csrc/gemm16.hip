@@ -14,9 +14,9 @@
 //   gemm16_pipe   M above the strip range up to the thousands: the same
 //                 loads with fragments read several steps ahead and one
 //                 barrier per stage.
-// The strip kernel also takes row-major (K, N) weights (M <= 64); everything
-// else with that layout, and other K, runs the generic kernels of gemm.hip,
-// which implement the same chain.  The batch-variant
+// The strip kernel (M <= 64) and the 128x128 pipelined kernel (K a multiple of
+// 64) also take row-major (K, N) weights; other K with that layout, and fp32,
+// run the generic kernels of gemm.hip, which implement the same chain.  The batch-variant
 // split-K comparator runs these same kernels with the stage loop cut into
 // ranges (grid dimension y) whose raw sums go to a workspace; with one split
 // (the invariant path) every workgroup runs the whole chain.
@@ -438,7 +438,15 @@ template <int KS> __device__ __forceinline__ int pipe_swz(int row) {
     else return (row >> 1) & 7;
 }
 
-template <int idt, int odt, int BM, int BN, int WGM, int WGN, int NS, int KS, int DR>
+// KN (B row-major (K, N); 128-column tiles, 64-k stages): the stage's B part is its 64 k-rows of the
+// tile's 128 columns, 256 bytes each, 16-byte chunk c of k-row r at slot c ^ kn_pipe_swz(r); load
+// instruction q moves four k-rows.  B fragments are read with transposing LDS reads as in the strip
+// kernel's (K, N) form (k-rows 8 g .. 8 g + 3 and 8 g + 4 .. 8 g + 7 of each 32-k step), the same k in
+// the same order as the (N, K) chunks.  The swizzle puts the four k-rows one read pass takes at distinct
+// 32-byte bank ranges, and the two lane groups served together (k-rows 8 apart) on different halves.
+__device__ __forceinline__ int kn_pipe_swz(int r) { return 2 * (r & 3) ^ 8 * ((r >> 3) & 1); }
+
+template <int idt, int odt, int BM, int BN, int WGM, int WGN, int NS, int KS, int DR, bool KN = false>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm16_pipe(GemmParams p) {
     constexpr int NW = WGM * WGN;
     constexpr int WM = BM / WGM, WN = BN / WGN;
@@ -454,6 +462,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm16_pipe(GemmParams p) {
     static_assert(Q % NW == 0, "every wave issues the same number of loads per stage");
     static_assert(NS >= 3 && QW * (NS - 2) <= 63, "vmcnt range");
     static_assert(DR >= 1 && DR <= SPS, "read-ahead");
+    static_assert(!KN || (BN == 128 && KS == 64 && BM % RPI == 0), "(K, N) form: 128-column tiles, 64-k stages");
+    constexpr int QA = BM / RPI;                     // load instructions of the A rows
     __shared__ __attribute__((aligned(1024))) char lds[NS * STAGE];
 
     const int tid = threadIdx.x;
@@ -478,18 +488,26 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm16_pipe(GemmParams p) {
         const int q = wave + NW * j;
         const int rloc = q * RPI + lane / CPR;
         const int c = (lane % CPR) ^ pipe_swz<KS>(rloc);
-        if (rloc < BM)
+        if (KN && q >= QA) {
+            // k-row 4 (q - QA) + L / 16 of the stage, the chunk that belongs at slot L mod 16
+            const int kr = 4 * (q - QA) + (lane >> 4);
+            const int cb = (lane & 15) ^ kn_pipe_swz(kr);
+            src[j] = static_cast<const char *>(p.B) + (int64_t)kr * p.ldb * 2 + (int64_t)min(n0 + 8 * cb, p.N - 8) * 2;
+        } else if (rloc < BM) {
             src[j] = static_cast<const char *>(p.A) + (int64_t)min(m0 + rloc, p.M - 1) * p.lda * 2 + c * 16;
-        else
+        } else {
             src[j] = static_cast<const char *>(p.B) + (int64_t)min(n0 + rloc - BM, p.N - 1) * p.ldb * 2 + c * 16;
+        }
     }
     auto issue = [&](int stage) {
         const int64_t koff = (int64_t)(sbase + stage) * ROWB;
+        const int64_t kroff = (int64_t)(sbase + stage) * KS * p.ldb * 2;
         char *buf = lds + (stage % NS) * STAGE;
 #pragma unroll
         for (int j = 0; j < QW; ++j) {
             const int q = wave + NW * j;
-            __builtin_amdgcn_global_load_lds(static_cast<const void *>(src[j] + koff), BI_LDS_PTR(buf + q * 1024), 16,
+            const int64_t off = (KN && q >= QA) ? kroff : koff;
+            __builtin_amdgcn_global_load_lds(static_cast<const void *>(src[j] + off), BI_LDS_PTR(buf + q * 1024), 16,
                                              0, 0);
         }
     };
@@ -506,8 +524,20 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm16_pipe(GemmParams p) {
         const int off = (c ^ swz) << 4;
 #pragma unroll
         for (int i = 0; i < FM; ++i) a[i] = *reinterpret_cast<const u32x4 *>(buf + aoff[i] + off);
+        if constexpr (KN) {
+            const char *bb = buf + BM * ROWB;
+            const int kr = 32 * (step % SPS) + 8 * g + (r16 >> 2);
 #pragma unroll
-        for (int j = 0; j < FN; ++j) b[j] = *reinterpret_cast<const u32x4 *>(buf + boff[j] + off);
+            for (int j = 0; j < FN; ++j) {
+                const int ch = (wn * WN + 16 * j) / 8 + ((r16 & 3) >> 1);   // chunk of this lane's 4 columns
+                const u32x2 lo = lds_tr16(bb + kr * 256 + ((ch ^ kn_pipe_swz(kr)) << 4) + 8 * (r16 & 1));
+                const u32x2 hi = lds_tr16(bb + (kr + 4) * 256 + ((ch ^ kn_pipe_swz(kr + 4)) << 4) + 8 * (r16 & 1));
+                b[j] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < FN; ++j) b[j] = *reinterpret_cast<const u32x4 *>(buf + boff[j] + off);
+        }
     };
     f32x4 acc[FM][FN];
 #pragma unroll
@@ -657,7 +687,7 @@ static TileCfg tile_cfg(int M, int N, int K) {
 bool gemm16_applies(int M, int N, int K, bool b_kn, int splits) {
     (void)N;
     (void)splits;                                // split-K ranges run on the same kernels
-    if (b_kn) return M <= 64;                    // the strip kernel's (K, N) form
+    if (b_kn) return M <= 64 || K % 64 == 0;     // the strip and 128x128 pipelined kernels' (K, N) forms
     return M <= 64 || K % 64 == 0;
 }
 
@@ -672,6 +702,11 @@ static StripCfg strip_cfg_kn(int M) {
 
 template <int idt, int odt>
 static hipError_t launch16_typed(const GemmParams &p, bool b_kn, hipStream_t st) {
+    if (b_kn && p.M > 64) {
+        const dim3 tiles((unsigned)(((p.M + 127) / 128) * ((p.N + 127) / 128)), p.splits);
+        hipLaunchKernelGGL((gemm16_pipe<idt, odt, 128, 128, 2, 4, 4, 64, 2, true>), tiles, dim3(512), 0, st, p);
+        return hipGetLastError();
+    }
     if (b_kn) {
         const StripCfg c = strip_cfg_kn(p.M);
         const int per = ((p.N + 15) / 16 + 7) / 8;   // strips per XCD
@@ -737,7 +772,8 @@ hipError_t launch_gemm16(const GemmParams &p, int in_dt, int out_dt, bool b_kn, 
 const char *gemm16_kernel_name(int M, int N, int K, bool b_kn) {
     static thread_local char buf[64];
     if (b_kn) {
-        snprintf(buf, sizeof buf, "gemm16_strip_kn/w16_a%d", strip_cfg_kn(M).ar);
+        if (M > 64) snprintf(buf, sizeof buf, "gemm16_pipe_kn/128x128");
+        else snprintf(buf, sizeof buf, "gemm16_strip_kn/w16_a%d", strip_cfg_kn(M).ar);
         return buf;
     }
     if (use_strip(M, N, K)) {

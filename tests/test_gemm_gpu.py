@@ -435,3 +435,25 @@ def test_kn_strip_equals_nk_strip(dt):
                               bi.bi_linear(x[:m], w, out_dtype=torch.float32), f"N={N} K={K} M={m}: fp32 out")
     ref = oracle.linear(x[:4].cpu(), w.cpu())
     assert_close_to_oracle(bi.bi_matmul(x[:4], wkn).cpu(), ref, "(K, N) strip vs oracle")
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16], ids=lambda d: str(d).split(".")[-1])
+def test_kn_pipe_equals_nk(dt):
+    """Row-major (K, N) weights above 64 rows with K a multiple of 64 run the 128x128 pipelined kernel's
+    (K, N) form (transposing LDS reads of 256-byte k-rows): ragged M and N, random inputs, bitwise equal
+    to the (N, K) path (whatever tile that takes), for matmul, addmm with a broadcast row and fp32 out."""
+    lib = bi._native.load()
+    BI = bi.BI_BF16 if dt == torch.bfloat16 else bi.BI_F16
+    for N, K in ((1000, 4096), (4104, 1024), (72, 192), (4096, 4096)):
+        x = synthetic.randn((1100, K), 0x5EED43 + K, 1.0, dt).to(DEV)
+        w = synthetic.randn((N, K), 0x5EED44 + N, 0.05, dt).to(DEV)
+        c = synthetic.randn((N,), 0x5EED45 + N, 1.0, dt).to(DEV)
+        wkn = w.t().contiguous()
+        for m in (65, 128, 129, 300, 1100):
+            assert lib.bi_gemm_kernel_name(m, N, K, BI, 1).decode() == "gemm16_pipe_kn/128x128", (m, N, K)
+            assert_bits_equal(bi.bi_matmul(x[:m], wkn), bi.bi_linear(x[:m], w), f"N={N} K={K} M={m}: (K, N) vs (N, K)")
+            assert_bits_equal(bi.bi_addmm(c, x[:m], wkn), bi.bi_linear(x[:m], w, c), f"N={N} K={K} M={m}: addmm")
+        assert_bits_equal(bi.bi_matmul(x[:300], wkn, out_dtype=torch.float32),
+                          bi.bi_linear(x[:300], w, out_dtype=torch.float32), f"N={N} K={K}: fp32 out")
+    ref = oracle.linear(x[[0, 1099]].cpu(), w.cpu())
+    assert_close_to_oracle(bi.bi_matmul(x, wkn)[[0, 1099]].cpu(), ref, "(K, N) pipe vs oracle")
