@@ -126,6 +126,23 @@ bi_status bi_matmul(const void *a, int64_t lda,
                     bi_dtype in_dt, bi_dtype out_dt,
                     void *stream);
 
+/* Batched bi_matmul: for z in [0, batch), c_z = a_z . b_z with a_z = a + z*stride_a,
+ * b_z = b + z*stride_b, c_z = c + z*stride_c (strides in elements, >= 0; a
+ * stride of 0 reuses one operand for every element).  Each element computes
+ * exactly bi_matmul's chain, so c_z has the bits bi_matmul(a_z, b_z) gives,
+ * whatever the batch and the element's position (the pages' matmul
+ * paragraph: the reduction of an output element never depends on the rest
+ * of the call); one launch per 65535 elements instead of one per element.
+ * Errors: as bi_matmul, plus BI_ERR_INVALID for a negative batch or stride
+ * or a stride_c that lets two elements' outputs overlap, BI_ERR_UNSUPPORTED
+ * for 16-bit stride_a / stride_b not a multiple of 8 elements (fp32: 4). */
+bi_status bi_matmul_batched(const void *a, int64_t lda, int64_t stride_a,
+                            const void *b, int64_t b_stride_k, int64_t b_stride_n, int64_t stride_b,
+                            void *c, int64_t ldc, int64_t stride_c,
+                            int64_t batch, int64_t M, int64_t N, int64_t K,
+                            bi_dtype in_dt, bi_dtype out_dt,
+                            void *stream);
+
 /* out (M,N) = alpha * (a (M,K) . b (K,N)) + beta * cin, b as for bi_matmul.
  * cin: out_dt elements, row m at cin + m*ldcin; ldcin == 0 broadcasts one
  * row of N elements to every m (the bias form).  When beta == 0, cin is not

@@ -10,6 +10,7 @@ back).
 Entry points (same names as the C ABI, plus the README's short names):
     bi_linear(x, w, bias=None)              y = x w^T + bias, w is (N, K)
     bi_matmul(a, b)                         y = a b, b is (K, N)
+    bi_matmul_batched(a, b)                 y[z] = a[z] b[z], 3-D operands, one launch
     bi_addmm(c, a, b, alpha=1, beta=1)      y = alpha a b + beta c
     bi_sdpa(q, k, v, causal=False, mask=None, scale=None)
     bi_sdpa_noalloc(q, k, v, ...)           bi_sdpa with no workspace allocation (per-GPU scratch)
@@ -27,7 +28,7 @@ import torch
 from . import _native
 from ._native import BI_BF16, BI_F16, BI_F32
 
-__all__ = ["bi_linear", "bi_matmul", "bi_addmm", "bi_sdpa", "bi_sdpa_noalloc", "bi_rowsum", "bi_variant_linear",
+__all__ = ["bi_linear", "bi_matmul", "bi_matmul_batched", "bi_addmm", "bi_sdpa", "bi_sdpa_noalloc", "bi_rowsum", "bi_variant_linear",
            "bi_variant_sdpa", "bi_quantized_linear", "quantize",
            "linear", "matmul", "addmm", "scaled_dot_product_attention",
            "abi_version", "library_path", "BiError"]
@@ -174,6 +175,38 @@ def bi_matmul(a: torch.Tensor, b: torch.Tensor, out_dtype: torch.dtype | None = 
                        _dt(a2, "bi_matmul"), _dt(y, "bi_matmul"), _stream(dev))
     _check(st, "bi_matmul")
     return y.reshape(*lead, N)
+
+
+def bi_matmul_batched(a: torch.Tensor, b: torch.Tensor, out_dtype: torch.dtype | None = None) -> torch.Tensor:
+    """y[z] = a[z] b[z] for 3-D a (batch, M, K) and b (batch, K, N), one launch; every element has the bits
+    bi_matmul(a[z], b[z]) gives."""
+    dev = _on_gpu(a, b)
+    if a.dtype != b.dtype:
+        raise ValueError("a and b must share a dtype")
+    if a.dim() != 3 or b.dim() != 3 or a.shape[0] != b.shape[0] or a.shape[2] != b.shape[1]:
+        raise ValueError(f"bi_matmul_batched: shapes {tuple(a.shape)} and {tuple(b.shape)} do not match")
+    out_dtype = out_dtype or a.dtype
+    Z, M, K = a.shape
+    N = b.shape[2]
+    epc = 16 // a.element_size()
+    # strides the kernels take as they are (a zero batch stride broadcasts one operand); else a copy
+    if not (a.stride(2) == 1 and (M <= 1 or (a.stride(1) >= K and a.stride(1) % epc == 0))
+            and a.stride(0) % epc == 0 and a.data_ptr() % 16 == 0):
+        a = a.clone(memory_format=torch.contiguous_format)
+    lda = a.stride(1) if M > 1 else max(K, 1)
+    row_major = b.stride(2) == 1 and (K <= 1 or (b.stride(1) >= N and b.stride(1) % epc == 0))
+    col_major = b.stride(1) == 1 and (N <= 1 or (b.stride(2) >= K and b.stride(2) % epc == 0))
+    if not ((row_major or col_major) and b.stride(0) % epc == 0 and b.data_ptr() % 16 == 0):
+        b = b.clone(memory_format=torch.contiguous_format)
+    y = torch.empty((Z, M, N), dtype=out_dtype, device=dev)
+    if Z == 0 or M == 0 or N == 0:
+        return y
+    lib = _native.load()
+    st = lib.bi_matmul_batched(_ptr(a), lda, a.stride(0), _ptr(b), b.stride(1), b.stride(2), b.stride(0),
+                               _ptr(y), max(N, 1), M * N, Z, M, N, K, _dt(a, "bi_matmul_batched"),
+                               _dt(y, "bi_matmul_batched"), _stream(dev))
+    _check(st, "bi_matmul_batched")
+    return y
 
 
 def bi_addmm(c: torch.Tensor | None, a: torch.Tensor, b: torch.Tensor, alpha: float = 1.0,

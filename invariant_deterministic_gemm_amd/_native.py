@@ -24,6 +24,8 @@ _i64p = ctypes.POINTER(ctypes.c_int64)
 SIGNATURES = {
     "bi_linear": (_i, [_p, _i64, _p, _i64, _p, _p, _i64, _i64, _i64, _i64, _i, _i, _p]),
     "bi_matmul": (_i, [_p, _i64, _p, _i64, _i64, _p, _i64, _i64, _i64, _i64, _i, _i, _p]),
+    "bi_matmul_batched": (_i, [_p, _i64, _i64, _p, _i64, _i64, _i64, _p, _i64, _i64, _i64, _i64, _i64, _i64, _i, _i,
+                               _p]),
     "bi_addmm": (_i, [_p, _i64, _p, _i64, _p, _i64, _i64, _p, _i64, _i64, _i64, _i64, _f, _f, _i, _i, _p]),
     "bi_sdpa": (_i, [_p, _i64p, _p, _i64p, _p, _i64p, _p, _i64p, _i64, _i64, _i64, _i64, _i64, _i64,
                      _f, _i, _p, _i64p, _i, _p, _sz, _p]),

@@ -208,6 +208,45 @@ bi_status bi_addmm(const void *cin, int64_t ldcin, const void *a, int64_t lda, c
     return device_status(bi::launch_gemm(p, in_dt, out_dt, b_kn, (hipStream_t)stream), "bi_addmm");
 }
 
+bi_status bi_matmul_batched(const void *a, int64_t lda, int64_t stride_a, const void *b, int64_t b_stride_k,
+                            int64_t b_stride_n, int64_t stride_b, void *c, int64_t ldc, int64_t stride_c,
+                            int64_t batch, int64_t M, int64_t N, int64_t K, bi_dtype in_dt, bi_dtype out_dt,
+                            void *stream) {
+    const char *fn = "bi_matmul_batched";
+    if (batch < 0) return fail(BI_ERR_INVALID, "%s: negative batch %lld", fn, (long long)batch);
+    if (batch > kMaxDim) return fail(BI_ERR_UNSUPPORTED, "%s: batch must be below 2^31", fn);
+    bool b_kn = true;
+    int64_t ldb = 0;
+    if (M > 0 && N > 0) {
+        bi_status r = resolve_b(fn, b_stride_k, b_stride_n, K, N, b_kn, ldb);
+        if (r != BI_OK) return r;
+    }
+    bi_status s = check_gemm(fn, a, lda, b, ldb, b_kn, c, ldc, M, N, K, in_dt, out_dt);
+    if (s != BI_OK || M == 0 || N == 0 || batch == 0) return s;
+    if (stride_a < 0 || stride_b < 0 || stride_c < 0)
+        return fail(BI_ERR_INVALID, "%s: negative batch stride", fn);
+    if (batch > 1 && stride_c < (M - 1) * ldc + N)
+        return fail(BI_ERR_INVALID, "%s: stride_c=%lld lets output elements overlap", fn, (long long)stride_c);
+    const int epc = 16 / esize(in_dt);
+    if (K > 0 && (stride_a % epc != 0 || stride_b % epc != 0))
+        return fail(BI_ERR_UNSUPPORTED, "%s: stride_a / stride_b must be multiples of %d elements", fn, epc);
+    bi::GemmParams p = make_params(a, lda, b, ldb, nullptr, 0, c, ldc, M, N, K, 1.0f, 0.0f);
+    p.sa = stride_a;
+    p.sb = stride_b;
+    p.sy = stride_c;
+    // one launch per 65535 elements (the grid's third dimension)
+    for (int64_t z0 = 0; z0 < batch; z0 += 65535) {
+        bi::GemmParams q = p;
+        q.batch = (int)std::min<int64_t>(65535, batch - z0);
+        q.A = static_cast<const char *>(a) + z0 * stride_a * esize(in_dt);
+        q.B = static_cast<const char *>(b) + z0 * stride_b * esize(in_dt);
+        q.Y = static_cast<char *>(c) + z0 * stride_c * esize(out_dt);
+        bi_status st = device_status(bi::launch_gemm(q, in_dt, out_dt, b_kn, (hipStream_t)stream), fn);
+        if (st != BI_OK) return st;
+    }
+    return BI_OK;
+}
+
 size_t bi_sdpa_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t S, int64_t D, bi_dtype dt) {
     if (!dtype_known(dt)) return 0;
     return bi::sdpa_workspace_bytes(B, Hq, Hkv, Lq, S, D, (int)dt);

@@ -23,7 +23,13 @@ struct GemmParams {
     // sums to partial[(s * M + m) * N + n] instead of running the epilogue.
     int splits;
     float *partial;
+    // Batched calls (bi_matmul_batched): `batch` independent products, element z at A + z sa, B + z sb,
+    // Y + z sy (strides in elements; grid dimension z).  0 or 1: one product.
+    int batch;
+    int64_t sa, sb, sy;
 };
+// Grid depth of a launch: the batch (at least 1).
+inline unsigned gemm_batch(const GemmParams &p) { return p.batch > 1 ? (unsigned)p.batch : 1u; }
 
 // The invariant path: picks a tile configuration from (M, N, K, layout) --
 // all configurations run the same per-element MFMA chain -- and enqueues it.

@@ -47,6 +47,7 @@ namespace bi {
 // B in the (N, K) layout: a lane's B chunk is 16 contiguous bytes of row n.
 template <int idt, int odt, int FM, int PD>
 __global__ __launch_bounds__(64) void gemm_skinny_nk(GemmParams p) {
+    batch_shift<idt, odt>(p, blockIdx.z);
     using C = Chunk<idt>;
     const int lane = threadIdx.x;
     const int r16 = lane & 15;
@@ -117,6 +118,7 @@ __global__ __launch_bounds__(64) void gemm_skinny_nk(GemmParams p) {
 // lane again holds EPC consecutive k of one column.
 template <int idt, int odt, int FM, int PD>
 __global__ __launch_bounds__(64) void gemm_skinny_kn(GemmParams p) {
+    batch_shift<idt, odt>(p, blockIdx.z);
     using C = Chunk<idt>;
     constexpr int CPR = C::EB;               // chunks per 16-column row piece (32 or 64 bytes)
     constexpr int TROW = C::CK * C::EB + 16; // LDS bytes per column (padded)
@@ -211,6 +213,7 @@ __global__ __launch_bounds__(64) void gemm_skinny_kn(GemmParams p) {
 // fragment reads free of bank conflicts.
 template <int idt, int odt, bool KN, int BM, int BN>
 __global__ __launch_bounds__(256) void gemm_tiled(GemmParams p) {
+    batch_shift<idt, odt>(p, (int)blockIdx.z / p.splits);       // z = batch element x splits + split
     using C = Chunk<idt>;
     constexpr int FM = BM / 32, FN = BN / 32;
     constexpr int ROWB = 128;                        // bytes of k per LDS row per tile
@@ -236,7 +239,7 @@ __global__ __launch_bounds__(256) void gemm_tiled(GemmParams p) {
 
     // global -> register staging
     u32x4 ra[A_CHUNKS], rb[B_CHUNKS];
-    const int split = blockIdx.z;
+    const int split = (int)blockIdx.z % p.splits;
     int s_begin, s_end;
     split_range(p, split, s_begin, s_end);
     const int nsteps = s_end - s_begin;
@@ -404,7 +407,7 @@ static hipError_t launch_generic(const GemmParams &p, bool b_kn, hipStream_t st)
     const GemmPlan16 pl = plan16(p.M, p.N);
     const unsigned sp = (unsigned)p.splits;
     if (pl.kind == 0) {
-        const dim3 grid((p.N + 15) / 16, sp), block(64);
+        const dim3 grid((p.N + 15) / 16, sp, gemm_batch(p)), block(64);
 #define SKINNY(FMV, PDV)                                                                             \
     do {                                                                                             \
         if (b_kn) hipLaunchKernelGGL((gemm_skinny_kn<idt, odt, FMV, PDV>), grid, block, 0, st, p); \
@@ -420,11 +423,11 @@ static hipError_t launch_generic(const GemmParams &p, bool b_kn, hipStream_t st)
         return hipGetLastError();
     }
     if (pl.bm == 128) {
-        const dim3 grid((p.N + 127) / 128, (p.M + 127) / 128, sp), block(256);
+        const dim3 grid((p.N + 127) / 128, (p.M + 127) / 128, sp * gemm_batch(p)), block(256);
         if (b_kn) hipLaunchKernelGGL((gemm_tiled<idt, odt, true, 128, 128>), grid, block, 0, st, p);
         else hipLaunchKernelGGL((gemm_tiled<idt, odt, false, 128, 128>), grid, block, 0, st, p);
     } else {
-        const dim3 grid((p.N + 63) / 64, (p.M + 63) / 64, sp), block(256);
+        const dim3 grid((p.N + 63) / 64, (p.M + 63) / 64, sp * gemm_batch(p)), block(256);
         if (b_kn) hipLaunchKernelGGL((gemm_tiled<idt, odt, true, 64, 64>), grid, block, 0, st, p);
         else hipLaunchKernelGGL((gemm_tiled<idt, odt, false, 64, 64>), grid, block, 0, st, p);
     }

@@ -61,6 +61,7 @@ __device__ __forceinline__ int kn_swz(int off) { return off ^ (((off >> 8) & 1) 
 
 template <int idt, int odt, int NB, int FM, int AR, int NS, int NL, bool KN = false>
 __global__ __launch_bounds__(64 * (1 + NL)) void gemm16_strip(GemmParams p) {
+    batch_shift<idt, odt>(p, blockIdx.z);
     constexpr int ROWB = 256;
     constexpr int SW = 16 * NB;                  // strip width: NB 16-column fragments
     constexpr int QB = SW / 4, QA = AR / 4, Q = QB + QA;
@@ -289,6 +290,7 @@ __global__ __launch_bounds__(64 * (1 + NL)) void gemm16_strip(GemmParams p) {
 // Every wave issues exactly QW loads per stage, so the vmcnt thresholds are exact.
 template <int idt, int odt, int BM, int BN, int WGM, int WGN, int NS>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm16_ring(GemmParams p) {
+    batch_shift<idt, odt>(p, blockIdx.z);
     constexpr int NW = WGM * WGN;
     constexpr int WM = BM / WGM, WN = BN / WGN;
     constexpr int FM = WM / 16, FN = WN / 16;
@@ -448,6 +450,7 @@ __device__ __forceinline__ int kn_pipe_swz(int r) { return 2 * (r & 3) ^ 8 * ((r
 
 template <int idt, int odt, int BM, int BN, int WGM, int WGN, int NS, int KS, int DR, bool KN = false>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm16_pipe(GemmParams p) {
+    batch_shift<idt, odt>(p, blockIdx.z);
     constexpr int NW = WGM * WGN;
     constexpr int WM = BM / WGM, WN = BN / WGN;
     constexpr int FM = WM / 16, FN = WN / 16;
@@ -703,14 +706,14 @@ static StripCfg strip_cfg_kn(int M) {
 template <int idt, int odt>
 static hipError_t launch16_typed(const GemmParams &p, bool b_kn, hipStream_t st) {
     if (b_kn && p.M > 64) {
-        const dim3 tiles((unsigned)(((p.M + 127) / 128) * ((p.N + 127) / 128)), p.splits);
+        const dim3 tiles((unsigned)(((p.M + 127) / 128) * ((p.N + 127) / 128)), p.splits, gemm_batch(p));
         hipLaunchKernelGGL((gemm16_pipe<idt, odt, 128, 128, 2, 4, 4, 64, 2, true>), tiles, dim3(512), 0, st, p);
         return hipGetLastError();
     }
     if (b_kn) {
         const StripCfg c = strip_cfg_kn(p.M);
         const int per = ((p.N + 15) / 16 + 7) / 8;   // strips per XCD
-        const dim3 grid(8 * per, p.splits), block(64 * (1 + c.nl));
+        const dim3 grid(8 * per, p.splits, gemm_batch(p)), block(64 * (1 + c.nl));
         if (c.ar == 4) hipLaunchKernelGGL((gemm16_strip<idt, odt, 1, 1, 4, 6, 3, true>), grid, block, 0, st, p);
         else if (c.ar == 8) hipLaunchKernelGGL((gemm16_strip<idt, odt, 1, 1, 8, 6, 3, true>), grid, block, 0, st, p);
         else if (c.ar == 16) hipLaunchKernelGGL((gemm16_strip<idt, odt, 1, 1, 16, 4, 3, true>), grid, block, 0, st, p);
@@ -720,7 +723,7 @@ static hipError_t launch16_typed(const GemmParams &p, bool b_kn, hipStream_t st)
     }
     if (use_strip(p.M, p.N, p.K)) {
         const StripCfg c = strip_cfg(p.M, p.N);
-        const dim3 grid((p.N + 16 * c.nb - 1) / (16 * c.nb), p.splits), block(64 * (1 + c.nl));
+        const dim3 grid((p.N + 16 * c.nb - 1) / (16 * c.nb), p.splits, gemm_batch(p)), block(64 * (1 + c.nl));
         if (c.ar == 4) hipLaunchKernelGGL((gemm16_strip<idt, odt, 1, 1, 4, 6, 3>), grid, block, 0, st, p);
         else if (c.ar == 8) hipLaunchKernelGGL((gemm16_strip<idt, odt, 1, 1, 8, 6, 3>), grid, block, 0, st, p);
         else if (c.ar == 16) hipLaunchKernelGGL((gemm16_strip<idt, odt, 1, 1, 16, 4, 3>), grid, block, 0, st, p);
@@ -731,7 +734,7 @@ static hipError_t launch16_typed(const GemmParams &p, bool b_kn, hipStream_t st)
         return hipGetLastError();
     }
     const TileCfg c = tile_cfg(p.M, p.N, p.K);
-    const dim3 tiles((unsigned)(((p.M + c.bm - 1) / c.bm) * ((p.N + c.bn - 1) / c.bn)), p.splits);
+    const dim3 tiles((unsigned)(((p.M + c.bm - 1) / c.bm) * ((p.N + c.bn - 1) / c.bn)), p.splits, gemm_batch(p));
     switch (c.kind) {
         case RING256x256:
             hipLaunchKernelGGL((gemm16_ring<idt, odt, 256, 256, 2, 4, 2>), tiles, dim3(512), 0, st, p);

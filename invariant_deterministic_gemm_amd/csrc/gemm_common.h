@@ -73,4 +73,13 @@ __device__ __forceinline__ void tile_coords(int b, int ntm, int ntn, int gm, int
     tn = r / gsize;
 }
 
+// Moves the operands to element z of a batched call (no C term there).
+template <int idt, int odt>
+__device__ __forceinline__ void batch_shift(GemmParams &p, int z) {
+    if (z == 0) return;
+    p.A = static_cast<const char *>(p.A) + (int64_t)z * p.sa * Elem<idt>::bytes;
+    p.B = static_cast<const char *>(p.B) + (int64_t)z * p.sb * Elem<idt>::bytes;
+    p.Y = static_cast<char *>(p.Y) + (int64_t)z * p.sy * Elem<odt>::bytes;
+}
+
 }  // namespace bi

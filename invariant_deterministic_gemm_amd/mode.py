@@ -24,7 +24,8 @@ function unchanged; the originals come back when the last mode exits):
     were measured invariant and are left alone.
 Every routed call runs the library's kernels through the C ABI binding, so
 results equal bi_linear / bi_matmul / bi_addmm / bi_sdpa / bi_rowsum bit for
-bit and no row depends on the batch.  A batched matmul runs one GEMM per batch element.
+bit and no row depends on the batch.  A batched matmul runs bi_matmul_batched (every element's bits
+those of bi_matmul on it).
 Calls whose tensors are all on the CPU are not the library's business and
 pass through untouched in either mode.  Every call of these functions is routed, including calls
 made inside other PyTorch Python functions (nn.Linear.forward, for example); calls made from C++
@@ -33,7 +34,7 @@ inside PyTorch, and references to the functions taken before the mode was entere
 Not routed (raises NotImplementedError when strict; runs stock PyTorch and
 is counted otherwise): dtypes other than fp32 / fp16 / bf16, mixed dtypes,
 inputs that require gradients while grad mode is on (the kernels are
-forward-only), out= arguments, broadcast batch dims in a matmul, attention
+forward-only), out= arguments, matmul batch dims that do not broadcast, attention
 with dropout, a float mask of another dtype than the query, head dims that
 are not a multiple of 32 up to 256, a causal flag together with a mask, and
 anything the library itself refuses
@@ -52,7 +53,7 @@ from collections import Counter
 import torch
 import torch.nn.functional as F
 
-from . import bi_addmm, bi_linear, bi_matmul, bi_rowsum, bi_sdpa
+from . import bi_addmm, bi_linear, bi_matmul, bi_matmul_batched, bi_rowsum, bi_sdpa
 
 _SUPPORTED = (torch.float32, torch.float16, torch.bfloat16)
 
@@ -86,8 +87,9 @@ def plan_matmul(a_shape, b_shape) -> str:
     """How torch.matmul(a, b) maps onto the kernels, from the shapes alone:
     'mm'  a (..., K) x b (K, N): one GEMM over the flattened rows of a;
     'mv'  a (..., K) x b (K,); 'vm' a (K,) x b (K, N); 'dot' a (K,) x b (K,);
-    'batched' a (*B, M, K) x b (*B, K, N) with equal batch dims: one GEMM per element.
-    Raises Unsupported otherwise (scalars, broadcast batch dims)."""
+    'batched' a (*Ba, M, K) or (K,) x b (*Bb, K, N) with at least one batch dim in b: the batch dims
+    broadcast (torch's rule) and one launch runs a GEMM per element.
+    Raises Unsupported otherwise (scalars, batch dims that do not broadcast)."""
     da, db = len(a_shape), len(b_shape)
     if da == 0 or db == 0:
         raise Unsupported("scalar operand")
@@ -95,9 +97,11 @@ def plan_matmul(a_shape, b_shape) -> str:
         return "mv" if da >= 2 else "dot"
     if db == 2:
         return "vm" if da == 1 else "mm"
-    if da == db and tuple(a_shape[:-2]) == tuple(b_shape[:-2]):
-        return "batched"
-    raise Unsupported(f"matmul of shapes {tuple(a_shape)} and {tuple(b_shape)} (broadcast batch dims)")
+    try:
+        torch.broadcast_shapes(tuple(a_shape[:-2]), tuple(b_shape[:-2]))
+    except RuntimeError:
+        raise Unsupported(f"matmul of shapes {tuple(a_shape)} and {tuple(b_shape)} (batch dims do not broadcast)")
+    return "batched"
 
 
 def _matmul(input, other):
@@ -112,13 +116,17 @@ def _matmul(input, other):
         return bi_matmul(a.reshape(1, -1), b).squeeze(0)
     if kind == "dot":
         return bi_linear(a.reshape(1, -1), b.reshape(1, -1)).reshape(())
-    lead = a.shape[:-2]
-    a3 = a.reshape(-1, a.shape[-2], a.shape[-1])
-    b3 = b.reshape(-1, b.shape[-2], b.shape[-1])
-    out = torch.empty((a3.shape[0], a.shape[-2], b.shape[-1]), dtype=a.dtype, device=a.device)
-    for i in range(a3.shape[0]):
-        out[i] = bi_matmul(a3[i], b3[i])
-    return out.reshape(*lead, a.shape[-2], b.shape[-1])
+    vec = a.dim() == 1                    # (K,) x (*B, K, N): a one-row matrix, the row dim dropped after
+    if vec:
+        a = a.reshape(1, -1)
+    lead = torch.broadcast_shapes(a.shape[:-2], b.shape[:-2])
+    M, K, N = a.shape[-2], a.shape[-1], b.shape[-1]
+    _need(b.shape[-2] == K, f"inner dims differ ({K} vs {b.shape[-2]})")
+    # a broadcast operand keeps batch stride 0 where the batch dims merge; a copy otherwise (exact)
+    a3 = a.expand(*lead, M, K).reshape(-1, M, K)
+    b3 = b.expand(*lead, K, N).reshape(-1, K, N)
+    y = bi_matmul_batched(a3, b3).reshape(*lead, M, N)
+    return y.squeeze(-2) if vec else y
 
 
 def _rmatmul(input, other):               # Tensor.__rmatmul__(self, other) computes other @ self

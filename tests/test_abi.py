@@ -117,6 +117,27 @@ def test_gemm_validation(lib):
     assert lib.bi_last_error().decode() == ""
 
 
+def test_matmul_batched_validation(lib):
+    # every call fails validation or is empty, so nothing is launched on the placeholder pointers
+    def bat(batch=2, sa=4096, sb=4096, sc=2048, b_k=32, b_n=1, M=64, N=32, K=64, ind=BF16, outd=BF16, c=P16):
+        return lib.bi_matmul_batched(P16, 64, sa, P16b, b_k, b_n, sb, c, 32, sc, batch, M, N, K, ind, outd, None)
+    assert bat(batch=-1) == INVALID
+    assert bat(batch=1 << 31) == UNSUPPORTED
+    assert bat(sa=-8) == INVALID
+    assert bat(sc=-32) == INVALID
+    assert bat(sc=2047) == INVALID                   # element z's last row overlaps element z+1's first
+    assert bat(sa=4100) == UNSUPPORTED                # 16-bit batch strides: multiples of 8 elements
+    assert bat(sb=12) == UNSUPPORTED
+    assert bat(b_k=2, b_n=128) == UNSUPPORTED         # no unit stride in b
+    assert bat(c=None) == INVALID
+    assert bat(ind=F32, outd=BF16) == UNSUPPORTED
+    # empty problems succeed without a launch
+    assert bat(batch=0) == OK
+    assert bat(M=0) == OK
+    assert bat(N=0, b_k=0) == OK
+    assert lib.bi_last_error().decode() == ""
+
+
 def test_matmul_addmm_validation(lib):
     # row-major (K, N) operand: N must be a multiple of 8 for 16-bit inputs
     assert lib.bi_matmul(P16, 64, P16b, 36, 1, P16, 36, 4, 36, 64, BF16, BF16, None) == UNSUPPORTED

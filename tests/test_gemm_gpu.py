@@ -457,3 +457,43 @@ def test_kn_pipe_equals_nk(dt):
                           bi.bi_linear(x[:300], w, out_dtype=torch.float32), f"N={N} K={K}: fp32 out")
     ref = oracle.linear(x[[0, 1099]].cpu(), w.cpu())
     assert_close_to_oracle(bi.bi_matmul(x, wkn)[[0, 1099]].cpu(), ref, "(K, N) pipe vs oracle")
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16, torch.float32], ids=lambda d: str(d).split(".")[-1])
+def test_batched_matmul_equals_per_element_calls(dt):
+    """bi_matmul_batched runs every batch element in one launch (the grid's third dimension); each element's
+    bits equal bi_matmul on that element alone, for every kernel family the shapes reach (strip, pipelined
+    and ring tiles, the generic tiled kernel), row-major and column-major b, a shared operand (batch stride
+    0), a strided slice of a larger batch, and fp32 output."""
+    Z = 3
+    shapes = ((1, 72, 136), (17, 264, 256), (100, 520, 520), (300, 1000, 1024), (1100, 256, 4096))
+    for M, N, K in shapes:
+        a = synthetic.randn((Z + 1, M, K), 0x5EED61 + M, 1.0, dt).to(DEV)[1:]      # storage offset: one element
+        w = synthetic.randn((Z, N, K), 0x5EED62 + N, 0.05, dt).to(DEV)
+        bkn = w.transpose(1, 2).contiguous()          # (Z, K, N) row-major
+        bnk = w.transpose(1, 2)                       # column-major views of the (N, K) rows
+        for name, b in (("(K, N)", bkn), ("(N, K)", bnk)):
+            y = bi.bi_matmul_batched(a, b)
+            assert y.shape == (Z, M, N)
+            for z in range(Z):
+                assert_bits_equal(y[z], bi.bi_matmul(a[z], b[z]), f"M={M} N={N} K={K} b {name} element {z}")
+        shared = bkn[1:2].expand(Z, K, N)             # batch stride 0: one weight for every element
+        y = bi.bi_matmul_batched(a, shared)
+        for z in range(Z):
+            assert_bits_equal(y[z], bi.bi_matmul(a[z], bkn[1]), f"M={M} N={N} K={K} shared b element {z}")
+        if dt != torch.float32:
+            y = bi.bi_matmul_batched(a, bkn, out_dtype=torch.float32)
+            assert_bits_equal(y[2], bi.bi_matmul(a[2], bkn[2], out_dtype=torch.float32), f"M={M}: fp32 out")
+        rows = [0, M - 1]
+        ref = oracle.matmul(a[1, rows].cpu(), bkn[1].cpu())
+        assert_close_to_oracle(bi.bi_matmul_batched(a, bkn)[1, rows].cpu(), ref, f"M={M} N={N} K={K} vs oracle")
+
+
+def test_batched_matmul_past_one_grid_of_elements():
+    """More than 65535 elements take several launches; integer inputs make every element exact."""
+    Z, M, N, K = 70001, 2, 8, 16
+    a = ints((Z, M, K), 0x5EED63, torch.bfloat16).to(DEV)
+    b = ints((Z, K, N), 0x5EED64, torch.bfloat16).to(DEV)
+    y = bi.bi_matmul_batched(a, b).cpu()
+    ref = torch.bmm(a.cpu().double(), b.cpu().double()).to(torch.bfloat16)
+    assert_bits_equal(y, ref, "70001 integer-valued elements")

@@ -13,13 +13,15 @@ def test_routed_functions():
 
 @pytest.mark.parametrize("a,b,kind", [((4, 5), (5, 3), "mm"), ((2, 4, 5), (5, 3), "mm"), ((5,), (5, 3), "vm"),
                                       ((4, 5), (5,), "mv"), ((5,), (5,), "dot"), ((2, 4, 5), (2, 5, 3), "batched"),
-                                      ((2, 3, 4, 5), (2, 3, 5, 6), "batched")])
+                                      ((2, 3, 4, 5), (2, 3, 5, 6), "batched"), ((2, 4, 5), (1, 5, 3), "batched"),
+                                      ((2, 4, 5), (3, 2, 5, 3), "batched"), ((4, 5), (2, 5, 3), "batched"),
+                                      ((5,), (2, 5, 3), "batched")])
 def test_plan_matmul(a, b, kind):
     assert mode.plan_matmul(a, b) == kind
 
 
-@pytest.mark.parametrize("a,b", [((), (3,)), ((2, 4, 5), (1, 5, 3)), ((2, 4, 5), (3, 2, 5, 3)), ((4, 5), (2, 5, 3))])
-def test_plan_matmul_refuses_broadcasts_and_scalars(a, b):
+@pytest.mark.parametrize("a,b", [((), (3,)), ((3, 4), ()), ((2, 4, 5), (3, 5, 3)), ((2, 3, 4, 5), (4, 5, 6))])
+def test_plan_matmul_refuses_scalars_and_batch_dims_that_do_not_broadcast(a, b):
     with pytest.raises(mode.Unsupported):
         mode.plan_matmul(a, b)
 

@@ -59,6 +59,25 @@ def test_routed_matmuls_equal_direct_calls():
     assert (lin.float() - ref).abs().max() / ref.abs().max() < 2e-2
 
 
+def test_broadcast_batched_matmuls_equal_per_element_calls():
+    """torch's broadcasting matmul forms run one batched launch; each element equals bi_matmul on it."""
+    a, b = _r((2, 3, 40, 64), 41), _r((2, 3, 64, 24), 42)
+    bb, v = _r((3, 64, 24), 43), _r((64,), 44)
+    with bi.batch_invariant_mode() as m:
+        ybc = a @ bb                      # b broadcast over the first batch dim (a copy when dims merge)
+        yab = a[0, 0] @ b                 # a 2-D left operand shared by every element (batch stride 0)
+        yv = torch.matmul(v, b)           # (K,) x (2, 3, K, N) -> (2, 3, N)
+        ybt = torch.matmul(a, b.transpose(-1, -2).contiguous().transpose(-1, -2))   # column-major b views
+    assert not m.fallbacks
+    assert ybc.shape == (2, 3, 40, 24) and yab.shape == (2, 3, 40, 24) and yv.shape == (2, 3, 24)
+    for i in range(2):
+        for j in range(3):
+            assert_bits_equal(ybc[i, j], bi.bi_matmul(a[i, j], bb[j]), f"b broadcast, element {i},{j}")
+            assert_bits_equal(yab[i, j], bi.bi_matmul(a[0, 0], b[i, j]), f"a broadcast, element {i},{j}")
+            assert_bits_equal(yv[i, j], bi.bi_matmul(v.reshape(1, 64), b[i, j])[0], f"vector, element {i},{j}")
+            assert_bits_equal(ybt[i, j], bi.bi_matmul(a[i, j], b[i, j]), f"column-major b, element {i},{j}")
+
+
 def test_nn_linear_rows_do_not_depend_on_batch():
     torch.manual_seed(0)
     net = torch.nn.Sequential(torch.nn.Linear(512, 1024), torch.nn.GELU(), torch.nn.Linear(1024, 512))
@@ -120,7 +139,7 @@ def test_strict_mode_raises_and_lenient_mode_falls_back():
         with pytest.raises(NotImplementedError):
             F.linear(xb.requires_grad_(), wb)
         with pytest.raises(NotImplementedError):
-            torch.matmul(_r((2, 4, 64), 34), _r((1, 64, 8), 35))     # broadcast batch dims
+            torch.matmul(_r((2, 4, 64), 34), _r((3, 64, 8), 35))     # batch dims that do not broadcast
     with bi.batch_invariant_mode(strict=False) as m:
         y = x64 @ x64.t()
         z = F.scaled_dot_product_attention(q, q, q, attn_mask=fmask)
