@@ -130,12 +130,14 @@ bi_status bi_matmul(const void *a, int64_t lda,
  * b_z = b + z*stride_b, c_z = c + z*stride_c (strides in elements, >= 0; a
  * stride of 0 reuses one operand for every element).  Each element computes
  * exactly bi_matmul's chain, so c_z has the bits bi_matmul(a_z, b_z) gives,
- * whatever the batch and the element's position (the pages' matmul
- * paragraph: the reduction of an output element never depends on the rest
- * of the call); one launch per 65535 elements instead of one per element.
+ * whatever the batch and the element's position (README, section "Why MLX
+ * is not invariant", matmul paragraph: an output element's reduction must
+ * not depend on the rest of the call); one launch per 65535 elements
+ * instead of one per element.  batch == 0 does nothing.
  * Errors: as bi_matmul, plus BI_ERR_INVALID for a negative batch or stride
  * or a stride_c that lets two elements' outputs overlap, BI_ERR_UNSUPPORTED
- * for 16-bit stride_a / stride_b not a multiple of 8 elements (fp32: 4). */
+ * for a batch of 2^31 or more and for 16-bit stride_a / stride_b not a
+ * multiple of 8 elements (fp32: 4). */
 bi_status bi_matmul_batched(const void *a, int64_t lda, int64_t stride_a,
                             const void *b, int64_t b_stride_k, int64_t b_stride_n, int64_t stride_b,
                             void *c, int64_t ldc, int64_t stride_c,
