@@ -203,6 +203,7 @@ template <int dt, int D>
 __global__ __launch_bounds__(64) void sdpa_split(SdpaParams p) {
     using A = AttnShape<dt, D>;
     constexpr float NEG_INF = -__builtin_huge_valf();
+    constexpr bool SLIM = A::EB == 4 && D > 128;
     __shared__ __attribute__((aligned(16))) char vs[KV_BLOCK * A::VROW];
 
     const int lane = threadIdx.x;
@@ -250,45 +251,81 @@ __global__ __launch_bounds__(64) void sdpa_split(SdpaParams p) {
 
     for (int blk = 0; blk < nblk; ++blk) {
         const int kb = kbeg + blk * KV_BLOCK;
-        // ---- K fragments straight from HBM (A operand of S^T = K Q^T)
-        u32x4 kf[4][A::NCH];
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-            const int key = kb + 16 * kt + r16;
-            const char *krow = kbase + (int64_t)key * p.ks[2] * A::EB;
-#pragma unroll
-            for (int c = 0; c < A::NCH; ++c)
-                kf[kt][c] = key < p.S ? ldg16(krow + A::d_of(c, g) * A::EB) : zero_u4();
-        }
-        // ---- V block -> LDS, row-major with padded rows; absent keys are zero
-        u32x4 vr[KV_BLOCK * A::VCH / 64];
-#pragma unroll
-        for (int i = 0; i < KV_BLOCK * A::VCH / 64; ++i) {
-            const int id = lane + 64 * i;
-            const int key = id / A::VCH, c = id % A::VCH;
-            vr[i] = (kb + key < p.S) ? ldg16(vbase + ((int64_t)(kb + key) * p.vs[2] + c * A::EPC) * A::EB)
-                                     : zero_u4();
-        }
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < KV_BLOCK * A::VCH / 64; ++i) {
-            const int id = lane + 64 * i;
-            const int key = id / A::VCH, c = id % A::VCH;
-            char *dst = vs + key * A::VROW + c * 16;
-            if constexpr (A::EB == 2) {
-                reinterpret_cast<u32x2 *>(dst)[0] = u32x2{vr[i][0], vr[i][1]};
-                reinterpret_cast<u32x2 *>(dst)[1] = u32x2{vr[i][2], vr[i][3]};
-            } else {
-                *reinterpret_cast<u32x4 *>(dst) = vr[i];
-            }
-        }
-        // ---- scores: lane holds S^T[key 16 kt + 4 g + i][row r16]
         f32x4 st[4];
+        if constexpr (SLIM) {
+            // fp32 rows above 128: V staged in four pieces, K one key tile at a time (the whole block's
+            // fragments would need 512 registers per lane); same loads, same chains
+            constexpr int NV = KV_BLOCK * A::VCH / 64, VP = NV / 4;
+            static_assert(NV % 4 == 0, "four V pieces");
+            __syncthreads();                             // the previous block's V reads are done
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-            st[kt] = zero4();
+            for (int piece = 0; piece < 4; ++piece) {
+                u32x4 vr[VP];
 #pragma unroll
-            for (int c = 0; c < A::NCH; ++c) st[kt] = attn_mfma_chunk<dt>(kf[kt][c], qf[c], st[kt]);
+                for (int i = 0; i < VP; ++i) {
+                    const int id = lane + 64 * (piece * VP + i);
+                    const int key = id / A::VCH, c = id % A::VCH;
+                    vr[i] = (kb + key < p.S) ? ldg16(vbase + ((int64_t)(kb + key) * p.vs[2] + c * A::EPC) * A::EB)
+                                             : zero_u4();
+                }
+#pragma unroll
+                for (int i = 0; i < VP; ++i) {
+                    const int id = lane + 64 * (piece * VP + i);
+                    const int key = id / A::VCH, c = id % A::VCH;
+                    *reinterpret_cast<u32x4 *>(vs + key * A::VROW + c * 16) = vr[i];
+                }
+            }
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) {
+                const int key = kb + 16 * kt + r16;
+                const char *krow = kbase + (int64_t)key * p.ks[2] * A::EB;
+                u32x4 kf[A::NCH];
+#pragma unroll
+                for (int c = 0; c < A::NCH; ++c) kf[c] = key < p.S ? ldg16(krow + A::d_of(c, g) * A::EB) : zero_u4();
+                st[kt] = zero4();
+#pragma unroll
+                for (int c = 0; c < A::NCH; ++c) st[kt] = attn_mfma_chunk<dt>(kf[c], qf[c], st[kt]);
+            }
+        } else {
+            // ---- K fragments straight from HBM (A operand of S^T = K Q^T)
+            u32x4 kf[4][A::NCH];
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) {
+                const int key = kb + 16 * kt + r16;
+                const char *krow = kbase + (int64_t)key * p.ks[2] * A::EB;
+#pragma unroll
+                for (int c = 0; c < A::NCH; ++c)
+                    kf[kt][c] = key < p.S ? ldg16(krow + A::d_of(c, g) * A::EB) : zero_u4();
+            }
+            // ---- V block -> LDS, row-major with padded rows; absent keys are zero
+            u32x4 vr[KV_BLOCK * A::VCH / 64];
+#pragma unroll
+            for (int i = 0; i < KV_BLOCK * A::VCH / 64; ++i) {
+                const int id = lane + 64 * i;
+                const int key = id / A::VCH, c = id % A::VCH;
+                vr[i] = (kb + key < p.S) ? ldg16(vbase + ((int64_t)(kb + key) * p.vs[2] + c * A::EPC) * A::EB)
+                                         : zero_u4();
+            }
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < KV_BLOCK * A::VCH / 64; ++i) {
+                const int id = lane + 64 * i;
+                const int key = id / A::VCH, c = id % A::VCH;
+                char *dst = vs + key * A::VROW + c * 16;
+                if constexpr (A::EB == 2) {
+                    reinterpret_cast<u32x2 *>(dst)[0] = u32x2{vr[i][0], vr[i][1]};
+                    reinterpret_cast<u32x2 *>(dst)[1] = u32x2{vr[i][2], vr[i][3]};
+                } else {
+                    *reinterpret_cast<u32x4 *>(dst) = vr[i];
+                }
+            }
+            // ---- scores: lane holds S^T[key 16 kt + 4 g + i][row r16]
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) {
+                st[kt] = zero4();
+#pragma unroll
+                for (int c = 0; c < A::NCH; ++c) st[kt] = attn_mfma_chunk<dt>(kf[kt][c], qf[c], st[kt]);
+            }
         }
         float s[4][4];
         float mb = NEG_INF;
